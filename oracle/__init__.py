@@ -1,0 +1,321 @@
+"""CPU oracle for block-scaled FP4 quantization and the GEMMs that consume it.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product package.  It shares no
+code with the HIP library.
+
+The arithmetic lives in fp4_oracle.c (plain C, binary32 step sequence with no
+contraction); this module marshals numpy arrays into it and adds the GEMM
+reference, which is the binary64 product of the exactly dequantized operands
+(numpy matmul as the library primitive) with the per-element tolerance
+T = 1e-5 * sum_k |a_k||b_k|.
+
+Page citations (see fp4_oracle.c for the full list):
+  quant_prune_distill/486 "Метод": NVFP4 = E2M1 / group 16 / E4M3 scale,
+  MXFP = group 32 / E8M0 scale.
+  gonzo_ML/3986 "Форматы FP4" and "Стохастическая квантизация".
+  ue5m3-fp4-pretraining "Что сделали": UE5M3, tensor max refreshed every 50.
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+except the UE5M3 exponent bias, which the pages do not give (parity unpinned
+beyond the format's own round-trip and the unsigned property).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_fp4.so")
+
+# scale format name -> (exponent bits, mantissa bits, has sign bit)
+FORMATS = {
+    "e4m3": (4, 3, 1),
+    "ue5m3": (5, 3, 0),
+    "e3m4": (3, 4, 1),
+    "e1m6": (1, 6, 1),
+    "e2m5": (2, 5, 1),
+    "e5m2": (5, 2, 1),
+    "e6m1": (6, 1, 1),
+    "e7m0": (7, 0, 1),
+    "e8m0": (8, 0, 0),
+}
+
+_lib = None
+
+
+def lib():
+    """Load (building first if needed) the oracle shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    src = os.path.join(_HERE, "fp4_oracle.c")
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        from . import build as _b
+        _b.build()
+    L = ctypes.CDLL(_LIB_PATH)
+    c_i64, c_u64, c_f, c_d, c_int, c_p = (ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
+                                         ctypes.c_double, ctypes.c_int, ctypes.c_void_p)
+    sig = {
+        "or_e2m1_decode": (c_d, [c_int]),
+        "or_e2m1_rtn": (c_int, [c_f]),
+        "or_e2m1_sr": (c_int, [c_f, ctypes.c_uint32]),
+        "or_scale_is_nan": (c_int, [c_int, c_int, c_int, c_int]),
+        "or_scale_decode": (c_d, [c_int, c_int, c_int, c_int]),
+        "or_scale_max": (c_d, [c_int, c_int, c_int]),
+        "or_scale_encode": (c_int, [c_int, c_int, c_int, c_f]),
+        "or_e8m0_block_code": (c_int, [c_f]),
+        "or_tensor_scale": (c_f, [c_f, c_int, c_int, c_int]),
+        "or_philox4x32_10": (None, [c_p, c_p, c_p]),
+        "or_sr_bits": (ctypes.c_uint32, [c_u64, c_u64, c_u64]),
+        "or_amax": (c_f, [c_p, c_int, c_i64, c_i64, c_i64]),
+        "or_quantize": (c_int, [c_p, c_int, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_f,
+                                c_int, c_u64, c_u64, c_i64, c_i64, c_p, c_p, c_int]),
+        "or_f32_to_bf16": (ctypes.c_uint16, [c_f]),
+        "or_dequantize": (c_int, [c_p, c_p, c_f, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                  c_p, c_i64]),
+        "or_dequantize_f64": (c_int, [c_p, c_p, c_f, c_i64, c_i64, c_int, c_int, c_int, c_int, c_p]),
+        "or_round_to_bf16": (c_d, [c_d]),
+        "or_round_to_bf16_array": (None, [c_p, c_p, c_i64]),
+        "or_e2m1_rtn_array": (None, [c_p, c_p, c_i64]),
+        "or_e2m1_sr_array": (None, [c_p, c_p, c_p, c_i64]),
+        "or_sr_bits_array": (None, [c_u64, c_u64, c_u64, c_i64, c_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _fmt(fmt: str):
+    try:
+        return FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown scale format {fmt!r}") from None
+
+
+def _as_input(x: np.ndarray):
+    """x is float32, or uint16 holding bf16 bit patterns."""
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), 0
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), 1
+    raise TypeError("oracle input must be float32 or uint16 (bf16 bits)")
+
+
+# --------------------------------------------------------------------------
+# element / scale codecs
+# --------------------------------------------------------------------------
+def e2m1_decode(code: int) -> float:
+    return lib().or_e2m1_decode(int(code))
+
+
+def e2m1_rtn(v: float) -> int:
+    return lib().or_e2m1_rtn(float(v))
+
+
+def e2m1_sr(v: float, r16: int) -> int:
+    return lib().or_e2m1_sr(float(v), int(r16))
+
+
+def e2m1_rtn_array(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    out = np.empty(v.size, dtype=np.uint8)
+    lib().or_e2m1_rtn_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def e2m1_sr_array(v: np.ndarray, r16: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    r = np.ascontiguousarray(r16, dtype=np.uint32).ravel()
+    assert r.size == v.size
+    out = np.empty(v.size, dtype=np.uint8)
+    lib().or_e2m1_sr_array(_ptr(v), _ptr(r), _ptr(out), v.size)
+    return out
+
+
+def sr_bits_array(seed: int, offset: int, i0: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint32)
+    lib().or_sr_bits_array(seed, offset, i0, n, _ptr(out))
+    return out
+
+
+def scale_decode(fmt: str, code: int) -> float:
+    return lib().or_scale_decode(*_fmt(fmt), int(code))
+
+
+def scale_is_nan(fmt: str, code: int) -> bool:
+    return bool(lib().or_scale_is_nan(*_fmt(fmt), int(code)))
+
+
+def scale_max(fmt: str) -> float:
+    return lib().or_scale_max(*_fmt(fmt))
+
+
+def scale_encode(fmt: str, u: float) -> int:
+    if fmt == "e8m0":
+        raise ValueError("E8M0 block scales use the exponent rule (e8m0_block_code)")
+    return lib().or_scale_encode(*_fmt(fmt), float(u))
+
+
+def e8m0_block_code(amax_b: float) -> int:
+    return lib().or_e8m0_block_code(float(amax_b))
+
+
+def tensor_scale(amax_t: float, fmt: str) -> float:
+    return lib().or_tensor_scale(float(amax_t), *_fmt(fmt))
+
+
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().or_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_bits(seed: int, offset: int, i: int) -> int:
+    return lib().or_sr_bits(seed, offset, i)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    f = lib().or_f32_to_bf16
+    return np.array([f(float(v)) for v in x], dtype=np.uint16)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Correct (RNE) rounding of binary64 values to bf16, returned as binary64."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib().or_round_to_bf16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+# --------------------------------------------------------------------------
+# tensor operations
+# --------------------------------------------------------------------------
+def amax(x: np.ndarray) -> float:
+    x, is_bf16 = _as_input(x)
+    rows, cols = x.shape
+    return lib().or_amax(_ptr(x), is_bf16, rows, cols, cols)
+
+
+def quantize(x: np.ndarray, block: int, fmt: str, g: float, *, stochastic: bool = False,
+             seed: int = 0, offset: int = 0, rows: tuple | None = None, nthreads: int = 1):
+    """Quantize rows [r0, r1) of x (all rows by default) with tensor scale g.
+
+    Returns (q, scales): q is uint8 [r1-r0, cols/2] (low nibble = even
+    element), scales is uint8 [r1-r0, cols/block].
+    """
+    x, is_bf16 = _as_input(x)
+    nrows, cols = x.shape
+    r0, r1 = (0, nrows) if rows is None else rows
+    q = np.zeros((r1 - r0, cols // 2), dtype=np.uint8)
+    s = np.zeros((r1 - r0, cols // block), dtype=np.uint8)
+    rc = lib().or_quantize(_ptr(x), is_bf16, nrows, cols, cols, block, *_fmt(fmt), float(g),
+                           int(stochastic), seed, offset, r0, r1, _ptr(q), _ptr(s), nthreads)
+    if rc != 0:
+        raise ValueError("oracle quantize: argument outside the contract")
+    return q, s
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str,
+               out: str = "f32") -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = q.shape[0], q.shape[1] * 2
+    if out == "f32":
+        y = np.empty((rows, cols), dtype=np.float32)
+    elif out == "bf16":
+        y = np.empty((rows, cols), dtype=np.uint16)
+    else:
+        raise ValueError(out)
+    rc = lib().or_dequantize(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt),
+                             int(out == "bf16"), _ptr(y), cols)
+    if rc != 0:
+        raise ValueError("oracle dequantize: argument outside the contract")
+    return y
+
+
+def dequantize_f64(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = q.shape[0], q.shape[1] * 2
+    y = np.empty((rows, cols), dtype=np.float64)
+    rc = lib().or_dequantize_f64(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle dequantize_f64: argument outside the contract")
+    return y
+
+
+# --------------------------------------------------------------------------
+# amax policies (ue5m3-fp4-pretraining "Что сделали": the tensor maximum is
+# refreshed once every 50 steps and the stored value is used in between)
+# --------------------------------------------------------------------------
+@dataclass
+class AmaxState:
+    interval: int = 50
+    calls: int = 0
+    amax: float = 0.0
+
+
+def resolve_tensor_scale(x: np.ndarray, fmt: str, policy: str, state: AmaxState | None = None):
+    """Return (g, amax_used) for one quantize call and advance a delayed state.
+
+    policy: "none" (g = 1), "current" (amax of this tensor), or "delayed"
+    (refresh from this tensor when calls % interval == 0, else reuse).
+    """
+    if policy == "none":
+        return 1.0, 0.0
+    if policy == "current":
+        a = amax(x)
+        return tensor_scale(a, fmt), a
+    if policy == "delayed":
+        if state is None:
+            raise ValueError("delayed policy needs a state")
+        if state.calls % state.interval == 0:
+            state.amax = amax(x)
+        state.calls += 1
+        return tensor_scale(state.amax, fmt), state.amax
+    raise ValueError(policy)
+
+
+def quantize_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *, state: AmaxState | None = None,
+                    stochastic: bool = False, seed: int = 0, offset: int = 0, nthreads: int = 1):
+    """Whole quantize call: tensor scale per policy, then every block.
+    Returns (q, scales, g, amax_used)."""
+    g, a = resolve_tensor_scale(x, fmt, policy, state)
+    q, s = quantize(x, block, fmt, g, stochastic=stochastic, seed=seed, offset=offset, nthreads=nthreads)
+    return q, s, g, a
+
+
+# --------------------------------------------------------------------------
+# GEMM references
+# --------------------------------------------------------------------------
+def gemm_ref(a_hat: np.ndarray, b_hat: np.ndarray):
+    """C = A_hat @ B_hat^T in binary64 and T = 1e-5 * |A_hat| @ |B_hat|^T.
+
+    a_hat: [M, K], b_hat: [N, K] exact binary64 dequantized operands (both
+    blocked along K; the weight is stored [N, K])."""
+    c = a_hat @ b_hat.T
+    t = 1e-5 * (np.abs(a_hat) @ np.abs(b_hat).T)
+    return c, t
+
+
+def gemm_check(c_out: np.ndarray, c_ref: np.ndarray, tol: np.ndarray) -> np.ndarray:
+    """Boolean mask of bf16 outputs (given as float values) that are the bf16
+    rounding of some value within [c_ref - tol, c_ref + tol]."""
+    lo = round_to_bf16(c_ref - tol)
+    hi = round_to_bf16(c_ref + tol)
+    c = np.asarray(c_out, dtype=np.float64)
+    return (lo <= c) & (c <= hi)

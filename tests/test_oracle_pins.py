@@ -1,0 +1,592 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here checks the oracle against something other than itself: values
+the pages print (tests/golden), closed forms of the formats, an independent
+library implementation (torch's float8 conversions, rocRAND's Philox engine),
+exact rational arithmetic, and invariants of the method.  None needs a GPU.
+"""
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.conftest import ROOT, read_golden
+
+ALL_FMTS = ["e1m6", "e2m5", "e3m4", "e4m3", "e5m2", "e6m1", "e7m0", "ue5m3", "e8m0"]
+GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def f32(bits):
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# E2M1 element codec
+# ---------------------------------------------------------------------------
+def test_e2m1_decode_matches_grid_fixture():
+    rows = read_golden("e2m1_grid.txt")
+    assert len(rows) == 16
+    for code, val in rows:
+        v = oracle.e2m1_decode(int(code))
+        assert v == float(val)
+        assert math.copysign(1.0, v) == math.copysign(1.0, float(val))
+
+
+def _rtn_threshold_form(a: np.ndarray) -> np.ndarray:
+    """Nearest-even E2M1 magnitude by counting crossed midpoints: a midpoint
+    between an even code and the next odd code rounds down (strict >), a
+    midpoint between an odd code and the next even code rounds up (>=);
+    everything at or beyond 6 is code 7."""
+    a = np.abs(a.astype(np.float64))
+    return ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+            + (a > 2.5) + (a >= 3.5) + (a > 5.0)).astype(np.uint8)
+
+
+def test_e2m1_rtn_against_midpoint_closed_form():
+    # every fp32 within +-4096 ulps of each midpoint and grid point, both signs
+    centres = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] + GRID[1:] + [8.0]
+    pieces = []
+    for c in centres:
+        b = np.float32(c).view(np.uint32).astype(np.int64)
+        pieces.append(np.arange(b - 4096, b + 4097, dtype=np.int64))
+    # plus a strided sweep of all fp32 in [0, 16) and the subnormals
+    pieces.append(np.arange(0, 0x41800000, 997, dtype=np.int64))
+    pieces.append(np.arange(0, 1 << 23, 4099, dtype=np.int64))
+    bits = np.concatenate(pieces).astype(np.uint32)
+    for sign in (0, 0x80000000):
+        v = f32(bits | np.uint32(sign))
+        got = oracle.e2m1_rtn_array(v)
+        want = _rtn_threshold_form(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (v[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_e2m1_rtn_is_nearest_with_even_ties_exact():
+    # exact rational check on random values: chosen magnitude is at minimum
+    # distance and on ties its code is even; beyond 6 it saturates.
+    rng = np.random.default_rng(11)
+    v = rng.uniform(0, 7, 20000).astype(np.float32)
+    got = oracle.e2m1_rtn_array(v)
+    for x, c in zip(v, got):
+        fx = Fraction(float(x))
+        if fx >= 6:
+            assert c == 7
+            continue
+        d = [abs(fx - Fraction(g)) for g in GRID]
+        m = min(d)
+        best = [i for i in range(8) if d[i] == m]
+        want = best[0] if len(best) == 1 else [i for i in best if i % 2 == 0][0]
+        assert c == want
+
+
+# ---------------------------------------------------------------------------
+# stochastic rounding: unbiased in expectation (gonzo_ML/3986,
+# "Стохастическая квантизация": its role is to remove rounding bias)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("v", [0.1, 0.25, 0.3333, 0.6, 0.75, 1.01, 1.7, 2.2, 2.5, 3.9, 4.5, 5.99,
+                               0.0, 0.5, 1.5, 4.0, 6.0])
+def test_sr_exact_expectation_over_all_random_values(v):
+    v = np.float32(v)
+    r = np.arange(1 << 16, dtype=np.uint32)
+    mags = oracle.e2m1_sr_array(np.full(r.size, v, dtype=np.float32), r)
+    vals = np.array(GRID)[mags]
+    # result is always one of the two neighbours
+    lo = max(g for g in GRID if g <= v)
+    hi = min([g for g in GRID if g > v] or [6.0])
+    assert set(np.unique(vals)) <= {lo, hi}
+    total = sum(Fraction(float(x)) for x in vals)
+    mean = total / (1 << 16)
+    fv = Fraction(float(v))
+    if fv >= 6:
+        assert mean == 6
+        return
+    # unbiased up to the 2^-16 resolution of the uniform variate
+    assert abs(mean - fv) <= Fraction(hi - lo) / (1 << 16)
+    # exact when the position between neighbours is a multiple of 2^-16
+    pos = (fv - Fraction(lo)) / Fraction(hi - lo)
+    if (pos * (1 << 16)).denominator == 1:
+        assert mean == fv
+    # a grid value never moves
+    if fv in [Fraction(g) for g in GRID]:
+        assert np.all(vals == float(v))
+
+
+def test_sr_statistical_unbiasedness_over_philox_stream():
+    # mean of SR over consecutive Philox-indexed elements of one value
+    n = 1 << 18
+    r = oracle.sr_bits_array(0x5EED, 3, 0, n)
+    for v in (0.3, 1.2, 2.7, 4.9):
+        mags = oracle.e2m1_sr_array(np.full(n, v, dtype=np.float32), r)
+        vals = np.array(GRID)[mags]
+        lo = max(g for g in GRID if g <= v)
+        hi = min(g for g in GRID if g > v)
+        p = (np.float32(v) - lo) / (hi - lo)
+        sd = (hi - lo) * math.sqrt(p * (1 - p) / n)
+        assert abs(vals.mean() - float(np.float32(v))) < 6 * sd
+
+
+def test_sr_bits_uniformity():
+    r = oracle.sr_bits_array(1, 0, 0, 1 << 18)
+    assert r.max() < (1 << 16)
+    hist = np.bincount(r >> 12, minlength=16)
+    expected = r.size / 16
+    chi2 = float(((hist - expected) ** 2 / expected).sum())
+    assert chi2 < 60  # 15 dof; p ~ 1e-7 threshold
+
+
+# ---------------------------------------------------------------------------
+# Philox4x32-10 against rocRAND's independent engine (host build)
+# ---------------------------------------------------------------------------
+def _rocrand_ref_binary():
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    hdr = "/opt/rocm/include/rocrand/rocrand_kernel.h"
+    if not (os.path.exists(hipcc) and os.path.exists(hdr)):
+        pytest.skip("rocRAND headers / hipcc not available")
+    out = os.path.join(tempfile.gettempdir(), f"rocrand_philox_ref_{os.getpid()}")
+    src = os.path.join(ROOT, "tests", "helpers", "rocrand_philox_ref.cpp")
+    subprocess.run([hipcc, "-O1", "-o", out, src], check=True, capture_output=True)
+    return out
+
+
+@pytest.mark.parametrize("seed,subseq,first", [
+    (0, 0, 0), (0x5EED, 3, 0), (0x0123456789ABCDEF, 7, 0xFFFFFFFE), (2**64 - 1, 2**40 + 5, 123456789)])
+def test_philox_matches_rocrand(seed, subseq, first):
+    exe = _rocrand_ref_binary()
+    n = 64
+    res = subprocess.run([exe, str(seed), str(subseq), str(first), str(n)], check=True,
+                         capture_output=True, text=True)
+    lines = res.stdout.strip().splitlines()
+    assert len(lines) == n
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for j, line in enumerate(lines):
+        c = first + j
+        ctr = [c & 0xFFFFFFFF, (c >> 32) & 0xFFFFFFFF, subseq & 0xFFFFFFFF, subseq >> 32]
+        want = [int(w, 16) for w in line.split()]
+        assert list(oracle.philox4x32_10(ctr, key)) == want
+
+
+def test_sr_bits_word_and_half_selection():
+    # element i uses Philox call i/8 (counter = (i>>3, offset)), word (i>>1)&3,
+    # half i&1 -- checked against the generator output directly
+    seed, off = 0xDEADBEEF12345678, 9
+    for i in [0, 1, 2, 3, 6, 7, 8, 15, 16, 12345, 2**33 + 5]:
+        blk = i >> 3
+        w = oracle.philox4x32_10([blk & 0xFFFFFFFF, blk >> 32, off, 0], [seed & 0xFFFFFFFF, seed >> 32])
+        want = (int(w[(i >> 1) & 3]) >> (16 * (i & 1))) & 0xFFFF
+        assert oracle.sr_bits(seed, off, i) == want
+
+
+# ---------------------------------------------------------------------------
+# scale formats
+# ---------------------------------------------------------------------------
+def test_scale_ranges_match_fixture():
+    for fmt, mx, mn in read_golden("scale_format_ranges.txt"):
+        vals = [oracle.scale_decode(fmt, c) for c in range(256)]
+        fin = [v for v in vals if v == v]
+        assert oracle.scale_max(fmt) == float(mx), fmt
+        assert min(v for v in fin if v > 0) == float(mn), fmt
+
+
+def test_e1m6_has_narrowest_range():
+    # gonzo_ML/3986 "Форматы FP4": of E1M6..E8M0 only E1M6 (narrowest range) diverges
+    def dyn(fmt):
+        fin = [oracle.scale_decode(fmt, c) for c in range(256)]
+        fin = [v for v in fin if v == v and v > 0]
+        return max(fin) / min(fin)
+    ranges = {f: dyn(f) for f in ALL_FMTS}
+    assert min(ranges, key=ranges.get) == "e1m6"
+
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        v = oracle.scale_decode("e4m3", c)
+        if math.isnan(t[c]):
+            assert math.isnan(v)
+        else:
+            assert v == t[c] and math.copysign(1, v) == math.copysign(1, t[c])
+
+
+def test_e5m2_decode_matches_torch_below_top_binade():
+    # torch's float8_e5m2 is IEEE-style (top exponent = Inf/NaN); below it the
+    # two agree bit for bit.
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).double().numpy()
+    for c in range(256):
+        if ((c >> 2) & 0x1F) == 0x1F:
+            continue
+        assert oracle.scale_decode("e5m2", c) == t[c]
+
+
+def test_e8m0_decode_matches_torch_float8_e8m0fnu():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    for c in range(256):
+        v = oracle.scale_decode("e8m0", c)
+        if c == 255:
+            assert math.isnan(v) and math.isnan(t[c])
+        else:
+            assert v == t[c] == 2.0 ** (c - 127)
+
+
+def test_ue5m3_unsigned_and_monotone():
+    # ue5m3-fp4-pretraining "Что сделали": no sign bit, the scale is never negative
+    vals = [oracle.scale_decode("ue5m3", c) for c in range(256)]
+    assert all(v >= 0 for v in vals if v == v)
+    assert sum(1 for v in vals if v != v) == 1
+    fin = [v for v in vals if v == v]
+    assert all(a < b for a, b in zip(fin, fin[1:]))
+
+
+@pytest.mark.parametrize("fmt", [f for f in ALL_FMTS if f != "e8m0"])
+def test_signed_formats_monotone_one_nan(fmt):
+    n = 256 if fmt == "ue5m3" else 128
+    vals = [oracle.scale_decode(fmt, c) for c in range(n)]
+    fin = [v for v in vals if v == v]
+    assert len(fin) == n - 1 and vals[-1] != vals[-1]
+    assert all(a < b for a, b in zip(fin, fin[1:]))
+
+
+def test_e4m3_encode_matches_torch_rne():
+    rng = np.random.default_rng(5)
+    u = np.concatenate([
+        rng.uniform(0, 464, 50000),
+        np.exp(rng.uniform(np.log(1e-4), np.log(464), 50000)),
+        # every midpoint between adjacent codes (ties) and their neighbours
+        *[np.array([(a + b) / 2]) for a, b in zip(
+            [oracle.scale_decode("e4m3", c) for c in range(126)],
+            [oracle.scale_decode("e4m3", c) for c in range(1, 127)])],
+    ]).astype(np.float32)
+    u = np.concatenate([u, np.nextafter(u, np.float32(0)), np.nextafter(u, np.float32(1e9))])
+    u = u[(u > 0) & (u <= 464)]
+    want = torch.from_numpy(u).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.scale_encode("e4m3", float(x)) for x in u], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", [f for f in ALL_FMTS if f != "e8m0"])
+def test_scale_encode_nearest_even_exact(fmt):
+    # exact rational nearest over the decoded code set, ties to the even code,
+    # saturation at the maximum
+    n = 256 if fmt == "ue5m3" else 128
+    table = [(c, Fraction(oracle.scale_decode(fmt, c))) for c in range(n)
+             if not oracle.scale_is_nan(fmt, c)]
+    mx = oracle.scale_max(fmt)
+    mn = min(float(v) for _, v in table if v > 0)
+    rng = np.random.default_rng(hash(fmt) & 0xFFFF)
+    u = np.exp(rng.uniform(np.log(mn / 4), np.log(mx * 2), 3000)).astype(np.float32)
+    mids = [float((a[1] + b[1]) / 2) for a, b in zip(table, table[1:])][::3]
+    u = np.concatenate([u, np.array(mids, dtype=np.float32)])
+    for x in u:
+        fx = Fraction(float(x))
+        d = [(abs(fx - v), c) for c, v in table]
+        m = min(dd for dd, _ in d)
+        cands = [c for dd, c in d if dd == m]
+        want = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        assert oracle.scale_encode(fmt, float(x)) == want, (fmt, float(x))
+
+
+def test_e8m0_block_code_closed_form():
+    # the block maximum lands in [4, 8) after scaling by 2^-(code-127)
+    rng = np.random.default_rng(8)
+    a = np.exp(rng.uniform(np.log(1e-30), np.log(1e30), 5000)).astype(np.float32)
+    for x in a:
+        c = oracle.e8m0_block_code(float(x))
+        s = 2.0 ** (c - 127)
+        assert 4 * s <= float(x) < 8 * s
+    for k in range(-120, 120, 7):
+        assert oracle.e8m0_block_code(4.0 * 2.0 ** k) == 127 + k
+        assert oracle.e8m0_block_code(np.nextafter(np.float32(8.0 * 2.0 ** k), np.float32(0))) == 127 + k
+    assert oracle.e8m0_block_code(0.0) == 0
+    assert oracle.e8m0_block_code(3.4e38) == 252     # floor(log2) = 127, minus 2, plus bias
+    assert oracle.e8m0_block_code(1e-44) == 0      # clamped: the exponent would be below -127
+
+
+def test_tensor_scale_nvfp4_recipe():
+    # NVFP4 tensor scale amax / (6 * 448): the block holding the tensor maximum
+    # then gets the largest E4M3 scale
+    for a in [1.0, 3.7, 2688.0, 1e-20, 5e30]:
+        assert oracle.tensor_scale(a, "e4m3") == np.float32(np.float32(a) / np.float32(2688.0))
+    assert oracle.tensor_scale(0.0, "e4m3") == 1.0
+    assert oracle.tensor_scale(5.0, "e8m0") == 1.0
+
+
+# ---------------------------------------------------------------------------
+# bf16 (quant_prune_distill/574, "Точность имеет значение": 1 + 1e-3 == 1)
+# ---------------------------------------------------------------------------
+def test_bf16_absorbs_small_update():
+    rows = {r[0]: r[1:] for r in read_golden("page_facts.txt")}
+    base, upd = float(rows["bf16_absorbs"][0]), float(rows["bf16_absorbs"][1])
+    x = np.float32(base) + np.float32(upd)
+    assert oracle.f32_to_bf16_bits(np.array([x]))[0] == oracle.f32_to_bf16_bits(np.array([base]))[0]
+    assert oracle.round_to_bf16(np.array([base + upd]))[0] == base
+
+
+def test_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)
+    bits = np.concatenate([bits, (bits & 0xFFFF0000) | 0x8000])     # exact ties
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.f32_to_bf16_bits(x)
+    assert np.array_equal(got, want)
+
+
+def test_round_to_bf16_matches_torch_on_f32_values():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(100000).astype(np.float32) * np.float32(1e3)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    got = oracle.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # double inputs between bf16 neighbours, including exact ties
+    assert oracle.round_to_bf16(np.array([1.0 + 2**-8]))[0] == 1.0            # tie -> even
+    assert oracle.round_to_bf16(np.array([1.0 + 3 * 2**-8]))[0] == 1.0 + 2**-6  # tie -> even
+    assert oracle.round_to_bf16(np.array([1.0 + 2**-8 + 2**-40]))[0] == 1.0 + 2**-7
+
+
+# ---------------------------------------------------------------------------
+# whole-tensor quantization invariants
+# ---------------------------------------------------------------------------
+def _sweep_like(rows, cols, seed, bf16=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)) * 0.02
+    m = rng.random((rows, cols)) < 0.01
+    x[m] *= 100
+    x = x.astype(np.float32)
+    if bf16:
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x
+
+
+def _to_f32(x):
+    return (x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x
+
+
+def test_bits_per_param_from_pages():
+    facts = [r for r in read_golden("page_facts.txt") if r[0] == "bits_per_param"]
+    assert len(facts) == 2
+    for _, name, block, fmt, bits in (f[:5] for f in facts):
+        block = int(block)
+        x = _sweep_like(32, 256, 1)
+        q, s, g, _ = oracle.quantize_tensor(x, block, fmt, "none" if fmt == "e8m0" else "current")
+        total_bits = 8 * (q.nbytes + s.nbytes)
+        assert total_bits / x.size == float(bits)
+
+
+@pytest.mark.parametrize("fmt", [f for f in ALL_FMTS if f != "e8m0"])
+def test_tensor_max_maps_to_six_and_max_scale(fmt):
+    # with a current tensor scale amax/(6*Smax) the block holding the tensor
+    # maximum takes the largest scale code and its maximum encodes to +-6
+    x = _sweep_like(64, 256, 2)
+    q, s, g, a = oracle.quantize_tensor(x, 16, fmt, "current")
+    xf = _to_f32(x)
+    r, c = np.unravel_index(np.argmax(np.abs(xf)), xf.shape)
+    n = 256 if fmt == "ue5m3" else 128
+    maxcode = max(cc for cc in range(n) if not oracle.scale_is_nan(fmt, cc))
+    assert s[r, c // 16] == maxcode
+    nib = (q[r, c // 2] >> (4 * (c & 1))) & 0xF
+    assert nib & 7 == 7 and (nib >> 3) == (xf[r, c] < 0)
+    assert a == float(np.abs(xf).max())
+
+
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("ue5m3", 16), ("e3m4", 16), ("e1m6", 16),
+                                       ("e8m0", 32), ("e4m3", 32)])
+def test_sign_symmetry_and_power_of_two_equivariance(fmt, block):
+    x = _sweep_like(16, 128, 3, bf16=False)
+    pol = "none" if fmt == "e8m0" else "current"
+    q, s, g, _ = oracle.quantize_tensor(x, block, fmt, pol)
+    qn, sn, gn, _ = oracle.quantize_tensor(-x, block, fmt, pol)
+    assert np.array_equal(s, sn) and g == gn
+    assert np.array_equal(qn, q ^ 0x88)
+    if fmt != "e8m0":
+        q2, s2, g2, _ = oracle.quantize_tensor(x * np.float32(8.0), block, fmt, pol)
+        assert np.array_equal(q2, q) and np.array_equal(s2, s) and g2 == g * 8
+    else:
+        q2, s2, _, _ = oracle.quantize_tensor(x * np.float32(8.0), block, fmt, pol)
+        assert np.array_equal(q2, q) and np.array_equal(s2.astype(int), s.astype(int) + 3)
+
+
+def test_permutation_within_block():
+    x = _sweep_like(8, 64, 4, bf16=False)
+    rng = np.random.default_rng(0)
+    perm = np.concatenate([rng.permutation(16) + 16 * b for b in range(4)])
+    q, s, g, _ = oracle.quantize_tensor(x, 16, "e4m3", "current")
+    qp, sp, gp, _ = oracle.quantize_tensor(np.ascontiguousarray(x[:, perm]), 16, "e4m3", "current")
+
+    def unpack(qq):
+        return np.stack([qq & 0xF, qq >> 4], axis=-1).reshape(qq.shape[0], -1)
+    assert np.array_equal(s, sp)
+    assert np.array_equal(unpack(q)[:, perm], unpack(qp))
+
+
+def test_e8m0_blocks_are_exact_nearest_of_x_over_scale():
+    # with a power-of-two scale x * 2^-e is exact, so each code must be the
+    # exact nearest-even E2M1 value of x / s, saturated at 6 (brute force)
+    x = _sweep_like(8, 128, 5, bf16=False)
+    q, s, _, _ = oracle.quantize_tensor(x, 32, "e8m0", "none")
+    for r in range(x.shape[0]):
+        for c in range(x.shape[1]):
+            sc = Fraction(2) ** (int(s[r, c // 32]) - 127)
+            amax_b = max(abs(Fraction(float(v))) for v in x[r, (c // 32) * 32:(c // 32 + 1) * 32])
+            assert 4 * sc <= amax_b < 8 * sc
+            v = abs(Fraction(float(x[r, c]))) / sc
+            if v >= 6:
+                want = 7
+            else:
+                d = [abs(v - Fraction(gv)) for gv in GRID]
+                m = min(d)
+                cands = [i for i in range(8) if d[i] == m]
+                want = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+            nib = (q[r, c // 2] >> (4 * (c & 1))) & 0xF
+            assert nib & 7 == want
+            assert (nib >> 3) == (np.signbit(x[r, c]))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e3m4", "e1m6"])
+def test_reconstruction_within_half_spacing(fmt):
+    # every non-saturated element is within half a grid step of x / S (up to
+    # the binary32 rounding of the reciprocal and product), and elements that
+    # differ from the exact nearest are rare and sit next to a midpoint
+    x = _sweep_like(64, 256, 6)
+    q, s, g, _ = oracle.quantize_tensor(x, 16, fmt, "current")
+    xf = _to_f32(x).astype(np.float64)
+    mags = np.stack([q & 7, (q >> 4) & 7], axis=-1).reshape(x.shape)
+    sc = np.array([oracle.scale_decode(fmt, c) for c in range(256)])[s]
+    S = (sc.astype(np.float32) * np.float32(g)).astype(np.float64)
+    S = np.repeat(S, 16, axis=1)
+    v = np.abs(xf) / np.where(S > 0, S, 1)
+    grid = np.array(GRID)
+    got = grid[mags]
+    nearest = grid[_rtn_threshold_form(v.astype(np.float32))]
+    ok = (S > 0) & (v < 6)
+    step = np.diff(np.concatenate([grid, [8.0]]))
+    lo_idx = np.clip(np.searchsorted(grid, v, side="right") - 1, 0, 7)
+    half = step[lo_idx] / 2
+    assert np.all(np.abs(got - v)[ok] <= half[ok] * (1 + 2**-20))
+    # the reciprocal-then-multiply sequence can only differ from the exact
+    # nearest of x / S where x / S sits within a few ulps of a midpoint
+    differ = ok & (got != nearest)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    dist = np.min(np.abs(v[differ][:, None] - mids[None, :]), axis=1)
+    assert np.all(dist <= v[differ] * 2.0**-21)
+    assert differ.sum() <= 1e-2 * ok.sum()
+
+
+def test_zero_tensor():
+    x = np.zeros((4, 64), dtype=np.float32)
+    q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "current")
+    assert g == 1.0 and a == 0.0 and not q.any() and not s.any()
+    xn = -x
+    q, s, g, a = oracle.quantize_tensor(xn, 16, "e4m3", "current")
+    assert np.all(q == 0x88)
+
+
+def test_delayed_refresh_schedule():
+    # ue5m3-fp4-pretraining "Что сделали": the maximum is refreshed once per
+    # 50 steps, the stored value used in between
+    facts = {r[0]: r[1:] for r in read_golden("page_facts.txt")}
+    n = int(facts["amax_refresh_interval"][0])
+    st = oracle.AmaxState(interval=n)
+    refreshed = []
+    prev = None
+    for t in range(200):
+        x = np.full((2, 32), np.float32(1.0 + t), dtype=np.float32)
+        g, a = oracle.resolve_tensor_scale(x, "e4m3", "delayed", st)
+        if a != prev:
+            refreshed.append(t)
+        prev = a
+        assert a == float(1 + (t // n) * n)
+    assert refreshed == [0, 50, 100, 150]
+    assert st.calls == 200
+
+
+def test_stale_amax_saturates():
+    # a tensor whose maximum grew 10x since the last refresh saturates at +-6
+    st = oracle.AmaxState(interval=50)
+    x0 = _sweep_like(8, 64, 7, bf16=False)
+    oracle.resolve_tensor_scale(x0, "e4m3", "delayed", st)
+    x1 = x0 * np.float32(10.0)
+    g, a = oracle.resolve_tensor_scale(x1, "e4m3", "delayed", st)
+    q, s = oracle.quantize(x1, 16, "e4m3", g)
+    assert a == oracle.amax(x0)
+    mags = np.stack([q & 7, (q >> 4) & 7], axis=-1).reshape(x1.shape)
+    big = np.abs(x1) > a * (1 + 1e-6)     # beyond the stale maximum: the block scale saturated
+    assert np.all(mags[big] == 7)
+
+
+def test_stochastic_quantize_uses_global_index_and_offset():
+    x = _sweep_like(8, 64, 8, bf16=False)
+    g = oracle.tensor_scale(oracle.amax(x), "e4m3")
+    q_all, s_all = oracle.quantize(x, 16, "e4m3", g, stochastic=True, seed=42, offset=5)
+    q_part, s_part = oracle.quantize(x, 16, "e4m3", g, stochastic=True, seed=42, offset=5, rows=(3, 6))
+    assert np.array_equal(q_all[3:6], q_part) and np.array_equal(s_all[3:6], s_part)
+    q_o, _ = oracle.quantize(x, 16, "e4m3", g, stochastic=True, seed=42, offset=6)
+    assert not np.array_equal(q_all, q_o)
+    q_r, s_r = oracle.quantize(x, 16, "e4m3", g)
+    assert np.array_equal(s_all, s_r)          # SR changes elements only
+
+
+# ---------------------------------------------------------------------------
+# dequantization and the GEMM reference
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("ue5m3", 16), ("e1m6", 16), ("e8m0", 32)])
+def test_dequantize_is_rounded_exact_product(fmt, block):
+    rng = np.random.default_rng(9)
+    q = rng.integers(0, 256, (4, block * 2), dtype=np.uint8)
+    n = 256 if fmt in ("ue5m3", "e8m0") else 128
+    s = rng.integers(0, n - 1, (4, 4), dtype=np.uint8)
+    s = np.where([[oracle.scale_is_nan(fmt, int(c)) for c in row] for row in s], 1, s).astype(np.uint8)
+    g = np.float32(0.0123) if fmt != "e8m0" else np.float32(1.0)
+    y = oracle.dequantize(q, s, float(g), block, fmt)
+    yb = oracle.dequantize(q, s, float(g), block, fmt, out="bf16")
+    for r in range(4):
+        for c in range(block * 2 * 2):
+            code = (q[r, c // 2] >> (4 * (c & 1))) & 0xF
+            exact = (Fraction(oracle.e2m1_decode(code)) * Fraction(oracle.scale_decode(fmt, int(s[r, c // block])))
+                     * Fraction(float(g)))
+            want = np.float32(float(exact)) if abs(exact) < 2**128 else np.float32(np.inf) * np.sign(float(exact))
+            assert y[r, c] == want or (np.isinf(want) and np.isinf(y[r, c]))
+            if np.isfinite(y[r, c]):
+                wb = torch.tensor(float(y[r, c]), dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+                assert yb[r, c] == wb
+
+
+def test_gemm_reference_exact_integer_case_and_orientation():
+    # E8M0 scales at 2^0 and g = 1: 2*value is an integer, so C is an exact
+    # rational computed with Python integers; M != N catches a transpose
+    rng = np.random.default_rng(10)
+    M, N, K = 5, 7, 64
+    qa = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    qb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sa = np.full((M, K // 32), 127, dtype=np.uint8)
+    sb = np.full((N, K // 32), 128, dtype=np.uint8)        # x2
+    a = oracle.dequantize_f64(qa, sa, 1.0, 32, "e8m0")
+    b = oracle.dequantize_f64(qb, sb, 1.0, 32, "e8m0")
+    c, t = oracle.gemm_ref(a, b)
+
+    def val(qq, r, k):
+        code = (qq[r, k // 2] >> (4 * (k & 1))) & 0xF
+        mag = [0, 1, 2, 3, 4, 6, 8, 12][code & 7]       # 2 * E2M1 magnitude
+        return -mag if code & 8 else mag
+    for i in range(M):
+        for j in range(N):
+            # a = val_a / 2 and b = 2 * (val_b / 2), so 2 * C = sum val_a * val_b
+            exact = sum(val(qa, i, k) * val(qb, j, k) for k in range(K))
+            assert c[i, j] * 2 == exact
+            absum = sum(abs(val(qa, i, k) * val(qb, j, k)) for k in range(K))
+            assert t[i, j] == pytest.approx(1e-5 * absum / 2, rel=1e-12)
+
+
+def test_gemm_check_bracket():
+    c_ref = np.array([1.0, 100.0, -3.3, 0.0])
+    tol = np.array([1e-5, 1e-3, 1e-5, 0.0])
+    exact = oracle.round_to_bf16(c_ref)
+    assert oracle.gemm_check(exact, c_ref, tol).all()
+    off = exact + np.array([2**-6, 1.0, 2**-5, 2**-130])      # two bf16 ulps away or more
+    assert not oracle.gemm_check(off, c_ref, tol).any()
