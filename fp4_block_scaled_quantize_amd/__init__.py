@@ -1,0 +1,219 @@
+"""Python binding of the gfx950 block-scaled FP4 library (libfp4.so).
+
+Argument marshalling only: every step of quantize, dequantize and the GEMMs
+runs in the HIP kernels behind the C ABI of include/fp4.h.  torch provides
+device memory and the current stream.  There is no fallback: if libfp4.so is
+missing or fails to load, every call raises.
+
+Names follow the C ABI: fp4_quantize, fp4_dequantize, fp4_gemm, fp4_wo_gemm,
+plus the amax state (per-tensor maximum refreshed every N calls,
+ue5m3-fp4-pretraining "Что сделали").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4.so")
+
+SCALE_FORMATS = {"e4m3": 0, "ue5m3": 1, "e3m4": 2, "e1m6": 3, "e8m0": 4, "e2m5": 5, "e5m2": 6, "e6m1": 7,
+                 "e7m0": 8}
+ROUNDING = {"nearest": 0, "stochastic": 1}
+AMAX = {"none": 0, "current": 1, "delayed": 2}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+FP4_OK = 0
+
+
+class Fp4Format(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("scale", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("amax", ctypes.c_int32)]
+
+
+class Fp4TensorC(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("fmt", Fp4Format)]
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfp4.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32
+    T = ctypes.POINTER(Fp4TensorC)
+    sig = {
+        "fp4_version": (i32, []),
+        "fp4_status_string": (ctypes.c_char_p, [i32]),
+        "fp4_amax_state_create": (i32, [u32, ctypes.POINTER(vp)]),
+        "fp4_amax_state_destroy": (i32, [vp]),
+        "fp4_amax_state_get": (i32, [vp, ctypes.POINTER(u64), ctypes.POINTER(ctypes.c_float)]),
+        "fp4_amax_state_set": (i32, [vp, u64, ctypes.c_float]),
+        "fp4_quantize": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
+        "fp4_dequantize": (i32, [T, vp, i32, i64, vp]),
+        "fp4_gemm": (i32, [T, T, vp, i64, vp]),
+        "fp4_wo_gemm": (i32, [vp, i64, i64, T, vp, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().fp4_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != FP4_OK:
+        raise Fp4Error(status, what)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ---------------------------------------------------------------------------
+@dataclass
+class QTensor:
+    """A quantized tensor: codes [rows, cols/2] (low nibble = even element),
+    scales [rows, cols/block], tensor_scale [2] = {g, amax used}."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+    rows: int
+    cols: int
+    block: int
+    scale: str
+    rounding: str = "nearest"
+    amax: str = "current"
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, block: int, scale: str, rounding: str = "nearest",
+              amax: str = "current", device="cuda"):
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        s = torch.empty((rows, cols // block), dtype=torch.uint8, device=device)
+        ts = torch.empty(2, dtype=torch.float32, device=device)
+        return cls(q, s, ts, rows, cols, block, scale, rounding, amax)
+
+    def c(self) -> Fp4TensorC:
+        fmt = Fp4Format(self.block, SCALE_FORMATS[self.scale], ROUNDING[self.rounding], AMAX[self.amax])
+        return Fp4TensorC(self.q.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
+                          self.rows, self.cols, fmt)
+
+
+class AmaxState:
+    """Per-tensor amax state: refreshed every `interval` calls (CURRENT uses
+    it too, refreshing on every call).  Owns 16 bytes of device memory."""
+
+    def __init__(self, interval: int = 50):
+        h = ctypes.c_void_p()
+        _check(lib().fp4_amax_state_create(interval, ctypes.byref(h)), "fp4_amax_state_create")
+        self._h = h
+        self.interval = interval
+
+    @property
+    def handle(self):
+        return self._h
+
+    def get(self):
+        calls, amax = ctypes.c_uint64(), ctypes.c_float()
+        _check(lib().fp4_amax_state_get(self._h, ctypes.byref(calls), ctypes.byref(amax)), "fp4_amax_state_get")
+        return calls.value, amax.value
+
+    def set(self, calls: int, amax: float):
+        _check(lib().fp4_amax_state_set(self._h, calls, amax), "fp4_amax_state_set")
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().fp4_amax_state_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
+                 amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
+                 out: QTensor | None = None, stream=None) -> QTensor:
+    """Quantize a 2-D fp32/bf16 CUDA tensor (rows may be strided: x.stride(1)
+    must be 1).  CURRENT and DELAYED need an AmaxState; one is created for
+    CURRENT if none is given."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = QTensor.empty(rows, cols, block, scale, rounding, amax, device=x.device)
+    else:
+        out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
+    if amax != "none" and state is None:
+        if amax == "delayed":
+            raise ValueError("the delayed amax policy needs an AmaxState")
+        state = AmaxState(1)
+    out._state = state        # keep the state alive while work is queued
+    tc = out.c()
+    st = lib().fp4_quantize(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tc),
+                            state.handle if state is not None else None, seed, offset, _stream(stream))
+    _check(st, "fp4_quantize")
+    return out
+
+
+def fp4_dequantize(t: QTensor, dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.q.device)
+    tc = t.c()
+    _check(lib().fp4_dequantize(ctypes.byref(tc), out.data_ptr(), DTYPE[out.dtype], out.stride(0), _stream(stream)),
+           "fp4_dequantize")
+    return out
+
+
+def fp4_gemm(a: QTensor, b: QTensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C[M, N] = A[M, K] @ W[N, K]^T in bf16 (fp32 accumulation)."""
+    if out is None:
+        out = torch.empty((a.rows, b.rows), dtype=torch.bfloat16, device=a.q.device)
+    ta, tb = a.c(), b.c()
+    _check(lib().fp4_gemm(ctypes.byref(ta), ctypes.byref(tb), out.data_ptr(), out.stride(0), _stream(stream)),
+           "fp4_gemm")
+    return out
+
+
+def fp4_wo_gemm(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] (bf16) @ W[N, K]^T with W quantized (bf16 out)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.rows), dtype=torch.bfloat16, device=x.device)
+    tw = w.c()
+    _check(lib().fp4_wo_gemm(x.data_ptr(), x.stride(0), m, ctypes.byref(tw), out.data_ptr(), out.stride(0),
+                             _stream(stream)), "fp4_wo_gemm")
+    return out
+
+
+__all__ = ["fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error",
+           "SCALE_FORMATS", "lib", "status_string", "LIB_PATH"]

@@ -1,0 +1,265 @@
+// api.cpp -- the C ABI declared in include/fp4.h: argument validation,
+// amax-policy bookkeeping on the host and kernel launches on the caller's
+// stream.  Nothing here computes on the host: every step of the quantize,
+// dequantize and GEMM paths runs in the HIP kernels.
+#include "fp4.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <new>
+#include <stdint.h>
+
+#include "fp4_internal.h"
+
+namespace fp4 {
+
+// ExMy (sign + x + y = 8 bits) and UE5M3: bias 2^(x-1)-1; the all-ones code
+// is NaN, so the largest finite code is all ones minus one.  E8M0: 2^(c-127).
+bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out)
+{
+    int e = 0, m = 0, e8 = 0;
+    switch (fmt) {
+    case FP4_SCALE_E4M3: e = 4; m = 3; break;
+    case FP4_SCALE_UE5M3: e = 5; m = 3; break;
+    case FP4_SCALE_E3M4: e = 3; m = 4; break;
+    case FP4_SCALE_E1M6: e = 1; m = 6; break;
+    case FP4_SCALE_E2M5: e = 2; m = 5; break;
+    case FP4_SCALE_E5M2: e = 5; m = 2; break;
+    case FP4_SCALE_E6M1: e = 6; m = 1; break;
+    case FP4_SCALE_E7M0: e = 7; m = 0; break;
+    case FP4_SCALE_E8M0: e8 = 1; break;
+    default: return false;
+    }
+    ScaleFmtHost f{};
+    f.is_e8m0 = e8;
+    if (e8) {
+        f.ebits = 8; f.mbits = 0; f.bias = 127; f.maxcode = 254;
+        f.smax = ldexpf(1.0f, 127);
+    } else {
+        f.ebits = e; f.mbits = m;
+        f.bias = (1 << (e - 1)) - 1;
+        f.maxcode = (1 << (e + m)) - 2;
+        const int ecode = f.maxcode >> m, mcode = f.maxcode & ((1 << m) - 1);
+        f.smax = ldexpf((float)(mcode | (1 << m)), ecode - f.bias - m);
+    }
+    *out = f;
+    return true;
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+struct fp4_amax_state {
+    uint32_t interval;
+    uint64_t calls;
+    int device;
+    AmaxDev* dev;
+};
+
+extern "C" {
+
+int32_t fp4_version(void) { return 100; }
+
+const char* fp4_status_string(fp4_status st)
+{
+    switch (st) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_INVALID_ARG: return "invalid argument";
+    case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP4_ERR_SHAPE: return "shape mismatch";
+    case FP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case FP4_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+fp4_status fp4_amax_state_create(uint32_t interval, fp4_amax_state** out)
+{
+    if (!out || interval == 0) return FP4_ERR_INVALID_ARG;
+    fp4_amax_state* st = new (std::nothrow) fp4_amax_state;
+    if (!st) return FP4_ERR_INVALID_ARG;
+    st->interval = interval;
+    st->calls = 0;
+    if (hipGetDevice(&st->device) != hipSuccess) { delete st; return FP4_ERR_HIP; }
+    if (hipMalloc((void**)&st->dev, sizeof(AmaxDev)) != hipSuccess) { delete st; return FP4_ERR_HIP; }
+    AmaxDev zero{0.0f, 0u, 0u, 0u};
+    if (hipMemcpy(st->dev, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(st->dev);
+        delete st;
+        return FP4_ERR_HIP;
+    }
+    *out = st;
+    return FP4_OK;
+}
+
+fp4_status fp4_amax_state_destroy(fp4_amax_state* st)
+{
+    if (!st) return FP4_ERR_INVALID_ARG;
+    hipError_t e = hipFree(st->dev);
+    delete st;
+    return e == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status fp4_amax_state_get(const fp4_amax_state* st, uint64_t* calls, float* amax)
+{
+    if (!st || !calls || !amax) return FP4_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return FP4_ERR_HIP;
+    AmaxDev h;
+    if (hipMemcpy(&h, st->dev, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return FP4_ERR_HIP;
+    *calls = st->calls;
+    *amax = h.amax;
+    return FP4_OK;
+}
+
+fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
+{
+    if (!st || !(amax >= 0.0f) || !isfinite(amax)) return FP4_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return FP4_ERR_HIP;
+    AmaxDev h{amax, 0u, 0u, 0u};
+    if (hipMemcpy(st->dev, &h, sizeof(h), hipMemcpyHostToDevice) != hipSuccess) return FP4_ERR_HIP;
+    st->calls = calls;
+    return FP4_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
+{
+    if (!t || !t->tensor_scale) return FP4_ERR_INVALID_ARG;
+    const bool empty = t->rows == 0 || t->cols == 0;
+    if (!empty && (!t->q || !t->scales)) return FP4_ERR_INVALID_ARG;
+    if (t->fmt.block != 16 && t->fmt.block != 32) return FP4_ERR_INVALID_ARG;
+    if (t->fmt.rounding != FP4_ROUND_NEAREST_EVEN && t->fmt.rounding != FP4_ROUND_STOCHASTIC)
+        return FP4_ERR_INVALID_ARG;
+    if (t->fmt.amax != FP4_AMAX_NONE && t->fmt.amax != FP4_AMAX_CURRENT && t->fmt.amax != FP4_AMAX_DELAYED)
+        return FP4_ERR_INVALID_ARG;
+    if (!scale_fmt_params(t->fmt.scale, f)) return FP4_ERR_INVALID_ARG;
+    if (t->rows < 0 || t->cols < 0) return FP4_ERR_SHAPE;
+    if (t->cols % t->fmt.block) return FP4_ERR_SHAPE;
+    if (((uintptr_t)t->q & 3u) != 0) return FP4_ERR_ALIGN;
+    if ((t->rows * (t->cols / 8)) >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
+static fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out, fp4_amax_state* state,
+                        uint64_t seed, uint64_t offset, void* stream)
+{
+    ScaleFmtHost f;
+    fp4_status st = check_tensor(out, &f);
+    if (st != FP4_OK) return st;
+    if (!x && out->rows * out->cols != 0) return FP4_ERR_INVALID_ARG;
+    if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
+    const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
+    if (ld_x < out->cols) return FP4_ERR_SHAPE;
+    if (!aligned16(x) || (ld_x * esz) % 16) return FP4_ERR_ALIGN;
+    const int32_t pol = out->fmt.amax;
+    if (f.is_e8m0 && pol != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
+    if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    const AmaxDev* src = nullptr;
+    if (pol != FP4_AMAX_NONE) {
+        const bool refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
+        if (refresh) {
+            st = hip_status(launch_amax(x, x_dtype == FP4_DTYPE_BF16, out->rows, out->cols, ld_x, state->dev, s));
+            if (st != FP4_OK) return st;
+        }
+        src = state->dev;
+    }
+    QuantLaunch p;
+    p.x = x;
+    p.x_bf16 = x_dtype == FP4_DTYPE_BF16;
+    p.rows = out->rows;
+    p.cols = out->cols;
+    p.ld = ld_x;
+    p.q = out->q;
+    p.scales = out->scales;
+    p.tensor_scale = out->tensor_scale;
+    p.amax_src = src;
+    p.block = out->fmt.block;
+    p.stochastic = out->fmt.rounding == FP4_ROUND_STOCHASTIC;
+    p.seed = seed;
+    p.offset = offset;
+    p.fmt = f;
+    st = hip_status(launch_quantize(p, s));
+    if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
+    return st;
+}
+
+fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream)
+{
+    ScaleFmtHost f;
+    fp4_status st = check_tensor(in, &f);
+    if (st != FP4_OK) return st;
+    if (y_dtype != FP4_DTYPE_F32 && y_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
+    if (in->rows * in->cols == 0) return FP4_OK;
+    if (!y) return FP4_ERR_INVALID_ARG;
+    const int64_t esz = y_dtype == FP4_DTYPE_BF16 ? 2 : 4;
+    if (ld_y < in->cols) return FP4_ERR_SHAPE;
+    if (!aligned16(y) || (ld_y * esz) % 16) return FP4_ERR_ALIGN;
+    DequantLaunch p;
+    p.q = in->q;
+    p.scales = in->scales;
+    p.tensor_scale = in->tensor_scale;
+    p.rows = in->rows;
+    p.cols = in->cols;
+    p.block = in->fmt.block;
+    p.fmt = f;
+    p.y = y;
+    p.y_bf16 = y_dtype == FP4_DTYPE_BF16;
+    p.ld = ld_y;
+    return hip_status(launch_dequantize(p, (hipStream_t)stream));
+}
+
+fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64_t ldc, void* stream)
+{
+    ScaleFmtHost fa, fb;
+    fp4_status st = check_tensor(a, &fa);
+    if (st != FP4_OK) return st;
+    st = check_tensor(b, &fb);
+    if (st != FP4_OK) return st;
+    if (!c) return FP4_ERR_INVALID_ARG;
+    if (a->cols != b->cols) return FP4_ERR_SHAPE;
+    if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
+    if (a->cols % 128) return FP4_ERR_SHAPE;
+    if (ldc < b->rows) return FP4_ERR_SHAPE;
+    if (!aligned16(c) || ldc % 8) return FP4_ERR_ALIGN;
+    if (a->rows == 0 || b->rows == 0) return FP4_OK;
+    GemmLaunch p;
+    p.qa = a->q; p.sa = a->scales; p.ga = a->tensor_scale;
+    p.qb = b->q; p.sb = b->scales; p.gb = b->tensor_scale;
+    p.m = a->rows; p.n = b->rows; p.k = a->cols;
+    p.block = a->fmt.block;
+    p.fa = fa; p.fb = fb;
+    p.c = c; p.ldc = ldc;
+    hipStream_t s = (hipStream_t)stream;
+    if (fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
+    return hip_status(launch_gemm_dq(p, s));
+}
+
+fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y, int64_t ldy,
+                       void* stream)
+{
+    ScaleFmtHost fw;
+    fp4_status st = check_tensor(w, &fw);
+    if (st != FP4_OK) return st;
+    if (!x || !y) return FP4_ERR_INVALID_ARG;
+    if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
+    if (w->cols % 256) return FP4_ERR_SHAPE;
+    if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
+    if (!aligned16(x) || ldx % 8) return FP4_ERR_ALIGN;
+    if (w->rows == 0) return FP4_OK;
+    WoGemmLaunch p;
+    p.x = x; p.ldx = ldx; p.m = m;
+    p.qw = w->q; p.sw = w->scales; p.gw = w->tensor_scale;
+    p.n = w->rows; p.k = w->cols;
+    p.block = w->fmt.block;
+    p.fw = fw;
+    p.y = y; p.ldy = ldy;
+    return hip_status(launch_wo_gemm(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

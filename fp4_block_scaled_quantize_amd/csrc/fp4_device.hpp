@@ -1,0 +1,182 @@
+// fp4_device.hpp -- device-side building blocks for the gfx950 kernels:
+// bf16 unpacking, block-scale encode/decode, E2M1 element encode/decode,
+// wave64 group reductions and the Philox4x32-10 counter-based generator.
+//
+// Formats (quant_prune_distill/486 "Метод"; gonzo_ML/3986 "Форматы FP4";
+// ue5m3-fp4-pretraining "Что сделали"): E2M1 elements; block scales in an
+// ExMy encoding (bias 2^(x-1)-1, subnormals, no infinity, the all-ones code
+// is NaN) or E8M0 (2^(code-127)).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bits_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f_bits(float f) { return __float_as_uint(f); }
+
+// bf16 pair packed in a dword -> two fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// block-scale formats
+// ---------------------------------------------------------------------------
+struct ScaleFmt {
+    int32_t ebits, mbits, bias, maxcode;   // ExMy parameters (unused for E8M0)
+    float smax;                            // largest finite value
+    int32_t is_e8m0;
+};
+
+// Nearest-even, saturating ExMy encode of u >= 0.  In the binade of u (or
+// the subnormal range), t = u * 2^(mbits - e) is exact and its integer part
+// indexes the code directly: code = ((e + bias - 1) << mbits) + floor(t),
+// rounded up past the midpoint and, on an exact midpoint, to the even code.
+__device__ __forceinline__ uint32_t scale_encode_exmy(float u, const ScaleFmt& f)
+{
+    if (!(u < f.smax)) return (u >= f.smax) ? (uint32_t)f.maxcode : 0u;
+    uint32_t ub = f_bits(u);
+    int eu = (int)((ub >> 23) & 0xFFu) - 127;          // floor(log2 u) for normal u
+    int emin = 1 - f.bias;
+    int e = eu > emin ? eu : emin;                      // fp32 subnormals fall below emin
+    float t = __builtin_amdgcn_ldexpf(u, f.mbits - e);
+    float fl = __builtin_floorf(t);
+    float fr = t - fl;
+    uint32_t lo = ((uint32_t)(e + f.bias - 1) << f.mbits) + (uint32_t)fl;
+    uint32_t up = (fr > 0.5f) | ((fr == 0.5f) & (lo & 1u));
+    uint32_t code = lo + up;
+    return code < (uint32_t)f.maxcode ? code : (uint32_t)f.maxcode;
+}
+
+__device__ __forceinline__ float scale_decode_exmy(uint32_t code, const ScaleFmt& f)
+{
+    uint32_t e = code >> f.mbits;
+    uint32_t m = code & ((1u << f.mbits) - 1u);
+    float sig = (float)(e == 0 ? m : (m | (1u << f.mbits)));
+    int ex = (e == 0 ? 1 : (int)e) - f.bias - f.mbits;
+    return __builtin_amdgcn_ldexpf(sig, ex);
+}
+
+// Decode any scale byte: sign bit above ebits+mbits for signed formats, the
+// all-ones magnitude is NaN; E8M0: 2^(code-127), 0xFF is NaN.
+__device__ __forceinline__ float scale_decode_any(uint32_t code, const ScaleFmt& f)
+{
+    if (f.is_e8m0) {
+        if (code == 0xFFu) return __uint_as_float(0x7FC00000u);
+        return bits_f(code ? code << 23 : 0x00400000u);
+    }
+    const int nb = f.ebits + f.mbits;
+    const uint32_t magmask = (1u << nb) - 1u;
+    const uint32_t mag = code & magmask;
+    if (mag == magmask) return __uint_as_float(0x7FC00000u);
+    float v = scale_decode_exmy(mag, f);
+    return (nb == 7 && (code & 0x80u)) ? -v : v;
+}
+
+// E8M0 block code: floor(log2 amax_b) - 2 + 127, clamped to [0, 254]; for a
+// normal amax_b this is its biased exponent minus 2.
+__device__ __forceinline__ uint32_t scale_code_e8m0(float amax_b)
+{
+    int ex = (int)((f_bits(amax_b) >> 23) & 0xFFu);
+    return (uint32_t)(ex > 2 ? ex - 2 : 0);
+}
+
+// 2^(127 - code): exact reciprocal of an E8M0 scale, code in [0, 252].
+__device__ __forceinline__ float e8m0_inv(uint32_t code) { return bits_f((254u - code) << 23); }
+
+// ---------------------------------------------------------------------------
+// E2M1 elements
+// ---------------------------------------------------------------------------
+// Hardware pack: two fp32 -> two E2M1 codes (round to nearest even,
+// saturating, sign kept) into byte `sel` of `old`, scale 1.
+#define FP4_CVT_PK(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// Software E2M1 nearest-even magnitude code of |v| (saturating at 6): in each
+// binade of the grid the spacing is a power of two, so a scaled rint with an
+// offset gives the code: [0,2) step 0.5, [2,4) step 1, [4,8) step 2.
+__device__ __forceinline__ uint32_t e2m1_rtn_sw(float v)
+{
+    float a = __builtin_fabsf(v);
+    float sp = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    float off = a < 2.0f ? 0.0f : (a < 4.0f ? 2.0f : 4.0f);
+    float c = __builtin_fminf(__builtin_rintf(a * sp) + off, 7.0f);
+    return (uint32_t)c | ((f_bits(v) >> 28) & 8u);
+}
+
+// Stochastic E2M1 code of v with 16 random bits r16: the lower grid
+// neighbour lo and the position frac in [0,1) to the upper one are exact;
+// the magnitude rounds up iff r16 < frac * 2^16.
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r16)
+{
+    float a = __builtin_fabsf(v);
+    float sp = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+    float off = a < 2.0f ? 0.0f : (a < 4.0f ? 2.0f : 4.0f);
+    float t = a * sp;                       // exact: power-of-two scaling
+    float fl = __builtin_floorf(t);
+    float frac = t - fl;                    // exact
+    float up = ((float)r16 < frac * 65536.0f) ? 1.0f : 0.0f;
+    float c = a >= 6.0f ? 7.0f : fl + off + up;
+    return (uint32_t)c | ((f_bits(v) >> 28) & 8u);
+}
+
+// E2M1 magnitude code -> value (exact): code 0..7 -> 0,.5,1,1.5,2,3,4,6.
+__device__ __forceinline__ float e2m1_value(uint32_t nib)
+{
+    uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+    // normal: (1 + m/2) * 2^(e-1) = bits (e + 126) << 23 | m << 22 ; subnormal: m * 0.5
+    float mag = e ? bits_f(((e + 126u) << 23) | (m << 22)) : (m ? 0.5f : 0.0f);
+    return (nib & 8u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 helpers
+// ---------------------------------------------------------------------------
+// Max across lane pairs / quads with DPP quad permutations.
+__device__ __forceinline__ float dpp_max_xor1(float v)
+{
+    int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    return __builtin_fmaxf(v, __int_as_float(o));
+}
+__device__ __forceinline__ float dpp_max_xor2(float v)
+{
+    int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    return __builtin_fmaxf(v, __int_as_float(o));
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds, multipliers
+// 0xD2511F53 / 0xCD9E8D57, Weyl key increments 0x9E3779B9 / 0xBB67AE85.
+// ---------------------------------------------------------------------------
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
+        uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
+        U4 n;
+        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        n.y = (uint32_t)p1;
+        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.w = (uint32_t)p0;
+        c = n;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+}  // namespace fp4

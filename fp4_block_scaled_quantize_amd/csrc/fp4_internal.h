@@ -1,0 +1,82 @@
+// fp4_internal.h -- host-side launcher interface between the C ABI (api.cpp)
+// and the kernel translation units.  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+struct ScaleFmtHost {
+    int32_t ebits, mbits, bias, maxcode;
+    float smax;
+    int32_t is_e8m0;
+};
+
+// Fill the parameters of a block-scale format (fp4_scale_fmt value).
+bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
+
+// Device workspace of an amax state: stored amax, reduction slot, counter.
+struct AmaxDev {
+    float amax;
+    uint32_t slot;
+    uint32_t count;
+    uint32_t pad;
+};
+
+struct QuantLaunch {
+    const void* x;
+    int32_t x_bf16;
+    int64_t rows, cols, ld;
+    uint8_t* q;
+    uint8_t* scales;
+    float* tensor_scale;       // out: {g, amax}
+    const AmaxDev* amax_src;   // null: no tensor scale (g = 1)
+    int32_t block;
+    int32_t stochastic;
+    uint64_t seed, offset;
+    ScaleFmtHost fmt;
+};
+
+struct DequantLaunch {
+    const uint8_t* q;
+    const uint8_t* scales;
+    const float* tensor_scale;
+    int64_t rows, cols;
+    int32_t block;
+    ScaleFmtHost fmt;
+    void* y;
+    int32_t y_bf16;
+    int64_t ld;
+};
+
+hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols, int64_t ld, AmaxDev* dst,
+                       hipStream_t s);
+hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);
+hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s);
+
+struct GemmLaunch {
+    const uint8_t* qa; const uint8_t* sa; const float* ga;   // A [M, K]
+    const uint8_t* qb; const uint8_t* sb; const float* gb;   // W [N, K]
+    int64_t m, n, k;
+    int32_t block;
+    ScaleFmtHost fa, fb;
+    uint16_t* c;
+    int64_t ldc;
+};
+
+hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s);
+hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
+
+struct WoGemmLaunch {
+    const uint16_t* x; int64_t ldx; int64_t m;
+    const uint8_t* qw; const uint8_t* sw; const float* gw;
+    int64_t n, k;
+    int32_t block;
+    ScaleFmtHost fw;
+    uint16_t* y; int64_t ldy;
+};
+
+hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s);
+
+}  // namespace fp4

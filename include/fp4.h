@@ -1,0 +1,205 @@
+/*
+ * fp4.h -- C ABI of the MI355X (gfx950) block-scaled FP4 library.
+ *
+ * The method (page citations; the pages print no formula, the reading taken
+ * where they are silent is stated at each call):
+ *   quant_prune_distill/486 "Метод": NVFP4 = E2M1 elements in groups of 16
+ *     with an E4M3 scale (4.5 bit/param); MXFP = groups of 32 with an E8M0
+ *     (power-of-two) scale (4.25 bit/param); small groups need efficient
+ *     kernels for the scale handling.
+ *   gonzo_ML/3986 "Форматы FP4": group 16; scale encodings swept from E1M6
+ *     to E8M0.  "Стохастическая квантизация": round to nearest, or up/down
+ *     with probability set by the distance; nearest for forward weights and
+ *     activations, stochastic for backward gradients.
+ *   ue5m3-fp4-pretraining "Что сделали": unsigned UE5M3 block scales; the
+ *     tensor maximum is refreshed every 50 steps, stored in between; all
+ *     suitable linear layers run in FP4.
+ *   quant_prune_distill/574 "Эксперименты": weight-only NVFP4 with a
+ *     memory-bound small-batch kernel for rollouts.
+ *
+ * Conventions for every call:
+ *   - Data pointers are DEVICE pointers owned by the caller (e.g. torch
+ *     tensors).  The library never allocates or frees caller memory and
+ *     allocates nothing per call; an fp4_amax_state owns 16 bytes of device
+ *     memory allocated at creation.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every launch is asynchronous on it; no call synchronizes the host
+ *     except fp4_amax_state_get / fp4_amax_state_set.
+ *   - Arguments are validated before any launch.  A negative status means
+ *     nothing was launched and nothing was written.  FP4_ERR_HIP means a
+ *     launch was attempted and the runtime reported an error.
+ *   - No exceptions cross the ABI.
+ *   - Element codes: row-major [rows, cols/2] bytes, the even-index element
+ *     in the low nibble; nibble = sign << 3 | E2M1 magnitude code.  Scales:
+ *     row-major [rows, cols/block] bytes.  (Reading: the pages fix the
+ *     storage cost, not the layout.)
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FP4_API __attribute__((visibility("default")))
+#else
+#define FP4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp4_status {
+    FP4_OK = 0,
+    FP4_ERR_INVALID_ARG = -1, /* null pointer, bad enum, bad block size     */
+    FP4_ERR_UNSUPPORTED = -2, /* valid but unsupported combination          */
+    FP4_ERR_SHAPE = -3,       /* cols % block != 0, K mismatch, ld < cols   */
+    FP4_ERR_ALIGN = -4,       /* pointer or leading dimension misaligned    */
+    FP4_ERR_HIP = -5          /* the HIP runtime reported an error          */
+} fp4_status;
+
+/* Block-scale encodings.  ExMy (sign + x exponent + y mantissa bits, x+y=7)
+ * and UE5M3 (no sign bit): bias 2^(x-1)-1, exponent field 0 is subnormal,
+ * no infinity, the code with every exponent and mantissa bit set is NaN
+ * (reading; the pages name the formats only).  E8M0: value 2^(code-127). */
+typedef enum fp4_scale_fmt {
+    FP4_SCALE_E4M3 = 0,
+    FP4_SCALE_UE5M3 = 1,
+    FP4_SCALE_E3M4 = 2,
+    FP4_SCALE_E1M6 = 3,
+    FP4_SCALE_E8M0 = 4,
+    FP4_SCALE_E2M5 = 5,
+    FP4_SCALE_E5M2 = 6,
+    FP4_SCALE_E6M1 = 7,
+    FP4_SCALE_E7M0 = 8
+} fp4_scale_fmt;
+
+typedef enum fp4_rounding {
+    FP4_ROUND_NEAREST_EVEN = 0, /* ties to the even code, saturate at 6      */
+    FP4_ROUND_STOCHASTIC = 1    /* Philox4x32-10, 16 random bits per element */
+} fp4_rounding;
+
+typedef enum fp4_amax_policy {
+    FP4_AMAX_NONE = 0,    /* no tensor scale (g = 1); required for E8M0      */
+    FP4_AMAX_CURRENT = 1, /* g from max|x| of this call's tensor             */
+    FP4_AMAX_DELAYED = 2  /* g from the stored max, refreshed every interval */
+} fp4_amax_policy;
+
+typedef enum fp4_dtype { FP4_DTYPE_F32 = 0, FP4_DTYPE_BF16 = 1 } fp4_dtype;
+
+typedef struct fp4_format {
+    int32_t block;    /* 16 or 32 elements per scale                        */
+    int32_t scale;    /* fp4_scale_fmt                                      */
+    int32_t rounding; /* fp4_rounding                                       */
+    int32_t amax;     /* fp4_amax_policy                                    */
+} fp4_format;
+
+/* A quantized tensor.  q: rows*cols/2 bytes; scales: rows*cols/block bytes;
+ * tensor_scale: 2 floats {g, amax used} (g = 1 and amax = 0 under NONE).
+ * All three are device pointers; q must be 4-byte aligned. */
+typedef struct fp4_tensor {
+    uint8_t* q;
+    uint8_t* scales;
+    float* tensor_scale;
+    int64_t rows;
+    int64_t cols;
+    fp4_format fmt;
+} fp4_tensor;
+
+/* Per-tensor amax state (ue5m3-fp4-pretraining "Что сделали": the maximum
+ * is refreshed every `interval` steps and the stored value used between).
+ * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 16
+ * bytes of device memory on the device current at creation: the stored
+ * amax and the reduction's workspace.  Not thread-safe; calls that use one
+ * state must be ordered (one stream, or synchronized). */
+typedef struct fp4_amax_state fp4_amax_state;
+
+/* interval >= 1.  Allocates the device workspace (zeroed, synchronously). */
+FP4_API fp4_status fp4_amax_state_create(uint32_t interval, fp4_amax_state** out);
+FP4_API fp4_status fp4_amax_state_destroy(fp4_amax_state* state);
+/* Checkpoint: number of quantize calls seen and the stored amax.  Waits for
+ * the device to finish outstanding work. */
+FP4_API fp4_status fp4_amax_state_get(const fp4_amax_state* state, uint64_t* calls, float* amax);
+/* Resume: overwrite the call count and stored amax (synchronous copy). */
+FP4_API fp4_status fp4_amax_state_set(fp4_amax_state* state, uint64_t calls, float amax);
+
+/*
+ * fp4_quantize -- quantize x[rows, cols] (row stride ld_x elements, f32 or
+ * bf16) into out->q / out->scales / out->tensor_scale with out->fmt.
+ *
+ * Per block of B elements (reading of the pages' "shared scale per small
+ * group"; every step binary32 round-to-nearest-even):
+ *   ExMy: g = amax_t / (6 * Smax) (g = 1 under NONE, or if the quotient is
+ *         0 or not finite); u = RN(amax_b / RN(6 g)); code = nearest-even
+ *         saturating ExMy encode of u; s = decode(code).
+ *   E8M0: code = clamp(floor(log2 amax_b) - 2 + 127, 0, 254) (0 for an
+ *         all-zero block); s = 2^(code-127); g = 1.
+ *   S = RN(s g); inv = RN(1/S) clamped to FLT_MAX (inv = 0 when S = 0);
+ *   v = RN(x inv); magnitude = nearest-even E2M1 code of |v| saturated at 6,
+ *   or, for FP4_ROUND_STOCHASTIC, lo + [r16 / 2^16 < (|v|-lo)/(hi-lo)] with
+ *   r16 the 16-bit half (i & 1) of word (i >> 1) & 3 of
+ *   Philox4x32-10(key = seed, counter = {i >> 3 as 64 bits, offset as 64
+ *   bits}), i = row * cols + col the logical element index.
+ *
+ * x: device, 16-byte aligned; ld_x * sizeof(elem) a multiple of 16; ld_x >=
+ * cols.  cols % block == 0; block in {16, 32}; rows * cols / 8 < 2^31.  For an
+ * empty tensor (rows or cols 0) x, q and scales may be null; tensor_scale
+ * is still written ({1, 0} under CURRENT).
+ * state: required for CURRENT and DELAYED (ignored for NONE).  CURRENT
+ * recomputes amax_t on every call; DELAYED recomputes it when
+ * state->calls % interval == 0 and otherwise reuses the stored value (a
+ * tensor that outgrew it saturates at +-6).  Each call increments the
+ * state's call count on the host (no device synchronization).
+ * seed, offset: used only for FP4_ROUND_STOCHASTIC.
+ * Errors: INVALID_ARG (null pointers, bad enums, missing state), SHAPE,
+ * ALIGN, UNSUPPORTED (E8M0 with a tensor-scale policy).
+ */
+FP4_API fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
+                        fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
+
+/*
+ * fp4_dequantize -- y[rows, cols] (row stride ld_y, f32 or bf16) =
+ * RN(RN(e2m1(code) * s) * g), rounded once more to bf16 (RNE) for bf16
+ * output (quant_prune_distill/486 "Метод": the element times its group's
+ * scale).  in->tensor_scale[0] is read on the device.  y: 16-byte aligned,
+ * ld_y * sizeof(elem) a multiple of 16.
+ */
+FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream);
+
+/*
+ * fp4_gemm -- C[M, N] (bf16, row stride ldc) = bf16_RNE(ga * gb *
+ * sum_k (e2m1(a_mk) s_a)(e2m1(b_nk) s_b)) with fp32 accumulation, for
+ * A = a [M, K] and W = b [N, K] both blocked along K (C = A W^T)
+ * (ue5m3-fp4-pretraining "Что сделали": the linear layers run in FP4;
+ * quant_prune_distill/574 "Выводы": weight + activation FP4 for the
+ * compute-bound regime).  Both operands must use the same block size.
+ * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
+ * instruction; every other format is dequantized exactly to bf16/f16 in
+ * LDS and runs on the bf16/f16 matrix cores.  Result within
+ * 1e-5 * sum_k |a||b| of the exact product before the bf16 rounding.
+ * K % 128 == 0, M and N arbitrary; ldc >= N, ldc % 8 == 0, c 16-byte aligned.
+ */
+FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64_t ldc, void* stream);
+
+/*
+ * fp4_wo_gemm -- Y[M, N] (bf16, row stride ldy) = bf16_RNE(gw *
+ * sum_k x[m, k] (e2m1(w_nk) s_w)), fp32 accumulation, weights dequantized
+ * in registers (quant_prune_distill/574 "Метод"/"Эксперименты":
+ * weight-only NVFP4, memory-bound small-batch generation).
+ * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
+ * 1 <= M <= 16; K % 256 == 0; ldx % 8 == 0, ldy >= N.
+ */
+FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
+                       int64_t ldy, void* stream);
+
+/* Static description of a status code. */
+FP4_API const char* fp4_status_string(fp4_status status);
+
+/* Library ABI version (major * 100 + minor). */
+FP4_API int32_t fp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/fp4.h declares, and rejects invalid arguments before
+touching the device (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+import fp4_block_scaled_quantize_amd as fq
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "fp4.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fq.lib()
+    names = _declared_functions()
+    assert {"fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_wo_gemm"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert fq.lib().fp4_version() >= 100
+    assert fq.status_string(0) == "ok"
+    for st in (-1, -2, -3, -4, -5):
+        assert fq.status_string(st) not in ("ok", "unknown status")
+
+
+FAKE = 0x10000      # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _tensor(block=16, scale=0, rounding=0, amax=1, rows=4, cols=64, q=FAKE, s=FAKE, ts=FAKE):
+    return fq.Fp4TensorC(q, s, ts, rows, cols, fq.Fp4Format(block, scale, rounding, amax))
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(block=8), -1),                 # block size not 16/32
+    (dict(scale=42), -1),                # unknown scale format
+    (dict(rounding=7), -1),
+    (dict(amax=9), -1),
+    (dict(q=0), -1),                     # null codes
+    (dict(cols=72), -3),                 # cols % block
+    (dict(q=FAKE + 2), -4),              # codes misaligned
+    (dict(scale=4, block=32), -2),       # E8M0 with a tensor-scale policy
+])
+def test_quantize_rejects_before_launch(kw, want):
+    t = _tensor(**kw)
+    st = fq.lib().fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None)
+    assert st == want
+
+
+def test_quantize_requires_state_for_tensor_scale():
+    t = _tensor(amax=2)
+    assert fq.lib().fp4_quantize(FAKE, 1, 64, ctypes.byref(t), None, 0, 0, None) == -1
+
+
+def test_quantize_input_checks():
+    t = _tensor()
+    L = fq.lib()
+    assert L.fp4_quantize(None, 1, 64, ctypes.byref(t), FAKE, 0, 0, None) == -1
+    assert L.fp4_quantize(FAKE, 5, 64, ctypes.byref(t), FAKE, 0, 0, None) == -1
+    assert L.fp4_quantize(FAKE, 1, 32, ctypes.byref(t), FAKE, 0, 0, None) == -3      # ld < cols
+    assert L.fp4_quantize(FAKE + 8, 1, 64, ctypes.byref(t), FAKE, 0, 0, None) == -4  # x misaligned
+    assert L.fp4_quantize(FAKE, 1, 68, ctypes.byref(t), FAKE, 0, 0, None) == -4      # ld*2 % 16
+
+
+def test_gemm_and_wo_gemm_shape_checks():
+    L = fq.lib()
+    a = _tensor(rows=8, cols=256)
+    b = _tensor(rows=8, cols=512)
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -3        # K mismatch
+    b32 = _tensor(rows=8, cols=256, block=32)
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b32), FAKE, 8, None) == -2      # block mismatch
+    a96 = _tensor(rows=8, cols=96)
+    assert L.fp4_gemm(ctypes.byref(a96), ctypes.byref(a96), FAKE, 8, None) == -3    # K % 128
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(a), FAKE, 4, None) == -3        # ldc < N
+    w = _tensor(rows=8, cols=256)
+    assert L.fp4_wo_gemm(FAKE, 256, 0, ctypes.byref(w), FAKE, 8, None) == -2        # M = 0
+    assert L.fp4_wo_gemm(FAKE, 256, 17, ctypes.byref(w), FAKE, 8, None) == -2       # M > 16
+    w2 = _tensor(rows=8, cols=128)
+    assert L.fp4_wo_gemm(FAKE, 128, 1, ctypes.byref(w2), FAKE, 8, None) == -3       # K % 256
+
+
+def test_amax_state_argument_checks():
+    L = fq.lib()
+    h = ctypes.c_void_p()
+    assert L.fp4_amax_state_create(0, ctypes.byref(h)) == -1
+    assert L.fp4_amax_state_create(50, None) == -1
+    assert L.fp4_amax_state_destroy(None) == -1
