@@ -1,0 +1,310 @@
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+Headline (one JSON line on stdout): quantize throughput in GB/s of
+algorithmic bytes over the scale-format sweep workload -- a 4096x4096 bf16
+tensor (N(0, 0.02), 0.1% of entries x100) quantized with E4M3, UE5M3, E3M4
+and E1M6 block-16 scales (current amax) and E8M0 block-32 scales (MXFP4),
+round-to-nearest.  One step = those five quantize calls.  Inputs rotate
+over 24 resident copies (768 MiB, three times the 256 MB last-level cache)
+so the rate is an HBM rate; each rotation slot is a captured HIP graph so
+the host launch rate does not limit the GPU.
+
+Algorithmic bytes per call: input read once (2 B/elem), codes (0.5 B/elem),
+scales (1/B B/elem), the tensor scale (8 B), plus one more input read for
+the current-amax pass.
+
+Further legs reported in "legs": stochastic rounding with delayed amax over
+200 successive 8192x8192 gradients, dequantize, the block-scaled GEMM on the
+Llama-2 7B linear shapes, and the weight-only GEMM at Qwen-2.5 decode
+shapes.  "roofline" is the dominant kernel (the E4M3 block-16 quantize
+kernel) timed alone with HIP events on its stream; "cpu_baseline" is the
+CPU oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+
+SWEEP = [("e4m3", 16, "current"), ("ue5m3", 16, "current"), ("e3m4", 16, "current"), ("e1m6", 16, "current"),
+         ("e8m0", 32, "none")]
+
+
+def quant_bytes(rows, cols, block, with_amax, in_bytes=2):
+    n = rows * cols
+    b = n * in_bytes + n // 2 + n // block + 8
+    if with_amax:
+        b += n * in_bytes
+    return b
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
+    p.add_argument("--legs", default="sr,dequant,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class GraphSet:
+    """One captured HIP graph per rotation slot; replay(i) runs slot i."""
+
+    def __init__(self, torch, n, record):
+        self.graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(n):          # eager warm-up of every slot (allocations, module load)
+                record(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                record(i)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, i):
+        self.graphs[i % len(self.graphs)].replay()
+
+
+def time_graphs(torch, gs, n_iter, n_warm, per_iter_slots=1):
+    """Replay the graphs n_iter times after n_warm; return ms per replay."""
+    for i in range(n_warm):
+        gs.replay(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_iter):
+        gs.replay(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_iter
+
+
+def leg_roofline(torch, fq, xs):
+    """E4M3 block-16 RTN quantize kernel alone (no tensor-scale pass), one
+    launch per graph node, timed over many replays."""
+    rows, cols = xs[0].shape
+    outs = [fq.QTensor.empty(rows, cols, 16, "e4m3", amax="none") for _ in xs]
+
+    def rec(i):
+        for j in range(len(xs)):
+            fq.fp4_quantize(xs[j], 16, "e4m3", amax="none", out=outs[j])
+    gs = GraphSet(torch, 1, rec)
+    ms = time_graphs(torch, gs, 40, 5)
+    per_launch_ms = ms / len(xs)
+    algo = quant_bytes(rows, cols, 16, False)
+    achieved = algo / (per_launch_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_quantize<bf16,16,RTN,ExMy,hw-pack>", "us_per_launch": round(per_launch_ms * 1e3, 3),
+            "algo_bytes_per_launch": algo}
+
+
+def leg_sr(torch, fq, inputs, steps):
+    """200 successive 8192x8192 bf16 Laplace(1e-4) gradients, E4M3 block 16,
+    stochastic rounding (seed 0x5EED, offset = t), delayed amax every 50."""
+    rows = cols = 8192
+    ntens = 200
+    xs = [inputs.device_laplace((rows, cols), 1e-4, inputs.GRADS_SEED0 + t, torch.bfloat16) for t in range(ntens)]
+    outs = [fq.QTensor.empty(rows, cols, 16, "e4m3", rounding="stochastic", amax="delayed") for _ in range(2)]
+    st = fq.AmaxState(50)
+
+    def rec(_):
+        for t in range(ntens):
+            fq.fp4_quantize(xs[t], 16, "e4m3", rounding="stochastic", amax="delayed", state=st, seed=0x5EED,
+                            offset=t, out=outs[t % 2])
+    gs = GraphSet(torch, 1, rec)
+    reps = max(1, min(3, steps // 10))
+    ms = time_graphs(torch, gs, reps, 1)
+    n = rows * cols
+    per_call = n * 2 + n // 2 + n // 16 + 8
+    total = ntens * per_call + 4 * n * 2          # 4 refresh reads of the input
+    gbs = total / (ms * 1e-3) / 1e9
+    del xs
+    return {"workload": "200 x 8192x8192 bf16 Laplace(1e-4) grads, E4M3 B16, SR Philox, delayed amax N=50",
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ms_per_sequence": round(ms, 3)}
+
+
+def leg_dequant(torch, fq, xs):
+    rows, cols = xs[0].shape
+    qts = [fq.fp4_quantize(x, 16, "e4m3", amax="current") for x in xs]
+    ys = [torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda") for _ in xs]
+
+    def rec(_):
+        for j in range(len(xs)):
+            fq.fp4_dequantize(qts[j], out=ys[j])
+    gs = GraphSet(torch, 1, rec)
+    ms = time_graphs(torch, gs, 20, 3) / len(xs)
+    n = rows * cols
+    algo = n // 2 + n // 16 + 8 + n * 2
+    return {"workload": "4096x4096 E4M3 B16 -> bf16", "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
+            "us_per_call": round(ms * 1e3, 3)}
+
+
+def leg_gemm(torch, fq, inputs):
+    """Llama-2 7B linears at M = 8192: both operands quantized NVFP4 (E4M3
+    block 16, exact dequantize path on bf16/f16 matrix cores) and MXFP4
+    (E8M0 block 32, native scaled FP4 matrix cores)."""
+    shapes = {"up": (11008, 4096), "down": (4096, 11008), "sq": (4096, 4096)}
+    res = {}
+    for fmt, block, pol, peak in [("e8m0", 32, "none", "fp4"), ("e4m3", 16, "current", "bf16")]:
+        for name, (n, k) in shapes.items():
+            m = 8192
+            a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
+            w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_" + name], torch.bfloat16)
+            qa = fq.fp4_quantize(a, block, fmt, amax=pol)
+            qw = fq.fp4_quantize(w, block, fmt, amax=pol)
+            c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            try:
+                fq.fp4_gemm(qa, qw, out=c)
+            except fq.Fp4Error as e:
+                res[f"{fmt}_{name}"] = {"error": str(e)}
+                continue
+
+            def rec(_):
+                fq.fp4_gemm(qa, qw, out=c)
+            gs = GraphSet(torch, 1, rec)
+            ms = time_graphs(torch, gs, 10, 2)
+            tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            res[f"{fmt}_{name}"] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
+                                    "frac_fp4_peak": round(tf / MFMA_PEAK_TFLOPS["fp4"], 4),
+                                    "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4),
+                                    "frac_path_peak": round(tf / MFMA_PEAK_TFLOPS[peak], 4)}
+            del a, w, qa, qw, c, gs
+    return res
+
+
+def leg_wo(torch, fq, inputs):
+    """Weight-only NVFP4 GEMM, W [N, K] = [18944, 3584] and [3584, 18944],
+    M in {1, 8, 16}; 12 weight copies rotate (>= 450 MB) so weights stream
+    from HBM."""
+    res = {}
+    for name, (n, k) in {"up": (18944, 3584), "down": (3584, 18944)}.items():
+        w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["decode_" + name], torch.bfloat16)
+        qws = [fq.fp4_quantize(w, 16, "e4m3", amax="current") for _ in range(12)]
+        del w
+        for m in (1, 8, 16):
+            x = inputs.device_normal((m, k), 1.0, 10 + m, torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            try:
+                fq.fp4_wo_gemm(x, qws[0], out=y)
+            except fq.Fp4Error as e:
+                res[f"{name}_m{m}"] = {"error": str(e)}
+                continue
+
+            def rec(_):
+                for q in qws:
+                    fq.fp4_wo_gemm(x, q, out=y)
+            gs = GraphSet(torch, 1, rec)
+            ms = time_graphs(torch, gs, 20, 3) / len(qws)
+            algo = n * k // 2 + n * k // 16 + 8 + m * k * 2 + m * n * 2
+            gbs = algo / (ms * 1e-3) / 1e9
+            res[f"{name}_m{m}"] = {"M": m, "N": n, "K": k, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del qws
+    return res
+
+
+def cpu_baseline():
+    """The CPU oracle (as written, not tuned) on a bounded sample of the
+    sweep workload: the first 256 rows of the 4096x4096 tensor through all
+    five formats, the same bytes accounting as the GPU step."""
+    import numpy as np
+    import oracle
+    import fp4_inputs as inputs
+    x = inputs.sweep()[:256]
+    threads = min(16, os.cpu_count() or 1)
+    rows, cols = x.shape
+    total = 0
+    t0 = time.perf_counter()
+    for fmt, block, pol in SWEEP:
+        oracle.quantize_tensor(x, block, fmt, pol, nthreads=threads)
+        total += quant_bytes(rows, cols, block, pol == "current")
+    dt = time.perf_counter() - t0
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"256x4096 rows of the sweep tensor, 5 formats, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp4_block_scaled_quantize_amd as fq
+    import fp4_inputs as inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    rows = cols = 4096
+    base = inputs.device_outliers(inputs.device_normal((rows, cols), 0.02, inputs.SEEDS["sweep"], torch.bfloat16),
+                                  0.001, 100.0, inputs.SEEDS["sweep"])
+    xs = [base.clone() for _ in range(args.rot)]
+    states = [fq.AmaxState(1) for _ in SWEEP]
+    outs = {f: [fq.QTensor.empty(rows, cols, b, f, amax=p) for _ in range(args.rot)] for f, b, p in SWEEP}
+
+    def step(i):
+        for (f, b, p), st in zip(SWEEP, states):
+            fq.fp4_quantize(xs[i], b, f, amax=p, state=st if p != "none" else None, out=outs[f][i])
+    gs = GraphSet(torch, args.rot, step)
+    for i in range(args.warmup):
+        gs.replay(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        gs.replay(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    step_bytes = sum(quant_bytes(rows, cols, b, p == "current") for _, b, p in SWEEP)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    roof = leg_roofline(torch, fq, xs)
+    legs = {}
+    want = [] if args.legs == "none" else args.legs.split(",")
+    if "dequant" in want:
+        legs["dequant"] = leg_dequant(torch, fq, xs[:8])
+    del outs
+    if "sr" in want:
+        legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)
+        torch.cuda.empty_cache()
+    if "gemm" in want:
+        legs["gemm_llama2_7b"] = leg_gemm(torch, fq, inputs)
+        torch.cuda.empty_cache()
+    if "wo" in want:
+        legs["wo_gemm_qwen25"] = leg_wo(torch, fq, inputs)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    line = {"metric": "FP4 quantize GB/s (% HBM peak); block-scaled FP4 GEMM TFLOP/s (% MFMA peak)",
+            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "wall_s": round(wall, 3), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16->e2m1 (fp32 decisions)", "data": "synthetic",
+            "frac_hbm": round(value / HBM_PEAK_GBS, 4),
+            "config": {"workload": "scale-format sweep: 4096x4096 bf16 N(0,0.02)+0.1% x100 outliers; "
+                                   "E4M3/UE5M3/E3M4/E1M6 block 16 (current amax) + E8M0 block 32, RTN",
+                       "rows": rows, "cols": cols, "formats": [f for f, _, _ in SWEEP],
+                       "rotating_inputs": args.rot, "bytes_per_step": step_bytes},
+            "roofline": roof, "cpu_baseline": cpu, "legs": legs}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

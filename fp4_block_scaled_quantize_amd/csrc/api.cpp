@@ -83,7 +83,7 @@ fp4_status fp4_amax_state_create(uint32_t interval, fp4_amax_state** out)
     st->calls = 0;
     if (hipGetDevice(&st->device) != hipSuccess) { delete st; return FP4_ERR_HIP; }
     if (hipMalloc((void**)&st->dev, sizeof(AmaxDev)) != hipSuccess) { delete st; return FP4_ERR_HIP; }
-    AmaxDev zero{0.0f, 0u, 0u, 0u};
+    AmaxDev zero{};
     if (hipMemcpy(st->dev, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(st->dev);
         delete st;
@@ -108,7 +108,7 @@ fp4_status fp4_amax_state_get(const fp4_amax_state* st, uint64_t* calls, float* 
     AmaxDev h;
     if (hipMemcpy(&h, st->dev, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return FP4_ERR_HIP;
     *calls = st->calls;
-    *amax = h.amax;
+    *amax = h.stored;
     return FP4_OK;
 }
 
@@ -116,7 +116,8 @@ fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
 {
     if (!st || !(amax >= 0.0f) || !isfinite(amax)) return FP4_ERR_INVALID_ARG;
     if (hipDeviceSynchronize() != hipSuccess) return FP4_ERR_HIP;
-    AmaxDev h{amax, 0u, 0u, 0u};
+    AmaxDev h{};
+    h.stored = amax;
     if (hipMemcpy(st->dev, &h, sizeof(h), hipMemcpyHostToDevice) != hipSuccess) return FP4_ERR_HIP;
     st->calls = calls;
     return FP4_OK;
@@ -160,9 +161,10 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
 
-    const AmaxDev* src = nullptr;
+    AmaxDev* src = nullptr;
+    bool refresh = false;
     if (pol != FP4_AMAX_NONE) {
-        const bool refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
+        refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
         if (refresh) {
             st = hip_status(launch_amax(x, x_dtype == FP4_DTYPE_BF16, out->rows, out->cols, ld_x, state->dev, s));
             if (st != FP4_OK) return st;
@@ -179,6 +181,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     p.scales = out->scales;
     p.tensor_scale = out->tensor_scale;
     p.amax_src = src;
+    p.refresh = refresh;
     p.block = out->fmt.block;
     p.stochastic = out->fmt.rounding == FP4_ROUND_STOCHASTIC;
     p.seed = seed;

@@ -143,6 +143,18 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib)
 // ---------------------------------------------------------------------------
 // wave64 helpers
 // ---------------------------------------------------------------------------
+// Max of non-negative binary32 bit patterns across lane pairs / quads.
+__device__ __forceinline__ uint32_t dpp_umax_xor1(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t dpp_umax_xor2(uint32_t v)
+{
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    return v > o ? v : o;
+}
+
 // Max across lane pairs / quads with DPP quad permutations.
 __device__ __forceinline__ float dpp_max_xor1(float v)
 {

@@ -16,12 +16,15 @@ struct ScaleFmtHost {
 // Fill the parameters of a block-scale format (fp4_scale_fmt value).
 bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 
-// Device workspace of an amax state: stored amax, reduction slot, counter.
+// Device workspace of an amax state.  A refresh writes one partial maximum
+// per workgroup of the amax kernel (no atomics, no fences); the quantize
+// kernel of the same call reduces them and stores the result in `stored`,
+// which calls between refreshes read.
+constexpr int kAmaxParts = 256;
 struct AmaxDev {
-    float amax;
-    uint32_t slot;
-    uint32_t count;
-    uint32_t pad;
+    float partial[kAmaxParts];
+    float stored;
+    uint32_t pad[63];
 };
 
 struct QuantLaunch {
@@ -31,7 +34,8 @@ struct QuantLaunch {
     uint8_t* q;
     uint8_t* scales;
     float* tensor_scale;       // out: {g, amax}
-    const AmaxDev* amax_src;   // null: no tensor scale (g = 1)
+    AmaxDev* amax_src;         // null: no tensor scale (g = 1)
+    int32_t refresh;           // amax_src->partial holds this call's maximum
     int32_t block;
     int32_t stochastic;
     uint64_t seed, offset;

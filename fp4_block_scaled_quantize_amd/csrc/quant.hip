@@ -60,6 +60,35 @@ struct Unit;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// max |x| of 8 elements as binary32 bits.  Non-negative floats order like
+// their bit patterns, so the maximum is taken on integers (no NaN
+// canonicalization): bf16 pairs with packed 16-bit max, fp32 with 32-bit max.
+__device__ __forceinline__ uint32_t absmax_bits_bf16(const u32x4& w)
+{
+    u16x2 a = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu);
+    u16x2 c = __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu);
+    u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    uint32_t mm = __builtin_bit_cast(uint32_t, m);
+    uint32_t lo = mm << 16, hi = mm & 0xFFFF0000u;
+    return lo > hi ? lo : hi;
+}
+
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c)
+{
+    uint32_t t = a > b ? a : b;
+    return t > c ? t : c;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits_f32(const f32x4& a, const f32x4& b)
+{
+    const uint32_t M = 0x7FFFFFFFu;
+    uint32_t m0 = umax3(__float_as_uint(a.x) & M, __float_as_uint(a.y) & M, __float_as_uint(a.z) & M);
+    uint32_t m1 = umax3(__float_as_uint(a.w) & M, __float_as_uint(b.x) & M, __float_as_uint(b.y) & M);
+    uint32_t m2 = umax3(__float_as_uint(b.z) & M, __float_as_uint(b.w) & M, m0);
+    return m1 > m2 ? m1 : m2;
+}
 
 template <>
 struct Unit<uint16_t> {                      // bf16
@@ -69,6 +98,7 @@ struct Unit<uint16_t> {                      // bf16
         w = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)x + off));
     }
     __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ uint32_t absmax() const { return absmax_bits_bf16(w); }
     __device__ __forceinline__ void get(float v[8]) const
     {
         v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
@@ -88,6 +118,7 @@ struct Unit<float> {
         b = __builtin_nontemporal_load(p + 1);
     }
     __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ uint32_t absmax() const { return absmax_bits_f32(a, b); }
     __device__ __forceinline__ void get(float v[8]) const
     {
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -95,60 +126,46 @@ struct Unit<float> {
     }
 };
 
-__device__ __forceinline__ float absmax8(const float v[8])
-{
-    float m0 = __builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
-    float m1 = __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3]));
-    float m2 = __builtin_fmaxf(__builtin_fabsf(v[4]), __builtin_fabsf(v[5]));
-    float m3 = __builtin_fmaxf(__builtin_fabsf(v[6]), __builtin_fabsf(v[7]));
-    return __builtin_fmaxf(__builtin_fmaxf(m0, m1), __builtin_fmaxf(m2, m3));
-}
 
 // ---------------------------------------------------------------------------
-// tensor amax: max |x| reduced to one value; the last workgroup to finish
-// publishes it and clears the workspace for the next call.
+// tensor amax: max |x| over the tensor.  Exactly kAmaxParts workgroups; each
+// writes the maximum of its grid-stride share to its own partial slot, so
+// the reduction needs neither atomics nor fences: the quantize kernel that
+// follows on the stream reduces the partials.
 // ---------------------------------------------------------------------------
-constexpr int kAmaxThreads = 256;
-constexpr int kAmaxUnroll = 4;
+constexpr int kAmaxThreads = 512;
 
-template <typename InT>
+template <typename InT, bool STRIDED>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* __restrict__ x, uint32_t nunits, FastDiv upr,
-                                                       int64_t ld, int strided, AmaxDev* __restrict__ dst)
+                                                       int64_t ld, AmaxDev* __restrict__ dst)
 {
-    float m = 0.0f;
-    const uint64_t stride = (uint64_t)gridDim.x * kAmaxThreads;
-    uint64_t u = (uint64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
-    for (; u < nunits; u += stride * kAmaxUnroll) {
-        Unit<InT> un[kAmaxUnroll];
+    constexpr int U = sizeof(InT) == 2 ? 8 : 4;
+    uint32_t m = 0u;
+    const uint64_t stride = (uint64_t)kAmaxParts * kAmaxThreads;
+    for (uint64_t u = (uint64_t)blockIdx.x * kAmaxThreads + threadIdx.x; u < nunits; u += stride * U) {
+        Unit<InT> un[U];
 #pragma unroll
-        for (int j = 0; j < kAmaxUnroll; ++j) {
+        for (int j = 0; j < U; ++j) {
             uint64_t uj = u + j * stride;
-            if (uj < nunits) un[j].load(x, unit_offset((uint32_t)uj, strided, upr, ld));
+            if (uj < nunits) un[j].load(x, unit_offset((uint32_t)uj, STRIDED, upr, ld));
             else un[j].zero();
         }
 #pragma unroll
-        for (int j = 0; j < kAmaxUnroll; ++j) {
-            float v[8];
-            un[j].get(v);
-            m = __builtin_fmaxf(m, absmax8(v));
+        for (int j = 0; j < U; ++j) {
+            uint32_t t = un[j].absmax();
+            m = m > t ? m : t;
         }
     }
-    // wave reduction (non-negative floats: max of the bit patterns)
-    for (int o = 32; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
-    __shared__ float wmax[kAmaxThreads / 64];
+    for (int o = 32; o > 0; o >>= 1) {
+        uint32_t t = (uint32_t)__shfl_xor((int)m, o, 64);
+        m = m > t ? m : t;
+    }
+    __shared__ uint32_t wmax[kAmaxThreads / 64];
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kAmaxThreads / 64; ++w) m = __builtin_fmaxf(m, wmax[w]);
-        atomicMax(&dst->slot, __float_as_uint(m));
-        __threadfence();
-        uint32_t done = atomicAdd(&dst->count, 1u);
-        if (done == gridDim.x - 1) {
-            __threadfence();
-            uint32_t v = atomicExch(&dst->slot, 0u);
-            dst->amax = __uint_as_float(v);
-            atomicExch(&dst->count, 0u);
-        }
+        for (int w = 1; w < kAmaxThreads / 64; ++w) m = m > wmax[w] ? m : wmax[w];
+        dst->partial[blockIdx.x] = __uint_as_float(m);
     }
 }
 
@@ -157,15 +174,16 @@ hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols
 {
     const uint32_t upr = (uint32_t)(cols / 8);
     const uint32_t nunits = (uint32_t)(rows * (cols / 8));
-    const int strided = (ld != cols);
+    const bool strided = (ld != cols);
     FastDiv fd = make_fastdiv(upr ? upr : 1);
-    uint32_t blocks = (nunits + kAmaxThreads * kAmaxUnroll - 1) / (kAmaxThreads * kAmaxUnroll);
-    if (blocks > 2048) blocks = 2048;
-    if (blocks == 0) blocks = 1;
-    if (x_bf16)
-        hipLaunchKernelGGL(k_amax<uint16_t>, dim3(blocks), dim3(kAmaxThreads), 0, s, x, nunits, fd, ld, strided, dst);
-    else
-        hipLaunchKernelGGL(k_amax<float>, dim3(blocks), dim3(kAmaxThreads), 0, s, x, nunits, fd, ld, strided, dst);
+    const dim3 g(kAmaxParts), b(kAmaxThreads);
+    if (x_bf16) {
+        if (strided) hipLaunchKernelGGL((k_amax<uint16_t, true>), g, b, 0, s, x, nunits, fd, ld, dst);
+        else hipLaunchKernelGGL((k_amax<uint16_t, false>), g, b, 0, s, x, nunits, fd, ld, dst);
+    } else {
+        if (strided) hipLaunchKernelGGL((k_amax<float, true>), g, b, 0, s, x, nunits, fd, ld, dst);
+        else hipLaunchKernelGGL((k_amax<float, false>), g, b, 0, s, x, nunits, fd, ld, dst);
+    }
     return hipGetLastError();
 }
 
@@ -173,89 +191,158 @@ hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols
 // quantize
 // ---------------------------------------------------------------------------
 constexpr int kQThreads = 256;
+constexpr int kQUnroll = 4;                  // units per lane (one load each, all in flight)
 
 struct QArgs {
     const void* x;
     uint32_t nunits;
     FastDiv upr;
     int64_t ld;
-    int32_t strided;
     uint32_t* q;                 // one dword of codes per unit
     uint8_t* scales;
     float* tensor_scale;
-    const AmaxDev* amax_src;
+    AmaxDev* amax_src;
+    int32_t refresh;
     ScaleFmt f;
     uint32_t key0, key1, off0, off1;
 };
 
+// The tensor maximum of this call: the reduction of the amax kernel's
+// partials on a refresh, the stored value otherwise.  Every wave reduces the
+// partials itself (one 16-byte load per lane), so no barrier is needed.
+__device__ __forceinline__ float tensor_amax(const QArgs& a)
+{
+    if (!a.refresh) return a.amax_src->stored;
+    static_assert(kAmaxParts == 256, "one float4 of partials per lane");
+    const uint32_t lane = threadIdx.x & 63;
+    const float4 p = reinterpret_cast<const float4*>(a.amax_src->partial)[lane];
+    float m = __builtin_fmaxf(__builtin_fmaxf(p.x, p.y), __builtin_fmaxf(p.z, p.w));
+    for (int o = 32; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+    return m;
+}
+
 // Tensor scale g = amax_t / RN(6 Smax); 1 when there is no tensor scale or
 // the quotient is zero or not finite.
-__device__ __forceinline__ float tensor_scale_of(const QArgs& a, float* amax_out)
+__device__ __forceinline__ float tensor_scale_of(float am, const QArgs& a)
 {
-    float g = 1.0f, am = 0.0f;
-    if (a.amax_src) {
-        am = a.amax_src->amax;
-        float den = 6.0f * a.f.smax;
-        g = am / den;
-        if (!(g > 0.0f) || !(g <= FLT_MAX)) g = 1.0f;
-    }
-    *amax_out = am;
+    if (!a.amax_src) return 1.0f;
+    float den = 6.0f * a.f.smax;
+    float g = am / den;
+    if (!(g > 0.0f) || !(g <= FLT_MAX)) g = 1.0f;
     return g;
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool HWCVT>
+// Block scale of an ExMy format: returns the code and the reciprocal of the
+// effective scale S = RN(s g) (clamped to FLT_MAX; 0 when S is 0).
+__device__ __forceinline__ uint32_t exmy_scale(float bmax, float d, float g, const ScaleFmt& f, float* inv)
+{
+    float us = bmax / d;
+    uint32_t code = scale_encode_exmy(us, f);
+    float S = scale_decode_exmy(code, f) * g;
+    float r = 0.0f;
+    if (S != 0.0f) {
+        r = 1.0f / S;
+        if (!(r <= FLT_MAX)) r = FLT_MAX;
+    }
+    *inv = r;
+    return code;
+}
+
+// Broadcast lane k of every quad to the whole quad.
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), K | (K << 2) | (K << 4) | (K << 6), 0xF, 0xF,
+                                                   false));
+}
+
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED>
 __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
 {
-    constexpr int UNROLL = sizeof(InT) == 2 ? 4 : 2;
-    constexpr int G = BLOCK / 8;                 // lanes per block
+    constexpr int U = kQUnroll;
+    constexpr int G = BLOCK / 8;                 // lanes per block (2 or 4)
+    constexpr int PER = U / G;                   // block scales computed per lane
+    static_assert(U % G == 0, "every lane of a block group computes U/G scales");
     const uint32_t lane = threadIdx.x & 63;
+    const uint32_t sub = lane & (G - 1);
     const uint32_t wave = blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
-    const uint32_t base = wave * (64u * UNROLL);
+    const uint32_t base = wave * (64u * U);
 
-    float amax_t;
-    const float g = tensor_scale_of(a, &amax_t);
-    const float d = 6.0f * g;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        a.tensor_scale[0] = g;
-        a.tensor_scale[1] = amax_t;
-    }
-
-    Unit<InT> un[UNROLL];
+    // issue every load first
+    Unit<InT> un[U];
 #pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
+    for (int j = 0; j < U; ++j) {
         uint32_t u = base + j * 64 + lane;
-        if (u < a.nunits) un[j].load(a.x, unit_offset(u, a.strided, a.upr, a.ld));
+        if (u < a.nunits) un[j].load(a.x, unit_offset(u, STRIDED, a.upr, a.ld));
         else un[j].zero();
     }
 
-#pragma unroll
-    for (int j = 0; j < UNROLL; ++j) {
-        const uint32_t u = base + j * 64 + lane;
-        float v[8];
-        un[j].get(v);
-        float bmax = absmax8(v);
-        bmax = dpp_max_xor1(bmax);
-        if (G == 4) bmax = dpp_max_xor2(bmax);
-
-        uint32_t scode;
-        float inv;
-        if (E8M0) {
-            scode = scale_code_e8m0(bmax);
-            inv = e8m0_inv(scode);
-        } else {
-            float us = bmax / d;
-            scode = scale_encode_exmy(us, a.f);
-            float s = scale_decode_exmy(scode, a.f);
-            float S = s * g;
-            inv = 0.0f;
-            if (S != 0.0f) {
-                inv = 1.0f / S;
-                if (!(inv <= FLT_MAX)) inv = FLT_MAX;
-            }
+    float g = 1.0f, d = 6.0f;
+    if (!E8M0 && a.amax_src) {
+        const float am = tensor_amax(a);
+        g = tensor_scale_of(am, a);
+        d = 6.0f * g;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.tensor_scale[0] = g;
+            a.tensor_scale[1] = am;
+            if (a.refresh) a.amax_src->stored = am;
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = v[k] * inv;
+    } else if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.tensor_scale[0] = 1.0f;
+        a.tensor_scale[1] = 0.0f;
+    }
 
+    // block maxima, reduced over the G lanes of each block
+    float v[U][8];
+    float bm[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        un[j].get(v[j]);
+        bm[j] = __uint_as_float(dpp_umax_xor1(un[j].absmax()));
+        if (G == 4) bm[j] = __uint_as_float(dpp_umax_xor2(__float_as_uint(bm[j])));
+    }
+
+    // lane `sub` of a group computes the scales of blocks j = sub*PER + t
+    float inv_own[PER];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+        float x = bm[t];
+#pragma unroll
+        for (int k = 1; k < G; ++k) x = (sub == (uint32_t)k) ? bm[k * PER + t] : x;
+        uint32_t code;
+        if (E8M0) {
+            code = scale_code_e8m0(x);
+            inv_own[t] = e8m0_inv(code);
+        } else {
+            code = exmy_scale(x, d, g, a.f, &inv_own[t]);
+        }
+        const uint32_t j = sub * PER + t;
+        const uint32_t u = base + j * 64 + lane;        // this lane's unit in block j
+        if (u < a.nunits) a.scales[u / G] = (uint8_t)code;
+    }
+
+    // gather the reciprocal of block j from lane j / PER of the quad
+    float inv[U];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+        if (G == 2) {
+            float mine = inv_own[t];
+            float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
+            inv[t] = sub == 0 ? mine : other;             // block t lives in sub 0
+            inv[PER + t] = sub == 1 ? mine : other;       // block PER+t lives in sub 1
+        } else {
+            inv[0 * PER + t] = quad_bcast<0>(inv_own[t]);
+            inv[1 * PER + t] = quad_bcast<1>(inv_own[t]);
+            inv[2 * PER + t] = quad_bcast<2>(inv_own[t]);
+            inv[3 * PER + t] = quad_bcast<3>(inv_own[t]);
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint32_t u = base + j * 64 + lane;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[j][k] = v[j][k] * inv[j];
         uint32_t packed;
         if (SR) {
             U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
@@ -264,45 +351,36 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                packed |= e2m1_sr(v[k], r16) << (4 * k);
+                packed |= e2m1_sr(v[j][k], r16) << (4 * k);
             }
-        } else if (HWCVT) {
-            packed = FP4_CVT_PK(0u, v[0], v[1], 0);
-            packed = FP4_CVT_PK(packed, v[2], v[3], 1);
-            packed = FP4_CVT_PK(packed, v[4], v[5], 2);
-            packed = FP4_CVT_PK(packed, v[6], v[7], 3);
         } else {
-            packed = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) packed |= e2m1_rtn_sw(v[k]) << (4 * k);
+            packed = FP4_CVT_PK(0u, v[j][0], v[j][1], 0);
+            packed = FP4_CVT_PK(packed, v[j][2], v[j][3], 1);
+            packed = FP4_CVT_PK(packed, v[j][4], v[j][5], 2);
+            packed = FP4_CVT_PK(packed, v[j][6], v[j][7], 3);
         }
-        if (u < a.nunits) {
-            __builtin_nontemporal_store(packed, a.q + u);
-            if ((lane & (G - 1)) == 0) a.scales[u / G] = (uint8_t)scode;
-        }
+        if (u < a.nunits) __builtin_nontemporal_store(packed, a.q + u);
     }
 }
 
-bool g_use_hw_cvt = true;    // hardware E2M1 pack for round-to-nearest
-
 template <typename InT, int BLOCK, bool SR, bool E8M0>
-static void launch_q4(const QArgs& a, uint32_t blocks, hipStream_t s)
+static void launch_q4(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
 {
-    if (!SR && g_use_hw_cvt)
+    if (strided)
         hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true>), dim3(blocks), dim3(kQThreads), 0, s, a);
     else
         hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false>), dim3(blocks), dim3(kQThreads), 0, s, a);
 }
 
 template <typename InT, int BLOCK>
-static void launch_q3(const QArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
+static void launch_q3(const QArgs& a, bool sr, bool e8, bool strided, uint32_t blocks, hipStream_t s)
 {
     if (sr) {
-        if (e8) launch_q4<InT, BLOCK, true, true>(a, blocks, s);
-        else launch_q4<InT, BLOCK, true, false>(a, blocks, s);
+        if (e8) launch_q4<InT, BLOCK, true, true>(a, strided, blocks, s);
+        else launch_q4<InT, BLOCK, true, false>(a, strided, blocks, s);
     } else {
-        if (e8) launch_q4<InT, BLOCK, false, true>(a, blocks, s);
-        else launch_q4<InT, BLOCK, false, false>(a, blocks, s);
+        if (e8) launch_q4<InT, BLOCK, false, true>(a, strided, blocks, s);
+        else launch_q4<InT, BLOCK, false, false>(a, strided, blocks, s);
     }
 }
 
@@ -313,27 +391,26 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.nunits = (uint32_t)(p.rows * (p.cols / 8));
     a.upr = make_fastdiv((uint32_t)(p.cols / 8 ? p.cols / 8 : 1));
     a.ld = p.ld;
-    a.strided = (p.ld != p.cols);
     a.q = (uint32_t*)p.q;
     a.scales = p.scales;
     a.tensor_scale = p.tensor_scale;
     a.amax_src = p.amax_src;
+    a.refresh = p.refresh;
     a.f = ScaleFmt{p.fmt.ebits, p.fmt.mbits, p.fmt.bias, p.fmt.maxcode, p.fmt.smax, p.fmt.is_e8m0};
     a.key0 = (uint32_t)p.seed;
     a.key1 = (uint32_t)(p.seed >> 32);
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
-    const int unroll = p.x_bf16 ? 4 : 2;
-    const uint32_t per_block = kQThreads * unroll;
+    const uint32_t per_block = kQThreads * kQUnroll;
     uint32_t blocks = (a.nunits + per_block - 1) / per_block;
     if (blocks == 0) blocks = 1;
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols;
     if (p.x_bf16) {
-        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, blocks, s);
-        else launch_q3<uint16_t, 32>(a, sr, e8, blocks, s);
+        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, strided, blocks, s);
+        else launch_q3<uint16_t, 32>(a, sr, e8, strided, blocks, s);
     } else {
-        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, blocks, s);
-        else launch_q3<float, 32>(a, sr, e8, blocks, s);
+        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, strided, blocks, s);
+        else launch_q3<float, 32>(a, sr, e8, strided, blocks, s);
     }
     return hipGetLastError();
 }
