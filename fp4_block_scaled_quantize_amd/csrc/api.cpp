@@ -229,7 +229,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
     if (a->cols % 128) return FP4_ERR_SHAPE;
     if (ldc < b->rows) return FP4_ERR_SHAPE;
-    if (!aligned16(c) || ldc % 8) return FP4_ERR_ALIGN;
+    if (((uintptr_t)c & 1u) != 0) return FP4_ERR_ALIGN;
     if (a->rows == 0 || b->rows == 0) return FP4_OK;
     GemmLaunch p;
     p.qa = a->q; p.sa = a->scales; p.ga = a->tensor_scale;
@@ -240,6 +240,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     p.c = c; p.ldc = ldc;
     hipStream_t s = (hipStream_t)stream;
     if (fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
+    if (!gemm_dq_supported(fa, fb)) return FP4_ERR_UNSUPPORTED;
     return hip_status(launch_gemm_dq(p, s));
 }
 

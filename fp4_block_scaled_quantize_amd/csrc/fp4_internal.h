@@ -69,6 +69,9 @@ struct GemmLaunch {
     int64_t ldc;
 };
 
+// The exact dequantize path needs one 16-bit type (f16 or bf16) that holds
+// every e2m1 * s product of both operands exactly.
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb);
 hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
 

@@ -1,7 +1,401 @@
-// gemm.hip -- placeholder launchers (filled in with the GEMM kernels)
+// gemm.hip -- block-scaled FP4 x FP4 -> bf16 GEMM for gfx950.
+//
+// C[M, N] = bf16_RNE(ga * gb * sum_k (e2m1(a_mk) s_a)(e2m1(w_nk) s_w)), fp32
+// accumulation, both operands blocked along K and stored K-major (A [M, K],
+// W [N, K]; C = A W^T).  ue5m3-fp4-pretraining "Что сделали": the linear
+// layers run in FP4; quant_prune_distill/574 "Выводы": weight + activation
+// FP4 for the compute-bound regime.
+//
+// Two kernels:
+//  * k_gemm_mx: both operands E8M0 at block 32 (MXFP4).  The gfx950
+//    block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4 takes
+//    FP4 operands and one E8M0 scale per 32 K-elements per row directly: lane
+//    l supplies row (l % 32), K-half (l / 32) as 16 contiguous bytes -- the
+//    packed row-major layout of the quantizer -- and that K-half's scale
+//    byte.  No dequantization.
+//  * k_gemm_dq: any other format pair (E4M3/UE5M3/ExMy at block 16 or 32).
+//    No gfx950 instruction takes a non-power-of-two scale per 16 elements,
+//    so FP4 tiles are dequantized exactly (e2m1 * s has at most 9
+//    significant bits) to f16 or bf16 in LDS and multiplied on the
+//    32x32x16 f16/bf16 matrix cores.
+//
+// Both compute the transposed tile D = W A^T so that each lane owns four
+// consecutive output columns of C (one 8-byte store).  Workgroup tile
+// 256 x 256, four waves of 128 x 128, K double-buffered through LDS.
+#include "fp4_device.hpp"
 #include "fp4_internal.h"
+
 namespace fp4 {
-hipError_t launch_gemm_mx(const GemmLaunch&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_gemm_dq(const GemmLaunch&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_wo_gemm(const WoGemmLaunch&, hipStream_t) { return hipErrorNotSupported; }
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = 256;        // workgroup tile (rows of W) x (rows of A)
+constexpr int kGemmThreads = 256;
+
+// ---------------------------------------------------------------------------
+// epilogue: acc[i][j] holds D[n = 32 i + 8 q + 4 (l/32) + e][m = 32 j + l%32]
+// for register r = 4 q + e; scale by g and store as bf16 into C[m][n].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], float g, uint16_t* __restrict__ c, int64_t ldc,
+                                           int64_t m_base, int64_t n_base, int64_t M, int64_t N)
+{
+    // 8-byte stores need 8-byte aligned rows; otherwise store element-wise
+    const bool vec = ((ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(c) & 7) == 0);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t m = m_base + 32 * j + (lane & 31);
+        if (m >= M) continue;
+        uint16_t* crow = c + m * ldc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n_base + 32 * i + 8 * q + 4 * (lane >> 5);
+                const uint32_t b0 = f32_to_bf16_rne(acc[i][j][4 * q + 0] * g);
+                const uint32_t b1 = f32_to_bf16_rne(acc[i][j][4 * q + 1] * g);
+                const uint32_t b2 = f32_to_bf16_rne(acc[i][j][4 * q + 2] * g);
+                const uint32_t b3 = f32_to_bf16_rne(acc[i][j][4 * q + 3] * g);
+                if (vec && n + 3 < N) {
+                    uint2 v;
+                    v.x = b0 | (b1 << 16);
+                    v.y = b2 | (b3 << 16);
+                    *reinterpret_cast<uint2*>(crow + n) = v;
+                } else {
+                    if (n + 0 < N) crow[n + 0] = (uint16_t)b0;
+                    if (n + 1 < N) crow[n + 1] = (uint16_t)b1;
+                    if (n + 2 < N) crow[n + 2] = (uint16_t)b2;
+                    if (n + 3 < N) crow[n + 3] = (uint16_t)b3;
+                }
+            }
+        }
+    }
 }
+
+// ---------------------------------------------------------------------------
+// MXFP4: native block-scaled FP4 matrix instruction
+// ---------------------------------------------------------------------------
+constexpr int kMxBK = 128;              // K elements per LDS stage (64 bytes per row)
+constexpr int kMxRow = 80;              // LDS row stride (64 B + 16 B pad: conflict-free 16 B reads)
+
+struct MxSmem {
+    uint8_t w[2][kTile * kMxRow];
+    uint8_t a[2][kTile * kMxRow];
+    uint32_t sw[2][kTile];              // 4 E8M0 bytes (K blocks of 32) per row per stage
+    uint32_t sa[2][kTile];
+};
+
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_mx(GemmLaunch p)
+{
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    MxSmem& sm = *reinterpret_cast<MxSmem*>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int64_t n_base = (int64_t)blockIdx.x * kTile;
+    const int64_t m_base = (int64_t)blockIdx.y * kTile;
+    const int64_t M = p.m, N = p.n, K = p.k;
+    const int64_t rowb = K / 2;          // bytes per row of codes
+    const int64_t rows = K / 32;         // scale bytes per row
+    const int KT = (int)(K / kMxBK);
+
+    // global -> register staging: thread t moves 16 B chunk (t & 3) of rows
+    // (t >> 2) + 64 r, r = 0..3, for both operands, plus the 4 scale bytes
+    // of row t.
+    v4i rw[4], ra[4];
+    uint32_t rsw, rsa;
+    const int crow = tid >> 2, cchunk = tid & 3;
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t nr = n_base + crow + 64 * r, mr = m_base + crow + 64 * r;
+            rw[r] = nr < N ? *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kt * 64 + cchunk * 16) : v4i{0, 0, 0, 0};
+            ra[r] = mr < M ? *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kt * 64 + cchunk * 16) : v4i{0, 0, 0, 0};
+        }
+        const int64_t nt = n_base + tid, mt = m_base + tid;
+        rsw = nt < N ? *reinterpret_cast<const uint32_t*>(p.sb + nt * rows + kt * 4) : 0x7F7F7F7Fu;
+        rsa = mt < M ? *reinterpret_cast<const uint32_t*>(p.sa + mt * rows + kt * 4) : 0x7F7F7F7Fu;
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<v4i*>(&sm.w[buf][(crow + 64 * r) * kMxRow + cchunk * 16]) = rw[r];
+            *reinterpret_cast<v4i*>(&sm.a[buf][(crow + 64 * r) * kMxRow + cchunk * 16]) = ra[r];
+        }
+        sm.sw[buf][tid] = rsw;
+        sm.sa[buf][tid] = rsa;
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int frow = lane & 31, khalf = lane >> 5;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) gload(kt + 1);
+        uint32_t swd[4], sad[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) swd[i] = sm.sw[buf][wn * 128 + 32 * i + frow];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sad[j] = sm.sa[buf][wm * 128 + 32 * j + frow];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            v4i wf[4], af[4];
+            const int off = ks * 32 + khalf * 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wf[i] = *reinterpret_cast<const v4i*>(&sm.w[buf][(wn * 128 + 32 * i + frow) * kMxRow + off]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                af[j] = *reinterpret_cast<const v4i*>(&sm.a[buf][(wm * 128 + 32 * j + frow) * kMxRow + off]);
+            const int sh = 8 * (2 * ks + khalf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sw = (int)((swd[i] >> sh) & 0xFFu);
+                const v8i wv = {wf[i][0], wf[i][1], wf[i][2], wf[i][3], 0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sa = (int)((sad[j] >> sh) & 0xFFu);
+                    const v8i av = {af[j][0], af[j][1], af[j][2], af[j][3], 0, 0, 0, 0};
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0, sa);
+                }
+            }
+        }
+        if (kt + 1 < KT) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    const float g = p.ga[0] * p.gb[0];
+    store_tile(acc, g, p.c, p.ldc, m_base + wm * 128, n_base + wn * 128, M, N);
+}
+
+// Kernels with more than 64 KiB of dynamic LDS must opt in once per device.
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t bytes)
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s)
+{
+    hipError_t e = allow_lds(k_gemm_mx, sizeof(MxSmem));
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
+    hipLaunchKernelGGL(k_gemm_mx, grid, dim3(kGemmThreads), sizeof(MxSmem), s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// exact dequantize path: FP4 tiles -> f16/bf16 in LDS -> 32x32x16 MFMA
+// ---------------------------------------------------------------------------
+constexpr int kDqBK = 64;                 // K elements per stage
+constexpr int kDqRow = 144;               // LDS row stride in bytes: 64 x 2 B + 16 B pad
+
+struct DqSmem {
+    uint8_t w[2][kTile * kDqRow];
+    uint8_t a[2][kTile * kDqRow];
+};
+
+// Largest power of two not above a positive normal g (1 for anything else):
+// g / split_pow2(g) lies in [1, 2) and the division is exact.
+__device__ __forceinline__ float split_pow2(float g)
+{
+    const uint32_t e = __float_as_uint(g) & 0x7F800000u;
+    return (e == 0u || e == 0x7F800000u || g < 0.0f) ? 1.0f : __uint_as_float(e);
+}
+
+// Dequantize 32 E2M1 codes (16 bytes) with scale(s) into 32 16-bit values.
+// The product e2m1 * s is exact in binary32 and, for the chosen element type,
+// exact in f16 / bf16, so the narrowing is exact (truncation = rounding).
+template <bool F16>
+__device__ __forceinline__ void dequant32(const v4i& codes, float s0, float s1, uint32_t out[16])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = (uint32_t)codes[d];
+        const float s = d < 2 ? s0 : s1;    // elements 0..15 use s0, 16..31 use s1
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float v0 = e2m1_value((w >> (8 * h)) & 0xFu) * s;
+            const float v1 = e2m1_value((w >> (8 * h + 4)) & 0xFu) * s;
+            uint32_t b0, b1;
+            if (F16) {
+                b0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0);
+                b1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1);
+            } else {
+                b0 = __float_as_uint(v0) >> 16;
+                b1 = __float_as_uint(v1) >> 16;
+            }
+            out[d * 4 + h] = b0 | (b1 << 16);
+        }
+    }
+}
+
+template <bool F16, int BLOCK>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
+{
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    DqSmem& sm = *reinterpret_cast<DqSmem*>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int64_t n_base = (int64_t)blockIdx.x * kTile;
+    const int64_t m_base = (int64_t)blockIdx.y * kTile;
+    const int64_t M = p.m, N = p.n, K = p.k;
+    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const int KT = (int)(K / kDqBK);
+    const ScaleFmt fw{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
+    const ScaleFmt fa{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
+    // bf16 spans the binary32 range, so the power-of-two part of each tensor
+    // scale is folded into the (still exact) dequantized values; this keeps
+    // products of wide-range scales (E7M0 up to 2^63) inside binary32.  The
+    // f16 formats have small scale ranges and keep g for the epilogue.
+    float pw = 1.0f, pa = 1.0f, g = p.ga[0] * p.gb[0];
+    if (!F16) {
+        const float gw = p.gb[0], ga = p.ga[0];
+        pw = split_pow2(gw);
+        pa = split_pow2(ga);
+        g = (gw / pw) * (ga / pa);
+    }
+
+    // staging: thread t owns 16 B chunk (t & 1) (32 elements) of rows
+    // (t >> 1) and (t >> 1) + 128 of each operand, with their scales
+    const int crow = tid >> 1, cchunk = tid & 1;
+    v4i rw[2], ra[2];
+    uint32_t scw[2], sca[2];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int64_t nr = n_base + crow + 128 * r, mr = m_base + crow + 128 * r;
+            const int64_t kb = (int64_t)kt * 32 + cchunk * 16;           // byte offset in the row
+            const int64_t sb = ((int64_t)kt * kDqBK + cchunk * 32) / BLOCK; // first scale of the chunk
+            if (nr < N) {
+                rw[r] = *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kb);
+                scw[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sb + nr * rows + sb)
+                                     : (uint32_t)p.sb[nr * rows + sb];
+            } else {
+                rw[r] = v4i{0, 0, 0, 0};
+                scw[r] = 0;
+            }
+            if (mr < M) {
+                ra[r] = *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kb);
+                sca[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sa + mr * rows + sb)
+                                     : (uint32_t)p.sa[mr * rows + sb];
+            } else {
+                ra[r] = v4i{0, 0, 0, 0};
+                sca[r] = 0;
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            uint32_t o[16];
+            {
+                const float s0 = scale_decode_any(scw[r] & 0xFFu, fw) * pw;
+                const float s1 = BLOCK == 16 ? scale_decode_any((scw[r] >> 8) & 0xFFu, fw) * pw : s0;
+                dequant32<F16>(rw[r], s0, s1, o);
+                uint8_t* dst = &sm.w[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<v4i*>(dst + 16 * v) = v4i{(int)o[4 * v], (int)o[4 * v + 1], (int)o[4 * v + 2],
+                                                               (int)o[4 * v + 3]};
+            }
+            {
+                const float s0 = scale_decode_any(sca[r] & 0xFFu, fa) * pa;
+                const float s1 = BLOCK == 16 ? scale_decode_any((sca[r] >> 8) & 0xFFu, fa) * pa : s0;
+                dequant32<F16>(ra[r], s0, s1, o);
+                uint8_t* dst = &sm.a[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<v4i*>(dst + 16 * v) = v4i{(int)o[4 * v], (int)o[4 * v + 1], (int)o[4 * v + 2],
+                                                               (int)o[4 * v + 3]};
+            }
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    const int frow = lane & 31, khalf = lane >> 5;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < kDqBK / 16; ++ks) {
+            v4i wf[4], af[4];
+            const int off = ks * 32 + khalf * 16;        // 16 K = 32 bytes per step; lane half = 8 K
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wf[i] = *reinterpret_cast<const v4i*>(&sm.w[buf][(wn * 128 + 32 * i + frow) * kDqRow + off]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                af[j] = *reinterpret_cast<const v4i*>(&sm.a[buf][(wm * 128 + 32 * j + frow) * kDqRow + off]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (F16)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wf[i]),
+                                                                          __builtin_bit_cast(v8h, af[j]), acc[i][j],
+                                                                          0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, wf[i]),
+                                                                           __builtin_bit_cast(v8bf, af[j]), acc[i][j],
+                                                                           0, 0, 0);
+                }
+        }
+        if (kt + 1 < KT) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    store_tile(acc, g, p.c, p.ldc, m_base + wm * 128, n_base + wn * 128, M, N);
+}
+
+// Formats whose e2m1 * s products are exact in f16 (normal range) and those
+// exact in bf16 (at most 8 significant bits).
+static bool exact_in_f16(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits <= 4 && (f.ebits + f.mbits == 7); }
+static bool exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 5; }
+
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb)
+{
+    return (exact_in_f16(fa) && exact_in_f16(fb)) || (exact_in_bf16(fa) && exact_in_bf16(fb));
+}
+
+hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
+{
+    const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
+    const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);
+    if (!f16 && !bf16) return hipErrorNotSupported;
+    dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
+    const size_t sh = sizeof(DqSmem);
+    hipError_t e = hipSuccess;
+    if (f16) e = p.block == 16 ? allow_lds(k_gemm_dq<true, 16>, sh) : allow_lds(k_gemm_dq<true, 32>, sh);
+    else e = p.block == 16 ? allow_lds(k_gemm_dq<false, 16>, sh) : allow_lds(k_gemm_dq<false, 32>, sh);
+    if (e != hipSuccess) return e;
+    if (f16) {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_dq<true, 16>), grid, dim3(kGemmThreads), sh, s, p);
+        else hipLaunchKernelGGL((k_gemm_dq<true, 32>), grid, dim3(kGemmThreads), sh, s, p);
+    } else {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_dq<false, 16>), grid, dim3(kGemmThreads), sh, s, p);
+        else hipLaunchKernelGGL((k_gemm_dq<false, 32>), grid, dim3(kGemmThreads), sh, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_wo_gemm(const WoGemmLaunch&, hipStream_t) { return hipErrorNotSupported; }
+
+}  // namespace fp4

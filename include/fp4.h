@@ -177,7 +177,8 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within
  * 1e-5 * sum_k |a||b| of the exact product before the bf16 rounding.
- * K % 128 == 0, M and N arbitrary; ldc >= N, ldc % 8 == 0, c 16-byte aligned.
+ * K % 128 == 0, M and N arbitrary; ldc >= N; c 2-byte aligned (rows that
+ * are 8-byte aligned are written with vector stores).
  */
 FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64_t ldc, void* stream);
 

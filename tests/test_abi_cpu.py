@@ -81,6 +81,7 @@ def test_gemm_and_wo_gemm_shape_checks():
     a96 = _tensor(rows=8, cols=96)
     assert L.fp4_gemm(ctypes.byref(a96), ctypes.byref(a96), FAKE, 8, None) == -3    # K % 128
     assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(a), FAKE, 4, None) == -3        # ldc < N
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(a), FAKE + 1, 8, None) == -4    # c misaligned
     w = _tensor(rows=8, cols=256)
     assert L.fp4_wo_gemm(FAKE, 256, 0, ctypes.byref(w), FAKE, 8, None) == -2        # M = 0
     assert L.fp4_wo_gemm(FAKE, 256, 17, ctypes.byref(w), FAKE, 8, None) == -2       # M > 16

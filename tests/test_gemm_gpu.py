@@ -1,0 +1,148 @@
+"""GPU tolerance tests of the block-scaled GEMM and the weight-only GEMM.
+
+Reference: the oracle quantizes the same seeded inputs, dequantizes them
+exactly in binary64 and takes the product; a bf16 output passes iff it is the
+bf16 rounding of some value within 1e-5 * sum_k |a_k||b_k| of the exact
+product.  The GPU operands are first checked to be byte-identical to the
+oracle's, so the reference never depends on the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_inputs as inputs
+import oracle
+from tests.gpu_util import assert_bytes_equal, host, to_device
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp4_block_scaled_quantize_amd")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _policy(fmt):
+    return "none" if fmt == "e8m0" else "current"
+
+
+def _quant_both(x_np, block, fmt):
+    """GPU quantization and the oracle's; asserts they are identical and
+    returns (gpu QTensor, oracle exact binary64 dequantization)."""
+    pol = _policy(fmt)
+    qt = fq.fp4_quantize(to_device(x_np), block, fmt, amax=pol)
+    q, s, g, _ = oracle.quantize_tensor(x_np, block, fmt, pol, nthreads=8)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qt.q), q, "operand codes")
+    assert_bytes_equal(host(qt.scales), s, "operand scales")
+    return qt, oracle.dequantize_f64(q, s, g, block, fmt)
+
+
+def _check_gemm(c_gpu, a_hat, w_hat, rows=None, tag=""):
+    if rows is not None:
+        a_hat = a_hat[rows]
+    cref, tol = oracle.gemm_ref(a_hat, w_hat)
+    c = c_gpu.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        c = c[rows]
+    ok = oracle.gemm_check(c, cref, tol)
+    if not ok.all():
+        i, j = np.argwhere(~ok)[0]
+        raise AssertionError(f"{tag}: {int((~ok).sum())} of {ok.size} outputs out of tolerance; first ({i},{j}) "
+                             f"got {c[i, j]!r} ref {cref[i, j]!r} tol {tol[i, j]!r}")
+
+
+def _normal(rows, cols, seed, std=1.0, dtype="f32"):
+    x = (np.random.default_rng(seed).standard_normal((rows, cols)) * std).astype(np.float32)
+    return inputs.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+# ---------------------------------------------------------------------------
+def test_small_nvfp4_gemm():
+    """64x256 @ (256x256)^T, NVFP4 E4M3 block 16 from the 1%-outlier matrix."""
+    qa, a = _quant_both(inputs.small_a(), 16, "e4m3")
+    qb, b = _quant_both(inputs.small_b(), 16, "e4m3")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag="small nvfp4")
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (70, 300, 256), (300, 70, 512), (1, 33, 128), (257, 513, 384),
+                                   (512, 256, 1024)])
+def test_mxfp4_native_shapes(m, n, k):
+    qa, a = _quant_both(_normal(m, k, 1), 32, "e8m0")
+    qb, b = _quant_both(_normal(n, k, 2, 0.02), 32, "e8m0")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag=f"mxfp4 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e3m4", "e1m6", "e2m5", "e5m2", "e6m1", "e7m0"])
+@pytest.mark.parametrize("block", [16, 32])
+def test_dequant_path_formats(fmt, block):
+    m, n, k = 96, 160, 256
+    qa, a = _quant_both(_normal(m, k, 3, dtype="bf16"), block, fmt)
+    qb, b = _quant_both(_normal(n, k, 4, 0.02, dtype="bf16"), block, fmt)
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag=f"{fmt}/{block}")
+
+
+def test_e8m0_at_block16_and_mixed_formats():
+    m, n, k = 40, 72, 256
+    x = _normal(m, k, 5)
+    w = _normal(n, k, 6, 0.05)
+    qa, a = _quant_both(x, 16, "e8m0")
+    qb, b = _quant_both(w, 16, "e8m0")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag="e8m0/16")
+    qa, a = _quant_both(x, 16, "e4m3")
+    qb, b = _quant_both(w, 16, "ue5m3")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag="e4m3 x ue5m3")
+    qa, a = _quant_both(x, 32, "e8m0")
+    qb, b = _quant_both(w, 32, "e4m3")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag="e8m0 x e4m3")
+
+
+def test_unsupported_pair_is_rejected():
+    x = torch.randn(32, 128, device="cuda")
+    qa = fq.fp4_quantize(x, 16, "e1m6")
+    qb = fq.fp4_quantize(x, 16, "ue5m3")
+    with pytest.raises(fq.Fp4Error) as e:
+        fq.fp4_gemm(qa, qb)
+    assert e.value.status == -2
+
+
+def test_zero_operand():
+    qa, a = _quant_both(np.zeros((33, 256), dtype=np.float32), 16, "e4m3")
+    qb, b = _quant_both(_normal(40, 256, 7), 16, "e4m3")
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert not bool(c.float().abs().sum() > 0)
+
+
+@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e4m3", 16)])
+@pytest.mark.parametrize("wname", ["up", "down", "sq"])
+def test_llama_shapes_sampled_rows(fmt, block, wname):
+    """Llama-2 7B linears at M = 8192 (batch 4 x seq 2048): sampled output
+    rows (including the last tile) checked against the binary64 reference."""
+    shapes = {"a": (8192, 4096), "up": (11008, 4096), "down": (4096, 11008), "sq": (4096, 4096)}
+    k = shapes[wname][1]
+    a_shape = (8192, k)
+    xa = inputs.llama("a", {**shapes, "a": a_shape})
+    xw = inputs.llama(wname, shapes)
+    qa, a = _quant_both(xa, block, fmt)
+    qw, w = _quant_both(xw, block, fmt)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([rng.integers(0, 8192, 40), [0, 255, 256, 8191]]))
+    _check_gemm(c, a, w, rows=rows, tag=f"llama {wname} {fmt}")
