@@ -231,6 +231,8 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (ldc < b->rows) return FP4_ERR_SHAPE;
     if (((uintptr_t)c & 1u) != 0) return FP4_ERR_ALIGN;
     if (a->rows == 0 || b->rows == 0) return FP4_OK;
+    if (!aligned16(a->q) || !aligned16(b->q) || ((uintptr_t)a->scales & 3u) || ((uintptr_t)b->scales & 3u))
+        return FP4_ERR_ALIGN;
     GemmLaunch p;
     p.qa = a->q; p.sa = a->scales; p.ga = a->tensor_scale;
     p.qb = b->q; p.sb = b->scales; p.gb = b->tensor_scale;
@@ -256,6 +258,7 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     if (!aligned16(x) || ldx % 8) return FP4_ERR_ALIGN;
     if (w->rows == 0) return FP4_OK;
+    if (!aligned16(w->q) || ((uintptr_t)w->scales & 3u)) return FP4_ERR_ALIGN;
     WoGemmLaunch p;
     p.x = x; p.ldx = ldx; p.m = m;
     p.qw = w->q; p.sw = w->scales; p.gw = w->tensor_scale;

@@ -240,6 +240,28 @@ __device__ __forceinline__ void dequant32(const v4i& codes, float s0, float s1, 
     }
 }
 
+// As dequant32<false>, for scales whose products need up to 9 significant
+// bits (E1M6): v = hi + lo with hi its bf16 truncation and lo the exact
+// remainder, both exact bf16 values.
+__device__ __forceinline__ void dequant32_split(const v4i& codes, float s0, float s1, uint32_t hi[16],
+                                                uint32_t lo[16])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = (uint32_t)codes[d];
+        const float s = d < 2 ? s0 : s1;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float v0 = e2m1_value((w >> (8 * h)) & 0xFu) * s;
+            const float v1 = e2m1_value((w >> (8 * h + 4)) & 0xFu) * s;
+            const uint32_t h0 = __float_as_uint(v0) & 0xFFFF0000u, h1 = __float_as_uint(v1) & 0xFFFF0000u;
+            const float l0 = v0 - __uint_as_float(h0), l1 = v1 - __uint_as_float(h1);
+            hi[d * 4 + h] = (h0 >> 16) | h1;
+            lo[d * 4 + h] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
+        }
+    }
+}
+
 template <bool F16, int BLOCK>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 {
@@ -396,6 +418,100 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_wo_gemm(const WoGemmLaunch&, hipStream_t) { return hipErrorNotSupported; }
+// ---------------------------------------------------------------------------
+// weight-only GEMM: Y[M, N] = bf16(gw * X[M, K] W[N, K]^T), 1 <= M <= 16
+// (quant_prune_distill/574 "Эксперименты": weight-only NVFP4 with a
+// memory-bound kernel for small-batch generation).
+//
+// A workgroup owns 16 rows of W and 8 waves that split K in 128-element
+// chunks; every byte of W is read once, streamed with one 16-byte load per
+// lane per chunk, dequantized exactly to bf16 in registers and multiplied on
+// the 16x16x32 bf16 matrix cores against X (M padded to 16 with zeros).  The
+// dot product is a sum, so the K order inside a chunk is free: lane group g
+// (lane / 16) takes the 32 contiguous elements [32 g, 32 g + 32) of the
+// chunk and feeds 8 of them to each of the chunk's four MFMAs, with X read
+// in the same order.  The eight waves' partial tiles are summed in LDS in a
+// fixed order (deterministic).
+// ---------------------------------------------------------------------------
+typedef float v4f __attribute__((ext_vector_type(4)));
+constexpr int kWoWaves = 8;
+constexpr int kWoThreads = 64 * kWoWaves;
+
+template <int BLOCK, bool SPLIT>
+__global__ __launch_bounds__(kWoThreads) void k_wo_gemm(WoGemmLaunch p)
+{
+    __shared__ float red[kWoWaves][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, grp = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t N = p.n, K = p.k, M = p.m;
+    const int64_t n = n0 + r16;
+    const bool nvalid = n < N;
+    const bool mvalid = r16 < M;
+    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const ScaleFmt fw{p.fw.ebits, p.fw.mbits, p.fw.bias, p.fw.maxcode, p.fw.smax, p.fw.is_e8m0};
+    const float gw = p.gw[0];
+    const float pw = split_pow2(gw);
+    const float gres = gw / pw;
+    const uint8_t* wrow = p.qw + (nvalid ? n : 0) * rowb;
+    const uint8_t* srow = p.sw + (nvalid ? n : 0) * rows;
+    const uint16_t* xrow = p.x + (mvalid ? r16 : 0) * p.ldx;
+    const int nchunks = (int)(K / 128);
+
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kc = wave; kc < nchunks; kc += kWoWaves) {
+        const int64_t kel = (int64_t)kc * 128 + 32 * grp;      // first K element of this lane's 32
+        v4i wq = nvalid ? *reinterpret_cast<const v4i*>(wrow + kel / 2) : v4i{0, 0, 0, 0};
+        uint32_t sc = 0;
+        if (nvalid) sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow + kel / 16)
+                                     : (uint32_t)srow[kel / 32];
+        v4i xv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            xv[t] = mvalid ? *reinterpret_cast<const v4i*>(xrow + kel + 8 * t) : v4i{0, 0, 0, 0};
+        const float s0 = scale_decode_any(sc & 0xFFu, fw) * pw;
+        const float s1 = BLOCK == 16 ? scale_decode_any((sc >> 8) & 0xFFu, fw) * pw : s0;
+        uint32_t wb[16], wl[16];
+        if (SPLIT) dequant32_split(wq, s0, s1, wb, wl);
+        else dequant32<false>(wq, s0, s1, wb);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const v4i wt = v4i{(int)wb[4 * t], (int)wb[4 * t + 1], (int)wb[4 * t + 2], (int)wb[4 * t + 3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xv[t]), __builtin_bit_cast(v8bf, wt),
+                                                          acc, 0, 0, 0);
+            if (SPLIT) {
+                const v4i wlt = v4i{(int)wl[4 * t], (int)wl[4 * t + 1], (int)wl[4 * t + 2], (int)wl[4 * t + 3]};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xv[t]),
+                                                              __builtin_bit_cast(v8bf, wlt), acc, 0, 0, 0);
+            }
+        }
+    }
+    // acc[r] = D[m = 4 grp + r][n = r16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
+    __syncthreads();
+    if (tid < 256) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWoWaves; ++w) sum += red[w][tid];
+        const int l = tid >> 2, r = tid & 3;
+        const int64_t m = 4 * (l >> 4) + r, nn = n0 + (l & 15);
+        if (m < M && nn < N) p.y[m * p.ldy + nn] = (uint16_t)f32_to_bf16_rne(sum * gres);
+    }
+}
+
+hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
+{
+    dim3 grid((unsigned)((p.n + 15) / 16));
+    const bool split = !exact_in_bf16(p.fw);
+    if (p.block == 16) {
+        if (split) hipLaunchKernelGGL((k_wo_gemm<16, true>), grid, dim3(kWoThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<16, false>), grid, dim3(kWoThreads), 0, s, p);
+    } else {
+        if (split) hipLaunchKernelGGL((k_wo_gemm<32, true>), grid, dim3(kWoThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<32, false>), grid, dim3(kWoThreads), 0, s, p);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace fp4

@@ -178,7 +178,8 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * LDS and runs on the bf16/f16 matrix cores.  Result within
  * 1e-5 * sum_k |a||b| of the exact product before the bf16 rounding.
  * K % 128 == 0, M and N arbitrary; ldc >= N; c 2-byte aligned (rows that
- * are 8-byte aligned are written with vector stores).
+ * are 8-byte aligned are written with vector stores); operand codes 16-byte
+ * and scales 4-byte aligned.
  */
 FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64_t ldc, void* stream);
 
@@ -188,7 +189,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * in registers (quant_prune_distill/574 "Метод"/"Эксперименты":
  * weight-only NVFP4, memory-bound small-batch generation).
  * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
- * 1 <= M <= 16; K % 256 == 0; ldx % 8 == 0, ldy >= N.
+ * 1 <= M <= 16; K % 256 == 0; x 16-byte aligned, ldx % 8 == 0, ldy >= N;
+ * w's codes 16-byte and scales 4-byte aligned.
  */
 FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
                        int64_t ldy, void* stream);

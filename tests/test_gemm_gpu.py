@@ -146,3 +146,44 @@ def test_llama_shapes_sampled_rows(fmt, block, wname):
     rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([rng.integers(0, 8192, 40), [0, 255, 256, 8191]]))
     _check_gemm(c, a, w, rows=rows, tag=f"llama {wname} {fmt}")
+
+
+# ---------------------------------------------------------------------------
+# weight-only GEMM
+# ---------------------------------------------------------------------------
+def _check_wo(y_gpu, x_bits, w_hat, tag=""):
+    xf = inputs.bf16_bits_to_f32(x_bits).astype(np.float64)
+    _check_gemm(y_gpu, xf, w_hat, tag=tag)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 16])
+@pytest.mark.parametrize("n,k", [(100, 256), (16, 512), (33, 1024)])
+def test_wo_gemm_small(m, n, k):
+    qw, w = _quant_both(_normal(n, k, 11, 0.02, dtype="bf16"), 16, "e4m3")
+    x = _normal(m, k, 12, dtype="bf16")
+    y = fq.fp4_wo_gemm(to_device(x), qw)
+    torch.cuda.synchronize()
+    _check_wo(y, x, w, tag=f"wo {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("ue5m3", 16), ("e7m0", 16), ("e1m6", 32)])
+def test_wo_gemm_formats(fmt, block):
+    qw, w = _quant_both(_normal(48, 512, 13, 0.02, dtype="bf16"), block, fmt)
+    x = _normal(5, 512, 14, dtype="bf16")
+    y = fq.fp4_wo_gemm(to_device(x), qw)
+    torch.cuda.synchronize()
+    _check_wo(y, x, w, tag=f"wo {fmt}/{block}")
+
+
+@pytest.mark.parametrize("wname", ["up", "down"])
+def test_wo_gemm_qwen_decode_shapes(wname):
+    """Qwen-2.5 decode shapes: W [18944, 3584] / [3584, 18944] NVFP4 E4M3
+    block 16, X [M, K] for M in {1, 8, 16}; every output checked."""
+    xw = inputs.decode_weight(wname)
+    qw, w = _quant_both(xw, 16, "e4m3")
+    k = w.shape[1]
+    for m in (1, 8, 16):
+        x = inputs.decode_x(m, k)
+        y = fq.fp4_wo_gemm(to_device(x), qw)
+        torch.cuda.synchronize()
+        _check_wo(y, x, w, tag=f"qwen {wname} m={m}")
