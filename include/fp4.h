@@ -20,8 +20,8 @@
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller (e.g. torch
  *     tensors).  The library never allocates or frees caller memory and
- *     allocates nothing per call; an fp4_amax_state owns 16 bytes of device
- *     memory allocated at creation.
+ *     allocates nothing per call; an fp4_amax_state owns 1280 bytes of
+ *     device memory allocated at creation.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch is asynchronous on it; no call synchronizes the host
  *     except fp4_amax_state_get / fp4_amax_state_set.
@@ -108,9 +108,9 @@ typedef struct fp4_tensor {
 
 /* Per-tensor amax state (ue5m3-fp4-pretraining "Что сделали": the maximum
  * is refreshed every `interval` steps and the stored value used between).
- * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 16
+ * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 1280
  * bytes of device memory on the device current at creation: the stored
- * amax and the reduction's workspace.  Not thread-safe; calls that use one
+ * amax and the reduction's per-workgroup partial maxima.  Not thread-safe; calls that use one
  * state must be ordered (one stream, or synchronized). */
 typedef struct fp4_amax_state fp4_amax_state;
 
