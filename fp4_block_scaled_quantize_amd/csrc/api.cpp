@@ -256,6 +256,8 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
+    // the kernel addresses W and x with 32-bit byte/element offsets
+    if (w->rows * (w->cols / 2) >= (int64_t(1) << 32) || ldx * m >= (int64_t(1) << 31)) return FP4_ERR_UNSUPPORTED;
     if (!aligned16(x) || ldx % 8) return FP4_ERR_ALIGN;
     if (w->rows == 0) return FP4_OK;
     if (!aligned16(w->q) || ((uintptr_t)w->scales & 3u)) return FP4_ERR_ALIGN;

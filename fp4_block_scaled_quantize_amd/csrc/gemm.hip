@@ -808,83 +808,187 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // fixed order (deterministic).
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
-constexpr int kWoWaves = 8;
-constexpr int kWoThreads = 64 * kWoWaves;
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-template <int BLOCK, bool SPLIT>
-__global__ __launch_bounds__(kWoThreads) void k_wo_gemm(WoGemmLaunch p)
+// Exact bf16 dequantization of one dword of 8 E2M1 codes with scale s.  The
+// gfx950 converts apply only the exponent of their scale operand, so:
+//  POW2 (E8M0 scales): v_cvt_scalef32_pk_bf16_fp4 with s does everything;
+//  otherwise: convert with scale 1 to fp32, multiply by s (exact: at most
+//  9 significant bits), keep the top half (exact when the value fits bf16).
+template <bool POW2>
+__device__ __forceinline__ v4i dq8_bf16(uint32_t w, float s)
 {
-    __shared__ float red[kWoWaves][256];
+    v4i r;
+    if (POW2) {
+        r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+        r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+        r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+        r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            v2f f = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                  : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                  : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+            const uint32_t lo = __float_as_uint(f[0] * s), hi = __float_as_uint(f[1] * s);
+            r[b] = (int)__builtin_amdgcn_perm(hi, lo, 0x07060302u);     // {hi[31:16], lo[31:16]}
+        }
+    }
+    return r;
+}
+
+// E1M6 products need 9 significant bits: split v = hi + lo, both exact bf16.
+__device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i& lo)
+{
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v2f f = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+              : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+              : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        const float v0 = f[0] * s, v1 = f[1] * s;
+        const uint32_t h0 = __float_as_uint(v0) & 0xFFFF0000u, h1 = __float_as_uint(v1) & 0xFFFF0000u;
+        const float l0 = v0 - __uint_as_float(h0), l1 = v1 - __uint_as_float(h1);
+        hi[b] = (int)((h0 >> 16) | h1);
+        lo[b] = (int)((__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u));
+    }
+}
+
+template <int NW, int BLOCK, bool SPLIT, bool POW2>
+__global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
+{
+    constexpr int U = 8;                      // 128-element chunks per batch; two batches of W in flight
+    __shared__ float red[NW][256];
+    __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, grp = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t N = p.n, K = p.k, M = p.m;
-    const int64_t n = n0 + r16;
-    const bool nvalid = n < N;
-    const bool mvalid = r16 < M;
+    const int64_t n = n0 + r16 < N ? n0 + r16 : N - 1;        // rows past N re-read the last row
     const int64_t rowb = K / 2, rows = K / BLOCK;
     const ScaleFmt fw{p.fw.ebits, p.fw.mbits, p.fw.bias, p.fw.maxcode, p.fw.smax, p.fw.is_e8m0};
     const float gw = p.gw[0];
     const float pw = split_pow2(gw);
     const float gres = gw / pw;
-    const uint8_t* wrow = p.qw + (nvalid ? n : 0) * rowb;
-    const uint8_t* srow = p.sw + (nvalid ? n : 0) * rows;
-    const uint16_t* xrow = p.x + (mvalid ? r16 : 0) * p.ldx;
+    for (int c = tid; c < 256; c += 64 * NW) sdec[c] = scale_decode_any((uint32_t)c, fw) * pw;
+    // 32-bit byte / element offsets from the operand bases (the ABI bounds W below 4 GiB)
+    const uint32_t woff = (uint32_t)(n * rowb) + 16u * grp;
+    const uint32_t soff = (uint32_t)(n * rows) + (BLOCK == 16 ? 2u * grp : (uint32_t)grp);
+    const bool mvalid = r16 < M;
+    const uint32_t xoff = (uint32_t)((mvalid ? r16 : 0) * p.ldx) + 32u * grp;
     const int nchunks = (int)(K / 128);
+    const int mine = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;   // chunks wave, wave + NW, ...
+    const int nb = (mine + U - 1) / U;
+    __syncthreads();
+
+    struct Batch { v4i w[U]; uint32_t sc[U]; };
+    // raw loads only: anything computed from a loaded value at load time would
+    // make the compiler wait for it before the MFMAs of the batch in progress
+    auto load_w = [&](int b, Batch& bt) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = b * U + u < mine ? b * U + u : mine - 1;             // clamped: always in bounds
+            const uint32_t kc = (uint32_t)(wave + i * NW);
+            bt.w[u] = *reinterpret_cast<const v4i*>(p.qw + woff + kc * 64u);
+            bt.sc[u] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff + kc * 8u)
+                                   : (uint32_t)p.sw[soff + kc * 4u];
+        }
+    };
+    // rows m >= M keep whatever their registers hold: they only feed output
+    // rows that are never stored
+    auto load_x = [&](int i, v4i (&x)[4]) {
+        const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
+        if (mvalid) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[t] = *reinterpret_cast<const v4i*>(p.x + xoff + kc * 128u + 8u * t);
+        }
+    };
 
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int kc = wave; kc < nchunks; kc += kWoWaves) {
-        const int64_t kel = (int64_t)kc * 128 + 32 * grp;      // first K element of this lane's 32
-        v4i wq = nvalid ? *reinterpret_cast<const v4i*>(wrow + kel / 2) : v4i{0, 0, 0, 0};
-        uint32_t sc = 0;
-        if (nvalid) sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow + kel / 16)
-                                     : (uint32_t)srow[kel / 32];
-        v4i xv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            xv[t] = mvalid ? *reinterpret_cast<const v4i*>(xrow + kel + 8 * t) : v4i{0, 0, 0, 0};
-        const float s0 = scale_decode_any(sc & 0xFFu, fw) * pw;
-        const float s1 = BLOCK == 16 ? scale_decode_any((sc >> 8) & 0xFFu, fw) * pw : s0;
-        uint32_t wb[16], wl[16];
-        if (SPLIT) dequant32_split(wq, s0, s1, wb, wl);
-        else dequant32<false>(wq, s0, s1, wb);
+    auto chunk = [&](const v4i& w, uint32_t sc, const v4i (&x)[4]) {
+        const float s0 = sdec[sc & 0xFFu];
+        const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const v4i wt = v4i{(int)wb[4 * t], (int)wb[4 * t + 1], (int)wb[4 * t + 2], (int)wb[4 * t + 3]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xv[t]), __builtin_bit_cast(v8bf, wt),
-                                                          acc, 0, 0, 0);
+            const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
             if (SPLIT) {
-                const v4i wlt = v4i{(int)wl[4 * t], (int)wl[4 * t + 1], (int)wl[4 * t + 2], (int)wl[4 * t + 3]};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xv[t]),
-                                                              __builtin_bit_cast(v8bf, wlt), acc, 0, 0, 0);
+                v4i hi, lo;
+                dq8_bf16_split((uint32_t)w[t], st, hi, lo);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                                                              __builtin_bit_cast(v8bf, hi), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                                                              __builtin_bit_cast(v8bf, lo), acc, 0, 0, 0);
+            } else {
+                const v4i wt = dq8_bf16<POW2>((uint32_t)w[t], st);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                                                              __builtin_bit_cast(v8bf, wt), acc, 0, 0, 0);
             }
         }
+    };
+    v4i xa[4] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+    v4i xb[4] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+    auto process = [&](int b, const Batch& bt) {
+        load_x(b * U, xa);
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            const int i = b * U + u;
+            load_x(i + 1, xb);
+            if (i < mine) chunk(bt.w[u], bt.sc[u], xa);
+            load_x(i + 2, xa);
+            if (i + 1 < mine) chunk(bt.w[u + 1], bt.sc[u + 1], xb);
+        }
+    };
+
+    Batch A, B;
+    if (nb > 0) load_w(0, A);
+    if (nb > 1) load_w(1, B);
+    for (int b = 0; b < nb; b += 2) {
+        process(b, A);
+        if (b + 2 < nb) load_w(b + 2, A);
+        if (b + 1 < nb) {
+            process(b + 1, B);
+            if (b + 3 < nb) load_w(b + 3, B);
+        }
     }
-    // acc[r] = D[m = 4 grp + r][n = r16]
+    // acc[r] = D[m = 4 grp + r][n = r16]; fixed-order sum over the waves
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
     __syncthreads();
     if (tid < 256) {
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWoWaves; ++w) sum += red[w][tid];
+        for (int w = 0; w < NW; ++w) sum += red[w][tid];
         const int l = tid >> 2, r = tid & 3;
         const int64_t m = 4 * (l >> 4) + r, nn = n0 + (l & 15);
         if (m < M && nn < N) p.y[m * p.ldy + nn] = (uint16_t)f32_to_bf16_rne(sum * gres);
     }
 }
 
+template <int NW>
+static void launch_wo_nw(const WoGemmLaunch& p, hipStream_t s)
+{
+    dim3 grid((unsigned)((p.n + 15) / 16)), block(64 * NW);
+    const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
+    if (p.block == 16) {
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, 16, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, 16, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, 16, false, false>), grid, block, 0, s, p);
+    } else {
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, 32, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, 32, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, 32, false, false>), grid, block, 0, s, p);
+    }
+}
+
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
-    dim3 grid((unsigned)((p.n + 15) / 16));
-    const bool split = !exact_in_bf16(p.fw);
-    if (p.block == 16) {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<16, true>), grid, dim3(kWoThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<16, false>), grid, dim3(kWoThreads), 0, s, p);
-    } else {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<32, true>), grid, dim3(kWoThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<32, false>), grid, dim3(kWoThreads), 0, s, p);
-    }
+    // waves per workgroup split K; short rows use fewer so each wave keeps
+    // several 128-element chunks to stream
+    const int64_t chunks = p.k / 128;
+    if (chunks >= 48) launch_wo_nw<8>(p, s);
+    else launch_wo_nw<4>(p, s);
     return hipGetLastError();
 }
 
