@@ -109,7 +109,7 @@ fp4_status fp4_amax_state_get(const fp4_amax_state* st, uint64_t* calls, float* 
     if (hipMemcpy(&h, st->dev, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return FP4_ERR_HIP;
     *calls = st->calls;
     *amax = h.stored;
-    return FP4_OK;
+    return h.error ? FP4_ERR_HIP : FP4_OK;
 }
 
 fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
@@ -165,10 +165,6 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     bool refresh = false;
     if (pol != FP4_AMAX_NONE) {
         refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
-        if (refresh) {
-            st = hip_status(launch_amax(x, x_dtype == FP4_DTYPE_BF16, out->rows, out->cols, ld_x, state->dev, s));
-            if (st != FP4_OK) return st;
-        }
         src = state->dev;
     }
     QuantLaunch p;

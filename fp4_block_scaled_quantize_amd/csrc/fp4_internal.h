@@ -16,16 +16,26 @@ struct ScaleFmtHost {
 // Fill the parameters of a block-scale format (fp4_scale_fmt value).
 bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 
-// Device workspace of an amax state.  A refresh writes one partial maximum
-// per workgroup of the amax kernel (no atomics, no fences); the quantize
-// kernel of the same call reduces them and stores the result in `stored`,
-// which calls between refreshes read.
+// Device workspace of an amax state.
+//  - partial/stored: the two-kernel refresh (tensors larger than the fused
+//    path holds in registers) writes one partial maximum per workgroup of
+//    the amax kernel; the quantize kernel of the same call reduces them and
+//    stores the result in `stored`, which calls between refreshes read.
+//  - epoch/slot: the single-pass refresh exchanges per-workgroup maxima
+//    through `slot` (64-bit {epoch, max bits} words) within one launch;
+//    `epoch` advances once per such launch, on the device.
+//  - error: set when a single-pass exchange timed out.
 constexpr int kAmaxParts = 256;
+constexpr int kXchgSlots = 256;
 struct AmaxDev {
     float partial[kAmaxParts];
     float stored;
-    uint32_t pad[63];
+    uint32_t epoch;
+    uint32_t error;
+    uint32_t pad[61];
+    uint64_t slot[kXchgSlots];
 };
+static_assert(sizeof(AmaxDev) == 3328, "amax state layout");
 
 struct QuantLaunch {
     const void* x;
@@ -35,7 +45,7 @@ struct QuantLaunch {
     uint8_t* scales;
     float* tensor_scale;       // out: {g, amax}
     AmaxDev* amax_src;         // null: no tensor scale (g = 1)
-    int32_t refresh;           // amax_src->partial holds this call's maximum
+    int32_t refresh;           // compute this call's maximum (else read amax_src->stored)
     int32_t block;
     int32_t stochastic;
     uint64_t seed, offset;
@@ -54,8 +64,6 @@ struct DequantLaunch {
     int64_t ld;
 };
 
-hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols, int64_t ld, AmaxDev* dst,
-                       hipStream_t s);
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);
 hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s);
 

@@ -16,6 +16,8 @@
 // contraction, in the order the C ABI documents.
 #include <float.h>
 
+#include <atomic>
+
 #include "fp4_device.hpp"
 #include "fp4_internal.h"
 
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* __restrict__ 
     }
 }
 
-hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols, int64_t ld, AmaxDev* dst,
+static hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols, int64_t ld, AmaxDev* dst,
                        hipStream_t s)
 {
     const uint32_t upr = (uint32_t)(cols / 8);
@@ -192,6 +194,12 @@ hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols
 // ---------------------------------------------------------------------------
 constexpr int kQThreads = 256;
 constexpr int kQUnroll = 4;                  // units per lane (one load each, all in flight)
+// Single-pass refresh: one 1024-thread workgroup per CU holds up to
+// kFUnroll units per lane in registers while the grid agrees on the tensor
+// maximum, so the input is read once.
+constexpr int kFThreads = 1024;
+constexpr int kFUnroll = 8;
+constexpr uint64_t kXchgTimeoutTicks = 20000000;   // 0.2 s of the 100 MHz real-time counter
 
 struct QArgs {
     const void* x;
@@ -219,6 +227,79 @@ __device__ __forceinline__ float tensor_amax(const QArgs& a)
     float m = __builtin_fmaxf(__builtin_fmaxf(p.x, p.y), __builtin_fmaxf(p.z, p.w));
     for (int o = 32; o > 0; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
     return m;
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t m)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)m, o, 64);
+        m = m > t ? m : t;
+    }
+    return m;
+}
+
+// Tensor maximum (as binary32 bits) agreed by every workgroup of a
+// single-pass launch.  Each workgroup publishes {epoch, its maximum} as one
+// 64-bit word in its own slot with a relaxed agent-scope atomic store; wave
+// 0 of every workgroup then polls all slots until each carries this
+// launch's epoch.  Flag and value share a word, so single-location
+// coherence suffices and no fence (L2 write-back or invalidate) is needed.
+// The epoch is read from the state at the start and advanced by workgroup 0
+// once it has seen every slot, i.e. after every workgroup has read it, so
+// each launch (graph replays included) gets a fresh epoch.  The launch
+// grid never exceeds one workgroup per CU, so all workgroups are resident
+// together; the poll is still bounded in time and a timeout sets the
+// state's error word instead of hanging.
+// The epoch of this launch: read at the start of the kernel (before any
+// slot of this launch is published), so the read overlaps the data loads.
+__device__ __forceinline__ uint32_t launch_epoch(const AmaxDev* st)
+{
+    uint32_t e = __hip_atomic_load(&st->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    return e == 0 ? 1u : e;
+}
+
+template <int T>
+__device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
+{
+    __shared__ uint32_t wmax[T / 64];
+    __shared__ uint32_t gmax;
+    const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    m = wave_umax(m);
+    if (lane == 0) wmax[wv] = m;
+    __syncthreads();
+    if (wv == 0) {
+        const uint32_t mm = wave_umax(lane < T / 64 ? wmax[lane] : 0u);
+        if (lane == 0)
+            __hip_atomic_store(&st->slot[blockIdx.x], ((uint64_t)e << 32) | mm, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t nwg = gridDim.x;
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        uint32_t tm = 0;
+        bool done = false;
+        for (;;) {
+            tm = 0;
+            bool mine = true;
+            for (uint32_t i = lane; i < nwg; i += 64) {
+                const uint64_t w = __hip_atomic_load(&st->slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                mine = mine && (uint32_t)(w >> 32) == e;
+                tm = tm > (uint32_t)w ? tm : (uint32_t)w;
+            }
+            if (__all(mine)) {
+                done = true;
+                break;
+            }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kXchgTimeoutTicks) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        tm = wave_umax(tm);
+        if (lane == 0) {
+            if (!done) __hip_atomic_store(&st->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (blockIdx.x == 0) __hip_atomic_store(&st->epoch, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gmax = tm;
+        }
+    }
+    __syncthreads();
+    return gmax;
 }
 
 // Tensor scale g = amax_t / RN(6 Smax); 1 when there is no tensor scale or
@@ -256,19 +337,26 @@ __device__ __forceinline__ float quad_bcast(float v)
                                                    false));
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED>
-__global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
+// FUSED: single-pass refresh (the tensor maximum of this call is agreed
+// across the grid while the units stay in registers); otherwise the maximum
+// comes from the amax kernel's partials (refresh) or the stored value.
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED>
+__global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArgs a)
 {
-    constexpr int U = kQUnroll;
+    constexpr int T = FUSED ? kFThreads : kQThreads;
+    constexpr int U = FUSED ? kFUnroll : kQUnroll;
     constexpr int G = BLOCK / 8;                 // lanes per block (2 or 4)
     constexpr int PER = U / G;                   // block scales computed per lane
     static_assert(U % G == 0, "every lane of a block group computes U/G scales");
+    static_assert(!(FUSED && E8M0), "E8M0 has no tensor scale");
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t sub = lane & (G - 1);
-    const uint32_t wave = blockIdx.x * (kQThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.x * (T / 64) + (threadIdx.x >> 6);
     const uint32_t base = wave * (64u * U);
 
     // issue every load first
+    uint32_t epoch = 0;                          // used by wave 0 only
+    if (FUSED && a.amax_src && threadIdx.x < 64) epoch = launch_epoch(a.amax_src);
     Unit<InT> un[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -277,9 +365,26 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
         else un[j].zero();
     }
 
+    // block maxima, reduced over the G lanes of each block (independent of
+    // the tensor scale)
+    float bm[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        bm[j] = __uint_as_float(dpp_umax_xor1(un[j].absmax()));
+        if (G == 4) bm[j] = __uint_as_float(dpp_umax_xor2(__float_as_uint(bm[j])));
+    }
+
     float g = 1.0f, d = 6.0f;
     if (!E8M0 && a.amax_src) {
-        const float am = tensor_amax(a);
+        float am;
+        if (FUSED) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < U; ++j) m = m > __float_as_uint(bm[j]) ? m : __float_as_uint(bm[j]);
+            am = __uint_as_float(grid_amax_bits<T>(m, epoch, a.amax_src));
+        } else {
+            am = tensor_amax(a);
+        }
         g = tensor_scale_of(am, a);
         d = 6.0f * g;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -290,16 +395,6 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
     } else if (blockIdx.x == 0 && threadIdx.x == 0) {
         a.tensor_scale[0] = 1.0f;
         a.tensor_scale[1] = 0.0f;
-    }
-
-    // block maxima, reduced over the G lanes of each block
-    float v[U][8];
-    float bm[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-        un[j].get(v[j]);
-        bm[j] = __uint_as_float(dpp_umax_xor1(un[j].absmax()));
-        if (G == 4) bm[j] = __uint_as_float(dpp_umax_xor2(__float_as_uint(bm[j])));
     }
 
     // lane `sub` of a group computes the scales of blocks j = sub*PER + t
@@ -341,8 +436,10 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const uint32_t u = base + j * 64 + lane;
+        float v[8];
+        un[j].get(v);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[j][k] = v[j][k] * inv[j];
+        for (int k = 0; k < 8; ++k) v[k] = v[k] * inv[j];
         uint32_t packed;
         if (SR) {
             U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
@@ -351,37 +448,53 @@ __global__ __launch_bounds__(kQThreads) void k_quantize(QArgs a)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                packed |= e2m1_sr(v[j][k], r16) << (4 * k);
+                packed |= e2m1_sr(v[k], r16) << (4 * k);
             }
         } else {
-            packed = FP4_CVT_PK(0u, v[j][0], v[j][1], 0);
-            packed = FP4_CVT_PK(packed, v[j][2], v[j][3], 1);
-            packed = FP4_CVT_PK(packed, v[j][4], v[j][5], 2);
-            packed = FP4_CVT_PK(packed, v[j][6], v[j][7], 3);
+            packed = FP4_CVT_PK(0u, v[0], v[1], 0);
+            packed = FP4_CVT_PK(packed, v[2], v[3], 1);
+            packed = FP4_CVT_PK(packed, v[4], v[5], 2);
+            packed = FP4_CVT_PK(packed, v[6], v[7], 3);
         }
         if (u < a.nunits) __builtin_nontemporal_store(packed, a.q + u);
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0>
-static void launch_q4(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED>
+static void launch_q5(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
 {
+    const dim3 t(FUSED ? kFThreads : kQThreads);
     if (strided)
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true>), dim3(blocks), dim3(kQThreads), 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED>), dim3(blocks), t, 0, s, a);
     else
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false>), dim3(blocks), dim3(kQThreads), 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED>), dim3(blocks), t, 0, s, a);
 }
 
 template <typename InT, int BLOCK>
-static void launch_q3(const QArgs& a, bool sr, bool e8, bool strided, uint32_t blocks, hipStream_t s)
+static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, uint32_t blocks, hipStream_t s)
 {
     if (sr) {
-        if (e8) launch_q4<InT, BLOCK, true, true>(a, strided, blocks, s);
-        else launch_q4<InT, BLOCK, true, false>(a, strided, blocks, s);
+        if (fused) launch_q5<InT, BLOCK, true, false, true>(a, strided, blocks, s);
+        else if (e8) launch_q5<InT, BLOCK, true, true, false>(a, strided, blocks, s);
+        else launch_q5<InT, BLOCK, true, false, false>(a, strided, blocks, s);
     } else {
-        if (e8) launch_q4<InT, BLOCK, false, true>(a, strided, blocks, s);
-        else launch_q4<InT, BLOCK, false, false>(a, strided, blocks, s);
+        if (fused) launch_q5<InT, BLOCK, false, false, true>(a, strided, blocks, s);
+        else if (e8) launch_q5<InT, BLOCK, false, true, false>(a, strided, blocks, s);
+        else launch_q5<InT, BLOCK, false, false, false>(a, strided, blocks, s);
     }
+}
+
+// Compute units of a device (cached; every thread computes the same value).
+static int device_cus(int dev)
+{
+    static std::atomic<int> cache[64];
+    if (dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
@@ -401,16 +514,38 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.key1 = (uint32_t)(p.seed >> 32);
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
-    const uint32_t per_block = kQThreads * kQUnroll;
-    uint32_t blocks = (a.nunits + per_block - 1) / per_block;
-    if (blocks == 0) blocks = 1;
     const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols;
+
+    // A refresh reads the input once when the whole tensor fits the
+    // single-pass grid (at most one workgroup per CU, kFUnroll units per
+    // lane); larger tensors take the amax kernel and a second read.
+    bool fused = false;
+    uint32_t blocks;
+    if (a.amax_src && a.refresh && !e8) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+        const int cus = device_cus(dev);
+        const uint32_t per_wg = kFThreads * kFUnroll;
+        const uint32_t max_wg = (uint32_t)(cus < kXchgSlots ? cus : kXchgSlots);
+        blocks = (a.nunits + per_wg - 1) / per_wg;
+        if (blocks == 0) blocks = 1;
+        fused = blocks <= max_wg;
+        if (!fused) {
+            hipError_t e = launch_amax(p.x, p.x_bf16, p.rows, p.cols, p.ld, p.amax_src, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    if (!fused) {
+        const uint32_t per_block = kQThreads * kQUnroll;
+        blocks = (a.nunits + per_block - 1) / per_block;
+        if (blocks == 0) blocks = 1;
+    }
     if (p.x_bf16) {
-        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, strided, blocks, s);
-        else launch_q3<uint16_t, 32>(a, sr, e8, strided, blocks, s);
+        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, blocks, s);
+        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, blocks, s);
     } else {
-        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, strided, blocks, s);
-        else launch_q3<float, 32>(a, sr, e8, strided, blocks, s);
+        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, blocks, s);
+        else launch_q3<float, 32>(a, sr, e8, fused, strided, blocks, s);
     }
     return hipGetLastError();
 }

@@ -168,6 +168,98 @@ def test_amax_state_checkpoint_resume():
         assert_bytes_equal(host(qt.q), outs[t], f"resume call {t}")
 
 
+def test_refresh_paths_see_the_whole_tensor():
+    """The tensor maximum of a refresh must cover every element whichever
+    path computes it: the single-pass kernel (tensor held in registers,
+    maximum agreed across the grid) up to 4096x4096 bf16 on a 256-CU device,
+    the amax kernel plus a second read beyond.  The maximum sits in the
+    first, a middle or the last unit; codes and scales are compared on
+    sampled rows."""
+    rng = np.random.default_rng(7)
+    for rows, where in [(4096, "last"), (4096, "first"), (4104, "last"), (4104, "mid"), (24, "last")]:
+        x = _sweep_like(rows, 4096, 77 + rows)
+        r, c = {"first": (0, 0), "mid": (rows // 2, 2049), "last": (rows - 1, 4095)}[where]
+        x[r, c] = inputs.f32_to_bf16_bits(np.array([-9216.0], dtype=np.float32))[0]
+        st = fq.AmaxState(1)
+        qt = fq.fp4_quantize(to_device(x), 16, "e4m3", amax="current", state=st)
+        torch.cuda.synchronize()
+        a = oracle.amax(x)
+        g = oracle.tensor_scale(a, "e4m3")
+        assert a == np.float32(9216.0)
+        assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{rows} {where} tensor_scale")
+        sample = sorted(set(rng.integers(0, rows, 12).tolist()) | {0, r, rows - 1})
+        for i in sample:
+            q, s_ = oracle.quantize(x, 16, "e4m3", g, rows=(i, i + 1))
+            assert_bytes_equal(host(qt.q[i:i + 1]), q, f"{rows} {where} row {i} codes")
+            assert_bytes_equal(host(qt.scales[i:i + 1]), s_, f"{rows} {where} row {i} scales")
+        st.get()                       # raises if a grid exchange timed out
+
+
+def test_current_repeated_calls_one_state():
+    """Many current-amax calls through one state, with grids of different
+    sizes in turn (1, 3 and 64 workgroups of the single-pass kernel): every
+    call's tensor scale comes from its own tensor, never from a slot left by
+    an earlier call."""
+    st = fq.AmaxState(1)
+    shapes = [(16, 256), (512, 384), (2048, 2048), (8, 64)]
+    for t in range(40):
+        rows, cols = shapes[t % len(shapes)]
+        x = _sweep_like(rows, cols, 3000 + t)
+        # the maximum alternates between large and small so stale values show
+        scale = np.float32(1000.0 if t % 2 else 0.001)
+        x = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x) * scale)
+        qt = fq.fp4_quantize(to_device(x), 16, "ue5m3", amax="current", state=st)
+        torch.cuda.synchronize()
+        q, s_, g, a = oracle.quantize_tensor(x, 16, "ue5m3", "current", nthreads=8)
+        assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"call {t} ts")
+        assert_bytes_equal(host(qt.scales), s_, f"call {t} scales")
+        assert_bytes_equal(host(qt.q), q, f"call {t} codes")
+    calls, amax = st.get()
+    assert calls == 40
+
+
+def test_current_amax_under_graph_replay():
+    """Current-amax quantize calls captured once in a HIP graph and replayed
+    with new input values each time (eager copies and synchronizations in
+    between): every replay agrees with the oracle."""
+    st = fq.AmaxState(1)
+    shapes = [(64, 512), (1024, 1024)]
+    xs = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    outs = [fq.QTensor.empty(r, c, 16, "e4m3") for r, c in shapes]
+    for x in xs:
+        x.zero_()
+
+    def record():
+        for x, o in zip(xs, outs):
+            fq.fp4_quantize(x, 16, "e4m3", amax="current", state=st, out=o)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        record()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        record()
+    torch.cuda.synchronize()
+    for rep in range(5):
+        hosts = []
+        for i, (r, c) in enumerate(shapes):
+            h = _sweep_like(r, c, 4000 + 10 * rep + i)
+            h = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(h) * np.float32(10.0 ** (rep - 2)))
+            xs[i].copy_(to_device(h))
+            hosts.append(h)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, h in enumerate(hosts):
+            q, s_, g, a = oracle.quantize_tensor(h, 16, "e4m3", "current", nthreads=8)
+            assert_bytes_equal(f32_bits(host(outs[i].tensor_scale)), f32_bits([g, a]), f"replay {rep}.{i} ts")
+            assert_bytes_equal(host(outs[i].scales), s_, f"replay {rep}.{i} scales")
+            assert_bytes_equal(host(outs[i].q), q, f"replay {rep}.{i} codes")
+    st.get()
+
+
 def test_edge_values():
     """Zeros, signed zeros, exact E2M1 midpoints, saturation, subnormals,
     single-outlier blocks and scales that underflow/saturate (E1M6)."""
