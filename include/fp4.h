@@ -20,7 +20,7 @@
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller (e.g. torch
  *     tensors).  The library never allocates or frees caller memory and
- *     allocates nothing per call; an fp4_amax_state owns 1280 bytes of
+ *     allocates nothing per call; an fp4_amax_state owns 3328 bytes of
  *     device memory allocated at creation.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch is asynchronous on it; no call synchronizes the host
@@ -108,9 +108,10 @@ typedef struct fp4_tensor {
 
 /* Per-tensor amax state (ue5m3-fp4-pretraining "Что сделали": the maximum
  * is refreshed every `interval` steps and the stored value used between).
- * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 1280
+ * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 3328
  * bytes of device memory on the device current at creation: the stored
- * amax and the reduction's per-workgroup partial maxima.  Not thread-safe; calls that use one
+ * amax, the per-workgroup partial maxima of the refresh and the exchange
+ * words of the single-pass refresh.  Not thread-safe; calls that use one
  * state must be ordered (one stream, or synchronized). */
 typedef struct fp4_amax_state fp4_amax_state;
 
@@ -118,7 +119,11 @@ typedef struct fp4_amax_state fp4_amax_state;
 FP4_API fp4_status fp4_amax_state_create(uint32_t interval, fp4_amax_state** out);
 FP4_API fp4_status fp4_amax_state_destroy(fp4_amax_state* state);
 /* Checkpoint: number of quantize calls seen and the stored amax.  Waits for
- * the device to finish outstanding work. */
+ * the device to finish outstanding work.  Returns FP4_ERR_HIP if a
+ * single-pass refresh of this state ever timed out waiting for the other
+ * workgroups of its grid (possible only if other work kept them from being
+ * scheduled for 0.2 s); that call's tensor scale is then not reliable.
+ * fp4_amax_state_set clears the condition. */
 FP4_API fp4_status fp4_amax_state_get(const fp4_amax_state* state, uint64_t* calls, float* amax);
 /* Resume: overwrite the call count and stored amax (synchronous copy). */
 FP4_API fp4_status fp4_amax_state_set(fp4_amax_state* state, uint64_t calls, float amax);
@@ -149,7 +154,11 @@ FP4_API fp4_status fp4_amax_state_set(fp4_amax_state* state, uint64_t calls, flo
  * recomputes amax_t on every call; DELAYED recomputes it when
  * state->calls % interval == 0 and otherwise reuses the stored value (a
  * tensor that outgrew it saturates at +-6).  Each call increments the
- * state's call count on the host (no device synchronization).
+ * state's call count on the host (no device synchronization).  A refresh
+ * reads x once when the tensor fits one workgroup per compute unit at 8192
+ * units of 8 elements each (4096 x 4096 on a 256-CU device; the
+ * workgroups agree on amax_t through the state), else twice (an amax pass,
+ * then the quantize pass).
  * seed, offset: used only for FP4_ROUND_STOCHASTIC.
  * Errors: INVALID_ARG (null pointers, bad enums, missing state), SHAPE,
  * ALIGN, UNSUPPORTED (E8M0 with a tensor-scale policy).
