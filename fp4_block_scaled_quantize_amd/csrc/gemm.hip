@@ -761,6 +761,185 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
     store_tile(acc, g, p.c, p.ldc, m_base + wm * 128, n_base + wn * 128, M, N);
 }
 
+// ---------------------------------------------------------------------------
+// f16 path (scale formats whose e2m1 * s products are exact in f16: E4M3,
+// E3M4, E2M5, E1M6 -- NVFP4 is E4M3 at block 16).  The stages hold FP4
+// codes and raw scale bytes, loaded straight into LDS as in k_gemm_mx4;
+// each wave converts its own fragments to f16 right before the matrix
+// instruction: the hardware FP4 -> f16 conversion (scale 1, exact) and one
+// packed f16 multiply by the block scale per two elements.  Eight waves
+// (2 x 4, 128 x 64 each) so one wave's conversions overlap the other's
+// matrix instructions on the same SIMD.
+//
+// K order inside a 128-element stage: lane half h of a 32x32x16 step (ks,
+// t) supplies elements 32 (2 ks + h) + 8 t + 0..7 of its row -- one 16-byte
+// fragment per lane and chunk.  The order is the same for both operands, so
+// every product pairs equal k.
+// ---------------------------------------------------------------------------
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+template <int BLOCK>
+struct NvStage {
+    static constexpr int kScaleRow = kMx3BK / BLOCK;           // scale bytes per row per stage
+    static constexpr int kScales = kTile * kScaleRow;          // per operand
+    static constexpr int kBytes = 2 * kMx3Codes + 2 * kScales;
+    static constexpr int kTable = 2 * 256 * 4;                 // f16x2 decode tables of W and A
+};
+
+// 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times
+// the f16 block scale s2 (replicated in both halves).
+__device__ __forceinline__ v8h nv_convert8(uint32_t w, v2h s2)
+{
+    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+template <int BLOCK, int NS>
+__global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
+{
+    using L = NvStage<BLOCK>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(smem + NS * L::kBytes);   // [2][256] f16x2
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int64_t M = p.m, N = p.n, K = p.k;
+    int tn, tm;
+    tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
+    const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
+    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const int KT = (int)(K / kMx3BK);
+
+    // scale code -> f16 (exact for these formats), replicated for packed math
+    {
+        const int t = tid & 255;
+        const ScaleFmtHost& fh = tid < 256 ? p.fb : p.fa;
+        const ScaleFmt f{fh.ebits, fh.mbits, fh.bias, fh.maxcode, fh.smax, fh.is_e8m0};
+        const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_decode_any((uint32_t)t, f));
+        tab[tid] = h | (h << 16);
+    }
+    __syncthreads();
+
+    const uint8_t* srcw[2];
+    const uint8_t* srca[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int r = 16 * (2 * wave + k) + (lane >> 2);
+        const int c = (lane & 3) ^ mx4_swz(r);
+        const int64_t nr = n_base + r < N ? n_base + r : N - 1;
+        const int64_t mr = m_base + r < M ? m_base + r : M - 1;
+        srcw[k] = p.qb + nr * rowb + 16 * c;
+        srca[k] = p.qa + mr * rowb + 16 * c;
+    }
+    // scales.  Block 16: 8 bytes per row and stage; DMA j (0: W, 1: A) of
+    // this wave fills dword 64 wave + lane = (row, half) of that operand.
+    // Block 32: 4 bytes per row; waves 0-3 fill W's rows, waves 4-7 A's.
+    constexpr int kSDma = BLOCK == 16 ? 2 : 1;
+    const uint8_t* srcs[kSDma];
+    int sdst[kSDma];
+    if (BLOCK == 16) {
+        const int q = 64 * wave + lane, r = q >> 1, d = q & 1;
+        srcs[0] = p.sb + (n_base + r < N ? n_base + r : N - 1) * rows + 4 * d;
+        srcs[kSDma - 1] = p.sa + (m_base + r < M ? m_base + r : M - 1) * rows + 4 * d;
+        sdst[0] = 2 * kMx3Codes + 256 * wave;
+        sdst[kSDma - 1] = 2 * kMx3Codes + L::kScales + 256 * wave;
+    } else {
+        const int r = 64 * (wave & 3) + lane;
+        srcs[0] = wave < 4 ? p.sb + (n_base + r < N ? n_base + r : N - 1) * rows
+                           : p.sa + (m_base + r < M ? m_base + r : M - 1) * rows;
+        sdst[0] = 2 * kMx3Codes + (wave < 4 ? 0 : L::kScales) + 256 * (wave & 3);
+    }
+
+    auto issue = [&](int kt, int buf) {
+        uint8_t* st = smem + buf * L::kBytes;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            dma16(srcw[k] + (int64_t)kt * kMx3RB, st + 1024 * (2 * wave + k));
+            dma16(srca[k] + (int64_t)kt * kMx3RB, st + kMx3Codes + 1024 * (2 * wave + k));
+        }
+#pragma unroll
+        for (int j = 0; j < kSDma; ++j) dma4(srcs[j] + (int64_t)kt * L::kScaleRow, st + sdst[j]);
+    };
+    constexpr int kLoads = 4 + kSDma;
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s < KT ? s : KT - 1, s);
+
+    const int frow = lane & 31, khalf = lane >> 5;
+    const uint32_t* tabw = tab;
+    const uint32_t* taba = tab + 256;
+    for (int kt = 0; kt < KT; ++kt) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
+        __builtin_amdgcn_s_barrier();
+        const int nxt = kt + NS - 1;
+        issue(nxt < KT ? nxt : KT - 1, nxt % NS);
+        const uint8_t* st = smem + (kt % NS) * L::kBytes;
+        const uint8_t* ssw = st + 2 * kMx3Codes;
+        const uint8_t* ssa = ssw + L::kScales;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 2 * ks + khalf;
+            v4i wf[4], af[2];
+            v2h sw[4][2], sa[2][2];          // [row block][t >> 1] (block 32: one scale per chunk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wn * 128 + 32 * i + frow;
+                wf[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+                if (BLOCK == 16) {
+                    const uint32_t b = *reinterpret_cast<const uint16_t*>(ssw + r * L::kScaleRow + 2 * c);
+                    sw[i][0] = __builtin_bit_cast(v2h, tabw[b & 0xFFu]);
+                    sw[i][1] = __builtin_bit_cast(v2h, tabw[b >> 8]);
+                } else {
+                    sw[i][0] = sw[i][1] = __builtin_bit_cast(v2h, tabw[ssw[r * L::kScaleRow + c]]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = wm * 64 + 32 * j + frow;
+                af[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+                if (BLOCK == 16) {
+                    const uint32_t b = *reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c);
+                    sa[j][0] = __builtin_bit_cast(v2h, taba[b & 0xFFu]);
+                    sa[j][1] = __builtin_bit_cast(v2h, taba[b >> 8]);
+                } else {
+                    sa[j][0] = sa[j][1] = __builtin_bit_cast(v2h, taba[ssa[r * L::kScaleRow + c]]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v8h av[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) av[j] = nv_convert8((uint32_t)af[j][t], sa[j][t >> 1]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v8h wv = nv_convert8((uint32_t)wf[i][t], sw[i][t >> 1]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv, av[j], acc[i][j], 0, 0, 0);
+                }
+                // keep the next step's conversions after this step's products
+                // (bounds the registers live at once)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const float g = p.ga[0] * p.gb[0];
+    store_tile_4x2(acc, g, p.c, p.ldc, m_base + wm * 64, n_base + wn * 128, M, N);
+}
+
+#ifndef FP4_NV_NS
+#define FP4_NV_NS 4
+#endif
+
 // Formats whose e2m1 * s products are exact in f16 (normal range) and those
 // exact in bf16 (at most 8 significant bits).
 static bool exact_in_f16(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits <= 4 && (f.ebits + f.mbits == 7); }
@@ -776,6 +955,21 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
     const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);
     if (!f16 && !bf16) return hipErrorNotSupported;
+    if (f16) {
+        const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
+        if (p.block == 16) {
+            constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<16>::kBytes + NvStage<16>::kTable;
+            hipError_t e = allow_lds(k_gemm_nv<16, FP4_NV_NS>, sh);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((k_gemm_nv<16, FP4_NV_NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+        } else {
+            constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<32>::kBytes + NvStage<32>::kTable;
+            hipError_t e = allow_lds(k_gemm_nv<32, FP4_NV_NS>, sh);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((k_gemm_nv<32, FP4_NV_NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+        }
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
     const size_t sh = sizeof(DqSmem);
     hipError_t e = hipSuccess;
