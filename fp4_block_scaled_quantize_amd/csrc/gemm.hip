@@ -797,10 +797,27 @@ __device__ __forceinline__ v8h nv_convert8(uint32_t w, v2h s2)
     return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-template <int BLOCK, int NS>
+// Fragments of one half stage (chunk pair ks) for one lane: four W and two
+// A 16-byte code fragments and their raw scale bytes (block 16: the two
+// scales of the chunk in one u16; block 32: one byte).
+struct NvHalf {
+    v4i w[4], a[2];
+    uint32_t sw[4], sa[2];
+};
+
+// HW_E4M3: both scale formats are E4M3, decoded to f16 by the hardware
+// FP8 -> f16 conversion (exact) instead of the LDS table.
+//
+// Schedule of one 128-element stage (per wave): the fragments of half 1 are
+// read from LDS while half 0's products run; the workgroup barrier sits
+// between the halves, and after it the first half of the next stage is
+// read while half 1's products run.  The conversions of each 32x32x16 step
+// are interleaved with the previous step's products.
+template <int BLOCK, int NS, bool HW_E4M3>
 __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 {
     using L = NvStage<BLOCK>;
+    static_assert(NS >= 2, "at least two stages");
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* tab = reinterpret_cast<uint32_t*>(smem + NS * L::kBytes);   // [2][256] f16x2
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -813,14 +830,14 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     const int KT = (int)(K / kMx3BK);
 
     // scale code -> f16 (exact for these formats), replicated for packed math
-    {
+    if (!HW_E4M3) {
         const int t = tid & 255;
         const ScaleFmtHost& fh = tid < 256 ? p.fb : p.fa;
         const ScaleFmt f{fh.ebits, fh.mbits, fh.bias, fh.maxcode, fh.smax, fh.is_e8m0};
         const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_decode_any((uint32_t)t, f));
         tab[tid] = h | (h << 16);
+        __syncthreads();
     }
-    __syncthreads();
 
     const uint8_t* srcw[2];
     const uint8_t* srca[2];
@@ -852,17 +869,58 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
         sdst[0] = 2 * kMx3Codes + (wave < 4 ? 0 : L::kScales) + 256 * (wave & 3);
     }
 
-    auto issue = [&](int kt, int buf) {
-        uint8_t* st = smem + buf * L::kBytes;
+    // DMA of stage kt into buffer kt % NS; past the last stage the last one
+    // is loaded again (into a buffer that is no longer read) so every wave
+    // always has the same number of loads in flight
+    auto issue = [&](int kt) {
+        const int ks = kt < KT ? kt : KT - 1;
+        uint8_t* st = smem + (kt % NS) * L::kBytes;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            dma16(srcw[k] + (int64_t)kt * kMx3RB, st + 1024 * (2 * wave + k));
-            dma16(srca[k] + (int64_t)kt * kMx3RB, st + kMx3Codes + 1024 * (2 * wave + k));
+            dma16(srcw[k] + (int64_t)ks * kMx3RB, st + 1024 * (2 * wave + k));
+            dma16(srca[k] + (int64_t)ks * kMx3RB, st + kMx3Codes + 1024 * (2 * wave + k));
         }
 #pragma unroll
-        for (int j = 0; j < kSDma; ++j) dma4(srcs[j] + (int64_t)kt * L::kScaleRow, st + sdst[j]);
+        for (int j = 0; j < kSDma; ++j) dma4(srcs[j] + (int64_t)ks * L::kScaleRow, st + sdst[j]);
     };
     constexpr int kLoads = 4 + kSDma;
+
+    const int frow = lane & 31, khalf = lane >> 5;
+    auto load_half = [&](NvHalf& h, int kt, int ks) {
+        const uint8_t* st = smem + (kt % NS) * L::kBytes;
+        const uint8_t* ssw = st + 2 * kMx3Codes;
+        const uint8_t* ssa = ssw + L::kScales;
+        const int c = 2 * ks + khalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wn * 128 + 32 * i + frow;
+            h.w[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+            h.sw[i] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssw + r * L::kScaleRow + 2 * c)
+                                  : (uint32_t)ssw[r * L::kScaleRow + c];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wm * 64 + 32 * j + frow;
+            h.a[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+            h.sa[j] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c)
+                                  : (uint32_t)ssa[r * L::kScaleRow + c];
+        }
+    };
+    // f16 scale of dword t (elements 8 t .. 8 t + 7) of a chunk, broadcast
+    auto scale_of = [&](uint32_t code, int t, const uint32_t* tb) -> v2h {
+        if (HW_E4M3) {
+            const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false);
+            return (BLOCK == 16 && t >= 2) ? v2h{s2[1], s2[1]} : v2h{s2[0], s2[0]};
+        }
+        const uint32_t b = BLOCK == 16 ? (t >= 2 ? code >> 8 : code & 0xFFu) : code;
+        return __builtin_bit_cast(v2h, tb[b]);
+    };
+    auto convert = [&](const NvHalf& h, int t, v8h (&cw)[4], v8h (&ca)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][t], scale_of(h.sw[i], t, tab));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
+    };
 
     v16f acc[4][2];
 #pragma unroll
@@ -870,70 +928,64 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
+    // four steps of one half: products of step t with the conversions of
+    // step t + 1 (the last step converts step 0 of `next`, if any)
+    auto run_half = [&](const NvHalf& h, const NvHalf& next, bool has_next, v8h (&cw)[4], v8h (&ca)[2]) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s < KT ? s : KT - 1, s);
-
-    const int frow = lane & 31, khalf = lane >> 5;
-    const uint32_t* tabw = tab;
-    const uint32_t* taba = tab + 256;
-    for (int kt = 0; kt < KT; ++kt) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
-        __builtin_amdgcn_s_barrier();
-        const int nxt = kt + NS - 1;
-        issue(nxt < KT ? nxt : KT - 1, nxt % NS);
-        const uint8_t* st = smem + (kt % NS) * L::kBytes;
-        const uint8_t* ssw = st + 2 * kMx3Codes;
-        const uint8_t* ssa = ssw + L::kScales;
+        for (int t = 0; t < 4; ++t) {
+            v8h nw[4], na[2];
+            const bool conv = t < 3 || has_next;
+            if (t < 3) convert(h, t + 1, nw, na);
+            else if (has_next) convert(next, 0, nw, na);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int c = 2 * ks + khalf;
-            v4i wf[4], af[2];
-            v2h sw[4][2], sa[2][2];          // [row block][t >> 1] (block 32: one scale per chunk)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wn * 128 + 32 * i + frow;
-                wf[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
-                if (BLOCK == 16) {
-                    const uint32_t b = *reinterpret_cast<const uint16_t*>(ssw + r * L::kScaleRow + 2 * c);
-                    sw[i][0] = __builtin_bit_cast(v2h, tabw[b & 0xFFu]);
-                    sw[i][1] = __builtin_bit_cast(v2h, tabw[b >> 8]);
-                } else {
-                    sw[i][0] = sw[i][1] = __builtin_bit_cast(v2h, tabw[ssw[r * L::kScaleRow + c]]);
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cw[i], ca[j], acc[i][j], 0, 0, 0);
+            if (conv) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one matrix instruction
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // six VALU
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (conv) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = wm * 64 + 32 * j + frow;
-                af[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
-                if (BLOCK == 16) {
-                    const uint32_t b = *reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c);
-                    sa[j][0] = __builtin_bit_cast(v2h, taba[b & 0xFFu]);
-                    sa[j][1] = __builtin_bit_cast(v2h, taba[b >> 8]);
-                } else {
-                    sa[j][0] = sa[j][1] = __builtin_bit_cast(v2h, taba[ssa[r * L::kScaleRow + c]]);
-                }
-            }
+                for (int i = 0; i < 4; ++i) cw[i] = nw[i];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v8h av[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) av[j] = nv_convert8((uint32_t)af[j][t], sa[j][t >> 1]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v8h wv = nv_convert8((uint32_t)wf[i][t], sw[i][t >> 1]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv, av[j], acc[i][j], 0, 0, 0);
-                }
-                // keep the next step's conversions after this step's products
-                // (bounds the registers live at once)
-                __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < 2; ++j) ca[j] = na[j];
             }
         }
+    };
+
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue(s);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * kLoads) : "memory");
+    __builtin_amdgcn_s_barrier();
+    NvHalf f, g;
+    load_half(f, 0, 0);
+    v8h cw[4], ca[2];
+    convert(f, 0, cw, ca);
+    // The loop body is uniform: after the last stage the prefetch reads a
+    // buffer whose contents are never used (a re-loaded copy of the last
+    // stage), which keeps one copy of the body and every barrier uniform.
+    for (int kt = 0; kt < KT; ++kt) {
+        load_half(g, kt, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        run_half(f, g, true, cw, ca);
+        // stage kt + 1 has landed for every wave, and every wave has
+        // finished reading stage kt, whose buffer is refilled next
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NS - 2) * kLoads) : "memory");
+        __builtin_amdgcn_s_barrier();
+        issue(kt + NS);
+        load_half(f, kt + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        run_half(g, f, true, cw, ca);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const float g = p.ga[0] * p.gb[0];
-    store_tile_4x2(acc, g, p.c, p.ldc, m_base + wm * 64, n_base + wn * 128, M, N);
+    const float gg = p.ga[0] * p.gb[0];
+    store_tile_4x2(acc, gg, p.c, p.ldc, m_base + wm * 64, n_base + wn * 128, M, N);
 }
 
 #ifndef FP4_NV_NS
@@ -944,6 +996,19 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 // exact in bf16 (at most 8 significant bits).
 static bool exact_in_f16(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits <= 4 && (f.ebits + f.mbits == 7); }
 static bool exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 5; }
+
+static bool is_e4m3(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits == 4 && f.mbits == 3; }
+
+template <int BLOCK, bool HW>
+static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
+{
+    constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<BLOCK>::kBytes + NvStage<BLOCK>::kTable;
+    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, HW>, sh);
+    if (e != hipSuccess) return e;
+    const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
+    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, HW>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+    return hipGetLastError();
+}
 
 bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb)
 {
@@ -956,19 +1021,13 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);
     if (!f16 && !bf16) return hipErrorNotSupported;
     if (f16) {
-        const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
+        const bool hw = is_e4m3(p.fa) && is_e4m3(p.fb);
         if (p.block == 16) {
-            constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<16>::kBytes + NvStage<16>::kTable;
-            hipError_t e = allow_lds(k_gemm_nv<16, FP4_NV_NS>, sh);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((k_gemm_nv<16, FP4_NV_NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
-        } else {
-            constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<32>::kBytes + NvStage<32>::kTable;
-            hipError_t e = allow_lds(k_gemm_nv<32, FP4_NV_NS>, sh);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((k_gemm_nv<32, FP4_NV_NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+            if (hw) return launch_nv<16, true>(p, s);
+            return launch_nv<16, false>(p, s);
         }
-        return hipGetLastError();
+        if (hw) return launch_nv<32, true>(p, s);
+        return launch_nv<32, false>(p, s);
     }
     dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
     const size_t sh = sizeof(DqSmem);
@@ -1050,13 +1109,17 @@ __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i
     }
 }
 
-template <int NW, int BLOCK, bool SPLIT, bool POW2>
+// NW waves per workgroup split K (wave w takes chunks w, w + NW, ...); each
+// wave keeps D chunks of W, their scales and the matching X fragments in
+// flight in a ring: the loads of chunk i + D are issued as chunk i is
+// consumed, so neither operand waits on a round trip per chunk.
+template <int NW, int D, int BLOCK, bool SPLIT, bool POW2>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
-    constexpr int U = 8;                      // 128-element chunks per batch; two batches of W in flight
     __shared__ float red[NW][256];
     __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // wave-uniform (scalar)
     const int r16 = lane & 15, grp = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t N = p.n, K = p.k, M = p.m;
@@ -1070,81 +1133,68 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     // 32-bit byte / element offsets from the operand bases (the ABI bounds W below 4 GiB)
     const uint32_t woff = (uint32_t)(n * rowb) + 16u * grp;
     const uint32_t soff = (uint32_t)(n * rows) + (BLOCK == 16 ? 2u * grp : (uint32_t)grp);
-    const bool mvalid = r16 < M;
-    const uint32_t xoff = (uint32_t)((mvalid ? r16 : 0) * p.ldx) + 32u * grp;
+    // rows m >= M of the padded X tile read row M - 1: in bounds, and they
+    // only feed output rows that are never stored
+    const int64_t mrow = r16 < M ? r16 : M - 1;
+    const uint32_t xoff = (uint32_t)(mrow * p.ldx) + 32u * grp;
     const int nchunks = (int)(K / 128);
     const int mine = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;   // chunks wave, wave + NW, ...
-    const int nb = (mine + U - 1) / U;
     __syncthreads();
 
-    struct Batch { v4i w[U]; uint32_t sc[U]; };
-    // raw loads only: anything computed from a loaded value at load time would
-    // make the compiler wait for it before the MFMAs of the batch in progress
-    auto load_w = [&](int b, Batch& bt) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = b * U + u < mine ? b * U + u : mine - 1;             // clamped: always in bounds
-            const uint32_t kc = (uint32_t)(wave + i * NW);
-            bt.w[u] = *reinterpret_cast<const v4i*>(p.qw + woff + kc * 64u);
-            bt.sc[u] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff + kc * 8u)
-                                   : (uint32_t)p.sw[soff + kc * 4u];
-        }
+    struct Slot {
+        v4i w;
+        uint32_t sc;
+        v4i x[4];
     };
-    // rows m >= M keep whatever their registers hold: they only feed output
-    // rows that are never stored
-    auto load_x = [&](int i, v4i (&x)[4]) {
+    // chunk min(i, mine - 1) of this wave.  Every load is unconditional (a
+    // prefetch past the end re-reads the last chunk, which is not used
+    // again), so the compiler can count loads in flight across the ring.
+    auto issue = [&](int i, Slot& s) {
         const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
-        if (mvalid) {
+        s.w = *reinterpret_cast<const v4i*>(p.qw + woff + kc * 64u);
+        s.sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff + kc * 8u)
+                           : (uint32_t)p.sw[soff + kc * 4u];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) x[t] = *reinterpret_cast<const v4i*>(p.x + xoff + kc * 128u + 8u * t);
-        }
+        for (int t = 0; t < 4; ++t) s.x[t] = *reinterpret_cast<const v4i*>(p.x + xoff + kc * 128u + 8u * t);
     };
 
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    auto chunk = [&](const v4i& w, uint32_t sc, const v4i (&x)[4]) {
-        const float s0 = sdec[sc & 0xFFu];
-        const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
+    auto chunk = [&](const Slot& sl) {
+        const float s0 = sdec[sl.sc & 0xFFu];
+        const float s1 = BLOCK == 16 ? sdec[(sl.sc >> 8) & 0xFFu] : s0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
             if (SPLIT) {
                 v4i hi, lo;
-                dq8_bf16_split((uint32_t)w[t], st, hi, lo);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                dq8_bf16_split((uint32_t)sl.w[t], st, hi, lo);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
                                                               __builtin_bit_cast(v8bf, hi), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
                                                               __builtin_bit_cast(v8bf, lo), acc, 0, 0, 0);
             } else {
-                const v4i wt = dq8_bf16<POW2>((uint32_t)w[t], st);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[t]),
+                const v4i wt = dq8_bf16<POW2>((uint32_t)sl.w[t], st);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
                                                               __builtin_bit_cast(v8bf, wt), acc, 0, 0, 0);
             }
         }
     };
-    v4i xa[4] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-    v4i xb[4] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-    auto process = [&](int b, const Batch& bt) {
-        load_x(b * U, xa);
-#pragma unroll
-        for (int u = 0; u < U; u += 2) {
-            const int i = b * U + u;
-            load_x(i + 1, xb);
-            if (i < mine) chunk(bt.w[u], bt.sc[u], xa);
-            load_x(i + 2, xa);
-            if (i + 1 < mine) chunk(bt.w[u + 1], bt.sc[u + 1], xb);
-        }
-    };
 
-    Batch A, B;
-    if (nb > 0) load_w(0, A);
-    if (nb > 1) load_w(1, B);
-    for (int b = 0; b < nb; b += 2) {
-        process(b, A);
-        if (b + 2 < nb) load_w(b + 2, A);
-        if (b + 1 < nb) {
-            process(b + 1, B);
-            if (b + 3 < nb) load_w(b + 3, B);
+    if (mine > 0) {
+        Slot ring[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(d, ring[d]);
+        int i0 = 0;
+        for (; i0 + D <= mine; i0 += D) {        // whole groups: no conditions inside
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                chunk(ring[d]);
+                issue(i0 + d + D, ring[d]);
+            }
         }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)           // the last mine % D chunks
+            if (i0 + d < mine) chunk(ring[d]);
     }
     // acc[r] = D[m = 4 grp + r][n = r16]; fixed-order sum over the waves
 #pragma unroll
@@ -1160,29 +1210,26 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     }
 }
 
-template <int NW>
-static void launch_wo_nw(const WoGemmLaunch& p, hipStream_t s)
+template <int NW, int D>
+static void launch_wo_cfg(const WoGemmLaunch& p, hipStream_t s)
 {
     dim3 grid((unsigned)((p.n + 15) / 16)), block(64 * NW);
     const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
     if (p.block == 16) {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, 16, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, 16, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, 16, false, false>), grid, block, 0, s, p);
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, false, false>), grid, block, 0, s, p);
     } else {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, 32, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, 32, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, 32, false, false>), grid, block, 0, s, p);
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, false, false>), grid, block, 0, s, p);
     }
 }
 
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
-    // waves per workgroup split K; short rows use fewer so each wave keeps
-    // several 128-element chunks to stream
-    const int64_t chunks = p.k / 128;
-    if (chunks >= 48) launch_wo_nw<8>(p, s);
-    else launch_wo_nw<4>(p, s);
+    // four waves split K; each keeps four 128-element chunks in flight
+    launch_wo_cfg<4, 4>(p, s);
     return hipGetLastError();
 }
 
