@@ -79,16 +79,6 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[4][4], float g, uin
 // ---------------------------------------------------------------------------
 // MXFP4: native block-scaled FP4 matrix instruction
 // ---------------------------------------------------------------------------
-#ifndef FP4_MX_BK
-#define FP4_MX_BK 256               // K elements per LDS stage
-#endif
-#ifndef FP4_MX_RS
-#define FP4_MX_RS 2                 // register stages: global loads run RS stages ahead
-#endif
-#ifndef FP4_MX_REMAP
-#define FP4_MX_REMAP 1              // XCD-aware tile order
-#endif
-
 // Output tile order.  Workgroups are dispatched round-robin over the 8 XCDs
 // (each with its own L2); remap so every XCD walks a contiguous band of
 // tiles, ordered in groups of 4 tile-rows, so the A and W panels a band
@@ -97,7 +87,7 @@ __device__ __forceinline__ void tile_coords(int tiles_n, int tiles_m, int* tn, i
 {
     const int nt = tiles_n * tiles_m;
     int r = blockIdx.x;
-    if (FP4_MX_REMAP && (nt % 8) == 0) r = (r % 8) * (nt / 8) + r / 8;
+    if ((nt % 8) == 0) r = (r % 8) * (nt / 8) + r / 8;
     constexpr int GM = 4;
     const int band = GM * tiles_n;
     const int g = r / band, in = r % band;
@@ -106,159 +96,21 @@ __device__ __forceinline__ void tile_coords(int tiles_n, int tiles_m, int* tn, i
     *tn = in / rows_in;
 }
 
-template <int BK>
-struct MxSmemT {
-    static constexpr int RB = BK / 2;          // bytes of codes per row per stage
-    static constexpr int ROW = RB + 16;        // padded LDS row (conflict-free 16-byte reads)
-    static constexpr int SW = BK / 128;        // 32-bit words of E8M0 bytes per row per stage
-    uint8_t w[2][kTile * ROW];
-    uint8_t a[2][kTile * ROW];
-    uint32_t sw[2][kTile * SW];
-    uint32_t sa[2][kTile * SW];
-};
-
-template <int BK, int RS>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_mx(GemmLaunch p)
-{
-    using Sm = MxSmemT<BK>;
-    constexpr int RB = Sm::RB, ROW = Sm::ROW, SW = Sm::SW;
-    constexpr int C = RB / 16;                 // 16-byte chunks per row per stage
-    constexpr int RPP = kGemmThreads / C;      // rows covered per pass of the staging loop
-    extern __shared__ __align__(16) uint8_t smem_raw[];
-    Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
-    const int64_t M = p.m, N = p.n, K = p.k;
-    int tn, tm;
-    tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
-    const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
-    const int64_t rowb = K / 2;          // bytes per row of codes
-    const int64_t rows = K / 32;         // scale bytes per row
-    const int KT = (int)(K / BK);
-
-    // staging registers, RS sets: thread t moves 16-byte chunk (t % C) of
-    // rows t / C + RPP r (r < C) of both operands, and the scale words of row t
-    v4i rw[RS][C], ra[RS][C];
-    uint32_t rsw[RS][SW], rsa[RS][SW];
-    const int crow = tid / C, cchunk = tid % C;
-    const uint8_t* gw_base[C];
-    const uint8_t* ga_base[C];
-    bool vw[C], va[C];
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-        const int64_t nr = n_base + crow + RPP * r, mr = m_base + crow + RPP * r;
-        vw[r] = nr < N;
-        va[r] = mr < M;
-        gw_base[r] = p.qb + (vw[r] ? nr : 0) * rowb + cchunk * 16;
-        ga_base[r] = p.qa + (va[r] ? mr : 0) * rowb + cchunk * 16;
-    }
-    const bool vsw = n_base + tid < N, vsa = m_base + tid < M;
-    const uint8_t* gsw = p.sb + (vsw ? n_base + tid : 0) * rows;
-    const uint8_t* gsa = p.sa + (vsa ? m_base + tid : 0) * rows;
-
-    auto gload = [&](int kt, int set) {
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            rw[set][r] = vw[r] ? *reinterpret_cast<const v4i*>(gw_base[r] + (int64_t)kt * RB) : v4i{0, 0, 0, 0};
-            ra[set][r] = va[r] ? *reinterpret_cast<const v4i*>(ga_base[r] + (int64_t)kt * RB) : v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int q = 0; q < SW; ++q) {
-            rsw[set][q] = vsw ? *reinterpret_cast<const uint32_t*>(gsw + (int64_t)kt * (BK / 32) + 4 * q) : 0x7F7F7F7Fu;
-            rsa[set][q] = vsa ? *reinterpret_cast<const uint32_t*>(gsa + (int64_t)kt * (BK / 32) + 4 * q) : 0x7F7F7F7Fu;
-        }
-    };
-    auto sstore = [&](int buf, int set) {
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            *reinterpret_cast<v4i*>(&sm.w[buf][(crow + RPP * r) * ROW + cchunk * 16]) = rw[set][r];
-            *reinterpret_cast<v4i*>(&sm.a[buf][(crow + RPP * r) * ROW + cchunk * 16]) = ra[set][r];
-        }
-#pragma unroll
-        for (int q = 0; q < SW; ++q) {
-            sm.sw[buf][tid * SW + q] = rsw[set][q];
-            sm.sa[buf][tid * SW + q] = rsa[set][q];
-        }
-    };
-
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-#pragma unroll
-    for (int s = 0; s < RS; ++s)
-        if (s < KT) gload(s, s);
-    sstore(0, 0);
-    __syncthreads();
-    const int frow = lane & 31, khalf = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const int set = kt % RS;
-        // prefetch stage kt + RS into this set (its stage kt is already in
-        // LDS); past the end it re-reads the last stage, keeping the loop
-        // body branch-free so the scheduler keeps the order below
-        gload(kt + RS < KT ? kt + RS : KT - 1, set);
-        uint32_t swd[4][SW], sad[4][SW];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < SW; ++q) swd[i][q] = sm.sw[buf][(wn * 128 + 32 * i + frow) * SW + q];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < SW; ++q) sad[j][q] = sm.sa[buf][(wm * 128 + 32 * j + frow) * SW + q];
-#pragma unroll
-        for (int ks = 0; ks < BK / 64; ++ks) {
-            v4i wf[4], af[4];
-            const int off = ks * 32 + khalf * 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                wf[i] = *reinterpret_cast<const v4i*>(&sm.w[buf][(wn * 128 + 32 * i + frow) * ROW + off]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                af[j] = *reinterpret_cast<const v4i*>(&sm.a[buf][(wm * 128 + 32 * j + frow) * ROW + off]);
-            const int blk = 2 * ks + khalf;                       // 32-element block within the stage
-            const int q = blk >> 2, sh = 8 * (blk & 3);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sw = (int)((swd[i][q] >> sh) & 0xFFu);
-                const v8i wv = {wf[i][0], wf[i][1], wf[i][2], wf[i][3], 0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int sa = (int)((sad[j][q] >> sh) & 0xFFu);
-                    const v8i av = {af[j][0], af[j][1], af[j][2], af[j][3], 0, 0, 0, 0};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0, sa);
-                }
-            }
-        }
-        // keep the LDS store of the prefetched stage after this stage's
-        // MFMAs: hoisted above them it would wait on loads just issued
-        __builtin_amdgcn_sched_barrier(0);
-        sstore(buf ^ 1, (kt + 1) % RS);
-        __syncthreads();
-    }
-    const float g = p.ga[0] * p.gb[0];
-    store_tile(acc, g, p.c, p.ldc, m_base + wm * 128, n_base + wn * 128, M, N);
-}
-
 // ---------------------------------------------------------------------------
-// MXFP4, multi-stage variant: operands go global -> LDS with the gfx950
-// direct-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
-// LDS base + 16 * lane), NS stages in flight, one barrier per stage.  The LDS
-// image of a 64-byte row is XOR-swizzled in 16-byte chunks (chunk c of row r
-// sits at c ^ ((r >> 1) & 3)) so the 32 rows a fragment read touches hit
-// distinct banks; the swizzle is applied by choosing each lane's global
-// source address.
+// MXFP4: operands go HBM -> LDS with the gfx950 direct-to-LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
+// lane) through NS stages of BK K-elements, one barrier per stage, and from
+// LDS straight into v_mfma_scale_f32_32x32x64_f8f6f4.  Eight waves, two per
+// SIMD (each 128 x 64 of the 256 x 256 tile, 128 accumulator registers), so
+// one wave's matrix instructions overlap the other's LDS reads and barrier
+// waits.  The LDS image of a row is XOR-swizzled in 16-byte chunks so that
+// the 32 rows one fragment read touches land on distinct banks; the swizzle
+// is applied by choosing each lane's global source address.
 // ---------------------------------------------------------------------------
-#ifndef FP4_MX_NS
-#define FP4_MX_NS 4
-#endif
-constexpr int kMx3BK = 128;                          // K elements per stage
+constexpr int kMx4Threads = 512;
+constexpr int kMx3BK = 128;                          // K elements per stage (f16 path)
 constexpr int kMx3RB = kMx3BK / 2;                   // 64 bytes of codes per row
 constexpr int kMx3Codes = kTile * kMx3RB;            // 16 KiB per operand per stage
-constexpr int kMx3Stage = 2 * kMx3Codes + 2 * kTile * 4;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -271,123 +123,27 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds)
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
 }
 
-template <int NS>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_mx3(GemmLaunch p)
+template <int BK>
+struct MxStage {
+    static constexpr int RB = BK / 2;                 // code bytes per row per stage
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;              // rows per DMA instruction
+    static constexpr int NI = kTile / (8 * RPI);      // DMA instructions per wave per operand
+    static constexpr int Codes = kTile * RB;          // per operand
+    static constexpr int SRow = BK / 32;              // E8M0 bytes per row per stage
+    static constexpr int Scales = kTile * SRow;       // per operand
+    static constexpr int SDma = 2 * Scales / (4 * kMx4Threads);   // dword DMAs per lane
+    static constexpr int Bytes = 2 * Codes + 2 * Scales;
+};
+
+// Position of 16-byte chunk c of row r: c ^ mx_swz(r).  64-byte rows:
+// ((r >> 1) ^ (r >> 3)) & 3; 128-byte rows: (r >> 1) & 7.  Both keep the
+// 8- and 16-lane phases of a fragment read (32 consecutive rows, one chunk)
+// on distinct banks.
+template <int BK>
+__device__ __forceinline__ int mx_swz(int r)
 {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
-    const int64_t M = p.m, N = p.n, K = p.k;
-    int tn, tm;
-    tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
-    const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
-    const int64_t rowb = K / 2, rows = K / 32;
-    const int KT = (int)(K / kMx3BK);
-
-    // per-lane global sources.  Codes: load k (0..3) of this wave fills rows
-    // 16 (4 wave + k) + lane / 4, physical chunk lane % 4.  Rows past the
-    // matrix read the last row (their outputs are never stored).
-    const uint8_t* srcw[4];
-    const uint8_t* srca[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int r = 16 * (4 * wave + k) + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
-        const int64_t nr = n_base + r < N ? n_base + r : N - 1;
-        const int64_t mr = m_base + r < M ? m_base + r : M - 1;
-        srcw[k] = p.qb + nr * rowb + 16 * c;
-        srca[k] = p.qa + mr * rowb + 16 * c;
-    }
-    const int rs = 64 * wave + lane;                 // scale row of this lane
-    const uint8_t* srcsw = p.sb + (n_base + rs < N ? n_base + rs : N - 1) * rows;
-    const uint8_t* srcsa = p.sa + (m_base + rs < M ? m_base + rs : M - 1) * rows;
-
-    auto issue = [&](int kt, int buf) {
-        uint8_t* st = smem + buf * kMx3Stage;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dma16(srcw[k] + (int64_t)kt * kMx3RB, st + 1024 * (4 * wave + k));
-            dma16(srca[k] + (int64_t)kt * kMx3RB, st + kMx3Codes + 1024 * (4 * wave + k));
-        }
-        dma4(srcsw + (int64_t)kt * 4, st + 2 * kMx3Codes + 256 * wave);
-        dma4(srcsa + (int64_t)kt * 4, st + 2 * kMx3Codes + kTile * 4 + 256 * wave);
-    };
-    constexpr int kLoads = 10;                       // DMA instructions per wave per stage
-
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s < KT ? s : KT - 1, s);
-
-    const int frow = lane & 31, khalf = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-        // this wave's loads of stage kt have landed; the barrier makes every
-        // wave's visible and retires all reads of stage kt - 1
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
-        __builtin_amdgcn_s_barrier();       // no fence: a fence would wait for every load in flight
-        const int nxt = kt + NS - 1;
-        issue(nxt < KT ? nxt : KT - 1, nxt % NS);
-        const uint8_t* st = smem + (kt % NS) * kMx3Stage;
-        const uint32_t* ssw = reinterpret_cast<const uint32_t*>(st + 2 * kMx3Codes);
-        const uint32_t* ssa = ssw + kTile;
-        uint32_t swd[4], sad[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) swd[i] = ssw[wn * 128 + 32 * i + frow];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sad[j] = ssa[wm * 128 + 32 * j + frow];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int c = 2 * ks + khalf;
-            v4i wf[4], af[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wn * 128 + 32 * i + frow;
-                wf[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ ((r >> 1) & 3)));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wm * 128 + 32 * j + frow;
-                af[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ ((r >> 1) & 3)));
-            }
-            const int sh = 8 * c;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sw = (int)((swd[i] >> sh) & 0xFFu);
-                const v8i wv = {wf[i][0], wf[i][1], wf[i][2], wf[i][3], 0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int sa = (int)((sad[j] >> sh) & 0xFFu);
-                    const v8i av = {af[j][0], af[j][1], af[j][2], af[j][3], 0, 0, 0, 0};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0, sa);
-                }
-            }
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const float g = p.ga[0] * p.gb[0];
-    store_tile(acc, g, p.c, p.ldc, m_base + wm * 128, n_base + wn * 128, M, N);
-}
-
-// ---------------------------------------------------------------------------
-// MXFP4, 8 waves: two waves per SIMD (each 128 x 64 of the 256 x 256 tile,
-// 128 accumulator registers) so one wave's MFMAs overlap the other's LDS
-// reads and barrier waits.  Swizzle f(r) = ((r >> 1) ^ (r >> 3)) & 3 keeps
-// both 8-lane and 16-lane phases of a 16-byte fragment read on distinct banks.
-// ---------------------------------------------------------------------------
-constexpr int kMx4Threads = 512;
-
-#ifndef FP4_MX_SWZ
-#define FP4_MX_SWZ 1
-#endif
-__device__ __forceinline__ int mx4_swz(int r)
-{
-    if (FP4_MX_SWZ == 0) return 0;
-    if (FP4_MX_SWZ == 2) return (((r >> 1) ^ (r >> 3)) & 1) << 1;   // swap 32-byte halves only
-    return ((r >> 1) ^ (r >> 3)) & 3;
+    return BK == 128 ? (((r >> 1) ^ (r >> 3)) & 3) : ((r >> 1) & 7);
 }
 
 __device__ __forceinline__ void store_tile_4x2(const v16f (&acc)[4][2], float g, uint16_t* __restrict__ c,
@@ -425,9 +181,11 @@ __device__ __forceinline__ void store_tile_4x2(const v16f (&acc)[4][2], float g,
     }
 }
 
-template <int NS>
-__global__ __launch_bounds__(kMx4Threads) void k_gemm_mx4(GemmLaunch p)
+template <int BK, int NS>
+__global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
 {
+    using L = MxStage<BK>;
+    static_assert(NS >= 2 && (BK == 128 || BK == 256), "stage shape");
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;            // 2 x 4 waves: 128 (n) x 64 (m) each
@@ -436,36 +194,53 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx4(GemmLaunch p)
     tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
     const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
     const int64_t rowb = K / 2, rows = K / 32;
-    const int KT = (int)(K / kMx3BK);
+    const int KT = (int)(K / BK);
+    auto row_w = [&](int r) { return n_base + r < N ? n_base + r : N - 1; };   // rows past the matrix
+    auto row_a = [&](int r) { return m_base + r < M ? m_base + r : M - 1; };   // re-read the last one
 
-    // codes: DMA k (0..1) of this wave fills rows 16 (2 wave + k) + lane / 4
-    const uint8_t* srcw[2];
-    const uint8_t* srca[2];
+    // codes: DMA k of this wave fills rows RPI (NI wave + k) + lane / CPR,
+    // physical chunk lane % CPR
+    const uint8_t* srcw[L::NI];
+    const uint8_t* srca[L::NI];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int r = 16 * (2 * wave + k) + (lane >> 2);
-        const int c = (lane & 3) ^ mx4_swz(r);
-        const int64_t nr = n_base + r < N ? n_base + r : N - 1;
-        const int64_t mr = m_base + r < M ? m_base + r : M - 1;
-        srcw[k] = p.qb + nr * rowb + 16 * c;
-        srca[k] = p.qa + mr * rowb + 16 * c;
+    for (int k = 0; k < L::NI; ++k) {
+        const int r = L::RPI * (L::NI * wave + k) + lane / L::CPR;
+        const int c = (lane % L::CPR) ^ mx_swz<BK>(r);
+        srcw[k] = p.qb + row_w(r) * rowb + 16 * c;
+        srca[k] = p.qa + row_a(r) * rowb + 16 * c;
     }
-    // scales: waves 0-3 load W's (rows 64 wave + lane), waves 4-7 A's
-    const int rs = 64 * (wave & 3) + lane;
-    const uint8_t* srcs = wave < 4 ? p.sb + (n_base + rs < N ? n_base + rs : N - 1) * rows
-                                   : p.sa + (m_base + rs < M ? m_base + rs : M - 1) * rows;
-    const int sdst = 2 * kMx3Codes + (wave < 4 ? 0 : kTile * 4) + 256 * (wave & 3);
+    // scales ([256][SRow] bytes per operand).  BK 128: waves 0-3 fill W's
+    // rows 64 wave + lane, waves 4-7 A's.  BK 256: DMA j fills operand j
+    // (0: W, 1: A), dword 64 wave + lane = (row, half).
+    const uint8_t* srcs[L::SDma];
+    int sdst[L::SDma];
+    if (BK == 128) {
+        const int r = 64 * (wave & 3) + lane;
+        srcs[0] = wave < 4 ? p.sb + row_w(r) * rows : p.sa + row_a(r) * rows;
+        sdst[0] = 2 * L::Codes + (wave < 4 ? 0 : L::Scales) + 256 * (wave & 3);
+    } else {
+        const int q = 64 * wave + lane, r = q >> 1, d = q & 1;
+        srcs[0] = p.sb + row_w(r) * rows + 4 * d;
+        srcs[L::SDma - 1] = p.sa + row_a(r) * rows + 4 * d;
+        sdst[0] = 2 * L::Codes + 256 * wave;
+        sdst[L::SDma - 1] = 2 * L::Codes + L::Scales + 256 * wave;
+    }
 
+    // stage kt into buffer buf; past the last stage the last one is loaded
+    // again (into a buffer that is no longer read), so every wave always has
+    // the same number of loads in flight
     auto issue = [&](int kt, int buf) {
-        uint8_t* st = smem + buf * kMx3Stage;
+        const int ks = kt < KT ? kt : KT - 1;
+        uint8_t* st = smem + buf * L::Bytes;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            dma16(srcw[k] + (int64_t)kt * kMx3RB, st + 1024 * (2 * wave + k));
-            dma16(srca[k] + (int64_t)kt * kMx3RB, st + kMx3Codes + 1024 * (2 * wave + k));
+        for (int k = 0; k < L::NI; ++k) {
+            dma16(srcw[k] + (int64_t)ks * L::RB, st + 1024 * (L::NI * wave + k));
+            dma16(srca[k] + (int64_t)ks * L::RB, st + L::Codes + 1024 * (L::NI * wave + k));
         }
-        dma4(srcs + (int64_t)kt * 4, st + sdst);
+#pragma unroll
+        for (int j = 0; j < L::SDma; ++j) dma4(srcs[j] + (int64_t)ks * L::SRow, st + sdst[j]);
     };
-    constexpr int kLoads = 5;
+    constexpr int kLoads = 2 * L::NI + L::SDma;
 
     v16f acc[4][2];
 #pragma unroll
@@ -474,35 +249,44 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx4(GemmLaunch p)
         for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s < KT ? s : KT - 1, s);
+    for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
     const int frow = lane & 31, khalf = lane >> 5;
     for (int kt = 0; kt < KT; ++kt) {
+        // this wave's loads of stage kt have landed; the barrier makes every
+        // wave's visible and retires all reads of stage kt - 1
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
-        __builtin_amdgcn_s_barrier();
-        const int nxt = kt + NS - 1;
-        issue(nxt < KT ? nxt : KT - 1, nxt % NS);
-        const uint8_t* st = smem + (kt % NS) * kMx3Stage;
-        const uint32_t* ssw = reinterpret_cast<const uint32_t*>(st + 2 * kMx3Codes);
-        const uint32_t* ssa = ssw + kTile;
-        uint32_t swd[4], sad[2];
+        __builtin_amdgcn_s_barrier();        // no fence: a fence would wait for every load in flight
+        issue(kt + NS - 1, (kt + NS - 1) % NS);
+        const uint8_t* st = smem + (kt % NS) * L::Bytes;
+        const uint8_t* ssw = st + 2 * L::Codes;
+        const uint8_t* ssa = ssw + L::Scales;
+        uint64_t swd[4], sad[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) swd[i] = ssw[wn * 128 + 32 * i + frow];
+        for (int i = 0; i < 4; ++i) {
+            const int r = wn * 128 + 32 * i + frow;
+            swd[i] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssw + 8 * r)
+                               : (uint64_t)*reinterpret_cast<const uint32_t*>(ssw + 4 * r);
+        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sad[j] = ssa[wm * 64 + 32 * j + frow];
+        for (int j = 0; j < 2; ++j) {
+            const int r = wm * 64 + 32 * j + frow;
+            sad[j] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssa + 8 * r)
+                               : (uint64_t)*reinterpret_cast<const uint32_t*>(ssa + 4 * r);
+        }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < BK / 64; ++ks) {
             const int c = 2 * ks + khalf;
             v4i wf[4], af[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = wn * 128 + 32 * i + frow;
-                wf[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+                wf[i] = *reinterpret_cast<const v4i*>(st + r * L::RB + 16 * (c ^ mx_swz<BK>(r)));
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int r = wm * 64 + 32 * j + frow;
-                af[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+                af[j] = *reinterpret_cast<const v4i*>(st + L::Codes + r * L::RB + 16 * (c ^ mx_swz<BK>(r)));
             }
             const int sh = 8 * c;
 #pragma unroll
@@ -531,41 +315,23 @@ static hipError_t allow_lds(K kernel, size_t bytes)
                                (int)bytes);
 }
 
-#ifndef FP4_MX_KERNEL
-#define FP4_MX_KERNEL 4
-#endif
-
-hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s)
+template <int BK, int NS>
+static hipError_t launch_mx(const GemmLaunch& p, hipStream_t s)
 {
-    if (FP4_MX_KERNEL == 4) {
-        constexpr size_t sh = (size_t)FP4_MX_NS * kMx3Stage;
-        hipError_t e = allow_lds(k_gemm_mx4<FP4_MX_NS>, sh);
-        if (e != hipSuccess) return e;
-        const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-        hipLaunchKernelGGL((k_gemm_mx4<FP4_MX_NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
-        return hipGetLastError();
-    }
-    if (FP4_MX_KERNEL == 3) {
-        constexpr size_t sh = (size_t)FP4_MX_NS * kMx3Stage;
-        hipError_t e = allow_lds(k_gemm_mx3<FP4_MX_NS>, sh);
-        if (e != hipSuccess) return e;
-        const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-        hipLaunchKernelGGL((k_gemm_mx3<FP4_MX_NS>), dim3(tiles), dim3(kGemmThreads), sh, s, p);
-        return hipGetLastError();
-    }
-    constexpr int BK = (FP4_MX_BK == 256) ? 256 : 128;
-    if (p.k % BK) {       // K % 128 == 0 is guaranteed; fall back to the 128 stage for odd multiples
-        hipError_t e = allow_lds(k_gemm_mx<128, FP4_MX_RS>, sizeof(MxSmemT<128>));
-        if (e != hipSuccess) return e;
-        const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-        hipLaunchKernelGGL((k_gemm_mx<128, FP4_MX_RS>), dim3(tiles), dim3(kGemmThreads), sizeof(MxSmemT<128>), s, p);
-        return hipGetLastError();
-    }
-    hipError_t e = allow_lds(k_gemm_mx<BK, FP4_MX_RS>, sizeof(MxSmemT<BK>));
+    constexpr size_t sh = (size_t)NS * MxStage<BK>::Bytes;
+    hipError_t e = allow_lds(k_gemm_mx<BK, NS>, sh);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-    hipLaunchKernelGGL((k_gemm_mx<BK, FP4_MX_RS>), dim3(tiles), dim3(kGemmThreads), sizeof(MxSmemT<BK>), s, p);
+    hipLaunchKernelGGL((k_gemm_mx<BK, NS>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
     return hipGetLastError();
+}
+
+// 256-element stages read whole 128-byte lines of every row (two stages fit
+// in LDS); K that is only a multiple of 128 takes four 128-element stages.
+hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s)
+{
+    if (p.k % 256 == 0) return launch_mx<256, 2>(p, s);
+    return launch_mx<128, 4>(p, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -764,7 +530,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 // ---------------------------------------------------------------------------
 // f16 path (scale formats whose e2m1 * s products are exact in f16: E4M3,
 // E3M4, E2M5, E1M6 -- NVFP4 is E4M3 at block 16).  The stages hold FP4
-// codes and raw scale bytes, loaded straight into LDS as in k_gemm_mx4;
+// codes and raw scale bytes, loaded straight into LDS as in k_gemm_mx;
 // each wave converts its own fragments to f16 right before the matrix
 // instruction: the hardware FP4 -> f16 conversion (scale 1, exact) and one
 // packed f16 multiply by the block scale per two elements.  Eight waves
@@ -844,7 +610,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int r = 16 * (2 * wave + k) + (lane >> 2);
-        const int c = (lane & 3) ^ mx4_swz(r);
+        const int c = (lane & 3) ^ mx_swz<128>(r);
         const int64_t nr = n_base + r < N ? n_base + r : N - 1;
         const int64_t mr = m_base + r < M ? m_base + r : M - 1;
         srcw[k] = p.qb + nr * rowb + 16 * c;
@@ -894,14 +660,14 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wn * 128 + 32 * i + frow;
-            h.w[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+            h.w[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx_swz<128>(r)));
             h.sw[i] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssw + r * L::kScaleRow + 2 * c)
                                   : (uint32_t)ssw[r * L::kScaleRow + c];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int r = wm * 64 + 32 * j + frow;
-            h.a[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx4_swz(r)));
+            h.a[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx_swz<128>(r)));
             h.sa[j] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c)
                                   : (uint32_t)ssa[r * L::kScaleRow + c];
         }
