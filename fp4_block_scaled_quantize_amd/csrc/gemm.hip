@@ -875,30 +875,37 @@ __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i
     }
 }
 
-// NW waves per workgroup split K (wave w takes chunks w, w + NW, ...); each
-// wave keeps D chunks of W, their scales and the matching X fragments in
-// flight in a ring: the loads of chunk i + D are issued as chunk i is
+// NW waves per workgroup split K (wave w takes chunks w, w + NW, ...); the
+// workgroup owns RG groups of 16 weight rows, and each wave multiplies every
+// X fragment it loads against all RG groups (X is read once per 16 RG rows).
+// Each wave keeps D chunks of W, their scales and the matching X fragments
+// in flight in a ring: the loads of chunk i + D are issued as chunk i is
 // consumed, so neither operand waits on a round trip per chunk.
-template <int NW, int D, int BLOCK, bool SPLIT, bool POW2>
+template <int NW, int D, int RG, int BLOCK, bool SPLIT, bool POW2>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
-    __shared__ float red[NW][256];
+    __shared__ float red[NW][RG][256];
     __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // wave-uniform (scalar)
     const int r16 = lane & 15, grp = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * RG);
     const int64_t N = p.n, K = p.k, M = p.m;
-    const int64_t n = n0 + r16 < N ? n0 + r16 : N - 1;        // rows past N re-read the last row
     const int64_t rowb = K / 2, rows = K / BLOCK;
     const ScaleFmt fw{p.fw.ebits, p.fw.mbits, p.fw.bias, p.fw.maxcode, p.fw.smax, p.fw.is_e8m0};
     const float gw = p.gw[0];
     const float pw = split_pow2(gw);
     const float gres = gw / pw;
     for (int c = tid; c < 256; c += 64 * NW) sdec[c] = scale_decode_any((uint32_t)c, fw) * pw;
-    // 32-bit byte / element offsets from the operand bases (the ABI bounds W below 4 GiB)
-    const uint32_t woff = (uint32_t)(n * rowb) + 16u * grp;
-    const uint32_t soff = (uint32_t)(n * rows) + (BLOCK == 16 ? 2u * grp : (uint32_t)grp);
+    // 32-bit byte / element offsets from the operand bases (the ABI bounds W below 4 GiB);
+    // rows past N re-read the last row
+    uint32_t woff[RG], soff[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int64_t n = n0 + 16 * g + r16 < N ? n0 + 16 * g + r16 : N - 1;
+        woff[g] = (uint32_t)(n * rowb) + 16u * grp;
+        soff[g] = (uint32_t)(n * rows) + (BLOCK == 16 ? 2u * grp : (uint32_t)grp);
+    }
     // rows m >= M of the padded X tile read row M - 1: in bounds, and they
     // only feed output rows that are never stored
     const int64_t mrow = r16 < M ? r16 : M - 1;
@@ -908,8 +915,8 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     __syncthreads();
 
     struct Slot {
-        v4i w;
-        uint32_t sc;
+        v4i w[RG];
+        uint32_t sc[RG];
         v4i x[4];
     };
     // chunk min(i, mine - 1) of this wave.  Every load is unconditional (a
@@ -917,31 +924,39 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     // again), so the compiler can count loads in flight across the ring.
     auto issue = [&](int i, Slot& s) {
         const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
-        s.w = *reinterpret_cast<const v4i*>(p.qw + woff + kc * 64u);
-        s.sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff + kc * 8u)
-                           : (uint32_t)p.sw[soff + kc * 4u];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            s.w[g] = *reinterpret_cast<const v4i*>(p.qw + woff[g] + kc * 64u);
+            s.sc[g] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff[g] + kc * 8u)
+                                  : (uint32_t)p.sw[soff[g] + kc * 4u];
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) s.x[t] = *reinterpret_cast<const v4i*>(p.x + xoff + kc * 128u + 8u * t);
     };
 
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    auto chunk = [&](const Slot& sl) {
-        const float s0 = sdec[sl.sc & 0xFFu];
-        const float s1 = BLOCK == 16 ? sdec[(sl.sc >> 8) & 0xFFu] : s0;
+    v4f acc[RG];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
-            if (SPLIT) {
-                v4i hi, lo;
-                dq8_bf16_split((uint32_t)sl.w[t], st, hi, lo);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
-                                                              __builtin_bit_cast(v8bf, hi), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
-                                                              __builtin_bit_cast(v8bf, lo), acc, 0, 0, 0);
-            } else {
-                const v4i wt = dq8_bf16<POW2>((uint32_t)sl.w[t], st);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
-                                                              __builtin_bit_cast(v8bf, wt), acc, 0, 0, 0);
+    for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto chunk = [&](const Slot& sl) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const float s0 = sdec[sl.sc[g] & 0xFFu];
+            const float s1 = BLOCK == 16 ? sdec[(sl.sc[g] >> 8) & 0xFFu] : s0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
+                if (SPLIT) {
+                    v4i hi, lo;
+                    dq8_bf16_split((uint32_t)sl.w[g][t], st, hi, lo);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                                                                     __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                                                                     __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
+                } else {
+                    const v4i wt = dq8_bf16<POW2>((uint32_t)sl.w[g][t], st);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                                                                     __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
+                }
             }
         }
     };
@@ -962,40 +977,48 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
         for (int d = 0; d < D - 1; ++d)           // the last mine % D chunks
             if (i0 + d < mine) chunk(ring[d]);
     }
-    // acc[r] = D[m = 4 grp + r][n = r16]; fixed-order sum over the waves
+    // acc[g][r] = D[m = 4 grp + r][n = 16 g + r16]; fixed-order sum over the waves
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][g][lane * 4 + r] = acc[g][r];
     __syncthreads();
-    if (tid < 256) {
+    for (int e = tid; e < 256 * RG; e += 64 * NW) {
+        const int g = e >> 8, t = e & 255;
         float sum = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[w][tid];
-        const int l = tid >> 2, r = tid & 3;
-        const int64_t m = 4 * (l >> 4) + r, nn = n0 + (l & 15);
+        for (int w = 0; w < NW; ++w) sum += red[w][g][t];
+        const int l = t >> 2, r = t & 3;
+        const int64_t m = 4 * (l >> 4) + r, nn = n0 + 16 * g + (l & 15);
         if (m < M && nn < N) p.y[m * p.ldy + nn] = (uint16_t)f32_to_bf16_rne(sum * gres);
     }
 }
 
-template <int NW, int D>
+template <int NW, int D, int RG>
 static void launch_wo_cfg(const WoGemmLaunch& p, hipStream_t s)
 {
-    dim3 grid((unsigned)((p.n + 15) / 16)), block(64 * NW);
+    dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
     const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
     if (p.block == 16) {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, D, 16, false, false>), grid, block, 0, s, p);
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, false, false>), grid, block, 0, s, p);
     } else {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, D, 32, false, false>), grid, block, 0, s, p);
+        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, true, false>), grid, block, 0, s, p);
+        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, false, false>), grid, block, 0, s, p);
     }
 }
 
+constexpr int64_t kWoRg2MinWg = 512;     // workgroups needed before two row groups share X
+
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
-    // four waves split K; each keeps four 128-element chunks in flight
-    launch_wo_cfg<4, 4>(p, s);
+    // four waves split K; each keeps four 128-element chunks in flight.  With
+    // M > 1 two 16-row groups share each X fragment when that still leaves
+    // enough workgroups to fill the device.
+    if (p.m > 1 && (p.n + 31) / 32 >= kWoRg2MinWg) launch_wo_cfg<4, 4, 2>(p, s);
+    else launch_wo_cfg<4, 4, 1>(p, s);
     return hipGetLastError();
 }
 

@@ -554,7 +554,11 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
 // dequantize: y = RN(RN(e2m1 * s) * g), bf16 output rounded once more (RNE)
 // ---------------------------------------------------------------------------
 constexpr int kDQThreads = 256;
+constexpr int kDQUnroll = 4;                 // units per lane, loads issued together
 
+// Each wave dequantizes kDQUnroll * 64 consecutive units; unit j of a lane
+// is base + 64 j + lane, so every load and store instruction of a wave
+// covers a contiguous span.
 template <bool OUT_BF16, int BLOCK, bool E8M0>
 __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ scales,
@@ -562,30 +566,43 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
                                                            FastDiv upr, int64_t ld, int strided, ScaleFmt f,
                                                            void* __restrict__ y)
 {
-    const uint32_t u = blockIdx.x * kDQThreads + threadIdx.x;
-    if (u >= nunits) return;
-    const float g = tensor_scale[0];
-    const uint32_t w = q[u];
-    const uint32_t sc = scales[u / (BLOCK / 8)];
-    const float s = scale_decode_any(sc, f);
-    float o[8];
+    constexpr int U = kDQUnroll;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = blockIdx.x * (kDQThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t base = wave * (64u * U);
+    uint32_t w[U], sc[U];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        float t = e2m1_value((w >> (4 * k)) & 0xFu) * s;
-        o[k] = t * g;
+    for (int j = 0; j < U; ++j) {
+        const uint32_t u = base + j * 64 + lane;
+        const uint32_t uu = u < nunits ? u : nunits - 1;           // in bounds; not stored
+        w[j] = __builtin_nontemporal_load(q + uu);
+        sc[j] = scales[uu / (BLOCK / 8)];
     }
-    const uint64_t off = unit_offset(u, strided, upr, ld);
-    if (OUT_BF16) {
-        uint4 r;
-        r.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-        r.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-        r.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
-        r.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
-        *(uint4*)((uint16_t*)y + off) = r;
-    } else {
-        float4* p = (float4*)((float*)y + off);
-        p[0] = make_float4(o[0], o[1], o[2], o[3]);
-        p[1] = make_float4(o[4], o[5], o[6], o[7]);
+    const float g = tensor_scale[0];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const uint32_t u = base + j * 64 + lane;
+        if (u >= nunits) continue;
+        const float s = scale_decode_any(sc[j], f);
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float t = e2m1_value((w[j] >> (4 * k)) & 0xFu) * s;
+            o[k] = t * g;
+        }
+        const uint64_t off = unit_offset(u, strided, upr, ld);
+        if (OUT_BF16) {
+            u32x4 r;
+            r.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+            r.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            r.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
+            r.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
+            __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>((uint16_t*)y + off));
+        } else {
+            f32x4* pp = reinterpret_cast<f32x4*>((float*)y + off);
+            __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, pp);
+            __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, pp + 1);
+        }
     }
 }
 
@@ -593,7 +610,8 @@ template <bool OUT_BF16, int BLOCK>
 static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
-    uint32_t blocks = (nunits + kDQThreads - 1) / kDQThreads;
+    const uint32_t per_block = kDQThreads * kDQUnroll;
+    uint32_t blocks = (nunits + per_block - 1) / per_block;
     if (blocks == 0) blocks = 1;
     if (f.is_e8m0)
         hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true>), dim3(blocks), dim3(kDQThreads), 0, s,
