@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "d2040afae6722e11f261ea66f5f2cddf27c17ffe3c5c075d4417481e3c294957",
-    "read_bytes": 33652199,
+    "sha256": "0ff30c0c97570fa27439f8039b591d2e9cd8ceb8e2c1137f6b1266c8ffa01f88",
+    "read_bytes": 33786413,
     "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }

@@ -126,7 +126,7 @@ class QTensor:
 
 class AmaxState:
     """Per-tensor amax state: refreshed every `interval` calls (CURRENT uses
-    it too, refreshing on every call).  Owns 3328 bytes of device memory."""
+    it too, refreshing on every call).  Owns 17664 bytes of device memory."""
 
     def __init__(self, interval: int = 50):
         h = ctypes.c_void_p()

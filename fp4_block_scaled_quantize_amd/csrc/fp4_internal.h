@@ -22,20 +22,22 @@ bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 //    the amax kernel; the quantize kernel of the same call reduces them and
 //    stores the result in `stored`, which calls between refreshes read.
 //  - epoch/slot: the single-pass refresh exchanges per-workgroup maxima
-//    through `slot` (64-bit {epoch, max bits} words) within one launch;
-//    `epoch` advances once per such launch, on the device.
+//    through `slot` (64-bit {epoch, max bits} words, one per 64-byte
+//    segment so that stores of different workgroups never share a line)
+//    within one launch; `epoch` advances once per such launch, on the device.
 //  - error: set when a single-pass exchange timed out.
 constexpr int kAmaxParts = 256;
 constexpr int kXchgSlots = 256;
+constexpr int kXchgStride = 8;          // 64-bit words between slots (64 bytes)
 struct AmaxDev {
     float partial[kAmaxParts];
     float stored;
     uint32_t epoch;
     uint32_t error;
     uint32_t pad[61];
-    uint64_t slot[kXchgSlots];
+    uint64_t slot[kXchgSlots * kXchgStride];
 };
-static_assert(sizeof(AmaxDev) == 3328, "amax state layout");
+static_assert(sizeof(AmaxDev) == 17664, "amax state layout");
 
 struct QuantLaunch {
     const void* x;

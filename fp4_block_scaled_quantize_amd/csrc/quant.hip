@@ -270,7 +270,7 @@ __device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
     if (wv == 0) {
         const uint32_t mm = wave_umax(lane < T / 64 ? wmax[lane] : 0u);
         if (lane == 0)
-            __hip_atomic_store(&st->slot[blockIdx.x], ((uint64_t)e << 32) | mm, __ATOMIC_RELAXED,
+            __hip_atomic_store(&st->slot[blockIdx.x * kXchgStride], ((uint64_t)e << 32) | mm, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t nwg = gridDim.x;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -280,7 +280,7 @@ __device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
             tm = 0;
             bool mine = true;
             for (uint32_t i = lane; i < nwg; i += 64) {
-                const uint64_t w = __hip_atomic_load(&st->slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t w = __hip_atomic_load(&st->slot[i * kXchgStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 mine = mine && (uint32_t)(w >> 32) == e;
                 tm = tm > (uint32_t)w ? tm : (uint32_t)w;
             }

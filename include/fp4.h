@@ -20,7 +20,7 @@
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller (e.g. torch
  *     tensors).  The library never allocates or frees caller memory and
- *     allocates nothing per call; an fp4_amax_state owns 3328 bytes of
+ *     allocates nothing per call; an fp4_amax_state owns 17664 bytes of
  *     device memory allocated at creation.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch is asynchronous on it; no call synchronizes the host
@@ -108,7 +108,7 @@ typedef struct fp4_tensor {
 
 /* Per-tensor amax state (ue5m3-fp4-pretraining "Что сделали": the maximum
  * is refreshed every `interval` steps and the stored value used between).
- * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 3328
+ * Required by CURRENT (which refreshes on every call) and DELAYED.  Owns 17664
  * bytes of device memory on the device current at creation: the stored
  * amax, the per-workgroup partial maxima of the refresh and the exchange
  * words of the single-pass refresh.  Not thread-safe; calls that use one
