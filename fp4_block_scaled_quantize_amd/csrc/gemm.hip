@@ -274,10 +274,10 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
             sad[j] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssa + 8 * r)
                                : (uint64_t)*reinterpret_cast<const uint32_t*>(ssa + 4 * r);
         }
-#pragma unroll
-        for (int ks = 0; ks < BK / 64; ++ks) {
+        // fragments of chunk pair ks (16-byte chunk c = 2 ks + khalf of each
+        // row) are read while the products of pair ks - 1 are issued
+        auto read_frags = [&](int ks, v4i (&wf)[4], v4i (&af)[2]) {
             const int c = 2 * ks + khalf;
-            v4i wf[4], af[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = wn * 128 + 32 * i + frow;
@@ -288,18 +288,33 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
                 const int r = wm * 64 + 32 * j + frow;
                 af[j] = *reinterpret_cast<const v4i*>(st + L::Codes + r * L::RB + 16 * (c ^ mx_swz<BK>(r)));
             }
-            const int sh = 8 * c;
+        };
+        v4i wf[2][4], af[2][2];
+        read_frags(0, wf[0], af[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 64; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < BK / 64) read_frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+            const int sh = 8 * (2 * ks + khalf);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sw = (int)((swd[i] >> sh) & 0xFFu);
-                const v8i wv = {wf[i][0], wf[i][1], wf[i][2], wf[i][3], 0, 0, 0, 0};
+                const v8i wv = {wf[cur][i][0], wf[cur][i][1], wf[cur][i][2], wf[cur][i][3], 0, 0, 0, 0};
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int sa = (int)((sad[j] >> sh) & 0xFFu);
-                    const v8i av = {af[j][0], af[j][1], af[j][2], af[j][3], 0, 0, 0, 0};
+                    const v8i av = {af[cur][j][0], af[cur][j][1], af[cur][j][2], af[cur][j][3], 0, 0, 0, 0};
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0, sa);
                 }
             }
+            if (ks + 1 < BK / 64) {
+#pragma unroll
+                for (int q = 0; q < 6; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one matrix instruction
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read of the next pair
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
