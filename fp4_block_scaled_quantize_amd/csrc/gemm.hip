@@ -831,14 +831,27 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // (quant_prune_distill/574 "Эксперименты": weight-only NVFP4 with a
 // memory-bound kernel for small-batch generation).
 //
-// A workgroup owns 16 rows of W and 8 waves that split K in 128-element
-// chunks; every byte of W is read once, streamed with one 16-byte load per
-// lane per chunk, dequantized exactly to bf16 in registers and multiplied on
-// the 16x16x32 bf16 matrix cores against X (M padded to 16 with zeros).  The
-// dot product is a sum, so the K order inside a chunk is free: lane group g
-// (lane / 16) takes the 32 contiguous elements [32 g, 32 g + 32) of the
-// chunk and feeds 8 of them to each of the chunk's four MFMAs, with X read
-// in the same order.  The eight waves' partial tiles are summed in LDS in a
+// A workgroup owns RG groups of 16 rows of W; its NW waves split K in
+// 128-element chunks (wave w takes chunks w, w + NW, ...), and every byte of
+// W is read once.  Each chunk is dequantized exactly to bf16 in registers
+// and multiplied on the 16x16x32 bf16 matrix cores against X (M padded to 16
+// by repeating row M - 1, whose outputs are dropped).  The dot product is a
+// sum, so the K order inside a chunk is free: lane group g (lane / 16) takes
+// the 32 contiguous elements [32 g, 32 g + 32) of the chunk and feeds 8 of
+// them to each of the chunk's four MFMAs, with X read in the same order.
+//
+// The operands reach the registers through LDS.  In the fragment layout
+// every four consecutive lanes hold four different rows, and the texture
+// address unit takes such a load one lane per cycle: 64 cycles per KiB of W,
+// as many again for the chunk's 2-byte scales and up to four times that for
+// X, against the ~13 bytes per cycle per CU that HBM delivers.  So each wave
+// streams its chunks with direct-to-LDS loads in an order that keeps every
+// four lanes on one 64-byte run of a row (four lanes per cycle) into a
+// private ring of D slots (W, its scales, the chunk's M rows of X), and reads
+// the fragments from there.  A wave reads only what it loaded itself, after
+// the load counter says it has landed, so the ring needs no barrier.  The
+// 16-byte pieces of a row are XOR-swizzled so that the fragment reads are
+// free of bank conflicts.  The waves' partial tiles are summed in LDS in a
 // fixed order (deterministic).
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -890,16 +903,34 @@ __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i
     }
 }
 
-// NW waves per workgroup split K (wave w takes chunks w, w + NW, ...); the
-// workgroup owns RG groups of 16 weight rows, and each wave multiplies every
-// X fragment it loads against all RG groups (X is read once per 16 RG rows).
-// Each wave keeps D chunks of W, their scales and the matching X fragments
-// in flight in a ring: the loads of chunk i + D are issued as chunk i is
-// consumed, so neither operand waits on a round trip per chunk.
-template <int NW, int D, int RG, int BLOCK, bool SPLIT, bool POW2>
+// One ring slot of the weight-only GEMM (byte offsets).  XQ = 0: M == 1,
+// the single X row arrives by 4-byte loads; else XQ loads of four 256-byte
+// X rows each.
+template <int RG, int XQ>
+struct WoSlot {
+    static constexpr int W = 0;                        // row r of group g at 1024 g + 64 r
+    static constexpr int SC = RG * 1024;               // the rows' scales for the chunk (<= 256 bytes)
+    static constexpr int X = SC + 256;                 // 256 bytes (128 bf16) per X row
+    static constexpr int XRows = XQ == 0 ? 1 : 4 * XQ;
+    static constexpr int Bytes = X + 256 * XRows;
+    static constexpr int Loads = RG + 1 + (XQ == 0 ? 1 : XQ);   // direct-to-LDS loads per chunk
+};
+
+__device__ __forceinline__ int wo_swz(int r) { return (r >> 1) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
-    __shared__ float red[NW][RG][256];
+    using S = WoSlot<RG, XQ>;
+    static_assert((D - 1) * S::Loads < 64, "loads in flight exceed the counter");
+    extern __shared__ __align__(16) uint8_t wo_ring[];
     __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);       // wave-uniform (scalar)
@@ -912,87 +943,142 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     const float pw = split_pow2(gw);
     const float gres = gw / pw;
     for (int c = tid; c < 256; c += 64 * NW) sdec[c] = scale_decode_any((uint32_t)c, fw) * pw;
-    // 32-bit byte / element offsets from the operand bases (the ABI bounds W below 4 GiB);
-    // rows past N re-read the last row
-    uint32_t woff[RG], soff[RG];
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        const int64_t n = n0 + 16 * g + r16 < N ? n0 + 16 * g + r16 : N - 1;
-        woff[g] = (uint32_t)(n * rowb) + 16u * grp;
-        soff[g] = (uint32_t)(n * rows) + (BLOCK == 16 ? 2u * grp : (uint32_t)grp);
-    }
-    // rows m >= M of the padded X tile read row M - 1: in bounds, and they
-    // only feed output rows that are never stored
-    const int64_t mrow = r16 < M ? r16 : M - 1;
-    const uint32_t xoff = (uint32_t)(mrow * p.ldx) + 32u * grp;
+    uint8_t* const ring = wo_ring + wave * (D * S::Bytes);
     const int nchunks = (int)(K / 128);
     const int mine = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;   // chunks wave, wave + NW, ...
-    __syncthreads();
 
-    struct Slot {
-        v4i w[RG];
-        uint32_t sc[RG];
-        v4i x[4];
-    };
-    // chunk min(i, mine - 1) of this wave.  Every load is unconditional (a
-    // prefetch past the end re-reads the last chunk, which is not used
-    // again), so the compiler can count loads in flight across the ring.
-    auto issue = [&](int i, Slot& s) {
-        const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
+    // Global sources of this lane's direct-to-LDS loads for chunk 0, as
+    // 32-bit offsets (the ABI bounds W below 4 GiB); rows past N re-read row
+    // N - 1, rows of X past M re-read row M - 1 (in bounds, never stored).
+    //  W: lane l -> row l / 4 of each group, 16-byte piece (l % 4) ^ swz(row),
+    //     landing at 64 row + 16 (l % 4);
+    //  scales: 128 / BLOCK bytes per row; block 16: lane l -> 4-byte half
+    //     l % 2 of row l / 2, block 32: lane l -> row l;
+    //  X: XQ = 0: lane l -> dword l of row 0; else load q, lane l -> row
+    //     m = 4 q + l / 16, piece (l % 16) ^ (m % 8), landing at 256 m + 16 (l % 16).
+    constexpr int SCB = 128 / BLOCK;
+    constexpr int ScLanes = 16 * RG * SCB / 4;
+    uint32_t wsrc[RG];
 #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            s.w[g] = *reinterpret_cast<const v4i*>(p.qw + woff[g] + kc * 64u);
-            s.sc[g] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sw + soff[g] + kc * 8u)
-                                  : (uint32_t)p.sw[soff[g] + kc * 4u];
+    for (int g = 0; g < RG; ++g) {
+        const int r = lane >> 2;
+        const int64_t n = n0 + 16 * g + r < N ? n0 + 16 * g + r : N - 1;
+        wsrc[g] = (uint32_t)(n * rowb) + 16u * (uint32_t)((lane & 3) ^ wo_swz(r));
+    }
+    uint32_t ssrc;
+    {
+        const int R = BLOCK == 16 ? lane >> 1 : lane;
+        const int64_t rr = R < 16 * RG ? R : 16 * RG - 1;
+        const int64_t n = n0 + rr < N ? n0 + rr : N - 1;
+        ssrc = (uint32_t)(n * rows) + (BLOCK == 16 ? 4u * (uint32_t)(lane & 1) : 0u);
+    }
+    constexpr int XL = XQ == 0 ? 1 : XQ;
+    const uint16_t* xsrc[XL];
+#pragma unroll
+    for (int q = 0; q < XL; ++q) {
+        if (XQ == 0) {
+            xsrc[q] = p.x + 2 * lane;
+        } else {
+            const int m = 4 * q + (lane >> 4);
+            const int64_t mr = m < M ? m : M - 1;
+            xsrc[q] = p.x + mr * p.ldx + 8 * ((lane & 15) ^ (m & 7));
         }
+    }
+    // chunk min(i, mine - 1) of this wave into slot d.  Every load is issued
+    // unconditionally (a prefetch past the end re-reads the last chunk), so
+    // the number in flight per slot is fixed.
+    auto issue = [&](int i, int d) {
+        const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
+        uint8_t* const sl = ring + d * S::Bytes;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s.x[t] = *reinterpret_cast<const v4i*>(p.x + xoff + kc * 128u + 8u * t);
+        for (int g = 0; g < RG; ++g) dma16(p.qw + wsrc[g] + kc * 64u, sl + S::W + 1024 * g);
+        if (lane < ScLanes) dma4(p.sw + ssrc + kc * (uint32_t)SCB, sl + S::SC);
+        if (XQ == 0) {
+            dma4(xsrc[0] + kc * 128u, sl + S::X);
+        } else {
+#pragma unroll
+            for (int q = 0; q < XL; ++q) dma16(xsrc[q] + kc * 128u, sl + S::X + 1024 * q);
+        }
     };
+
+    // this lane's fragment addresses inside a slot
+    const int mr = r16 < M ? r16 : (int)M - 1;
+    int xoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        xoff[t] = S::X + (XQ == 0 ? 16 * (4 * grp + t) : 256 * mr + 16 * ((4 * grp + t) ^ (mr & 7)));
+    const int woff = S::W + 64 * r16 + 16 * (grp ^ wo_swz(r16));
+    const int soff = S::SC + (BLOCK == 16 ? 8 * r16 + 2 * grp : 4 * r16 + grp);
 
     v4f acc[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
-    auto chunk = [&](const Slot& sl) {
+    auto consume = [&](int d) {
+        const uint8_t* const sl = ring + d * S::Bytes;
+        v4i xf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xf[t] = *reinterpret_cast<const v4i*>(sl + xoff[t]);
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-            const float s0 = sdec[sl.sc[g] & 0xFFu];
-            const float s1 = BLOCK == 16 ? sdec[(sl.sc[g] >> 8) & 0xFFu] : s0;
+            const v4i wv = *reinterpret_cast<const v4i*>(sl + woff + 1024 * g);
+            const uint32_t sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + soff + 128 * g)
+                                            : (uint32_t)sl[soff + 64 * g];
+            const float s0 = sdec[sc & 0xFFu];
+            const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
                 if (SPLIT) {
                     v4i hi, lo;
-                    dq8_bf16_split((uint32_t)sl.w[g][t], st, hi, lo);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                    dq8_bf16_split((uint32_t)wv[t], st, hi, lo);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
                 } else {
-                    const v4i wt = dq8_bf16<POW2>((uint32_t)sl.w[g][t], st);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sl.x[t]),
+                    const v4i wt = dq8_bf16<POW2>((uint32_t)wv[t], st);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
                 }
             }
         }
+        // the slot's reads have returned before a load may overwrite it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
 
     if (mine > 0) {
-        Slot ring[D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) issue(d, ring[d]);
+        for (int d = 0; d < D; ++d) issue(d, d);
+    }
+    // sdec is complete once every wave's LDS writes are; a plain barrier (no
+    // fence) leaves the ring's loads in flight
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (mine > 0) {
         int i0 = 0;
         for (; i0 + D <= mine; i0 += D) {        // whole groups: no conditions inside
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                chunk(ring[d]);
-                issue(i0 + d + D, ring[d]);
+                wait_vmcnt<(D - 1) * S::Loads>();
+                consume(d);
+                issue(i0 + d + D, d);
             }
         }
-#pragma unroll
-        for (int d = 0; d < D - 1; ++d)           // the last mine % D chunks
-            if (i0 + d < mine) chunk(ring[d]);
+        // the last mine % D chunks: slot d has the loads of slots d + 1 .. D - 1 behind it
+        if (i0 + 0 < mine) { wait_vmcnt<(D - 1) * S::Loads>(); consume(0); }
+        if (D > 2 && i0 + 1 < mine) { wait_vmcnt<(D > 2 ? (D - 2) * S::Loads : 0)>(); consume(1); }
+        if (D > 3 && i0 + 2 < mine) { wait_vmcnt<(D > 3 ? (D - 3) * S::Loads : 0)>(); consume(2); }
+        if (D > 4 && i0 + 3 < mine) { wait_vmcnt<(D > 4 ? (D - 4) * S::Loads : 0)>(); consume(3); }
+        if (D > 5 && i0 + 4 < mine) { wait_vmcnt<(D > 5 ? (D - 5) * S::Loads : 0)>(); consume(4); }
+        if (D > 6 && i0 + 5 < mine) { wait_vmcnt<(D > 6 ? (D - 6) * S::Loads : 0)>(); consume(5); }
+        if (D > 7 && i0 + 6 < mine) { wait_vmcnt<(D > 7 ? (D - 7) * S::Loads : 0)>(); consume(6); }
     }
+    // every wave's loads have landed and its reads returned before the ring
+    // is reused for the partial tiles
+    wait_vmcnt<0>();
+    __syncthreads();
     // acc[g][r] = D[m = 4 grp + r][n = 16 g + r16]; fixed-order sum over the waves
+    float (*red)[RG][256] = reinterpret_cast<float (*)[RG][256]>(wo_ring);
 #pragma unroll
     for (int g = 0; g < RG; ++g)
 #pragma unroll
@@ -1009,32 +1095,59 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     }
 }
 
-template <int NW, int D, int RG>
-static void launch_wo_cfg(const WoGemmLaunch& p, hipStream_t s)
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2>
+static hipError_t launch_wo_k(const WoGemmLaunch& p, hipStream_t s)
 {
-    dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
-    const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
-    if (p.block == 16) {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 16, false, false>), grid, block, 0, s, p);
-    } else {
-        if (split) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, true, false>), grid, block, 0, s, p);
-        else if (pow2) hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, false, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, 32, false, false>), grid, block, 0, s, p);
+    constexpr size_t sh = (size_t)NW * D * WoSlot<RG, XQ>::Bytes;   // the ring, later the partial tiles
+    static_assert(sh >= sizeof(float) * NW * RG * 256, "partial tiles fit the ring");
+    static_assert(sh + sizeof(float) * 256 <= 160 * 1024, "LDS");
+    if (sh > 64 * 1024) {
+        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2>, sh);
+        if (e != hipSuccess) return e;
     }
+    const dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
+    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2>), grid, block, sh, s, p);
+    return hipGetLastError();
 }
 
-constexpr int64_t kWoRg2MinWg = 512;     // workgroups needed before two row groups share X
+template <int NW, int D, int RG, int XQ>
+static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
+{
+    const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
+    if (p.block == 16) {
+        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false>(p, s);
+        if (pow2) return launch_wo_k<NW, D, RG, XQ, 16, false, true>(p, s);
+        return launch_wo_k<NW, D, RG, XQ, 16, false, false>(p, s);
+    }
+    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false>(p, s);
+    if (pow2) return launch_wo_k<NW, D, RG, XQ, 32, false, true>(p, s);
+    return launch_wo_k<NW, D, RG, XQ, 32, false, false>(p, s);
+}
 
+// Ring shape per problem class: NW waves, D slots per wave, RG row groups.
+template <int NW, int D, int RG, int XQ>
+static hipError_t launch_wo_fit(const WoGemmLaunch& p, hipStream_t s)
+{
+    if constexpr ((size_t)NW * D * WoSlot<RG, XQ>::Bytes + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ>(p, s);
+    else return launch_wo_x<4, 2, RG, XQ>(p, s);
+}
+
+constexpr int64_t kWoManyGroups = 512;   // 16-row groups that fill the device on their own
+
+// Per problem class (measured on the Qwen-2.5 7B MLP decode shapes):
+//  M = 1: four waves with four slots each; with fewer than 512 row groups
+//   eight waves, so that the single workgroup per CU still keeps 32 chunks
+//   in flight.
+//  M > 1 with many row groups: two row groups share every X chunk; for
+//   M > 8 the slot is 6.4 KB and two slots per wave keep three workgroups
+//   per CU resident.
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
-    // four waves split K; each keeps four 128-element chunks in flight.  With
-    // M > 1 two 16-row groups share each X fragment when that still leaves
-    // enough workgroups to fill the device.
-    if (p.m > 1 && (p.n + 31) / 32 >= kWoRg2MinWg) launch_wo_cfg<4, 4, 2>(p, s);
-    else launch_wo_cfg<4, 4, 1>(p, s);
-    return hipGetLastError();
+    const bool many = (p.n + 15) / 16 >= kWoManyGroups;
+    if (p.m == 1) return many ? launch_wo_fit<4, 4, 1, 0>(p, s) : launch_wo_fit<8, 4, 1, 0>(p, s);
+    if (p.m <= 4) return many ? launch_wo_fit<4, 4, 2, 1>(p, s) : launch_wo_fit<4, 4, 1, 1>(p, s);
+    if (p.m <= 8) return many ? launch_wo_fit<4, 4, 2, 2>(p, s) : launch_wo_fit<4, 4, 1, 2>(p, s);
+    return many ? launch_wo_fit<4, 2, 2, 4>(p, s) : launch_wo_fit<4, 4, 1, 4>(p, s);
 }
 
 }  // namespace fp4

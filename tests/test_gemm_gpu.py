@@ -175,6 +175,18 @@ def test_wo_gemm_formats(fmt, block):
     _check_wo(y, x, w, tag=f"wo {fmt}/{block}")
 
 
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e8m0", 32), ("e1m6", 32)])
+def test_wo_gemm_many_row_groups(fmt, block):
+    """N = 8200: 513 groups of 16 rows (the launch that pairs row groups),
+    the last pair ragged; M in each X-load class."""
+    qw, w = _quant_both(_normal(8200, 256, 15, 0.02, dtype="bf16"), block, fmt)
+    for m in (1, 2, 5, 12):
+        x = _normal(m, 256, 16 + m, dtype="bf16")
+        y = fq.fp4_wo_gemm(to_device(x), qw)
+        torch.cuda.synchronize()
+        _check_wo(y, x, w, tag=f"wo many {fmt}/{block} m={m}")
+
+
 @pytest.mark.parametrize("wname", ["up", "down"])
 def test_wo_gemm_qwen_decode_shapes(wname):
     """Qwen-2.5 decode shapes: W [18944, 3584] / [3584, 18944] NVFP4 E4M3
