@@ -181,6 +181,55 @@ __device__ __forceinline__ void store_tile_4x2(const v16f (&acc)[4][2], float g,
     }
 }
 
+// Epilogue of the 256 x 256 tiles through LDS (the stage buffers are free by
+// then).  Each wave writes its scaled bf16 sub-tile, whose lanes each hold
+// one column m and runs of four n, into a row-major image of the C tile
+// (rows padded by 16 bytes); then every thread stores 16-byte pieces of C
+// rows, so four consecutive lanes cover 64 contiguous bytes and a wave two
+// whole 512-byte rows.  The caller has retired every load into LDS.
+constexpr int kCTileRow = 2 * kTile + 16;           // bytes per LDS row of the C image
+constexpr int kCTileBytes = kTile * kCTileRow;
+
+__device__ __forceinline__ void store_tile_4x2_lds(const v16f (&acc)[4][2], float g, uint8_t* __restrict__ img,
+                                                   uint16_t* __restrict__ c, int64_t ldc, int wm_off, int wn_off,
+                                                   int64_t m_base, int64_t n_base, int64_t M, int64_t N)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    __syncthreads();                                 // every wave is done reading the stages
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int ml = wm_off + 32 * j + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn_off + 32 * i + 8 * q + 4 * (lane >> 5);
+                uint2 v;
+                v.x = f32_to_bf16_rne(acc[i][j][4 * q + 0] * g) | (f32_to_bf16_rne(acc[i][j][4 * q + 1] * g) << 16);
+                v.y = f32_to_bf16_rne(acc[i][j][4 * q + 2] * g) | (f32_to_bf16_rne(acc[i][j][4 * q + 3] * g) << 16);
+                *reinterpret_cast<uint2*>(img + ml * kCTileRow + 2 * nl) = v;
+            }
+        }
+    }
+    __syncthreads();
+    const bool vec = ((ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(c) & 15) == 0);
+    for (int piece = tid; piece < kTile * (kTile / 8); piece += (int)blockDim.x) {
+        const int ml = piece / (kTile / 8), cb = piece % (kTile / 8);
+        const int64_t m = m_base + ml, n = n_base + 8 * cb;
+        if (m >= M || n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(img + ml * kCTileRow + 16 * cb);
+        uint16_t* dst = c + m * ldc + n;
+        if (vec && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 template <int BK, int NS>
 __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
 {
@@ -318,8 +367,9 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(NS * L::Bytes >= kCTileBytes, "the C image fits the stage buffers");
     const float g = p.ga[0] * p.gb[0];
-    store_tile_4x2(acc, g, p.c, p.ldc, m_base + wm * 64, n_base + wn * 128, M, N);
+    store_tile_4x2_lds(acc, g, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
 
 // Kernels with more than 64 KiB of dynamic LDS must opt in once per device.
@@ -765,8 +815,9 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
         run_half(g, f, true, cw, ca);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(NS * L::kBytes >= kCTileBytes, "the C image fits the stage buffers");
     const float gg = p.ga[0] * p.gb[0];
-    store_tile_4x2(acc, gg, p.c, p.ldc, m_base + wm * 64, n_base + wn * 128, M, N);
+    store_tile_4x2_lds(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
 
 #ifndef FP4_NV_NS
