@@ -133,7 +133,14 @@ struct MxStage {
     static constexpr int SRow = BK / 32;              // E8M0 bytes per row per stage
     static constexpr int Scales = kTile * SRow;       // per operand
     static constexpr int SDma = 2 * Scales / (4 * kMx4Threads);   // dword DMAs per lane
-    static constexpr int Bytes = 2 * Codes + 2 * Scales;
+    // 256-element stages keep the scales out of the stage: 32 bytes per row
+    // (four stages) arrive at once, two lanes per row, into one of two
+    // group buffers after the stages
+    static constexpr bool Grouped = BK == 256;
+    static constexpr int GroupStages = 4;
+    static constexpr int GroupRow = GroupStages * SRow;               // 32 bytes
+    static constexpr int GroupBytes = 2 * kTile * GroupRow;           // W then A: 16 KiB
+    static constexpr int Bytes = 2 * Codes + (Grouped ? 0 : 2 * Scales);
 };
 
 // Position of 16-byte chunk c of row r: c ^ mx_swz(r).  64-byte rows:
@@ -263,17 +270,29 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
     // (0: W, 1: A), dword 64 wave + lane = (row, half).
     const uint8_t* srcs[L::SDma];
     int sdst[L::SDma];
+    // grouped scales: DMA j fills operand j, lanes 2 r + h take 16-byte half
+    // h of row r's 32 bytes; a half past the row end (the last, partial
+    // group) is read from the row's last 16 bytes instead
+    const uint8_t* gsrc[2];
+    int ghalf = 0;
+    if (L::Grouped) {
+        const int r = tid >> 1;
+        ghalf = tid & 1;
+        gsrc[0] = p.sb + row_w(r) * rows;
+        gsrc[1] = p.sa + row_a(r) * rows;
+    }
     if (BK == 128) {
         const int r = 64 * (wave & 3) + lane;
         srcs[0] = wave < 4 ? p.sb + row_w(r) * rows : p.sa + row_a(r) * rows;
         sdst[0] = 2 * L::Codes + (wave < 4 ? 0 : L::Scales) + 256 * (wave & 3);
-    } else {
+    } else if (!L::Grouped) {
         const int q = 64 * wave + lane, r = q >> 1, d = q & 1;
         srcs[0] = p.sb + row_w(r) * rows + 4 * d;
         srcs[L::SDma - 1] = p.sa + row_a(r) * rows + 4 * d;
         sdst[0] = 2 * L::Codes + 256 * wave;
         sdst[L::SDma - 1] = 2 * L::Codes + L::Scales + 256 * wave;
     }
+    uint8_t* const gbuf = smem + NS * L::Bytes;
 
     // stage kt into buffer buf; past the last stage the last one is loaded
     // again (into a buffer that is no longer read), so every wave always has
@@ -286,10 +305,20 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
             dma16(srcw[k] + (int64_t)ks * L::RB, st + 1024 * (L::NI * wave + k));
             dma16(srca[k] + (int64_t)ks * L::RB, st + L::Codes + 1024 * (L::NI * wave + k));
         }
+        if (!L::Grouped) {
 #pragma unroll
-        for (int j = 0; j < L::SDma; ++j) dma4(srcs[j] + (int64_t)ks * L::SRow, st + sdst[j]);
+            for (int j = 0; j < L::SDma; ++j) dma4(srcs[j] + (int64_t)ks * L::SRow, st + sdst[j]);
+        } else if (kt % L::GroupStages == 0 && kt < KT) {
+            // group kt / 4 (stages kt .. kt + 3) with the codes of its first stage
+            const int64_t off = (int64_t)(kt / L::GroupStages) * L::GroupRow + 16 * ghalf;
+            const int64_t o = off + 16 <= rows ? off : rows - 16;
+            uint8_t* const gb = gbuf + ((kt / L::GroupStages) & 1) * L::GroupBytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma16(gsrc[j] + o, gb + j * (L::GroupBytes / 2) + 1024 * wave);
+        }
     };
-    constexpr int kLoads = 2 * L::NI + L::SDma;
+    static_assert(!L::Grouped || NS == 2, "grouped scales rely on waiting for every load each stage");
+    constexpr int kLoads = 2 * L::NI + (L::Grouped ? 0 : L::SDma);
 
     v16f acc[4][2];
 #pragma unroll
@@ -308,20 +337,34 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         __builtin_amdgcn_s_barrier();        // no fence: a fence would wait for every load in flight
         issue(kt + NS - 1, (kt + NS - 1) % NS);
         const uint8_t* st = smem + (kt % NS) * L::Bytes;
-        const uint8_t* ssw = st + 2 * L::Codes;
-        const uint8_t* ssa = ssw + L::Scales;
         uint64_t swd[4], sad[2];
+        if (L::Grouped) {
+            // stage kt's 8 bytes of row r: 32 r + 8 (kt % 4), 8 further on for
+            // the last stage of an odd count (its half was read from the row end)
+            const uint8_t* gb = gbuf + ((kt / L::GroupStages) & 1) * L::GroupBytes;
+            const int so = 8 * (kt % L::GroupStages) + ((kt == KT - 1 && (KT & 1)) ? 8 : 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wn * 128 + 32 * i + frow;
-            swd[i] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssw + 8 * r)
-                               : (uint64_t)*reinterpret_cast<const uint32_t*>(ssw + 4 * r);
-        }
+            for (int i = 0; i < 4; ++i)
+                swd[i] = *reinterpret_cast<const uint64_t*>(gb + L::GroupRow * (wn * 128 + 32 * i + frow) + so);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = wm * 64 + 32 * j + frow;
-            sad[j] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssa + 8 * r)
-                               : (uint64_t)*reinterpret_cast<const uint32_t*>(ssa + 4 * r);
+            for (int j = 0; j < 2; ++j)
+                sad[j] = *reinterpret_cast<const uint64_t*>(gb + L::GroupBytes / 2 +
+                                                            L::GroupRow * (wm * 64 + 32 * j + frow) + so);
+        } else {
+            const uint8_t* ssw = st + 2 * L::Codes;
+            const uint8_t* ssa = ssw + L::Scales;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wn * 128 + 32 * i + frow;
+                swd[i] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssw + 8 * r)
+                                   : (uint64_t)*reinterpret_cast<const uint32_t*>(ssw + 4 * r);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = wm * 64 + 32 * j + frow;
+                sad[j] = BK == 256 ? *reinterpret_cast<const uint64_t*>(ssa + 8 * r)
+                                   : (uint64_t)*reinterpret_cast<const uint32_t*>(ssa + 4 * r);
+            }
         }
         // fragments of chunk pair ks (16-byte chunk c = 2 ks + khalf of each
         // row) are read while the products of pair ks - 1 are issued
@@ -367,7 +410,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    static_assert(NS * L::Bytes >= kCTileBytes, "the C image fits the stage buffers");
+    static_assert(NS * L::Bytes + (L::Grouped ? 2 * L::GroupBytes : 0) >= kCTileBytes, "the C image fits the LDS");
     const float g = p.ga[0] * p.gb[0];
     store_tile_4x2_lds(acc, g, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
@@ -383,7 +426,8 @@ static hipError_t allow_lds(K kernel, size_t bytes)
 template <int BK, int NS>
 static hipError_t launch_mx(const GemmLaunch& p, hipStream_t s)
 {
-    constexpr size_t sh = (size_t)NS * MxStage<BK>::Bytes;
+    constexpr size_t sh = (size_t)NS * MxStage<BK>::Bytes + (MxStage<BK>::Grouped ? 2 * MxStage<BK>::GroupBytes : 0);
+    static_assert(sh <= 160 * 1024, "LDS");
     hipError_t e = allow_lds(k_gemm_mx<BK, NS>, sh);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
@@ -395,7 +439,7 @@ static hipError_t launch_mx(const GemmLaunch& p, hipStream_t s)
 // in LDS); K that is only a multiple of 128 takes four 128-element stages.
 hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s)
 {
-    if (p.k % 256 == 0) return launch_mx<256, 2>(p, s);
+    if (p.k % 256 == 0 && p.k >= 512) return launch_mx<256, 2>(p, s);
     return launch_mx<128, 4>(p, s);
 }
 

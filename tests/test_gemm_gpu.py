@@ -71,8 +71,11 @@ def test_small_nvfp4_gemm():
 
 
 @pytest.mark.parametrize("m,n,k", [(64, 256, 256), (70, 300, 256), (300, 70, 512), (1, 33, 128), (257, 513, 384),
-                                   (512, 256, 1024)])
+                                   (512, 256, 1024), (96, 200, 768), (130, 260, 1280), (40, 520, 1536)])
 def test_mxfp4_native_shapes(m, n, k):
+    """K in 256-element stages with scales in groups of four stages: K/256 =
+    2, 3, 4, 5, 6 cover a partial last group, odd and even; K = 256 and
+    multiples of 128 take the 128-element stages."""
     qa, a = _quant_both(_normal(m, k, 1), 32, "e8m0")
     qb, b = _quant_both(_normal(n, k, 2, 0.02), 32, "e8m0")
     c = fq.fp4_gemm(qa, qb)
