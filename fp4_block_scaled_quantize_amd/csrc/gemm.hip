@@ -270,14 +270,16 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
     // (0: W, 1: A), dword 64 wave + lane = (row, half).
     const uint8_t* srcs[L::SDma];
     int sdst[L::SDma];
-    // grouped scales: DMA j fills operand j, lanes 2 r + h take 16-byte half
-    // h of row r's 32 bytes; a half past the row end (the last, partial
-    // group) is read from the row's last 16 bytes instead
+    // grouped scales: DMA j fills operand j; LDS unit 2 r + u of row r holds
+    // the row's 16-byte half u ^ b3(r) (rows with bit 3 set swap halves, so a
+    // 16-lane read of one half over 16 consecutive rows meets every bank
+    // once).  A half past the row end (the last, partial group) is read from
+    // the row's last 16 bytes instead.
     const uint8_t* gsrc[2];
     int ghalf = 0;
     if (L::Grouped) {
         const int r = tid >> 1;
-        ghalf = tid & 1;
+        ghalf = (tid & 1) ^ ((r >> 3) & 1);
         gsrc[0] = p.sb + row_w(r) * rows;
         gsrc[1] = p.sa + row_a(r) * rows;
     }
@@ -330,6 +332,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
     for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
     const int frow = lane & 31, khalf = lane >> 5;
+    uint4 swp[4], sap[2];                     // grouped scales: the pair of the current two stages
     for (int kt = 0; kt < KT; ++kt) {
         // this wave's loads of stage kt have landed; the barrier makes every
         // wave's visible and retires all reads of stage kt - 1
@@ -339,17 +342,31 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         const uint8_t* st = smem + (kt % NS) * L::Bytes;
         uint64_t swd[4], sad[2];
         if (L::Grouped) {
-            // stage kt's 8 bytes of row r: 32 r + 8 (kt % 4), 8 further on for
+            // the 16-byte scale pair of stages kt, kt + 1 (kt even) is read once;
+            // stage kt takes its low 8 bytes, kt + 1 the high ones, and so does
             // the last stage of an odd count (its half was read from the row end)
-            const uint8_t* gb = gbuf + ((kt / L::GroupStages) & 1) * L::GroupBytes;
-            const int so = 8 * (kt % L::GroupStages) + ((kt == KT - 1 && (KT & 1)) ? 8 : 0);
+            if ((kt & 1) == 0) {
+                const uint8_t* gb = gbuf + ((kt / L::GroupStages) & 1) * L::GroupBytes;
+                const int h = (kt % L::GroupStages) >> 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wn * 128 + 32 * i + frow;
+                    swp[i] = *reinterpret_cast<const uint4*>(gb + L::GroupRow * r + 16 * (h ^ ((r >> 3) & 1)));
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int r = wm * 64 + 32 * j + frow;
+                    sap[j] = *reinterpret_cast<const uint4*>(gb + L::GroupBytes / 2 + L::GroupRow * r +
+                                                             16 * (h ^ ((r >> 3) & 1)));
+                }
+            }
+            const bool hi = (kt & 1) || (kt == KT - 1 && (KT & 1));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                swd[i] = *reinterpret_cast<const uint64_t*>(gb + L::GroupRow * (wn * 128 + 32 * i + frow) + so);
+                swd[i] = hi ? ((uint64_t)swp[i].w << 32 | swp[i].z) : ((uint64_t)swp[i].y << 32 | swp[i].x);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                sad[j] = *reinterpret_cast<const uint64_t*>(gb + L::GroupBytes / 2 +
-                                                            L::GroupRow * (wm * 64 + 32 * j + frow) + so);
+                sad[j] = hi ? ((uint64_t)sap[j].w << 32 | sap[j].z) : ((uint64_t)sap[j].y << 32 | sap[j].x);
         } else {
             const uint8_t* ssw = st + 2 * L::Codes;
             const uint8_t* ssa = ssw + L::Scales;
