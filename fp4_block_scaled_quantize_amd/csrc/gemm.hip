@@ -320,6 +320,31 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         }
     };
     static_assert(!L::Grouped || NS == 2, "grouped scales rely on waiting for every load each stage");
+    // 256-element stages: the loads of the next stage are spread over the
+    // first two 64-element steps of this one, between its matrix
+    // instructions.  A load waits for the texture address unit, which the
+    // eight waves' loads keep busy for thousands of cycles per stage; issued
+    // all at once after the barrier, they held back the matrix instructions
+    // behind them in every wave's program.  (Later steps leave too little
+    // time for the loads to land before the next stage.)
+    constexpr int kParts = L::Grouped ? 2 : 0;
+    auto issue_part = [&](int kt, int buf, int part) {
+        const int ks = kt < KT ? kt : KT - 1;
+        uint8_t* st = smem + buf * L::Bytes;
+        constexpr int kP = kParts > 0 ? kParts : 1;
+#pragma unroll
+        for (int k = part * L::NI / kP; k < (part + 1) * L::NI / kP; ++k) {
+            dma16(srcw[k] + (int64_t)ks * L::RB, st + 1024 * (L::NI * wave + k));
+            dma16(srca[k] + (int64_t)ks * L::RB, st + L::Codes + 1024 * (L::NI * wave + k));
+        }
+        if (part == 0 && kt % L::GroupStages == 0 && kt < KT) {
+            const int64_t off = (int64_t)(kt / L::GroupStages) * L::GroupRow + 16 * ghalf;
+            const int64_t o = off + 16 <= rows ? off : rows - 16;
+            uint8_t* const gb = gbuf + ((kt / L::GroupStages) & 1) * L::GroupBytes;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma16(gsrc[j] + o, gb + j * (L::GroupBytes / 2) + 1024 * wave);
+        }
+    };
     constexpr int kLoads = 2 * L::NI + (L::Grouped ? 0 : L::SDma);
 
     v16f acc[4][2];
@@ -338,7 +363,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         // wave's visible and retires all reads of stage kt - 1
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * kLoads) : "memory");
         __builtin_amdgcn_s_barrier();        // no fence: a fence would wait for every load in flight
-        issue(kt + NS - 1, (kt + NS - 1) % NS);
+        if (kParts == 0) issue(kt + NS - 1, (kt + NS - 1) % NS);
         const uint8_t* st = smem + (kt % NS) * L::Bytes;
         uint64_t swd[4], sad[2];
         if (L::Grouped) {
@@ -404,6 +429,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
         for (int ks = 0; ks < BK / 64; ++ks) {
             const int cur = ks & 1;
             if (ks + 1 < BK / 64) read_frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+            if (kParts > 0 && ks < kParts) issue_part(kt + NS - 1, (kt + NS - 1) % NS, ks);
             const int sh = 8 * (2 * ks + khalf);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -421,6 +447,13 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
                 for (int q = 0; q < 6; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one matrix instruction
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read of the next pair
+                }
+            }
+            if (kParts > 0 && ks < kParts) {
+#pragma unroll
+                for (int q = 0; q < 2 * L::NI / (kParts > 0 ? kParts : 1) + (ks == 0 ? 2 : 0); ++q) {   // codes (+ scales)
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one matrix instruction
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one load of the next stage
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
