@@ -319,3 +319,26 @@ def gemm_check(c_out: np.ndarray, c_ref: np.ndarray, tol: np.ndarray) -> np.ndar
     hi = round_to_bf16(c_ref + tol)
     c = np.asarray(c_out, dtype=np.float64)
     return (lo <= c) & (c <= hi)
+
+
+# --------------------------------------------------------------------------
+# column-wise (transposed) quantization: the operands of the backward pass
+# (gonzo_ML/3986 "Стохастическая квантизация": stochastic rounding for the
+# backward gradients; ue5m3-fp4-pretraining "Что сделали": every linear layer
+# in FP4, so the weight-gradient product needs its operands blocked along the
+# token dimension, i.e. along the columns of x)
+# --------------------------------------------------------------------------
+def quantize_transposed_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *,
+                               state: AmaxState | None = None, stochastic: bool = False, seed: int = 0,
+                               offset: int = 0, nthreads: int = 1):
+    """The whole quantize call applied to the transpose of x.
+
+    x: [R, C]; the result describes x^T: codes [C, R/2], scales [C, R/block],
+    blocks of `block` consecutive rows of one column of x.  The logical
+    element index of the stochastic-rounding counter is that of x^T
+    (i = c * R + r).  Reading: the pages give no layout for the transposed
+    operand; taking it as the plain quantization of x^T makes it the [N, K]
+    operand the GEMM consumes.  Returns (q, scales, g, amax_used)."""
+    xt = np.ascontiguousarray(np.asarray(x).T)
+    return quantize_tensor(xt, block, fmt, policy, state=state, stochastic=stochastic, seed=seed,
+                           offset=offset, nthreads=nthreads)

@@ -590,3 +590,65 @@ def test_gemm_check_bracket():
     assert oracle.gemm_check(exact, c_ref, tol).all()
     off = exact + np.array([2**-6, 1.0, 2**-5, 2**-130])      # two bf16 ulps away or more
     assert not oracle.gemm_check(off, c_ref, tol).any()
+
+
+# ---------------------------------------------------------------------------
+# column-wise (transposed) quantization: the backward-pass operands
+# ---------------------------------------------------------------------------
+def _nib(q, r, c):
+    return (int(q[r, c // 2]) >> (4 * (c & 1))) & 0xF
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_transposed_blocks_run_down_columns_closed_form(block):
+    # column c of x holds +-6 * 2^(c-8) with the sign alternating down the
+    # rows: blocked down the columns every block maximum is 6 * 2^(c-8), so
+    # the E8M0 code of output row c is 127 + (c - 8) (floor(log2(6 * 2^k)) -
+    # 2 = k) and every element encodes to +-6.  Blocking along the rows of x
+    # instead would mix columns of different magnitude in one block.
+    R, C = 2 * block, 24
+    mag = 6.0 * 2.0 ** (np.arange(C) - 8.0)
+    sign = np.where(np.arange(R) % 2 == 0, 1.0, -1.0)
+    x = (sign[:, None] * mag[None, :]).astype(np.float32)
+    q, s, g, a = oracle.quantize_transposed_tensor(x, block, "e8m0", "none")
+    assert q.shape == (C, R // 2) and s.shape == (C, R // block)
+    assert (g, a) == (1.0, 0.0)
+    for c in range(C):
+        assert np.all(s[c] == 127 + c - 8)
+        for r in range(R):
+            assert _nib(q, c, r) == (7 | (8 if r % 2 else 0))
+
+
+def test_transposed_tensor_max_invariant():
+    # current E4M3 tensor scale: the output block holding the maximum takes
+    # code 0x7E (448) and the maximum itself encodes to +-6, at the transposed
+    # position (row = column of x, element = row of x)
+    x = _sweep_like(96, 48, 21, bf16=False)
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "current")
+    r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert a == float(np.abs(x).max()) and g == np.float32(a) / np.float32(2688.0)
+    assert s[c, r // 16] == 0x7E
+    nib = _nib(q, c, r)
+    assert nib & 7 == 7 and (nib >> 3) == (x[r, c] < 0)
+
+
+def test_transposed_stochastic_counter_uses_transposed_index():
+    # every block of x^T holds one 4 (E8M0 code 127, scale 1) and otherwise
+    # 0.75, the midpoint of 0.5 and 1: that element rounds up iff its 16
+    # random bits are below 2^15, the bits of logical index i = c * R + r
+    R, C, seed, offset = 32, 8, 0xC0FFEE, 9
+    x = np.full((R, C), 0.75, dtype=np.float32)
+    x[0::16, :] = 4.0
+    q, s, _, _ = oracle.quantize_transposed_tensor(x, 16, "e8m0", "none", stochastic=True, seed=seed,
+                                                   offset=offset)
+    assert np.all(s == 127)
+    ups = 0
+    for c in range(C):
+        for r in range(R):
+            if r % 16 == 0:
+                assert _nib(q, c, r) == 6                 # 4 is on the grid
+                continue
+            want = 2 if oracle.sr_bits(seed, offset, c * R + r) < 0x8000 else 1
+            assert _nib(q, c, r) == want, (r, c)
+            ups += want == 2
+    assert 0 < ups < C * (R - 2)
