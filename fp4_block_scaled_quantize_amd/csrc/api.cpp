@@ -188,6 +188,53 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     return st;
 }
 
+fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
+                                   fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream)
+{
+    ScaleFmtHost f;
+    fp4_status st = check_tensor(out, &f);
+    if (st != FP4_OK) return st;
+    if (!x && out->rows * out->cols != 0) return FP4_ERR_INVALID_ARG;
+    if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
+    const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
+    // x is [out->cols, out->rows]: its rows are the blocked dimension
+    if (out->rows % 8) return FP4_ERR_SHAPE;
+    if (out->rows * out->cols != 0) {
+        if (ld_x < out->rows) return FP4_ERR_SHAPE;
+        if (!aligned16(x) || (ld_x * esz) % 16 || !aligned16(out->q)) return FP4_ERR_ALIGN;
+    }
+    const int32_t pol = out->fmt.amax;
+    if (f.is_e8m0 && pol != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
+    if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    AmaxDev* src = nullptr;
+    bool refresh = false;
+    if (pol != FP4_AMAX_NONE) {
+        refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
+        src = state->dev;
+    }
+    QuantLaunch p;
+    p.x = x;
+    p.x_bf16 = x_dtype == FP4_DTYPE_BF16;
+    p.rows = out->rows;
+    p.cols = out->cols;
+    p.ld = ld_x;
+    p.q = out->q;
+    p.scales = out->scales;
+    p.tensor_scale = out->tensor_scale;
+    p.amax_src = src;
+    p.refresh = refresh;
+    p.block = out->fmt.block;
+    p.stochastic = out->fmt.rounding == FP4_ROUND_STOCHASTIC;
+    p.seed = seed;
+    p.offset = offset;
+    p.fmt = f;
+    st = hip_status(launch_quantize_t(p, s));
+    if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
+    return st;
+}
+
 fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream)
 {
     ScaleFmtHost f;

@@ -67,6 +67,8 @@ struct DequantLaunch {
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);
+// Column-wise: rows/cols describe the output (x^T); x is [cols, rows].
+hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s);
 hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s);
 
 struct GemmLaunch {

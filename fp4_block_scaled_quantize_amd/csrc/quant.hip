@@ -63,6 +63,7 @@ struct Unit;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // max |x| of 8 elements as binary32 bits.  Non-negative floats order like
 // their bit patterns, so the maximum is taken on integers (no NaN
@@ -218,7 +219,8 @@ struct QArgs {
 // The tensor maximum of this call: the reduction of the amax kernel's
 // partials on a refresh, the stored value otherwise.  Every wave reduces the
 // partials itself (one 16-byte load per lane), so no barrier is needed.
-__device__ __forceinline__ float tensor_amax(const QArgs& a)
+template <typename A>
+__device__ __forceinline__ float tensor_amax(const A& a)
 {
     if (!a.refresh) return a.amax_src->stored;
     static_assert(kAmaxParts == 256, "one float4 of partials per lane");
@@ -304,7 +306,8 @@ __device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
 
 // Tensor scale g = amax_t / RN(6 Smax); 1 when there is no tensor scale or
 // the quotient is zero or not finite.
-__device__ __forceinline__ float tensor_scale_of(float am, const QArgs& a)
+template <typename A>
+__device__ __forceinline__ float tensor_scale_of(float am, const A& a)
 {
     if (!a.amax_src) return 1.0f;
     float den = 6.0f * a.f.smax;
@@ -546,6 +549,263 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     } else {
         if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, blocks, s);
         else launch_q3<float, 32>(a, sr, e8, fused, strided, blocks, s);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// column-wise (transposed) quantize: the quantization of x^T for x [R, C],
+// i.e. blocks of B consecutive rows of one column of x (the operands of the
+// backward pass are blocked along the token dimension).  Output codes
+// [C, R/2] and scales [C, R/B]; the stochastic-rounding index is that of
+// x^T, i = c * R + r, so the result equals the row-wise quantization of the
+// materialized transpose bit for bit.
+//
+// A workgroup owns a tile of kTR rows x kTC columns of x: coalesced 16-byte
+// row loads into LDS, one barrier, then lane l of every wave takes column l
+// and reads its kTR / 4 rows down the tile (consecutive lanes read
+// consecutive LDS addresses, so the reads are free of bank conflicts).
+// ---------------------------------------------------------------------------
+constexpr int kTR = 256;
+constexpr int kTC = 64;
+constexpr int kTThreads = 256;
+#ifndef FP4_T_SR_WAVES
+#define FP4_T_SR_WAVES 3
+#endif
+
+struct QTArgs {
+    const void* x;
+    int64_t ld;
+    uint32_t R, C;               // x is [R, C]
+    uint32_t ntr;                // tiles along R
+    uint32_t xcd_chunk;          // consecutive tiles per XCD (0: plain order)
+    uint8_t* q;                  // [C, R/2]
+    uint8_t* scales;             // [C, R/B]
+    float* tensor_scale;
+    AmaxDev* amax_src;
+    int32_t refresh;
+    ScaleFmt f;
+    uint32_t key0, key1, off0, off1;
+};
+
+template <typename InT>
+__device__ __forceinline__ float lds_elem(const InT* t, uint32_t i);
+template <>
+__device__ __forceinline__ float lds_elem<uint16_t>(const uint16_t* t, uint32_t i)
+{
+    return __uint_as_float((uint32_t)t[i] << 16);
+}
+template <>
+__device__ __forceinline__ float lds_elem<float>(const float* t, uint32_t i)
+{
+    return t[i];
+}
+
+template <typename InT, int BLOCK, bool SR, bool E8M0>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : 5)))) void k_quantize_t(QTArgs a)
+{
+    constexpr int EPP = 16 / (int)sizeof(InT);   // elements per 16-byte piece
+    constexpr int PPR = kTC / EPP;               // pieces per tile row
+    constexpr int RPR = kTThreads / PPR;         // tile rows per load round
+    constexpr int NLD = kTR / RPR;               // 16-byte loads per thread
+    constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
+    constexpr int NB = RPW / BLOCK;              // blocks per lane
+    __shared__ __align__(16) InT tile[kTR * kTC];
+
+    // XCD-aware order: consecutive tiles (down one column strip, which share
+    // the lines of the scale rows) run on one XCD
+    uint32_t t = blockIdx.x;
+    if (a.xcd_chunk) t = (t & 7u) * a.xcd_chunk + (t >> 3);
+    const uint32_t tc = t / a.ntr, tr = t - tc * a.ntr;
+    const uint32_t r0 = tr * kTR, c0 = tc * kTC;
+
+    const uint32_t piece = threadIdx.x % PPR, prow = threadIdx.x / PPR;
+    const uint32_t gc = c0 + piece * EPP;
+    u32x4 v[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+        const uint32_t gr = r0 + prow + k * RPR;
+        if (gr < a.R && gc < a.C)
+            v[k] = __builtin_nontemporal_load((const u32x4*)((const InT*)a.x + (uint64_t)gr * (uint64_t)a.ld + gc));
+        else
+            v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float g = 1.0f, d = 6.0f;
+    if (!E8M0 && a.amax_src) {
+        const float am = tensor_amax(a);
+        g = tensor_scale_of(am, a);
+        d = 6.0f * g;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.tensor_scale[0] = g;
+            a.tensor_scale[1] = am;
+            if (a.refresh) a.amax_src->stored = am;
+        }
+    } else if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.tensor_scale[0] = 1.0f;
+        a.tensor_scale[1] = 0.0f;
+    }
+
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) *(u32x4*)&tile[(prow + k * RPR) * kTC + piece * EPP] = v[k];
+    __syncthreads();
+
+    const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t col = c0 + lane;
+    const uint32_t rw = r0 + w * RPW;            // first row of x in this wave's blocks
+    const InT* tw = tile + w * RPW * kTC + lane;
+
+    // codes of this lane's NB blocks (column `col`, rows rw ..) and their
+    // scale bytes; blocks past the end of x (R % BLOCK == 0, so blocks are
+    // whole) compute on zeros and are never stored
+    uint32_t packed[NB][BLOCK / 8];
+    uint32_t sc = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t rb = rw + b * BLOCK;
+        float val[BLOCK];
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < BLOCK; ++j) {
+            val[j] = lds_elem<InT>(tw, (b * BLOCK + j) * kTC);
+            const uint32_t u = __float_as_uint(val[j]) & 0x7FFFFFFFu;
+            m = m > u ? m : u;
+        }
+        float inv;
+        uint32_t code;
+        if (E8M0) {
+            code = scale_code_e8m0(__uint_as_float(m));
+            inv = e8m0_inv(code);
+        } else {
+            code = exmy_scale(__uint_as_float(m), d, g, a.f, &inv);
+        }
+        sc |= code << (8 * b);
+#pragma unroll
+        for (int k = 0; k < BLOCK / 8; ++k) {
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = val[k * 8 + i] * inv;
+            if (SR) {
+                const uint32_t u = col * (a.R / 8u) + (rb >> 3) + k;      // unit (i >> 3) of x^T
+                U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+                uint32_t pk = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pk |= e2m1_sr(e[i], (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << (4 * i);
+                packed[b][k] = pk;
+            } else {
+                uint32_t pk = FP4_CVT_PK(0u, e[0], e[1], 0);
+                pk = FP4_CVT_PK(pk, e[2], e[3], 1);
+                pk = FP4_CVT_PK(pk, e[4], e[5], 2);
+                packed[b][k] = FP4_CVT_PK(pk, e[6], e[7], 3);
+            }
+        }
+    }
+
+    // Stage the tile's output in LDS ([kTC] output rows of kTR/2 code bytes
+    // and kTR/BLOCK scale bytes), then store whole row pieces: each wave
+    // store instruction covers full 128-byte lines of eight output rows,
+    // instead of one 8- or 16-byte piece per lane in 64 different rows.
+    constexpr int QB = kTR / 2;                  // code bytes per output row and tile
+    constexpr int QP = QB + 16;                  // padded LDS pitch
+    constexpr int SB = kTR / BLOCK;              // scale bytes per output row and tile
+    static_assert(kTC * (QP + SB) <= kTR * kTC * (int)sizeof(InT), "output stage fits the input tile");
+    uint8_t* oq = reinterpret_cast<uint8_t*>(tile);
+    uint8_t* os = oq + kTC * QP;
+    __syncthreads();                             // every wave has read its rows of the tile
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        uint8_t* dst = oq + lane * QP + (w * RPW + b * BLOCK) / 2;
+        if (BLOCK == 16) *(u32x2*)dst = u32x2{packed[b][0], packed[b][1]};
+        else *(u32x4*)dst = u32x4{packed[b][0], packed[b][1], packed[b][2], packed[b][3]};
+    }
+    if (NB == 4) *(uint32_t*)(os + lane * SB + w * NB) = sc;
+    else *(uint16_t*)(os + lane * SB + w * NB) = (uint16_t)sc;
+    __syncthreads();
+
+    const uint32_t rows_here = a.R - r0 < (uint32_t)kTR ? a.R - r0 : (uint32_t)kTR;   // multiple of BLOCK
+    const uint32_t qbytes = rows_here / 2, sbytes = rows_here / BLOCK;
+    const uint64_t qrow = a.R / 2, srow = a.R / BLOCK;
+    const bool q16 = (qrow & 15u) == 0;          // 16-byte aligned output rows
+    constexpr int QCH = QB / 16;                 // 16-byte chunks per output row
+#pragma unroll
+    for (int k = 0; k < kTC * QCH / kTThreads; ++k) {
+        const uint32_t p = threadIdx.x + k * kTThreads;
+        const uint32_t orow = p / QCH, ch = p % QCH;
+        const uint32_t oc = c0 + orow;
+        if (oc >= a.C || ch * 16 >= qbytes) continue;
+        const u32x4 v4 = *(const u32x4*)(oq + orow * QP + ch * 16);
+        uint8_t* g8 = a.q + (uint64_t)oc * qrow + r0 / 2 + ch * 16;
+        if (q16 && ch * 16 + 16 <= qbytes) {
+            __builtin_nontemporal_store(v4, (u32x4*)g8);
+        } else {
+            __builtin_nontemporal_store(u32x2{v4.x, v4.y}, (u32x2*)g8);
+            if (ch * 16 + 16 <= qbytes) __builtin_nontemporal_store(u32x2{v4.z, v4.w}, (u32x2*)(g8 + 8));
+        }
+    }
+    if (threadIdx.x < kTC) {
+        const uint32_t oc = c0 + threadIdx.x;
+        if (oc < a.C) {
+            const uint8_t* src = os + threadIdx.x * SB;
+            uint8_t* g8 = a.scales + (uint64_t)oc * srow + r0 / BLOCK;
+            if ((srow % SB) == 0 && sbytes == (uint32_t)SB && ((uintptr_t)a.scales % SB) == 0) {
+                if (SB == 16) *(u32x4*)g8 = *(const u32x4*)src;
+                else *(u32x2*)g8 = *(const u32x2*)src;
+            } else {
+                for (uint32_t i = 0; i < sbytes; ++i) g8[i] = src[i];
+            }
+        }
+    }
+}
+
+template <typename InT, int BLOCK>
+static void launch_qt2(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
+{
+    const dim3 g(blocks), t(kTThreads);
+    if (sr) {
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false>), g, t, 0, s, a);
+    } else {
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false>), g, t, 0, s, a);
+    }
+}
+
+// p.rows / p.cols are the output's shape (C, R); x is [R, C] with row stride
+// p.ld.  A refresh takes the amax kernel first (x is read twice).
+hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
+{
+    QTArgs a;
+    a.x = p.x;
+    a.ld = p.ld;
+    a.R = (uint32_t)p.cols;
+    a.C = (uint32_t)p.rows;
+    const uint32_t ntr = (a.R + kTR - 1) / kTR, ntc = (a.C + kTC - 1) / kTC;
+    const uint32_t ntiles = ntr * ntc;
+    a.ntr = ntr ? ntr : 1;
+    a.xcd_chunk = (ntiles % 8 == 0) ? ntiles / 8 : 0;
+    a.q = p.q;
+    a.scales = p.scales;
+    a.tensor_scale = p.tensor_scale;
+    a.amax_src = p.amax_src;
+    a.refresh = p.refresh;
+    a.f = ScaleFmt{p.fmt.ebits, p.fmt.mbits, p.fmt.bias, p.fmt.maxcode, p.fmt.smax, p.fmt.is_e8m0};
+    a.key0 = (uint32_t)p.seed;
+    a.key1 = (uint32_t)(p.seed >> 32);
+    a.off0 = (uint32_t)p.offset;
+    a.off1 = (uint32_t)(p.offset >> 32);
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0;
+    if (a.amax_src && a.refresh && !e8) {
+        hipError_t e = launch_amax(p.x, p.x_bf16, a.R, a.C, p.ld, p.amax_src, s);
+        if (e != hipSuccess) return e;
+    }
+    const uint32_t blocks = ntiles ? ntiles : 1;
+    if (p.x_bf16) {
+        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, blocks, s);
+        else launch_qt2<uint16_t, 32>(a, sr, e8, blocks, s);
+    } else {
+        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, blocks, s);
+        else launch_qt2<float, 32>(a, sr, e8, blocks, s);
     }
     return hipGetLastError();
 }

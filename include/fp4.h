@@ -167,6 +167,27 @@ FP4_API fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp
                         fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
 
 /*
+ * fp4_quantize_transposed -- column-wise quantization for the backward
+ * pass: out describes x^T, where x is [out->cols, out->rows] (row stride
+ * ld_x elements, f32 or bf16), so each block holds `block` consecutive rows
+ * of one column of x.  The result is, bit for bit, fp4_quantize applied to
+ * the materialized transpose of x: same scale, rounding and amax rules,
+ * and the stochastic-rounding index is that of x^T (i = c * out->cols + r
+ * for element x[r, c]).  (gonzo_ML/3986 "Стохастическая квантизация":
+ * stochastic rounding for the backward gradients; ue5m3-fp4-pretraining
+ * "Что сделали": every suitable linear layer in FP4, which needs the
+ * weight-gradient operands blocked along the token dimension.  Reading:
+ * the pages give no layout for them; the transpose's row-major layout is
+ * the [N, K] operand fp4_gemm consumes.)
+ * x: device, 16-byte aligned, ld_x * sizeof(elem) a multiple of 16, ld_x >=
+ * out->rows; out->rows % 8 == 0; out->cols % block == 0; out->q 16-byte
+ * aligned.  A refresh of the tensor maximum reads x twice (an amax pass,
+ * then the quantize pass).  Errors as fp4_quantize.
+ */
+FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
+                                   fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
+
+/*
  * fp4_dequantize -- y[rows, cols] (row stride ld_y, f32 or bf16) =
  * RN(RN(e2m1(code) * s) * g), rounded once more to bf16 (RNE) for bf16
  * output (quant_prune_distill/486 "Метод": the element times its group's

@@ -95,3 +95,20 @@ def test_amax_state_argument_checks():
     assert L.fp4_amax_state_create(0, ctypes.byref(h)) == -1
     assert L.fp4_amax_state_create(50, None) == -1
     assert L.fp4_amax_state_destroy(None) == -1
+
+
+def test_quantize_transposed_checks():
+    L = fq.lib()
+    t = _tensor(rows=64, cols=32)                 # x is [32, 64]
+    assert L.fp4_quantize_transposed(FAKE, 1, 63, ctypes.byref(t), FAKE, 0, 0, None) == -3   # ld < 64
+    assert L.fp4_quantize_transposed(FAKE, 1, 68, ctypes.byref(t), FAKE, 0, 0, None) == -4   # ld*2 % 16
+    assert L.fp4_quantize_transposed(FAKE + 8, 1, 64, ctypes.byref(t), FAKE, 0, 0, None) == -4
+    t6 = _tensor(rows=60, cols=32)                 # x columns not a multiple of 8
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(t6), FAKE, 0, 0, None) == -3
+    tq = _tensor(rows=64, cols=32, q=FAKE + 4)     # codes not 16-byte aligned
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tq), FAKE, 0, 0, None) == -4
+    tb = _tensor(rows=64, cols=40)                 # x rows not a multiple of the block
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tb), FAKE, 0, 0, None) == -3
+    te = _tensor(rows=64, cols=32, scale=4, block=32)
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(te), FAKE, 0, 0, None) == -2
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(t), None, 0, 0, None) == -1   # no state
