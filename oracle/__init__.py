@@ -83,6 +83,10 @@ def lib():
         "or_e2m1_rtn_array": (None, [c_p, c_p, c_i64]),
         "or_e2m1_sr_array": (None, [c_p, c_p, c_p, c_i64]),
         "or_sr_bits_array": (None, [c_u64, c_u64, c_u64, c_i64, c_p]),
+        "or_rht_norm": (c_f, [c_int]),
+        "or_rht_forward": (c_int, [c_p, c_int, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
+        "or_rht_inverse": (c_int, [c_p, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
+        "or_f32_to_bf16_array": (None, [c_p, c_p, c_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -259,6 +263,53 @@ def dequantize_f64(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt:
 
 
 # --------------------------------------------------------------------------
+# blockwise randomized Hadamard transform (ue5m3-fp4-pretraining "Что
+# сделали": a randomized Hadamard transform spreads outliers before
+# quantization; quant_prune_distill/574 "Метод": Hadamard rotations make
+# distributions closer to Gaussian).  See fp4_oracle.c for the reading.
+# --------------------------------------------------------------------------
+def rht_norm(block: int) -> float:
+    return lib().or_rht_norm(block)
+
+
+def rht_forward(x: np.ndarray, block: int, signs: int) -> np.ndarray:
+    """y = c_B * H_B * D * v for every block of `block` elements of a row
+    (binary32 butterfly); returns float32 [rows, cols]."""
+    x, is_bf16 = _as_input(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), dtype=np.float32)
+    if lib().or_rht_forward(_ptr(x), is_bf16, rows, cols, block, signs & 0xFFFFFFFF, _ptr(y)) != 0:
+        raise ValueError("oracle rht_forward: argument outside the contract")
+    return y
+
+
+def rht_inverse(y: np.ndarray, block: int, signs: int) -> np.ndarray:
+    """v = D * (c_B * H_B * y) per block (binary32 butterfly)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    rows, cols = y.shape
+    x = np.empty((rows, cols), dtype=np.float32)
+    if lib().or_rht_inverse(_ptr(y), rows, cols, block, signs & 0xFFFFFFFF, _ptr(x)) != 0:
+        raise ValueError("oracle rht_inverse: argument outside the contract")
+    return x
+
+
+def f32_to_bf16_bits_array(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    lib().or_f32_to_bf16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def dequantize_rht(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str, signs: int,
+                   out: str = "f32") -> np.ndarray:
+    """Dequantize a tensor quantized after the blockwise RHT: the binary32
+    dequantized values, then the inverse transform, then (bf16 output) one
+    more nearest-even rounding."""
+    x = rht_inverse(dequantize(q, scales, g, block, fmt, out="f32"), block, signs)
+    return f32_to_bf16_bits_array(x) if out == "bf16" else x
+
+
+# --------------------------------------------------------------------------
 # amax policies (ue5m3-fp4-pretraining "Что сделали": the tensor maximum is
 # refreshed once every 50 steps and the stored value is used in between)
 # --------------------------------------------------------------------------
@@ -291,9 +342,15 @@ def resolve_tensor_scale(x: np.ndarray, fmt: str, policy: str, state: AmaxState 
 
 
 def quantize_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *, state: AmaxState | None = None,
-                    stochastic: bool = False, seed: int = 0, offset: int = 0, nthreads: int = 1):
+                    stochastic: bool = False, seed: int = 0, offset: int = 0, nthreads: int = 1,
+                    rht_signs: int | None = None):
     """Whole quantize call: tensor scale per policy, then every block.
+    With rht_signs the blockwise randomized Hadamard transform is applied
+    first (rht_forward) and everything after it, the tensor maximum
+    included, sees the transformed binary32 tensor.
     Returns (q, scales, g, amax_used)."""
+    if rht_signs is not None:
+        x = rht_forward(x, block, rht_signs)
     g, a = resolve_tensor_scale(x, fmt, policy, state)
     q, s = quantize(x, block, fmt, g, stochastic=stochastic, seed=seed, offset=offset, nthreads=nthreads)
     return q, s, g, a

@@ -27,6 +27,8 @@
  *            mantissa, the tensor maximum is refreshed every 50 steps and the
  *            stored value used in between, stochastic rounding on backward
  *            gradients.
+ *  [P-INT]   news.1rj.ru/str/quant_prune_distill/574 (INT vs FP review),
+ *            "Метод": Hadamard rotations make distributions more Gaussian.
  * Where the pages are silent the reading taken is stated at each function.
  */
 #include <math.h>
@@ -424,6 +426,79 @@ OR_EXPORT int or_dequantize(const uint8_t* q, const uint8_t* scales, float g,
             else ((float*)y)[r * ld_y + c] = xh;
         }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Blockwise randomized Hadamard transform (RHT), applied before            */
+/* quantization.  [P-UE5M3] "Что сделали": a randomized Hadamard transform   */
+/* spreads outliers over the block before quantization (that scheme drops    */
+/* it); [P-INT] quant_prune_distill/574 "Метод": Hadamard rotations make     */
+/* weights and activations closer to Gaussian.  The pages give no formula.   */
+/* Reading: for every block v of B consecutive elements of a row,            */
+/*   y = c_B * (H_B (D v)),                                                  */
+/*   D = diag(s_j), s_j = -1 where bit j of `signs` is set, else +1;         */
+/*   H_B the Sylvester Hadamard matrix, (H_B)_ij = (-1)^popcount(i & j);     */
+/*   c_B = 1/sqrt(B) rounded to binary32 (exactly 1/4 for B = 16).           */
+/* H_B v is the in-place butterfly: stages h = 1, 2, 4, ..., B/2 in that     */
+/* order, each pair (i, i + h) with bit h of i clear becoming (a + b, a - b),*/
+/* every operation binary32 round-to-nearest-even.  The inverse is           */
+/* v = D (c_B * (H_B y)) (H_B is symmetric and H_B H_B = B I), evaluated by  */
+/* the same butterfly.  bf16 input is widened exactly to binary32 first.     */
+/* ------------------------------------------------------------------------ */
+OR_EXPORT float or_rht_norm(int block)
+{
+    return block == 16 ? 0.25f : (float)(1.0 / sqrt((double)block));
+}
+
+static void fwht_f32(float* v, int n)
+{
+    for (int h = 1; h < n; h <<= 1)
+        for (int i = 0; i < n; ++i)
+            if (!(i & h)) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+}
+
+OR_EXPORT int or_rht_forward(const void* x, int is_bf16, int64_t rows, int64_t cols, int block, uint32_t signs,
+                             float* y)
+{
+    if ((block != 16 && block != 32) || cols % block || !y) return -1;
+    const float c = or_rht_norm(block);
+    float v[32];
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b0 = 0; b0 < cols; b0 += block) {
+            for (int j = 0; j < block; ++j) {
+                float t = load_elem(x, is_bf16, r * cols + b0 + j);
+                v[j] = ((signs >> j) & 1u) ? -t : t;
+            }
+            fwht_f32(v, block);
+            for (int j = 0; j < block; ++j) y[r * cols + b0 + j] = v[j] * c;
+        }
+    return 0;
+}
+
+OR_EXPORT int or_rht_inverse(const float* y, int64_t rows, int64_t cols, int block, uint32_t signs, float* x)
+{
+    if ((block != 16 && block != 32) || cols % block || !y || !x) return -1;
+    const float c = or_rht_norm(block);
+    float v[32];
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b0 = 0; b0 < cols; b0 += block) {
+            for (int j = 0; j < block; ++j) v[j] = y[r * cols + b0 + j];
+            fwht_f32(v, block);
+            for (int j = 0; j < block; ++j) {
+                float t = v[j] * c;
+                x[r * cols + b0 + j] = ((signs >> j) & 1u) ? -t : t;
+            }
+        }
+    return 0;
+}
+
+OR_EXPORT void or_f32_to_bf16_array(const float* x, uint16_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = or_f32_to_bf16(x[i]);
 }
 
 /* Exact binary64 dequantization for the GEMM reference: e2m1 * s * g. */

@@ -652,3 +652,108 @@ def test_transposed_stochastic_counter_uses_transposed_index():
             assert _nib(q, c, r) == want, (r, c)
             ups += want == 2
     assert 0 < ups < C * (R - 2)
+
+
+# ---------------------------------------------------------------------------
+# blockwise randomized Hadamard transform (applied before quantization)
+# ---------------------------------------------------------------------------
+def _sylvester(n):
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def test_rht_norm_correctly_rounded():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    assert oracle.rht_norm(16) == 0.25
+    c = np.float32(oracle.rht_norm(32))
+    t = Decimal(1) / Decimal(32).sqrt()
+    for nb in (np.nextafter(c, np.float32(0)), np.nextafter(c, np.float32(1))):
+        assert abs(Decimal(float(c)) - t) < abs(Decimal(float(nb)) - t)
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_rht_matches_sylvester_closed_form(block):
+    # integer inputs keep every butterfly sum exact, so the binary32 result
+    # is the closed-form matrix product times c_B, rounded once
+    rng = np.random.default_rng(40 + block)
+    rows, cols = 6, 4 * block
+    x = rng.integers(-50, 51, (rows, cols)).astype(np.float32)
+    signs = int(rng.integers(0, 2**32))
+    d = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(block)])
+    H = _sylvester(block)
+    want = np.empty((rows, cols), dtype=np.float32)
+    c = float(np.float32(oracle.rht_norm(block)))
+    for r in range(rows):
+        for b0 in range(0, cols, block):
+            want[r, b0:b0 + block] = ((H @ (d * x[r, b0:b0 + block].astype(np.float64))) * c).astype(np.float32)
+    got = oracle.rht_forward(x, block, signs)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_rht_signs_apply_before_the_transform(block):
+    # a unit vector at position j with bit j set maps to -c * column j of H
+    # (D after H would flip entries by row instead)
+    c = np.float32(oracle.rht_norm(block))
+    H = _sylvester(block)
+    for j in (0, 3, block - 1):
+        x = np.zeros((1, block), dtype=np.float32)
+        x[0, j] = 1.0
+        signs = (1 << j) | (1 << ((j + 5) % block))
+        y = oracle.rht_forward(x, block, signs)
+        assert np.array_equal(y[0], (-H[:, j] * c).astype(np.float32))
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_rht_inverse_is_orthogonal_inverse(block):
+    rng = np.random.default_rng(7 + block)
+    x = (rng.standard_normal((20, 8 * block)) * 0.02).astype(np.float32)
+    signs = 0xA5C3_1E77
+    y = oracle.rht_forward(x, block, signs)
+    back = oracle.rht_inverse(y, block, signs)
+    # orthogonal up to binary32 rounding: relative error a few ulps of the block norm
+    err = np.abs(back.astype(np.float64) - x)
+    nrm = np.sqrt((x.astype(np.float64).reshape(20, -1, block) ** 2).sum(-1, keepdims=True))
+    assert (err.reshape(20, -1, block) <= 8 * 2.0 ** -24 * nrm).all()
+    # Parseval: block norms are preserved
+    ny = np.sqrt((y.astype(np.float64).reshape(20, -1, block) ** 2).sum(-1))
+    assert np.allclose(ny, nrm[..., 0], rtol=1e-6)
+    if block == 16:
+        xi = rng.integers(-1000, 1001, (4, 64)).astype(np.float32)
+        assert np.array_equal(oracle.rht_inverse(oracle.rht_forward(xi, 16, signs), 16, signs), xi)
+
+
+def test_rht_quantize_uses_transformed_tensor_max():
+    # with the transform, the tensor maximum is that of the transformed
+    # values: the block holding it takes the largest E4M3 code and encodes
+    # to +-6 there
+    x = _sweep_like(32, 256, 23, bf16=False)
+    signs = 0x0F0F_3C3C
+    q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "current", rht_signs=signs)
+    y = oracle.rht_forward(x, 16, signs)
+    assert a == float(np.abs(y).max()) and a != float(np.abs(x).max())
+    r, c = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    assert s[r, c // 16] == 0x7E
+    nib = (int(q[r, c // 2]) >> (4 * (c & 1))) & 0xF
+    assert nib & 7 == 7 and (nib >> 3) == (y[r, c] < 0)
+
+
+@pytest.mark.parametrize("block,fmt", [(16, "e4m3"), (32, "e8m0")])
+def test_rht_dequantize_error_equals_transformed_error(block, fmt):
+    # the inverse transform is orthogonal, so the reconstruction error of x
+    # per block equals the quantization error of the transformed block
+    x = _sweep_like(16, 512, 29, bf16=False)
+    signs = 0x1234_5678
+    pol = "none" if fmt == "e8m0" else "current"
+    q, s, g, _ = oracle.quantize_tensor(x, block, fmt, pol, rht_signs=signs)
+    y = oracle.rht_forward(x, block, signs).astype(np.float64)
+    yh = oracle.dequantize(q, s, g, block, fmt).astype(np.float64)
+    xh = oracle.dequantize_rht(q, s, g, block, fmt, signs).astype(np.float64)
+    e_y = np.sqrt(((yh - y).reshape(16, -1, block) ** 2).sum(-1))
+    e_x = np.sqrt(((xh - x).reshape(16, -1, block) ** 2).sum(-1))
+    scale = np.sqrt((x.astype(np.float64).reshape(16, -1, block) ** 2).sum(-1))
+    assert np.all(np.abs(e_x - e_y) <= 1e-6 * scale + 1e-30)
+    bf = oracle.dequantize_rht(q, s, g, block, fmt, signs, out="bf16")
+    assert np.array_equal(bf, oracle.f32_to_bf16_bits(xh.astype(np.float32)).reshape(bf.shape))
