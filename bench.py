@@ -16,7 +16,8 @@ read: the single-pass kernel holds the tensor in registers while the grid
 agrees on the maximum.
 
 Further legs reported in "legs": stochastic rounding with delayed amax over
-200 successive 8192x8192 gradients, dequantize, the block-scaled GEMM on the
+200 successive 8192x8192 gradients, the same gradients quantized column-wise
+(the backward-pass operands), dequantize, the block-scaled GEMM on the
 Llama-2 7B linear shapes, and the weight-only GEMM at Qwen-2.5 decode
 shapes.  "roofline" is the dominant kernel of the step (the single-pass
 E4M3 block-16 current-amax quantize kernel: four of the five calls) timed
@@ -42,8 +43,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "0ff30c0c97570fa27439f8039b591d2e9cd8ceb8e2c1137f6b1266c8ffa01f88",
-    "read_bytes": 33786413,
+    "sha256": "de923d20c6c44c36ab04a89d2d2ca6dbafdd3487e008090e9d11ebc2fda7015b",
+    "read_bytes": 33786900,
     "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
@@ -75,7 +76,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,dequant,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--legs", default="sr,srt,dequant,gemm,wo", help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 64 MiB device copy three times (calibrates HBM byte counters)")
@@ -174,6 +175,36 @@ def leg_sr(torch, fq, inputs, steps):
     del xs
     return {"workload": "200 x 8192x8192 bf16 Laplace(1e-4) grads, E4M3 B16, SR Philox, delayed amax N=50",
             "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ms_per_sequence": round(ms, 3)}
+
+
+def leg_sr_transposed(torch, fq, inputs, steps):
+    """Backward-pass operands: the same 200 gradients quantized column-wise
+    (blocks of 16 down the columns, i.e. the quantized transpose), E4M3,
+    stochastic rounding (seed 0x5EED, offset = t), delayed amax every 50;
+    and the round-to-nearest column-wise kernel on the same tensors."""
+    rows = cols = 8192
+    ntens = 200
+    xs = [inputs.device_laplace((rows, cols), 1e-4, inputs.GRADS_SEED0 + t, torch.bfloat16) for t in range(ntens)]
+    res = {}
+    for rnd in ("stochastic", "nearest"):
+        outs = [fq.QTensor.empty(cols, rows, 16, "e4m3", rounding=rnd, amax="delayed") for _ in range(2)]
+        st = fq.AmaxState(50)
+
+        def rec(_):
+            for t in range(ntens):
+                fq.fp4_quantize_transposed(xs[t], 16, "e4m3", rounding=rnd, amax="delayed", state=st, seed=0x5EED,
+                                           offset=t, out=outs[t % 2])
+        gs = GraphSet(torch, 1, rec)
+        reps = max(1, min(3, steps // 10))
+        ms = time_graphs(torch, gs, reps, 1)
+        gbs = ntens * quant_bytes(rows, cols, 16) / (ms * 1e-3) / 1e9
+        res["sr" if rnd == "stochastic" else "rtn"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                                     "ms_per_sequence": round(ms, 3)}
+        del gs, outs
+    del xs
+    res["workload"] = ("200 x 8192x8192 bf16 Laplace(1e-4) grads quantized column-wise (x^T), E4M3 B16, "
+                       "delayed amax N=50; SR Philox and RTN")
+    return res
 
 
 def leg_dequant(torch, fq, xs):
@@ -333,6 +364,9 @@ def main():
     del outs
     if "sr" in want:
         legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)
+        torch.cuda.empty_cache()
+    if "srt" in want:
+        legs["transposed_delayed"] = leg_sr_transposed(torch, fq, inputs, args.steps)
         torch.cuda.empty_cache()
     if "gemm" in want:
         legs["gemm_llama2_7b"] = leg_gemm(torch, fq, inputs)
