@@ -59,7 +59,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 100; }
+int32_t fp4_version(void) { return 101; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -136,6 +136,7 @@ static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
     if (t->fmt.amax != FP4_AMAX_NONE && t->fmt.amax != FP4_AMAX_CURRENT && t->fmt.amax != FP4_AMAX_DELAYED)
         return FP4_ERR_INVALID_ARG;
     if (!scale_fmt_params(t->fmt.scale, f)) return FP4_ERR_INVALID_ARG;
+    if (t->fmt.transform != FP4_TRANSFORM_NONE && t->fmt.transform != FP4_TRANSFORM_RHT) return FP4_ERR_INVALID_ARG;
     if (t->rows < 0 || t->cols < 0) return FP4_ERR_SHAPE;
     if (t->cols % t->fmt.block) return FP4_ERR_SHAPE;
     if (((uintptr_t)t->q & 3u) != 0) return FP4_ERR_ALIGN;
@@ -183,6 +184,8 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     p.seed = seed;
     p.offset = offset;
     p.fmt = f;
+    p.rht = out->fmt.transform == FP4_TRANSFORM_RHT;
+    p.rht_signs = out->fmt.transform_signs;
     st = hip_status(launch_quantize(p, s));
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
     return st;
@@ -198,6 +201,7 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     // x is [out->cols, out->rows]: its rows are the blocked dimension
+    if (out->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;
     if (out->rows % 8) return FP4_ERR_SHAPE;
     if (out->rows * out->cols != 0) {
         if (ld_x < out->rows) return FP4_ERR_SHAPE;
@@ -230,6 +234,8 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     p.seed = seed;
     p.offset = offset;
     p.fmt = f;
+    p.rht = 0;
+    p.rht_signs = 0;
     st = hip_status(launch_quantize_t(p, s));
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
     return st;
@@ -257,6 +263,8 @@ fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_
     p.y = y;
     p.y_bf16 = y_dtype == FP4_DTYPE_BF16;
     p.ld = ld_y;
+    p.rht = in->fmt.transform == FP4_TRANSFORM_RHT;
+    p.rht_signs = in->fmt.transform_signs;
     return hip_status(launch_dequantize(p, (hipStream_t)stream));
 }
 
@@ -270,6 +278,11 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (!c) return FP4_ERR_INVALID_ARG;
     if (a->cols != b->cols) return FP4_ERR_SHAPE;
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
+    // transformed operands multiply to the same product only when both carry
+    // the same transform along K
+    if (a->fmt.transform != b->fmt.transform) return FP4_ERR_UNSUPPORTED;
+    if (a->fmt.transform != FP4_TRANSFORM_NONE && a->fmt.transform_signs != b->fmt.transform_signs)
+        return FP4_ERR_UNSUPPORTED;
     if (a->cols % 128) return FP4_ERR_SHAPE;
     if (ldc < b->rows) return FP4_ERR_SHAPE;
     if (((uintptr_t)c & 1u) != 0) return FP4_ERR_ALIGN;
@@ -297,6 +310,7 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (st != FP4_OK) return st;
     if (!x || !y) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
+    if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     // the kernel addresses W and x with 32-bit byte/element offsets

@@ -168,6 +168,90 @@ __device__ __forceinline__ float dpp_max_xor2(float v)
 }
 
 // ---------------------------------------------------------------------------
+// Blockwise randomized Hadamard transform, applied before quantization
+// (ue5m3-fp4-pretraining "Что сделали": a randomized Hadamard transform
+// spreads outliers over the block before quantization; quant_prune_distill/
+// 574 "Метод": Hadamard rotations bring distributions closer to Gaussian).
+// A block of 8*G elements lives in G adjacent lanes, lane `sub` holding
+// elements 8*sub .. 8*sub+7.  Forward: y = c * H * D * v, D negating element
+// j where bit j of `signs` is set, H the Sylvester Hadamard matrix by
+// butterfly stages h = 1, 2, 4 inside the lane and h = 8 (lane pairs), 16
+// (lane quads) across lanes, each pair (i, i + h) becoming (a + b, a - b) in
+// binary32; c = 1/sqrt(8 G) in binary32.  Inverse: v = D * (c * (H * y)).
+// ---------------------------------------------------------------------------
+constexpr float kRhtNorm16 = 0.25f;
+constexpr float kRhtNorm32 = 0x1.6a09e6p-3f;     // 1/sqrt(32), nearest binary32
+
+template <int G>
+__device__ __forceinline__ void fwht_block(float v[8], uint32_t sub)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & h) continue;
+            const float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+    // h = 8: the partner lane is sub ^ 1; the lower lane keeps a + b, the
+    // upper one a - b with a the lower lane's element
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[k]), 0xB1, 0xF, 0xF, false));
+        v[k] = (sub & 1u) ? o - v[k] : v[k] + o;
+    }
+    if (G == 4) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {                                   // h = 16: partner sub ^ 2
+            const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[k]), 0x4E, 0xF, 0xF, false));
+            v[k] = (sub & 2u) ? o - v[k] : v[k] + o;
+        }
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void rht_forward(float v[8], uint32_t sub, uint32_t signs)
+{
+    static_assert(G == 2 || G == 4, "blocks of 16 or 32");
+    const uint32_t m = signs >> (8 * sub);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = ((m >> k) & 1u) ? -v[k] : v[k];
+    fwht_block<G>(v, sub);
+    const float c = G == 2 ? kRhtNorm16 : kRhtNorm32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = v[k] * c;
+}
+
+template <int G>
+__device__ __forceinline__ void rht_inverse(float v[8], uint32_t sub, uint32_t signs)
+{
+    static_assert(G == 2 || G == 4, "blocks of 16 or 32");
+    fwht_block<G>(v, sub);
+    const uint32_t m = signs >> (8 * sub);
+    const float c = G == 2 ? kRhtNorm16 : kRhtNorm32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float t = v[k] * c;
+        v[k] = ((m >> k) & 1u) ? -t : t;
+    }
+}
+
+// max |v| of 8 binary32 values as bits (non-negative floats order like
+// their bit patterns)
+__device__ __forceinline__ uint32_t absmax_bits8(const float v[8])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t u = __float_as_uint(v[k]) & 0x7FFFFFFFu;
+        m = m > u ? m : u;
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds, multipliers
 // 0xD2511F53 / 0xCD9E8D57, Weyl key increments 0x9E3779B9 / 0xBB67AE85.
 // ---------------------------------------------------------------------------

@@ -52,6 +52,8 @@ struct QuantLaunch {
     int32_t stochastic;
     uint64_t seed, offset;
     ScaleFmtHost fmt;
+    int32_t rht;               // blockwise randomized Hadamard transform first
+    uint32_t rht_signs;
 };
 
 struct DequantLaunch {
@@ -64,6 +66,8 @@ struct DequantLaunch {
     void* y;
     int32_t y_bf16;
     int64_t ld;
+    int32_t rht;               // inverse blockwise Hadamard transform last
+    uint32_t rht_signs;
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);

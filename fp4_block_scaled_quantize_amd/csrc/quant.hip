@@ -138,9 +138,12 @@ struct Unit<float> {
 // ---------------------------------------------------------------------------
 constexpr int kAmaxThreads = 512;
 
-template <typename InT, bool STRIDED>
+// ROTG > 0: the maximum of the blockwise Hadamard-transformed tensor, blocks
+// of 8*ROTG elements (adjacent units live in adjacent lanes, and a block's
+// units are all in range or all out of it).
+template <typename InT, bool STRIDED, int ROTG>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* __restrict__ x, uint32_t nunits, FastDiv upr,
-                                                       int64_t ld, AmaxDev* __restrict__ dst)
+                                                       int64_t ld, AmaxDev* __restrict__ dst, uint32_t signs)
 {
     constexpr int U = sizeof(InT) == 2 ? 8 : 4;
     uint32_t m = 0u;
@@ -155,7 +158,15 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* __restrict__ 
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            uint32_t t = un[j].absmax();
+            uint32_t t;
+            if (ROTG) {
+                float v[8];
+                un[j].get(v);
+                rht_forward<ROTG ? ROTG : 2>(v, threadIdx.x & (ROTG - 1), signs);
+                t = absmax_bits8(v);
+            } else {
+                t = un[j].absmax();
+            }
             m = m > t ? m : t;
         }
     }
@@ -172,20 +183,31 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const void* __restrict__ 
     }
 }
 
+template <typename InT, int ROTG>
+static void launch_amax2(const void* x, uint32_t nunits, const FastDiv& fd, int64_t ld, bool strided, AmaxDev* dst,
+                         uint32_t signs, hipStream_t s)
+{
+    const dim3 g(kAmaxParts), b(kAmaxThreads);
+    if (strided) hipLaunchKernelGGL((k_amax<InT, true, ROTG>), g, b, 0, s, x, nunits, fd, ld, dst, signs);
+    else hipLaunchKernelGGL((k_amax<InT, false, ROTG>), g, b, 0, s, x, nunits, fd, ld, dst, signs);
+}
+
+// rot_block: 0 (plain maximum) or the block size of the Hadamard transform
 static hipError_t launch_amax(const void* x, int32_t x_bf16, int64_t rows, int64_t cols, int64_t ld, AmaxDev* dst,
-                       hipStream_t s)
+                              hipStream_t s, int rot_block = 0, uint32_t signs = 0)
 {
     const uint32_t upr = (uint32_t)(cols / 8);
     const uint32_t nunits = (uint32_t)(rows * (cols / 8));
     const bool strided = (ld != cols);
     FastDiv fd = make_fastdiv(upr ? upr : 1);
-    const dim3 g(kAmaxParts), b(kAmaxThreads);
     if (x_bf16) {
-        if (strided) hipLaunchKernelGGL((k_amax<uint16_t, true>), g, b, 0, s, x, nunits, fd, ld, dst);
-        else hipLaunchKernelGGL((k_amax<uint16_t, false>), g, b, 0, s, x, nunits, fd, ld, dst);
+        if (rot_block == 16) launch_amax2<uint16_t, 2>(x, nunits, fd, ld, strided, dst, signs, s);
+        else if (rot_block == 32) launch_amax2<uint16_t, 4>(x, nunits, fd, ld, strided, dst, signs, s);
+        else launch_amax2<uint16_t, 0>(x, nunits, fd, ld, strided, dst, signs, s);
     } else {
-        if (strided) hipLaunchKernelGGL((k_amax<float, true>), g, b, 0, s, x, nunits, fd, ld, dst);
-        else hipLaunchKernelGGL((k_amax<float, false>), g, b, 0, s, x, nunits, fd, ld, dst);
+        if (rot_block == 16) launch_amax2<float, 2>(x, nunits, fd, ld, strided, dst, signs, s);
+        else if (rot_block == 32) launch_amax2<float, 4>(x, nunits, fd, ld, strided, dst, signs, s);
+        else launch_amax2<float, 0>(x, nunits, fd, ld, strided, dst, signs, s);
     }
     return hipGetLastError();
 }
@@ -214,6 +236,7 @@ struct QArgs {
     int32_t refresh;
     ScaleFmt f;
     uint32_t key0, key1, off0, off1;
+    uint32_t signs;              // blockwise Hadamard transform sign mask (ROT kernels)
 };
 
 // The tensor maximum of this call: the reduction of the amax kernel's
@@ -343,7 +366,10 @@ __device__ __forceinline__ float quad_bcast(float v)
 // FUSED: single-pass refresh (the tensor maximum of this call is agreed
 // across the grid while the units stay in registers); otherwise the maximum
 // comes from the amax kernel's partials (refresh) or the stored value.
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED>
+// ROT: the blockwise randomized Hadamard transform is applied to every block
+// right after the loads; block maxima, the tensor maximum and the codes all
+// see the transformed values.
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT>
 __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArgs a)
 {
     constexpr int T = FUSED ? kFThreads : kQThreads;
@@ -368,12 +394,24 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         else un[j].zero();
     }
 
+    // the transformed values (ROT only; units past the end are zeros, and a
+    // block's units are all in range or all out of it)
+    float rv[ROT ? U : 1][8];
+    if (ROT) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            un[j].get(rv[j]);
+            rht_forward<G>(rv[j], sub, a.signs);
+        }
+    }
+
     // block maxima, reduced over the G lanes of each block (independent of
     // the tensor scale)
     float bm[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-        bm[j] = __uint_as_float(dpp_umax_xor1(un[j].absmax()));
+        const uint32_t um = ROT ? absmax_bits8(rv[ROT ? j : 0]) : un[j].absmax();
+        bm[j] = __uint_as_float(dpp_umax_xor1(um));
         if (G == 4) bm[j] = __uint_as_float(dpp_umax_xor2(__float_as_uint(bm[j])));
     }
 
@@ -440,7 +478,12 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     for (int j = 0; j < U; ++j) {
         const uint32_t u = base + j * 64 + lane;
         float v[8];
-        un[j].get(v);
+        if (ROT) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = rv[ROT ? j : 0][k];
+        } else {
+            un[j].get(v);
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = v[k] * inv[j];
         uint32_t packed;
@@ -463,28 +506,36 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED>
-static void launch_q5(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT>
+static void launch_q6(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
 {
     const dim3 t(FUSED ? kFThreads : kQThreads);
     if (strided)
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED, ROT>), dim3(blocks), t, 0, s, a);
     else
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED, ROT>), dim3(blocks), t, 0, s, a);
+}
+
+template <typename InT, int BLOCK, bool ROT>
+static void launch_q4(const QArgs& a, bool sr, bool e8, bool fused, bool strided, uint32_t blocks, hipStream_t s)
+{
+    if (sr) {
+        if (fused) launch_q6<InT, BLOCK, true, false, true, ROT>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, true, true, false, ROT>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, true, false, false, ROT>(a, strided, blocks, s);
+    } else {
+        if (fused) launch_q6<InT, BLOCK, false, false, true, ROT>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, false, true, false, ROT>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, false, false, false, ROT>(a, strided, blocks, s);
+    }
 }
 
 template <typename InT, int BLOCK>
-static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, uint32_t blocks, hipStream_t s)
+static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, uint32_t blocks,
+                      hipStream_t s)
 {
-    if (sr) {
-        if (fused) launch_q5<InT, BLOCK, true, false, true>(a, strided, blocks, s);
-        else if (e8) launch_q5<InT, BLOCK, true, true, false>(a, strided, blocks, s);
-        else launch_q5<InT, BLOCK, true, false, false>(a, strided, blocks, s);
-    } else {
-        if (fused) launch_q5<InT, BLOCK, false, false, true>(a, strided, blocks, s);
-        else if (e8) launch_q5<InT, BLOCK, false, true, false>(a, strided, blocks, s);
-        else launch_q5<InT, BLOCK, false, false, false>(a, strided, blocks, s);
-    }
+    if (rot) launch_q4<InT, BLOCK, true>(a, sr, e8, fused, strided, blocks, s);
+    else launch_q4<InT, BLOCK, false>(a, sr, e8, fused, strided, blocks, s);
 }
 
 // Compute units of a device (cached; every thread computes the same value).
@@ -517,7 +568,8 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.key1 = (uint32_t)(p.seed >> 32);
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols;
+    a.signs = p.rht_signs;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols, rot = p.rht != 0;
 
     // A refresh reads the input once when the whole tensor fits the
     // single-pass grid (at most one workgroup per CU, kFUnroll units per
@@ -534,7 +586,8 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         if (blocks == 0) blocks = 1;
         fused = blocks <= max_wg;
         if (!fused) {
-            hipError_t e = launch_amax(p.x, p.x_bf16, p.rows, p.cols, p.ld, p.amax_src, s);
+            hipError_t e = launch_amax(p.x, p.x_bf16, p.rows, p.cols, p.ld, p.amax_src, s, rot ? p.block : 0,
+                                       p.rht_signs);
             if (e != hipSuccess) return e;
         }
     }
@@ -544,11 +597,11 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         if (blocks == 0) blocks = 1;
     }
     if (p.x_bf16) {
-        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, blocks, s);
-        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, blocks, s);
+        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, rot, blocks, s);
+        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, rot, blocks, s);
     } else {
-        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, blocks, s);
-        else launch_q3<float, 32>(a, sr, e8, fused, strided, blocks, s);
+        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, rot, blocks, s);
+        else launch_q3<float, 32>(a, sr, e8, fused, strided, rot, blocks, s);
     }
     return hipGetLastError();
 }
@@ -819,12 +872,15 @@ constexpr int kDQUnroll = 4;                 // units per lane, loads issued tog
 // Each wave dequantizes kDQUnroll * 64 consecutive units; unit j of a lane
 // is base + 64 j + lane, so every load and store instruction of a wave
 // covers a contiguous span.
-template <bool OUT_BF16, int BLOCK, bool E8M0>
+// ROT: the inverse blockwise Hadamard transform follows the binary32
+// dequantization (the G units of a block are adjacent lanes and are all in
+// range or all out of it).
+template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT>
 __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ tensor_scale, uint32_t nunits,
                                                            FastDiv upr, int64_t ld, int strided, ScaleFmt f,
-                                                           void* __restrict__ y)
+                                                           void* __restrict__ y, uint32_t signs)
 {
     constexpr int U = kDQUnroll;
     const uint32_t lane = threadIdx.x & 63;
@@ -850,6 +906,7 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
             float t = e2m1_value((w[j] >> (4 * k)) & 0xFu) * s;
             o[k] = t * g;
         }
+        if (ROT) rht_inverse<BLOCK / 8>(o, lane & (BLOCK / 8 - 1), signs);
         const uint64_t off = unit_offset(u, strided, upr, ld);
         if (OUT_BF16) {
             u32x4 r;
@@ -866,19 +923,29 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
     }
 }
 
-template <bool OUT_BF16, int BLOCK>
-static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
+template <bool OUT_BF16, int BLOCK, bool ROT>
+static void launch_dq3(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
     const uint32_t per_block = kDQThreads * kDQUnroll;
     uint32_t blocks = (nunits + per_block - 1) / per_block;
     if (blocks == 0) blocks = 1;
     if (f.is_e8m0)
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true>), dim3(blocks), dim3(kDQThreads), 0, s,
-                           (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y);
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true, ROT>), dim3(blocks), dim3(kDQThreads), 0, s,
+                           (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
+                           p.rht_signs);
     else
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false>), dim3(blocks), dim3(kDQThreads), 0, s,
-                           (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y);
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false, ROT>), dim3(blocks), dim3(kDQThreads), 0, s,
+                           (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
+                           p.rht_signs);
+}
+
+template <bool OUT_BF16, int BLOCK>
+static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
+                       hipStream_t s)
+{
+    if (p.rht) launch_dq3<OUT_BF16, BLOCK, true>(p, nunits, fd, strided, f, s);
+    else launch_dq3<OUT_BF16, BLOCK, false>(p, nunits, fd, strided, f, s);
 }
 
 hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s)

@@ -87,11 +87,34 @@ typedef enum fp4_amax_policy {
 
 typedef enum fp4_dtype { FP4_DTYPE_F32 = 0, FP4_DTYPE_BF16 = 1 } fp4_dtype;
 
+/* Transform applied to every block before quantization
+ * (ue5m3-fp4-pretraining "Что сделали": a randomized Hadamard transform
+ * spreads outliers over the block before quantization, and that scheme
+ * leaves it out; quant_prune_distill/574 "Метод": Hadamard rotations bring
+ * weights and activations closer to Gaussian).  The pages give no formula;
+ * reading, for every block v of `block` consecutive elements along the
+ * blocked dimension:
+ *   y = c * H * D * v,  D = diag(-1 where bit j of transform_signs is set,
+ *   else +1),  H the Sylvester Hadamard matrix ((H)_ij = (-1)^popcount(i&j)),
+ *   c = 1/sqrt(block) rounded to binary32 (exactly 1/4 for block 16),
+ * in binary32: H by butterfly stages h = 1, 2, 4, ... (each pair (i, i+h)
+ * becomes (a + b, a - b)), then the product by c.  Block maxima, the tensor
+ * maximum and the codes all see y.  Dequantization applies the inverse
+ * v = D * (c * (H * y)) to the binary32 dequantized values.  H D / sqrt(B) is
+ * orthogonal, so fp4_gemm of two operands transformed with the same
+ * block and signs along K computes the same product. */
+typedef enum fp4_transform {
+    FP4_TRANSFORM_NONE = 0,
+    FP4_TRANSFORM_RHT = 1      /* blockwise randomized Hadamard transform     */
+} fp4_transform;
+
 typedef struct fp4_format {
-    int32_t block;    /* 16 or 32 elements per scale                        */
-    int32_t scale;    /* fp4_scale_fmt                                      */
-    int32_t rounding; /* fp4_rounding                                       */
-    int32_t amax;     /* fp4_amax_policy                                    */
+    int32_t block;            /* 16 or 32 elements per scale                  */
+    int32_t scale;            /* fp4_scale_fmt                                */
+    int32_t rounding;         /* fp4_rounding                                 */
+    int32_t amax;             /* fp4_amax_policy                              */
+    int32_t transform;        /* fp4_transform                                */
+    uint32_t transform_signs; /* RHT: bit j negates element j of each block   */
 } fp4_format;
 
 /* A quantized tensor.  q: rows*cols/2 bytes; scales: rows*cols/block bytes;
@@ -160,6 +183,8 @@ FP4_API fp4_status fp4_amax_state_set(fp4_amax_state* state, uint64_t calls, flo
  * workgroups agree on amax_t through the state), else twice (an amax pass,
  * then the quantize pass).
  * seed, offset: used only for FP4_ROUND_STOCHASTIC.
+ * out->fmt.transform = FP4_TRANSFORM_RHT transforms every block first (see
+ * fp4_transform); the tensor maximum is then that of the transformed tensor.
  * Errors: INVALID_ARG (null pointers, bad enums, missing state), SHAPE,
  * ALIGN, UNSUPPORTED (E8M0 with a tensor-scale policy).
  */
@@ -182,7 +207,8 @@ FP4_API fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp
  * x: device, 16-byte aligned, ld_x * sizeof(elem) a multiple of 16, ld_x >=
  * out->rows; out->rows % 8 == 0; out->cols % block == 0; out->q 16-byte
  * aligned.  A refresh of the tensor maximum reads x twice (an amax pass,
- * then the quantize pass).  Errors as fp4_quantize.
+ * then the quantize pass).  Errors as fp4_quantize; a transform other than
+ * FP4_TRANSFORM_NONE is UNSUPPORTED here.
  */
 FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
                                    fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
@@ -191,7 +217,9 @@ FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64
  * fp4_dequantize -- y[rows, cols] (row stride ld_y, f32 or bf16) =
  * RN(RN(e2m1(code) * s) * g), rounded once more to bf16 (RNE) for bf16
  * output (quant_prune_distill/486 "Метод": the element times its group's
- * scale).  in->tensor_scale[0] is read on the device.  y: 16-byte aligned,
+ * scale).  With in->fmt.transform = FP4_TRANSFORM_RHT the inverse transform
+ * is applied to the binary32 values before any bf16 rounding.
+ * in->tensor_scale[0] is read on the device.  y: 16-byte aligned,
  * ld_y * sizeof(elem) a multiple of 16.
  */
 FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream);
@@ -202,7 +230,8 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * A = a [M, K] and W = b [N, K] both blocked along K (C = A W^T)
  * (ue5m3-fp4-pretraining "Что сделали": the linear layers run in FP4;
  * quant_prune_distill/574 "Выводы": weight + activation FP4 for the
- * compute-bound regime).  Both operands must use the same block size.
+ * compute-bound regime).  Both operands must use the same block size and
+ * the same transform (kind and signs; UNSUPPORTED otherwise).
  * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within
@@ -220,8 +249,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * weight-only NVFP4, memory-bound small-batch generation).
  * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
  * 1 <= M <= 16; K % 256 == 0; x 16-byte aligned, ldx % 8 == 0, ldy >= N;
- * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB
- * (UNSUPPORTED otherwise).
+ * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB and no
+ * transform on w (UNSUPPORTED otherwise).
  */
 FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
                        int64_t ldy, void* stream);

@@ -112,3 +112,23 @@ def test_quantize_transposed_checks():
     te = _tensor(rows=64, cols=32, scale=4, block=32)
     assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(te), FAKE, 0, 0, None) == -2
     assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(t), None, 0, 0, None) == -1   # no state
+
+
+def test_transform_checks():
+    L = fq.lib()
+    assert L.fp4_version() >= 101
+    t = _tensor()
+    t.fmt.transform = 7                                            # unknown transform
+    assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -1
+    a = _tensor(rows=8, cols=256)
+    b = _tensor(rows=8, cols=256)
+    a.fmt.transform, a.fmt.transform_signs = 1, 5
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2   # only one operand transformed
+    b.fmt.transform, b.fmt.transform_signs = 1, 6
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2   # different signs
+    w = _tensor(rows=8, cols=256)
+    w.fmt.transform = 1
+    assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
+    tt = _tensor(rows=64, cols=32)
+    tt.fmt.transform = 1
+    assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -2
