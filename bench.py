@@ -17,7 +17,8 @@ agrees on the maximum.
 
 Further legs reported in "legs": stochastic rounding with delayed amax over
 200 successive 8192x8192 gradients, the same gradients quantized column-wise
-(the backward-pass operands), dequantize, the block-scaled GEMM on the
+(the backward-pass operands), dequantize, quantize with the blockwise
+randomized Hadamard transform, the block-scaled GEMM on the
 Llama-2 7B linear shapes, and the weight-only GEMM at Qwen-2.5 decode
 shapes.  "roofline" is the dominant kernel of the step (the single-pass
 E4M3 block-16 current-amax quantize kernel: four of the five calls) timed
@@ -43,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "de923d20c6c44c36ab04a89d2d2ca6dbafdd3487e008090e9d11ebc2fda7015b",
-    "read_bytes": 33786900,
+    "sha256": "d986e2fba5c566f01c750dbce0d97ded1fead302860180c037b4834352f80718",
+    "read_bytes": 33787456,
     "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
@@ -76,7 +77,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,srt,dequant,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--legs", default="sr,srt,dequant,rht,gemm,wo", help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 64 MiB device copy three times (calibrates HBM byte counters)")
@@ -204,6 +205,31 @@ def leg_sr_transposed(torch, fq, inputs, steps):
     del xs
     res["workload"] = ("200 x 8192x8192 bf16 Laplace(1e-4) grads quantized column-wise (x^T), E4M3 B16, "
                        "delayed amax N=50; SR Philox and RTN")
+    return res
+
+
+def leg_rht(torch, fq, xs):
+    """Cost of the blockwise randomized Hadamard transform fused into the
+    quantize kernel: the sweep tensor quantized E4M3 block 16 (current
+    amax, single-pass kernel) and E8M0 block 32, with and without the
+    transform, over the rotating inputs."""
+    rows, cols = xs[0].shape
+    res = {}
+    for fmt, block, pol in (("e4m3", 16, "current"), ("e8m0", 32, "none")):
+        for signs in (None, 0x9E3779B9):
+            outs = [fq.QTensor.empty(rows, cols, block, fmt, amax=pol) for _ in xs]
+            st = fq.AmaxState(1) if pol == "current" else None
+
+            def rec(_):
+                for j in range(len(xs)):
+                    fq.fp4_quantize(xs[j], block, fmt, amax=pol, state=st, out=outs[j], rht_signs=signs)
+            gs = GraphSet(torch, 1, rec)
+            ms = time_graphs(torch, gs, 20, 3) / len(xs)
+            algo = quant_bytes(rows, cols, block)
+            res[f"{fmt}_b{block}_{'rht' if signs is not None else 'plain'}"] = {
+                "us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1)}
+            del gs, outs
+    res["workload"] = "4096x4096 bf16 sweep tensor, RTN, with / without the block-16/32 randomized Hadamard transform"
     return res
 
 
@@ -361,6 +387,8 @@ def main():
     want = [] if args.legs == "none" else args.legs.split(",")
     if "dequant" in want:
         legs["dequant"] = leg_dequant(torch, fq, xs[:8])
+    if "rht" in want:
+        legs["rht"] = leg_rht(torch, fq, xs[:8])
     del outs
     if "sr" in want:
         legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)
