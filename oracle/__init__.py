@@ -44,7 +44,16 @@ FORMATS = {
     "e8m0": (8, 0, 0),
 }
 
+ELEMS = {"e2m1": 0, "int4": 1}
+
 _lib = None
+
+
+def _elem(elem: str) -> int:
+    try:
+        return ELEMS[elem]
+    except KeyError:
+        raise ValueError(f"unknown element grid {elem!r}") from None
 
 
 def lib():
@@ -84,6 +93,15 @@ def lib():
         "or_e2m1_sr_array": (None, [c_p, c_p, c_p, c_i64]),
         "or_sr_bits_array": (None, [c_u64, c_u64, c_u64, c_i64, c_p]),
         "or_rht_norm": (c_f, [c_int]),
+        "or_int4_decode": (c_d, [c_int]),
+        "or_int4_rtn": (c_int, [c_f]),
+        "or_int4_sr": (c_int, [c_f, ctypes.c_uint32]),
+        "or_tensor_scale_elem": (c_f, [c_f, c_int, c_int, c_int, c_int]),
+        "or_quantize_elem": (c_int, [c_p, c_int, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_f,
+                                     c_int, c_u64, c_u64, c_i64, c_i64, c_p, c_p, c_int, c_int]),
+        "or_dequantize_elem": (c_int, [c_p, c_p, c_f, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int,
+                                       c_p, c_i64, c_int]),
+        "or_dequantize_f64_elem": (c_int, [c_p, c_p, c_f, c_i64, c_i64, c_int, c_int, c_int, c_int, c_p, c_int]),
         "or_rht_forward": (c_int, [c_p, c_int, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
         "or_rht_inverse": (c_int, [c_p, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
         "or_f32_to_bf16_array": (None, [c_p, c_p, c_i64]),
@@ -175,8 +193,20 @@ def e8m0_block_code(amax_b: float) -> int:
     return lib().or_e8m0_block_code(float(amax_b))
 
 
-def tensor_scale(amax_t: float, fmt: str) -> float:
-    return lib().or_tensor_scale(float(amax_t), *_fmt(fmt))
+def tensor_scale(amax_t: float, fmt: str, elem: str = "e2m1") -> float:
+    return lib().or_tensor_scale_elem(float(amax_t), *_fmt(fmt), _elem(elem))
+
+
+def int4_decode(code: int) -> float:
+    return lib().or_int4_decode(int(code))
+
+
+def int4_rtn(v: float) -> int:
+    return lib().or_int4_rtn(float(v))
+
+
+def int4_sr(v: float, r16: int) -> int:
+    return lib().or_int4_sr(float(v), int(r16))
 
 
 def philox4x32_10(ctr, key):
@@ -215,7 +245,7 @@ def amax(x: np.ndarray) -> float:
 
 
 def quantize(x: np.ndarray, block: int, fmt: str, g: float, *, stochastic: bool = False,
-             seed: int = 0, offset: int = 0, rows: tuple | None = None, nthreads: int = 1):
+             seed: int = 0, offset: int = 0, rows: tuple | None = None, nthreads: int = 1, elem: str = "e2m1"):
     """Quantize rows [r0, r1) of x (all rows by default) with tensor scale g.
 
     Returns (q, scales): q is uint8 [r1-r0, cols/2] (low nibble = even
@@ -226,15 +256,15 @@ def quantize(x: np.ndarray, block: int, fmt: str, g: float, *, stochastic: bool 
     r0, r1 = (0, nrows) if rows is None else rows
     q = np.zeros((r1 - r0, cols // 2), dtype=np.uint8)
     s = np.zeros((r1 - r0, cols // block), dtype=np.uint8)
-    rc = lib().or_quantize(_ptr(x), is_bf16, nrows, cols, cols, block, *_fmt(fmt), float(g),
-                           int(stochastic), seed, offset, r0, r1, _ptr(q), _ptr(s), nthreads)
+    rc = lib().or_quantize_elem(_ptr(x), is_bf16, nrows, cols, cols, block, *_fmt(fmt), float(g),
+                                int(stochastic), seed, offset, r0, r1, _ptr(q), _ptr(s), nthreads, _elem(elem))
     if rc != 0:
         raise ValueError("oracle quantize: argument outside the contract")
     return q, s
 
 
 def dequantize(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str,
-               out: str = "f32") -> np.ndarray:
+               out: str = "f32", elem: str = "e2m1") -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     rows, cols = q.shape[0], q.shape[1] * 2
@@ -244,19 +274,21 @@ def dequantize(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str
         y = np.empty((rows, cols), dtype=np.uint16)
     else:
         raise ValueError(out)
-    rc = lib().or_dequantize(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt),
-                             int(out == "bf16"), _ptr(y), cols)
+    rc = lib().or_dequantize_elem(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt),
+                                  int(out == "bf16"), _ptr(y), cols, _elem(elem))
     if rc != 0:
         raise ValueError("oracle dequantize: argument outside the contract")
     return y
 
 
-def dequantize_f64(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str) -> np.ndarray:
+def dequantize_f64(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str,
+                   elem: str = "e2m1") -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     rows, cols = q.shape[0], q.shape[1] * 2
     y = np.empty((rows, cols), dtype=np.float64)
-    rc = lib().or_dequantize_f64(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt), _ptr(y))
+    rc = lib().or_dequantize_f64_elem(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt), _ptr(y),
+                                      _elem(elem))
     if rc != 0:
         raise ValueError("oracle dequantize_f64: argument outside the contract")
     return y
@@ -320,7 +352,8 @@ class AmaxState:
     amax: float = 0.0
 
 
-def resolve_tensor_scale(x: np.ndarray, fmt: str, policy: str, state: AmaxState | None = None):
+def resolve_tensor_scale(x: np.ndarray, fmt: str, policy: str, state: AmaxState | None = None,
+                         elem: str = "e2m1"):
     """Return (g, amax_used) for one quantize call and advance a delayed state.
 
     policy: "none" (g = 1), "current" (amax of this tensor), or "delayed"
@@ -330,29 +363,32 @@ def resolve_tensor_scale(x: np.ndarray, fmt: str, policy: str, state: AmaxState 
         return 1.0, 0.0
     if policy == "current":
         a = amax(x)
-        return tensor_scale(a, fmt), a
+        return tensor_scale(a, fmt, elem), a
     if policy == "delayed":
         if state is None:
             raise ValueError("delayed policy needs a state")
         if state.calls % state.interval == 0:
             state.amax = amax(x)
         state.calls += 1
-        return tensor_scale(state.amax, fmt), state.amax
+        return tensor_scale(state.amax, fmt, elem), state.amax
     raise ValueError(policy)
 
 
 def quantize_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *, state: AmaxState | None = None,
                     stochastic: bool = False, seed: int = 0, offset: int = 0, nthreads: int = 1,
-                    rht_signs: int | None = None):
+                    rht_signs: int | None = None, elem: str = "e2m1"):
     """Whole quantize call: tensor scale per policy, then every block.
     With rht_signs the blockwise randomized Hadamard transform is applied
     first (rht_forward) and everything after it, the tensor maximum
     included, sees the transformed binary32 tensor.
+    elem: "e2m1" (FP4) or "int4" (the integer grid -7..7, two's-complement
+    nibbles; quant_prune_distill/574 "Метод": NVINT4 / MXINT4).
     Returns (q, scales, g, amax_used)."""
     if rht_signs is not None:
         x = rht_forward(x, block, rht_signs)
-    g, a = resolve_tensor_scale(x, fmt, policy, state)
-    q, s = quantize(x, block, fmt, g, stochastic=stochastic, seed=seed, offset=offset, nthreads=nthreads)
+    g, a = resolve_tensor_scale(x, fmt, policy, state, elem)
+    q, s = quantize(x, block, fmt, g, stochastic=stochastic, seed=seed, offset=offset, nthreads=nthreads,
+                    elem=elem)
     return q, s, g, a
 
 

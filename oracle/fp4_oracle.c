@@ -99,6 +99,55 @@ OR_EXPORT int or_e2m1_sr(float v, uint32_t r16)
 }
 
 /* ------------------------------------------------------------------------ */
+/* INT4 element grid.  [P-INT] quant_prune_distill/574 "Метод": the NV and   */
+/* MX block/scale schemes are paired with an integer element grid (NVINT4:  */
+/* groups of 16 with E4M3 scales, MXINT4: groups of 32 with E8M0 scales).    */
+/* The page gives no encoding.  Reading: a 4-bit two's-complement integer on */
+/* the symmetric grid -7..7 (the code 0x8 = -8 is never produced), the block */
+/* maximum mapped to 7, round to nearest with ties to the even integer,      */
+/* |v| beyond 7 saturating; stochastic rounding as for E2M1 with grid        */
+/* spacing 1.  A zero result has no sign (code 0).                            */
+/* ------------------------------------------------------------------------ */
+OR_EXPORT double or_int4_decode(int code)
+{
+    code &= 0xF;
+    return (double)(code >= 8 ? code - 16 : code);
+}
+
+/* Nearest integer magnitude 0..7 of |v|: plain search over the grid, ties
+ * to the even integer, saturating at 7. */
+OR_EXPORT int or_int4_rtn(float v)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 7.0) return 7;
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - (double)c);
+        if (d < bd || (d == bd && (c & 1) == 0)) { best = c; bd = d; }
+    }
+    return best;
+}
+
+OR_EXPORT int or_int4_sr(float v, uint32_t r16)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 7.0) return 7;
+    int lo = (int)floor(a);
+    double frac = a - (double)lo;
+    double u = (double)(r16 & 0xFFFFu) / 65536.0;
+    return (u < frac) ? lo + 1 : lo;
+}
+
+/* two's-complement nibble of sign * magnitude (magnitude 0 -> code 0) */
+static int int4_code(int negative, int mag) { return negative ? ((16 - mag) & 0xF) : mag; }
+
+/* largest element magnitude of a grid: 6 (E2M1) or 7 (INT4) */
+static float elem_max(int elem) { return elem ? 7.0f : 6.0f; }
+
+/* ------------------------------------------------------------------------ */
 /* Scale formats.                                                            */
 /*   ExMy signed (x+y = 7, sign bit on top) and UE5M3 (unsigned, 8 bits):    */
 /*   reading: bias 2^(x-1)-1, exponent field 0 is subnormal, no infinity,    */
@@ -209,11 +258,19 @@ OR_EXPORT int or_e8m0_block_code(float amax_b)
 /* Per-tensor scale (reading generalising the NVFP4 recipe amax/(6*448)):
  * g = amax_t / (6 * Smax) in binary32; a zero, underflowed or non-finite
  * quotient gives g = 1.  E8M0 carries no tensor scale (g = 1). */
+OR_EXPORT float or_tensor_scale_elem(float amax_t, int eb, int mb, int sg, int elem);
 OR_EXPORT float or_tensor_scale(float amax_t, int eb, int mb, int sg)
+{
+    return or_tensor_scale_elem(amax_t, eb, mb, sg, 0);
+}
+
+/* As above for the element grid `elem`: the grid's largest magnitude (6 for
+ * E2M1, 7 for INT4) takes the place of 6. */
+OR_EXPORT float or_tensor_scale_elem(float amax_t, int eb, int mb, int sg, int elem)
 {
     if (is_e8m0(eb, mb, sg)) return 1.0f;
     float smax = (float)or_scale_max(eb, mb, sg);
-    float den = 6.0f * smax;
+    float den = elem_max(elem) * smax;
     float g = amax_t / den;
     if (!(g > 0.0f) || g > FLT_MAX) g = 1.0f;
     return g;
@@ -297,13 +354,14 @@ typedef struct {
     int stochastic; uint64_t seed, offset;
     int64_t row0, row1;
     uint8_t* q; uint8_t* scales;
+    int elem;                        /* 0 = E2M1, 1 = INT4 */
 } quant_job;
 
 static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
 {
     const int64_t nb = J->cols / J->block;
     const int e8 = is_e8m0(J->eb, J->mb, J->sg);
-    const float d = 6.0f * J->g;
+    const float d = elem_max(J->elem) * J->g;
     double tab[256];
     decode_table(J->eb, J->mb, J->sg, tab);
     const int ncodes = fmt_ncodes(J->eb, J->mb, J->sg);
@@ -342,12 +400,14 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
                     float v = xv * inv;
                     if (J->stochastic) {
                         uint64_t i = (uint64_t)r * (uint64_t)J->cols + (uint64_t)col;
-                        mag = or_e2m1_sr(v, or_sr_bits(J->seed, J->offset, i));
+                        uint32_t r16 = or_sr_bits(J->seed, J->offset, i);
+                        mag = J->elem ? or_int4_sr(v, r16) : or_e2m1_sr(v, r16);
                     } else {
-                        mag = or_e2m1_rtn(v);
+                        mag = J->elem ? or_int4_rtn(v) : or_e2m1_rtn(v);
                     }
                 }
-                int code = (int)((bits_of_f(xv) >> 31) << 3) | mag;
+                int code = J->elem ? int4_code((int)(bits_of_f(xv) >> 31), mag)
+                                   : (int)((bits_of_f(xv) >> 31) << 3) | mag;
                 if ((col & 1) == 0) qrow[col >> 1] = (uint8_t)code;
                 else qrow[col >> 1] |= (uint8_t)(code << 4);
             }
@@ -364,18 +424,35 @@ static void* quant_thread(void* p)
 }
 
 /* Returns 0 on success, -1 on an argument outside the contract. */
+OR_EXPORT int or_quantize_elem(const void* x, int is_bf16, int64_t rows, int64_t cols, int64_t ld,
+                               int block, int eb, int mb, int sg, float g,
+                               int stochastic, uint64_t seed, uint64_t offset,
+                               int64_t row0, int64_t row1, uint8_t* q, uint8_t* scales, int nthreads, int elem);
+
 OR_EXPORT int or_quantize(const void* x, int is_bf16, int64_t rows, int64_t cols, int64_t ld,
                           int block, int eb, int mb, int sg, float g,
                           int stochastic, uint64_t seed, uint64_t offset,
                           int64_t row0, int64_t row1, uint8_t* q, uint8_t* scales, int nthreads)
 {
+    return or_quantize_elem(x, is_bf16, rows, cols, ld, block, eb, mb, sg, g, stochastic, seed, offset, row0, row1,
+                            q, scales, nthreads, 0);
+}
+
+/* As or_quantize, on the element grid `elem` (0 = E2M1, 1 = INT4). */
+OR_EXPORT int or_quantize_elem(const void* x, int is_bf16, int64_t rows, int64_t cols, int64_t ld,
+                               int block, int eb, int mb, int sg, float g,
+                               int stochastic, uint64_t seed, uint64_t offset,
+                               int64_t row0, int64_t row1, uint8_t* q, uint8_t* scales, int nthreads, int elem)
+{
+    if (elem != 0 && elem != 1) return -1;
     if (!x || !q || !scales || rows < 0 || cols < 0 || ld < cols) return -1;
     if (block != 16 && block != 32) return -1;
     if (cols % block) return -1;
     if (!fmt_valid(eb, mb, sg)) return -1;
     if (row0 < 0 || row1 > rows || row0 > row1) return -1;
     if (!(g > 0.0f)) return -1;
-    quant_job J = {x, is_bf16, rows, cols, ld, block, eb, mb, sg, g, stochastic, seed, offset, row0, row1, q, scales};
+    quant_job J = {x, is_bf16, rows, cols, ld, block, eb, mb, sg, g, stochastic, seed, offset, row0, row1, q, scales,
+                   elem};
     int64_t n = row1 - row0;
     if (nthreads <= 1 || n < 2 * nthreads) {
         quantize_rows(&J, row0, row1);
@@ -407,9 +484,22 @@ OR_EXPORT uint16_t or_f32_to_bf16(float f)
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+static double elem_decode(int code, int elem) { return elem ? or_int4_decode(code) : or_e2m1_decode(code); }
+
+OR_EXPORT int or_dequantize_elem(const uint8_t* q, const uint8_t* scales, float g,
+                                 int64_t rows, int64_t cols, int block, int eb, int mb, int sg,
+                                 int out_bf16, void* y, int64_t ld_y, int elem);
 OR_EXPORT int or_dequantize(const uint8_t* q, const uint8_t* scales, float g,
                             int64_t rows, int64_t cols, int block, int eb, int mb, int sg,
                             int out_bf16, void* y, int64_t ld_y)
+{
+    return or_dequantize_elem(q, scales, g, rows, cols, block, eb, mb, sg, out_bf16, y, ld_y, 0);
+}
+
+/* As or_dequantize on the element grid `elem` (0 = E2M1, 1 = INT4). */
+OR_EXPORT int or_dequantize_elem(const uint8_t* q, const uint8_t* scales, float g,
+                                 int64_t rows, int64_t cols, int block, int eb, int mb, int sg,
+                                 int out_bf16, void* y, int64_t ld_y, int elem)
 {
     if (!q || !scales || !y || (block != 16 && block != 32) || cols % block || ld_y < cols) return -1;
     if (!fmt_valid(eb, mb, sg)) return -1;
@@ -419,7 +509,7 @@ OR_EXPORT int or_dequantize(const uint8_t* q, const uint8_t* scales, float g,
             uint8_t byte = q[r * (cols / 2) + c / 2];
             int code = (c & 1) ? (byte >> 4) : (byte & 0xF);
             float s = (float)or_scale_decode(eb, mb, sg, scales[r * nb + c / block]);
-            float e = (float)or_e2m1_decode(code);
+            float e = (float)elem_decode(code, elem);
             float t = e * s;
             float xh = t * g;
             if (out_bf16) ((uint16_t*)y)[r * ld_y + c] = or_f32_to_bf16(xh);
@@ -502,8 +592,16 @@ OR_EXPORT void or_f32_to_bf16_array(const float* x, uint16_t* y, int64_t n)
 }
 
 /* Exact binary64 dequantization for the GEMM reference: e2m1 * s * g. */
+OR_EXPORT int or_dequantize_f64_elem(const uint8_t* q, const uint8_t* scales, float g, int64_t rows, int64_t cols,
+                                     int block, int eb, int mb, int sg, double* y, int elem);
 OR_EXPORT int or_dequantize_f64(const uint8_t* q, const uint8_t* scales, float g,
                                 int64_t rows, int64_t cols, int block, int eb, int mb, int sg, double* y)
+{
+    return or_dequantize_f64_elem(q, scales, g, rows, cols, block, eb, mb, sg, y, 0);
+}
+
+OR_EXPORT int or_dequantize_f64_elem(const uint8_t* q, const uint8_t* scales, float g, int64_t rows, int64_t cols,
+                                     int block, int eb, int mb, int sg, double* y, int elem)
 {
     if (!q || !scales || !y || (block != 16 && block != 32) || cols % block) return -1;
     if (!fmt_valid(eb, mb, sg)) return -1;
@@ -513,7 +611,7 @@ OR_EXPORT int or_dequantize_f64(const uint8_t* q, const uint8_t* scales, float g
             uint8_t byte = q[r * (cols / 2) + c / 2];
             int code = (c & 1) ? (byte >> 4) : (byte & 0xF);
             double s = or_scale_decode(eb, mb, sg, scales[r * nb + c / block]);
-            y[r * cols + c] = or_e2m1_decode(code) * s * (double)g;
+            y[r * cols + c] = elem_decode(code, elem) * s * (double)g;
         }
     return 0;
 }

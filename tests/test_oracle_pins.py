@@ -757,3 +757,90 @@ def test_rht_dequantize_error_equals_transformed_error(block, fmt):
     assert np.all(np.abs(e_x - e_y) <= 1e-6 * scale + 1e-30)
     bf = oracle.dequantize_rht(q, s, g, block, fmt, signs, out="bf16")
     assert np.array_equal(bf, oracle.f32_to_bf16_bits(xh.astype(np.float32)).reshape(bf.shape))
+
+
+# ---------------------------------------------------------------------------
+# INT4 element grid (NVINT4 / MXINT4)
+# ---------------------------------------------------------------------------
+def test_int4_decode_is_twos_complement():
+    for code in range(16):
+        assert oracle.int4_decode(code) == float(np.array([code << 4], dtype=np.uint8).view(np.int8)[0] >> 4)
+
+
+def test_int4_rtn_matches_numpy_rint():
+    # numpy's rint rounds half to even; the grid saturates at 7
+    centres = [k + 0.5 for k in range(8)] + list(range(9))
+    pieces = []
+    for c in centres:
+        b = np.float32(c).view(np.uint32).astype(np.int64)
+        pieces.append(np.arange(max(b - 2048, 0), b + 2049, dtype=np.int64))
+    pieces.append(np.arange(0, 0x41400000, 1013, dtype=np.int64))
+    bits = np.unique(np.concatenate(pieces)).astype(np.uint32)
+    v = bits.view(np.float32)
+    want = np.minimum(np.rint(v.astype(np.float64)), 7).astype(int)
+    got = np.array([oracle.int4_rtn(float(x)) for x in v[::7]])
+    assert np.array_equal(got, want[::7])
+    for x in (-3.5, -2.5, 0.5, 1.5, 6.5, 7.49, 100.0):
+        assert oracle.int4_rtn(x) == min(int(np.rint(abs(x))), 7)
+
+
+@pytest.mark.parametrize("v", [0.3, 1.0, 2.75, 4.5, 6.999, -5.25, 7.0, 9.0])
+def test_int4_sr_exact_expectation(v):
+    # over all 2^16 random values the mean code is lo + ceil(frac 2^16) / 2^16
+    a = abs(v)
+    mags = np.array([oracle.int4_sr(v, r) for r in range(0, 65536, 1)])
+    if a >= 7:
+        assert np.all(mags == 7)
+        return
+    lo = np.floor(a)
+    frac = a - lo
+    assert set(np.unique(mags)) <= {int(lo), int(lo) + 1}
+    assert (mags == lo + 1).sum() == int(np.ceil(np.float64(np.float32(frac)) * 65536))
+
+
+def test_int4_tensor_max_maps_to_seven():
+    x = _sweep_like(48, 256, 31, bf16=False)
+    for fmt in ("e4m3", "ue5m3"):
+        q, s, g, a = oracle.quantize_tensor(x, 16, fmt, "current", elem="int4")
+        assert g == np.float32(a) / (np.float32(7.0) * np.float32(oracle.scale_max(fmt)))
+        r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+        n = 256 if fmt == "ue5m3" else 128
+        assert s[r, c // 16] == max(cc for cc in range(n) if not oracle.scale_is_nan(fmt, cc))
+        nib = (int(q[r, c // 2]) >> (4 * (c & 1))) & 0xF
+        assert oracle.int4_decode(nib) == (7.0 if x[r, c] > 0 else -7.0)
+
+
+def test_int4_e8m0_blocks_are_exact_nearest():
+    # MX rule: code = floor(log2 amax_b) - 2 + 127, so x / s is exact and the
+    # element is the nearest-even integer of it, clamped to +-7
+    x = _sweep_like(8, 256, 33, bf16=False)
+    q, s, g, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem="int4")
+    assert g == 1.0
+    for r in range(8):
+        for b in range(8):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            am = np.abs(blk).max()
+            assert s[r, b] == int(np.floor(np.log2(am))) - 2 + 127
+            scaled = blk * 2.0 ** (127 - int(s[r, b]))
+            want = np.clip(np.rint(scaled), -7, 7)
+            for k in range(32):
+                col = 32 * b + k
+                nib = (int(q[r, col // 2]) >> (4 * (col & 1))) & 0xF
+                assert oracle.int4_decode(nib) == want[k]
+
+
+def test_int4_dequantize_exact_product_and_gemm_orientation():
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 256, (6, 32), dtype=np.uint8)
+    s = rng.integers(0x30, 0x60, (6, 4), dtype=np.uint8)
+    g = np.float32(0.0371)
+    y = oracle.dequantize(q, s, float(g), 16, "e4m3", elem="int4")
+    yd = oracle.dequantize_f64(q, s, float(g), 16, "e4m3", elem="int4")
+    for r in range(6):
+        for c in range(64):
+            code = (int(q[r, c // 2]) >> (4 * (c & 1))) & 0xF
+            sv = oracle.scale_decode("e4m3", int(s[r, c // 16]))
+            exact = Fraction(oracle.int4_decode(code)) * Fraction(sv) * Fraction(float(g))
+            assert Fraction(float(yd[r, c])) == exact           # exact in binary64
+            t = np.float32(np.float32(oracle.int4_decode(code)) * np.float32(sv))
+            assert y[r, c] == np.float32(t * g)
