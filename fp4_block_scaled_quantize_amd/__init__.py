@@ -25,6 +25,7 @@ SCALE_FORMATS = {"e4m3": 0, "ue5m3": 1, "e3m4": 2, "e1m6": 3, "e8m0": 4, "e2m5":
 ROUNDING = {"nearest": 0, "stochastic": 1}
 AMAX = {"none": 0, "current": 1, "delayed": 2}
 TRANSFORM = {"none": 0, "rht": 1}
+ELEMENT = {"e2m1": 0, "int4": 1}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 FP4_OK = 0
@@ -32,7 +33,8 @@ FP4_OK = 0
 
 class Fp4Format(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("scale", ctypes.c_int32), ("rounding", ctypes.c_int32),
-                ("amax", ctypes.c_int32), ("transform", ctypes.c_int32), ("transform_signs", ctypes.c_uint32)]
+                ("amax", ctypes.c_int32), ("transform", ctypes.c_int32), ("transform_signs", ctypes.c_uint32),
+                ("element", ctypes.c_int32)]
 
 
 class Fp4TensorC(ctypes.Structure):
@@ -115,18 +117,20 @@ class QTensor:
     amax: str = "current"
     transform: str = "none"
     rht_signs: int = 0
+    element: str = "e2m1"
 
     @classmethod
     def empty(cls, rows: int, cols: int, block: int, scale: str, rounding: str = "nearest",
-              amax: str = "current", device="cuda", transform: str = "none", rht_signs: int = 0):
+              amax: str = "current", device="cuda", transform: str = "none", rht_signs: int = 0,
+              element: str = "e2m1"):
         q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
         s = torch.empty((rows, cols // block), dtype=torch.uint8, device=device)
         ts = torch.empty(2, dtype=torch.float32, device=device)
-        return cls(q, s, ts, rows, cols, block, scale, rounding, amax, transform, rht_signs)
+        return cls(q, s, ts, rows, cols, block, scale, rounding, amax, transform, rht_signs, element)
 
     def c(self) -> Fp4TensorC:
         fmt = Fp4Format(self.block, SCALE_FORMATS[self.scale], ROUNDING[self.rounding], AMAX[self.amax],
-                        TRANSFORM[self.transform], self.rht_signs & 0xFFFFFFFF)
+                        TRANSFORM[self.transform], self.rht_signs & 0xFFFFFFFF, ELEMENT[self.element])
         return Fp4TensorC(self.q.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
                           self.rows, self.cols, fmt)
 
@@ -167,11 +171,13 @@ class AmaxState:
 
 def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
                  amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
-                 out: QTensor | None = None, stream=None, rht_signs: int | None = None) -> QTensor:
+                 out: QTensor | None = None, stream=None, rht_signs: int | None = None,
+                 element: str = "e2m1") -> QTensor:
     """Quantize a 2-D fp32/bf16 CUDA tensor (rows may be strided: x.stride(1)
     must be 1).  CURRENT and DELAYED need an AmaxState; one is created for
     CURRENT if none is given.  rht_signs (32-bit sign mask) applies the
-    blockwise randomized Hadamard transform before quantization."""
+    blockwise randomized Hadamard transform before quantization; element
+    "int4" selects the INT4 grid (-7..7) instead of E2M1."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
@@ -180,6 +186,7 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     else:
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)
+    out.element = element
     if amax != "none" and state is None:
         if amax == "delayed":
             raise ValueError("the delayed amax policy needs an AmaxState")
@@ -194,7 +201,7 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
 
 def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
                             amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
-                            out: QTensor | None = None, stream=None) -> QTensor:
+                            out: QTensor | None = None, stream=None, element: str = "e2m1") -> QTensor:
     """Column-wise quantization of a 2-D fp32/bf16 CUDA tensor x [R, C]: the
     result is the quantized x^T [C, R] (blocks run down the columns of x)."""
     if x.dim() != 2 or x.stride(1) != 1:
@@ -204,6 +211,7 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
         out = QTensor.empty(c, r, block, scale, rounding, amax, device=x.device)
     else:
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
+    out.element = element
     if amax != "none" and state is None:
         if amax == "delayed":
             raise ValueError("the delayed amax policy needs an AmaxState")

@@ -59,7 +59,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 101; }
+int32_t fp4_version(void) { return 102; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -137,6 +137,7 @@ static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
         return FP4_ERR_INVALID_ARG;
     if (!scale_fmt_params(t->fmt.scale, f)) return FP4_ERR_INVALID_ARG;
     if (t->fmt.transform != FP4_TRANSFORM_NONE && t->fmt.transform != FP4_TRANSFORM_RHT) return FP4_ERR_INVALID_ARG;
+    if (t->fmt.element != FP4_ELEM_E2M1 && t->fmt.element != FP4_ELEM_INT4) return FP4_ERR_INVALID_ARG;
     if (t->rows < 0 || t->cols < 0) return FP4_ERR_SHAPE;
     if (t->cols % t->fmt.block) return FP4_ERR_SHAPE;
     if (((uintptr_t)t->q & 3u) != 0) return FP4_ERR_ALIGN;
@@ -186,6 +187,7 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     p.fmt = f;
     p.rht = out->fmt.transform == FP4_TRANSFORM_RHT;
     p.rht_signs = out->fmt.transform_signs;
+    p.elem_int4 = out->fmt.element == FP4_ELEM_INT4;
     st = hip_status(launch_quantize(p, s));
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
     return st;
@@ -236,6 +238,7 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     p.fmt = f;
     p.rht = 0;
     p.rht_signs = 0;
+    p.elem_int4 = out->fmt.element == FP4_ELEM_INT4;
     st = hip_status(launch_quantize_t(p, s));
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
     return st;
@@ -265,6 +268,7 @@ fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_
     p.ld = ld_y;
     p.rht = in->fmt.transform == FP4_TRANSFORM_RHT;
     p.rht_signs = in->fmt.transform_signs;
+    p.elem_int4 = in->fmt.element == FP4_ELEM_INT4;
     return hip_status(launch_dequantize(p, (hipStream_t)stream));
 }
 
@@ -280,6 +284,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
     // transformed operands multiply to the same product only when both carry
     // the same transform along K
+    if (a->fmt.element != b->fmt.element) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != b->fmt.transform) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != FP4_TRANSFORM_NONE && a->fmt.transform_signs != b->fmt.transform_signs)
         return FP4_ERR_UNSUPPORTED;
@@ -296,9 +301,10 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     p.block = a->fmt.block;
     p.fa = fa; p.fb = fb;
     p.c = c; p.ldc = ldc;
+    p.elem_int4 = a->fmt.element == FP4_ELEM_INT4;
     hipStream_t s = (hipStream_t)stream;
-    if (fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
-    if (!gemm_dq_supported(fa, fb)) return FP4_ERR_UNSUPPORTED;
+    if (!p.elem_int4 && fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
+    if (!gemm_dq_supported(fa, fb, p.elem_int4 != 0)) return FP4_ERR_UNSUPPORTED;
     return hip_status(launch_gemm_dq(p, s));
 }
 
@@ -311,6 +317,7 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (!x || !y) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
+    if (w->fmt.element != FP4_ELEM_E2M1) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     // the kernel addresses W and x with 32-bit byte/element offsets

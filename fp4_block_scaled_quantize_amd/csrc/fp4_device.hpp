@@ -141,6 +141,35 @@ __device__ __forceinline__ float e2m1_value(uint32_t nib)
 }
 
 // ---------------------------------------------------------------------------
+// INT4 elements (quant_prune_distill/574 "Метод": the NV and MX block/scale
+// schemes paired with an integer grid, NVINT4 / MXINT4).  Reading: the
+// symmetric grid -7..7 as two's-complement nibbles (zero has no sign),
+// nearest with ties to the even integer, saturating at 7; stochastic
+// rounding with grid spacing 1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t int4_nibble(float v, float mag)
+{
+    const uint32_t m = (uint32_t)mag;
+    return (f_bits(v) >> 31) ? ((16u - m) & 15u) : m;
+}
+
+__device__ __forceinline__ uint32_t int4_rtn_code(float v)
+{
+    return int4_nibble(v, __builtin_fminf(__builtin_rintf(__builtin_fabsf(v)), 7.0f));
+}
+
+__device__ __forceinline__ uint32_t int4_sr_code(float v, uint32_t r16)
+{
+    const float a = __builtin_fabsf(v);
+    const float fl = __builtin_floorf(a);
+    const float frac = a - fl;                                     // exact
+    const float up = ((float)r16 < frac * 65536.0f) ? 1.0f : 0.0f;
+    return int4_nibble(v, a >= 7.0f ? 7.0f : fl + up);
+}
+
+__device__ __forceinline__ float int4_value(uint32_t nib) { return (float)((int32_t)(nib << 28) >> 28); }
+
+// ---------------------------------------------------------------------------
 // wave64 helpers
 // ---------------------------------------------------------------------------
 // Max of non-negative binary32 bit patterns across lane pairs / quads.

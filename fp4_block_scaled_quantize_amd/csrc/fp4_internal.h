@@ -54,6 +54,7 @@ struct QuantLaunch {
     ScaleFmtHost fmt;
     int32_t rht;               // blockwise randomized Hadamard transform first
     uint32_t rht_signs;
+    int32_t elem_int4;         // INT4 element grid instead of E2M1
 };
 
 struct DequantLaunch {
@@ -68,6 +69,7 @@ struct DequantLaunch {
     int64_t ld;
     int32_t rht;               // inverse blockwise Hadamard transform last
     uint32_t rht_signs;
+    int32_t elem_int4;         // INT4 element grid instead of E2M1
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);
@@ -83,11 +85,12 @@ struct GemmLaunch {
     ScaleFmtHost fa, fb;
     uint16_t* c;
     int64_t ldc;
+    int32_t elem_int4;         // both operands on the INT4 grid
 };
 
 // The exact dequantize path needs one 16-bit type (f16 or bf16) that holds
 // every e2m1 * s product of both operands exactly.
-bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb);
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, bool int4);
 hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
 

@@ -515,7 +515,7 @@ __device__ __forceinline__ float split_pow2(float g)
 // Dequantize 32 E2M1 codes (16 bytes) with scale(s) into 32 16-bit values.
 // The product e2m1 * s is exact in binary32 and, for the chosen element type,
 // exact in f16 / bf16, so the narrowing is exact (truncation = rounding).
-template <bool F16>
+template <bool F16, bool INT = false>
 __device__ __forceinline__ void dequant32(const v4i& codes, float s0, float s1, uint32_t out[16])
 {
 #pragma unroll
@@ -524,8 +524,9 @@ __device__ __forceinline__ void dequant32(const v4i& codes, float s0, float s1, 
         const float s = d < 2 ? s0 : s1;    // elements 0..15 use s0, 16..31 use s1
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            const float v0 = e2m1_value((w >> (8 * h)) & 0xFu) * s;
-            const float v1 = e2m1_value((w >> (8 * h + 4)) & 0xFu) * s;
+            const uint32_t n0 = (w >> (8 * h)) & 0xFu, n1 = (w >> (8 * h + 4)) & 0xFu;
+            const float v0 = (INT ? int4_value(n0) : e2m1_value(n0)) * s;
+            const float v1 = (INT ? int4_value(n1) : e2m1_value(n1)) * s;
             uint32_t b0, b1;
             if (F16) {
                 b0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0);
@@ -561,7 +562,9 @@ __device__ __forceinline__ void dequant32_split(const v4i& codes, float s0, floa
     }
 }
 
-template <bool F16, int BLOCK>
+// INT: both operands on the INT4 grid (products of at most 3 + 5 = 8
+// significant bits in the bf16 variant, 3 + 7 in the f16 one: exact).
+template <bool F16, int BLOCK, bool INT = false>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 {
     extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(scw[r] & 0xFFu, fw) * pw;
                 const float s1 = BLOCK == 16 ? scale_decode_any((scw[r] >> 8) & 0xFFu, fw) * pw : s0;
-                dequant32<F16>(rw[r], s0, s1, o);
+                dequant32<F16, INT>(rw[r], s0, s1, o);
                 uint8_t* dst = &sm.w[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(sca[r] & 0xFFu, fa) * pa;
                 const float s1 = BLOCK == 16 ? scale_decode_any((sca[r] >> 8) & 0xFFu, fa) * pa : s0;
-                dequant32<F16>(ra[r], s0, s1, o);
+                dequant32<F16, INT>(ra[r], s0, s1, o);
                 uint8_t* dst = &sm.a[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -936,13 +939,39 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
     return hipGetLastError();
 }
 
-bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb)
+// INT4 elements carry 3 significant bits (E2M1: 2), so bf16 holds int * s
+// exactly for scale formats with at most 4 mantissa bits.
+static bool int4_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 4; }
+
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, bool int4)
 {
+    if (int4)
+        return (exact_in_f16(fa) && exact_in_f16(fb)) || (int4_exact_in_bf16(fa) && int4_exact_in_bf16(fb));
     return (exact_in_f16(fa) && exact_in_f16(fb)) || (exact_in_bf16(fa) && exact_in_bf16(fb));
+}
+
+// Both operands on the INT4 grid: the exact dequantize path with the integer
+// decode, bf16 when it is exact for both scale formats, else f16.
+template <int BLOCK>
+static hipError_t launch_dq_int4(const GemmLaunch& p, bool f16, hipStream_t s)
+{
+    dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
+    const size_t sh = sizeof(DqSmem);
+    hipError_t e = f16 ? allow_lds(k_gemm_dq<true, BLOCK, true>, sh) : allow_lds(k_gemm_dq<false, BLOCK, true>, sh);
+    if (e != hipSuccess) return e;
+    if (f16) hipLaunchKernelGGL((k_gemm_dq<true, BLOCK, true>), grid, dim3(kGemmThreads), sh, s, p);
+    else hipLaunchKernelGGL((k_gemm_dq<false, BLOCK, true>), grid, dim3(kGemmThreads), sh, s, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 {
+    if (p.elem_int4) {
+        const bool bf16 = int4_exact_in_bf16(p.fa) && int4_exact_in_bf16(p.fb);
+        const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
+        if (!bf16 && !f16) return hipErrorNotSupported;
+        return p.block == 16 ? launch_dq_int4<16>(p, !bf16, s) : launch_dq_int4<32>(p, !bf16, s);
+    }
     const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
     const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);
     if (!f16 && !bf16) return hipErrorNotSupported;

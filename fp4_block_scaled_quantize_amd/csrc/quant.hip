@@ -327,13 +327,14 @@ __device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
     return gmax;
 }
 
-// Tensor scale g = amax_t / RN(6 Smax); 1 when there is no tensor scale or
-// the quotient is zero or not finite.
+// Tensor scale g = amax_t / RN(qmax Smax), qmax the grid's largest
+// magnitude (6 for E2M1, 7 for INT4); 1 when there is no tensor scale or the
+// quotient is zero or not finite.
 template <typename A>
-__device__ __forceinline__ float tensor_scale_of(float am, const A& a)
+__device__ __forceinline__ float tensor_scale_of(float am, const A& a, float qmax)
 {
     if (!a.amax_src) return 1.0f;
-    float den = 6.0f * a.f.smax;
+    float den = qmax * a.f.smax;
     float g = am / den;
     if (!(g > 0.0f) || !(g <= FLT_MAX)) g = 1.0f;
     return g;
@@ -369,9 +370,11 @@ __device__ __forceinline__ float quad_bcast(float v)
 // ROT: the blockwise randomized Hadamard transform is applied to every block
 // right after the loads; block maxima, the tensor maximum and the codes all
 // see the transformed values.
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT>
+// INT: the INT4 element grid (-7..7) instead of E2M1.
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT, bool INT>
 __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArgs a)
 {
+    constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
     constexpr int T = FUSED ? kFThreads : kQThreads;
     constexpr int U = FUSED ? kFUnroll : kQUnroll;
     constexpr int G = BLOCK / 8;                 // lanes per block (2 or 4)
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         if (G == 4) bm[j] = __uint_as_float(dpp_umax_xor2(__float_as_uint(bm[j])));
     }
 
-    float g = 1.0f, d = 6.0f;
+    float g = 1.0f, d = QMAX;
     if (!E8M0 && a.amax_src) {
         float am;
         if (FUSED) {
@@ -426,8 +429,8 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         } else {
             am = tensor_amax(a);
         }
-        g = tensor_scale_of(am, a);
-        d = 6.0f * g;
+        g = tensor_scale_of(am, a, QMAX);
+        d = QMAX * g;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.tensor_scale[0] = g;
             a.tensor_scale[1] = am;
@@ -494,8 +497,12 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                packed |= e2m1_sr(v[k], r16) << (4 * k);
+                packed |= (INT ? int4_sr_code(v[k], r16) : e2m1_sr(v[k], r16)) << (4 * k);
             }
+        } else if (INT) {
+            packed = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) packed |= int4_rtn_code(v[k]) << (4 * k);
         } else {
             packed = FP4_CVT_PK(0u, v[0], v[1], 0);
             packed = FP4_CVT_PK(packed, v[2], v[3], 1);
@@ -506,36 +513,41 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT>
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT, bool INT>
 static void launch_q6(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
 {
     const dim3 t(FUSED ? kFThreads : kQThreads);
     if (strided)
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED, ROT>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED, ROT, INT>), dim3(blocks), t, 0, s, a);
     else
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED, ROT>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED, ROT, INT>), dim3(blocks), t, 0, s, a);
 }
 
-template <typename InT, int BLOCK, bool ROT>
+template <typename InT, int BLOCK, bool ROT, bool INT>
 static void launch_q4(const QArgs& a, bool sr, bool e8, bool fused, bool strided, uint32_t blocks, hipStream_t s)
 {
     if (sr) {
-        if (fused) launch_q6<InT, BLOCK, true, false, true, ROT>(a, strided, blocks, s);
-        else if (e8) launch_q6<InT, BLOCK, true, true, false, ROT>(a, strided, blocks, s);
-        else launch_q6<InT, BLOCK, true, false, false, ROT>(a, strided, blocks, s);
+        if (fused) launch_q6<InT, BLOCK, true, false, true, ROT, INT>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, true, true, false, ROT, INT>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, true, false, false, ROT, INT>(a, strided, blocks, s);
     } else {
-        if (fused) launch_q6<InT, BLOCK, false, false, true, ROT>(a, strided, blocks, s);
-        else if (e8) launch_q6<InT, BLOCK, false, true, false, ROT>(a, strided, blocks, s);
-        else launch_q6<InT, BLOCK, false, false, false, ROT>(a, strided, blocks, s);
+        if (fused) launch_q6<InT, BLOCK, false, false, true, ROT, INT>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, false, true, false, ROT, INT>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, false, false, false, ROT, INT>(a, strided, blocks, s);
     }
 }
 
 template <typename InT, int BLOCK>
-static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, uint32_t blocks,
-                      hipStream_t s)
+static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, bool int4,
+                      uint32_t blocks, hipStream_t s)
 {
-    if (rot) launch_q4<InT, BLOCK, true>(a, sr, e8, fused, strided, blocks, s);
-    else launch_q4<InT, BLOCK, false>(a, sr, e8, fused, strided, blocks, s);
+    if (int4) {
+        if (rot) launch_q4<InT, BLOCK, true, true>(a, sr, e8, fused, strided, blocks, s);
+        else launch_q4<InT, BLOCK, false, true>(a, sr, e8, fused, strided, blocks, s);
+    } else {
+        if (rot) launch_q4<InT, BLOCK, true, false>(a, sr, e8, fused, strided, blocks, s);
+        else launch_q4<InT, BLOCK, false, false>(a, sr, e8, fused, strided, blocks, s);
+    }
 }
 
 // Compute units of a device (cached; every thread computes the same value).
@@ -570,6 +582,7 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.off1 = (uint32_t)(p.offset >> 32);
     a.signs = p.rht_signs;
     const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols, rot = p.rht != 0;
+    const bool int4 = p.elem_int4 != 0;
 
     // A refresh reads the input once when the whole tensor fits the
     // single-pass grid (at most one workgroup per CU, kFUnroll units per
@@ -597,11 +610,11 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         if (blocks == 0) blocks = 1;
     }
     if (p.x_bf16) {
-        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, rot, blocks, s);
-        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, rot, blocks, s);
+        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, rot, int4, blocks, s);
+        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, rot, int4, blocks, s);
     } else {
-        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, rot, blocks, s);
-        else launch_q3<float, 32>(a, sr, e8, fused, strided, rot, blocks, s);
+        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, rot, int4, blocks, s);
+        else launch_q3<float, 32>(a, sr, e8, fused, strided, rot, int4, blocks, s);
     }
     return hipGetLastError();
 }
@@ -654,9 +667,10 @@ __device__ __forceinline__ float lds_elem<float>(const float* t, uint32_t i)
     return t[i];
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0>
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : 5)))) void k_quantize_t(QTArgs a)
 {
+    constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
     constexpr int EPP = 16 / (int)sizeof(InT);   // elements per 16-byte piece
     constexpr int PPR = kTC / EPP;               // pieces per tile row
     constexpr int RPR = kTThreads / PPR;         // tile rows per load round
@@ -684,11 +698,11 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
             v[k] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    float g = 1.0f, d = 6.0f;
+    float g = 1.0f, d = QMAX;
     if (!E8M0 && a.amax_src) {
         const float am = tensor_amax(a);
-        g = tensor_scale_of(am, a);
-        d = 6.0f * g;
+        g = tensor_scale_of(am, a, QMAX);
+        d = QMAX * g;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.tensor_scale[0] = g;
             a.tensor_scale[1] = am;
@@ -744,7 +758,15 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
                 const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
                 uint32_t pk = 0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pk |= e2m1_sr(e[i], (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << (4 * i);
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t r16 = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    pk |= (INT ? int4_sr_code(e[i], r16) : e2m1_sr(e[i], r16)) << (4 * i);
+                }
+                packed[b][k] = pk;
+            } else if (INT) {
+                uint32_t pk = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pk |= int4_rtn_code(e[i]) << (4 * i);
                 packed[b][k] = pk;
             } else {
                 uint32_t pk = FP4_CVT_PK(0u, e[0], e[1], 0);
@@ -811,17 +833,24 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 }
 
-template <typename InT, int BLOCK>
-static void launch_qt2(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
+template <typename InT, int BLOCK, bool INT>
+static void launch_qt3(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
 {
     const dim3 g(blocks), t(kTThreads);
     if (sr) {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT>), g, t, 0, s, a);
     } else {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT>), g, t, 0, s, a);
     }
+}
+
+template <typename InT, int BLOCK>
+static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, uint32_t blocks, hipStream_t s)
+{
+    if (int4) launch_qt3<InT, BLOCK, true>(a, sr, e8, blocks, s);
+    else launch_qt3<InT, BLOCK, false>(a, sr, e8, blocks, s);
 }
 
 // p.rows / p.cols are the output's shape (C, R); x is [R, C] with row stride
@@ -847,18 +876,18 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
     a.key1 = (uint32_t)(p.seed >> 32);
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem_int4 != 0;
     if (a.amax_src && a.refresh && !e8) {
         hipError_t e = launch_amax(p.x, p.x_bf16, a.R, a.C, p.ld, p.amax_src, s);
         if (e != hipSuccess) return e;
     }
     const uint32_t blocks = ntiles ? ntiles : 1;
     if (p.x_bf16) {
-        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, blocks, s);
-        else launch_qt2<uint16_t, 32>(a, sr, e8, blocks, s);
+        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, blocks, s);
+        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, blocks, s);
     } else {
-        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, blocks, s);
-        else launch_qt2<float, 32>(a, sr, e8, blocks, s);
+        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, blocks, s);
+        else launch_qt2<float, 32>(a, sr, e8, int4, blocks, s);
     }
     return hipGetLastError();
 }
@@ -875,7 +904,7 @@ constexpr int kDQUnroll = 4;                 // units per lane, loads issued tog
 // ROT: the inverse blockwise Hadamard transform follows the binary32
 // dequantization (the G units of a block are adjacent lanes and are all in
 // range or all out of it).
-template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT>
+template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT, bool INT>
 __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ tensor_scale, uint32_t nunits,
@@ -903,7 +932,8 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
         float o[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            float t = e2m1_value((w[j] >> (4 * k)) & 0xFu) * s;
+            const uint32_t nib = (w[j] >> (4 * k)) & 0xFu;
+            float t = (INT ? int4_value(nib) : e2m1_value(nib)) * s;
             o[k] = t * g;
         }
         if (ROT) rht_inverse<BLOCK / 8>(o, lane & (BLOCK / 8 - 1), signs);
@@ -923,19 +953,19 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
     }
 }
 
-template <bool OUT_BF16, int BLOCK, bool ROT>
-static void launch_dq3(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
+template <bool OUT_BF16, int BLOCK, bool ROT, bool INT>
+static void launch_dq4(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
     const uint32_t per_block = kDQThreads * kDQUnroll;
     uint32_t blocks = (nunits + per_block - 1) / per_block;
     if (blocks == 0) blocks = 1;
     if (f.is_e8m0)
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true, ROT>), dim3(blocks), dim3(kDQThreads), 0, s,
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true, ROT, INT>), dim3(blocks), dim3(kDQThreads), 0, s,
                            (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
                            p.rht_signs);
     else
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false, ROT>), dim3(blocks), dim3(kDQThreads), 0, s,
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false, ROT, INT>), dim3(blocks), dim3(kDQThreads), 0, s,
                            (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
                            p.rht_signs);
 }
@@ -944,8 +974,13 @@ template <bool OUT_BF16, int BLOCK>
 static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
-    if (p.rht) launch_dq3<OUT_BF16, BLOCK, true>(p, nunits, fd, strided, f, s);
-    else launch_dq3<OUT_BF16, BLOCK, false>(p, nunits, fd, strided, f, s);
+    if (p.elem_int4) {
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, true>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, true>(p, nunits, fd, strided, f, s);
+    } else {
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, false>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, false>(p, nunits, fd, strided, f, s);
+    }
 }
 
 hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s)

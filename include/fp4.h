@@ -108,6 +108,20 @@ typedef enum fp4_transform {
     FP4_TRANSFORM_RHT = 1      /* blockwise randomized Hadamard transform     */
 } fp4_transform;
 
+/* Element grid (quant_prune_distill/574 "Метод": the NV and MX block/scale
+ * schemes paired with an FP or an INT element grid).  Reading for INT4: the
+ * symmetric grid -7..7 as a two's-complement nibble (zero has no sign; the
+ * code 0x8 is never produced); every rule that maps a maximum to the E2M1
+ * maximum 6 maps it to 7 instead (g = amax_t / (7 Smax), u = amax_b /
+ * RN(7 g)); the E8M0 exponent rule is unchanged (amax_b / s in [4, 8), the
+ * MX convention for a sign + 3-bit fixed-point element); nearest rounding
+ * ties to the even integer and saturates at 7; stochastic rounding as for
+ * E2M1 with grid spacing 1. */
+typedef enum fp4_element {
+    FP4_ELEM_E2M1 = 0,
+    FP4_ELEM_INT4 = 1
+} fp4_element;
+
 typedef struct fp4_format {
     int32_t block;            /* 16 or 32 elements per scale                  */
     int32_t scale;            /* fp4_scale_fmt                                */
@@ -115,6 +129,7 @@ typedef struct fp4_format {
     int32_t amax;             /* fp4_amax_policy                              */
     int32_t transform;        /* fp4_transform                                */
     uint32_t transform_signs; /* RHT: bit j negates element j of each block   */
+    int32_t element;          /* fp4_element                                  */
 } fp4_format;
 
 /* A quantized tensor.  q: rows*cols/2 bytes; scales: rows*cols/block bytes;
@@ -230,8 +245,10 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * A = a [M, K] and W = b [N, K] both blocked along K (C = A W^T)
  * (ue5m3-fp4-pretraining "Что сделали": the linear layers run in FP4;
  * quant_prune_distill/574 "Выводы": weight + activation FP4 for the
- * compute-bound regime).  Both operands must use the same block size and
- * the same transform (kind and signs; UNSUPPORTED otherwise).
+ * compute-bound regime).  Both operands must use the same block size, the
+ * same element grid and the same transform (kind and signs; UNSUPPORTED
+ * otherwise).  INT4 operands run on the exact dequantize path (bf16 when
+ * int * s fits it exactly for both scale formats, else f16).
  * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within
@@ -249,8 +266,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * weight-only NVFP4, memory-bound small-batch generation).
  * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
  * 1 <= M <= 16; K % 256 == 0; x 16-byte aligned, ldx % 8 == 0, ldy >= N;
- * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB and no
- * transform on w (UNSUPPORTED otherwise).
+ * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB, E2M1
+ * elements and no transform on w (UNSUPPORTED otherwise).
  */
 FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
                        int64_t ldy, void* stream);

@@ -132,3 +132,18 @@ def test_transform_checks():
     tt = _tensor(rows=64, cols=32)
     tt.fmt.transform = 1
     assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -2
+
+
+def test_element_checks():
+    L = fq.lib()
+    assert L.fp4_version() >= 102
+    t = _tensor()
+    t.fmt.element = 5
+    assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -1
+    a = _tensor(rows=8, cols=256)
+    b = _tensor(rows=8, cols=256)
+    a.fmt.element = 1
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2     # mixed grids
+    w = _tensor(rows=8, cols=256)
+    w.fmt.element = 1
+    assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
