@@ -18,7 +18,7 @@ agrees on the maximum.
 Further legs reported in "legs": stochastic rounding with delayed amax over
 200 successive 8192x8192 gradients, the same gradients quantized column-wise
 (the backward-pass operands), dequantize, quantize with the blockwise
-randomized Hadamard transform, the block-scaled GEMM on the
+randomized Hadamard transform, the INT4 element grid (quantize and GEMM), the block-scaled GEMM on the
 Llama-2 7B linear shapes, and the weight-only GEMM at Qwen-2.5 decode
 shapes.  "roofline" is the dominant kernel of the step (the single-pass
 E4M3 block-16 current-amax quantize kernel: four of the five calls) timed
@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,srt,dequant,rht,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,gemm,wo", help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 64 MiB device copy three times (calibrates HBM byte counters)")
@@ -282,6 +282,46 @@ def leg_gemm(torch, fq, inputs):
     return res
 
 
+def leg_int4(torch, fq, inputs, xs):
+    """The INT4 element grid: quantize throughput on the sweep tensor
+    (NVINT4 = E4M3 block 16 with current amax, MXINT4 = E8M0 block 32) and
+    the GEMM at the Llama-2 7B up-projection shape on the exact dequantize
+    path (bf16 matrix cores)."""
+    rows, cols = xs[0].shape
+    res = {}
+    for name, (fmt, block, pol) in {"nvint4": ("e4m3", 16, "current"), "mxint4": ("e8m0", 32, "none")}.items():
+        outs = [fq.QTensor.empty(rows, cols, block, fmt, amax=pol, element="int4") for _ in xs]
+        st = fq.AmaxState(1) if pol == "current" else None
+
+        def rec(_):
+            for j in range(len(xs)):
+                fq.fp4_quantize(xs[j], block, fmt, amax=pol, state=st, out=outs[j], element="int4")
+        gs = GraphSet(torch, 1, rec)
+        ms = time_graphs(torch, gs, 20, 3) / len(xs)
+        algo = quant_bytes(rows, cols, block)
+        res[f"{name}_quantize"] = {"us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gs, outs
+        m, n, k = 8192, 11008, 4096
+        a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
+        w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_up"], torch.bfloat16)
+        qa = fq.fp4_quantize(a, block, fmt, amax=pol, element="int4")
+        qw = fq.fp4_quantize(w, block, fmt, amax=pol, element="int4")
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+        def rec_g(_):
+            fq.fp4_gemm(qa, qw, out=c)
+        gs = GraphSet(torch, 1, rec_g)
+        ms = time_graphs(torch, gs, 10, 2)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        res[f"{name}_gemm_up"] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
+                                  "frac_bf16_peak": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        del a, w, qa, qw, c, gs
+    res["workload"] = ("INT4 grid: 4096x4096 bf16 sweep tensor quantized NVINT4 (E4M3 B16, current amax) and MXINT4 "
+                       "(E8M0 B32); Llama-2 7B up projection 8192x4096 @ 11008x4096 on the exact dequantize path")
+    return res
+
+
 def leg_wo(torch, fq, inputs):
     """Weight-only NVFP4 GEMM, W [N, K] = [18944, 3584] and [3584, 18944],
     M in {1, 8, 16}; 12 weight copies rotate (>= 450 MB) so weights stream
@@ -389,6 +429,9 @@ def main():
         legs["dequant"] = leg_dequant(torch, fq, xs[:8])
     if "rht" in want:
         legs["rht"] = leg_rht(torch, fq, xs[:8])
+    if "int4" in want:
+        legs["int4"] = leg_int4(torch, fq, inputs, xs[:8])
+        torch.cuda.empty_cache()
     del outs
     if "sr" in want:
         legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)

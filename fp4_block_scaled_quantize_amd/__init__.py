@@ -201,7 +201,8 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
 
 def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
                             amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
-                            out: QTensor | None = None, stream=None, element: str = "e2m1") -> QTensor:
+                            out: QTensor | None = None, stream=None, element: str = "e2m1",
+                            rht_signs: int | None = None) -> QTensor:
     """Column-wise quantization of a 2-D fp32/bf16 CUDA tensor x [R, C]: the
     result is the quantized x^T [C, R] (blocks run down the columns of x)."""
     if x.dim() != 2 or x.stride(1) != 1:
@@ -212,6 +213,8 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
     else:
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.element = element
+    if rht_signs is not None:
+        out.transform, out.rht_signs = "rht", rht_signs & 0xFFFFFFFF
     if amax != "none" and state is None:
         if amax == "delayed":
             raise ValueError("the delayed amax policy needs an AmaxState")

@@ -203,7 +203,6 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     // x is [out->cols, out->rows]: its rows are the blocked dimension
-    if (out->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;
     if (out->rows % 8) return FP4_ERR_SHAPE;
     if (out->rows * out->cols != 0) {
         if (ld_x < out->rows) return FP4_ERR_SHAPE;
@@ -236,8 +235,8 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     p.seed = seed;
     p.offset = offset;
     p.fmt = f;
-    p.rht = 0;
-    p.rht_signs = 0;
+    p.rht = out->fmt.transform == FP4_TRANSFORM_RHT;
+    p.rht_signs = out->fmt.transform_signs;
     p.elem_int4 = out->fmt.element == FP4_ELEM_INT4;
     st = hip_status(launch_quantize_t(p, s));
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;

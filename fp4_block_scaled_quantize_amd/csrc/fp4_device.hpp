@@ -267,6 +267,29 @@ __device__ __forceinline__ void rht_inverse(float v[8], uint32_t sub, uint32_t s
     }
 }
 
+// The same transform on a block held whole by one lane (column-wise
+// quantization): v[0 .. B-1], stages h = 1, 2, ..., B/2 in order.
+template <int B>
+__device__ __forceinline__ void rht_forward_lane(float v[B], uint32_t signs)
+{
+    static_assert(B == 16 || B == 32, "blocks of 16 or 32");
+#pragma unroll
+    for (int k = 0; k < B; ++k) v[k] = ((signs >> k) & 1u) ? -v[k] : v[k];
+#pragma unroll
+    for (int h = 1; h < B; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            if (i & h) continue;
+            const float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+    const float c = B == 16 ? kRhtNorm16 : kRhtNorm32;
+#pragma unroll
+    for (int k = 0; k < B; ++k) v[k] = v[k] * c;
+}
+
 // max |v| of 8 binary32 values as bits (non-negative floats order like
 // their bit patterns)
 __device__ __forceinline__ uint32_t absmax_bits8(const float v[8])

@@ -652,6 +652,7 @@ struct QTArgs {
     int32_t refresh;
     ScaleFmt f;
     uint32_t key0, key1, off0, off1;
+    uint32_t signs;              // Hadamard transform sign mask (ROT kernels)
 };
 
 template <typename InT>
@@ -667,14 +668,86 @@ __device__ __forceinline__ float lds_elem<float>(const float* t, uint32_t i)
     return t[i];
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT>
+// Coalesced 16-byte loads of the tile at (r0, c0) into registers (zeros past
+// the edges of x), then their store to the LDS tile.
+template <typename InT>
+struct TileLoad {
+    static constexpr int EPP = 16 / (int)sizeof(InT);   // elements per 16-byte piece
+    static constexpr int PPR = kTC / EPP;               // pieces per tile row
+    static constexpr int RPR = kTThreads / PPR;         // tile rows per load round
+    static constexpr int NLD = kTR / RPR;               // 16-byte loads per thread
+    u32x4 v[NLD];
+    __device__ __forceinline__ void load(const QTArgs& a, uint32_t r0, uint32_t c0)
+    {
+        const uint32_t piece = threadIdx.x % PPR, prow = threadIdx.x / PPR;
+        const uint32_t gc = c0 + piece * EPP;
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const uint32_t gr = r0 + prow + k * RPR;
+            if (gr < a.R && gc < a.C)
+                v[k] = __builtin_nontemporal_load(
+                    (const u32x4*)((const InT*)a.x + (uint64_t)gr * (uint64_t)a.ld + gc));
+            else
+                v[k] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(InT* tile) const
+    {
+        const uint32_t piece = threadIdx.x % PPR, prow = threadIdx.x / PPR;
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) *(u32x4*)&tile[(prow + k * RPR) * kTC + piece * EPP] = v[k];
+    }
+};
+
+// Tensor maximum of x transformed blockwise down its columns (the refresh
+// of a transformed column-wise call): exactly kAmaxParts workgroups take the
+// tiles in a grid stride, stage each through LDS as k_quantize_t does, and
+// lane l transforms the blocks of column l; one partial maximum per
+// workgroup, reduced by the quantize kernel.
+template <typename InT, int BLOCK>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : 4))) void k_amax_t(
+    QTArgs a, uint32_t ntiles)
+{
+    constexpr int RPW = kTR / (kTThreads / 64);
+    constexpr int NB = RPW / BLOCK;
+    __shared__ __align__(16) InT tile[kTR * kTC];
+    const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t m = 0;
+    for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint32_t tc = t / a.ntr, tr = t - tc * a.ntr;
+        TileLoad<InT> ld;
+        ld.load(a, tr * kTR, tc * kTC);
+        __syncthreads();                         // the previous tile has been read
+        ld.store(tile);
+        __syncthreads();
+        const InT* tw = tile + w * RPW * kTC + lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float val[BLOCK];
+#pragma unroll
+            for (int j = 0; j < BLOCK; ++j) val[j] = lds_elem<InT>(tw, (b * BLOCK + j) * kTC);
+            rht_forward_lane<BLOCK>(val, a.signs);
+#pragma unroll
+            for (int j = 0; j < BLOCK; ++j) {
+                const uint32_t u = __float_as_uint(val[j]) & 0x7FFFFFFFu;
+                m = m > u ? m : u;
+            }
+        }
+    }
+    m = wave_umax(m);
+    __shared__ uint32_t wmax[kTThreads / 64];
+    if (lane == 0) wmax[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < kTThreads / 64; ++i) m = m > wmax[i] ? m : wmax[i];
+        a.amax_src->partial[blockIdx.x] = __uint_as_float(m);
+    }
+}
+
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT, bool ROT>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : 5)))) void k_quantize_t(QTArgs a)
 {
     constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
-    constexpr int EPP = 16 / (int)sizeof(InT);   // elements per 16-byte piece
-    constexpr int PPR = kTC / EPP;               // pieces per tile row
-    constexpr int RPR = kTThreads / PPR;         // tile rows per load round
-    constexpr int NLD = kTR / RPR;               // 16-byte loads per thread
     constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
     constexpr int NB = RPW / BLOCK;              // blocks per lane
     __shared__ __align__(16) InT tile[kTR * kTC];
@@ -686,17 +759,8 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     const uint32_t tc = t / a.ntr, tr = t - tc * a.ntr;
     const uint32_t r0 = tr * kTR, c0 = tc * kTC;
 
-    const uint32_t piece = threadIdx.x % PPR, prow = threadIdx.x / PPR;
-    const uint32_t gc = c0 + piece * EPP;
-    u32x4 v[NLD];
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-        const uint32_t gr = r0 + prow + k * RPR;
-        if (gr < a.R && gc < a.C)
-            v[k] = __builtin_nontemporal_load((const u32x4*)((const InT*)a.x + (uint64_t)gr * (uint64_t)a.ld + gc));
-        else
-            v[k] = u32x4{0u, 0u, 0u, 0u};
-    }
+    TileLoad<InT> ld;
+    ld.load(a, r0, c0);
 
     float g = 1.0f, d = QMAX;
     if (!E8M0 && a.amax_src) {
@@ -713,8 +777,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         a.tensor_scale[1] = 0.0f;
     }
 
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) *(u32x4*)&tile[(prow + k * RPR) * kTC + piece * EPP] = v[k];
+    ld.store(tile);
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -733,8 +796,10 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         float val[BLOCK];
         uint32_t m = 0;
 #pragma unroll
+        for (int j = 0; j < BLOCK; ++j) val[j] = lds_elem<InT>(tw, (b * BLOCK + j) * kTC);
+        if (ROT) rht_forward_lane<BLOCK>(val, a.signs);
+#pragma unroll
         for (int j = 0; j < BLOCK; ++j) {
-            val[j] = lds_elem<InT>(tw, (b * BLOCK + j) * kTC);
             const uint32_t u = __float_as_uint(val[j]) & 0x7FFFFFFFu;
             m = m > u ? m : u;
         }
@@ -833,28 +898,42 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 }
 
-template <typename InT, int BLOCK, bool INT>
+template <typename InT, int BLOCK, bool INT, bool ROT>
 static void launch_qt3(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
 {
     const dim3 g(blocks), t(kTThreads);
     if (sr) {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT, ROT>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT, ROT>), g, t, 0, s, a);
     } else {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT, ROT>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT, ROT>), g, t, 0, s, a);
     }
 }
 
 template <typename InT, int BLOCK>
-static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, uint32_t blocks, hipStream_t s)
+static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, bool rot, uint32_t blocks, hipStream_t s)
 {
-    if (int4) launch_qt3<InT, BLOCK, true>(a, sr, e8, blocks, s);
-    else launch_qt3<InT, BLOCK, false>(a, sr, e8, blocks, s);
+    if (int4) {
+        if (rot) launch_qt3<InT, BLOCK, true, true>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, true, false>(a, sr, e8, blocks, s);
+    } else {
+        if (rot) launch_qt3<InT, BLOCK, false, true>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, false, false>(a, sr, e8, blocks, s);
+    }
+}
+
+template <typename InT>
+static void launch_amax_t(const QTArgs& a, int block, uint32_t ntiles, hipStream_t s)
+{
+    const dim3 g(kAmaxParts), t(kTThreads);
+    if (block == 16) hipLaunchKernelGGL((k_amax_t<InT, 16>), g, t, 0, s, a, ntiles);
+    else hipLaunchKernelGGL((k_amax_t<InT, 32>), g, t, 0, s, a, ntiles);
 }
 
 // p.rows / p.cols are the output's shape (C, R); x is [R, C] with row stride
-// p.ld.  A refresh takes the amax kernel first (x is read twice).
+// p.ld.  A refresh takes an amax kernel first (x is read twice): the row-wise
+// one, or the tiled one when the blocks are transformed.
 hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
 {
     QTArgs a;
@@ -876,18 +955,27 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
     a.key1 = (uint32_t)(p.seed >> 32);
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem_int4 != 0;
+    a.signs = p.rht_signs;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem_int4 != 0, rot = p.rht != 0;
     if (a.amax_src && a.refresh && !e8) {
-        hipError_t e = launch_amax(p.x, p.x_bf16, a.R, a.C, p.ld, p.amax_src, s);
-        if (e != hipSuccess) return e;
+        if (rot) {
+            // the maximum of the column-transformed tensor
+            if (p.x_bf16) launch_amax_t<uint16_t>(a, p.block, ntiles, s);
+            else launch_amax_t<float>(a, p.block, ntiles, s);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        } else {
+            hipError_t e = launch_amax(p.x, p.x_bf16, a.R, a.C, p.ld, p.amax_src, s);
+            if (e != hipSuccess) return e;
+        }
     }
     const uint32_t blocks = ntiles ? ntiles : 1;
     if (p.x_bf16) {
-        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, blocks, s);
-        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, blocks, s);
+        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, rot, blocks, s);
+        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, rot, blocks, s);
     } else {
-        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, blocks, s);
-        else launch_qt2<float, 32>(a, sr, e8, int4, blocks, s);
+        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, rot, blocks, s);
+        else launch_qt2<float, 32>(a, sr, e8, int4, rot, blocks, s);
     }
     return hipGetLastError();
 }

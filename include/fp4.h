@@ -222,8 +222,10 @@ FP4_API fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp
  * x: device, 16-byte aligned, ld_x * sizeof(elem) a multiple of 16, ld_x >=
  * out->rows; out->rows % 8 == 0; out->cols % block == 0; out->q 16-byte
  * aligned.  A refresh of the tensor maximum reads x twice (an amax pass,
- * then the quantize pass).  Errors as fp4_quantize; a transform other than
- * FP4_TRANSFORM_NONE is UNSUPPORTED here.
+ * then the quantize pass).  With out->fmt.transform = FP4_TRANSFORM_RHT the
+ * transform runs down the columns of x (over each block of x^T), and a
+ * refresh takes the maximum of the transformed tensor.  Errors as
+ * fp4_quantize.
  */
 FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
                                    fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);

@@ -423,7 +423,8 @@ def gemm_check(c_out: np.ndarray, c_ref: np.ndarray, tol: np.ndarray) -> np.ndar
 # --------------------------------------------------------------------------
 def quantize_transposed_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *,
                                state: AmaxState | None = None, stochastic: bool = False, seed: int = 0,
-                               offset: int = 0, nthreads: int = 1):
+                               offset: int = 0, nthreads: int = 1, rht_signs: int | None = None,
+                               elem: str = "e2m1"):
     """The whole quantize call applied to the transpose of x.
 
     x: [R, C]; the result describes x^T: codes [C, R/2], scales [C, R/block],
@@ -434,4 +435,4 @@ def quantize_transposed_tensor(x: np.ndarray, block: int, fmt: str, policy: str,
     operand the GEMM consumes.  Returns (q, scales, g, amax_used)."""
     xt = np.ascontiguousarray(np.asarray(x).T)
     return quantize_tensor(xt, block, fmt, policy, state=state, stochastic=stochastic, seed=seed,
-                           offset=offset, nthreads=nthreads)
+                           offset=offset, nthreads=nthreads, rht_signs=rht_signs, elem=elem)

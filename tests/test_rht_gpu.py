@@ -177,7 +177,49 @@ def test_rht_gemm_same_signs(fmt, block):
     with pytest.raises(fq.Fp4Error) as e:
         fq.fp4_gemm(qa, qw2)
     assert e.value.status == -2
-    with pytest.raises(fq.Fp4Error) as e:
-        fq.fp4_quantize_transposed(to_device(w), block, fmt, amax=pol,
-                                   out=fq.QTensor.empty(k, n, block, fmt, transform="rht", rht_signs=1))
-    assert e.value.status == -2
+
+
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e8m0", 32), ("ue5m3", 32)])
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rht_transposed_parity(fmt, block, rounding, dtype):
+    """Column-wise quantization with the transform down the columns of x;
+    a current-amax refresh takes the maximum of the transformed tensor
+    (tiled amax kernel, ragged tiles in both directions)."""
+    x = _like(352, 136, 77, dtype)
+    pol = _policy(fmt)
+    st = fq.AmaxState(1) if pol == "current" else None
+    signs = SIGNS[2]
+    qt = fq.fp4_quantize_transposed(to_device(x), block, fmt, rounding=rounding, amax=pol, state=st, seed=5,
+                                    offset=6, rht_signs=signs)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, block, fmt, pol, stochastic=(rounding == "stochastic"),
+                                                   seed=5, offset=6, rht_signs=signs, nthreads=8)
+    assert_bytes_equal(host(qt.scales), s, "rht T scales")
+    assert_bytes_equal(host(qt.q), q, "rht T codes")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), "rht T tensor_scale")
+    # dequantizing the transposed operand inverts the transform along its rows
+    y = fq.fp4_dequantize(qt, torch.float32)
+    torch.cuda.synchronize()
+    assert_bytes_equal(f32_bits(host(y)), f32_bits(oracle.dequantize_rht(q, s, g, block, fmt, signs)), "rht T dequant")
+
+
+def test_rht_transposed_grads_sampled():
+    """8192x8192 gradients, column-wise, transform + SR + delayed amax (a
+    refresh on the first call): tensor scale over the whole transformed
+    tensor, sampled output rows."""
+    x = inputs.grads(1)
+    signs = SIGNS[3]
+    st = fq.AmaxState(50)
+    qt = fq.fp4_quantize_transposed(to_device(x), 16, "e4m3", rounding="stochastic", amax="delayed", state=st,
+                                    seed=0x5EED, offset=1, rht_signs=signs)
+    torch.cuda.synchronize()
+    xt = np.ascontiguousarray(x.T)
+    y = oracle.rht_forward(xt, 16, signs)
+    a = oracle.amax(y)
+    g = oracle.tensor_scale(a, "e4m3")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), "rht T grads tensor_scale")
+    for c in (0, 63, 64, 4097, 8191):
+        q, s = oracle.quantize(y, 16, "e4m3", g, stochastic=True, seed=0x5EED, offset=1, rows=(c, c + 1))
+        assert_bytes_equal(host(qt.q[c:c + 1]), q, f"rht T grads col {c} codes")
+        assert_bytes_equal(host(qt.scales[c:c + 1]), s, f"rht T grads col {c} scales")
