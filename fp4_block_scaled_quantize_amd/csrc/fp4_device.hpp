@@ -153,9 +153,12 @@ __device__ __forceinline__ uint32_t int4_nibble(float v, float mag)
     return (f_bits(v) >> 31) ? ((16u - m) & 15u) : m;
 }
 
+// Clamping to the integer bounds commutes with the nearest-even rounding, so
+// the signed integer of RN(clamp(v, -7, 7)), masked to 4 bits, is the
+// two's-complement code (rint(-0.4) = -0 converts to 0: zero has no sign).
 __device__ __forceinline__ uint32_t int4_rtn_code(float v)
 {
-    return int4_nibble(v, __builtin_fminf(__builtin_rintf(__builtin_fabsf(v)), 7.0f));
+    return (uint32_t)(int32_t)__builtin_rintf(__builtin_amdgcn_fmed3f(v, -7.0f, 7.0f)) & 15u;
 }
 
 __device__ __forceinline__ uint32_t int4_sr_code(float v, uint32_t r16)
