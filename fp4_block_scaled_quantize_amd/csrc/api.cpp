@@ -316,7 +316,6 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (!x || !y) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
-    if (w->fmt.element != FP4_ELEM_E2M1) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     // the kernel addresses W and x with 32-bit byte/element offsets
@@ -328,6 +327,7 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     p.x = x; p.ldx = ldx; p.m = m;
     p.qw = w->q; p.sw = w->scales; p.gw = w->tensor_scale;
     p.n = w->rows; p.k = w->cols;
+    p.elem_int4 = w->fmt.element == FP4_ELEM_INT4;
     p.block = w->fmt.block;
     p.fw = fw;
     p.y = y; p.ldy = ldy;

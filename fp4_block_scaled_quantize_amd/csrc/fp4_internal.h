@@ -101,6 +101,7 @@ struct WoGemmLaunch {
     int32_t block;
     ScaleFmtHost fw;
     uint16_t* y; int64_t ldy;
+    int32_t elem_int4;         // weights on the INT4 grid
 };
 
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s);

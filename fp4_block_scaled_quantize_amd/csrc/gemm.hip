@@ -1037,11 +1037,25 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 //  POW2 (E8M0 scales): v_cvt_scalef32_pk_bf16_fp4 with s does everything;
 //  otherwise: convert with scale 1 to fp32, multiply by s (exact: at most
 //  9 significant bits), keep the top half (exact when the value fits bf16).
-template <bool POW2>
+// Elements 2b and 2b + 1 of a dword of codes as binary32: the hardware
+// E2M1 conversion (scale 1), or for INT4 the sign-extended nibbles.
+template <bool INT>
+__device__ __forceinline__ v2f elem_pair_f32(uint32_t w, int b)
+{
+    if (INT)
+        return v2f{(float)((int32_t)(w << (28 - 8 * b)) >> 28), (float)((int32_t)(w << (24 - 8 * b)) >> 28)};
+    return b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+         : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+         : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                  : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+}
+
+// INT: INT4 elements (never POW2: the multiply by s is exact for E8M0 too).
+template <bool POW2, bool INT = false>
 __device__ __forceinline__ v4i dq8_bf16(uint32_t w, float s)
 {
     v4i r;
-    if (POW2) {
+    if (POW2 && !INT) {
         r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
         r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
         r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
@@ -1049,10 +1063,7 @@ __device__ __forceinline__ v4i dq8_bf16(uint32_t w, float s)
     } else {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            v2f f = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
-                  : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
-                  : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
-                           : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+            const v2f f = elem_pair_f32<INT>(w, b);
             const uint32_t lo = __float_as_uint(f[0] * s), hi = __float_as_uint(f[1] * s);
             r[b] = (int)__builtin_amdgcn_perm(hi, lo, 0x07060302u);     // {hi[31:16], lo[31:16]}
         }
@@ -1060,15 +1071,14 @@ __device__ __forceinline__ v4i dq8_bf16(uint32_t w, float s)
     return r;
 }
 
-// E1M6 products need 9 significant bits: split v = hi + lo, both exact bf16.
+// Products wider than bf16 (E1M6 with E2M1: 9 significant bits; INT4 with
+// 5- or 6-bit mantissas: up to 10): split v = hi + lo, both exact bf16.
+template <bool INT = false>
 __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i& lo)
 {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        v2f f = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
-              : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
-              : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
-                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        const v2f f = elem_pair_f32<INT>(w, b);
         const float v0 = f[0] * s, v1 = f[1] * s;
         const uint32_t h0 = __float_as_uint(v0) & 0xFFFF0000u, h1 = __float_as_uint(v1) & 0xFFFF0000u;
         const float l0 = v0 - __uint_as_float(h0), l1 = v1 - __uint_as_float(h1);
@@ -1099,7 +1109,7 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2>
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, bool INT = false>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
     using S = WoSlot<RG, XQ>;
@@ -1204,13 +1214,13 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
                 const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
                 if (SPLIT) {
                     v4i hi, lo;
-                    dq8_bf16_split((uint32_t)wv[t], st, hi, lo);
+                    dq8_bf16_split<INT>((uint32_t)wv[t], st, hi, lo);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
                 } else {
-                    const v4i wt = dq8_bf16<POW2>((uint32_t)wv[t], st);
+                    const v4i wt = dq8_bf16<POW2, INT>((uint32_t)wv[t], st);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
                 }
@@ -1269,24 +1279,34 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     }
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2>
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, bool INT = false>
 static hipError_t launch_wo_k(const WoGemmLaunch& p, hipStream_t s)
 {
     constexpr size_t sh = (size_t)NW * D * WoSlot<RG, XQ>::Bytes;   // the ring, later the partial tiles
     static_assert(sh >= sizeof(float) * NW * RG * 256, "partial tiles fit the ring");
     static_assert(sh + sizeof(float) * 256 <= 160 * 1024, "LDS");
     if (sh > 64 * 1024) {
-        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2>, sh);
+        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, INT>, sh);
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
-    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2>), grid, block, sh, s, p);
+    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, INT>), grid, block, sh, s, p);
     return hipGetLastError();
 }
 
 template <int NW, int D, int RG, int XQ>
 static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
 {
+    if (p.elem_int4) {
+        // INT4 x s is exact in bf16 for at most 4 mantissa bits, else split
+        const bool isplit = !int4_exact_in_bf16(p.fw);
+        if (p.block == 16) {
+            if (isplit) return launch_wo_k<NW, D, RG, XQ, 16, true, false, true>(p, s);
+            return launch_wo_k<NW, D, RG, XQ, 16, false, false, true>(p, s);
+        }
+        if (isplit) return launch_wo_k<NW, D, RG, XQ, 32, true, false, true>(p, s);
+        return launch_wo_k<NW, D, RG, XQ, 32, false, false, true>(p, s);
+    }
     const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
     if (p.block == 16) {
         if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false>(p, s);

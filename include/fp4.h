@@ -268,8 +268,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * weight-only NVFP4, memory-bound small-batch generation).
  * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
  * 1 <= M <= 16; K % 256 == 0; x 16-byte aligned, ldx % 8 == 0, ldy >= N;
- * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB, E2M1
- * elements and no transform on w (UNSUPPORTED otherwise).
+ * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB and no
+ * transform on w (UNSUPPORTED otherwise).  E2M1 or INT4 weights.
  */
 FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
                        int64_t ldy, void* stream);

@@ -146,4 +146,4 @@ def test_element_checks():
     assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2     # mixed grids
     w = _tensor(rows=8, cols=256)
     w.fmt.element = 1
-    assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
+    assert L.fp4_wo_gemm(FAKE, 256, 0, ctypes.byref(w), FAKE, 8, None) == -2      # INT4 weights accepted: M = 0 decides

@@ -152,13 +152,33 @@ def test_int4_gemm(fmt, block, m, n, k):
     assert ok.all(), f"int4 gemm {fmt}: {int((~ok).sum())} of {ok.size} outputs out of tolerance"
 
 
-def test_int4_mixed_and_weight_only_rejected():
+def test_int4_mixed_grids_rejected():
     x = to_device(_like(64, 256, 53, "f32"))
     q4 = fq.fp4_quantize(x, 16, "e4m3", element="int4")
     qf = fq.fp4_quantize(x, 16, "e4m3")
     with pytest.raises(fq.Fp4Error) as e:
         fq.fp4_gemm(q4, qf)
     assert e.value.status == -2
-    with pytest.raises(fq.Fp4Error) as e:
-        fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q4)
-    assert e.value.status == -2
+
+
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e8m0", 32), ("e1m6", 16), ("e2m5", 32), ("ue5m3", 16)])
+@pytest.mark.parametrize("n", [48, 8200])
+def test_int4_weight_only_gemm(fmt, block, n):
+    """Weight-only GEMM with INT4 weights: bf16 dequant in registers (split
+    into two exact bf16 terms where int * s needs more than 8 bits), every M
+    class, few and many row groups."""
+    k = 512
+    w = _like(n, k, 54, "bf16")
+    pol = _policy(fmt)
+    qw = fq.fp4_quantize(to_device(w), block, fmt, amax=pol, element="int4")
+    ow = oracle.quantize_tensor(w, block, fmt, pol, elem="int4")
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qw.q), ow[0], "W codes")
+    w_hat = oracle.dequantize_f64(ow[0], ow[1], ow[2], block, fmt, elem="int4")
+    for m in (1, 3, 8, 16):
+        xb = inputs.f32_to_bf16_bits((np.random.default_rng(55 + m).standard_normal((m, k))).astype(np.float32))
+        y = fq.fp4_wo_gemm(to_device(xb), qw)
+        torch.cuda.synchronize()
+        cref, tol = oracle.gemm_ref(inputs.bf16_bits_to_f32(xb).astype(np.float64), w_hat)
+        ok = oracle.gemm_check(y.float().cpu().numpy().astype(np.float64), cref, tol)
+        assert ok.all(), f"int4 wo {fmt} n={n} m={m}: {int((~ok).sum())} outputs out of tolerance"
