@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "d986e2fba5c566f01c750dbce0d97ded1fead302860180c037b4834352f80718",
-    "read_bytes": 33787456,
-    "write_bytes": 9453760,
+    "sha256": "8c2abd88395492a8c5d3170217f86dfe366d3be4ec41623cf3ab788527d57acc",
+    "read_bytes": 33784896,
+    "write_bytes": 9453761,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
