@@ -5,7 +5,7 @@ runs in the HIP kernels behind the C ABI of include/fp4.h.  torch provides
 device memory and the current stream.  There is no fallback: if libfp4.so is
 missing or fails to load, every call raises.
 
-Names follow the C ABI: fp4_quantize, fp4_quantize_transposed, fp4_dequantize, fp4_gemm, fp4_wo_gemm,
+Names follow the C ABI: fp4_quantize, fp4_quantize_transposed, fp4_quantize_both, fp4_dequantize, fp4_gemm, fp4_wo_gemm,
 plus the amax state (per-tensor maximum refreshed every N calls,
 ue5m3-fp4-pretraining "Что сделали").
 """
@@ -70,6 +70,7 @@ def lib():
         "fp4_amax_state_set": (i32, [vp, u64, ctypes.c_float]),
         "fp4_quantize": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
         "fp4_quantize_transposed": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
+        "fp4_quantize_both": (i32, [vp, i32, i64, T, T, vp, u64, u64, vp]),
         "fp4_dequantize": (i32, [T, vp, i32, i64, vp]),
         "fp4_gemm": (i32, [T, T, vp, i64, vp]),
         "fp4_wo_gemm": (i32, [vp, i64, i64, T, vp, i64, vp]),
@@ -227,6 +228,33 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
     return out
 
 
+def fp4_quantize_both(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
+                      amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
+                      out: tuple | None = None, stream=None, element: str = "e2m1"):
+    """Row-wise and column-wise quantization of x [R, C] from one read:
+    returns (rowwise [R, C], colwise [C, R]) QTensors, each identical to the
+    corresponding single-orientation call."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    r, c = x.shape
+    if out is None:
+        out = (QTensor.empty(r, c, block, scale, rounding, amax, device=x.device, element=element),
+               QTensor.empty(c, r, block, scale, rounding, amax, device=x.device, element=element))
+    qr, qc = out
+    for t in (qr, qc):
+        t.block, t.scale, t.rounding, t.amax, t.element = block, scale, rounding, amax, element
+    if amax != "none" and state is None:
+        if amax == "delayed":
+            raise ValueError("the delayed amax policy needs an AmaxState")
+        state = AmaxState(1)
+    qr._state = qc._state = state
+    tr, tcw = qr.c(), qc.c()
+    st = lib().fp4_quantize_both(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tr), ctypes.byref(tcw),
+                                 state.handle if state is not None else None, seed, offset, _stream(stream))
+    _check(st, "fp4_quantize_both")
+    return qr, qc
+
+
 def fp4_dequantize(t: QTensor, dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.q.device)
@@ -259,5 +287,5 @@ def fp4_wo_gemm(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None, st
     return out
 
 
-__all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_dequantize", "fp4_gemm", "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error",
+__all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_quantize_both", "fp4_dequantize", "fp4_gemm", "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error",
            "SCALE_FORMATS", "lib", "status_string", "LIB_PATH"]

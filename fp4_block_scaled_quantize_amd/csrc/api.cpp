@@ -243,6 +243,65 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     return st;
 }
 
+fp4_status fp4_quantize_both(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* rowwise,
+                             fp4_tensor* colwise, fp4_amax_state* state, uint64_t seed, uint64_t offset,
+                             void* stream)
+{
+    ScaleFmtHost f, fc;
+    fp4_status st = check_tensor(rowwise, &f);
+    if (st != FP4_OK) return st;
+    st = check_tensor(colwise, &fc);
+    if (st != FP4_OK) return st;
+    if (rowwise->rows != colwise->cols || rowwise->cols != colwise->rows) return FP4_ERR_SHAPE;
+    const fp4_format &fr = rowwise->fmt, &fl = colwise->fmt;
+    if (fr.block != fl.block || fr.scale != fl.scale || fr.rounding != fl.rounding || fr.amax != fl.amax ||
+        fr.element != fl.element)
+        return FP4_ERR_UNSUPPORTED;
+    // a transform would run along different axes, with different maxima
+    if (fr.transform != FP4_TRANSFORM_NONE || fl.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;
+    if (!x && rowwise->rows * rowwise->cols != 0) return FP4_ERR_INVALID_ARG;
+    if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
+    const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
+    if (rowwise->rows * rowwise->cols != 0) {
+        if (ld_x < rowwise->cols) return FP4_ERR_SHAPE;
+        if (!aligned16(x) || (ld_x * esz) % 16 || !aligned16(colwise->q)) return FP4_ERR_ALIGN;
+    }
+    const int32_t pol = fr.amax;
+    if (f.is_e8m0 && pol != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
+    if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    AmaxDev* src = nullptr;
+    bool refresh = false;
+    if (pol != FP4_AMAX_NONE) {
+        refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
+        src = state->dev;
+    }
+    QuantLaunch p;
+    p.x = x;
+    p.x_bf16 = x_dtype == FP4_DTYPE_BF16;
+    p.rows = colwise->rows;
+    p.cols = colwise->cols;
+    p.ld = ld_x;
+    p.q = colwise->q;
+    p.scales = colwise->scales;
+    p.tensor_scale = colwise->tensor_scale;
+    p.amax_src = src;
+    p.refresh = refresh;
+    p.block = fr.block;
+    p.stochastic = fr.rounding == FP4_ROUND_STOCHASTIC;
+    p.seed = seed;
+    p.offset = offset;
+    p.fmt = f;
+    p.rht = 0;
+    p.rht_signs = 0;
+    p.elem_int4 = fr.element == FP4_ELEM_INT4;
+    const RowOut ro{rowwise->q, rowwise->scales, rowwise->tensor_scale};
+    st = hip_status(launch_quantize_t(p, s, &ro));
+    if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
+    return st;
+}
+
 fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream)
 {
     ScaleFmtHost f;

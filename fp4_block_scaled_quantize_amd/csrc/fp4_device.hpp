@@ -293,18 +293,20 @@ __device__ __forceinline__ void rht_forward_lane(float v[B], uint32_t signs)
     for (int k = 0; k < B; ++k) v[k] = v[k] * c;
 }
 
-// max |v| of 8 binary32 values as bits (non-negative floats order like
+// max |v| of N binary32 values as bits (non-negative floats order like
 // their bit patterns)
-__device__ __forceinline__ uint32_t absmax_bits8(const float v[8])
+template <int N>
+__device__ __forceinline__ uint32_t absmax_bits_n(const float v[N])
 {
     uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < N; ++k) {
         const uint32_t u = __float_as_uint(v[k]) & 0x7FFFFFFFu;
         m = m > u ? m : u;
     }
     return m;
 }
+__device__ __forceinline__ uint32_t absmax_bits8(const float v[8]) { return absmax_bits_n<8>(v); }
 
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds, multipliers

@@ -73,8 +73,15 @@ struct DequantLaunch {
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);
-// Column-wise: rows/cols describe the output (x^T); x is [cols, rows].
-hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s);
+// The row-wise output of a two-orientation call.
+struct RowOut {
+    uint8_t* q;
+    uint8_t* scales;
+    float* tensor_scale;
+};
+// Column-wise: rows/cols describe the output (x^T); x is [cols, rows].  With
+// `rows`, the row-wise quantization of x is written there too (one read).
+hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* rows = nullptr);
 hipError_t launch_dequantize(const DequantLaunch& p, hipStream_t s);
 
 struct GemmLaunch {

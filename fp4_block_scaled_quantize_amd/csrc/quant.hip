@@ -653,6 +653,9 @@ struct QTArgs {
     ScaleFmt f;
     uint32_t key0, key1, off0, off1;
     uint32_t signs;              // Hadamard transform sign mask (ROT kernels)
+    uint8_t* q_row;              // ROWS kernels: the row-wise output too,
+    uint8_t* s_row;              // codes [R, C/2], scales [R, C/B],
+    float* ts_row;               // tensor scale {g, amax}
 };
 
 template <typename InT>
@@ -744,9 +747,91 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT, bool ROT>
+// Row-wise quantization of the tile's loaded 16-byte pieces (ROWS kernels):
+// piece p of a tile row holds elements c0 + EPP p .. of row r, and the
+// BLOCK / EPP pieces of a row block sit in adjacent lanes, so the block
+// maximum is a shuffle reduction over those lanes; every rule (scale,
+// nearest or stochastic rounding with the row-wise counter index r C + c)
+// is that of the row-wise kernel.
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT>
+__device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoad<InT>& ld, uint32_t r0, uint32_t c0,
+                                                  float g, float d)
+{
+    constexpr int EPP = TileLoad<InT>::EPP;
+    constexpr int G = BLOCK / EPP;               // lanes per row block
+    const uint32_t piece = threadIdx.x % TileLoad<InT>::PPR, prow = threadIdx.x / TileLoad<InT>::PPR;
+    const uint32_t gc = c0 + piece * EPP;
+#pragma unroll
+    for (int k = 0; k < TileLoad<InT>::NLD; ++k) {
+        const uint32_t gr = r0 + prow + k * TileLoad<InT>::RPR;
+        float v[EPP];
+        if (sizeof(InT) == 2) {
+            const u32x4 w = ld.v[k];
+            v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+            if (EPP == 8) {
+                v[2 % EPP] = bf16_lo(w.y); v[3 % EPP] = bf16_hi(w.y);
+                v[4 % EPP] = bf16_lo(w.z); v[5 % EPP] = bf16_hi(w.z);
+                v[6 % EPP] = bf16_lo(w.w); v[7 % EPP] = bf16_hi(w.w);
+            }
+        } else {
+            const u32x4 w = ld.v[k];
+            v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+            v[2 % EPP] = __uint_as_float(w.z); v[3 % EPP] = __uint_as_float(w.w);
+        }
+        uint32_t m = absmax_bits_n<EPP>(v);
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) {
+            const uint32_t t = (uint32_t)__shfl_xor((int)m, o, 64);
+            m = m > t ? m : t;
+        }
+        float inv;
+        uint32_t code;
+        if (E8M0) {
+            code = scale_code_e8m0(__uint_as_float(m));
+            inv = e8m0_inv(code);
+        } else {
+            code = exmy_scale(__uint_as_float(m), d, g, a.f, &inv);
+        }
+#pragma unroll
+        for (int i = 0; i < EPP; ++i) v[i] = v[i] * inv;
+        uint32_t packed = 0;
+        if (SR) {
+            const uint32_t u = (uint32_t)(((uint64_t)gr * a.C + gc) >> 3);   // unit (i >> 3), row-wise index
+            const U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+            const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+            const uint32_t e0 = gc & 7u;                             // first element of the piece in its unit
+#pragma unroll
+            for (int i = 0; i < EPP; ++i) {
+                const uint32_t e = e0 + i;
+                const uint32_t r16 = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                packed |= (INT ? int4_sr_code(v[i], r16) : e2m1_sr(v[i], r16)) << (4 * i);
+            }
+        } else if (INT) {
+#pragma unroll
+            for (int i = 0; i < EPP; ++i) packed |= int4_rtn_code(v[i]) << (4 * i);
+        } else {
+            packed = FP4_CVT_PK(0u, v[0], v[1], 0);
+            packed = FP4_CVT_PK(packed, v[2 % EPP], v[3 % EPP], 1);
+            if (EPP == 8) {
+                packed = FP4_CVT_PK(packed, v[4 % EPP], v[5 % EPP], 2);
+                packed = FP4_CVT_PK(packed, v[6 % EPP], v[7 % EPP], 3);
+            }
+        }
+        if (gr < a.R && gc < a.C) {
+            uint8_t* qd = a.q_row + (uint64_t)gr * (a.C / 2) + gc / 2;
+            if (EPP == 8) __builtin_nontemporal_store(packed, (uint32_t*)qd);
+            else __builtin_nontemporal_store((uint16_t)packed, (uint16_t*)qd);
+            if (piece % G == 0) a.s_row[(uint64_t)gr * (a.C / BLOCK) + gc / BLOCK] = (uint8_t)code;
+        }
+    }
+}
+
+// ROWS: also the row-wise quantization of the same tile from the loaded
+// registers (x read once for both orientations; no transform).
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT, bool ROT, bool ROWS>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : 5)))) void k_quantize_t(QTArgs a)
 {
+    static_assert(!(ROWS && ROT), "the two orientations would need different transforms and maxima");
     constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
     constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
     constexpr int NB = RPW / BLOCK;              // blocks per lane
@@ -770,14 +855,23 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             a.tensor_scale[0] = g;
             a.tensor_scale[1] = am;
+            if (ROWS) {
+                a.ts_row[0] = g;
+                a.ts_row[1] = am;
+            }
             if (a.refresh) a.amax_src->stored = am;
         }
     } else if (blockIdx.x == 0 && threadIdx.x == 0) {
         a.tensor_scale[0] = 1.0f;
         a.tensor_scale[1] = 0.0f;
+        if (ROWS) {
+            a.ts_row[0] = 1.0f;
+            a.ts_row[1] = 0.0f;
+        }
     }
 
     ld.store(tile);
+    if (ROWS) rowwise_from_tile<InT, BLOCK, SR, E8M0, INT>(a, ld, r0, c0, g, d);
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -898,28 +992,33 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 }
 
-template <typename InT, int BLOCK, bool INT, bool ROT>
+template <typename InT, int BLOCK, bool INT, bool ROT, bool ROWS>
 static void launch_qt3(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
 {
     const dim3 g(blocks), t(kTThreads);
     if (sr) {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT, ROT>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT, ROT>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT, ROT, ROWS>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT, ROT, ROWS>), g, t, 0, s, a);
     } else {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT, ROT>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT, ROT>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT, ROT, ROWS>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT, ROT, ROWS>), g, t, 0, s, a);
     }
 }
 
+// rows: the two-orientation variant (never with a transform)
 template <typename InT, int BLOCK>
-static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, bool rot, uint32_t blocks, hipStream_t s)
+static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, bool rot, bool rows, uint32_t blocks,
+                       hipStream_t s)
 {
-    if (int4) {
-        if (rot) launch_qt3<InT, BLOCK, true, true>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, true, false>(a, sr, e8, blocks, s);
+    if (rows) {
+        if (int4) launch_qt3<InT, BLOCK, true, false, true>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, false, false, true>(a, sr, e8, blocks, s);
+    } else if (int4) {
+        if (rot) launch_qt3<InT, BLOCK, true, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, true, false, false>(a, sr, e8, blocks, s);
     } else {
-        if (rot) launch_qt3<InT, BLOCK, false, true>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, false, false>(a, sr, e8, blocks, s);
+        if (rot) launch_qt3<InT, BLOCK, false, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, false, false, false>(a, sr, e8, blocks, s);
     }
 }
 
@@ -934,9 +1033,12 @@ static void launch_amax_t(const QTArgs& a, int block, uint32_t ntiles, hipStream
 // p.rows / p.cols are the output's shape (C, R); x is [R, C] with row stride
 // p.ld.  A refresh takes an amax kernel first (x is read twice): the row-wise
 // one, or the tiled one when the blocks are transformed.
-hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
+hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* rows)
 {
     QTArgs a;
+    a.q_row = rows ? rows->q : nullptr;
+    a.s_row = rows ? rows->scales : nullptr;
+    a.ts_row = rows ? rows->tensor_scale : nullptr;
     a.x = p.x;
     a.ld = p.ld;
     a.R = (uint32_t)p.cols;
@@ -971,11 +1073,11 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s)
     }
     const uint32_t blocks = ntiles ? ntiles : 1;
     if (p.x_bf16) {
-        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, rot, blocks, s);
-        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, rot, blocks, s);
+        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
+        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
     } else {
-        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, rot, blocks, s);
-        else launch_qt2<float, 32>(a, sr, e8, int4, rot, blocks, s);
+        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
+        else launch_qt2<float, 32>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
     }
     return hipGetLastError();
 }

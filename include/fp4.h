@@ -231,6 +231,26 @@ FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64
                                    fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
 
 /*
+ * fp4_quantize_both -- both orientations of x [R, C] from one read: rowwise
+ * [R, C] receives exactly what fp4_quantize(x) writes, colwise [C, R]
+ * exactly what fp4_quantize_transposed(x) writes, and both get the same
+ * tensor scale (gonzo_ML/3986 "Стохастическая квантизация" and
+ * ue5m3-fp4-pretraining "Что сделали": the backward pass quantizes the
+ * same gradient and activation tensors along both dimensions, one for each
+ * of its two products).  Both tensors must carry the same block size, scale
+ * encoding, rounding, amax policy and element grid, and no transform
+ * (UNSUPPORTED otherwise: a transform along each axis would give the two
+ * outputs different maxima).  The amax state counts the pair as one call.
+ * Requirements as for the two calls together: R % block == 0, C % block ==
+ * 0, x 16-byte aligned with ld_x * sizeof(elem) a multiple of 16, colwise->q
+ * 16-byte aligned.  A refresh of the tensor maximum reads x twice (an amax
+ * pass, then this one); otherwise x is read once.
+ */
+FP4_API fp4_status fp4_quantize_both(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* rowwise,
+                                     fp4_tensor* colwise, fp4_amax_state* state, uint64_t seed, uint64_t offset,
+                                     void* stream);
+
+/*
  * fp4_dequantize -- y[rows, cols] (row stride ld_y, f32 or bf16) =
  * RN(RN(e2m1(code) * s) * g), rounded once more to bf16 (RNE) for bf16
  * output (quant_prune_distill/486 "Метод": the element times its group's

@@ -147,3 +147,19 @@ def test_element_checks():
     w = _tensor(rows=8, cols=256)
     w.fmt.element = 1
     assert L.fp4_wo_gemm(FAKE, 256, 0, ctypes.byref(w), FAKE, 8, None) == -2      # INT4 weights accepted: M = 0 decides
+
+
+def test_quantize_both_checks():
+    L = fq.lib()
+    r = _tensor(rows=32, cols=64)
+    c = _tensor(rows=64, cols=32)
+    bad = _tensor(rows=64, cols=64)
+    assert L.fp4_quantize_both(FAKE, 1, 64, ctypes.byref(r), ctypes.byref(bad), FAKE, 0, 0, None) == -3
+    c2 = _tensor(rows=64, cols=32, scale=1)                       # different scale encoding
+    assert L.fp4_quantize_both(FAKE, 1, 64, ctypes.byref(r), ctypes.byref(c2), FAKE, 0, 0, None) == -2
+    c3 = _tensor(rows=64, cols=32)
+    c3.fmt.transform = 1
+    assert L.fp4_quantize_both(FAKE, 1, 64, ctypes.byref(r), ctypes.byref(c3), FAKE, 0, 0, None) == -2
+    assert L.fp4_quantize_both(FAKE, 1, 60, ctypes.byref(r), ctypes.byref(c), FAKE, 0, 0, None) == -3   # ld < C
+    assert L.fp4_quantize_both(FAKE + 8, 1, 64, ctypes.byref(r), ctypes.byref(c), FAKE, 0, 0, None) == -4
+    assert L.fp4_quantize_both(FAKE, 1, 64, ctypes.byref(r), ctypes.byref(c), None, 0, 0, None) == -1   # no state
