@@ -202,9 +202,39 @@ def leg_sr_transposed(torch, fq, inputs, steps):
         res["sr" if rnd == "stochastic" else "rtn"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                                      "ms_per_sequence": round(ms, 3)}
         del gs, outs
+    # both orientations of every gradient: one two-orientation call against
+    # a row-wise plus a column-wise call (each reads the tensor)
+    for rnd, mode in (("stochastic", "both"), ("stochastic", "separate"), ("nearest", "both"),
+                      ("nearest", "separate")):
+        outs = [(fq.QTensor.empty(rows, cols, 16, "e4m3", rounding=rnd, amax="delayed"),
+                 fq.QTensor.empty(cols, rows, 16, "e4m3", rounding=rnd, amax="delayed")) for _ in range(2)]
+        st, st2 = fq.AmaxState(50), fq.AmaxState(50)
+
+        def rec(_):
+            for t in range(ntens):
+                o = outs[t % 2]
+                if mode == "both":
+                    fq.fp4_quantize_both(xs[t], 16, "e4m3", rounding=rnd, amax="delayed", state=st,
+                                         seed=0x5EED, offset=t, out=o)
+                else:
+                    fq.fp4_quantize(xs[t], 16, "e4m3", rounding=rnd, amax="delayed", state=st, seed=0x5EED,
+                                    offset=t, out=o[0])
+                    fq.fp4_quantize_transposed(xs[t], 16, "e4m3", rounding=rnd, amax="delayed", state=st2,
+                                               seed=0x5EED, offset=t, out=o[1])
+        gs = GraphSet(torch, 1, rec)
+        reps = max(1, min(3, steps // 10))
+        ms = time_graphs(torch, gs, reps, 1)
+        n = rows * cols
+        algo = ntens * (n * 2 + 2 * (n // 2 + n // 16 + 8))        # the input read once, both outputs
+        res[f"{'sr' if rnd == 'stochastic' else 'rtn'}_{mode}"] = {
+            "ms_per_sequence": round(ms, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gs, outs
     del xs
     res["workload"] = ("200 x 8192x8192 bf16 Laplace(1e-4) grads quantized column-wise (x^T), E4M3 B16, "
-                       "delayed amax N=50; SR Philox and RTN")
+                       "delayed amax N=50; SR Philox and RTN; both orientations from one read (*_both) "
+                       "against a row-wise plus a column-wise call (*_separate), GB/s of one input read "
+                       "plus both outputs")
     return res
 
 

@@ -179,7 +179,7 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     CURRENT if none is given.  rht_signs (32-bit sign mask) applies the
     blockwise randomized Hadamard transform before quantization; element
     "int4" selects the INT4 grid (-7..7) instead of E2M1."""
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
     if out is None:
@@ -206,7 +206,7 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
                             rht_signs: int | None = None) -> QTensor:
     """Column-wise quantization of a 2-D fp32/bf16 CUDA tensor x [R, C]: the
     result is the quantized x^T [C, R] (blocks run down the columns of x)."""
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
     r, c = x.shape
     if out is None:
@@ -234,7 +234,7 @@ def fp4_quantize_both(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rou
     """Row-wise and column-wise quantization of x [R, C] from one read:
     returns (rowwise [R, C], colwise [C, R]) QTensors, each identical to the
     corresponding single-orientation call."""
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
     r, c = x.shape
     if out is None:

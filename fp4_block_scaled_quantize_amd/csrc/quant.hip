@@ -644,6 +644,8 @@ struct QTArgs {
     int64_t ld;
     uint32_t R, C;               // x is [R, C]
     uint32_t ntr;                // tiles along R
+    uint32_t ntc;                // tiles along C
+    uint32_t ntr_pad;            // ROWS kernels: ntr rounded up to a multiple of 8
     uint32_t xcd_chunk;          // consecutive tiles per XCD (0: plain order)
     uint8_t* q;                  // [C, R/2]
     uint8_t* scales;             // [C, R/B]
@@ -753,53 +755,111 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
 // maximum is a shuffle reduction over those lanes; every rule (scale,
 // nearest or stochastic rounding with the row-wise counter index r C + c)
 // is that of the row-wise kernel.
+template <typename InT>
+__device__ __forceinline__ void unpack_piece(const u32x4& w, float v[16 / sizeof(InT)])
+{
+    if (sizeof(InT) == 2) {
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4 % (16 / sizeof(InT))] = bf16_lo(w.z); v[5 % (16 / sizeof(InT))] = bf16_hi(w.z);
+        v[6 % (16 / sizeof(InT))] = bf16_lo(w.w); v[7 % (16 / sizeof(InT))] = bf16_hi(w.w);
+    } else {
+        v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+        v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    }
+}
+
 template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT>
 __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoad<InT>& ld, uint32_t r0, uint32_t c0,
                                                   float g, float d)
 {
     constexpr int EPP = TileLoad<InT>::EPP;
+    constexpr int NLD = TileLoad<InT>::NLD;
     constexpr int G = BLOCK / EPP;               // lanes per row block
     const uint32_t piece = threadIdx.x % TileLoad<InT>::PPR, prow = threadIdx.x / TileLoad<InT>::PPR;
     const uint32_t gc = c0 + piece * EPP;
+    const uint32_t sub = threadIdx.x & (G - 1);  // position of this lane's piece in its block
+
+    // block maxima of every loaded piece, reduced over the block's lanes
+    uint32_t bm[NLD];
 #pragma unroll
-    for (int k = 0; k < TileLoad<InT>::NLD; ++k) {
-        const uint32_t gr = r0 + prow + k * TileLoad<InT>::RPR;
+    for (int k = 0; k < NLD; ++k) {
         float v[EPP];
-        if (sizeof(InT) == 2) {
-            const u32x4 w = ld.v[k];
-            v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-            if (EPP == 8) {
-                v[2 % EPP] = bf16_lo(w.y); v[3 % EPP] = bf16_hi(w.y);
-                v[4 % EPP] = bf16_lo(w.z); v[5 % EPP] = bf16_hi(w.z);
-                v[6 % EPP] = bf16_lo(w.w); v[7 % EPP] = bf16_hi(w.w);
-            }
-        } else {
-            const u32x4 w = ld.v[k];
-            v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
-            v[2 % EPP] = __uint_as_float(w.z); v[3 % EPP] = __uint_as_float(w.w);
-        }
-        uint32_t m = absmax_bits_n<EPP>(v);
-#pragma unroll
-        for (int o = 1; o < G; o <<= 1) {
-            const uint32_t t = (uint32_t)__shfl_xor((int)m, o, 64);
+        unpack_piece<InT>(ld.v[k], v);
+        uint32_t m = dpp_umax_xor1(absmax_bits_n<EPP>(v));
+        if (G >= 4) m = dpp_umax_xor2(m);
+        if (G >= 8) {
+            const uint32_t t = (uint32_t)__shfl_xor((int)m, 4, 64);
             m = m > t ? m : t;
         }
-        float inv;
-        uint32_t code;
+        bm[k] = m;
+    }
+
+    // scales: with G <= 4 lane `sub` computes those of pieces k = sub PER + t
+    // and the block's lanes exchange them (DPP within the quad); with G = 8
+    // every lane computes its own
+    float inv[NLD];
+    uint32_t code[NLD];
+    auto scale_of = [&](uint32_t m, float* iv) -> uint32_t {
         if (E8M0) {
-            code = scale_code_e8m0(__uint_as_float(m));
-            inv = e8m0_inv(code);
-        } else {
-            code = exmy_scale(__uint_as_float(m), d, g, a.f, &inv);
+            const uint32_t c = scale_code_e8m0(__uint_as_float(m));
+            *iv = e8m0_inv(c);
+            return c;
+        }
+        return exmy_scale(__uint_as_float(m), d, g, a.f, iv);
+    };
+    constexpr bool SHARE = G <= 4;
+    if (SHARE) {
+        constexpr int PER = NLD / (SHARE ? G : 1);
+        float inv_own[PER];
+        uint32_t code_own[PER];
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            uint32_t m = bm[t];
+#pragma unroll
+            for (int j = 1; j < G; ++j) m = (sub == (uint32_t)j) ? bm[(j * PER + t) % NLD] : m;
+            code_own[t] = scale_of(m, &inv_own[t]);
         }
 #pragma unroll
-        for (int i = 0; i < EPP; ++i) v[i] = v[i] * inv;
+        for (int t = 0; t < PER; ++t) {
+            if (G == 2) {
+                const float mine = inv_own[t];
+                const float other = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mine), 0xB1, 0xF, 0xF, false));
+                inv[t] = sub == 0 ? mine : other;
+                inv[(PER + t) % NLD] = sub == 1 ? mine : other;
+            } else {
+                inv[t] = quad_bcast<0>(inv_own[t]);
+                inv[(PER + t) % NLD] = quad_bcast<1>(inv_own[t]);
+                inv[(2 * PER + t) % NLD] = quad_bcast<2>(inv_own[t]);
+                inv[(3 * PER + t) % NLD] = quad_bcast<3>(inv_own[t]);
+            }
+            // this lane stores the scale bytes it computed
+            const uint32_t k = sub * PER + t;
+            const uint32_t gr = r0 + prow + k * TileLoad<InT>::RPR;
+            if (gr < a.R && gc < a.C) a.s_row[(uint64_t)gr * (a.C / BLOCK) + gc / BLOCK] = (uint8_t)code_own[t];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            code[k] = scale_of(bm[k], &inv[k]);
+            const uint32_t gr = r0 + prow + k * TileLoad<InT>::RPR;
+            if (sub == 0 && gr < a.R && gc < a.C) a.s_row[(uint64_t)gr * (a.C / BLOCK) + gc / BLOCK] = (uint8_t)code[k];
+        }
+    }
+
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+        const uint32_t gr = r0 + prow + k * TileLoad<InT>::RPR;
+        float v[EPP];
+        unpack_piece<InT>(ld.v[k], v);
+#pragma unroll
+        for (int i = 0; i < EPP; ++i) v[i] = v[i] * inv[k];
         uint32_t packed = 0;
         if (SR) {
             const uint32_t u = (uint32_t)(((uint64_t)gr * a.C + gc) >> 3);   // unit (i >> 3), row-wise index
             const U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
             const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-            const uint32_t e0 = gc & 7u;                             // first element of the piece in its unit
+            const uint32_t e0 = gc & 7u;                                   // first element of the piece in its unit
 #pragma unroll
             for (int i = 0; i < EPP; ++i) {
                 const uint32_t e = e0 + i;
@@ -817,11 +877,12 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
                 packed = FP4_CVT_PK(packed, v[6 % EPP], v[7 % EPP], 3);
             }
         }
+        // plain (not streaming) stores: each is a 32-byte piece of a line
+        // that the neighbouring tiles of the super-tile complete in L2
         if (gr < a.R && gc < a.C) {
             uint8_t* qd = a.q_row + (uint64_t)gr * (a.C / 2) + gc / 2;
-            if (EPP == 8) __builtin_nontemporal_store(packed, (uint32_t*)qd);
-            else __builtin_nontemporal_store((uint16_t)packed, (uint16_t*)qd);
-            if (piece % G == 0) a.s_row[(uint64_t)gr * (a.C / BLOCK) + gc / BLOCK] = (uint8_t)code;
+            if (EPP == 8) *(uint32_t*)qd = packed;
+            else *(uint16_t*)qd = (uint16_t)packed;
         }
     }
 }
@@ -829,7 +890,7 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
 // ROWS: also the row-wise quantization of the same tile from the loaded
 // registers (x read once for both orientations; no transform).
 template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT, bool ROT, bool ROWS>
-__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : 5)))) void k_quantize_t(QTArgs a)
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && INT ? 4 : 5))))) void k_quantize_t(QTArgs a)
 {
     static_assert(!(ROWS && ROT), "the two orientations would need different transforms and maxima");
     constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
@@ -841,7 +902,22 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     // the lines of the scale rows) run on one XCD
     uint32_t t = blockIdx.x;
     if (a.xcd_chunk) t = (t & 7u) * a.xcd_chunk + (t >> 3);
-    const uint32_t tc = t / a.ntr, tr = t - tc * a.ntr;
+    uint32_t tc, tr;
+    if (ROWS) {
+        // super-tiles of 8 (down) x 4 (across) tiles: the 128-byte lines of
+        // the row-wise codes (4 tiles across) and of the column-wise scales
+        // (8 tiles down) are written by tiles that run close together on
+        // one XCD.  The grid is padded to whole super-tiles.
+        const uint32_t st = t >> 5, wi = t & 31u, nsr = a.ntr_pad >> 3;
+        tr = (st % nsr) * 8 + (wi & 7u);
+        tc = (st / nsr) * 4 + (wi >> 3);
+        // padding (whole workgroup); workgroup 0 always runs (it writes the
+        // tensor scale, and every load and store below is bounds-checked)
+        if ((tr >= a.ntr || tc >= a.ntc) && blockIdx.x != 0) return;
+    } else {
+        tc = t / a.ntr;
+        tr = t - tc * a.ntr;
+    }
     const uint32_t r0 = tr * kTR, c0 = tc * kTC;
 
     TileLoad<InT> ld;
@@ -1046,7 +1122,10 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* 
     const uint32_t ntr = (a.R + kTR - 1) / kTR, ntc = (a.C + kTC - 1) / kTC;
     const uint32_t ntiles = ntr * ntc;
     a.ntr = ntr ? ntr : 1;
-    a.xcd_chunk = (ntiles % 8 == 0) ? ntiles / 8 : 0;
+    a.ntc = ntc;
+    a.ntr_pad = (a.ntr + 7) & ~7u;
+    const uint32_t grid_tiles = rows ? a.ntr_pad * ((ntc + 3) & ~3u) : ntiles;     // super-tile padding
+    a.xcd_chunk = (grid_tiles % 8 == 0) ? grid_tiles / 8 : 0;
     a.q = p.q;
     a.scales = p.scales;
     a.tensor_scale = p.tensor_scale;
@@ -1071,7 +1150,7 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* 
             if (e != hipSuccess) return e;
         }
     }
-    const uint32_t blocks = ntiles ? ntiles : 1;
+    const uint32_t blocks = grid_tiles ? grid_tiles : 1;
     if (p.x_bf16) {
         if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
         else launch_qt2<uint16_t, 32>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);

@@ -117,3 +117,11 @@ def test_both_rejects_mismatch_and_transform():
         fq.fp4_quantize_both(xd, 16, "e4m3", out=(fq.QTensor.empty(64, 64, 16, "e4m3"),
                                                   fq.QTensor.empty(32, 64, 16, "e4m3")))
     assert e.value.status == -3
+
+
+def test_both_empty_and_tiny():
+    for shape in [(0, 64), (64, 0), (32, 32)]:
+        x = np.zeros(shape, dtype=np.float32)
+        if shape == (32, 32):
+            x = _like(32, 32, 63, "f32")
+        _check_both(x, 16, "e4m3", "current", tag=f"both {shape}")
