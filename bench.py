@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "8c2abd88395492a8c5d3170217f86dfe366d3be4ec41623cf3ab788527d57acc",
-    "read_bytes": 33784896,
+    "sha256": "84b40722fdb881190e6ade28cf4887c7897977e3427445d83387fc40d413a5aa",
+    "read_bytes": 33788064,
     "write_bytes": 9453761,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
