@@ -125,3 +125,22 @@ def test_both_empty_and_tiny():
         if shape == (32, 32):
             x = _like(32, 32, 63, "f32")
         _check_both(x, 16, "e4m3", "current", tag=f"both {shape}")
+
+
+def test_both_strided_rows():
+    """A row stride larger than the row (a column slice of a wider tensor):
+    both outputs as for the contiguous tensor."""
+    x = _like(96, 128, 64)
+    big = np.zeros((96, 200), dtype=np.uint16)
+    big[:, :128] = x
+    xd = to_device(big)[:, :128]
+    assert xd.stride(0) == 200
+    st = fq.AmaxState(1)
+    qr, qc = fq.fp4_quantize_both(xd, 16, "e4m3", rounding="stochastic", state=st, seed=4, offset=8)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "current", stochastic=True, seed=4, offset=8)
+    assert_bytes_equal(host(qr.q), q, "strided both row codes")
+    assert_bytes_equal(host(qr.scales), s, "strided both row scales")
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "current", stochastic=True, seed=4, offset=8)
+    assert_bytes_equal(host(qc.q), q, "strided both col codes")
+    assert_bytes_equal(host(qc.scales), s, "strided both col scales")
