@@ -44,7 +44,8 @@ FORMATS = {
     "e8m0": (8, 0, 0),
 }
 
-ELEMS = {"e2m1": 0, "int4": 1}
+ELEMS = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3}
+ELEM_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8}
 
 _lib = None
 
@@ -94,6 +95,10 @@ def lib():
         "or_sr_bits_array": (None, [c_u64, c_u64, c_u64, c_i64, c_p]),
         "or_rht_norm": (c_f, [c_int]),
         "or_int4_decode": (c_d, [c_int]),
+        "or_int8_decode": (c_d, [c_int]),
+        "or_int8_rtn": (c_int, [c_f]),
+        "or_int8_sr": (c_int, [c_f, ctypes.c_uint32]),
+        "or_e8m0_block_code_emax": (c_int, [c_f, c_int]),
         "or_int4_rtn": (c_int, [c_f]),
         "or_int4_sr": (c_int, [c_f, ctypes.c_uint32]),
         "or_tensor_scale_elem": (c_f, [c_f, c_int, c_int, c_int, c_int]),
@@ -197,6 +202,22 @@ def tensor_scale(amax_t: float, fmt: str, elem: str = "e2m1") -> float:
     return lib().or_tensor_scale_elem(float(amax_t), *_fmt(fmt), _elem(elem))
 
 
+def int8_decode(code: int) -> float:
+    return lib().or_int8_decode(int(code))
+
+
+def int8_rtn(v: float) -> int:
+    return lib().or_int8_rtn(float(v))
+
+
+def int8_sr(v: float, r16: int) -> int:
+    return lib().or_int8_sr(float(v), int(r16))
+
+
+def e8m0_block_code_emax(amax_b: float, emax: int) -> int:
+    return lib().or_e8m0_block_code_emax(float(amax_b), int(emax))
+
+
 def int4_decode(code: int) -> float:
     return lib().or_int4_decode(int(code))
 
@@ -254,7 +275,7 @@ def quantize(x: np.ndarray, block: int, fmt: str, g: float, *, stochastic: bool 
     x, is_bf16 = _as_input(x)
     nrows, cols = x.shape
     r0, r1 = (0, nrows) if rows is None else rows
-    q = np.zeros((r1 - r0, cols // 2), dtype=np.uint8)
+    q = np.zeros((r1 - r0, cols * ELEM_BITS[elem] // 8), dtype=np.uint8)
     s = np.zeros((r1 - r0, cols // block), dtype=np.uint8)
     rc = lib().or_quantize_elem(_ptr(x), is_bf16, nrows, cols, cols, block, *_fmt(fmt), float(g),
                                 int(stochastic), seed, offset, r0, r1, _ptr(q), _ptr(s), nthreads, _elem(elem))
@@ -267,7 +288,7 @@ def dequantize(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt: str
                out: str = "f32", elem: str = "e2m1") -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
-    rows, cols = q.shape[0], q.shape[1] * 2
+    rows, cols = q.shape[0], q.shape[1] * 8 // ELEM_BITS[elem]
     if out == "f32":
         y = np.empty((rows, cols), dtype=np.float32)
     elif out == "bf16":
@@ -285,7 +306,7 @@ def dequantize_f64(q: np.ndarray, scales: np.ndarray, g: float, block: int, fmt:
                    elem: str = "e2m1") -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
-    rows, cols = q.shape[0], q.shape[1] * 2
+    rows, cols = q.shape[0], q.shape[1] * 8 // ELEM_BITS[elem]
     y = np.empty((rows, cols), dtype=np.float64)
     rc = lib().or_dequantize_f64_elem(_ptr(q), _ptr(scales), float(g), rows, cols, block, *_fmt(fmt), _ptr(y),
                                       _elem(elem))
@@ -381,8 +402,10 @@ def quantize_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *, state: 
     With rht_signs the blockwise randomized Hadamard transform is applied
     first (rht_forward) and everything after it, the tensor maximum
     included, sees the transformed binary32 tensor.
-    elem: "e2m1" (FP4) or "int4" (the integer grid -7..7, two's-complement
-    nibbles; quant_prune_distill/574 "Метод": NVINT4 / MXINT4).
+    elem: "e2m1" (FP4), "int4" (the integer grid -7..7, two's-complement
+    nibbles; quant_prune_distill/574 "Метод": NVINT4 / MXINT4), or the 8-bit
+    grids "fp8_e4m3" and "int8" (-127..127), one byte per element (MXFP8 /
+    MXINT8).
     Returns (q, scales, g, amax_used)."""
     if rht_signs is not None:
         x = rht_forward(x, block, rht_signs)

@@ -144,8 +144,65 @@ OR_EXPORT int or_int4_sr(float v, uint32_t r16)
 /* two's-complement nibble of sign * magnitude (magnitude 0 -> code 0) */
 static int int4_code(int negative, int mag) { return negative ? ((16 - mag) & 0xF) : mag; }
 
-/* largest element magnitude of a grid: 6 (E2M1) or 7 (INT4) */
-static float elem_max(int elem) { return elem ? 7.0f : 6.0f; }
+/* Element grids: 0 = E2M1, 1 = INT4 (4-bit codes, two per byte), 2 = FP8
+ * E4M3, 3 = INT8 (one byte each).  [P-INT] quant_prune_distill/574 "Метод":
+ * MXFP8/MXINT8 pair the MX groups of 32 with E8M0 scales with the FP8 and
+ * INT8 grids.  Reading for the 8-bit grids: FP8 E4M3 elements take the E4M3
+ * magnitudes (largest 448), nearest-even and saturating, the sign bit kept
+ * (also for zero, as for E2M1); INT8 takes the symmetric grid -127..127 as
+ * two's complement (0x80 never produced, zero unsigned). */
+static int elem_bits(int elem) { return elem >= 2 ? 8 : 4; }
+
+/* largest element magnitude of a grid */
+static float elem_max(int elem)
+{
+    switch (elem) {
+    case 0: return 6.0f;
+    case 1: return 7.0f;
+    case 2: return 448.0f;
+    default: return 127.0f;
+    }
+}
+
+/* exponent of the grid's largest binade, the E8M0 rule's offset: the block
+ * maximum lands in [2^emax, 2^(emax+1)) after scaling (OCP MX convention) */
+static int elem_emax(int elem)
+{
+    switch (elem) {
+    case 2: return 8;
+    case 3: return 6;
+    default: return 2;
+    }
+}
+
+/* INT8: nearest integer magnitude of |v| (ties to even), saturating at 127 */
+OR_EXPORT int or_int8_rtn(float v)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 127.0) return 127;
+    double lo = floor(a), frac = a - lo;
+    int m = (int)lo;
+    if (frac > 0.5 || (frac == 0.5 && (m & 1))) m += 1;
+    return m;
+}
+
+OR_EXPORT int or_int8_sr(float v, uint32_t r16)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 127.0) return 127;
+    int lo = (int)floor(a);
+    double frac = a - (double)lo;
+    double u = (double)(r16 & 0xFFFFu) / 65536.0;
+    return (u < frac) ? lo + 1 : lo;
+}
+
+OR_EXPORT double or_int8_decode(int code)
+{
+    code &= 0xFF;
+    return (double)(code >= 128 ? code - 256 : code);
+}
 
 /* ------------------------------------------------------------------------ */
 /* Scale formats.                                                            */
@@ -242,13 +299,18 @@ OR_EXPORT int or_scale_encode(int eb, int mb, int sg, float u)
  * brought into the top binade of E2M1, e = floor(log2(amax_b)) - 2, so the
  * largest element lands in [4, 8) and anything above 6 saturates;
  * code = clamp(e + 127, 0, 254); amax_b = 0 gives code 0. */
-OR_EXPORT int or_e8m0_block_code(float amax_b)
+OR_EXPORT int or_e8m0_block_code_emax(float amax_b, int emax);
+OR_EXPORT int or_e8m0_block_code(float amax_b) { return or_e8m0_block_code_emax(amax_b, 2); }
+
+/* As above with the element grid's offset emax (2 for E2M1 and INT4, 8 for
+ * FP8 E4M3, 6 for INT8): floor(log2 amax_b) - emax + 127, clamped. */
+OR_EXPORT int or_e8m0_block_code_emax(float amax_b, int emax)
 {
     if (!(amax_b > 0.0f)) return 0;
     int ex;
     double m = frexp((double)amax_b, &ex);      /* amax_b = m * 2^ex, m in [0.5,1) */
     (void)m;
-    int e = (ex - 1) - 2;                       /* floor(log2 amax_b) - 2, exact */
+    int e = (ex - 1) - emax;                    /* floor(log2 amax_b) - emax, exact */
     int code = e + 127;
     if (code < 0) code = 0;
     if (code > 254) code = 254;
@@ -357,6 +419,21 @@ typedef struct {
     int elem;                        /* 0 = E2M1, 1 = INT4 */
 } quant_job;
 
+/* FP8 E4M3 element, stochastic: |v| between adjacent grid magnitudes lo <= |v|
+ * < hi rounds up iff u = r16 / 2^16 < (|v| - lo) / (hi - lo) (exact: the
+ * spacing is a power of two); |v| at or beyond the largest (448) saturates. */
+static int fp8_sr(const double* etab, int n, float v, uint32_t r16)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= etab[n - 1]) return n - 1;
+    int lo = 0;
+    while (lo + 1 < n && etab[lo + 1] <= a) ++lo;
+    double frac = (a - etab[lo]) / (etab[lo + 1] - etab[lo]);
+    double u = (double)(r16 & 0xFFFFu) / 65536.0;
+    return (u < frac) ? lo + 1 : lo;
+}
+
 static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
 {
     const int64_t nb = J->cols / J->block;
@@ -365,8 +442,12 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
     double tab[256];
     decode_table(J->eb, J->mb, J->sg, tab);
     const int ncodes = fmt_ncodes(J->eb, J->mb, J->sg);
+    double etab[256];                               /* FP8 E4M3 element magnitudes */
+    decode_table(4, 3, 1, etab);
+    const int encodes = fmt_ncodes(4, 3, 1);
+    const int64_t qstride = J->cols * elem_bits(J->elem) / 8;
     for (int64_t r = ra; r < rb; ++r) {
-        uint8_t* qrow = J->q + (r - J->row0) * (J->cols / 2);
+        uint8_t* qrow = J->q + (r - J->row0) * qstride;
         uint8_t* srow = J->scales + (r - J->row0) * nb;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t c0 = b * J->block;
@@ -378,7 +459,7 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
             int scode;
             float s;
             if (e8) {
-                scode = or_e8m0_block_code(amax_b);
+                scode = or_e8m0_block_code_emax(amax_b, elem_emax(J->elem));
                 s = (float)ldexp(1.0, scode - 127);
             } else {
                 float u = amax_b / d;
@@ -401,14 +482,31 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
                     if (J->stochastic) {
                         uint64_t i = (uint64_t)r * (uint64_t)J->cols + (uint64_t)col;
                         uint32_t r16 = or_sr_bits(J->seed, J->offset, i);
-                        mag = J->elem ? or_int4_sr(v, r16) : or_e2m1_sr(v, r16);
+                        switch (J->elem) {
+                        case 0: mag = or_e2m1_sr(v, r16); break;
+                        case 1: mag = or_int4_sr(v, r16); break;
+                        case 2: mag = fp8_sr(etab, encodes, v, r16); break;
+                        default: mag = or_int8_sr(v, r16); break;
+                        }
                     } else {
-                        mag = J->elem ? or_int4_rtn(v) : or_e2m1_rtn(v);
+                        switch (J->elem) {
+                        case 0: mag = or_e2m1_rtn(v); break;
+                        case 1: mag = or_int4_rtn(v); break;
+                        case 2: mag = encode_nearest(etab, encodes, fabsf(v)); break;
+                        default: mag = or_int8_rtn(v); break;
+                        }
                     }
                 }
-                int code = J->elem ? int4_code((int)(bits_of_f(xv) >> 31), mag)
-                                   : (int)((bits_of_f(xv) >> 31) << 3) | mag;
-                if ((col & 1) == 0) qrow[col >> 1] = (uint8_t)code;
+                const int neg = (int)(bits_of_f(xv) >> 31);
+                int code;
+                switch (J->elem) {
+                case 0: code = (neg << 3) | mag; break;
+                case 1: code = int4_code(neg, mag); break;
+                case 2: code = (neg << 7) | mag; break;
+                default: code = neg ? ((256 - mag) & 0xFF) : mag; break;
+                }
+                if (elem_bits(J->elem) == 8) qrow[col] = (uint8_t)code;
+                else if ((col & 1) == 0) qrow[col >> 1] = (uint8_t)code;
                 else qrow[col >> 1] |= (uint8_t)(code << 4);
             }
         }
@@ -444,7 +542,7 @@ OR_EXPORT int or_quantize_elem(const void* x, int is_bf16, int64_t rows, int64_t
                                int stochastic, uint64_t seed, uint64_t offset,
                                int64_t row0, int64_t row1, uint8_t* q, uint8_t* scales, int nthreads, int elem)
 {
-    if (elem != 0 && elem != 1) return -1;
+    if (elem < 0 || elem > 3) return -1;
     if (!x || !q || !scales || rows < 0 || cols < 0 || ld < cols) return -1;
     if (block != 16 && block != 32) return -1;
     if (cols % block) return -1;
@@ -484,7 +582,22 @@ OR_EXPORT uint16_t or_f32_to_bf16(float f)
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
-static double elem_decode(int code, int elem) { return elem ? or_int4_decode(code) : or_e2m1_decode(code); }
+static double elem_decode(int code, int elem)
+{
+    switch (elem) {
+    case 0: return or_e2m1_decode(code);
+    case 1: return or_int4_decode(code);
+    case 2: return or_scale_decode(4, 3, 1, code);
+    default: return or_int8_decode(code);
+    }
+}
+
+static int elem_code_at(const uint8_t* q, int64_t r, int64_t c, int64_t cols, int elem)
+{
+    if (elem_bits(elem) == 8) return q[r * cols + c];
+    uint8_t byte = q[r * (cols / 2) + c / 2];
+    return (c & 1) ? (byte >> 4) : (byte & 0xF);
+}
 
 OR_EXPORT int or_dequantize_elem(const uint8_t* q, const uint8_t* scales, float g,
                                  int64_t rows, int64_t cols, int block, int eb, int mb, int sg,
@@ -506,8 +619,7 @@ OR_EXPORT int or_dequantize_elem(const uint8_t* q, const uint8_t* scales, float 
     const int64_t nb = cols / block;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
-            uint8_t byte = q[r * (cols / 2) + c / 2];
-            int code = (c & 1) ? (byte >> 4) : (byte & 0xF);
+            int code = elem_code_at(q, r, c, cols, elem);
             float s = (float)or_scale_decode(eb, mb, sg, scales[r * nb + c / block]);
             float e = (float)elem_decode(code, elem);
             float t = e * s;
@@ -608,8 +720,7 @@ OR_EXPORT int or_dequantize_f64_elem(const uint8_t* q, const uint8_t* scales, fl
     const int64_t nb = cols / block;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
-            uint8_t byte = q[r * (cols / 2) + c / 2];
-            int code = (c & 1) ? (byte >> 4) : (byte & 0xF);
+            int code = elem_code_at(q, r, c, cols, elem);
             double s = or_scale_decode(eb, mb, sg, scales[r * nb + c / block]);
             y[r * cols + c] = elem_decode(code, elem) * s * (double)g;
         }

@@ -844,3 +844,110 @@ def test_int4_dequantize_exact_product_and_gemm_orientation():
             assert Fraction(float(yd[r, c])) == exact           # exact in binary64
             t = np.float32(np.float32(oracle.int4_decode(code)) * np.float32(sv))
             assert y[r, c] == np.float32(t * g)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit MX element grids (MXFP8 with E4M3 elements, MXINT8)
+# ---------------------------------------------------------------------------
+def test_e8m0_emax_rule_closed_form():
+    rng = np.random.default_rng(81)
+    for emax in (2, 6, 8):
+        for a in np.exp(rng.uniform(np.log(1e-20), np.log(1e20), 400)).astype(np.float32):
+            c = oracle.e8m0_block_code_emax(float(a), emax)
+            s = 2.0 ** (c - 127)
+            assert 2.0 ** emax * s <= float(a) < 2.0 ** (emax + 1) * s
+    assert oracle.e8m0_block_code_emax(0.0, 8) == 0
+
+
+def _unit_scale_blocks(rng, rows, lim, top):
+    # 32-element blocks whose maximum |x| is `top` in [2^emax, 2^(emax+1)), so
+    # the E8M0 code is 127 (scale exactly 1) and the elements are encoded as is
+    x = rng.uniform(-lim, lim, (rows, 32 * 8)).astype(np.float32)
+    x[:, ::32] = np.float32(top)
+    return x
+
+
+def test_fp8_elements_match_torch_float8_e4m3fn():
+    rng = np.random.default_rng(82)
+    x = _unit_scale_blocks(rng, 16, 448.0, 300.0)
+    x[:, 5] = 0.0
+    x[:, 6] = -0.0
+    x[:, 7] = np.float32(1e-5)                          # below half the smallest subnormal
+    q, s, g, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem="fp8_e4m3")
+    assert np.all(s == 127) and g == 1.0
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, want)
+
+
+def test_int8_elements_match_numpy_rint():
+    rng = np.random.default_rng(83)
+    x = _unit_scale_blocks(rng, 16, 127.0, 100.0)
+    x[:, 9] = np.float32(2.5)
+    x[:, 10] = np.float32(-3.5)
+    q, s, g, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem="int8")
+    assert np.all(s == 127)
+    want = np.clip(np.rint(x.astype(np.float64)), -127, 127).astype(np.int8).view(np.uint8)
+    assert np.array_equal(q, want)
+    for code in range(256):
+        assert oracle.int8_decode(code) == float(np.array([code], dtype=np.uint8).view(np.int8)[0])
+
+
+@pytest.mark.parametrize("v", [0.3, 17.75, 126.9, -44.1, 200.0])
+def test_int8_sr_exact_expectation(v):
+    mags = np.array([oracle.int8_sr(v, r) for r in range(65536)])
+    a = abs(v)
+    if a >= 127:
+        assert np.all(mags == 127)
+        return
+    lo = np.floor(np.float32(a))
+    frac = np.float64(np.float32(a)) - lo
+    assert set(np.unique(mags)) <= {int(lo), int(lo) + 1}
+    assert (mags == lo + 1).sum() == int(np.ceil(frac * 65536))
+
+
+def test_fp8_sr_rounds_between_grid_neighbours():
+    # E8M0 block 32 with scale 1 (block maximum 300): 100.5 lies between the
+    # E4M3 neighbours 96 and 104 (spacing 8), frac = 4.5 / 8; every block is
+    # seeded differently, so the up fraction approaches 0.5625
+    x = np.full((64, 256), 100.5, dtype=np.float32)
+    x[:, ::32] = 300.0
+    q, s, _, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem="fp8_e4m3", stochastic=True, seed=9,
+                                        offset=0)
+    vals = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).float().numpy()
+    mid = vals[:, [c for c in range(256) if c % 32]]
+    assert set(np.unique(mid)) <= {96.0, 104.0}
+    frac_up = float((mid == 104.0).mean())
+    assert abs(frac_up - 4.5 / 8) < 0.02
+
+
+@pytest.mark.parametrize("elem,qmax", [("fp8_e4m3", 448.0), ("int8", 127.0)])
+def test_8bit_tensor_max_maps_to_grid_max(elem, qmax):
+    x = _sweep_like(32, 256, 84, bf16=False)
+    q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "current", elem=elem)
+    assert g == np.float32(a) / (np.float32(qmax) * np.float32(448.0))
+    r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert s[r, c // 16] == 0x7E
+    if elem == "fp8_e4m3":
+        v = float(torch.tensor([int(q[r, c])], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+    else:
+        v = oracle.int8_decode(int(q[r, c]))
+    assert v == (qmax if x[r, c] > 0 else -qmax)
+
+
+@pytest.mark.parametrize("elem", ["fp8_e4m3", "int8"])
+def test_8bit_dequantize_exact_product(elem):
+    rng = np.random.default_rng(85)
+    q = rng.integers(0, 256, (4, 64), dtype=np.uint8)
+    if elem == "fp8_e4m3":
+        q[(q & 0x7F) == 0x7F] = 0x11                      # no NaN codes
+    s = rng.integers(0x30, 0x60, (4, 4), dtype=np.uint8)
+    g = np.float32(0.0173)
+    y = oracle.dequantize(q, s, float(g), 16, "e4m3", elem=elem)
+    for r in range(4):
+        for c in range(64):
+            if elem == "fp8_e4m3":
+                e = float(torch.tensor([int(q[r, c])], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+            else:
+                e = float(np.array([q[r, c]], dtype=np.uint8).view(np.int8)[0])
+            sv = oracle.scale_decode("e4m3", int(s[r, c // 16]))
+            assert y[r, c] == np.float32(np.float32(np.float32(e) * np.float32(sv)) * g)
