@@ -25,7 +25,8 @@ SCALE_FORMATS = {"e4m3": 0, "ue5m3": 1, "e3m4": 2, "e1m6": 3, "e8m0": 4, "e2m5":
 ROUNDING = {"nearest": 0, "stochastic": 1}
 AMAX = {"none": 0, "current": 1, "delayed": 2}
 TRANSFORM = {"none": 0, "rht": 1}
-ELEMENT = {"e2m1": 0, "int4": 1}
+ELEMENT = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3}
+ELEMENT_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 FP4_OK = 0
@@ -124,7 +125,7 @@ class QTensor:
     def empty(cls, rows: int, cols: int, block: int, scale: str, rounding: str = "nearest",
               amax: str = "current", device="cuda", transform: str = "none", rht_signs: int = 0,
               element: str = "e2m1"):
-        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        q = torch.empty((rows, cols * ELEMENT_BITS[element] // 8), dtype=torch.uint8, device=device)
         s = torch.empty((rows, cols // block), dtype=torch.uint8, device=device)
         ts = torch.empty(2, dtype=torch.float32, device=device)
         return cls(q, s, ts, rows, cols, block, scale, rounding, amax, transform, rht_signs, element)
@@ -178,12 +179,13 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     must be 1).  CURRENT and DELAYED need an AmaxState; one is created for
     CURRENT if none is given.  rht_signs (32-bit sign mask) applies the
     blockwise randomized Hadamard transform before quantization; element
-    "int4" selects the INT4 grid (-7..7) instead of E2M1."""
+    selects the grid: "e2m1" (default), "int4" (-7..7), or the one-byte
+    "fp8_e4m3" and "int8" (-127..127)."""
     if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
     if out is None:
-        out = QTensor.empty(rows, cols, block, scale, rounding, amax, device=x.device)
+        out = QTensor.empty(rows, cols, block, scale, rounding, amax, device=x.device, element=element)
     else:
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)

@@ -93,6 +93,16 @@ __device__ __forceinline__ uint32_t scale_code_e8m0(float amax_b)
     return (uint32_t)(ex > 2 ? ex - 2 : 0);
 }
 
+// As scale_code_e8m0 with the element grid's offset EMAX (the block maximum
+// lands in [2^EMAX, 2^(EMAX+1)) after scaling): 8 for FP8 E4M3 elements, 6
+// for INT8.
+template <int EMAX>
+__device__ __forceinline__ uint32_t scale_code_e8m0_emax(float amax_b)
+{
+    int ex = (int)((f_bits(amax_b) >> 23) & 0xFFu);
+    return (uint32_t)(ex > EMAX ? ex - EMAX : 0);
+}
+
 // 2^(127 - code): exact reciprocal of an E8M0 scale, code in [0, 252].
 __device__ __forceinline__ float e8m0_inv(uint32_t code) { return bits_f((254u - code) << 23); }
 
@@ -171,6 +181,55 @@ __device__ __forceinline__ uint32_t int4_sr_code(float v, uint32_t r16)
 }
 
 __device__ __forceinline__ float int4_value(uint32_t nib) { return (float)((int32_t)(nib << 28) >> 28); }
+
+// ---------------------------------------------------------------------------
+// 8-bit MX elements (quant_prune_distill/574 "Метод": MXFP8 / MXINT8).
+// Reading: FP8 E4M3 elements, nearest-even and saturating at 448, the sign
+// bit kept (also for zero); INT8 on the symmetric grid -127..127 (two's
+// complement, zero unsigned).  One byte per element.
+// ---------------------------------------------------------------------------
+constexpr ScaleFmt kFp8E4M3{4, 3, 7, 0x7E, 448.0f, 0};
+
+__device__ __forceinline__ uint32_t fp8_rtn_code(float v)
+{
+    return scale_encode_exmy(__builtin_fabsf(v), kFp8E4M3) | ((f_bits(v) >> 24) & 0x80u);
+}
+
+// Stochastic: in the binade e of |v| (e >= -6; below 2^-6 the subnormal
+// spacing 2^-9) t = |v| 2^(3-e) is exact, floor(t) indexes the lower grid
+// neighbour and the code ((e + 7) << 3) + m - 8 also covers the carry into
+// the next binade and the subnormals.
+__device__ __forceinline__ uint32_t fp8_sr_code(float v, uint32_t r16)
+{
+    const float a = __builtin_fabsf(v);
+    const uint32_t sign = (f_bits(v) >> 24) & 0x80u;
+    if (!(a < 448.0f)) return 0x7Eu | sign;
+    const int eu = (int)((f_bits(a) >> 23) & 0xFFu) - 127;
+    const int e = eu > -6 ? eu : -6;
+    const float t = __builtin_amdgcn_ldexpf(a, 3 - e);
+    const float fl = __builtin_floorf(t);
+    const float frac = t - fl;
+    const uint32_t m = (uint32_t)fl + (((float)r16 < frac * 65536.0f) ? 1u : 0u);
+    const uint32_t code = (uint32_t)((e + 7) << 3) + m - 8u;
+    return (code < 0x7Eu ? code : 0x7Eu) | sign;
+}
+
+__device__ __forceinline__ uint32_t int8_rtn_code(float v)
+{
+    return (uint32_t)(int32_t)__builtin_rintf(__builtin_amdgcn_fmed3f(v, -127.0f, 127.0f)) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t int8_sr_code(float v, uint32_t r16)
+{
+    const float a = __builtin_fabsf(v);
+    const float fl = __builtin_floorf(a);
+    const float frac = a - fl;                                      // exact
+    const float up = ((float)r16 < frac * 65536.0f) ? 1.0f : 0.0f;
+    const uint32_t m = (uint32_t)(a >= 127.0f ? 127.0f : fl + up);
+    return (f_bits(v) >> 31) ? ((256u - m) & 0xFFu) : m;
+}
+
+__device__ __forceinline__ float int8_value(uint32_t b) { return (float)(int32_t)(int8_t)(b & 0xFFu); }
 
 // ---------------------------------------------------------------------------
 // wave64 helpers

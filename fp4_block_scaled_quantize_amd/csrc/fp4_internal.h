@@ -54,7 +54,7 @@ struct QuantLaunch {
     ScaleFmtHost fmt;
     int32_t rht;               // blockwise randomized Hadamard transform first
     uint32_t rht_signs;
-    int32_t elem_int4;         // INT4 element grid instead of E2M1
+    int32_t elem;              // element grid: 0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8
 };
 
 struct DequantLaunch {
@@ -69,7 +69,7 @@ struct DequantLaunch {
     int64_t ld;
     int32_t rht;               // inverse blockwise Hadamard transform last
     uint32_t rht_signs;
-    int32_t elem_int4;         // INT4 element grid instead of E2M1
+    int32_t elem;              // element grid: 0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);

@@ -371,10 +371,14 @@ __device__ __forceinline__ float quad_bcast(float v)
 // right after the loads; block maxima, the tensor maximum and the codes all
 // see the transformed values.
 // INT: the INT4 element grid (-7..7) instead of E2M1.
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT, bool INT>
+// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8; the last two
+// one byte per element).
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT, int ELEM>
 __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArgs a)
 {
-    constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
+    constexpr bool INT = ELEM == 1;
+    constexpr bool W8 = ELEM >= 2;
+    constexpr float QMAX = ELEM == 0 ? 6.0f : ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : 127.0f;   // grid maximum
     constexpr int T = FUSED ? kFThreads : kQThreads;
     constexpr int U = FUSED ? kFUnroll : kQUnroll;
     constexpr int G = BLOCK / 8;                 // lanes per block (2 or 4)
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         for (int k = 1; k < G; ++k) x = (sub == (uint32_t)k) ? bm[k * PER + t] : x;
         uint32_t code;
         if (E8M0) {
-            code = scale_code_e8m0(x);
+            code = ELEM == 2 ? scale_code_e8m0_emax<8>(x) : ELEM == 3 ? scale_code_e8m0_emax<6>(x) : scale_code_e8m0(x);
             inv_own[t] = e8m0_inv(code);
         } else {
             code = exmy_scale(x, d, g, a.f, &inv_own[t]);
@@ -490,6 +494,26 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = v[k] * inv[j];
         uint32_t packed;
+        if (W8) {
+            // one byte per element: eight codes in two dwords
+            uint32_t c[8];
+            if (SR) {
+                U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                    c[k] = ELEM == 2 ? fp8_sr_code(v[k], r16) : int8_sr_code(v[k], r16);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) c[k] = ELEM == 2 ? fp8_rtn_code(v[k]) : int8_rtn_code(v[k]);
+            }
+            const u32x2 pk{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                           c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+            if (u < a.nunits) __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(a.q) + u);
+            continue;
+        }
         if (SR) {
             U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
             const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -513,40 +537,47 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT, bool INT>
+template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT, int ELEM>
 static void launch_q6(const QArgs& a, bool strided, uint32_t blocks, hipStream_t s)
 {
     const dim3 t(FUSED ? kFThreads : kQThreads);
     if (strided)
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED, ROT, INT>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, true, FUSED, ROT, ELEM>), dim3(blocks), t, 0, s, a);
     else
-        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED, ROT, INT>), dim3(blocks), t, 0, s, a);
+        hipLaunchKernelGGL((k_quantize<InT, BLOCK, SR, E8M0, false, FUSED, ROT, ELEM>), dim3(blocks), t, 0, s, a);
 }
 
-template <typename InT, int BLOCK, bool ROT, bool INT>
+template <typename InT, int BLOCK, bool ROT, int ELEM>
 static void launch_q4(const QArgs& a, bool sr, bool e8, bool fused, bool strided, uint32_t blocks, hipStream_t s)
 {
     if (sr) {
-        if (fused) launch_q6<InT, BLOCK, true, false, true, ROT, INT>(a, strided, blocks, s);
-        else if (e8) launch_q6<InT, BLOCK, true, true, false, ROT, INT>(a, strided, blocks, s);
-        else launch_q6<InT, BLOCK, true, false, false, ROT, INT>(a, strided, blocks, s);
+        if (fused) launch_q6<InT, BLOCK, true, false, true, ROT, ELEM>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, true, true, false, ROT, ELEM>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, true, false, false, ROT, ELEM>(a, strided, blocks, s);
     } else {
-        if (fused) launch_q6<InT, BLOCK, false, false, true, ROT, INT>(a, strided, blocks, s);
-        else if (e8) launch_q6<InT, BLOCK, false, true, false, ROT, INT>(a, strided, blocks, s);
-        else launch_q6<InT, BLOCK, false, false, false, ROT, INT>(a, strided, blocks, s);
+        if (fused) launch_q6<InT, BLOCK, false, false, true, ROT, ELEM>(a, strided, blocks, s);
+        else if (e8) launch_q6<InT, BLOCK, false, true, false, ROT, ELEM>(a, strided, blocks, s);
+        else launch_q6<InT, BLOCK, false, false, false, ROT, ELEM>(a, strided, blocks, s);
     }
 }
 
+template <typename InT, int BLOCK, int ELEM>
+static void launch_q35(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, uint32_t blocks,
+                       hipStream_t s)
+{
+    if (rot) launch_q4<InT, BLOCK, true, ELEM>(a, sr, e8, fused, strided, blocks, s);
+    else launch_q4<InT, BLOCK, false, ELEM>(a, sr, e8, fused, strided, blocks, s);
+}
+
 template <typename InT, int BLOCK>
-static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, bool int4,
+static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided, bool rot, int elem,
                       uint32_t blocks, hipStream_t s)
 {
-    if (int4) {
-        if (rot) launch_q4<InT, BLOCK, true, true>(a, sr, e8, fused, strided, blocks, s);
-        else launch_q4<InT, BLOCK, false, true>(a, sr, e8, fused, strided, blocks, s);
-    } else {
-        if (rot) launch_q4<InT, BLOCK, true, false>(a, sr, e8, fused, strided, blocks, s);
-        else launch_q4<InT, BLOCK, false, false>(a, sr, e8, fused, strided, blocks, s);
+    switch (elem) {
+    case 1: launch_q35<InT, BLOCK, 1>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    case 2: launch_q35<InT, BLOCK, 2>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    case 3: launch_q35<InT, BLOCK, 3>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    default: launch_q35<InT, BLOCK, 0>(a, sr, e8, fused, strided, rot, blocks, s); break;
     }
 }
 
@@ -582,7 +613,7 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.off1 = (uint32_t)(p.offset >> 32);
     a.signs = p.rht_signs;
     const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols, rot = p.rht != 0;
-    const bool int4 = p.elem_int4 != 0;
+    const int elem = p.elem;
 
     // A refresh reads the input once when the whole tensor fits the
     // single-pass grid (at most one workgroup per CU, kFUnroll units per
@@ -610,11 +641,11 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         if (blocks == 0) blocks = 1;
     }
     if (p.x_bf16) {
-        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, rot, int4, blocks, s);
-        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, rot, int4, blocks, s);
+        if (p.block == 16) launch_q3<uint16_t, 16>(a, sr, e8, fused, strided, rot, elem, blocks, s);
+        else launch_q3<uint16_t, 32>(a, sr, e8, fused, strided, rot, elem, blocks, s);
     } else {
-        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, rot, int4, blocks, s);
-        else launch_q3<float, 32>(a, sr, e8, fused, strided, rot, int4, blocks, s);
+        if (p.block == 16) launch_q3<float, 16>(a, sr, e8, fused, strided, rot, elem, blocks, s);
+        else launch_q3<float, 32>(a, sr, e8, fused, strided, rot, elem, blocks, s);
     }
     return hipGetLastError();
 }
@@ -1137,7 +1168,7 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* 
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
     a.signs = p.rht_signs;
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem_int4 != 0, rot = p.rht != 0;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem == 1, rot = p.rht != 0;
     if (a.amax_src && a.refresh && !e8) {
         if (rot) {
             // the maximum of the column-transformed tensor
@@ -1173,7 +1204,7 @@ constexpr int kDQUnroll = 4;                 // units per lane, loads issued tog
 // ROT: the inverse blockwise Hadamard transform follows the binary32
 // dequantization (the G units of a block are adjacent lanes and are all in
 // range or all out of it).
-template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT, bool INT>
+template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT, int ELEM>
 __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ tensor_scale, uint32_t nunits,
@@ -1184,12 +1215,20 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = blockIdx.x * (kDQThreads / 64) + (threadIdx.x >> 6);
     const uint32_t base = wave * (64u * U);
-    uint32_t w[U], sc[U];
+    constexpr bool W8 = ELEM >= 2;               // one byte per element
+    uint32_t w[U], w2[U], sc[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const uint32_t u = base + j * 64 + lane;
         const uint32_t uu = u < nunits ? u : nunits - 1;           // in bounds; not stored
-        w[j] = __builtin_nontemporal_load(q + uu);
+        if (W8) {
+            const u32x2 p2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q) + uu);
+            w[j] = p2.x;
+            w2[j] = p2.y;
+        } else {
+            w[j] = __builtin_nontemporal_load(q + uu);
+            w2[j] = 0u;
+        }
         sc[j] = scales[uu / (BLOCK / 8)];
     }
     const float g = tensor_scale[0];
@@ -1201,8 +1240,15 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
         float o[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const uint32_t nib = (w[j] >> (4 * k)) & 0xFu;
-            float t = (INT ? int4_value(nib) : e2m1_value(nib)) * s;
+            float e;
+            if (W8) {
+                const uint32_t b = ((k < 4 ? w[j] : w2[j]) >> (8 * (k & 3))) & 0xFFu;
+                e = ELEM == 2 ? scale_decode_any(b, kFp8E4M3) : int8_value(b);
+            } else {
+                const uint32_t nib = (w[j] >> (4 * k)) & 0xFu;
+                e = ELEM == 1 ? int4_value(nib) : e2m1_value(nib);
+            }
+            float t = e * s;
             o[k] = t * g;
         }
         if (ROT) rht_inverse<BLOCK / 8>(o, lane & (BLOCK / 8 - 1), signs);
@@ -1222,7 +1268,7 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
     }
 }
 
-template <bool OUT_BF16, int BLOCK, bool ROT, bool INT>
+template <bool OUT_BF16, int BLOCK, bool ROT, int ELEM>
 static void launch_dq4(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
@@ -1230,11 +1276,11 @@ static void launch_dq4(const DequantLaunch& p, uint32_t nunits, const FastDiv& f
     uint32_t blocks = (nunits + per_block - 1) / per_block;
     if (blocks == 0) blocks = 1;
     if (f.is_e8m0)
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true, ROT, INT>), dim3(blocks), dim3(kDQThreads), 0, s,
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, true, ROT, ELEM>), dim3(blocks), dim3(kDQThreads), 0, s,
                            (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
                            p.rht_signs);
     else
-        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false, ROT, INT>), dim3(blocks), dim3(kDQThreads), 0, s,
+        hipLaunchKernelGGL((k_dequantize<OUT_BF16, BLOCK, false, ROT, ELEM>), dim3(blocks), dim3(kDQThreads), 0, s,
                            (const uint32_t*)p.q, p.scales, p.tensor_scale, nunits, fd, p.ld, strided, f, p.y,
                            p.rht_signs);
 }
@@ -1243,12 +1289,23 @@ template <bool OUT_BF16, int BLOCK>
 static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& fd, int strided, const ScaleFmt& f,
                        hipStream_t s)
 {
-    if (p.elem_int4) {
-        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, true>(p, nunits, fd, strided, f, s);
-        else launch_dq4<OUT_BF16, BLOCK, false, true>(p, nunits, fd, strided, f, s);
-    } else {
-        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, false>(p, nunits, fd, strided, f, s);
-        else launch_dq4<OUT_BF16, BLOCK, false, false>(p, nunits, fd, strided, f, s);
+    switch (p.elem) {
+    case 1:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 1>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 1>(p, nunits, fd, strided, f, s);
+        break;
+    case 2:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 2>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 2>(p, nunits, fd, strided, f, s);
+        break;
+    case 3:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 3>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 3>(p, nunits, fd, strided, f, s);
+        break;
+    default:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 0>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 0>(p, nunits, fd, strided, f, s);
+        break;
     }
 }
 

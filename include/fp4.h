@@ -116,10 +116,20 @@ typedef enum fp4_transform {
  * RN(7 g)); the E8M0 exponent rule is unchanged (amax_b / s in [4, 8), the
  * MX convention for a sign + 3-bit fixed-point element); nearest rounding
  * ties to the even integer and saturates at 7; stochastic rounding as for
- * E2M1 with grid spacing 1. */
+ * E2M1 with grid spacing 1.
+ * The 8-bit grids (the same page's MXFP8 / MXINT8) store one byte per
+ * element, codes [rows, cols] (reading): FP8 E4M3 elements, nearest-even
+ * and saturating at 448, the sign bit kept (also for zero); INT8 on the
+ * symmetric grid -127..127 (two's complement, zero unsigned).  448 or 127
+ * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
+ * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
+ * Quantize and dequantize only: the column-wise and two-orientation calls
+ * and the GEMMs return UNSUPPORTED for them. */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
-    FP4_ELEM_INT4 = 1
+    FP4_ELEM_INT4 = 1,
+    FP4_ELEM_FP8_E4M3 = 2,    /* MXFP8-style, one byte per element           */
+    FP4_ELEM_INT8 = 3         /* MXINT8-style, one byte per element          */
 } fp4_element;
 
 typedef struct fp4_format {
@@ -132,9 +142,10 @@ typedef struct fp4_format {
     int32_t element;          /* fp4_element                                  */
 } fp4_format;
 
-/* A quantized tensor.  q: rows*cols/2 bytes; scales: rows*cols/block bytes;
- * tensor_scale: 2 floats {g, amax used} (g = 1 and amax = 0 under NONE).
- * All three are device pointers; q must be 4-byte aligned. */
+/* A quantized tensor.  q: rows*cols/2 bytes (4-bit grids) or rows*cols
+ * bytes (8-bit grids); scales: rows*cols/block bytes; tensor_scale: 2 floats
+ * {g, amax used} (g = 1 and amax = 0 under NONE).  All three are device
+ * pointers; q must be 4-byte aligned (8-byte for the 8-bit grids). */
 typedef struct fp4_tensor {
     uint8_t* q;
     uint8_t* scales;

@@ -163,3 +163,13 @@ def test_quantize_both_checks():
     assert L.fp4_quantize_both(FAKE, 1, 60, ctypes.byref(r), ctypes.byref(c), FAKE, 0, 0, None) == -3   # ld < C
     assert L.fp4_quantize_both(FAKE + 8, 1, 64, ctypes.byref(r), ctypes.byref(c), FAKE, 0, 0, None) == -4
     assert L.fp4_quantize_both(FAKE, 1, 64, ctypes.byref(r), ctypes.byref(c), None, 0, 0, None) == -1   # no state
+
+
+def test_8bit_element_checks():
+    L = fq.lib()
+    assert L.fp4_version() >= 103
+    t = _tensor(q=FAKE + 4)
+    t.fmt.element = 2                                  # 8-bit codes need 8-byte alignment
+    assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -4
+    t.fmt.element = 4
+    assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -1
