@@ -18,7 +18,7 @@ agrees on the maximum.
 Further legs reported in "legs": stochastic rounding with delayed amax over
 200 successive 8192x8192 gradients, the same gradients quantized column-wise
 (the backward-pass operands), dequantize, quantize with the blockwise
-randomized Hadamard transform, the INT4 element grid (quantize and GEMM), the block-scaled GEMM on the
+randomized Hadamard transform, the INT4 element grid (quantize and GEMM), the 8-bit MX grids (quantize), the block-scaled GEMM on the
 Llama-2 7B linear shapes, and the weight-only GEMM at Qwen-2.5 decode
 shapes.  "roofline" is the dominant kernel of the step (the single-pass
 E4M3 block-16 current-amax quantize kernel: four of the five calls) timed
@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "84b40722fdb881190e6ade28cf4887c7897977e3427445d83387fc40d413a5aa",
-    "read_bytes": 33788064,
-    "write_bytes": 9453761,
+    "sha256": "8b738772305a968977a3a35cdbe5572d6b0292ed20041081141028e43258dc50",
+    "read_bytes": 33788767,
+    "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,w8,gemm,wo", help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 64 MiB device copy three times (calibrates HBM byte counters)")
@@ -352,6 +352,29 @@ def leg_int4(torch, fq, inputs, xs):
     return res
 
 
+def leg_8bit(torch, fq, xs):
+    """The 8-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
+    elements) and MXINT8-style (E8M0 block 32), one byte per element."""
+    rows, cols = xs[0].shape
+    res = {}
+    n = rows * cols
+    algo = n * 2 + n + n // 32 + 8
+    for elem in ("fp8_e4m3", "int8"):
+        outs = [fq.QTensor.empty(rows, cols, 32, "e8m0", amax="none", element=elem) for _ in xs]
+
+        def rec(_):
+            for j in range(len(xs)):
+                fq.fp4_quantize(xs[j], 32, "e8m0", amax="none", out=outs[j], element=elem)
+        gs = GraphSet(torch, 1, rec)
+        ms = time_graphs(torch, gs, 20, 3) / len(xs)
+        res[f"mx{'fp8' if elem == 'fp8_e4m3' else 'int8'}_quantize"] = {
+            "us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gs, outs
+    res["workload"] = "4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each), RTN"
+    return res
+
+
 def leg_wo(torch, fq, inputs):
     """Weight-only NVFP4 GEMM, W [N, K] = [18944, 3584] and [3584, 18944],
     M in {1, 8, 16}; 12 weight copies rotate (>= 450 MB) so weights stream
@@ -462,6 +485,8 @@ def main():
     if "int4" in want:
         legs["int4"] = leg_int4(torch, fq, inputs, xs[:8])
         torch.cuda.empty_cache()
+    if "w8" in want:
+        legs["mx8"] = leg_8bit(torch, fq, xs[:8])
     del outs
     if "sr" in want:
         legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)
