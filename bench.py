@@ -352,9 +352,11 @@ def leg_int4(torch, fq, inputs, xs):
     return res
 
 
-def leg_8bit(torch, fq, xs):
+def leg_8bit(torch, fq, inputs, xs):
     """The 8-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
-    elements) and MXINT8-style (E8M0 block 32), one byte per element."""
+    elements) and MXINT8-style (E8M0 block 32), one byte per element, and
+    the GEMM at the Llama-2 7B up-projection shape on the exact dequantize
+    path (MXFP8 in bf16; INT8 elements with E4M3 block-16 scales in f16)."""
     rows, cols = xs[0].shape
     res = {}
     n = rows * cols
@@ -371,7 +373,26 @@ def leg_8bit(torch, fq, xs):
             "us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del gs, outs
-    res["workload"] = "4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each), RTN"
+    m, n, k = 8192, 11008, 4096
+    for name, (elem, fmt, block, pol) in {"mxfp8": ("fp8_e4m3", "e8m0", 32, "none"),
+                                          "nvint8": ("int8", "e4m3", 16, "current")}.items():
+        a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
+        w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_up"], torch.bfloat16)
+        qa = fq.fp4_quantize(a, block, fmt, amax=pol, element=elem)
+        qw = fq.fp4_quantize(w, block, fmt, amax=pol, element=elem)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+        def rec_g(_):
+            fq.fp4_gemm(qa, qw, out=c)
+        gs = GraphSet(torch, 1, rec_g)
+        ms = time_graphs(torch, gs, 10, 2)
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        res[f"{name}_gemm_up"] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
+                                  "frac_bf16_peak": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4),
+                                  "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)}
+        del a, w, qa, qw, c, gs
+    res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each), RTN; "
+                       "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8 and INT8 with E4M3 block-16 scales")
     return res
 
 
@@ -486,7 +507,8 @@ def main():
         legs["int4"] = leg_int4(torch, fq, inputs, xs[:8])
         torch.cuda.empty_cache()
     if "w8" in want:
-        legs["mx8"] = leg_8bit(torch, fq, xs[:8])
+        legs["mx8"] = leg_8bit(torch, fq, inputs, xs[:8])
+        torch.cuda.empty_cache()
     del outs
     if "sr" in want:
         legs["sr_delayed"] = leg_sr(torch, fq, inputs, args.steps)

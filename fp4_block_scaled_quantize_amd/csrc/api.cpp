@@ -346,7 +346,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
     // transformed operands multiply to the same product only when both carry
     // the same transform along K
-    if (a->fmt.element != b->fmt.element || elem_is_8bit(a->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    if (a->fmt.element != b->fmt.element) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != b->fmt.transform) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != FP4_TRANSFORM_NONE && a->fmt.transform_signs != b->fmt.transform_signs)
         return FP4_ERR_UNSUPPORTED;
@@ -363,10 +363,10 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     p.block = a->fmt.block;
     p.fa = fa; p.fb = fb;
     p.c = c; p.ldc = ldc;
-    p.elem_int4 = a->fmt.element == FP4_ELEM_INT4;
+    p.elem = a->fmt.element;
     hipStream_t s = (hipStream_t)stream;
-    if (!p.elem_int4 && fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
-    if (!gemm_dq_supported(fa, fb, p.elem_int4 != 0)) return FP4_ERR_UNSUPPORTED;
+    if (p.elem == FP4_ELEM_E2M1 && fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
+    if (!gemm_dq_supported(fa, fb, p.elem)) return FP4_ERR_UNSUPPORTED;
     return hip_status(launch_gemm_dq(p, s));
 }
 

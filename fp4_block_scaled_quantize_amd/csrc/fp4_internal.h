@@ -92,12 +92,12 @@ struct GemmLaunch {
     ScaleFmtHost fa, fb;
     uint16_t* c;
     int64_t ldc;
-    int32_t elem_int4;         // both operands on the INT4 grid
+    int32_t elem;              // element grid of both operands (fp4_element)
 };
 
 // The exact dequantize path needs one 16-bit type (f16 or bf16) that holds
-// every e2m1 * s product of both operands exactly.
-bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, bool int4);
+// every element * scale product of both operands exactly.
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, int elem);
 hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
 

@@ -562,11 +562,57 @@ __device__ __forceinline__ void dequant32_split(const v4i& codes, float s0, floa
     }
 }
 
-// INT: both operands on the INT4 grid (products of at most 3 + 5 = 8
-// significant bits in the bf16 variant, 3 + 7 in the f16 one: exact).
-template <bool F16, int BLOCK, bool INT = false>
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Dequantize 16 one-byte elements (FP8 E4M3 codes for ELEM 2, INT8 for
+// ELEM 3) with one scale into 16 16-bit values; out[j] holds elements 2j and
+// 2j + 1.  As in dequant32 the launch only picks a 16-bit type that holds
+// every product e * s exactly.
+template <bool F16, int ELEM>
+__device__ __forceinline__ void dequant16_w8(const v4i& codes, float s, uint32_t out[8])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = (uint32_t)codes[d];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float v0, v1;
+            if constexpr (ELEM == 2) {
+                // the hardware OCP E4M3 -> f32 conversion of bytes 2h, 2h + 1
+                // (exact; the NaN codes, which no quantizer writes, give NaN)
+                const v2f e = h == 0 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false)
+                                     : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+                v0 = e[0] * s;
+                v1 = e[1] * s;
+            } else {
+                v0 = int8_value((w >> (16 * h)) & 0xFFu) * s;
+                v1 = int8_value((w >> (16 * h + 8)) & 0xFFu) * s;
+            }
+            uint32_t b0, b1;
+            if (F16) {
+                b0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0);
+                b1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1);
+            } else {
+                b0 = __float_as_uint(v0) >> 16;
+                b1 = __float_as_uint(v1) >> 16;
+            }
+            out[d * 2 + h] = b0 | (b1 << 16);
+        }
+    }
+}
+
+// ELEM: the element grid of both operands (fp4_element order: 0 E2M1, 1
+// INT4, 2 FP8 E4M3, 3 INT8).  The launch picks bf16 or f16 so that every
+// dequantized value is exact: INT4 products carry at most 3 + 5 = 8
+// significant bits in bf16 (3 + 7 in f16), FP8 ones 4 + 4 in bf16, INT8
+// ones 7 + 1 in bf16 (power-of-two scales) or 7 + 4 in f16 (E4M3 scales,
+// at most 127 * 448 < 65504).  The 8-bit grids stage 32 bytes per thread
+// and row instead of 16; the LDS tiles and the matrix loop are the same.
+template <bool F16, int BLOCK, int ELEM = 0>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 {
+    constexpr bool INT = ELEM == 1;
+    constexpr bool W8 = ELEM >= 2;
     extern __shared__ __align__(16) uint8_t smem_raw[];
     DqSmem& sm = *reinterpret_cast<DqSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -574,7 +620,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
     const int64_t n_base = (int64_t)blockIdx.x * kTile;
     const int64_t m_base = (int64_t)blockIdx.y * kTile;
     const int64_t M = p.m, N = p.n, K = p.k;
-    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const int64_t rowb = W8 ? K : K / 2, rows = K / BLOCK;
     const int KT = (int)(K / kDqBK);
     const ScaleFmt fw{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
     const ScaleFmt fa{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
@@ -590,33 +636,48 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
         g = (gw / pw) * (ga / pa);
     }
 
-    // staging: thread t owns 16 B chunk (t & 1) (32 elements) of rows
-    // (t >> 1) and (t >> 1) + 128 of each operand, with their scales
+    // staging: thread t owns chunk (t & 1) (32 elements: 16 B of FP4 / INT4
+    // codes, 32 B of 8-bit ones) of rows (t >> 1) and (t >> 1) + 128 of
+    // each operand, with their scales
+    constexpr int kVec = W8 ? 2 : 1;                                  // 16-byte loads per chunk
     const int crow = tid >> 1, cchunk = tid & 1;
-    v4i rw[2], ra[2];
+    v4i rw[2][kVec], ra[2][kVec];
     uint32_t scw[2], sca[2];
     auto gload = [&](int kt) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int64_t nr = n_base + crow + 128 * r, mr = m_base + crow + 128 * r;
-            const int64_t kb = (int64_t)kt * 32 + cchunk * 16;           // byte offset in the row
+            const int64_t kb = (int64_t)kt * (16 * kVec * 2) + cchunk * (16 * kVec);   // byte offset in the row
             const int64_t sb = ((int64_t)kt * kDqBK + cchunk * 32) / BLOCK; // first scale of the chunk
             if (nr < N) {
-                rw[r] = *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kb);
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) rw[r][v] = *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kb + 16 * v);
                 scw[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sb + nr * rows + sb)
                                      : (uint32_t)p.sb[nr * rows + sb];
             } else {
-                rw[r] = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) rw[r][v] = v4i{0, 0, 0, 0};
                 scw[r] = 0;
             }
             if (mr < M) {
-                ra[r] = *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kb);
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) ra[r][v] = *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kb + 16 * v);
                 sca[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sa + mr * rows + sb)
                                      : (uint32_t)p.sa[mr * rows + sb];
             } else {
-                ra[r] = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int v = 0; v < kVec; ++v) ra[r][v] = v4i{0, 0, 0, 0};
                 sca[r] = 0;
             }
+        }
+    };
+    // 32 elements -> 16 words of 16-bit pairs
+    auto dq = [&](const v4i* c, float s0, float s1, uint32_t o[16]) {
+        if constexpr (W8) {
+            dequant16_w8<F16, ELEM>(c[0], s0, o);
+            dequant16_w8<F16, ELEM>(c[kVec - 1], s1, o + 8);
+        } else {
+            dequant32<F16, INT>(c[0], s0, s1, o);
         }
     };
     auto sstore = [&](int buf) {
@@ -626,7 +687,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(scw[r] & 0xFFu, fw) * pw;
                 const float s1 = BLOCK == 16 ? scale_decode_any((scw[r] >> 8) & 0xFFu, fw) * pw : s0;
-                dequant32<F16, INT>(rw[r], s0, s1, o);
+                dq(rw[r], s0, s1, o);
                 uint8_t* dst = &sm.w[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -636,7 +697,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(sca[r] & 0xFFu, fa) * pa;
                 const float s1 = BLOCK == 16 ? scale_decode_any((sca[r] >> 8) & 0xFFu, fa) * pa : s0;
-                dequant32<F16, INT>(ra[r], s0, s1, o);
+                dq(ra[r], s0, s1, o);
                 uint8_t* dst = &sm.a[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -942,35 +1003,73 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // INT4 elements carry 3 significant bits (E2M1: 2), so bf16 holds int * s
 // exactly for scale formats with at most 4 mantissa bits.
 static bool int4_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 4; }
+// FP8 E4M3 elements carry 4 significant bits: bf16 holds e * s for scales
+// with at most 3 mantissa bits.  f16 is never used for them: 448 times a
+// scale above 146 overflows it.
+static bool fp8_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 3; }
+// INT8 elements carry 7 significant bits: bf16 needs power-of-two scales,
+// f16 holds them times E4M3 scales (11 bits, at most 127 * 448 = 56896).
+static bool int8_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits == 0; }
 
-bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, bool int4)
+// The 16-bit type of the exact dequantize path for element grid elem and
+// scale formats fa, fb: 1 bf16, 2 f16, 0 none exact.
+static int dq_type(const ScaleFmtHost& fa, const ScaleFmtHost& fb, int elem)
 {
-    if (int4)
-        return (exact_in_f16(fa) && exact_in_f16(fb)) || (int4_exact_in_bf16(fa) && int4_exact_in_bf16(fb));
-    return (exact_in_f16(fa) && exact_in_f16(fb)) || (exact_in_bf16(fa) && exact_in_bf16(fb));
+    switch (elem) {
+    case 1:
+        if (int4_exact_in_bf16(fa) && int4_exact_in_bf16(fb)) return 1;
+        return exact_in_f16(fa) && exact_in_f16(fb) ? 2 : 0;
+    case 2:
+        return fp8_exact_in_bf16(fa) && fp8_exact_in_bf16(fb) ? 1 : 0;
+    case 3:
+        if (int8_exact_in_bf16(fa) && int8_exact_in_bf16(fb)) return 1;
+        return is_e4m3(fa) && is_e4m3(fb) ? 2 : 0;
+    default:
+        if (exact_in_f16(fa) && exact_in_f16(fb)) return 2;
+        return exact_in_bf16(fa) && exact_in_bf16(fb) ? 1 : 0;
+    }
 }
 
-// Both operands on the INT4 grid: the exact dequantize path with the integer
-// decode, bf16 when it is exact for both scale formats, else f16.
-template <int BLOCK>
-static hipError_t launch_dq_int4(const GemmLaunch& p, bool f16, hipStream_t s)
+bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, int elem)
+{
+    return dq_type(fa, fb, elem) != 0;
+}
+
+// Operands on the INT4 or an 8-bit grid: the exact dequantize path with the
+// grid's decode, in the 16-bit type dq_type picks.
+template <int BLOCK, int ELEM>
+static hipError_t launch_dq_elem(const GemmLaunch& p, bool f16, hipStream_t s)
 {
     dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
     const size_t sh = sizeof(DqSmem);
-    hipError_t e = f16 ? allow_lds(k_gemm_dq<true, BLOCK, true>, sh) : allow_lds(k_gemm_dq<false, BLOCK, true>, sh);
+    if constexpr (ELEM != 2) {      // FP8 elements have no f16 variant
+        if (f16) {
+            hipError_t e = allow_lds(k_gemm_dq<true, BLOCK, ELEM>, sh);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((k_gemm_dq<true, BLOCK, ELEM>), grid, dim3(kGemmThreads), sh, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipError_t e = allow_lds(k_gemm_dq<false, BLOCK, ELEM>, sh);
     if (e != hipSuccess) return e;
-    if (f16) hipLaunchKernelGGL((k_gemm_dq<true, BLOCK, true>), grid, dim3(kGemmThreads), sh, s, p);
-    else hipLaunchKernelGGL((k_gemm_dq<false, BLOCK, true>), grid, dim3(kGemmThreads), sh, s, p);
+    hipLaunchKernelGGL((k_gemm_dq<false, BLOCK, ELEM>), grid, dim3(kGemmThreads), sh, s, p);
     return hipGetLastError();
+}
+
+template <int ELEM>
+static hipError_t launch_dq_grid(const GemmLaunch& p, bool f16, hipStream_t s)
+{
+    return p.block == 16 ? launch_dq_elem<16, ELEM>(p, f16, s) : launch_dq_elem<32, ELEM>(p, f16, s);
 }
 
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 {
-    if (p.elem_int4) {
-        const bool bf16 = int4_exact_in_bf16(p.fa) && int4_exact_in_bf16(p.fb);
-        const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
-        if (!bf16 && !f16) return hipErrorNotSupported;
-        return p.block == 16 ? launch_dq_int4<16>(p, !bf16, s) : launch_dq_int4<32>(p, !bf16, s);
+    if (p.elem != 0) {
+        const int t = dq_type(p.fa, p.fb, p.elem);
+        if (t == 0) return hipErrorNotSupported;
+        if (p.elem == 1) return launch_dq_grid<1>(p, t == 2, s);
+        if (p.elem == 2) return launch_dq_grid<2>(p, false, s);   // bf16 only
+        return launch_dq_grid<3>(p, t == 2, s);
     }
     const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
     const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);
@@ -1029,7 +1128,6 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // fixed order (deterministic).
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Exact bf16 dequantization of one dword of 8 E2M1 codes with scale s.  The

@@ -123,8 +123,8 @@ typedef enum fp4_transform {
  * symmetric grid -127..127 (two's complement, zero unsigned).  448 or 127
  * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
  * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
- * Quantize and dequantize only: the column-wise and two-orientation calls
- * and the GEMMs return UNSUPPORTED for them. */
+ * Row-wise quantize, dequantize and fp4_gemm take them; the column-wise and
+ * two-orientation calls and fp4_wo_gemm return UNSUPPORTED for them. */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,
@@ -281,7 +281,11 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * compute-bound regime).  Both operands must use the same block size, the
  * same element grid and the same transform (kind and signs; UNSUPPORTED
  * otherwise).  INT4 operands run on the exact dequantize path (bf16 when
- * int * s fits it exactly for both scale formats, else f16).
+ * int * s fits it exactly for both scale formats, else f16); so do the
+ * 8-bit grids: FP8 E4M3 elements in bf16 for scale formats with at most 3
+ * mantissa bits (E8M0, E7M0, E6M1, E5M2, E4M3, UE5M3), INT8 elements in
+ * bf16 for power-of-two scales (E8M0, E7M0) and in f16 for E4M3 scales;
+ * other 8-bit pairings return UNSUPPORTED.
  * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within

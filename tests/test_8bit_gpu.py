@@ -2,8 +2,9 @@
 MXINT8-style symmetric INT8; one byte per element) against the CPU oracle:
 codes, scales and tensor scale bit for bit for every scale encoding, both
 rounding modes, the single-pass and two-pass refreshes and the Hadamard
-transform; dequantization bit for bit; the paths that do not take 8-bit
-grids reject them.  Every call goes through the C ABI.
+transform; dequantization bit for bit; the GEMM within the binary64
+reference's tolerance on every scale pairing it takes; the paths that do not
+take 8-bit grids reject them.  Every call goes through the C ABI.
 """
 import numpy as np
 import pytest
@@ -122,10 +123,145 @@ def test_8bit_quantize_dequantize_roundtrip_bound():
     assert np.all(err <= bound + 1e-30)
 
 
+def _gemm_check(c, a_hat, w_hat, rows=None, tag=""):
+    if rows is not None:
+        a_hat = a_hat[rows]
+    cref, tol = oracle.gemm_ref(a_hat, w_hat)
+    got = c.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[rows]
+    ok = oracle.gemm_check(got, cref, tol)
+    assert ok.all(), f"{tag}: {int((~ok).sum())} of {ok.size} outputs out of tolerance"
+
+
+def _quant_pair(x, block, fmt, elem, *, rounding="nearest", seed=0, rht=None):
+    """GPU and oracle quantization of one operand; codes, scales and tensor
+    scale must agree bit for bit.  Returns (QTensor, oracle binary64 values)."""
+    pol = _policy(fmt)
+    qt = fq.fp4_quantize(to_device(x), block, fmt, amax=pol, rounding=rounding, seed=seed, rht_signs=rht,
+                         element=elem)
+    q, s, g, _ = oracle.quantize_tensor(x, block, fmt, pol, stochastic=rounding == "stochastic", seed=seed,
+                                        nthreads=8, rht_signs=rht, elem=elem)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qt.q), q, f"{elem} {fmt} operand codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} {fmt} operand scales")
+    return qt, oracle.dequantize_f64(q, s, g, block, fmt, elem=elem)
+
+
+# Every scale pairing the exact dequantize GEMM takes for the 8-bit grids:
+# FP8 elements in bf16 for scales with at most 3 mantissa bits, INT8 in bf16
+# for power-of-two scales and in f16 for E4M3 scales.
+GEMM_8BIT = [("fp8_e4m3", "e8m0", 32), ("fp8_e4m3", "e8m0", 16), ("fp8_e4m3", "e4m3", 16),
+             ("fp8_e4m3", "ue5m3", 32), ("fp8_e4m3", "e5m2", 16), ("fp8_e4m3", "e6m1", 32),
+             ("fp8_e4m3", "e7m0", 16), ("int8", "e8m0", 32), ("int8", "e7m0", 16), ("int8", "e4m3", 16),
+             ("int8", "e4m3", 32)]
+
+
+@pytest.mark.parametrize("elem,fmt,block", GEMM_8BIT)
+def test_8bit_gemm(elem, fmt, block):
+    """Ragged M and N (partial 256-row tiles on both sides), K over several
+    64-element stages."""
+    m, n, k = 200, 330, 768
+    qa, a = _quant_pair(_like(m, k, 81, "f32"), block, fmt, elem)
+    qw, w = _quant_pair(_like(n, k, 82, "f32"), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    assert c.shape == (m, n)
+    _gemm_check(c, a, w, tag=f"{elem} {fmt}/{block} gemm")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_8bit_gemm_transform_and_sr(elem):
+    """Both operands Hadamard-rotated with the same signs (the product is
+    that of the rotated operands) and stochastically rounded operands."""
+    fmt, block = ("e8m0", 32)
+    xa, xw = _like(96, 512, 83, "f32"), _like(72, 512, 84, "f32")
+    qa, a = _quant_pair(xa, block, fmt, elem, rht=0x2468ACE1)
+    qw, w = _quant_pair(xw, block, fmt, elem, rht=0x2468ACE1)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    _gemm_check(c, a, w, tag=f"{elem} rht gemm")
+    qa, a = _quant_pair(xa, block, fmt, elem, rounding="stochastic", seed=11)
+    qw, w = _quant_pair(xw, block, fmt, elem, rounding="stochastic", seed=12)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    _gemm_check(c, a, w, tag=f"{elem} sr gemm")
+
+
+@pytest.mark.parametrize("elem,fmt,block", [("fp8_e4m3", "e8m0", 32), ("int8", "e4m3", 16)])
+def test_8bit_gemm_llama_sampled_rows(elem, fmt, block):
+    """Llama-2 7B square projection at M = 8192 (batch 4 x seq 2048), the
+    launch the GEMM timing uses: sampled output rows, including both ends of
+    the first tile and the last row, against the binary64 reference."""
+    shapes = {"a": (8192, 4096), "sq": (4096, 4096)}
+    qa, a = _quant_pair(inputs.llama("a", shapes), block, fmt, elem)
+    qw, w = _quant_pair(inputs.llama("sq", shapes), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([rng.integers(0, 8192, 24), [0, 255, 256, 8191]]))
+    _gemm_check(c, a, w, rows=rows, tag=f"{elem} {fmt} llama sq")
+
+
+@pytest.mark.parametrize("elem,fmt", [("fp8_e4m3", "e8m0"), ("int8", "e8m0"), ("int8", "e4m3")])
+def test_8bit_gemm_every_code(elem, fmt):
+    """Every element code through the GEMM's decode, subnormals and signed
+    zeros included: A holds all 256 codes (the two FP8 NaN codes replaced)
+    with mixed block scales, W selects one column per output
+    (W[n, k] = 1 if k == n, one scale of 1), so C[m, n] is the bf16 rounding
+    of A's value at (m, n) times the tensor scales."""
+    k = 256
+    codes = np.arange(256, dtype=np.uint8)
+    if elem == "fp8_e4m3":
+        codes[(codes & 0x7F) == 0x7F] = 0x00
+    q_a = np.stack([codes, codes[::-1], np.roll(codes, 77)])
+    rng = np.random.default_rng(23)
+    block = 32 if fmt == "e8m0" else 16
+    if fmt == "e8m0":
+        s_a = rng.integers(110, 145, (3, k // block), dtype=np.uint8)
+        one, g_a, pol = 127, 1.0, "none"
+    else:
+        s_a = rng.integers(0, 0x7F, (3, k // block), dtype=np.uint8)
+        one, g_a, pol = 0x38, 0.0625, "current"   # a power of two: g * acc stays exact
+    q_w = np.zeros((k, k), dtype=np.uint8)
+    q_w[np.arange(k), np.arange(k)] = 0x38 if elem == "fp8_e4m3" else 1
+    s_w = np.full((k, k // block), one, dtype=np.uint8)
+
+    def qt(q, s, g):
+        return fq.QTensor(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(),
+                          torch.tensor([g, 0.0], dtype=torch.float32).cuda(), q.shape[0], k, block, fmt, amax=pol,
+                          element=elem)
+    c = fq.fp4_gemm(qt(q_a, s_a, g_a), qt(q_w, s_w, 1.0))
+    torch.cuda.synchronize()
+    a_hat = oracle.dequantize_f64(q_a, s_a, np.float32(g_a), block, fmt, elem=elem)
+    w_hat = oracle.dequantize_f64(q_w, s_w, np.float32(1.0), block, fmt, elem=elem)
+    assert np.array_equal(w_hat, np.eye(k))
+    want = oracle.round_to_bf16(a_hat)
+    got = c.float().cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (f"{elem} {fmt}: {len(bad)} outputs differ; first {tuple(bad[0])}: got "
+                           f"{got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}")
+
+
+@pytest.mark.parametrize("elem,fmt", [("fp8_e4m3", "e3m4"), ("fp8_e4m3", "e1m6"), ("int8", "ue5m3"),
+                                      ("int8", "e3m4"), ("int8", "e5m2")])
+def test_8bit_gemm_inexact_pairing_rejected(elem, fmt):
+    """Scale formats whose products with the grid's elements no 16-bit type
+    holds exactly are refused, not rounded."""
+    xd = to_device(_like(64, 256, 85, "f32"))
+    q = fq.fp4_quantize(xd, 16, fmt, element=elem)
+    with pytest.raises(fq.Fp4Error) as e:
+        fq.fp4_gemm(q, q)
+    assert e.value.status == -2
+
+
 def test_8bit_rejected_elsewhere():
     xd = to_device(_like(64, 256, 74, "f32"))
     q8 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element="int8")
-    for call in (lambda: fq.fp4_gemm(q8, q8),
+    f8 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element="fp8_e4m3")
+    f4 = fq.fp4_quantize(xd, 32, "e8m0", amax="none")
+    for call in (lambda: fq.fp4_gemm(q8, f8),
+                 lambda: fq.fp4_gemm(f8, f4),
                  lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q8),
                  lambda: fq.fp4_quantize_transposed(xd, 32, "e8m0", amax="none", element="int8"),
                  lambda: fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element="int8")):
