@@ -190,9 +190,17 @@ __device__ __forceinline__ float int4_value(uint32_t nib) { return (float)((int3
 // ---------------------------------------------------------------------------
 constexpr ScaleFmt kFp8E4M3{4, 3, 7, 0x7E, 448.0f, 0};
 
-__device__ __forceinline__ uint32_t fp8_rtn_code(float v)
+// Four RTN codes, element k in byte k: clamp to the largest finite value,
+// then the hardware OCP E4M3 conversion (nearest-even, subnormals, sign of
+// zero kept): on every finite input the nearest-even E4M3 encoding that
+// saturates at 448.
+__device__ __forceinline__ uint32_t fp8_rtn_pack4(float v0, float v1, float v2, float v3)
 {
-    return scale_encode_exmy(__builtin_fabsf(v), kFp8E4M3) | ((f_bits(v) >> 24) & 0x80u);
+    const float c0 = __builtin_amdgcn_fmed3f(v0, -448.0f, 448.0f), c1 = __builtin_amdgcn_fmed3f(v1, -448.0f, 448.0f);
+    const float c2 = __builtin_amdgcn_fmed3f(v2, -448.0f, 448.0f), c3 = __builtin_amdgcn_fmed3f(v3, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+    return (uint32_t)w;
 }
 
 // Stochastic: in the binade e of |v| (e >= -6; below 2^-6 the subnormal

@@ -505,9 +505,15 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
                     const uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
                     c[k] = ELEM == 2 ? fp8_sr_code(v[k], r16) : int8_sr_code(v[k], r16);
                 }
+            } else if (ELEM == 2) {
+                // the hardware OCP E4M3 conversion (nearest-even, sign kept)
+                // after the saturating clamp to +-448
+                const u32x2 pk{fp8_rtn_pack4(v[0], v[1], v[2], v[3]), fp8_rtn_pack4(v[4], v[5], v[6], v[7])};
+                if (u < a.nunits) __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(a.q) + u);
+                continue;
             } else {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) c[k] = ELEM == 2 ? fp8_rtn_code(v[k]) : int8_rtn_code(v[k]);
+                for (int k = 0; k < 8; ++k) c[k] = int8_rtn_code(v[k]);
             }
             const u32x2 pk{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                            c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};

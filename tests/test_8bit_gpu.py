@@ -72,6 +72,41 @@ def test_8bit_quantize_parity(elem, fmt, block, dtype, rounding):
            tag=f"{elem} {fmt}/{block}/{dtype}/{rounding}")
 
 
+def _e4m3_values():
+    """The 127 non-negative finite E4M3 values (codes 0x00..0x7E), from the
+    format's definition: bias 7, 3 mantissa bits, subnormals below 2^-6."""
+    out = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        out.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+def test_fp8_rtn_every_midpoint():
+    """Nearest-even FP8 encoding at every decision point: each E4M3 value,
+    each midpoint between neighbours (ties to even) and the binary32 values
+    on either side of it, the saturation range (448, 512) and both signs.
+    Every block holds 256, so its E8M0 scale is exactly 1 and the encoder
+    sees the values unchanged."""
+    q = _e4m3_values()
+    mid = (q[:-1] + q[1:]) / 2
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    vals = np.concatenate([f32(q), f32(mid), np.nextafter(f32(mid), f32(np.inf)),
+                           np.nextafter(f32(mid), f32(-np.inf)),
+                           f32([448.5, 449, 463.99, 464, 464.01, 479, 480, 500, 511.99])])
+    vals = np.concatenate([vals, -vals])
+    per = 31
+    nblk = -(-vals.size // per)
+    vals = np.concatenate([vals, np.zeros(nblk * per - vals.size, dtype=np.float32)])
+    blocks = np.concatenate([np.full((nblk, 1), 256.0, dtype=np.float32), vals.reshape(nblk, per)], axis=1)
+    cols = 512
+    nblk_pad = -(-nblk // (cols // 32)) * (cols // 32)
+    blocks = np.concatenate([blocks, np.tile(blocks[:1], (nblk_pad - nblk, 1))])
+    x = np.ascontiguousarray(blocks.reshape(-1, cols))
+    qt = _check(x, 32, "e8m0", "none", "fp8_e4m3", tag="fp8 midpoints")
+    assert np.all(host(qt.scales) == 127)
+
+
 @pytest.mark.parametrize("elem", ELEMS)
 def test_8bit_full_size_two_pass_and_transform(elem):
     x = inputs.sweep()
