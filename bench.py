@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "7c3c67a305b084183a250e04f04e8cbb1203d39d99696bd4970d64b2437f700b",
-    "read_bytes": 33784653,
+    "sha256": "ebbb284ef3b64238cae500913a3dc73255fa3a9b4490bbc56b357c66b55c911d",
+    "read_bytes": 33787637,
     "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
