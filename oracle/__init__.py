@@ -44,8 +44,8 @@ FORMATS = {
     "e8m0": (8, 0, 0),
 }
 
-ELEMS = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3}
-ELEM_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8}
+ELEMS = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3, "fp6_e2m3": 4, "fp6_e3m2": 5, "int6": 6}
+ELEM_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8, "fp6_e2m3": 6, "fp6_e3m2": 6, "int6": 6}
 
 _lib = None
 
@@ -405,7 +405,9 @@ def quantize_tensor(x: np.ndarray, block: int, fmt: str, policy: str, *, state: 
     elem: "e2m1" (FP4), "int4" (the integer grid -7..7, two's-complement
     nibbles; quant_prune_distill/574 "Метод": NVINT4 / MXINT4), or the 8-bit
     grids "fp8_e4m3" and "int8" (-127..127), one byte per element (MXFP8 /
-    MXINT8).
+    MXINT8), or the 6-bit grids "fp6_e2m3", "fp6_e3m2" and "int6" (-31..31),
+    packed as a little-endian bit stream of 6 bits per element (MXFP6 /
+    MXINT6).
     Returns (q, scales, g, amax_used)."""
     if rht_signs is not None:
         x = rht_forward(x, block, rht_signs)

@@ -151,7 +151,15 @@ static int int4_code(int negative, int mag) { return negative ? ((16 - mag) & 0x
  * magnitudes (largest 448), nearest-even and saturating, the sign bit kept
  * (also for zero, as for E2M1); INT8 takes the symmetric grid -127..127 as
  * two's complement (0x80 never produced, zero unsigned). */
-static int elem_bits(int elem) { return elem >= 2 ? 8 : 4; }
+/* 6-bit grids: 4 = FP6 E2M3, 5 = FP6 E3M2, 6 = INT6.  [P-INT]
+ * quant_prune_distill/574 "Метод" also pairs MXFP6 with MXINT6 (groups of
+ * 32, E8M0 scales) and gives no element encoding.  Reading: the two FP6
+ * element formats of the OCP MX family (sign bit on top, bias 1 / 3,
+ * subnormals, every code finite: largest magnitudes 7.5 / 28), and INT6 on
+ * the symmetric grid -31..31 as six-bit two's complement.  Codes are packed
+ * little-endian as a bit stream: element c of a row occupies bits 6c ..
+ * 6c + 5 of the row's cols * 3 / 4 bytes. */
+static int elem_bits(int elem) { return elem >= 4 ? 6 : elem >= 2 ? 8 : 4; }
 
 /* largest element magnitude of a grid */
 static float elem_max(int elem)
@@ -160,6 +168,9 @@ static float elem_max(int elem)
     case 0: return 6.0f;
     case 1: return 7.0f;
     case 2: return 448.0f;
+    case 4: return 7.5f;
+    case 5: return 28.0f;
+    case 6: return 31.0f;
     default: return 127.0f;
     }
 }
@@ -171,6 +182,8 @@ static int elem_emax(int elem)
     switch (elem) {
     case 2: return 8;
     case 3: return 6;
+    case 5: return 4;
+    case 6: return 4;
     default: return 2;
     }
 }
@@ -202,6 +215,48 @@ OR_EXPORT double or_int8_decode(int code)
 {
     code &= 0xFF;
     return (double)(code >= 128 ? code - 256 : code);
+}
+
+/* INT6 magnitude: nearest integer of |v| (ties to even), saturating at 31;
+ * stochastic as INT8 with spacing 1. */
+OR_EXPORT int or_int6_rtn(float v)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 31.0) return 31;
+    double lo = floor(a), frac = a - lo;
+    int m = (int)lo;
+    if (frac > 0.5 || (frac == 0.5 && (m & 1))) m += 1;
+    return m;
+}
+
+OR_EXPORT int or_int6_sr(float v, uint32_t r16)
+{
+    double a = fabs((double)v);
+    if (a != a) return 0;
+    if (a >= 31.0) return 31;
+    int lo = (int)floor(a);
+    double frac = a - (double)lo;
+    double u = (double)(r16 & 0xFFFFu) / 65536.0;
+    return (u < frac) ? lo + 1 : lo;
+}
+
+OR_EXPORT double or_int6_decode(int code)
+{
+    code &= 0x3F;
+    return (double)(code >= 32 ? code - 64 : code);
+}
+
+/* FP6 element value of a 6-bit code (sign bit 5): E2M3 (elem 4) has
+ * exponent bias 1 and 3 mantissa bits, E3M2 (elem 5) bias 3 and 2; an
+ * exponent field of 0 is subnormal; no code is reserved. */
+OR_EXPORT double or_fp6_decode(int code, int elem)
+{
+    const int mb = elem == 4 ? 3 : 2, bias = elem == 4 ? 1 : 3;
+    const int mag = code & 0x1F, e = mag >> mb, m = mag & ((1 << mb) - 1);
+    const double frac = ldexp((double)m, -mb);
+    const double v = e == 0 ? ldexp(frac, 1 - bias) : ldexp(1.0 + frac, e - bias);
+    return (code & 0x20) ? -v : v;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -442,12 +497,19 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
     double tab[256];
     decode_table(J->eb, J->mb, J->sg, tab);
     const int ncodes = fmt_ncodes(J->eb, J->mb, J->sg);
-    double etab[256];                               /* FP8 E4M3 element magnitudes */
-    decode_table(4, 3, 1, etab);
-    const int encodes = fmt_ncodes(4, 3, 1);
+    double etab[256];                               /* FP8 E4M3 / FP6 element magnitudes */
+    int encodes;
+    if (J->elem == 4 || J->elem == 5) {
+        for (int c = 0; c < 32; ++c) etab[c] = or_fp6_decode(c, J->elem);
+        encodes = 32;
+    } else {
+        decode_table(4, 3, 1, etab);
+        encodes = fmt_ncodes(4, 3, 1);
+    }
     const int64_t qstride = J->cols * elem_bits(J->elem) / 8;
     for (int64_t r = ra; r < rb; ++r) {
         uint8_t* qrow = J->q + (r - J->row0) * qstride;
+        if (elem_bits(J->elem) == 6) memset(qrow, 0, (size_t)qstride);
         uint8_t* srow = J->scales + (r - J->row0) * nb;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t c0 = b * J->block;
@@ -485,14 +547,16 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
                         switch (J->elem) {
                         case 0: mag = or_e2m1_sr(v, r16); break;
                         case 1: mag = or_int4_sr(v, r16); break;
-                        case 2: mag = fp8_sr(etab, encodes, v, r16); break;
+                        case 2: case 4: case 5: mag = fp8_sr(etab, encodes, v, r16); break;
+                        case 6: mag = or_int6_sr(v, r16); break;
                         default: mag = or_int8_sr(v, r16); break;
                         }
                     } else {
                         switch (J->elem) {
                         case 0: mag = or_e2m1_rtn(v); break;
                         case 1: mag = or_int4_rtn(v); break;
-                        case 2: mag = encode_nearest(etab, encodes, fabsf(v)); break;
+                        case 2: case 4: case 5: mag = encode_nearest(etab, encodes, fabsf(v)); break;
+                        case 6: mag = or_int6_rtn(v); break;
                         default: mag = or_int8_rtn(v); break;
                         }
                     }
@@ -503,9 +567,16 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
                 case 0: code = (neg << 3) | mag; break;
                 case 1: code = int4_code(neg, mag); break;
                 case 2: code = (neg << 7) | mag; break;
+                case 4: case 5: code = (neg << 5) | mag; break;
+                case 6: code = neg ? ((64 - mag) & 0x3F) : mag; break;
                 default: code = neg ? ((256 - mag) & 0xFF) : mag; break;
                 }
-                if (elem_bits(J->elem) == 8) qrow[col] = (uint8_t)code;
+                if (elem_bits(J->elem) == 6) {
+                    const int64_t bit = 6 * col;
+                    const int sh = (int)(bit & 7);
+                    qrow[bit >> 3] |= (uint8_t)(code << sh);
+                    if (sh > 2) qrow[(bit >> 3) + 1] |= (uint8_t)(code >> (8 - sh));
+                } else if (elem_bits(J->elem) == 8) qrow[col] = (uint8_t)code;
                 else if ((col & 1) == 0) qrow[col >> 1] = (uint8_t)code;
                 else qrow[col >> 1] |= (uint8_t)(code << 4);
             }
@@ -542,7 +613,7 @@ OR_EXPORT int or_quantize_elem(const void* x, int is_bf16, int64_t rows, int64_t
                                int stochastic, uint64_t seed, uint64_t offset,
                                int64_t row0, int64_t row1, uint8_t* q, uint8_t* scales, int nthreads, int elem)
 {
-    if (elem < 0 || elem > 3) return -1;
+    if (elem < 0 || elem > 6) return -1;
     if (!x || !q || !scales || rows < 0 || cols < 0 || ld < cols) return -1;
     if (block != 16 && block != 32) return -1;
     if (cols % block) return -1;
@@ -588,6 +659,8 @@ static double elem_decode(int code, int elem)
     case 0: return or_e2m1_decode(code);
     case 1: return or_int4_decode(code);
     case 2: return or_scale_decode(4, 3, 1, code);
+    case 4: case 5: return or_fp6_decode(code, elem);
+    case 6: return or_int6_decode(code);
     default: return or_int8_decode(code);
     }
 }
@@ -595,6 +668,14 @@ static double elem_decode(int code, int elem)
 static int elem_code_at(const uint8_t* q, int64_t r, int64_t c, int64_t cols, int elem)
 {
     if (elem_bits(elem) == 8) return q[r * cols + c];
+    if (elem_bits(elem) == 6) {
+        const uint8_t* row = q + r * (cols * 3 / 4);
+        const int64_t bit = 6 * c;
+        const int sh = (int)(bit & 7);
+        int v = row[bit >> 3] >> sh;
+        if (sh > 2) v |= row[(bit >> 3) + 1] << (8 - sh);
+        return v & 0x3F;
+    }
     uint8_t byte = q[r * (cols / 2) + c / 2];
     return (c & 1) ? (byte >> 4) : (byte & 0xF);
 }
@@ -615,7 +696,7 @@ OR_EXPORT int or_dequantize_elem(const uint8_t* q, const uint8_t* scales, float 
                                  int out_bf16, void* y, int64_t ld_y, int elem)
 {
     if (!q || !scales || !y || (block != 16 && block != 32) || cols % block || ld_y < cols) return -1;
-    if (!fmt_valid(eb, mb, sg)) return -1;
+    if (!fmt_valid(eb, mb, sg) || elem < 0 || elem > 6) return -1;
     const int64_t nb = cols / block;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
@@ -716,7 +797,7 @@ OR_EXPORT int or_dequantize_f64_elem(const uint8_t* q, const uint8_t* scales, fl
                                      int block, int eb, int mb, int sg, double* y, int elem)
 {
     if (!q || !scales || !y || (block != 16 && block != 32) || cols % block) return -1;
-    if (!fmt_valid(eb, mb, sg)) return -1;
+    if (!fmt_valid(eb, mb, sg) || elem < 0 || elem > 6) return -1;
     const int64_t nb = cols / block;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {

@@ -951,3 +951,135 @@ def test_8bit_dequantize_exact_product(elem):
                 e = float(np.array([q[r, c]], dtype=np.uint8).view(np.int8)[0])
             sv = oracle.scale_decode("e4m3", int(s[r, c // 16]))
             assert y[r, c] == np.float32(np.float32(np.float32(e) * np.float32(sv)) * g)
+
+
+# ---------------------------------------------------------------------------
+# 6-bit MX element grids (MXFP6 with FP6 E2M3 / E3M2 elements, MXINT6)
+# ---------------------------------------------------------------------------
+def _fp6_values(elem):
+    """Signed values of the 64 FP6 codes, written out from the format
+    definitions: E2M3 = 1 sign, 2 exponent (bias 1), 3 mantissa bits; E3M2 =
+    1 sign, 3 exponent (bias 3), 2 mantissa bits; exponent 0 is subnormal and
+    every code is finite."""
+    eb, mb, bias = (2, 3, 1) if elem == "fp6_e2m3" else (3, 2, 3)
+    out = []
+    for code in range(64):
+        mag = code & 31
+        e, m = mag >> mb, mag & ((1 << mb) - 1)
+        v = Fraction(m, 1 << mb) * Fraction(2) ** (1 - bias) if e == 0 else \
+            (1 + Fraction(m, 1 << mb)) * Fraction(2) ** (e - bias)
+        out.append(-v if code & 32 else v)
+    return out
+
+
+def _unpack6(q, cols):
+    """Independent bit-stream unpack: element c of a row at bits 6c..6c+5
+    (little-endian over the row's bytes)."""
+    out = np.zeros((q.shape[0], cols), dtype=np.int64)
+    for r in range(q.shape[0]):
+        big = int.from_bytes(bytes(q[r]), "little")
+        for c in range(cols):
+            out[r, c] = (big >> (6 * c)) & 63
+    return out
+
+
+def test_fp6_format_facts():
+    for elem, top, sub, norm in [("fp6_e2m3", 7.5, 0.125, 1.0), ("fp6_e3m2", 28.0, 0.0625, 0.25)]:
+        vals = _fp6_values(elem)
+        pos = sorted(set(v for v in vals[:32]))
+        assert len(pos) == 32 and pos[0] == 0 and max(pos) == top
+        assert pos[1] == sub                     # smallest subnormal
+        assert min(v for v in pos if v >= norm) == norm
+
+
+@pytest.mark.parametrize("elem", ["fp6_e2m3", "fp6_e3m2"])
+def test_fp6_dequantize_decodes_every_code(elem):
+    # every code in a row with E8M0 scale 1: the oracle's values are the
+    # definition's
+    q_codes = np.arange(64, dtype=np.int64).reshape(1, 64)
+    big = 0
+    for c in range(64):
+        big |= int(q_codes[0, c]) << (6 * c)
+    q = np.frombuffer(big.to_bytes(48, "little"), dtype=np.uint8).reshape(1, 48).copy()
+    s = np.full((1, 2), 127, dtype=np.uint8)
+    y = oracle.dequantize_f64(q, s, 1.0, 32, "e8m0", elem=elem)
+    want = [float(v) for v in _fp6_values(elem)]
+    assert np.array_equal(y[0], np.array(want))
+
+
+@pytest.mark.parametrize("elem,top,emax", [("fp6_e2m3", 6.0, 2), ("fp6_e3m2", 20.0, 4)])
+def test_fp6_rtn_is_brute_force_nearest(elem, top, emax):
+    # blocks whose maximum is in [2^emax, 2^(emax+1)) get the E8M0 scale 1;
+    # each element must be the nearest FP6 value (ties to the even code,
+    # saturating at the top), found by brute force over the 32 magnitudes
+    rng = np.random.default_rng(91)
+    vals = _fp6_values(elem)
+    pos = [float(v) for v in vals[:32]]
+    mids = [(pos[i] + pos[i + 1]) / 2 for i in range(31)]
+    extra = np.array(mids + pos + [pos[-1] * 1.01, 0.999 * 2.0 ** (emax + 1)], dtype=np.float32)
+    x = rng.uniform(-2 ** (emax + 1), 2 ** (emax + 1), (8, 256)).astype(np.float32)
+    flat = x.reshape(-1)
+    flat[1:1 + extra.size] = extra
+    flat[300:300 + extra.size] = -extra
+    x[:, ::32] = np.float32(top)
+    q, s, g, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem=elem)
+    assert np.all(s == 127) and g == 1.0
+    codes = _unpack6(q, 256)
+    for r in range(8):
+        for c in range(256):
+            a = abs(float(x[r, c]))
+            d = [abs(a - p) for p in pos]
+            best = min(d)
+            cands = [i for i in range(32) if d[i] == best]
+            mag = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+            want = mag | (32 if np.signbit(x[r, c]) else 0)
+            assert codes[r, c] == want, (r, c, x[r, c])
+
+
+def test_int6_rtn_and_layout():
+    rng = np.random.default_rng(92)
+    x = rng.uniform(-32, 32, (8, 256)).astype(np.float32)
+    x[:, ::32] = np.float32(20.0)                        # E8M0 offset 4: scale 1
+    x[0, 1:5] = [2.5, -3.5, 31.6, -31.9]
+    q, s, g, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem="int6")
+    assert np.all(s == 127) and q.shape == (8, 192)
+    codes = _unpack6(q, 256)
+    want = np.clip(np.rint(x.astype(np.float64)), -31, 31).astype(np.int64) & 63
+    assert np.array_equal(codes, want)
+    y = oracle.dequantize_f64(q, s, 1.0, 32, "e8m0", elem="int6")
+    assert np.array_equal(y, np.clip(np.rint(x.astype(np.float64)), -31, 31))
+
+
+@pytest.mark.parametrize("elem,emax", [("fp6_e2m3", 2), ("fp6_e3m2", 4), ("int6", 4)])
+def test_6bit_e8m0_offset_closed_form(elem, emax):
+    rng = np.random.default_rng(93)
+    x = (rng.standard_normal((16, 256)) * np.exp(rng.uniform(-6, 6, (16, 1)))).astype(np.float32)
+    _, s, _, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem=elem)
+    amax = np.abs(x).reshape(16, 8, 32).max(axis=2).astype(np.float64)
+    sc = 2.0 ** (s.astype(np.float64) - 127)
+    assert np.all((2.0 ** emax * sc <= amax) & (amax < 2.0 ** (emax + 1) * sc))
+
+
+@pytest.mark.parametrize("elem,v,lo,hi", [("fp6_e2m3", 2.6, 2.5, 2.75), ("fp6_e3m2", 11.0, 10.0, 12.0),
+                                          ("int6", 7.3, 7.0, 8.0)])
+def test_6bit_sr_between_neighbours(elem, v, lo, hi):
+    x = np.full((64, 256), v, dtype=np.float32)
+    x[:, ::32] = np.float32(6.0 if elem == "fp6_e2m3" else 20.0)
+    q, s, _, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem=elem, stochastic=True, seed=5)
+    assert np.all(s == 127)
+    y = oracle.dequantize_f64(q, s, 1.0, 32, "e8m0", elem=elem)
+    mid = y[:, [c for c in range(256) if c % 32]]
+    assert set(np.unique(mid)) <= {lo, hi}
+    frac_up = float((mid == hi).mean())
+    assert abs(frac_up - (np.float64(np.float32(v)) - lo) / (hi - lo)) < 0.02
+
+
+@pytest.mark.parametrize("elem,qmax", [("fp6_e2m3", 7.5), ("fp6_e3m2", 28.0), ("int6", 31.0)])
+def test_6bit_tensor_max_maps_to_grid_max(elem, qmax):
+    x = _sweep_like(32, 256, 94, bf16=False)
+    q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "current", elem=elem)
+    assert g == np.float32(a) / (np.float32(qmax) * np.float32(448.0))
+    y = oracle.dequantize_f64(q, s, 1.0, 16, "e4m3", elem=elem)
+    r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert s[r, c // 16] == 0x7E
+    assert y[r, c] == (qmax if x[r, c] > 0 else -qmax) * 448.0
