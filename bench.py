@@ -353,15 +353,17 @@ def leg_int4(torch, fq, inputs, xs):
 
 
 def leg_8bit(torch, fq, inputs, xs):
-    """The 8-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
-    elements) and MXINT8-style (E8M0 block 32), one byte per element, and
+    """The 8- and 6-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
+    elements), MXINT8-style (E8M0 block 32), one byte per element, and
+    MXFP6 / MXINT6-style (six bits per element), and
     the GEMM at the Llama-2 7B up-projection shape on the exact dequantize
     path (MXFP8 in bf16; INT8 elements with E4M3 block-16 scales in f16)."""
     rows, cols = xs[0].shape
     res = {}
     n = rows * cols
-    algo = n * 2 + n + n // 32 + 8
-    for elem in ("fp8_e4m3", "int8"):
+    names = {"fp8_e4m3": "mxfp8", "int8": "mxint8", "fp6_e2m3": "mxfp6_e2m3", "fp6_e3m2": "mxfp6_e3m2",
+             "int6": "mxint6"}
+    for elem, name in names.items():
         outs = [fq.QTensor.empty(rows, cols, 32, "e8m0", amax="none", element=elem) for _ in xs]
 
         def rec(_):
@@ -369,9 +371,10 @@ def leg_8bit(torch, fq, inputs, xs):
                 fq.fp4_quantize(xs[j], 32, "e8m0", amax="none", out=outs[j], element=elem)
         gs = GraphSet(torch, 1, rec)
         ms = time_graphs(torch, gs, 20, 3) / len(xs)
-        res[f"mx{'fp8' if elem == 'fp8_e4m3' else 'int8'}_quantize"] = {
-            "us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        nb = n * 2 + n * fq.ELEMENT_BITS[elem] // 8 + n // 32 + 8
+        res[f"{name}_quantize"] = {
+            "us_per_call": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del gs, outs
     m, n, k = 8192, 11008, 4096
     for name, (elem, fmt, block, pol) in {"mxfp8": ("fp8_e4m3", "e8m0", 32, "none"),
@@ -391,7 +394,8 @@ def leg_8bit(torch, fq, inputs, xs):
                                   "frac_bf16_peak": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4),
                                   "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)}
         del a, w, qa, qw, c, gs
-    res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each), RTN; "
+    res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each) and "
+                       "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN; "
                        "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8 and INT8 with E4M3 block-16 scales")
     return res
 

@@ -25,8 +25,8 @@ SCALE_FORMATS = {"e4m3": 0, "ue5m3": 1, "e3m4": 2, "e1m6": 3, "e8m0": 4, "e2m5":
 ROUNDING = {"nearest": 0, "stochastic": 1}
 AMAX = {"none": 0, "current": 1, "delayed": 2}
 TRANSFORM = {"none": 0, "rht": 1}
-ELEMENT = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3}
-ELEMENT_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8}
+ELEMENT = {"e2m1": 0, "int4": 1, "fp8_e4m3": 2, "int8": 3, "fp6_e2m3": 4, "fp6_e3m2": 5, "int6": 6}
+ELEMENT_BITS = {"e2m1": 4, "int4": 4, "fp8_e4m3": 8, "int8": 8, "fp6_e2m3": 6, "fp6_e3m2": 6, "int6": 6}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 
 FP4_OK = 0

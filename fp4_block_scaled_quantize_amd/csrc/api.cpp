@@ -59,7 +59,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 103; }
+int32_t fp4_version(void) { return 104; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -125,6 +125,9 @@ fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool elem_is_8bit(int32_t e) { return e == FP4_ELEM_FP8_E4M3 || e == FP4_ELEM_INT8; }
+static bool elem_is_6bit(int32_t e) { return e >= FP4_ELEM_FP6_E2M3 && e <= FP4_ELEM_INT6; }
+// the 8- and 6-bit grids: row-wise quantize and dequantize (and the GEMM for 8 bits)
+static bool elem_is_wide(int32_t e) { return elem_is_8bit(e) || elem_is_6bit(e); }
 
 static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
 {
@@ -138,11 +141,13 @@ static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
         return FP4_ERR_INVALID_ARG;
     if (!scale_fmt_params(t->fmt.scale, f)) return FP4_ERR_INVALID_ARG;
     if (t->fmt.transform != FP4_TRANSFORM_NONE && t->fmt.transform != FP4_TRANSFORM_RHT) return FP4_ERR_INVALID_ARG;
-    if (t->fmt.element < FP4_ELEM_E2M1 || t->fmt.element > FP4_ELEM_INT8) return FP4_ERR_INVALID_ARG;
+    if (t->fmt.element < FP4_ELEM_E2M1 || t->fmt.element > FP4_ELEM_INT6) return FP4_ERR_INVALID_ARG;
     if (t->rows < 0 || t->cols < 0) return FP4_ERR_SHAPE;
     if (t->cols % t->fmt.block) return FP4_ERR_SHAPE;
-    // codes leave as 4-byte pieces (4-bit grids) or 8-byte pieces (8-bit grids)
-    if (((uintptr_t)t->q & (elem_is_8bit(t->fmt.element) ? 7u : 3u)) != 0) return FP4_ERR_ALIGN;
+    // codes leave as 4-byte pieces (4-bit grids), 8-byte pieces (8-bit
+    // grids) or 2-byte pieces at 6-byte steps (6-bit grids; 8-byte alignment
+    // asked for as for 8 bits)
+    if (((uintptr_t)t->q & (elem_is_wide(t->fmt.element) ? 7u : 3u)) != 0) return FP4_ERR_ALIGN;
     if ((t->rows * (t->cols / 8)) >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
     return FP4_OK;
 }
@@ -205,7 +210,7 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     // x is [out->cols, out->rows]: its rows are the blocked dimension
-    if (elem_is_8bit(out->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    if (elem_is_wide(out->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (out->rows % 8) return FP4_ERR_SHAPE;
     if (out->rows * out->cols != 0) {
         if (ld_x < out->rows) return FP4_ERR_SHAPE;
@@ -262,7 +267,7 @@ fp4_status fp4_quantize_both(const void* x, int32_t x_dtype, int64_t ld_x, fp4_t
         return FP4_ERR_UNSUPPORTED;
     // a transform would run along different axes, with different maxima
     if (fr.transform != FP4_TRANSFORM_NONE || fl.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;
-    if (elem_is_8bit(fr.element)) return FP4_ERR_UNSUPPORTED;
+    if (elem_is_wide(fr.element)) return FP4_ERR_UNSUPPORTED;
     if (!x && rowwise->rows * rowwise->cols != 0) return FP4_ERR_INVALID_ARG;
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
@@ -346,7 +351,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
     // transformed operands multiply to the same product only when both carry
     // the same transform along K
-    if (a->fmt.element != b->fmt.element) return FP4_ERR_UNSUPPORTED;
+    if (a->fmt.element != b->fmt.element || elem_is_6bit(a->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != b->fmt.transform) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != FP4_TRANSFORM_NONE && a->fmt.transform_signs != b->fmt.transform_signs)
         return FP4_ERR_UNSUPPORTED;
@@ -379,7 +384,7 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (!x || !y) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
-    if (elem_is_8bit(w->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    if (elem_is_wide(w->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     // the kernel addresses W and x with 32-bit byte/element offsets

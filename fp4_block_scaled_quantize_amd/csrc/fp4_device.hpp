@@ -240,6 +240,86 @@ __device__ __forceinline__ uint32_t int8_sr_code(float v, uint32_t r16)
 __device__ __forceinline__ float int8_value(uint32_t b) { return (float)(int32_t)(int8_t)(b & 0xFFu); }
 
 // ---------------------------------------------------------------------------
+// 6-bit MX elements (quant_prune_distill/574 "Метод": MXFP6 / MXINT6).
+// Reading: the OCP FP6 element formats E2M3 (bias 1, largest 7.5) and E3M2
+// (bias 3, largest 28), sign bit 5, subnormals, every code finite; INT6 on
+// the symmetric grid -31..31 (six-bit two's complement).  Element c of a
+// row sits at bits 6c .. 6c + 5 of the row (a little-endian bit stream).
+// ---------------------------------------------------------------------------
+constexpr ScaleFmt kFp6E2M3{2, 3, 1, 0x1F, 7.5f, 0};
+constexpr ScaleFmt kFp6E3M2{3, 2, 3, 0x1F, 28.0f, 0};
+
+__device__ __forceinline__ uint32_t fp6_rtn_code(float v, const ScaleFmt& f)
+{
+    return scale_encode_exmy(__builtin_fabsf(v), f) | ((f_bits(v) >> 26) & 0x20u);
+}
+
+// Stochastic, as fp8_sr_code: in the binade e of |v| (at least the
+// subnormal exponent 1 - BIAS) t = |v| 2^(MB - e) is exact, floor(t) is the
+// lower neighbour's significand and ((e + BIAS) << MB) + m - 2^MB its code.
+template <int MB, int BIAS>
+__device__ __forceinline__ uint32_t fp6_sr_code(float v, uint32_t r16, float smax)
+{
+    const float a = __builtin_fabsf(v);
+    const uint32_t sign = (f_bits(v) >> 26) & 0x20u;
+    if (!(a < smax)) return 0x1Fu | sign;
+    const int eu = (int)((f_bits(a) >> 23) & 0xFFu) - 127;
+    const int e = eu > 1 - BIAS ? eu : 1 - BIAS;
+    const float t = __builtin_amdgcn_ldexpf(a, MB - e);
+    const float fl = __builtin_floorf(t);
+    const float frac = t - fl;
+    const uint32_t m = (uint32_t)fl + (((float)r16 < frac * 65536.0f) ? 1u : 0u);
+    const uint32_t code = (uint32_t)((e + BIAS) << MB) + m - (1u << MB);
+    return (code < 0x1Fu ? code : 0x1Fu) | sign;
+}
+
+__device__ __forceinline__ float fp6_value(uint32_t c, const ScaleFmt& f)
+{
+    const float v = scale_decode_exmy(c & 0x1Fu, f);
+    return (c & 0x20u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t int6_rtn_code(float v)
+{
+    return (uint32_t)(int32_t)__builtin_rintf(__builtin_amdgcn_fmed3f(v, -31.0f, 31.0f)) & 0x3Fu;
+}
+
+__device__ __forceinline__ uint32_t int6_sr_code(float v, uint32_t r16)
+{
+    const float a = __builtin_fabsf(v);
+    const float fl = __builtin_floorf(a);
+    const float frac = a - fl;
+    const float up = ((float)r16 < frac * 65536.0f) ? 1.0f : 0.0f;
+    const uint32_t m = (uint32_t)(a >= 31.0f ? 31.0f : fl + up);
+    return (f_bits(v) >> 31) ? ((64u - m) & 0x3Fu) : m;
+}
+
+__device__ __forceinline__ float int6_value(uint32_t c) { return (float)(((int32_t)(c << 26)) >> 26); }
+
+// One element grid's code of v (ELEM 4 FP6 E2M3, 5 FP6 E3M2, 6 INT6).
+template <int ELEM>
+__device__ __forceinline__ uint32_t w6_rtn_code(float v)
+{
+    if constexpr (ELEM == 6) return int6_rtn_code(v);
+    else return fp6_rtn_code(v, ELEM == 4 ? kFp6E2M3 : kFp6E3M2);
+}
+
+template <int ELEM>
+__device__ __forceinline__ uint32_t w6_sr_code(float v, uint32_t r16)
+{
+    if constexpr (ELEM == 6) return int6_sr_code(v, r16);
+    else if constexpr (ELEM == 4) return fp6_sr_code<3, 1>(v, r16, 7.5f);
+    else return fp6_sr_code<2, 3>(v, r16, 28.0f);
+}
+
+template <int ELEM>
+__device__ __forceinline__ float w6_value(uint32_t c)
+{
+    if constexpr (ELEM == 6) return int6_value(c);
+    else return fp6_value(c, ELEM == 4 ? kFp6E2M3 : kFp6E3M2);
+}
+
+// ---------------------------------------------------------------------------
 // wave64 helpers
 // ---------------------------------------------------------------------------
 // Max of non-negative binary32 bit patterns across lane pairs / quads.

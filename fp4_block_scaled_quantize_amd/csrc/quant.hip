@@ -371,14 +371,16 @@ __device__ __forceinline__ float quad_bcast(float v)
 // right after the loads; block maxima, the tensor maximum and the codes all
 // see the transformed values.
 // INT: the INT4 element grid (-7..7) instead of E2M1.
-// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8; the last two
-// one byte per element).
+// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8, 4 FP6 E2M3,
+// 5 FP6 E3M2, 6 INT6; 2 and 3 one byte per element, 4..6 six bits).
 template <typename InT, int BLOCK, bool SR, bool E8M0, bool STRIDED, bool FUSED, bool ROT, int ELEM>
 __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArgs a)
 {
     constexpr bool INT = ELEM == 1;
-    constexpr bool W8 = ELEM >= 2;
-    constexpr float QMAX = ELEM == 0 ? 6.0f : ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : 127.0f;   // grid maximum
+    constexpr bool W8 = ELEM == 2 || ELEM == 3;
+    constexpr bool W6 = ELEM >= 4;
+    constexpr float QMAX = ELEM == 0 ? 6.0f : ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : ELEM == 3 ? 127.0f
+                         : ELEM == 4 ? 7.5f : ELEM == 5 ? 28.0f : 31.0f;   // grid maximum
     constexpr int T = FUSED ? kFThreads : kQThreads;
     constexpr int U = FUSED ? kFUnroll : kQUnroll;
     constexpr int G = BLOCK / 8;                 // lanes per block (2 or 4)
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         for (int k = 1; k < G; ++k) x = (sub == (uint32_t)k) ? bm[k * PER + t] : x;
         uint32_t code;
         if (E8M0) {
-            code = ELEM == 2 ? scale_code_e8m0_emax<8>(x) : ELEM == 3 ? scale_code_e8m0_emax<6>(x) : scale_code_e8m0(x);
+            code = ELEM == 2 ? scale_code_e8m0_emax<8>(x) : ELEM == 3 ? scale_code_e8m0_emax<6>(x)
+                 : (ELEM == 5 || ELEM == 6) ? scale_code_e8m0_emax<4>(x) : scale_code_e8m0(x);
             inv_own[t] = e8m0_inv(code);
         } else {
             code = exmy_scale(x, d, g, a.f, &inv_own[t]);
@@ -494,6 +497,28 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = v[k] * inv[j];
         uint32_t packed;
+        if (W6) {
+            // six bits per element: the unit's 48 bits leave as three
+            // 16-bit stores at byte 6u
+            uint64_t bits = 0;
+            if (SR) {
+                U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    bits |= (uint64_t)w6_sr_code<ELEM>(v[k], (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu) << (6 * k);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) bits |= (uint64_t)w6_rtn_code<ELEM>(v[k]) << (6 * k);
+            }
+            if (u < a.nunits) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(a.q) + 3 * (uint64_t)u;
+                __builtin_nontemporal_store((uint16_t)bits, dst);
+                __builtin_nontemporal_store((uint16_t)(bits >> 16), dst + 1);
+                __builtin_nontemporal_store((uint16_t)(bits >> 32), dst + 2);
+            }
+            continue;
+        }
         if (W8) {
             // one byte per element: eight codes in two dwords
             uint32_t c[8];
@@ -583,6 +608,9 @@ static void launch_q3(const QArgs& a, bool sr, bool e8, bool fused, bool strided
     case 1: launch_q35<InT, BLOCK, 1>(a, sr, e8, fused, strided, rot, blocks, s); break;
     case 2: launch_q35<InT, BLOCK, 2>(a, sr, e8, fused, strided, rot, blocks, s); break;
     case 3: launch_q35<InT, BLOCK, 3>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    case 4: launch_q35<InT, BLOCK, 4>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    case 5: launch_q35<InT, BLOCK, 5>(a, sr, e8, fused, strided, rot, blocks, s); break;
+    case 6: launch_q35<InT, BLOCK, 6>(a, sr, e8, fused, strided, rot, blocks, s); break;
     default: launch_q35<InT, BLOCK, 0>(a, sr, e8, fused, strided, rot, blocks, s); break;
     }
 }
@@ -1221,13 +1249,18 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = blockIdx.x * (kDQThreads / 64) + (threadIdx.x >> 6);
     const uint32_t base = wave * (64u * U);
-    constexpr bool W8 = ELEM >= 2;               // one byte per element
+    constexpr bool W8 = ELEM == 2 || ELEM == 3;  // one byte per element
+    constexpr bool W6 = ELEM >= 4;               // six bits per element
     uint32_t w[U], w2[U], sc[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
         const uint32_t u = base + j * 64 + lane;
         const uint32_t uu = u < nunits ? u : nunits - 1;           // in bounds; not stored
-        if (W8) {
+        if (W6) {
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(q) + 3 * (uint64_t)uu;
+            w[j] = (uint32_t)__builtin_nontemporal_load(src) | ((uint32_t)__builtin_nontemporal_load(src + 1) << 16);
+            w2[j] = (uint32_t)__builtin_nontemporal_load(src + 2);
+        } else if (W8) {
             const u32x2 p2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q) + uu);
             w[j] = p2.x;
             w2[j] = p2.y;
@@ -1247,7 +1280,11 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             float e;
-            if (W8) {
+            if (W6) {
+                // bits 6k .. 6k + 5 of the 48-bit unit (w2 holds bits 32..47)
+                const uint64_t bits = (uint64_t)w[j] | ((uint64_t)w2[j] << 32);
+                e = w6_value<ELEM>((uint32_t)(bits >> (6 * k)) & 0x3Fu);
+            } else if (W8) {
                 const uint32_t b = ((k < 4 ? w[j] : w2[j]) >> (8 * (k & 3))) & 0xFFu;
                 e = ELEM == 2 ? scale_decode_any(b, kFp8E4M3) : int8_value(b);
             } else {
@@ -1307,6 +1344,18 @@ static void launch_dq2(const DequantLaunch& p, uint32_t nunits, const FastDiv& f
     case 3:
         if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 3>(p, nunits, fd, strided, f, s);
         else launch_dq4<OUT_BF16, BLOCK, false, 3>(p, nunits, fd, strided, f, s);
+        break;
+    case 4:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 4>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 4>(p, nunits, fd, strided, f, s);
+        break;
+    case 5:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 5>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 5>(p, nunits, fd, strided, f, s);
+        break;
+    case 6:
+        if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 6>(p, nunits, fd, strided, f, s);
+        else launch_dq4<OUT_BF16, BLOCK, false, 6>(p, nunits, fd, strided, f, s);
         break;
     default:
         if (p.rht) launch_dq4<OUT_BF16, BLOCK, true, 0>(p, nunits, fd, strided, f, s);

@@ -124,12 +124,24 @@ typedef enum fp4_transform {
  * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
  * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
  * Row-wise quantize, dequantize and fp4_gemm take them; the column-wise and
- * two-orientation calls and fp4_wo_gemm return UNSUPPORTED for them. */
+ * two-orientation calls and fp4_wo_gemm return UNSUPPORTED for them.
+ * The 6-bit grids (the same page's MXFP6 / MXINT6; reading: the OCP FP6
+ * element formats E2M3 and E3M2, and INT6 on -31..31) pack six bits per
+ * element as a little-endian bit stream: element c of a row at bits
+ * 6c .. 6c + 5 of the row's cols*3/4 bytes.  FP6 E2M3: bias 1, largest 7.5;
+ * E3M2: bias 3, largest 28; sign bit 5, subnormals, no reserved codes;
+ * nearest-even, saturating.  INT6: six-bit two's complement, zero unsigned.
+ * 7.5, 28 or 31 takes the place of 6; the E8M0 offsets are 2, 4 and 4.
+ * Row-wise quantize and dequantize only (the other calls return
+ * UNSUPPORTED). */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,
     FP4_ELEM_FP8_E4M3 = 2,    /* MXFP8-style, one byte per element           */
-    FP4_ELEM_INT8 = 3         /* MXINT8-style, one byte per element          */
+    FP4_ELEM_INT8 = 3,        /* MXINT8-style, one byte per element          */
+    FP4_ELEM_FP6_E2M3 = 4,    /* MXFP6-style, six bits per element           */
+    FP4_ELEM_FP6_E3M2 = 5,    /* MXFP6-style, six bits per element           */
+    FP4_ELEM_INT6 = 6         /* MXINT6-style, six bits per element          */
 } fp4_element;
 
 typedef struct fp4_format {
@@ -142,10 +154,11 @@ typedef struct fp4_format {
     int32_t element;          /* fp4_element                                  */
 } fp4_format;
 
-/* A quantized tensor.  q: rows*cols/2 bytes (4-bit grids) or rows*cols
- * bytes (8-bit grids); scales: rows*cols/block bytes; tensor_scale: 2 floats
- * {g, amax used} (g = 1 and amax = 0 under NONE).  All three are device
- * pointers; q must be 4-byte aligned (8-byte for the 8-bit grids). */
+/* A quantized tensor.  q: rows*cols/2 bytes (4-bit grids), rows*cols
+ * bytes (8-bit grids) or rows*cols*3/4 bytes (6-bit grids); scales:
+ * rows*cols/block bytes; tensor_scale: 2 floats {g, amax used} (g = 1 and
+ * amax = 0 under NONE).  All three are device pointers; q must be 4-byte
+ * aligned (8-byte for the 8- and 6-bit grids). */
 typedef struct fp4_tensor {
     uint8_t* q;
     uint8_t* scales;

@@ -138,7 +138,7 @@ def test_element_checks():
     L = fq.lib()
     assert L.fp4_version() >= 102
     t = _tensor()
-    t.fmt.element = 5
+    t.fmt.element = 7
     assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -1
     a = _tensor(rows=8, cols=256)
     b = _tensor(rows=8, cols=256)
@@ -171,5 +171,24 @@ def test_8bit_element_checks():
     t = _tensor(q=FAKE + 4)
     t.fmt.element = 2                                  # 8-bit codes need 8-byte alignment
     assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -4
-    t.fmt.element = 4
+    t.fmt.element = 7
     assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -1
+
+
+def test_6bit_element_checks():
+    L = fq.lib()
+    assert L.fp4_version() >= 104
+    for elem in (4, 5, 6):
+        t = _tensor(q=FAKE + 4)                        # 6-bit codes need 8-byte alignment
+        t.fmt.element = elem
+        assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -4
+        tt = _tensor(rows=64, cols=32)                 # not on the column-wise path
+        tt.fmt.element = elem
+        assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -2
+        a = _tensor(rows=8, cols=256)
+        b = _tensor(rows=8, cols=256)
+        a.fmt.element = b.fmt.element = elem
+        assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2
+        w = _tensor(rows=8, cols=256)
+        w.fmt.element = elem
+        assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
