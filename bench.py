@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "ebbb284ef3b64238cae500913a3dc73255fa3a9b4490bbc56b357c66b55c911d",
-    "read_bytes": 33787637,
+    "sha256": "46fe31a9ce03dede1b2e45a7eb0cb69f7ebcfebb3adcb112830d051ad9f4299e",
+    "read_bytes": 33786532,
     "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
