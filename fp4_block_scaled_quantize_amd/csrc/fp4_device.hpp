@@ -296,6 +296,34 @@ __device__ __forceinline__ uint32_t int6_sr_code(float v, uint32_t r16)
 
 __device__ __forceinline__ float int6_value(uint32_t c) { return (float)(((int32_t)(c << 26)) >> 26); }
 
+// Four FP6 RTN codes packed at bits 0, 6, 12, 18.  FP6 E2M3 is FP8 E4M3
+// scaled by 2^-6 (the E4M3 minimum normal 2^-6 and subnormal spacing 2^-9
+// are E2M3's 1 and 2^-3 times 2^-6, both with 3 mantissa bits), and FP6 E3M2
+// is FP8 E5M2 scaled by 2^-12 (2^-14 and 2^-16 against 2^-2 and 2^-4, 2
+// mantissa bits).  So after the saturating clamp and the exact power-of-two
+// scaling the hardware OCP FP8 / BF8 conversion (nearest-even) yields the
+// FP6 magnitude in its low 5 bits; the sign moves from bit 7 to bit 5.
+template <int ELEM>
+__device__ __forceinline__ uint32_t fp6_rtn_pack4_hw(float v0, float v1, float v2, float v3)
+{
+    constexpr float kMax = ELEM == 4 ? 7.5f : 28.0f;
+    constexpr float kShift = ELEM == 4 ? 0x1p-6f : 0x1p-12f;
+    const float c0 = __builtin_amdgcn_fmed3f(v0, -kMax, kMax) * kShift;
+    const float c1 = __builtin_amdgcn_fmed3f(v1, -kMax, kMax) * kShift;
+    const float c2 = __builtin_amdgcn_fmed3f(v2, -kMax, kMax) * kShift;
+    const float c3 = __builtin_amdgcn_fmed3f(v3, -kMax, kMax) * kShift;
+    int w;
+    if constexpr (ELEM == 4) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c2, c3, w, true);
+    }
+    const uint32_t b = ((uint32_t)w & 0x1F1F1F1Fu) | (((uint32_t)w >> 2) & 0x20202020u);   // 6-bit codes per byte
+    return (b & 0x3Fu) | ((b >> 2) & (0x3Fu << 6)) | ((b >> 4) & (0x3Fu << 12)) | ((b >> 6) & (0x3Fu << 18));
+}
+
 // One element grid's code of v (ELEM 4 FP6 E2M3, 5 FP6 E3M2, 6 INT6).
 template <int ELEM>
 __device__ __forceinline__ uint32_t w6_rtn_code(float v)

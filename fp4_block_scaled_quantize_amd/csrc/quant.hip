@@ -507,9 +507,12 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     bits |= (uint64_t)w6_sr_code<ELEM>(v[k], (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu) << (6 * k);
-            } else {
+            } else if (ELEM == 6) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) bits |= (uint64_t)w6_rtn_code<ELEM>(v[k]) << (6 * k);
+            } else {
+                bits = (uint64_t)fp6_rtn_pack4_hw<ELEM>(v[0], v[1], v[2], v[3]) |
+                       ((uint64_t)fp6_rtn_pack4_hw<ELEM>(v[4], v[5], v[6], v[7]) << 24);
             }
             if (u < a.nunits) {
                 uint16_t* dst = reinterpret_cast<uint16_t*>(a.q) + 3 * (uint64_t)u;
