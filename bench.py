@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "46fe31a9ce03dede1b2e45a7eb0cb69f7ebcfebb3adcb112830d051ad9f4299e",
-    "read_bytes": 33786532,
-    "write_bytes": 9453760,
+    "sha256": "31eefc30fefc61da583cdd96c41893ae4f17f38586a2b9e986e9f0b5f60e8691",
+    "read_bytes": 33786984,
+    "write_bytes": 9453761,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
