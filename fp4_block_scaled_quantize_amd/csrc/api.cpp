@@ -126,7 +126,7 @@ fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool elem_is_8bit(int32_t e) { return e == FP4_ELEM_FP8_E4M3 || e == FP4_ELEM_INT8; }
 static bool elem_is_6bit(int32_t e) { return e >= FP4_ELEM_FP6_E2M3 && e <= FP4_ELEM_INT6; }
-// the 8- and 6-bit grids: row-wise quantize and dequantize (and the GEMM for 8 bits)
+// the 8- and 6-bit grids: row-wise quantize, dequantize and the GEMM only
 static bool elem_is_wide(int32_t e) { return elem_is_8bit(e) || elem_is_6bit(e); }
 
 static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
@@ -351,7 +351,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (a->fmt.block != b->fmt.block) return FP4_ERR_UNSUPPORTED;
     // transformed operands multiply to the same product only when both carry
     // the same transform along K
-    if (a->fmt.element != b->fmt.element || elem_is_6bit(a->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    if (a->fmt.element != b->fmt.element) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != b->fmt.transform) return FP4_ERR_UNSUPPORTED;
     if (a->fmt.transform != FP4_TRANSFORM_NONE && a->fmt.transform_signs != b->fmt.transform_signs)
         return FP4_ERR_UNSUPPORTED;

@@ -601,18 +601,71 @@ __device__ __forceinline__ void dequant16_w8(const v4i& codes, float s, uint32_t
     }
 }
 
+// Dequantize 32 six-bit codes (192 bits, element k at bit 6k of d[0..2])
+// with scales s0 (elements 0..15) and s1 (16..31).  An FP6 code is the FP8
+// byte of its value times 2^-6 (E2M3 -> E4M3) or 2^-12 (E3M2 -> E5M2): the
+// hardware converts that exactly and one multiply by 2^6 / 2^12 restores
+// the value.  INT6 codes are sign-extended.
+template <bool F16, int ELEM>
+__device__ __forceinline__ void dequant32_w6(const uint64_t d[3], float s0, float s1, uint32_t out[16])
+{
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {                   // four elements 4q .. 4q + 3
+        uint32_t c[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int bit = 6 * (4 * q + t), lo = bit >> 6, sh = bit & 63;
+            uint64_t v = d[lo] >> sh;
+            if (sh > 58) v |= d[lo + 1] << (64 - sh);
+            c[t] = (uint32_t)v & 0x3Fu;
+        }
+        const float s = q < 4 ? s0 : s1;
+        float e[4];
+        if constexpr (ELEM == 6) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) e[t] = (float)(((int32_t)(c[t] << 26)) >> 26);
+        } else {
+            uint32_t w = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w |= ((c[t] & 0x1Fu) | ((c[t] & 0x20u) << 2)) << (8 * t);
+            const v2f lo2 = ELEM == 4 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false)
+                                      : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+            const v2f hi2 = ELEM == 4 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                                      : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+            constexpr float kFold = ELEM == 4 ? 64.0f : 4096.0f;      // exact: back to the FP6 value
+            e[0] = lo2[0] * kFold; e[1] = lo2[1] * kFold; e[2] = hi2[0] * kFold; e[3] = hi2[1] * kFold;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float v0 = e[2 * h] * s, v1 = e[2 * h + 1] * s;
+            uint32_t b0, b1;
+            if (F16) {
+                b0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0);
+                b1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1);
+            } else {
+                b0 = __float_as_uint(v0) >> 16;
+                b1 = __float_as_uint(v1) >> 16;
+            }
+            out[2 * q + h] = b0 | (b1 << 16);
+        }
+    }
+}
+
 // ELEM: the element grid of both operands (fp4_element order: 0 E2M1, 1
-// INT4, 2 FP8 E4M3, 3 INT8).  The launch picks bf16 or f16 so that every
+// INT4, 2 FP8 E4M3, 3 INT8, 4 FP6 E2M3, 5 FP6 E3M2, 6 INT6).  The launch picks bf16 or f16 so that every
 // dequantized value is exact: INT4 products carry at most 3 + 5 = 8
 // significant bits in bf16 (3 + 7 in f16), FP8 ones 4 + 4 in bf16, INT8
 // ones 7 + 1 in bf16 (power-of-two scales) or 7 + 4 in f16 (E4M3 scales,
 // at most 127 * 448 < 65504).  The 8-bit grids stage 32 bytes per thread
-// and row instead of 16; the LDS tiles and the matrix loop are the same.
+// and row instead of 16, the 6-bit grids 24 (three 8-byte loads; FP6 E2M3
+// products carry 4 + 4 bits, E3M2 3 + 5, INT6 5 + 3 in bf16 or 5 + 6 in
+// f16); the LDS tiles and the matrix loop are the same.
 template <bool F16, int BLOCK, int ELEM = 0>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 {
     constexpr bool INT = ELEM == 1;
-    constexpr bool W8 = ELEM >= 2;
+    constexpr bool W8 = ELEM == 2 || ELEM == 3;
+    constexpr bool W6 = ELEM >= 4;
     extern __shared__ __align__(16) uint8_t smem_raw[];
     DqSmem& sm = *reinterpret_cast<DqSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -620,7 +673,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
     const int64_t n_base = (int64_t)blockIdx.x * kTile;
     const int64_t m_base = (int64_t)blockIdx.y * kTile;
     const int64_t M = p.m, N = p.n, K = p.k;
-    const int64_t rowb = W8 ? K : K / 2, rows = K / BLOCK;
+    const int64_t rowb = W8 ? K : W6 ? K / 4 * 3 : K / 2, rows = K / BLOCK;
     const int KT = (int)(K / kDqBK);
     const ScaleFmt fw{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
     const ScaleFmt fa{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
@@ -642,16 +695,26 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
     constexpr int kVec = W8 ? 2 : 1;                                  // 16-byte loads per chunk
     const int crow = tid >> 1, cchunk = tid & 1;
     v4i rw[2][kVec], ra[2][kVec];
+    uint64_t r6w[2][W6 ? 3 : 1], r6a[2][W6 ? 3 : 1];                   // 6-bit chunks: 24 bytes
     uint32_t scw[2], sca[2];
     auto gload = [&](int kt) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int64_t nr = n_base + crow + 128 * r, mr = m_base + crow + 128 * r;
-            const int64_t kb = (int64_t)kt * (16 * kVec * 2) + cchunk * (16 * kVec);   // byte offset in the row
             const int64_t sb = ((int64_t)kt * kDqBK + cchunk * 32) / BLOCK; // first scale of the chunk
+            if constexpr (W6) {
+                const int64_t kb6 = (int64_t)kt * 48 + cchunk * 24;
+#pragma unroll
+                for (int v = 0; v < 3; ++v) {
+                    r6w[r][v] = nr < N ? *reinterpret_cast<const uint64_t*>(p.qb + nr * rowb + kb6 + 8 * v) : 0ull;
+                    r6a[r][v] = mr < M ? *reinterpret_cast<const uint64_t*>(p.qa + mr * rowb + kb6 + 8 * v) : 0ull;
+                }
+            }
+            const int64_t kb = (int64_t)kt * (16 * kVec * 2) + cchunk * (16 * kVec);   // byte offset in the row
             if (nr < N) {
 #pragma unroll
-                for (int v = 0; v < kVec; ++v) rw[r][v] = *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kb + 16 * v);
+                for (int v = 0; v < kVec; ++v)
+                    if (!W6) rw[r][v] = *reinterpret_cast<const v4i*>(p.qb + nr * rowb + kb + 16 * v);
                 scw[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sb + nr * rows + sb)
                                      : (uint32_t)p.sb[nr * rows + sb];
             } else {
@@ -661,7 +724,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             }
             if (mr < M) {
 #pragma unroll
-                for (int v = 0; v < kVec; ++v) ra[r][v] = *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kb + 16 * v);
+                for (int v = 0; v < kVec; ++v)
+                    if (!W6) ra[r][v] = *reinterpret_cast<const v4i*>(p.qa + mr * rowb + kb + 16 * v);
                 sca[r] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(p.sa + mr * rows + sb)
                                      : (uint32_t)p.sa[mr * rows + sb];
             } else {
@@ -687,7 +751,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(scw[r] & 0xFFu, fw) * pw;
                 const float s1 = BLOCK == 16 ? scale_decode_any((scw[r] >> 8) & 0xFFu, fw) * pw : s0;
-                dq(rw[r], s0, s1, o);
+                if constexpr (W6) dequant32_w6<F16, ELEM>(r6w[r], s0, s1, o);
+                else dq(rw[r], s0, s1, o);
                 uint8_t* dst = &sm.w[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -697,7 +762,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
             {
                 const float s0 = scale_decode_any(sca[r] & 0xFFu, fa) * pa;
                 const float s1 = BLOCK == 16 ? scale_decode_any((sca[r] >> 8) & 0xFFu, fa) * pa : s0;
-                dq(ra[r], s0, s1, o);
+                if constexpr (W6) dequant32_w6<F16, ELEM>(r6a[r], s0, s1, o);
+                else dq(ra[r], s0, s1, o);
                 uint8_t* dst = &sm.a[buf][(crow + 128 * r) * kDqRow + cchunk * 64];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
@@ -1010,6 +1076,11 @@ static bool fp8_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbi
 // INT8 elements carry 7 significant bits: bf16 needs power-of-two scales,
 // f16 holds them times E4M3 scales (11 bits, at most 127 * 448 = 56896).
 static bool int8_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits == 0; }
+// INT6 elements carry 5 significant bits: bf16 for scales with at most 2
+// mantissa bits, f16 for the f16-ranged scale formats with at most 5
+// (E4M3, E3M4, E2M5: 31 * 448 = 13888 < 65504).
+static bool int6_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 2; }
+static bool int6_exact_in_f16(const ScaleFmtHost& f) { return exact_in_f16(f) && f.mbits <= 5; }
 
 // The 16-bit type of the exact dequantize path for element grid elem and
 // scale formats fa, fb: 1 bf16, 2 f16, 0 none exact.
@@ -1024,6 +1095,13 @@ static int dq_type(const ScaleFmtHost& fa, const ScaleFmtHost& fb, int elem)
     case 3:
         if (int8_exact_in_bf16(fa) && int8_exact_in_bf16(fb)) return 1;
         return is_e4m3(fa) && is_e4m3(fb) ? 2 : 0;
+    case 4:                                         // FP6 E2M3: 4 significant bits, as FP8
+        return fp8_exact_in_bf16(fa) && fp8_exact_in_bf16(fb) ? 1 : 0;
+    case 5:                                         // FP6 E3M2: 3 significant bits, as INT4
+        return int4_exact_in_bf16(fa) && int4_exact_in_bf16(fb) ? 1 : 0;
+    case 6:                                         // INT6: 5 significant bits
+        if (int6_exact_in_bf16(fa) && int6_exact_in_bf16(fb)) return 1;
+        return int6_exact_in_f16(fa) && int6_exact_in_f16(fb) ? 2 : 0;
     default:
         if (exact_in_f16(fa) && exact_in_f16(fb)) return 2;
         return exact_in_bf16(fa) && exact_in_bf16(fb) ? 1 : 0;
@@ -1042,7 +1120,7 @@ static hipError_t launch_dq_elem(const GemmLaunch& p, bool f16, hipStream_t s)
 {
     dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
     const size_t sh = sizeof(DqSmem);
-    if constexpr (ELEM != 2) {      // FP8 elements have no f16 variant
+    if constexpr (ELEM != 2 && ELEM != 4 && ELEM != 5) {      // FP8 / FP6 elements have no f16 variant
         if (f16) {
             hipError_t e = allow_lds(k_gemm_dq<true, BLOCK, ELEM>, sh);
             if (e != hipSuccess) return e;
@@ -1069,7 +1147,10 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
         if (t == 0) return hipErrorNotSupported;
         if (p.elem == 1) return launch_dq_grid<1>(p, t == 2, s);
         if (p.elem == 2) return launch_dq_grid<2>(p, false, s);   // bf16 only
-        return launch_dq_grid<3>(p, t == 2, s);
+        if (p.elem == 3) return launch_dq_grid<3>(p, t == 2, s);
+        if (p.elem == 4) return launch_dq_grid<4>(p, false, s);   // bf16 only
+        if (p.elem == 5) return launch_dq_grid<5>(p, false, s);   // bf16 only
+        return launch_dq_grid<6>(p, t == 2, s);
     }
     const bool f16 = exact_in_f16(p.fa) && exact_in_f16(p.fb);
     const bool bf16 = exact_in_bf16(p.fa) && exact_in_bf16(p.fb);

@@ -132,8 +132,8 @@ typedef enum fp4_transform {
  * E3M2: bias 3, largest 28; sign bit 5, subnormals, no reserved codes;
  * nearest-even, saturating.  INT6: six-bit two's complement, zero unsigned.
  * 7.5, 28 or 31 takes the place of 6; the E8M0 offsets are 2, 4 and 4.
- * Row-wise quantize and dequantize only (the other calls return
- * UNSUPPORTED). */
+ * Row-wise quantize, dequantize and fp4_gemm take them (the other calls
+ * return UNSUPPORTED). */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,
@@ -298,7 +298,10 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * 8-bit grids: FP8 E4M3 elements in bf16 for scale formats with at most 3
  * mantissa bits (E8M0, E7M0, E6M1, E5M2, E4M3, UE5M3), INT8 elements in
  * bf16 for power-of-two scales (E8M0, E7M0) and in f16 for E4M3 scales;
- * other 8-bit pairings return UNSUPPORTED.
+ * and the 6-bit grids: FP6 E2M3 as FP8, FP6 E3M2 in bf16 for scales with
+ * at most 4 mantissa bits, INT6 in bf16 for at most 2 (E8M0, E7M0, E6M1,
+ * E5M2) and in f16 for E4M3 / E3M4 / E2M5; other 8- and 6-bit pairings
+ * return UNSUPPORTED.
  * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within

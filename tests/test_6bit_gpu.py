@@ -4,7 +4,9 @@ little-endian bit stream) against the CPU oracle: codes, scales and tensor
 scale bit for bit for every scale encoding, both rounding modes, the
 single-pass and two-pass refreshes, the Hadamard transform and ragged row
 counts; every FP6 rounding midpoint; dequantization of every code bit for
-bit; the paths that do not take 6-bit grids reject them.  Every call goes
+bit; the GEMM within the binary64 reference's tolerance on every scale
+pairing it takes and bit for bit on every code; the paths that do not take
+6-bit grids reject them.  Every call goes
 through the C ABI.
 """
 import numpy as np
@@ -155,11 +157,140 @@ def test_6bit_dequantize_rht_roundtrip_parity(elem):
     assert_bytes_equal(f32_bits(y), f32_bits(want), f"{elem} rht dequant")
 
 
+def _gemm_check(c, a_hat, w_hat, rows=None, tag=""):
+    if rows is not None:
+        a_hat = a_hat[rows]
+    cref, tol = oracle.gemm_ref(a_hat, w_hat)
+    got = c.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[rows]
+    ok = oracle.gemm_check(got, cref, tol)
+    assert ok.all(), f"{tag}: {int((~ok).sum())} of {ok.size} outputs out of tolerance"
+
+
+def _quant_pair(x, block, fmt, elem, *, rounding="nearest", seed=0, rht=None):
+    pol = _policy(fmt)
+    qt = fq.fp4_quantize(to_device(x), block, fmt, amax=pol, rounding=rounding, seed=seed, rht_signs=rht,
+                         element=elem)
+    q, s, g, _ = oracle.quantize_tensor(x, block, fmt, pol, stochastic=rounding == "stochastic", seed=seed,
+                                        nthreads=8, rht_signs=rht, elem=elem)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qt.q), q, f"{elem} {fmt} operand codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} {fmt} operand scales")
+    return qt, oracle.dequantize_f64(q, s, g, block, fmt, elem=elem)
+
+
+# Scale pairings the exact dequantize GEMM takes for the 6-bit grids: FP6
+# E2M3 (4 significant bits) in bf16 for scales with at most 3 mantissa bits,
+# E3M2 (3 bits) for at most 4, INT6 (5 bits) in bf16 for at most 2 and in
+# f16 for E4M3 / E3M4 / E2M5.
+GEMM_6BIT = [("fp6_e2m3", "e8m0", 32), ("fp6_e2m3", "e4m3", 16), ("fp6_e2m3", "ue5m3", 32),
+             ("fp6_e3m2", "e8m0", 32), ("fp6_e3m2", "e3m4", 16), ("fp6_e3m2", "e4m3", 16),
+             ("int6", "e8m0", 32), ("int6", "e5m2", 16), ("int6", "e4m3", 16), ("int6", "e3m4", 32),
+             ("int6", "e2m5", 16)]
+
+
+@pytest.mark.parametrize("elem,fmt,block", GEMM_6BIT)
+def test_6bit_gemm(elem, fmt, block):
+    """Ragged M and N (partial 256-row tiles), K over several 64-element
+    stages."""
+    m, n, k = 200, 330, 768
+    qa, a = _quant_pair(_like(m, k, 95, "f32"), block, fmt, elem)
+    qw, w = _quant_pair(_like(n, k, 96, "f32"), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    assert c.shape == (m, n)
+    _gemm_check(c, a, w, tag=f"{elem} {fmt}/{block} gemm")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_6bit_gemm_transform_sr_and_llama(elem):
+    """Hadamard-rotated and stochastically rounded operands, then the Llama-2
+    7B square projection at M = 8192 on sampled output rows."""
+    fmt, block = "e8m0", 32
+    xa, xw = _like(96, 512, 97, "f32"), _like(72, 512, 98, "f32")
+    qa, a = _quant_pair(xa, block, fmt, elem, rht=0x2468ACE1)
+    qw, w = _quant_pair(xw, block, fmt, elem, rht=0x2468ACE1)
+    _gemm_check(fq.fp4_gemm(qa, qw), a, w, tag=f"{elem} rht gemm")
+    qa, a = _quant_pair(xa, block, fmt, elem, rounding="stochastic", seed=11)
+    qw, w = _quant_pair(xw, block, fmt, elem, rounding="stochastic", seed=12)
+    _gemm_check(fq.fp4_gemm(qa, qw), a, w, tag=f"{elem} sr gemm")
+    shapes = {"a": (8192, 4096), "sq": (4096, 4096)}
+    qa, a = _quant_pair(inputs.llama("a", shapes), block, fmt, elem)
+    qw, w = _quant_pair(inputs.llama("sq", shapes), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.integers(0, 8192, 16), [0, 255, 256, 8191]]))
+    _gemm_check(c, a, w, rows=rows, tag=f"{elem} llama sq")
+
+
+@pytest.mark.parametrize("elem,fmt", [("fp6_e2m3", "e8m0"), ("fp6_e3m2", "e8m0"), ("int6", "e8m0"),
+                                      ("int6", "e4m3")])
+def test_6bit_gemm_every_code(elem, fmt):
+    """All 64 codes through the GEMM's decode: A holds every code (four
+    times per row, shifted) with mixed block scales, W selects one column per
+    output (one code of value 1, one scale of 1), so C[m, n] is the bf16
+    rounding of A's value at (m, n)."""
+    k = 256
+    codes = np.tile(np.arange(64, dtype=np.int64), 4)
+    rows_codes = np.stack([codes, codes[::-1], np.roll(codes, 21)])
+
+    def pack(c):
+        out = np.zeros((c.shape[0], c.shape[1] * 3 // 4), dtype=np.uint8)
+        for r in range(c.shape[0]):
+            big = 0
+            for j, v in enumerate(c[r]):
+                big |= int(v) << (6 * j)
+            out[r] = np.frombuffer(big.to_bytes(out.shape[1], "little"), dtype=np.uint8)
+        return out
+    one = {"fp6_e2m3": 0x08, "fp6_e3m2": 0x0C, "int6": 0x01}[elem]      # the code of 1.0
+    block = 32 if fmt == "e8m0" else 16
+    rng = np.random.default_rng(27)
+    if fmt == "e8m0":
+        s_a = rng.integers(110, 145, (3, k // block), dtype=np.uint8)
+        s_one, g_a, pol = 127, 1.0, "none"
+    else:
+        s_a = rng.integers(0, 0x7F, (3, k // block), dtype=np.uint8)
+        s_one, g_a, pol = 0x38, 0.0625, "current"
+    q_a = pack(rows_codes)
+    w_codes = np.zeros((k, k), dtype=np.int64)
+    w_codes[np.arange(k), np.arange(k)] = one
+    q_w = pack(w_codes)
+    s_w = np.full((k, k // block), s_one, dtype=np.uint8)
+
+    def qt(q, s, g, rows):
+        return fq.QTensor(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(),
+                          torch.tensor([g, 0.0], dtype=torch.float32).cuda(), rows, k, block, fmt, amax=pol,
+                          element=elem)
+    c = fq.fp4_gemm(qt(q_a, s_a, g_a, 3), qt(q_w, s_w, 1.0, k))
+    torch.cuda.synchronize()
+    a_hat = oracle.dequantize_f64(q_a, s_a, np.float32(g_a), block, fmt, elem=elem)
+    w_hat = oracle.dequantize_f64(q_w, s_w, np.float32(1.0), block, fmt, elem=elem)
+    assert np.array_equal(w_hat, np.eye(k))
+    want = oracle.round_to_bf16(a_hat)
+    got = c.float().cpu().numpy().astype(np.float64)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (f"{elem} {fmt}: {len(bad)} outputs differ; first {tuple(bad[0])}: got "
+                           f"{got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}")
+
+
+@pytest.mark.parametrize("elem,fmt", [("fp6_e2m3", "e3m4"), ("fp6_e3m2", "e1m6"), ("int6", "ue5m3"),
+                                      ("int6", "e1m6")])
+def test_6bit_gemm_inexact_pairing_rejected(elem, fmt):
+    xd = to_device(_like(64, 256, 99, "f32"))
+    q = fq.fp4_quantize(xd, 16, fmt, element=elem)
+    with pytest.raises(fq.Fp4Error) as e:
+        fq.fp4_gemm(q, q)
+    assert e.value.status == -2
+
+
 def test_6bit_rejected_elsewhere():
     xd = to_device(_like(64, 256, 94, "f32"))
     for elem in ELEMS:
         q6 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element=elem)
-        for call in (lambda: fq.fp4_gemm(q6, q6),
+        f6 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element="fp6_e3m2" if elem != "fp6_e3m2" else "int6")
+        for call in (lambda: fq.fp4_gemm(q6, f6),
                      lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q6),
                      lambda: fq.fp4_quantize_transposed(xd, 32, "e8m0", amax="none", element=elem),
                      lambda: fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element=elem)):

@@ -185,8 +185,8 @@ def test_6bit_element_checks():
         tt = _tensor(rows=64, cols=32)                 # not on the column-wise path
         tt.fmt.element = elem
         assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -2
-        a = _tensor(rows=8, cols=256)
-        b = _tensor(rows=8, cols=256)
+        a = _tensor(rows=8, cols=256, scale=3)         # E1M6 scales: no 16-bit type is exact
+        b = _tensor(rows=8, cols=256, scale=3)
         a.fmt.element = b.fmt.element = elem
         assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2
         w = _tensor(rows=8, cols=256)
