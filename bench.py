@@ -357,7 +357,8 @@ def leg_8bit(torch, fq, inputs, xs):
     elements), MXINT8-style (E8M0 block 32), one byte per element, and
     MXFP6 / MXINT6-style (six bits per element), and
     the GEMM at the Llama-2 7B up-projection shape on the exact dequantize
-    path (MXFP8 in bf16; INT8 elements with E4M3 block-16 scales in f16)."""
+    path (MXFP8, MXFP6 and MXINT6 in bf16; INT8 elements with E4M3 block-16
+    scales in f16)."""
     rows, cols = xs[0].shape
     res = {}
     n = rows * cols
@@ -378,7 +379,9 @@ def leg_8bit(torch, fq, inputs, xs):
         del gs, outs
     m, n, k = 8192, 11008, 4096
     for name, (elem, fmt, block, pol) in {"mxfp8": ("fp8_e4m3", "e8m0", 32, "none"),
-                                          "nvint8": ("int8", "e4m3", 16, "current")}.items():
+                                          "nvint8": ("int8", "e4m3", 16, "current"),
+                                          "mxfp6_e2m3": ("fp6_e2m3", "e8m0", 32, "none"),
+                                          "mxint6": ("int6", "e8m0", 32, "none")}.items():
         a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
         w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_up"], torch.bfloat16)
         qa = fq.fp4_quantize(a, block, fmt, amax=pol, element=elem)
@@ -396,7 +399,8 @@ def leg_8bit(torch, fq, inputs, xs):
         del a, w, qa, qw, c, gs
     res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each) and "
                        "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN; "
-                       "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8 and INT8 with E4M3 block-16 scales")
+                       "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8, INT8 with E4M3 block-16 scales, "
+                       "MXFP6 (E2M3) and MXINT6")
     return res
 
 
