@@ -179,8 +179,9 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     must be 1).  CURRENT and DELAYED need an AmaxState; one is created for
     CURRENT if none is given.  rht_signs (32-bit sign mask) applies the
     blockwise randomized Hadamard transform before quantization; element
-    selects the grid: "e2m1" (default), "int4" (-7..7), or the one-byte
-    "fp8_e4m3" and "int8" (-127..127)."""
+    selects the grid: "e2m1" (default), "int4" (-7..7), the one-byte
+    "fp8_e4m3" and "int8" (-127..127), or the six-bit "fp6_e2m3",
+    "fp6_e3m2" and "int6" (-31..31)."""
     if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape

@@ -164,7 +164,8 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     if (ld_x < out->cols) return FP4_ERR_SHAPE;
-    if (!aligned16(x) || (ld_x * esz) % 16) return FP4_ERR_ALIGN;
+    // an empty x is never read (a [rows, 0] tensor may carry row stride 1)
+    if (out->rows * out->cols != 0 && (!aligned16(x) || (ld_x * esz) % 16)) return FP4_ERR_ALIGN;
     const int32_t pol = out->fmt.amax;
     if (f.is_e8m0 && pol != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
     if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;

@@ -157,6 +157,36 @@ def test_6bit_dequantize_rht_roundtrip_parity(elem):
     assert_bytes_equal(f32_bits(y), f32_bits(want), f"{elem} rht dequant")
 
 
+@pytest.mark.parametrize("elem", ELEMS + ["fp8_e4m3", "int8"])
+def test_wide_grid_edge_shapes(elem):
+    """Empty tensors (no rows, no columns), the smallest row (one 16-element
+    block), strided input rows and strided dequantized output, for the 6- and
+    8-bit grids."""
+    for shape in [(0, 64), (64, 0), (0, 0)]:
+        x = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        qt = fq.fp4_quantize(x, 16, "e4m3", element=elem)
+        y = fq.fp4_dequantize(qt, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert tuple(y.shape) == shape
+    x1 = _like(1, 16, 101, "f32")
+    _check(x1, 16, "e4m3", "current", elem, tag=f"{elem} 1x16")
+    _check(x1, 16, "e8m0", "none", elem, rounding="stochastic", seed=2, tag=f"{elem} 1x16 sr")
+    big = _like(37, 512, 102, "f32")
+    xs = to_device(big)[:, 64:448]                      # rows strided by 512, 384 columns
+    sub = np.ascontiguousarray(big[:, 64:448])
+    qt = fq.fp4_quantize(xs, 32, "e8m0", amax="none", element=elem)
+    q, s, g, _ = oracle.quantize_tensor(sub, 32, "e8m0", "none", elem=elem)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qt.q), q, f"{elem} strided codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} strided scales")
+    wide = torch.full((37, 400), -1.0, dtype=torch.float32, device="cuda")
+    fq.fp4_dequantize(qt, torch.float32, out=wide[:, :384])
+    torch.cuda.synchronize()
+    want = oracle.dequantize(q, s, float(g), 32, "e8m0", out="f32", elem=elem)
+    assert_bytes_equal(f32_bits(host(wide[:, :384])), f32_bits(want), f"{elem} strided dequant")
+    assert bool((wide[:, 384:] == -1.0).all())            # padding columns untouched
+
+
 def _gemm_check(c, a_hat, w_hat, rows=None, tag=""):
     if rows is not None:
         a_hat = a_hat[rows]

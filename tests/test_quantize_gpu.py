@@ -282,12 +282,19 @@ def test_edge_values():
             _check_quant(x, block, fmt, pol, rounding="stochastic", seed=3, offset=1, tag=f"edge sr {fmt} {pol}")
 
 
-def test_empty_tensor():
-    x = np.zeros((0, 64), dtype=np.float32)
-    xd = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
-    qt = fq.fp4_quantize(xd, 16, "e4m3", amax="current")
+@pytest.mark.parametrize("shape", [(0, 64), (64, 0), (0, 0)])
+@pytest.mark.parametrize("element", ["e2m1", "int4"])
+def test_empty_tensor(shape, element):
+    """No rows or no columns: nothing is read (a [64, 0] tensor carries row
+    stride 1, which is not an aligned leading dimension) and the tensor
+    scale is that of an all-zero tensor."""
+    x = np.zeros(shape, dtype=np.float32)
+    xd = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    qt = fq.fp4_quantize(xd, 16, "e4m3", amax="current", element=element)
+    y = fq.fp4_dequantize(qt, torch.bfloat16)
     torch.cuda.synchronize()
-    g, a = oracle.resolve_tensor_scale(x, "e4m3", "current")
+    assert tuple(y.shape) == shape
+    g, a = oracle.resolve_tensor_scale(x, "e4m3", "current", elem=element)
     assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), "empty ts")
 
 
