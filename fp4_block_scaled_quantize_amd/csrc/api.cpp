@@ -360,6 +360,8 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     if (ldc < b->rows) return FP4_ERR_SHAPE;
     if (((uintptr_t)c & 1u) != 0) return FP4_ERR_ALIGN;
     if (a->rows == 0 || b->rows == 0) return FP4_OK;
+    // an empty K: C is the empty sum, zero; no operand is read
+    if (a->cols == 0) return hip_status(launch_fill_zero_bf16(c, ldc, a->rows, b->rows, (hipStream_t)stream));
     if (!aligned16(a->q) || !aligned16(b->q) || ((uintptr_t)a->scales & 3u) || ((uintptr_t)b->scales & 3u))
         return FP4_ERR_ALIGN;
     GemmLaunch p;
@@ -382,16 +384,18 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     ScaleFmtHost fw;
     fp4_status st = check_tensor(w, &fw);
     if (st != FP4_OK) return st;
-    if (!x || !y) return FP4_ERR_INVALID_ARG;
+    if (!y || (!x && w->cols != 0)) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
     if (elem_is_wide(w->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
+    if (w->rows == 0) return FP4_OK;
+    // an empty K: Y is the empty sum, zero; neither x nor W is read
+    if (w->cols == 0) return hip_status(launch_fill_zero_bf16(y, ldy, m, w->rows, (hipStream_t)stream));
     // the kernel addresses W and x with 32-bit byte/element offsets
     if (w->rows * (w->cols / 2) >= (int64_t(1) << 32) || ldx * m >= (int64_t(1) << 31)) return FP4_ERR_UNSUPPORTED;
     if (!aligned16(x) || ldx % 8) return FP4_ERR_ALIGN;
-    if (w->rows == 0) return FP4_OK;
     if (!aligned16(w->q) || ((uintptr_t)w->scales & 3u)) return FP4_ERR_ALIGN;
     WoGemmLaunch p;
     p.x = x; p.ldx = ldx; p.m = m;

@@ -112,5 +112,7 @@ struct WoGemmLaunch {
 };
 
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s);
+// C[rows, cols] (bf16, row stride ld) = 0: the product over an empty K.
+hipError_t launch_fill_zero_bf16(uint16_t* c, int64_t ld, int64_t rows, int64_t cols, hipStream_t s);
 
 }  // namespace fp4

@@ -1514,6 +1514,27 @@ constexpr int64_t kWoManyGroups = 512;   // 16-row groups that fill the device o
 //  M > 1 with many row groups: two row groups share every X chunk; for
 //   M > 8 the slot is 6.4 KB and two slots per wave keep three workgroups
 //   per CU resident.
+// Zero fill of a bf16 matrix with row stride ld, one 2-byte store per
+// element (a kernel rather than a memset, so graph capture records a kernel
+// node).
+__global__ __launch_bounds__(256) void k_fill_zero_bf16(uint16_t* __restrict__ c, int64_t ld, int64_t rows,
+                                                        int64_t cols)
+{
+    const int64_t n = rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        c[(i / cols) * ld + i % cols] = 0;
+}
+
+hipError_t launch_fill_zero_bf16(uint16_t* c, int64_t ld, int64_t rows, int64_t cols, hipStream_t s)
+{
+    const int64_t n = rows * cols;
+    if (n == 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(k_fill_zero_bf16, dim3(blocks), dim3(256), 0, s, c, ld, rows, cols);
+    return hipGetLastError();
+}
+
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
     const bool many = (p.n + 15) / 16 >= kWoManyGroups;

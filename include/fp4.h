@@ -306,7 +306,8 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * instruction; every other format is dequantized exactly to bf16/f16 in
  * LDS and runs on the bf16/f16 matrix cores.  Result within
  * 1e-5 * sum_k |a||b| of the exact product before the bf16 rounding.
- * K % 128 == 0, M and N arbitrary; ldc >= N; c 2-byte aligned (rows that
+ * K % 128 == 0 (K = 0 writes C = 0 and reads no operand), M and N
+ * arbitrary; ldc >= N; c 2-byte aligned (rows that
  * are 8-byte aligned are written with vector stores); operand codes 16-byte
  * and scales 4-byte aligned.
  */
@@ -318,7 +319,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * in registers (quant_prune_distill/574 "Метод"/"Эксперименты":
  * weight-only NVFP4, memory-bound small-batch generation).
  * x: bf16 [M, K] (row stride ldx), w: [N, K] quantized along K.
- * 1 <= M <= 16; K % 256 == 0; x 16-byte aligned, ldx % 8 == 0, ldy >= N;
+ * 1 <= M <= 16; K % 256 == 0 (K = 0 writes Y = 0 and reads neither x nor w);
+ * x 16-byte aligned, ldx % 8 == 0, ldy >= N;
  * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB and no
  * transform on w (UNSUPPORTED otherwise).  E2M1 or INT4 weights.
  */

@@ -133,6 +133,22 @@ def test_zero_operand():
 
 
 @pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e4m3", 16)])
+def test_empty_k_gives_zero(fmt, block):
+    """K = 0: C and Y are empty sums, all zero, whatever the output held; no
+    operand is read."""
+    pol = _policy(fmt)
+    qa = fq.fp4_quantize(torch.zeros((33, 0), dtype=torch.float32, device="cuda"), block, fmt, amax=pol)
+    qw = fq.fp4_quantize(torch.zeros((40, 0), dtype=torch.float32, device="cuda"), block, fmt, amax=pol)
+    c = torch.full((33, 48), 7.0, dtype=torch.bfloat16, device="cuda")
+    fq.fp4_gemm(qa, qw, out=c[:, :40])
+    y = torch.full((3, 48), 7.0, dtype=torch.bfloat16, device="cuda")
+    fq.fp4_wo_gemm(torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda"), qw, out=y[:, :40])
+    torch.cuda.synchronize()
+    assert bool((c[:, :40] == 0).all()) and bool((c[:, 40:] == 7.0).all())
+    assert bool((y[:, :40] == 0).all()) and bool((y[:, 40:] == 7.0).all())
+
+
+@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e4m3", 16)])
 @pytest.mark.parametrize("wname", ["up", "down", "sq"])
 def test_llama_shapes_sampled_rows(fmt, block, wname):
     """Llama-2 7B linears at M = 8192 (batch 4 x seq 2048): sampled output
