@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "31eefc30fefc61da583cdd96c41893ae4f17f38586a2b9e986e9f0b5f60e8691",
-    "read_bytes": 33786984,
-    "write_bytes": 9453761,
+    "sha256": "744cd16fe85173f947a22b4a247c7eec3967b98e274e108ca57106b67301ff91",
+    "read_bytes": 33785919,
+    "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
