@@ -609,25 +609,21 @@ __device__ __forceinline__ void dequant16_w8(const v4i& codes, float s, uint32_t
 template <bool F16, int ELEM>
 __device__ __forceinline__ void dequant32_w6(const uint64_t d[3], float s0, float s1, uint32_t out[16])
 {
+    const uint32_t dw[6] = {(uint32_t)d[0], (uint32_t)(d[0] >> 32), (uint32_t)d[1],
+                            (uint32_t)(d[1] >> 32), (uint32_t)d[2], (uint32_t)(d[2] >> 32)};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {                   // four elements 4q .. 4q + 3
-        uint32_t c[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int bit = 6 * (4 * q + t), lo = bit >> 6, sh = bit & 63;
-            uint64_t v = d[lo] >> sh;
-            if (sh > 58) v |= d[lo + 1] << (64 - sh);
-            c[t] = (uint32_t)v & 0x3Fu;
-        }
+    for (int q = 0; q < 8; ++q) {                   // four elements 4q .. 4q + 3: bits 24q .. 24q + 23
+        const int bit = 24 * q, i = bit >> 5, sh = bit & 31;
+        const uint32_t x = sh == 0 ? dw[i] : sh <= 8 ? dw[i] >> sh : __builtin_amdgcn_alignbit(dw[i + 1], dw[i], sh);
         const float s = q < 4 ? s0 : s1;
         float e[4];
         if constexpr (ELEM == 6) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) e[t] = (float)(((int32_t)(c[t] << 26)) >> 26);
+            for (int t = 0; t < 4; ++t) e[t] = (float)(((int32_t)(x << (26 - 6 * t))) >> 26);
         } else {
-            uint32_t w = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) w |= ((c[t] & 0x1Fu) | ((c[t] & 0x20u) << 2)) << (8 * t);
+            // the four codes to one byte each, then to FP8 bytes (sign bit 5 -> 7)
+            const uint32_t y = (x & 0x3Fu) | ((x << 2) & 0x3F00u) | ((x << 4) & 0x3F0000u) | ((x << 6) & 0x3F000000u);
+            const uint32_t w = (y & 0x1F1F1F1Fu) | ((y & 0x20202020u) << 2);
             const v2f lo2 = ELEM == 4 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false)
                                       : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
             const v2f hi2 = ELEM == 4 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
