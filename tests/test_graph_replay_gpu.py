@@ -1,4 +1,5 @@
-"""Column-wise, two-orientation and Hadamard-transformed quantize calls
+"""Column-wise, two-orientation, Hadamard-transformed and 8- / 6-bit grid
+quantize calls, GEMMs and dequantize calls
 captured once in a HIP graph and replayed with new input values (eager
 copies and synchronizations between replays): every replay agrees with the
 oracle, the current-amax refreshes included (the captured amax kernel and
@@ -71,3 +72,66 @@ def test_graph_replay_transposed_both_and_transform():
         q, s, _, _ = oracle.quantize_tensor(h, 32, "e8m0", "none", rht_signs=signs)
         assert_bytes_equal(host(out_r.q), q, f"replay {rep} transform codes")
         assert_bytes_equal(host(out_r.scales), s, f"replay {rep} transform scales")
+
+
+WIDE = ["fp8_e4m3", "int8", "fp6_e2m3", "fp6_e3m2", "int6"]
+
+
+def test_graph_replay_wide_grids_gemm_and_dequantize():
+    """The 8- and 6-bit grids in one captured graph: single-pass current-amax
+    quantize calls (the grid exchange's epoch advances on every replay), a
+    GEMM of two MXFP8 operands quantized in the same graph, and a dequantize
+    of an MXFP6 tensor; each replay with new input values agrees with the
+    oracle."""
+    R, C, N = 96, 256, 72
+    x = torch.zeros((R, C), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((N, C), dtype=torch.bfloat16, device="cuda")
+    states = {e: fq.AmaxState(1) for e in WIDE}
+    outs = {e: fq.QTensor.empty(R, C, 16, "e4m3", element=e) for e in WIDE}
+    qa = fq.QTensor.empty(R, C, 32, "e8m0", amax="none", element="fp8_e4m3")
+    qw = fq.QTensor.empty(N, C, 32, "e8m0", amax="none", element="fp8_e4m3")
+    q6 = fq.QTensor.empty(R, C, 32, "e8m0", amax="none", element="fp6_e3m2")
+    c = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((R, C), dtype=torch.float32, device="cuda")
+
+    def record():
+        for e in WIDE:
+            fq.fp4_quantize(x, 16, "e4m3", state=states[e], out=outs[e], element=e)
+        fq.fp4_quantize(x, 32, "e8m0", amax="none", out=qa, element="fp8_e4m3")
+        fq.fp4_quantize(w, 32, "e8m0", amax="none", out=qw, element="fp8_e4m3")
+        fq.fp4_gemm(qa, qw, out=c)
+        fq.fp4_quantize(x, 32, "e8m0", amax="none", out=q6, element="fp6_e3m2")
+        fq.fp4_dequantize(q6, torch.float32, out=y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        record()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        record()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        hx = _like(R, C, 6000 + rep, 10.0 ** (rep - 1))
+        hw = _like(N, C, 7000 + rep, 1.0)
+        x.copy_(to_device(hx))
+        w.copy_(to_device(hw))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e in WIDE:
+            q, s, g, a = oracle.quantize_tensor(hx, 16, "e4m3", "current", elem=e)
+            assert_bytes_equal(host(outs[e].q), q, f"replay {rep} {e} codes")
+            assert_bytes_equal(host(outs[e].scales), s, f"replay {rep} {e} scales")
+            assert_bytes_equal(f32_bits(host(outs[e].tensor_scale)), f32_bits([g, a]), f"replay {rep} {e} ts")
+        oa = oracle.quantize_tensor(hx, 32, "e8m0", "none", elem="fp8_e4m3")
+        ow = oracle.quantize_tensor(hw, 32, "e8m0", "none", elem="fp8_e4m3")
+        a_hat = oracle.dequantize_f64(oa[0], oa[1], oa[2], 32, "e8m0", elem="fp8_e4m3")
+        w_hat = oracle.dequantize_f64(ow[0], ow[1], ow[2], 32, "e8m0", elem="fp8_e4m3")
+        cref, tol = oracle.gemm_ref(a_hat, w_hat)
+        ok = oracle.gemm_check(c.float().cpu().numpy().astype(np.float64), cref, tol)
+        assert ok.all(), f"replay {rep} gemm: {int((~ok).sum())} outputs out of tolerance"
+        q, s, g, _ = oracle.quantize_tensor(hx, 32, "e8m0", "none", elem="fp6_e3m2")
+        want = oracle.dequantize(q, s, float(g), 32, "e8m0", out="f32", elem="fp6_e3m2")
+        assert_bytes_equal(f32_bits(host(y)), f32_bits(want), f"replay {rep} fp6 dequant")
