@@ -131,6 +131,14 @@ class QTensor:
         return cls(q, s, ts, rows, cols, block, scale, rounding, amax, transform, rht_signs, element)
 
     def c(self) -> Fp4TensorC:
+        # the library reads or writes rows * cols * bits / 8 code bytes and
+        # rows * cols / block scale bytes through these pointers
+        qb = self.rows * (self.cols * ELEMENT_BITS[self.element] // 8)
+        if self.q.numel() * self.q.element_size() < qb or \
+                self.scales.numel() * self.scales.element_size() < self.rows * (self.cols // self.block) or \
+                self.tensor_scale.numel() < 2:
+            raise ValueError(f"QTensor buffers are smaller than a [{self.rows}, {self.cols}] tensor on the "
+                             f"{self.element} grid needs")
         fmt = Fp4Format(self.block, SCALE_FORMATS[self.scale], ROUNDING[self.rounding], AMAX[self.amax],
                         TRANSFORM[self.transform], self.rht_signs & 0xFFFFFFFF, ELEMENT[self.element])
         return Fp4TensorC(self.q.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
@@ -171,6 +179,15 @@ class AmaxState:
             pass
 
 
+def _check_out(t: QTensor, rows: int, cols: int, block: int, element: str):
+    """A caller-provided output must hold the codes and scales of a [rows,
+    cols] tensor on `element` (the kernels write exactly that many bytes)."""
+    qb = cols * ELEMENT_BITS[element] // 8
+    if (t.rows, t.cols) != (rows, cols) or t.q.numel() < rows * qb or t.scales.numel() < rows * (cols // block) \
+            or t.tensor_scale.numel() < 2 or not (t.q.is_contiguous() and t.scales.is_contiguous()):
+        raise ValueError(f"out does not hold a [{rows}, {cols}] tensor on the {element} grid with block {block}")
+
+
 def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
                  amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
                  out: QTensor | None = None, stream=None, rht_signs: int | None = None,
@@ -188,6 +205,7 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     if out is None:
         out = QTensor.empty(rows, cols, block, scale, rounding, amax, device=x.device, element=element)
     else:
+        _check_out(out, rows, cols, block, element)
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)
     out.element = element
@@ -213,8 +231,9 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
         raise ValueError("x must be 2-D with unit column stride")
     r, c = x.shape
     if out is None:
-        out = QTensor.empty(c, r, block, scale, rounding, amax, device=x.device)
+        out = QTensor.empty(c, r, block, scale, rounding, amax, device=x.device, element=element)
     else:
+        _check_out(out, c, r, block, element)
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.element = element
     if rht_signs is not None:
@@ -244,6 +263,8 @@ def fp4_quantize_both(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rou
         out = (QTensor.empty(r, c, block, scale, rounding, amax, device=x.device, element=element),
                QTensor.empty(c, r, block, scale, rounding, amax, device=x.device, element=element))
     qr, qc = out
+    _check_out(qr, r, c, block, element)
+    _check_out(qc, c, r, block, element)
     for t in (qr, qc):
         t.block, t.scale, t.rounding, t.amax, t.element = block, scale, rounding, amax, element
     if amax != "none" and state is None:

@@ -192,3 +192,18 @@ def test_6bit_element_checks():
         w = _tensor(rows=8, cols=256)
         w.fmt.element = elem
         assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
+
+
+def test_binding_refuses_buffers_too_small_for_the_grid():
+    """The binding checks buffer sizes before any call: codes allocated for
+    4-bit elements cannot describe an 8- or 6-bit tensor."""
+    q4 = fq.QTensor.empty(4, 64, 16, "e4m3", device="cpu")
+    for elem in ("fp8_e4m3", "int8", "fp6_e2m3", "int6"):
+        q4.element = elem
+        with pytest.raises(ValueError):
+            q4.c()
+    q4.element = "e2m1"
+    q4.c()
+    with pytest.raises(ValueError):
+        fq._check_out(q4, 4, 64, 16, "int8")
+    fq._check_out(q4, 4, 64, 16, "int4")

@@ -113,10 +113,12 @@ def test_both_rejects_mismatch_and_transform():
         fq.fp4_quantize_both(xd, 16, "e4m3", out=(fq.QTensor.empty(64, 64, 16, "e4m3"),
                                                   fq.QTensor.empty(64, 64, 16, "e4m3", transform="rht", rht_signs=3)))
     assert e.value.status == -2
-    with pytest.raises(fq.Fp4Error) as e:
+    # a column-wise output of the wrong shape: the binding refuses it before
+    # the call (the library's own SHAPE status is checked through the ABI
+    # on the CPU)
+    with pytest.raises(ValueError):
         fq.fp4_quantize_both(xd, 16, "e4m3", out=(fq.QTensor.empty(64, 64, 16, "e4m3"),
                                                   fq.QTensor.empty(32, 64, 16, "e4m3")))
-    assert e.value.status == -3
 
 
 def test_both_empty_and_tiny():
