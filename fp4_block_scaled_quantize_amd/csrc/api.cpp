@@ -126,7 +126,7 @@ fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool elem_is_8bit(int32_t e) { return e == FP4_ELEM_FP8_E4M3 || e == FP4_ELEM_INT8; }
 static bool elem_is_6bit(int32_t e) { return e >= FP4_ELEM_FP6_E2M3 && e <= FP4_ELEM_INT6; }
-// the 8- and 6-bit grids: row-wise quantize, dequantize and the GEMM only
+// the 8- and 6-bit grids: no two-orientation call and no weight-only GEMM
 static bool elem_is_wide(int32_t e) { return elem_is_8bit(e) || elem_is_6bit(e); }
 
 static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
@@ -211,7 +211,7 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     // x is [out->cols, out->rows]: its rows are the blocked dimension
-    if (elem_is_wide(out->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    if (elem_is_6bit(out->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (out->rows % 8) return FP4_ERR_SHAPE;
     if (out->rows * out->cols != 0) {
         if (ld_x < out->rows) return FP4_ERR_SHAPE;

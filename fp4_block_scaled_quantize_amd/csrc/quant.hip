@@ -957,11 +957,16 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
 
 // ROWS: also the row-wise quantization of the same tile from the loaded
 // registers (x read once for both orientations; no transform).
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT, bool ROT, bool ROWS>
-__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && INT ? 4 : 5))))) void k_quantize_t(QTArgs a)
+// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8; the 8-bit
+// grids one byte per element, transposed-only).
+template <typename InT, int BLOCK, bool SR, bool E8M0, int ELEM, bool ROT, bool ROWS>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && ELEM == 1 ? 4 : 5))))) void k_quantize_t(QTArgs a)
 {
+    constexpr bool INT = ELEM == 1;
+    constexpr bool W8 = ELEM >= 2;
     static_assert(!(ROWS && ROT), "the two orientations would need different transforms and maxima");
-    constexpr float QMAX = INT ? 7.0f : 6.0f;    // the grid's largest magnitude
+    static_assert(!(ROWS && W8), "the two-orientation variant writes 4-bit codes");
+    constexpr float QMAX = ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : ELEM == 3 ? 127.0f : 6.0f;   // grid maximum
     constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
     constexpr int NB = RPW / BLOCK;              // blocks per lane
     __shared__ __align__(16) InT tile[kTR * kTC];
@@ -1026,7 +1031,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     // codes of this lane's NB blocks (column `col`, rows rw ..) and their
     // scale bytes; blocks past the end of x (R % BLOCK == 0, so blocks are
     // whole) compute on zeros and are never stored
-    uint32_t packed[NB][BLOCK / 8];
+    uint32_t packed[NB][W8 ? BLOCK / 4 : BLOCK / 8];
     uint32_t sc = 0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -1044,7 +1049,8 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         float inv;
         uint32_t code;
         if (E8M0) {
-            code = scale_code_e8m0(__uint_as_float(m));
+            code = ELEM == 2 ? scale_code_e8m0_emax<8>(__uint_as_float(m))
+                 : ELEM == 3 ? scale_code_e8m0_emax<6>(__uint_as_float(m)) : scale_code_e8m0(__uint_as_float(m));
             inv = e8m0_inv(code);
         } else {
             code = exmy_scale(__uint_as_float(m), d, g, a.f, &inv);
@@ -1055,6 +1061,32 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
             float e[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) e[i] = val[k * 8 + i] * inv;
+            if constexpr (W8) {
+                // one byte per element: the unit's eight codes in two dwords
+                if (SR) {
+                    const uint32_t u = col * (a.R / 8u) + (rb >> 3) + k;  // unit (i >> 3) of x^T
+                    U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+                    uint32_t c[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t r16 = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                        c[i] = ELEM == 2 ? fp8_sr_code(e[i], r16) : int8_sr_code(e[i], r16);
+                    }
+                    packed[b][2 * k] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+                    packed[b][2 * k + 1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+                } else if (ELEM == 2) {
+                    packed[b][2 * k] = fp8_rtn_pack4(e[0], e[1], e[2], e[3]);
+                    packed[b][2 * k + 1] = fp8_rtn_pack4(e[4], e[5], e[6], e[7]);
+                } else {
+                    uint32_t c[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) c[i] = int8_rtn_code(e[i]);
+                    packed[b][2 * k] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+                    packed[b][2 * k + 1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+                }
+                continue;
+            }
             if (SR) {
                 const uint32_t u = col * (a.R / 8u) + (rb >> 3) + k;      // unit (i >> 3) of x^T
                 U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
@@ -1084,7 +1116,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     // and kTR/BLOCK scale bytes), then store whole row pieces: each wave
     // store instruction covers full 128-byte lines of eight output rows,
     // instead of one 8- or 16-byte piece per lane in 64 different rows.
-    constexpr int QB = kTR / 2;                  // code bytes per output row and tile
+    constexpr int QB = W8 ? kTR : kTR / 2;       // code bytes per output row and tile
     constexpr int QP = QB + 16;                  // padded LDS pitch
     constexpr int SB = kTR / BLOCK;              // scale bytes per output row and tile
     static_assert(kTC * (QP + SB) <= kTR * kTC * (int)sizeof(InT), "output stage fits the input tile");
@@ -1093,17 +1125,25 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     __syncthreads();                             // every wave has read its rows of the tile
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        uint8_t* dst = oq + lane * QP + (w * RPW + b * BLOCK) / 2;
-        if (BLOCK == 16) *(u32x2*)dst = u32x2{packed[b][0], packed[b][1]};
-        else *(u32x4*)dst = u32x4{packed[b][0], packed[b][1], packed[b][2], packed[b][3]};
+        if constexpr (W8) {
+            uint8_t* dst = oq + lane * QP + (w * RPW + b * BLOCK);
+#pragma unroll
+            for (int v = 0; v < BLOCK / 16; ++v)
+                *(u32x4*)(dst + 16 * v) =
+                    u32x4{packed[b][4 * v], packed[b][4 * v + 1], packed[b][4 * v + 2], packed[b][4 * v + 3]};
+        } else {
+            uint8_t* dst = oq + lane * QP + (w * RPW + b * BLOCK) / 2;
+            if (BLOCK == 16) *(u32x2*)dst = u32x2{packed[b][0], packed[b][1]};
+            else *(u32x4*)dst = u32x4{packed[b][0], packed[b][1], packed[b][2], packed[b][3]};
+        }
     }
     if (NB == 4) *(uint32_t*)(os + lane * SB + w * NB) = sc;
     else *(uint16_t*)(os + lane * SB + w * NB) = (uint16_t)sc;
     __syncthreads();
 
     const uint32_t rows_here = a.R - r0 < (uint32_t)kTR ? a.R - r0 : (uint32_t)kTR;   // multiple of BLOCK
-    const uint32_t qbytes = rows_here / 2, sbytes = rows_here / BLOCK;
-    const uint64_t qrow = a.R / 2, srow = a.R / BLOCK;
+    const uint32_t qbytes = W8 ? rows_here : rows_here / 2, sbytes = rows_here / BLOCK;
+    const uint64_t qrow = W8 ? a.R : a.R / 2, srow = a.R / BLOCK;
     const bool q16 = (qrow & 15u) == 0;          // 16-byte aligned output rows
     constexpr int QCH = QB / 16;                 // 16-byte chunks per output row
 #pragma unroll
@@ -1113,7 +1153,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         const uint32_t oc = c0 + orow;
         if (oc >= a.C || ch * 16 >= qbytes) continue;
         const u32x4 v4 = *(const u32x4*)(oq + orow * QP + ch * 16);
-        uint8_t* g8 = a.q + (uint64_t)oc * qrow + r0 / 2 + ch * 16;
+        uint8_t* g8 = a.q + (uint64_t)oc * qrow + (W8 ? r0 : r0 / 2) + ch * 16;
         if (q16 && ch * 16 + 16 <= qbytes) {
             __builtin_nontemporal_store(v4, (u32x4*)g8);
         } else {
@@ -1136,33 +1176,46 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 }
 
-template <typename InT, int BLOCK, bool INT, bool ROT, bool ROWS>
+template <typename InT, int BLOCK, int ELEM, bool ROT, bool ROWS>
 static void launch_qt3(const QTArgs& a, bool sr, bool e8, uint32_t blocks, hipStream_t s)
 {
     const dim3 g(blocks), t(kTThreads);
     if (sr) {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, INT, ROT, ROWS>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, INT, ROT, ROWS>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, true, ELEM, ROT, ROWS>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, true, false, ELEM, ROT, ROWS>), g, t, 0, s, a);
     } else {
-        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, INT, ROT, ROWS>), g, t, 0, s, a);
-        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, INT, ROT, ROWS>), g, t, 0, s, a);
+        if (e8) hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, true, ELEM, ROT, ROWS>), g, t, 0, s, a);
+        else hipLaunchKernelGGL((k_quantize_t<InT, BLOCK, false, false, ELEM, ROT, ROWS>), g, t, 0, s, a);
     }
 }
 
 // rows: the two-orientation variant (never with a transform)
 template <typename InT, int BLOCK>
-static void launch_qt2(const QTArgs& a, bool sr, bool e8, bool int4, bool rot, bool rows, uint32_t blocks,
+static void launch_qt2(const QTArgs& a, bool sr, bool e8, int elem, bool rot, bool rows, uint32_t blocks,
                        hipStream_t s)
 {
     if (rows) {
-        if (int4) launch_qt3<InT, BLOCK, true, false, true>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, false, false, true>(a, sr, e8, blocks, s);
-    } else if (int4) {
-        if (rot) launch_qt3<InT, BLOCK, true, true, false>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, true, false, false>(a, sr, e8, blocks, s);
-    } else {
-        if (rot) launch_qt3<InT, BLOCK, false, true, false>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, false, false, false>(a, sr, e8, blocks, s);
+        if (elem == 1) launch_qt3<InT, BLOCK, 1, false, true>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 0, false, true>(a, sr, e8, blocks, s);
+        return;
+    }
+    switch (elem) {
+    case 1:
+        if (rot) launch_qt3<InT, BLOCK, 1, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 1, false, false>(a, sr, e8, blocks, s);
+        break;
+    case 2:
+        if (rot) launch_qt3<InT, BLOCK, 2, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 2, false, false>(a, sr, e8, blocks, s);
+        break;
+    case 3:
+        if (rot) launch_qt3<InT, BLOCK, 3, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 3, false, false>(a, sr, e8, blocks, s);
+        break;
+    default:
+        if (rot) launch_qt3<InT, BLOCK, 0, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 0, false, false>(a, sr, e8, blocks, s);
+        break;
     }
 }
 
@@ -1205,7 +1258,8 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* 
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
     a.signs = p.rht_signs;
-    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, int4 = p.elem == 1, rot = p.rht != 0;
+    const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, rot = p.rht != 0;
+    const int elem = p.elem;
     if (a.amax_src && a.refresh && !e8) {
         if (rot) {
             // the maximum of the column-transformed tensor
@@ -1220,11 +1274,11 @@ hipError_t launch_quantize_t(const QuantLaunch& p, hipStream_t s, const RowOut* 
     }
     const uint32_t blocks = grid_tiles ? grid_tiles : 1;
     if (p.x_bf16) {
-        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
-        else launch_qt2<uint16_t, 32>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
+        if (p.block == 16) launch_qt2<uint16_t, 16>(a, sr, e8, elem, rot, rows != nullptr, blocks, s);
+        else launch_qt2<uint16_t, 32>(a, sr, e8, elem, rot, rows != nullptr, blocks, s);
     } else {
-        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
-        else launch_qt2<float, 32>(a, sr, e8, int4, rot, rows != nullptr, blocks, s);
+        if (p.block == 16) launch_qt2<float, 16>(a, sr, e8, elem, rot, rows != nullptr, blocks, s);
+        else launch_qt2<float, 32>(a, sr, e8, elem, rot, rows != nullptr, blocks, s);
     }
     return hipGetLastError();
 }

@@ -2,7 +2,8 @@
 MXINT8-style symmetric INT8; one byte per element) against the CPU oracle:
 codes, scales and tensor scale bit for bit for every scale encoding, both
 rounding modes, the single-pass and two-pass refreshes and the Hadamard
-transform; dequantization bit for bit; the GEMM within the binary64
+transform; column-wise quantization bit for bit; dequantization bit for
+bit; the GEMM within the binary64
 reference's tolerance on every scale pairing it takes; the paths that do not
 take 8-bit grids reject them.  Every call goes through the C ABI.
 """
@@ -142,6 +143,52 @@ def test_8bit_dequantize_parity(elem, fmt, block, out):
         assert_bytes_equal(f32_bits(host(y)), f32_bits(want), f"{elem} dequant f32")
     else:
         assert_bytes_equal(bf16_bits(y), want, f"{elem} dequant bf16")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("fmt,block,pol", [("e8m0", 32, "none"), ("e8m0", 16, "none"), ("e4m3", 16, "current"),
+                                           ("ue5m3", 32, "current")])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+def test_8bit_transposed_parity(elem, fmt, block, pol, dtype, rounding):
+    """Column-wise quantization on the 8-bit grids: 320 rows (a partial
+    256-row tile) by 200 columns (a partial 64-column tile), against the
+    oracle's quantization of the transpose."""
+    x = _like(320, 200, 720 + block, dtype)
+    st = fq.AmaxState(1) if pol == "current" else None
+    qt = fq.fp4_quantize_transposed(to_device(x), block, fmt, rounding=rounding, amax=pol, state=st, seed=0x5EED,
+                                    offset=5, element=elem)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, block, fmt, pol, stochastic=rounding == "stochastic",
+                                                   seed=0x5EED, offset=5, nthreads=8, elem=elem)
+    tag = f"{elem} {fmt}/{block}/{dtype}/{rounding} transposed"
+    assert_bytes_equal(host(qt.scales), s, f"{tag} scales")
+    assert_bytes_equal(host(qt.q), q, f"{tag} codes")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{tag} tensor_scale")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_8bit_transposed_transform_and_larger(elem):
+    """The column-wise Hadamard transform (its own amax kernel) and a
+    2048 x 1000 tensor (8 x 16 tiles, ragged in columns)."""
+    x = _like(512, 136, 730)
+    st = fq.AmaxState(1)
+    qt = fq.fp4_quantize_transposed(to_device(x), 16, "e4m3", amax="current", state=st, rht_signs=0x13579BDF,
+                                    element=elem)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "current", nthreads=8, rht_signs=0x13579BDF,
+                                                   elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} rht transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} rht transposed scales")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{elem} rht transposed ts")
+    big = _like(2048, 1000, 731)
+    qt = fq.fp4_quantize_transposed(to_device(big), 32, "e8m0", amax="none", rounding="stochastic", seed=4,
+                                    element=elem)
+    torch.cuda.synchronize()
+    q, s, _, _ = oracle.quantize_transposed_tensor(big, 32, "e8m0", "none", stochastic=True, seed=4, nthreads=8,
+                                                   elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} large transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} large transposed scales")
 
 
 def test_8bit_quantize_dequantize_roundtrip_bound():
@@ -298,7 +345,6 @@ def test_8bit_rejected_elsewhere():
     for call in (lambda: fq.fp4_gemm(q8, f8),
                  lambda: fq.fp4_gemm(f8, f4),
                  lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q8),
-                 lambda: fq.fp4_quantize_transposed(xd, 32, "e8m0", amax="none", element="int8"),
                  lambda: fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element="int8")):
         with pytest.raises(fq.Fp4Error) as e:
             call()
