@@ -123,8 +123,8 @@ typedef enum fp4_transform {
  * symmetric grid -127..127 (two's complement, zero unsigned).  448 or 127
  * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
  * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
- * Row-wise quantize, dequantize and fp4_gemm take them; the column-wise and
- * two-orientation calls and fp4_wo_gemm return UNSUPPORTED for them.
+ * Row-wise and column-wise quantize, dequantize and fp4_gemm take them;
+ * the two-orientation call and fp4_wo_gemm return UNSUPPORTED for them.
  * The 6-bit grids (the same page's MXFP6 / MXINT6; reading: the OCP FP6
  * element formats E2M3 and E3M2, and INT6 on -31..31) pack six bits per
  * element as a little-endian bit stream: element c of a row at bits
