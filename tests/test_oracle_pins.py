@@ -1083,3 +1083,37 @@ def test_6bit_tensor_max_maps_to_grid_max(elem, qmax):
     r, c = np.unravel_index(np.argmax(np.abs(x)), x.shape)
     assert s[r, c // 16] == 0x7E
     assert y[r, c] == (qmax if x[r, c] > 0 else -qmax) * 448.0
+
+
+@pytest.mark.parametrize("elem,f8,shift", [("fp6_e2m3", torch.float8_e4m3fn, -6), ("fp6_e3m2", torch.float8_e5m2, -12)])
+def test_fp6_is_scaled_fp8(elem, f8, shift):
+    """The identity behind encoding and decoding FP6 with FP8 conversions:
+    FP6 E2M3 (E3M2) times 2^-6 (2^-12) is FP8 E4M3 (E5M2) with the same low
+    five code bits, and nearest-even FP8 rounding of a scaled value, after
+    the clamp to the FP6 maximum, lands on the scaled FP6 nearest-even
+    result.  torch's float8 types stand in for the FP8 side; the FP6 side
+    is the oracle (itself pinned by brute force above)."""
+    vals = [float(v) for v in _fp6_values(elem)[:32]]
+    top = vals[-1]
+    for code, v in enumerate(vals):
+        b = torch.tensor([v * 2.0 ** shift], dtype=torch.float32).to(f8).view(torch.uint8).item()
+        assert b == code, (elem, code, v, b)
+    mids = [(vals[i] + vals[i + 1]) / 2 for i in range(31)]
+    probe = np.array(mids + vals, dtype=np.float32)
+    probe = np.concatenate([probe, np.nextafter(probe, np.float32(np.inf)), np.nextafter(probe, np.float32(-np.inf)),
+                            np.float32([top * 1.01, top * 1.3])])
+    probe = probe[(probe >= 0) & (probe < 2.0 ** (2 if elem == "fp6_e2m3" else 4) * 2)]
+    x = np.zeros((1, 32 * (probe.size // 31 + 1)), dtype=np.float32)
+    blocks = x.reshape(-1, 32)
+    blocks[:, 0] = 2.0 ** (2 if elem == "fp6_e2m3" else 4)            # E8M0 scale 1
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:probe.size] = probe
+    blocks[:, 1:] = flat.reshape(blocks.shape[0], 31)
+    x = blocks.reshape(1, -1)
+    q, s, _, _ = oracle.quantize_tensor(x, 32, "e8m0", "none", elem=elem)
+    assert np.all(s == 127)
+    big = int.from_bytes(bytes(q[0]), "little")
+    codes = [(big >> (6 * c)) & 63 for c in range(x.shape[1])]
+    hw = torch.from_numpy(np.clip(x[0], -top, top) * np.float32(2.0 ** shift)).to(f8).view(torch.uint8).numpy()
+    for c in range(x.shape[1]):
+        assert codes[c] == (int(hw[c]) & 0x1F) | ((int(hw[c]) >> 2) & 0x20), (elem, c, x[0, c])
