@@ -211,7 +211,8 @@ fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x,
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;
     // x is [out->cols, out->rows]: its rows are the blocked dimension
-    if (elem_is_6bit(out->fmt.element)) return FP4_ERR_UNSUPPORTED;
+    // 6-bit codes: whole 16-byte output chunks need R % 64 == 0
+    if (elem_is_6bit(out->fmt.element) && out->cols % 64) return FP4_ERR_SHAPE;
     if (out->rows % 8) return FP4_ERR_SHAPE;
     if (out->rows * out->cols != 0) {
         if (ld_x < out->rows) return FP4_ERR_SHAPE;

@@ -957,16 +957,19 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
 
 // ROWS: also the row-wise quantization of the same tile from the loaded
 // registers (x read once for both orientations; no transform).
-// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8; the 8-bit
-// grids one byte per element, transposed-only).
+// ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8, 4 FP6 E2M3,
+// 5 FP6 E3M2, 6 INT6; the 8- and 6-bit grids transposed-only, the 6-bit
+// ones with R % 64 == 0 so that every output chunk is 16 whole bytes).
 template <typename InT, int BLOCK, bool SR, bool E8M0, int ELEM, bool ROT, bool ROWS>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && ELEM == 1 ? 4 : 5))))) void k_quantize_t(QTArgs a)
 {
     constexpr bool INT = ELEM == 1;
-    constexpr bool W8 = ELEM >= 2;
+    constexpr bool W8 = ELEM == 2 || ELEM == 3;
+    constexpr bool W6 = ELEM >= 4;
     static_assert(!(ROWS && ROT), "the two orientations would need different transforms and maxima");
-    static_assert(!(ROWS && W8), "the two-orientation variant writes 4-bit codes");
-    constexpr float QMAX = ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : ELEM == 3 ? 127.0f : 6.0f;   // grid maximum
+    static_assert(!(ROWS && (W8 || W6)), "the two-orientation variant writes 4-bit codes");
+    constexpr float QMAX = ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : ELEM == 3 ? 127.0f : ELEM == 4 ? 7.5f
+                         : ELEM == 5 ? 28.0f : ELEM == 6 ? 31.0f : 6.0f;   // grid maximum
     constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
     constexpr int NB = RPW / BLOCK;              // blocks per lane
     __shared__ __align__(16) InT tile[kTR * kTC];
@@ -1031,7 +1034,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     // codes of this lane's NB blocks (column `col`, rows rw ..) and their
     // scale bytes; blocks past the end of x (R % BLOCK == 0, so blocks are
     // whole) compute on zeros and are never stored
-    uint32_t packed[NB][W8 ? BLOCK / 4 : BLOCK / 8];
+    uint32_t packed[NB][W8 ? BLOCK / 4 : W6 ? BLOCK * 3 / 16 : BLOCK / 8];
     uint32_t sc = 0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -1050,7 +1053,9 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         uint32_t code;
         if (E8M0) {
             code = ELEM == 2 ? scale_code_e8m0_emax<8>(__uint_as_float(m))
-                 : ELEM == 3 ? scale_code_e8m0_emax<6>(__uint_as_float(m)) : scale_code_e8m0(__uint_as_float(m));
+                 : ELEM == 3 ? scale_code_e8m0_emax<6>(__uint_as_float(m))
+                 : (ELEM == 5 || ELEM == 6) ? scale_code_e8m0_emax<4>(__uint_as_float(m))
+                 : scale_code_e8m0(__uint_as_float(m));
             inv = e8m0_inv(code);
         } else {
             code = exmy_scale(__uint_as_float(m), d, g, a.f, &inv);
@@ -1061,6 +1066,34 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
             float e[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) e[i] = val[k * 8 + i] * inv;
+            if constexpr (W6) {
+                // six bits per element: unit k's 48 bits at bit 48 k of the block
+                uint64_t bits = 0;
+                if (SR) {
+                    const uint32_t u = col * (a.R / 8u) + (rb >> 3) + k;  // unit (i >> 3) of x^T
+                    U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        bits |= (uint64_t)w6_sr_code<ELEM>(e[i], (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << (6 * i);
+                } else if (ELEM == 6) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) bits |= (uint64_t)w6_rtn_code<ELEM>(e[i]) << (6 * i);
+                } else {
+                    bits = (uint64_t)fp6_rtn_pack4_hw<ELEM>(e[0], e[1], e[2], e[3]) |
+                           ((uint64_t)fp6_rtn_pack4_hw<ELEM>(e[4], e[5], e[6], e[7]) << 24);
+                }
+                // units pair up into three dwords: even k fills dword 3k/2 and
+                // the low half of the next, odd k the high half and the one after
+                if ((k & 1) == 0) {
+                    packed[b][3 * k / 2] = (uint32_t)bits;
+                    packed[b][3 * k / 2 + 1] = (uint32_t)(bits >> 32);
+                } else {
+                    packed[b][3 * (k - 1) / 2 + 1] |= (uint32_t)bits << 16;
+                    packed[b][3 * (k - 1) / 2 + 2] = (uint32_t)(bits >> 16);
+                }
+                continue;
+            }
             if constexpr (W8) {
                 // one byte per element: the unit's eight codes in two dwords
                 if (SR) {
@@ -1116,7 +1149,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     // and kTR/BLOCK scale bytes), then store whole row pieces: each wave
     // store instruction covers full 128-byte lines of eight output rows,
     // instead of one 8- or 16-byte piece per lane in 64 different rows.
-    constexpr int QB = W8 ? kTR : kTR / 2;       // code bytes per output row and tile
+    constexpr int QB = W8 ? kTR : W6 ? kTR * 3 / 4 : kTR / 2;   // code bytes per output row and tile
     constexpr int QP = QB + 16;                  // padded LDS pitch
     constexpr int SB = kTR / BLOCK;              // scale bytes per output row and tile
     static_assert(kTC * (QP + SB) <= kTR * kTC * (int)sizeof(InT), "output stage fits the input tile");
@@ -1125,7 +1158,11 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     __syncthreads();                             // every wave has read its rows of the tile
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        if constexpr (W8) {
+        if constexpr (W6) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(oq + lane * QP + (w * RPW + b * BLOCK) * 3 / 4);
+#pragma unroll
+            for (int v = 0; v < BLOCK * 3 / 16; ++v) dst[v] = packed[b][v];
+        } else if constexpr (W8) {
             uint8_t* dst = oq + lane * QP + (w * RPW + b * BLOCK);
 #pragma unroll
             for (int v = 0; v < BLOCK / 16; ++v)
@@ -1142,8 +1179,8 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     __syncthreads();
 
     const uint32_t rows_here = a.R - r0 < (uint32_t)kTR ? a.R - r0 : (uint32_t)kTR;   // multiple of BLOCK
-    const uint32_t qbytes = W8 ? rows_here : rows_here / 2, sbytes = rows_here / BLOCK;
-    const uint64_t qrow = W8 ? a.R : a.R / 2, srow = a.R / BLOCK;
+    const uint32_t qbytes = W8 ? rows_here : W6 ? rows_here / 4 * 3 : rows_here / 2, sbytes = rows_here / BLOCK;
+    const uint64_t qrow = W8 ? a.R : W6 ? a.R / 4 * 3 : a.R / 2, srow = a.R / BLOCK;
     const bool q16 = (qrow & 15u) == 0;          // 16-byte aligned output rows
     constexpr int QCH = QB / 16;                 // 16-byte chunks per output row
 #pragma unroll
@@ -1153,7 +1190,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
         const uint32_t oc = c0 + orow;
         if (oc >= a.C || ch * 16 >= qbytes) continue;
         const u32x4 v4 = *(const u32x4*)(oq + orow * QP + ch * 16);
-        uint8_t* g8 = a.q + (uint64_t)oc * qrow + (W8 ? r0 : r0 / 2) + ch * 16;
+        uint8_t* g8 = a.q + (uint64_t)oc * qrow + (W8 ? r0 : W6 ? r0 / 4 * 3 : r0 / 2) + ch * 16;
         if (q16 && ch * 16 + 16 <= qbytes) {
             __builtin_nontemporal_store(v4, (u32x4*)g8);
         } else {
@@ -1211,6 +1248,18 @@ static void launch_qt2(const QTArgs& a, bool sr, bool e8, int elem, bool rot, bo
     case 3:
         if (rot) launch_qt3<InT, BLOCK, 3, true, false>(a, sr, e8, blocks, s);
         else launch_qt3<InT, BLOCK, 3, false, false>(a, sr, e8, blocks, s);
+        break;
+    case 4:
+        if (rot) launch_qt3<InT, BLOCK, 4, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 4, false, false>(a, sr, e8, blocks, s);
+        break;
+    case 5:
+        if (rot) launch_qt3<InT, BLOCK, 5, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 5, false, false>(a, sr, e8, blocks, s);
+        break;
+    case 6:
+        if (rot) launch_qt3<InT, BLOCK, 6, true, false>(a, sr, e8, blocks, s);
+        else launch_qt3<InT, BLOCK, 6, false, false>(a, sr, e8, blocks, s);
         break;
     default:
         if (rot) launch_qt3<InT, BLOCK, 0, true, false>(a, sr, e8, blocks, s);

@@ -132,8 +132,9 @@ typedef enum fp4_transform {
  * E3M2: bias 3, largest 28; sign bit 5, subnormals, no reserved codes;
  * nearest-even, saturating.  INT6: six-bit two's complement, zero unsigned.
  * 7.5, 28 or 31 takes the place of 6; the E8M0 offsets are 2, 4 and 4.
- * Row-wise quantize, dequantize and fp4_gemm take them (the other calls
- * return UNSUPPORTED). */
+ * Row-wise quantize, dequantize, fp4_gemm and the column-wise call (with
+ * R % 64 == 0, SHAPE otherwise) take them; the other calls return
+ * UNSUPPORTED. */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,

@@ -187,6 +187,49 @@ def test_wide_grid_edge_shapes(elem):
     assert bool((wide[:, 384:] == -1.0).all())            # padding columns untouched
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("fmt,block,pol", [("e8m0", 32, "none"), ("e8m0", 16, "none"), ("e4m3", 16, "current")])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+def test_6bit_transposed_parity(elem, fmt, block, pol, dtype, rounding):
+    """Column-wise quantization on the 6-bit grids: 320 rows (a partial
+    256-row tile of 64 rows) by 200 columns (a partial 64-column tile)."""
+    x = _like(320, 200, 740 + block, dtype)
+    st = fq.AmaxState(1) if pol == "current" else None
+    qt = fq.fp4_quantize_transposed(to_device(x), block, fmt, rounding=rounding, amax=pol, state=st, seed=0x5EED,
+                                    offset=5, element=elem)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, block, fmt, pol, stochastic=rounding == "stochastic",
+                                                   seed=0x5EED, offset=5, nthreads=8, elem=elem)
+    tag = f"{elem} {fmt}/{block}/{dtype}/{rounding} transposed"
+    assert_bytes_equal(host(qt.scales), s, f"{tag} scales")
+    assert_bytes_equal(host(qt.q), q, f"{tag} codes")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{tag} tensor_scale")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_6bit_transposed_transform_larger_and_shape_rule(elem):
+    x = _like(512, 136, 750)
+    qt = fq.fp4_quantize_transposed(to_device(x), 16, "e4m3", amax="current", rht_signs=0x13579BDF, element=elem)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "current", nthreads=8, rht_signs=0x13579BDF,
+                                                   elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} rht transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} rht transposed scales")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{elem} rht transposed ts")
+    big = _like(2048, 1000, 751)
+    qt = fq.fp4_quantize_transposed(to_device(big), 32, "e8m0", amax="none", rounding="stochastic", seed=4,
+                                    element=elem)
+    torch.cuda.synchronize()
+    q, s, _, _ = oracle.quantize_transposed_tensor(big, 32, "e8m0", "none", stochastic=True, seed=4, nthreads=8,
+                                                   elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} large transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} large transposed scales")
+    with pytest.raises(fq.Fp4Error) as e:                 # R = 96: not a multiple of 64
+        fq.fp4_quantize_transposed(to_device(_like(96, 64, 752)), 32, "e8m0", amax="none", element=elem)
+    assert e.value.status == -3
+
+
 def _gemm_check(c, a_hat, w_hat, rows=None, tag=""):
     if rows is not None:
         a_hat = a_hat[rows]
@@ -322,7 +365,6 @@ def test_6bit_rejected_elsewhere():
         f6 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element="fp6_e3m2" if elem != "fp6_e3m2" else "int6")
         for call in (lambda: fq.fp4_gemm(q6, f6),
                      lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q6),
-                     lambda: fq.fp4_quantize_transposed(xd, 32, "e8m0", amax="none", element=elem),
                      lambda: fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element=elem)):
             with pytest.raises(fq.Fp4Error) as e:
                 call()

@@ -182,9 +182,9 @@ def test_6bit_element_checks():
         t = _tensor(q=FAKE + 4)                        # 6-bit codes need 8-byte alignment
         t.fmt.element = elem
         assert L.fp4_quantize(FAKE, 1, t.cols, ctypes.byref(t), FAKE, 0, 0, None) == -4
-        tt = _tensor(rows=64, cols=32)                 # not on the column-wise path
+        tt = _tensor(rows=64, cols=32)                 # column-wise 6-bit codes need R % 64 == 0
         tt.fmt.element = elem
-        assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -2
+        assert L.fp4_quantize_transposed(FAKE, 1, 64, ctypes.byref(tt), FAKE, 0, 0, None) == -3
         a = _tensor(rows=8, cols=256, scale=3)         # E1M6 scales: no 16-bit type is exact
         b = _tensor(rows=8, cols=256, scale=3)
         a.fmt.element = b.fmt.element = elem
