@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "7ea2be320bea0fdcf67dcc1d054255735e15f4a186493845299dfa42774adfff",
-    "read_bytes": 33784852,
-    "write_bytes": 9453760,
+    "sha256": "e19763091f706f3e5a5dc035f425500cb860939dcefb11fdf7ebb5edc47cc445",
+    "read_bytes": 33786791,
+    "write_bytes": 9453762,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
