@@ -45,8 +45,8 @@ MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
     "sha256": "e19763091f706f3e5a5dc035f425500cb860939dcefb11fdf7ebb5edc47cc445",
-    "read_bytes": 33786791,
-    "write_bytes": 9453762,
+    "read_bytes": 33787494,
+    "write_bytes": 9453760,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
@@ -377,7 +377,7 @@ def leg_8bit(torch, fq, inputs, xs):
             "us_per_call": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del gs, outs
-    for elem, name in (("fp8_e4m3", "mxfp8"), ("int8", "mxint8")):
+    for elem, name in (("fp8_e4m3", "mxfp8"), ("int8", "mxint8"), ("fp6_e2m3", "mxfp6_e2m3"), ("int6", "mxint6")):
         outs = [fq.QTensor.empty(cols, rows, 32, "e8m0", amax="none", element=elem) for _ in xs]
 
         def rec_t(_):
@@ -385,7 +385,7 @@ def leg_8bit(torch, fq, inputs, xs):
                 fq.fp4_quantize_transposed(xs[j], 32, "e8m0", amax="none", out=outs[j], element=elem)
         gs = GraphSet(torch, 1, rec_t)
         ms = time_graphs(torch, gs, 20, 3) / len(xs)
-        nb = n * 2 + n + n // 32 + 8
+        nb = n * 2 + n * fq.ELEMENT_BITS[elem] // 8 + n // 32 + 8
         res[f"{name}_quantize_colwise"] = {
             "us_per_call": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -411,7 +411,7 @@ def leg_8bit(torch, fq, inputs, xs):
                                   "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)}
         del a, w, qa, qw, c, gs
     res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each) and "
-                       "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise (8-bit also column-wise); "
+                       "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise and column-wise; "
                        "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8, INT8 with E4M3 block-16 scales, "
                        "MXFP6 (E2M3) and MXINT6")
     return res
