@@ -110,6 +110,7 @@ def lib():
         "or_rht_forward": (c_int, [c_p, c_int, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
         "or_rht_inverse": (c_int, [c_p, c_i64, c_i64, c_int, ctypes.c_uint32, c_p]),
         "or_f32_to_bf16_array": (None, [c_p, c_p, c_i64]),
+        "or_elem_mag_array": (None, [c_p, c_p, c_p, c_i64, c_int, c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -167,6 +168,20 @@ def e2m1_sr_array(v: np.ndarray, r16: np.ndarray) -> np.ndarray:
     assert r.size == v.size
     out = np.empty(v.size, dtype=np.uint8)
     lib().or_e2m1_sr_array(_ptr(v), _ptr(r), _ptr(out), v.size)
+    return out
+
+
+def elem_mag_array(v: np.ndarray, elem: str, r16: np.ndarray | None = None) -> np.ndarray:
+    """Magnitude codes of the scaled values v on an element grid: nearest
+    rounding, or stochastic with the given 16-bit variates."""
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    out = np.empty(v.size, dtype=np.uint8)
+    if r16 is None:
+        lib().or_elem_mag_array(_ptr(v), None, _ptr(out), v.size, _elem(elem), 0)
+    else:
+        r = np.ascontiguousarray(r16, dtype=np.uint32).ravel()
+        assert r.size == v.size
+        lib().or_elem_mag_array(_ptr(v), _ptr(r), _ptr(out), v.size, _elem(elem), 1)
     return out
 
 

@@ -323,10 +323,15 @@ OR_EXPORT double or_scale_max(int eb, int mb, int sg)
  * (reading: ties to the even code, values above the maximum saturate to
  * it).  Brute force over every code.  Not used for E8M0, whose block rule
  * is the exponent rule below. */
+static int last_finite(const double* etab, int n);
 static int encode_nearest(const double* tab, int n, float u)
 {
     double a = (double)u;
     if (!(a > 0.0)) return 0;          /* 0, negative or NaN: outside contract */
+    /* saturation, explicitly: far above the top the binary64 distances to
+     * the two largest codes are equal and a tie rule would decide */
+    const int top = last_finite(tab, n);
+    if (a >= tab[top]) return top;
     int best = -1;
     double bd = INFINITY;
     for (int c = 0; c < n; ++c) {
@@ -474,19 +479,77 @@ typedef struct {
     int elem;                        /* 0 = E2M1, 1 = INT4 */
 } quant_job;
 
-/* FP8 E4M3 element, stochastic: |v| between adjacent grid magnitudes lo <= |v|
- * < hi rounds up iff u = r16 / 2^16 < (|v| - lo) / (hi - lo) (exact: the
- * spacing is a power of two); |v| at or beyond the largest (448) saturates. */
+/* Index of the largest finite magnitude in a decoded element table: the
+ * E4M3 table's last non-negative code (0x7F) is NaN, so its largest finite
+ * magnitude (448) sits at 0x7E; every FP6 code is finite. */
+static int last_finite(const double* etab, int n)
+{
+    int top = n - 1;
+    while (top > 0 && etab[top] != etab[top]) --top;
+    return top;
+}
+
+/* FP8 E4M3 / FP6 element, stochastic: |v| between adjacent grid magnitudes
+ * lo <= |v| < hi rounds up iff u = r16 / 2^16 < (|v| - lo) / (hi - lo) (exact:
+ * the spacing is a power of two); |v| at or beyond the largest finite
+ * magnitude saturates to it. */
 static int fp8_sr(const double* etab, int n, float v, uint32_t r16)
 {
     double a = fabs((double)v);
     if (a != a) return 0;
-    if (a >= etab[n - 1]) return n - 1;
+    const int top = last_finite(etab, n);
+    if (a >= etab[top]) return top;
     int lo = 0;
-    while (lo + 1 < n && etab[lo + 1] <= a) ++lo;
+    while (lo + 1 < top && etab[lo + 1] <= a) ++lo;
     double frac = (a - etab[lo]) / (etab[lo + 1] - etab[lo]);
     double u = (double)(r16 & 0xFFFFu) / 65536.0;
     return (u < frac) ? lo + 1 : lo;
+}
+
+/* Element magnitude table of the FP8 E4M3 (elem 2) and FP6 (elem 4, 5)
+ * grids; returns the number of non-negative codes. */
+static int elem_table(int elem, double etab[256])
+{
+    if (elem == 4 || elem == 5) {
+        for (int c = 0; c < 32; ++c) etab[c] = or_fp6_decode(c, elem);
+        return 32;
+    }
+    decode_table(4, 3, 1, etab);
+    return fmt_ncodes(4, 3, 1);
+}
+
+/* Magnitude code of the scaled value v on an element grid, nearest or
+ * stochastic (r16 used only when stochastic). */
+static int elem_mag(int elem, const double* etab, int encodes, float v, int stochastic, uint32_t r16)
+{
+    if (stochastic) {
+        switch (elem) {
+        case 0: return or_e2m1_sr(v, r16);
+        case 1: return or_int4_sr(v, r16);
+        case 2: case 4: case 5: return fp8_sr(etab, encodes, v, r16);
+        case 6: return or_int6_sr(v, r16);
+        default: return or_int8_sr(v, r16);
+        }
+    }
+    switch (elem) {
+    case 0: return or_e2m1_rtn(v);
+    case 1: return or_int4_rtn(v);
+    case 2: case 4: case 5: return encode_nearest(etab, encodes, fabsf(v));
+    case 6: return or_int6_rtn(v);
+    default: return or_int8_rtn(v);
+    }
+}
+
+/* Array form of the element rounding on any grid, for exhaustive sweeps in
+ * the tests: the magnitude code of each v[i] (r16 may be null for
+ * nearest rounding). */
+OR_EXPORT void or_elem_mag_array(const float* v, const uint32_t* r16, uint8_t* mag, int64_t n, int elem,
+                                 int stochastic)
+{
+    double etab[256];
+    const int encodes = elem_table(elem, etab);
+    for (int64_t i = 0; i < n; ++i)
+        mag[i] = (uint8_t)elem_mag(elem, etab, encodes, v[i], stochastic, stochastic ? r16[i] : 0u);
 }
 
 static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
@@ -498,14 +561,7 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
     decode_table(J->eb, J->mb, J->sg, tab);
     const int ncodes = fmt_ncodes(J->eb, J->mb, J->sg);
     double etab[256];                               /* FP8 E4M3 / FP6 element magnitudes */
-    int encodes;
-    if (J->elem == 4 || J->elem == 5) {
-        for (int c = 0; c < 32; ++c) etab[c] = or_fp6_decode(c, J->elem);
-        encodes = 32;
-    } else {
-        decode_table(4, 3, 1, etab);
-        encodes = fmt_ncodes(4, 3, 1);
-    }
+    const int encodes = elem_table(J->elem, etab);
     const int64_t qstride = J->cols * elem_bits(J->elem) / 8;
     for (int64_t r = ra; r < rb; ++r) {
         uint8_t* qrow = J->q + (r - J->row0) * qstride;
@@ -541,25 +597,12 @@ static void quantize_rows(const quant_job* J, int64_t ra, int64_t rb)
                 int mag = 0;
                 if (S != 0.0f) {
                     float v = xv * inv;
+                    uint32_t r16 = 0;
                     if (J->stochastic) {
                         uint64_t i = (uint64_t)r * (uint64_t)J->cols + (uint64_t)col;
-                        uint32_t r16 = or_sr_bits(J->seed, J->offset, i);
-                        switch (J->elem) {
-                        case 0: mag = or_e2m1_sr(v, r16); break;
-                        case 1: mag = or_int4_sr(v, r16); break;
-                        case 2: case 4: case 5: mag = fp8_sr(etab, encodes, v, r16); break;
-                        case 6: mag = or_int6_sr(v, r16); break;
-                        default: mag = or_int8_sr(v, r16); break;
-                        }
-                    } else {
-                        switch (J->elem) {
-                        case 0: mag = or_e2m1_rtn(v); break;
-                        case 1: mag = or_int4_rtn(v); break;
-                        case 2: case 4: case 5: mag = encode_nearest(etab, encodes, fabsf(v)); break;
-                        case 6: mag = or_int6_rtn(v); break;
-                        default: mag = or_int8_rtn(v); break;
-                        }
+                        r16 = or_sr_bits(J->seed, J->offset, i);
                     }
+                    mag = elem_mag(J->elem, etab, encodes, v, J->stochastic, r16);
                 }
                 const int neg = (int)(bits_of_f(xv) >> 31);
                 int code;

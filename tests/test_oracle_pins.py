@@ -1117,3 +1117,89 @@ def test_fp6_is_scaled_fp8(elem, f8, shift):
     hw = torch.from_numpy(np.clip(x[0], -top, top) * np.float32(2.0 ** shift)).to(f8).view(torch.uint8).numpy()
     for c in range(x.shape[1]):
         assert codes[c] == (int(hw[c]) & 0x1F) | ((int(hw[c]) >> 2) & 0x20), (elem, c, x[0, c])
+
+
+# ---------------------------------------------------------------------------
+# Exact stochastic-rounding expectation on the FP8 E4M3 and FP6 grids
+# (gonzo_ML/3986 "Стохастическая квантизация": up or down with a probability
+# set by the distance to the neighbours).  Every one of the 2^16 variates is
+# fed in; the set that rounds up must be exactly {r16 < ceil(frac * 2^16)}
+# with frac computed here in exact rationals from the format definitions, and
+# every result must be one of the two neighbours.  Values whose frac * 2^16 is
+# an integer separate "u < frac" from "u <= frac"; values at and beyond the
+# largest finite magnitude check the saturation; subnormal values and values
+# next to a power of two check the binade and subnormal neighbours.
+# ---------------------------------------------------------------------------
+def _e4m3_magnitudes():
+    """Non-negative FP8 E4M3 values written out from the definition: 4
+    exponent bits (bias 7), 3 mantissa bits, exponent 0 subnormal, the
+    all-ones code 0x7F NaN (so 0x7E = 448 is the largest finite)."""
+    out = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        out.append(Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return out
+
+
+def test_e4m3_magnitudes_agree_with_torch():
+    mags = _e4m3_magnitudes()
+    assert mags[-1] == 448 and mags[1] == Fraction(1, 512)
+    dec = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert [Fraction(float(v)) for v in dec] == mags
+
+
+_SR_PROBES = {
+    "fp8_e4m3": [100.5, -100.5, 0.3, 2.0 ** -10, 3 * 2.0 ** -9 + 2.0 ** -11, 2.0 ** -30, 1.0 + 1.0 / 24,
+                 float(np.nextafter(np.float32(2.0), np.float32(0))), 2.0, 0.0, 440.0, 447.9, 448.0, 449.0, 500.0,
+                 1e6, 0.015625 + 2.0 ** -12],
+    "fp6_e2m3": [2.6, -2.6, 0.0625, 0.01, float(np.nextafter(np.float32(1.0), np.float32(0))), 1.0, 7.25, 7.4, 7.5,
+                 8.0, 100.0, 0.0, 3.3, 2.0 ** -20],
+    "fp6_e3m2": [11.0, -11.0, 0.03125, 0.2, float(np.nextafter(np.float32(4.0), np.float32(0))), 4.0, 26.0, 27.9,
+                 28.0, 29.0, 1e5, 0.0, 0.3, 2.0 ** -20],
+}
+
+
+def _grid(elem):
+    if elem == "fp8_e4m3":
+        return _e4m3_magnitudes()
+    return [v for v in _fp6_values(elem)[:32]]
+
+
+@pytest.mark.parametrize("elem", ["fp8_e4m3", "fp6_e2m3", "fp6_e3m2"])
+def test_fp8_fp6_sr_exact_enumeration(elem):
+    grid = _grid(elem)
+    top = len(grid) - 1
+    r16 = np.arange(65536, dtype=np.uint32)
+    for v in _SR_PROBES[elem]:
+        v32 = np.float32(v)
+        mags = oracle.elem_mag_array(np.full(65536, v32, dtype=np.float32), elem, r16)
+        a = abs(Fraction(float(v32)))
+        if a >= grid[top]:
+            assert np.all(mags == top), (elem, v)
+            continue
+        lo = max(i for i in range(top + 1) if grid[i] <= a)
+        frac = (a - grid[lo]) / (grid[lo + 1] - grid[lo])
+        n_up = math.ceil(frac * 65536)
+        assert set(np.unique(mags).tolist()) <= {lo, lo + 1}, (elem, v)
+        up = mags == lo + 1
+        assert np.array_equal(np.nonzero(up)[0], np.arange(n_up)), (elem, v, n_up, int(up.sum()))
+
+
+@pytest.mark.parametrize("elem", ["fp8_e4m3", "fp6_e2m3", "fp6_e3m2"])
+def test_fp8_fp6_rtn_saturates_explicitly(elem):
+    # nearest rounding at and beyond the largest finite magnitude gives its
+    # code (never the NaN code 0x7F of E4M3)
+    grid = _grid(elem)
+    top = len(grid) - 1
+    v = np.array([float(grid[top]), float(grid[top]) * 1.01, 1e9, 3e38], dtype=np.float32)
+    assert np.all(oracle.elem_mag_array(v, elem) == top)
+    assert np.all(oracle.elem_mag_array(-v, elem) == top)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e3m4", "e1m6", "e2m5", "e5m2", "e6m1", "e7m0"])
+def test_scale_encode_saturates_far_above_the_top(fmt):
+    # the largest finite code, also where binary64 can no longer tell the
+    # distances to the two largest values apart
+    top = max(c for c in range(256 if fmt == "ue5m3" else 128) if not oracle.scale_is_nan(fmt, c))
+    for u in (oracle.scale_max(fmt), oracle.scale_max(fmt) * 1.5, 1e30, 3e38):
+        assert oracle.scale_encode(fmt, u) == top, (fmt, u)
