@@ -69,6 +69,8 @@ def lib():
         "fp4_amax_state_destroy": (i32, [vp]),
         "fp4_amax_state_get": (i32, [vp, ctypes.POINTER(u64), ctypes.POINTER(ctypes.c_float)]),
         "fp4_amax_state_set": (i32, [vp, u64, ctypes.c_float]),
+        "fp4_amax_state_fallbacks": (i32, [vp, ctypes.POINTER(u32)]),
+        "fp4_set_exchange_wait": (i32, [u64, ctypes.POINTER(u64)]),
         "fp4_quantize": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
         "fp4_quantize_transposed": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
         "fp4_quantize_both": (i32, [vp, i32, i64, T, T, vp, u64, u64, vp]),
@@ -93,12 +95,34 @@ def _check(status: int, what: str):
         raise Fp4Error(status, what)
 
 
-def _stream(stream) -> int:
+def _stream(stream, device: torch.device | None = None) -> int:
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _on_device(what: str, *tensors: torch.Tensor) -> torch.device:
+    """Every tensor a call hands to the library must be a CUDA tensor, all on
+    one device (the kernels dereference these pointers on that device)."""
+    dev = None
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{what}: every tensor must be a CUDA tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{what}: tensors on different devices ({dev} and {t.device})")
+    return dev
+
+
+def _check_dense_out(out: torch.Tensor, shape: tuple, dtypes: tuple, what: str):
+    """An output the kernels write row by row through (pointer, row stride):
+    exactly the shape, one of the dtypes and unit column stride."""
+    if tuple(out.shape) != tuple(shape) or out.dtype not in dtypes or (out.dim() == 2 and out.numel() != 0
+                                                                         and out.stride(1) != 1):
+        raise ValueError(f"{what}: out must be {list(shape)} with unit column stride and dtype in {dtypes}")
 
 
 # ---------------------------------------------------------------------------
@@ -132,8 +156,10 @@ class QTensor:
 
     def c(self) -> Fp4TensorC:
         # the library reads or writes rows * cols * bits / 8 code bytes and
-        # rows * cols / block scale bytes through these pointers
+        # rows * cols / block scale bytes through these pointers, densely
         qb = self.rows * (self.cols * ELEMENT_BITS[self.element] // 8)
+        if not (self.q.is_contiguous() and self.scales.is_contiguous() and self.tensor_scale.is_contiguous()):
+            raise ValueError("QTensor buffers must be contiguous")
         if self.q.numel() * self.q.element_size() < qb or \
                 self.scales.numel() * self.scales.element_size() < self.rows * (self.cols // self.block) or \
                 self.tensor_scale.numel() < 2:
@@ -167,6 +193,13 @@ class AmaxState:
     def set(self, calls: int, amax: float):
         _check(lib().fp4_amax_state_set(self._h, calls, amax), "fp4_amax_state_set")
 
+    def fallbacks(self) -> int:
+        """Workgroups of single-pass refreshes on this state that gave up
+        waiting for the others and read the whole tensor themselves."""
+        n = ctypes.c_uint32()
+        _check(lib().fp4_amax_state_fallbacks(self._h, ctypes.byref(n)), "fp4_amax_state_fallbacks")
+        return n.value
+
     def close(self):
         if self._h is not None and self._h.value:
             lib().fp4_amax_state_destroy(self._h)
@@ -177,6 +210,39 @@ class AmaxState:
             self.close()
         except Exception:
             pass
+
+
+def set_exchange_wait(ticks: int) -> int:
+    """Set the process-wide bound on a single-pass refresh's wait for the
+    other workgroups (ticks of the 100 MHz device clock); returns the
+    previous bound."""
+    prev = ctypes.c_uint64()
+    _check(lib().fp4_set_exchange_wait(ticks, ctypes.byref(prev)), "fp4_set_exchange_wait")
+    return prev.value
+
+
+# One amax workspace per (device, stream) for calls with the current policy
+# that bring no state: calls on one stream run in order, so they can share
+# it, and no call allocates.
+_default_states: dict = {}
+
+
+def _default_state(device: torch.device, stream_handle: int) -> AmaxState:
+    key = (device.index, stream_handle)
+    st = _default_states.get(key)
+    if st is None:
+        with torch.cuda.device(device):
+            st = AmaxState(1)
+        _default_states[key] = st
+    return st
+
+
+def _resolve_state(amax: str, state: AmaxState | None, device: torch.device, stream_handle: int):
+    if amax == "none" or state is not None:
+        return state
+    if amax == "delayed":
+        raise ValueError("the delayed amax policy needs an AmaxState")
+    return _default_state(device, stream_handle)
 
 
 def _check_out(t: QTensor, rows: int, cols: int, block: int, element: str):
@@ -193,14 +259,17 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
                  out: QTensor | None = None, stream=None, rht_signs: int | None = None,
                  element: str = "e2m1") -> QTensor:
     """Quantize a 2-D fp32/bf16 CUDA tensor (rows may be strided: x.stride(1)
-    must be 1).  CURRENT and DELAYED need an AmaxState; one is created for
-    CURRENT if none is given.  rht_signs (32-bit sign mask) applies the
+    must be 1).  DELAYED needs an AmaxState; CURRENT without one uses a
+    workspace shared by the calls on the same device and stream.  rht_signs (32-bit sign mask) applies the
     blockwise randomized Hadamard transform before quantization; element
     selects the grid: "e2m1" (default), "int4" (-7..7), the one-byte
     "fp8_e4m3" and "int8" (-127..127), or the six-bit "fp6_e2m3",
     "fp6_e3m2" and "int6" (-31..31)."""
     if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype not in DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
+    _on_device("fp4_quantize", x, *(() if out is None else (out.q, out.scales, out.tensor_scale)))
     rows, cols = x.shape
     if out is None:
         out = QTensor.empty(rows, cols, block, scale, rounding, amax, device=x.device, element=element)
@@ -209,14 +278,12 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)
     out.element = element
-    if amax != "none" and state is None:
-        if amax == "delayed":
-            raise ValueError("the delayed amax policy needs an AmaxState")
-        state = AmaxState(1)
+    sh = _stream(stream, x.device)
+    state = _resolve_state(amax, state, x.device, sh)
     out._state = state        # keep the state alive while work is queued
     tc = out.c()
     st = lib().fp4_quantize(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tc),
-                            state.handle if state is not None else None, seed, offset, _stream(stream))
+                            state.handle if state is not None else None, seed, offset, sh)
     _check(st, "fp4_quantize")
     return out
 
@@ -229,6 +296,9 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
     result is the quantized x^T [C, R] (blocks run down the columns of x)."""
     if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype not in DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
+    _on_device("fp4_quantize_transposed", x, *(() if out is None else (out.q, out.scales, out.tensor_scale)))
     r, c = x.shape
     if out is None:
         out = QTensor.empty(c, r, block, scale, rounding, amax, device=x.device, element=element)
@@ -236,16 +306,13 @@ def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3
         _check_out(out, c, r, block, element)
         out.block, out.scale, out.rounding, out.amax = block, scale, rounding, amax
     out.element = element
-    if rht_signs is not None:
-        out.transform, out.rht_signs = "rht", rht_signs & 0xFFFFFFFF
-    if amax != "none" and state is None:
-        if amax == "delayed":
-            raise ValueError("the delayed amax policy needs an AmaxState")
-        state = AmaxState(1)
+    out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)
+    sh = _stream(stream, x.device)
+    state = _resolve_state(amax, state, x.device, sh)
     out._state = state
     tc = out.c()
     st = lib().fp4_quantize_transposed(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tc),
-                                       state.handle if state is not None else None, seed, offset, _stream(stream))
+                                       state.handle if state is not None else None, seed, offset, sh)
     _check(st, "fp4_quantize_transposed")
     return out
 
@@ -258,58 +325,70 @@ def fp4_quantize_both(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rou
     corresponding single-orientation call."""
     if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype not in DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
     r, c = x.shape
     if out is None:
         out = (QTensor.empty(r, c, block, scale, rounding, amax, device=x.device, element=element),
                QTensor.empty(c, r, block, scale, rounding, amax, device=x.device, element=element))
     qr, qc = out
+    _on_device("fp4_quantize_both", x, qr.q, qr.scales, qr.tensor_scale, qc.q, qc.scales, qc.tensor_scale)
     _check_out(qr, r, c, block, element)
     _check_out(qc, c, r, block, element)
     for t in (qr, qc):
         t.block, t.scale, t.rounding, t.amax, t.element = block, scale, rounding, amax, element
-    if amax != "none" and state is None:
-        if amax == "delayed":
-            raise ValueError("the delayed amax policy needs an AmaxState")
-        state = AmaxState(1)
+        t.transform, t.rht_signs = "none", 0
+    sh = _stream(stream, x.device)
+    state = _resolve_state(amax, state, x.device, sh)
     qr._state = qc._state = state
     tr, tcw = qr.c(), qc.c()
     st = lib().fp4_quantize_both(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tr), ctypes.byref(tcw),
-                                 state.handle if state is not None else None, seed, offset, _stream(stream))
+                                 state.handle if state is not None else None, seed, offset, sh)
     _check(st, "fp4_quantize_both")
     return qr, qc
 
 
 def fp4_dequantize(t: QTensor, dtype=torch.float32, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    dev = _on_device("fp4_dequantize", t.q, t.scales, t.tensor_scale, *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.q.device)
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=dev)
+    _check_dense_out(out, (t.rows, t.cols), (torch.float32, torch.bfloat16), "fp4_dequantize")
     tc = t.c()
-    _check(lib().fp4_dequantize(ctypes.byref(tc), out.data_ptr(), DTYPE[out.dtype], out.stride(0), _stream(stream)),
-           "fp4_dequantize")
+    _check(lib().fp4_dequantize(ctypes.byref(tc), out.data_ptr(), DTYPE[out.dtype], out.stride(0),
+                                _stream(stream, dev)), "fp4_dequantize")
     return out
 
 
 def fp4_gemm(a: QTensor, b: QTensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """C[M, N] = A[M, K] @ W[N, K]^T in bf16 (fp32 accumulation)."""
+    dev = _on_device("fp4_gemm", a.q, a.scales, a.tensor_scale, b.q, b.scales, b.tensor_scale,
+                     *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((a.rows, b.rows), dtype=torch.bfloat16, device=a.q.device)
+        out = torch.empty((a.rows, b.rows), dtype=torch.bfloat16, device=dev)
+    _check_dense_out(out, (a.rows, b.rows), (torch.bfloat16,), "fp4_gemm")
     ta, tb = a.c(), b.c()
-    _check(lib().fp4_gemm(ctypes.byref(ta), ctypes.byref(tb), out.data_ptr(), out.stride(0), _stream(stream)),
+    _check(lib().fp4_gemm(ctypes.byref(ta), ctypes.byref(tb), out.data_ptr(), out.stride(0), _stream(stream, dev)),
            "fp4_gemm")
     return out
 
 
 def fp4_wo_gemm(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y[M, N] = X[M, K] (bf16) @ W[N, K]^T with W quantized (bf16 out)."""
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
         raise ValueError("x must be a 2-D bf16 tensor with unit column stride")
+    if x.shape[1] != w.cols:
+        raise ValueError(f"x has {x.shape[1]} columns, the weight {w.cols}")
+    dev = _on_device("fp4_wo_gemm", x, w.q, w.scales, w.tensor_scale, *(() if out is None else (out,)))
     m = x.shape[0]
     if out is None:
-        out = torch.empty((m, w.rows), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((m, w.rows), dtype=torch.bfloat16, device=dev)
+    _check_dense_out(out, (m, w.rows), (torch.bfloat16,), "fp4_wo_gemm")
     tw = w.c()
     _check(lib().fp4_wo_gemm(x.data_ptr(), x.stride(0), m, ctypes.byref(tw), out.data_ptr(), out.stride(0),
-                             _stream(stream)), "fp4_wo_gemm")
+                             _stream(stream, dev)), "fp4_wo_gemm")
     return out
 
 
-__all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_quantize_both", "fp4_dequantize", "fp4_gemm", "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error",
-           "SCALE_FORMATS", "lib", "status_string", "LIB_PATH"]
+__all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_quantize_both", "fp4_dequantize", "fp4_gemm",
+           "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error", "SCALE_FORMATS", "lib", "status_string", "LIB_PATH",
+           "set_exchange_wait"]

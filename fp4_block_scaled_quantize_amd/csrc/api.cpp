@@ -59,7 +59,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 104; }
+int32_t fp4_version(void) { return 105; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -109,7 +109,22 @@ fp4_status fp4_amax_state_get(const fp4_amax_state* st, uint64_t* calls, float* 
     if (hipMemcpy(&h, st->dev, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return FP4_ERR_HIP;
     *calls = st->calls;
     *amax = h.stored;
-    return h.error ? FP4_ERR_HIP : FP4_OK;
+    return FP4_OK;
+}
+
+fp4_status fp4_amax_state_fallbacks(const fp4_amax_state* st, uint32_t* n)
+{
+    if (!st || !n) return FP4_ERR_INVALID_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return FP4_ERR_HIP;
+    if (hipMemcpy(n, &st->dev->fallbacks, sizeof(*n), hipMemcpyDeviceToHost) != hipSuccess) return FP4_ERR_HIP;
+    return FP4_OK;
+}
+
+fp4_status fp4_set_exchange_wait(uint64_t ticks, uint64_t* previous)
+{
+    const uint64_t old = __atomic_exchange_n(&g_exchange_wait_ticks, ticks, __ATOMIC_RELAXED);
+    if (previous) *previous = old;
+    return FP4_OK;
 }
 
 fp4_status fp4_amax_state_set(fp4_amax_state* st, uint64_t calls, float amax)

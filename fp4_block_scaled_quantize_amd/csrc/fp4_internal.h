@@ -21,11 +21,15 @@ bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 //    path holds in registers) writes one partial maximum per workgroup of
 //    the amax kernel; the quantize kernel of the same call reduces them and
 //    stores the result in `stored`, which calls between refreshes read.
-//  - epoch/slot: the single-pass refresh exchanges per-workgroup maxima
-//    through `slot` (64-bit {epoch, max bits} words, one per 64-byte
+//  - epoch/slot/depart: the single-pass refresh exchanges per-workgroup
+//    maxima through `slot` (64-bit {epoch, max bits} words, one per 64-byte
 //    segment so that stores of different workgroups never share a line)
-//    within one launch; `epoch` advances once per such launch, on the device.
-//  - error: set when a single-pass exchange timed out.
+//    within one launch; every workgroup counts itself out in `depart` once
+//    it no longer needs the slots, and the last one advances `epoch` (so
+//    every workgroup of a launch reads the same epoch) and resets `depart`.
+//  - fallbacks: number of workgroups that did not see every other
+//    workgroup's maximum within the wait bound and read the whole tensor
+//    themselves instead (the result is the same either way).
 constexpr int kAmaxParts = 256;
 constexpr int kXchgSlots = 256;
 constexpr int kXchgStride = 8;          // 64-bit words between slots (64 bytes)
@@ -33,8 +37,9 @@ struct AmaxDev {
     float partial[kAmaxParts];
     float stored;
     uint32_t epoch;
-    uint32_t error;
-    uint32_t pad[61];
+    uint32_t fallbacks;
+    uint32_t depart;
+    uint32_t pad[60];
     uint64_t slot[kXchgSlots * kXchgStride];
 };
 static_assert(sizeof(AmaxDev) == 17664, "amax state layout");
@@ -54,8 +59,12 @@ struct QuantLaunch {
     ScaleFmtHost fmt;
     int32_t rht;               // blockwise randomized Hadamard transform first
     uint32_t rht_signs;
-    int32_t elem;              // element grid: 0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8
+    int32_t elem;              // element grid (fp4_element)
 };
+
+// Bound on a single-pass refresh's wait for the other workgroups' maxima, in
+// ticks of the 100 MHz real-time counter (process-wide; 0.2 s by default).
+extern uint64_t g_exchange_wait_ticks;
 
 struct DequantLaunch {
     const uint8_t* q;
@@ -69,7 +78,7 @@ struct DequantLaunch {
     int64_t ld;
     int32_t rht;               // inverse blockwise Hadamard transform last
     uint32_t rht_signs;
-    int32_t elem;              // element grid: 0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8
+    int32_t elem;              // element grid (fp4_element)
 };
 
 hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s);

@@ -222,7 +222,7 @@ constexpr int kQUnroll = 4;                  // units per lane (one load each, a
 // maximum, so the input is read once.
 constexpr int kFThreads = 1024;
 constexpr int kFUnroll = 8;
-constexpr uint64_t kXchgTimeoutTicks = 20000000;   // 0.2 s of the 100 MHz real-time counter
+uint64_t g_exchange_wait_ticks = 20000000;   // 0.2 s of the 100 MHz real-time counter
 
 struct QArgs {
     const void* x;
@@ -237,6 +237,7 @@ struct QArgs {
     ScaleFmt f;
     uint32_t key0, key1, off0, off1;
     uint32_t signs;              // blockwise Hadamard transform sign mask (ROT kernels)
+    uint64_t wait_ticks;         // FUSED: bound on the wait for the other workgroups' maxima
 };
 
 // The tensor maximum of this call: the reduction of the amax kernel's
@@ -269,25 +270,30 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t m)
 // 0 of every workgroup then polls all slots until each carries this
 // launch's epoch.  Flag and value share a word, so single-location
 // coherence suffices and no fence (L2 write-back or invalidate) is needed.
-// The epoch is read from the state at the start and advanced by workgroup 0
-// once it has seen every slot, i.e. after every workgroup has read it, so
-// each launch (graph replays included) gets a fresh epoch.  The launch
-// grid never exceeds one workgroup per CU, so all workgroups are resident
-// together; the poll is still bounded in time and a timeout sets the
-// state's error word instead of hanging.
-// The epoch of this launch: read at the start of the kernel (before any
-// slot of this launch is published), so the read overlaps the data loads.
+// The launch grid never exceeds one workgroup per CU, but other work on the
+// device can still keep some of them from being scheduled, so the poll is
+// bounded in time: a workgroup that gives up takes the maximum of the whole
+// tensor itself (full_tensor_amax), which is the same value, so the result
+// never depends on co-residency.
+// Epochs: every workgroup reads the state's epoch at its start and uses
+// epoch + 1; once it no longer needs the slots it counts itself out in
+// `depart`, and the last workgroup to do so advances the epoch and resets
+// the count.  So the epoch cannot change while any workgroup of the launch
+// has yet to read it, every workgroup of a launch uses the same epoch, and
+// each launch (graph replays included) gets a fresh one.
 __device__ __forceinline__ uint32_t launch_epoch(const AmaxDev* st)
 {
     uint32_t e = __hip_atomic_load(&st->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     return e == 0 ? 1u : e;
 }
 
+// Publishes m and polls; returns true with *gm = the maximum over every
+// workgroup, or false when the wait bound passed first.
 template <int T>
-__device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
+__device__ bool grid_exchange(uint32_t m, uint32_t e, AmaxDev* st, uint64_t wait_ticks, uint32_t* gm)
 {
     __shared__ uint32_t wmax[T / 64];
-    __shared__ uint32_t gmax;
+    __shared__ uint32_t gmax, gok;
     const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     m = wave_umax(m);
     if (lane == 0) wmax[wv] = m;
@@ -306,25 +312,58 @@ __device__ uint32_t grid_amax_bits(uint32_t m, uint32_t e, AmaxDev* st)
             bool mine = true;
             for (uint32_t i = lane; i < nwg; i += 64) {
                 const uint64_t w = __hip_atomic_load(&st->slot[i * kXchgStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                mine = mine && (uint32_t)(w >> 32) == e;
-                tm = tm > (uint32_t)w ? tm : (uint32_t)w;
+                const bool cur = (uint32_t)(w >> 32) == e;
+                mine = mine && cur;
+                if (cur) tm = tm > (uint32_t)w ? tm : (uint32_t)w;
             }
             if (__all(mine)) {
                 done = true;
                 break;
             }
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kXchgTimeoutTicks) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
             __builtin_amdgcn_s_sleep(1);
         }
         tm = wave_umax(tm);
         if (lane == 0) {
-            if (!done) __hip_atomic_store(&st->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (blockIdx.x == 0) __hip_atomic_store(&st->epoch, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             gmax = tm;
+            gok = done ? 1u : 0u;
         }
     }
     __syncthreads();
-    return gmax;
+    *gm = gmax;
+    return gok != 0;
+}
+
+// max |x| (of the blockwise-transformed x with ROT) over the whole tensor,
+// by every thread of the workgroup: the fallback of a single-pass refresh
+// whose exchange gave up.  Unit u = it * T + threadIdx.x, so a block's G
+// units sit in adjacent lanes as in the quantize loop.
+template <typename InT, int T, int G, bool STRIDED, bool ROT>
+__device__ uint32_t full_tensor_amax(const void* x, uint32_t nunits, const FastDiv& upr, int64_t ld, uint32_t signs)
+{
+    __shared__ uint32_t wmax[T / 64];
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t m = 0;
+    for (uint32_t u0 = 0; u0 < nunits; u0 += T) {
+        const uint32_t u = u0 + threadIdx.x;
+        Unit<InT> un;
+        if (u < nunits) un.load(x, unit_offset(u, STRIDED, upr, ld));
+        else un.zero();
+        uint32_t t;
+        if (ROT) {
+            float v[8];
+            un.get(v);
+            rht_forward<G>(v, lane & (G - 1), signs);
+            t = absmax_bits8(v);
+        } else {
+            t = un.absmax();
+        }
+        m = m > t ? m : t;
+    }
+    m = wave_umax(m);
+    if (lane == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return wave_umax(lane < T / 64 ? wmax[lane] : 0u);
 }
 
 // Tensor scale g = amax_t / RN(qmax Smax), qmax the grid's largest
@@ -425,13 +464,23 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     }
 
     float g = 1.0f, d = QMAX;
+    uint32_t departed = 0;                       // FUSED: the departure count before this workgroup's
     if (!E8M0 && a.amax_src) {
         float am;
         if (FUSED) {
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < U; ++j) m = m > __float_as_uint(bm[j]) ? m : __float_as_uint(bm[j]);
-            am = __uint_as_float(grid_amax_bits<T>(m, epoch, a.amax_src));
+            uint32_t gm;
+            if (!grid_exchange<T>(m, epoch, a.amax_src, a.wait_ticks, &gm)) {
+                gm = full_tensor_amax<InT, T, G, STRIDED, ROT>(a.x, a.nunits, a.upr, a.ld, a.signs);
+                if (threadIdx.x == 0)
+                    __hip_atomic_fetch_add(&a.amax_src->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // this workgroup no longer reads the slots or the epoch
+            if (threadIdx.x == 0)
+                departed = __hip_atomic_fetch_add(&a.amax_src->depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            am = __uint_as_float(gm);
         } else {
             am = tensor_amax(a);
         }
@@ -569,6 +618,13 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         }
         if (u < a.nunits) __builtin_nontemporal_store(packed, a.q + u);
     }
+
+    // the last workgroup to leave the slots of a single-pass refresh opens
+    // the next epoch (read only by later launches)
+    if (FUSED && a.amax_src && threadIdx.x == 0 && departed == gridDim.x - 1) {
+        __hip_atomic_store(&a.amax_src->depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.amax_src->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT, int ELEM>
@@ -649,6 +705,7 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
     a.off0 = (uint32_t)p.offset;
     a.off1 = (uint32_t)(p.offset >> 32);
     a.signs = p.rht_signs;
+    a.wait_ticks = __atomic_load_n(&g_exchange_wait_ticks, __ATOMIC_RELAXED);
     const bool sr = p.stochastic != 0, e8 = p.fmt.is_e8m0 != 0, strided = p.ld != p.cols, rot = p.rht != 0;
     const int elem = p.elem;
 

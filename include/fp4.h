@@ -182,14 +182,26 @@ typedef struct fp4_amax_state fp4_amax_state;
 FP4_API fp4_status fp4_amax_state_create(uint32_t interval, fp4_amax_state** out);
 FP4_API fp4_status fp4_amax_state_destroy(fp4_amax_state* state);
 /* Checkpoint: number of quantize calls seen and the stored amax.  Waits for
- * the device to finish outstanding work.  Returns FP4_ERR_HIP if a
- * single-pass refresh of this state ever timed out waiting for the other
- * workgroups of its grid (possible only if other work kept them from being
- * scheduled for 0.2 s); that call's tensor scale is then not reliable.
- * fp4_amax_state_set clears the condition. */
+ * the device to finish outstanding work. */
 FP4_API fp4_status fp4_amax_state_get(const fp4_amax_state* state, uint64_t* calls, float* amax);
-/* Resume: overwrite the call count and stored amax (synchronous copy). */
+/* Resume: overwrite the call count and stored amax (synchronous copy; also
+ * clears the exchange words and the fallback count). */
 FP4_API fp4_status fp4_amax_state_set(fp4_amax_state* state, uint64_t calls, float amax);
+
+/* Single-pass refresh diagnostics.  In a single-pass refresh (see
+ * fp4_quantize) the workgroups exchange their maxima through the state and
+ * each waits a bounded time for all the others; a workgroup that gives up
+ * (other work on the device kept some from being scheduled) reads the whole
+ * tensor to take its maximum itself.  That maximum is the same value, so
+ * codes, scales and tensor scale never depend on it; only the time does.
+ * fp4_amax_state_fallbacks: the number of workgroups that took this path on
+ * this state since its creation or last fp4_amax_state_set (waits for the
+ * device).  fp4_set_exchange_wait: the process-wide wait bound in ticks of
+ * the device's 100 MHz real-time counter (default 20000000, 0.2 s; 0 gives
+ * up after one look at the other workgroups' words), for tests of the
+ * fallback; the previous bound is returned in *previous if not null. */
+FP4_API fp4_status fp4_amax_state_fallbacks(const fp4_amax_state* state, uint32_t* n);
+FP4_API fp4_status fp4_set_exchange_wait(uint64_t ticks, uint64_t* previous);
 
 /*
  * fp4_quantize -- quantize x[rows, cols] (row stride ld_x elements, f32 or

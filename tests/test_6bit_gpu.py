@@ -208,6 +208,40 @@ def test_6bit_transposed_parity(elem, fmt, block, pol, dtype, rounding):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+def test_6bit_transposed_ue5m3_delayed_and_strided(elem):
+    """Column-wise 6-bit quantization with UE5M3 scales at block 32, a delayed
+    maximum across a refresh (interval 3, five calls, the later tensors
+    growing so the stored maximum saturates them), and a row-strided view."""
+    x = _like(320, 200, 760)
+    qt = fq.fp4_quantize_transposed(to_device(x), 32, "ue5m3", amax="current", element=elem)
+    torch.cuda.synchronize()
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 32, "ue5m3", "current", nthreads=8, elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} ue5m3 transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} ue5m3 transposed scales")
+    assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{elem} ue5m3 transposed ts")
+    st = fq.AmaxState(3)
+    ost = oracle.AmaxState(interval=3)
+    for t in range(5):
+        xt = _like(192, 136, 761 + t, "f32") * np.float32(1.0 + 0.5 * t)
+        qt = fq.fp4_quantize_transposed(to_device(xt), 16, "e4m3", amax="delayed", state=st, element=elem,
+                                        rounding="stochastic" if t % 2 else "nearest", seed=9, offset=t)
+        torch.cuda.synchronize()
+        q, s, g, a = oracle.quantize_transposed_tensor(xt, 16, "e4m3", "delayed", state=ost, nthreads=8, elem=elem,
+                                                       stochastic=bool(t % 2), seed=9, offset=t)
+        assert_bytes_equal(host(qt.q), q, f"{elem} delayed call {t} codes")
+        assert_bytes_equal(host(qt.scales), s, f"{elem} delayed call {t} scales")
+        assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, a]), f"{elem} delayed call {t} ts")
+    xs = _like(256, 200, 770, "f32")
+    wide = torch.zeros((256, 264), dtype=torch.float32, device="cuda")
+    wide[:, :200] = torch.from_numpy(xs).cuda()
+    qt = fq.fp4_quantize_transposed(wide[:, :200], 32, "e8m0", amax="none", element=elem)
+    torch.cuda.synchronize()
+    q, s, _, _ = oracle.quantize_transposed_tensor(xs, 32, "e8m0", "none", nthreads=8, elem=elem)
+    assert_bytes_equal(host(qt.q), q, f"{elem} strided transposed codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} strided transposed scales")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 def test_6bit_transposed_transform_larger_and_shape_rule(elem):
     x = _like(512, 136, 750)
     qt = fq.fp4_quantize_transposed(to_device(x), 16, "e4m3", amax="current", rht_signs=0x13579BDF, element=elem)

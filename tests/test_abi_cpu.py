@@ -207,3 +207,60 @@ def test_binding_refuses_buffers_too_small_for_the_grid():
     with pytest.raises(ValueError):
         fq._check_out(q4, 4, 64, 16, "int8")
     fq._check_out(q4, 4, 64, 16, "int4")
+
+
+class _NoCalls:
+    """Stands in for the library: any call is a test failure."""
+    def __getattr__(self, name):
+        raise AssertionError(f"library function {name} reached")
+
+
+def test_binding_checks_every_buffer_before_any_call(monkeypatch):
+    import torch
+    monkeypatch.setattr(fq, "lib", lambda: _NoCalls())
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    q = fq.QTensor.empty(4, 64, 16, "e4m3", device="cpu")
+    # host tensors never reach the kernels
+    for call in (lambda: fq.fp4_quantize(x), lambda: fq.fp4_quantize_transposed(x.t().contiguous().t()[:, :]),
+                 lambda: fq.fp4_quantize_both(x), lambda: fq.fp4_dequantize(q), lambda: fq.fp4_gemm(q, q),
+                 lambda: fq.fp4_wo_gemm(x, q)):
+        with pytest.raises(ValueError):
+            call()
+    # a weight with a different K than x
+    w = fq.QTensor.empty(8, 128, 16, "e4m3", device="cpu")
+    with pytest.raises(ValueError, match="columns"):
+        fq.fp4_wo_gemm(x, w)
+    # outputs: exact shape, dtype and unit column stride
+    fq._check_dense_out(torch.empty(4, 8, dtype=torch.bfloat16), (4, 8), (torch.bfloat16,), "t")
+    for bad in (torch.empty(3, 8, dtype=torch.bfloat16), torch.empty(4, 8, dtype=torch.float32),
+                torch.empty(8, 4, dtype=torch.bfloat16).t()):
+        with pytest.raises(ValueError):
+            fq._check_dense_out(bad, (4, 8), (torch.bfloat16,), "t")
+    # quantized buffers must be dense
+    q.q = torch.empty(4, 64, dtype=torch.uint8)[:, ::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        q.c()
+
+
+def test_transposed_call_resets_a_reused_outputs_transform(monkeypatch):
+    """A reused output that carried the Hadamard transform must not keep it
+    on a later call without one (the format the library receives is
+    checked through a recording stand-in for the library)."""
+    import torch
+    seen = []
+
+    class _Rec:
+        def fp4_quantize_transposed(self, xp, dt, ld, tc, st, seed, off, s):
+            t = tc._obj
+            seen.append((t.fmt.transform, t.fmt.transform_signs))
+            return 0
+
+    monkeypatch.setattr(fq, "lib", lambda: _Rec())
+    monkeypatch.setattr(fq, "_on_device", lambda what, *t: torch.device("cpu"))
+    monkeypatch.setattr(fq, "_stream", lambda stream, device=None: 0)
+    x = torch.zeros(32, 16, dtype=torch.bfloat16)
+    out = fq.QTensor.empty(16, 32, 16, "e8m0", amax="none", device="cpu")
+    fq.fp4_quantize_transposed(x, 16, "e8m0", amax="none", out=out, rht_signs=0x1234)
+    fq.fp4_quantize_transposed(x, 16, "e8m0", amax="none", out=out)
+    assert seen == [(1, 0x1234), (0, 0)]
+    assert out.transform == "none" and out.rht_signs == 0

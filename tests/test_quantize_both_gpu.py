@@ -107,12 +107,21 @@ def test_both_grads_sampled_and_matches_single_calls():
     assert st.get()[0] == 1
 
 
-def test_both_rejects_mismatch_and_transform():
-    xd = to_device(_like(64, 64, 62))
-    with pytest.raises(fq.Fp4Error) as e:
-        fq.fp4_quantize_both(xd, 16, "e4m3", out=(fq.QTensor.empty(64, 64, 16, "e4m3"),
-                                                  fq.QTensor.empty(64, 64, 16, "e4m3", transform="rht", rht_signs=3)))
-    assert e.value.status == -2
+def test_both_reused_transformed_output_and_mismatch():
+    """A reused output that carried the Hadamard transform is quantized
+    without it (the two-orientation call takes no transform; the library's
+    own UNSUPPORTED for a transformed operand is checked through the ABI on
+    the CPU)."""
+    x = _like(64, 64, 62)
+    xd = to_device(x)
+    qr, qc = fq.fp4_quantize_both(xd, 16, "e4m3", out=(fq.QTensor.empty(64, 64, 16, "e4m3"),
+                                                       fq.QTensor.empty(64, 64, 16, "e4m3", transform="rht",
+                                                                        rht_signs=3)))
+    torch.cuda.synchronize()
+    assert qc.transform == "none" and qc.rht_signs == 0
+    q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "current", nthreads=8)
+    assert_bytes_equal(host(qc.q), q, "reused colwise codes")
+    assert_bytes_equal(host(qc.scales), s, "reused colwise scales")
     # a column-wise output of the wrong shape: the binding refuses it before
     # the call (the library's own SHAPE status is checked through the ABI
     # on the CPU)
