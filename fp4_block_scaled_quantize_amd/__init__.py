@@ -72,6 +72,7 @@ def lib():
         "fp4_amax_state_fallbacks": (i32, [vp, ctypes.POINTER(u32)]),
         "fp4_set_exchange_wait": (i32, [u64, ctypes.POINTER(u64)]),
         "fp4_quantize": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
+        "fp4_quantize_noalloc": (i32, [vp, i32, i64, T, u64, u64, vp]),
         "fp4_quantize_transposed": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
         "fp4_quantize_both": (i32, [vp, i32, i64, T, T, vp, u64, u64, vp]),
         "fp4_dequantize": (i32, [T, vp, i32, i64, vp]),
@@ -288,6 +289,28 @@ def fp4_quantize(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding
     return out
 
 
+def fp4_quantize_noalloc(x: torch.Tensor, out: QTensor, block: int = 16, scale: str = "e4m3",
+                         rounding: str = "nearest", amax: str = "current", seed: int = 0, offset: int = 0,
+                         stream=None, rht_signs: int | None = None, element: str = "e2m1") -> QTensor:
+    """fp4_quantize into a caller-provided output with no allocation: the
+    current-amax workspace is the library's static per-device array (calls
+    that overlap on one device must be ordered by the caller).  Policies
+    "none" and "current"."""
+    if x.dim() != 2 or (x.stride(1) != 1 and x.numel() != 0):
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype not in DTYPE:
+        raise ValueError("x must be float32 or bfloat16")
+    _on_device("fp4_quantize_noalloc", x, out.q, out.scales, out.tensor_scale)
+    rows, cols = x.shape
+    _check_out(out, rows, cols, block, element)
+    out.block, out.scale, out.rounding, out.amax, out.element = block, scale, rounding, amax, element
+    out.transform, out.rht_signs = ("none", 0) if rht_signs is None else ("rht", rht_signs & 0xFFFFFFFF)
+    tc = out.c()
+    _check(lib().fp4_quantize_noalloc(x.data_ptr(), DTYPE[x.dtype], x.stride(0), ctypes.byref(tc), seed, offset,
+                                      _stream(stream, x.device)), "fp4_quantize_noalloc")
+    return out
+
+
 def fp4_quantize_transposed(x: torch.Tensor, block: int = 16, scale: str = "e4m3", rounding: str = "nearest",
                             amax: str = "current", state: AmaxState | None = None, seed: int = 0, offset: int = 0,
                             out: QTensor | None = None, stream=None, element: str = "e2m1",
@@ -391,4 +414,4 @@ def fp4_wo_gemm(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None, st
 
 __all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_quantize_both", "fp4_dequantize", "fp4_gemm",
            "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error", "SCALE_FORMATS", "lib", "status_string", "LIB_PATH",
-           "set_exchange_wait"]
+           "set_exchange_wait", "fp4_quantize_noalloc"]

@@ -6,8 +6,10 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
-#include <new>
 #include <stdint.h>
+
+#include <atomic>
+#include <new>
 
 #include "fp4_internal.h"
 
@@ -169,11 +171,11 @@ static fp4_status check_tensor(const fp4_tensor* t, ScaleFmtHost* f)
 
 static fp4_status hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 
-fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out, fp4_amax_state* state,
-                        uint64_t seed, uint64_t offset, void* stream)
+// Checks of fp4_quantize's arguments other than the amax state.
+static fp4_status check_quantize_args(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
+                                      ScaleFmtHost* f)
 {
-    ScaleFmtHost f;
-    fp4_status st = check_tensor(out, &f);
+    fp4_status st = check_tensor(out, f);
     if (st != FP4_OK) return st;
     if (!x && out->rows * out->cols != 0) return FP4_ERR_INVALID_ARG;
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
@@ -181,17 +183,16 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     if (ld_x < out->cols) return FP4_ERR_SHAPE;
     // an empty x is never read (a [rows, 0] tensor may carry row stride 1)
     if (out->rows * out->cols != 0 && (!aligned16(x) || (ld_x * esz) % 16)) return FP4_ERR_ALIGN;
-    const int32_t pol = out->fmt.amax;
-    if (f.is_e8m0 && pol != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
-    if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
-    hipStream_t s = (hipStream_t)stream;
+    if (f->is_e8m0 && out->fmt.amax != FP4_AMAX_NONE) return FP4_ERR_UNSUPPORTED;
+    return FP4_OK;
+}
 
-    AmaxDev* src = nullptr;
-    bool refresh = false;
-    if (pol != FP4_AMAX_NONE) {
-        refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
-        src = state->dev;
-    }
+// The row-wise quantize launch with the amax workspace `src` (null under
+// NONE) and whether this call takes its own tensor maximum.
+static fp4_status quantize_launch(const void* x, int32_t x_dtype, int64_t ld_x, const fp4_tensor* out,
+                                  const ScaleFmtHost& f, AmaxDev* src, bool refresh, uint64_t seed, uint64_t offset,
+                                  hipStream_t s)
+{
     QuantLaunch p;
     p.x = x;
     p.x_bf16 = x_dtype == FP4_DTYPE_BF16;
@@ -211,9 +212,74 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
     p.rht = out->fmt.transform == FP4_TRANSFORM_RHT;
     p.rht_signs = out->fmt.transform_signs;
     p.elem = out->fmt.element;
-    st = hip_status(launch_quantize(p, s));
+    return hip_status(launch_quantize(p, s));
+}
+
+fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out, fp4_amax_state* state,
+                        uint64_t seed, uint64_t offset, void* stream)
+{
+    ScaleFmtHost f;
+    fp4_status st = check_quantize_args(x, x_dtype, ld_x, out, &f);
+    if (st != FP4_OK) return st;
+    const int32_t pol = out->fmt.amax;
+    if (pol != FP4_AMAX_NONE && !state) return FP4_ERR_INVALID_ARG;
+    AmaxDev* src = nullptr;
+    bool refresh = false;
+    if (pol != FP4_AMAX_NONE) {
+        refresh = (pol == FP4_AMAX_CURRENT) || (state->calls % state->interval == 0);
+        src = state->dev;
+    }
+    st = quantize_launch(x, x_dtype, ld_x, out, f, src, refresh, seed, offset, (hipStream_t)stream);
     if (st == FP4_OK && state && pol != FP4_AMAX_NONE) state->calls += 1;
     return st;
+}
+
+// ---------------------------------------------------------------------------
+// fp4_quantize_noalloc: the amax workspace of a current-amax call lives in
+// this static device array instead of an fp4_amax_state.  Its size does not
+// depend on the tensor: the single-pass refresh uses at most kXchgSlots
+// exchange words and the two-pass refresh exactly kAmaxParts partials.  It
+// is zero at load; each single-pass launch leaves `depart` at zero again and
+// the two-pass refresh overwrites every partial, so nothing needs clearing
+// per call.  Host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's own (host-side) name.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = sizeof(AmaxDev);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<AmaxDev*> g_scratch_ptr[kMaxDevices];
+
+static fp4_status scratch_of_current_device(AmaxDev** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FP4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FP4_ERR_UNSUPPORTED;
+    AmaxDev* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return FP4_ERR_HIP;
+        p = static_cast<AmaxDev*>(a);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return FP4_OK;
+}
+
+fp4_status fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out, uint64_t seed,
+                                uint64_t offset, void* stream)
+{
+    ScaleFmtHost f;
+    fp4_status st = check_quantize_args(x, x_dtype, ld_x, out, &f);
+    if (st != FP4_OK) return st;
+    const int32_t pol = out->fmt.amax;
+    if (pol == FP4_AMAX_DELAYED) return FP4_ERR_UNSUPPORTED;   // the stored maximum belongs to one tensor
+    AmaxDev* src = nullptr;
+    if (pol == FP4_AMAX_CURRENT) {
+        st = scratch_of_current_device(&src);
+        if (st != FP4_OK) return st;
+    }
+    return quantize_launch(x, x_dtype, ld_x, out, f, src, pol == FP4_AMAX_CURRENT, seed, offset,
+                           (hipStream_t)stream);
 }
 
 fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,

@@ -244,6 +244,25 @@ FP4_API fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp
                         fp4_amax_state* state, uint64_t seed, uint64_t offset, void* stream);
 
 /*
+ * fp4_quantize_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): fp4_quantize with the policies NONE and CURRENT, the same
+ * result bit for bit, but the current-amax workspace (17664 bytes) comes
+ * from a static device array of the library, one per device, held until
+ * the process ends, instead of an fp4_amax_state.  The workspace does not
+ * grow with the tensor, so no size is refused on its account (fp4_quantize's
+ * own limits apply).  The caller passes x and out as for fp4_quantize;
+ * nothing is allocated or freed, on any call.  The first call on a device
+ * looks up that device's array address (with the device current).
+ * Every call on a device shares that one array: calls that overlap on one
+ * device (different streams, or threads without ordering) race and must be
+ * ordered by the caller.  Errors as fp4_quantize; UNSUPPORTED for DELAYED
+ * (the stored maximum belongs to one tensor and needs an fp4_amax_state).
+ */
+FP4_API fp4_status fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* out,
+                                        uint64_t seed, uint64_t offset, void* stream);
+
+/*
  * fp4_quantize_transposed -- column-wise quantization for the backward
  * pass: out describes x^T, where x is [out->cols, out->rows] (row stride
  * ld_x elements, f32 or bf16), so each block holds `block` consecutive rows

@@ -264,3 +264,18 @@ def test_transposed_call_resets_a_reused_outputs_transform(monkeypatch):
     fq.fp4_quantize_transposed(x, 16, "e8m0", amax="none", out=out)
     assert seen == [(1, 0x1234), (0, 0)]
     assert out.transform == "none" and out.rht_signs == 0
+
+
+def test_quantize_noalloc_rejects_before_launch():
+    """The no-allocation quantize validates like fp4_quantize and refuses the
+    delayed policy before touching the device."""
+    L = fq.lib()
+    t = _tensor(rows=4, cols=64)
+    assert L.fp4_quantize_noalloc(FAKE, 1, 64, None, 0, 0, None) == -1
+    t.fmt.amax = 2
+    assert L.fp4_quantize_noalloc(FAKE, 1, 64, ctypes.byref(t), 0, 0, None) == -2
+    t.fmt.amax = 1
+    t.fmt.scale = 4                                     # E8M0 with a tensor scale
+    assert L.fp4_quantize_noalloc(FAKE, 1, 64, ctypes.byref(t), 0, 0, None) == -2
+    t.fmt.scale = 0
+    assert L.fp4_quantize_noalloc(FAKE, 1, 32, ctypes.byref(t), 0, 0, None) == -3   # ld < cols
