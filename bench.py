@@ -61,6 +61,9 @@ def measured_traffic():
         return None
     return MEASURED_TRAFFIC["read_bytes"] + MEASURED_TRAFFIC["write_bytes"]
 MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+# the one kernel each GEMM call launches, by the operands' scale encoding
+GEMM_KERNEL = {"e8m0": "k_gemm_mx (scaled FP4 MFMA)", "e4m3": "k_gemm_nv (FP4->f16 in registers, f16 MFMA)",
+               "ue5m3": "k_gemm_dq (bf16 dequantized in LDS, bf16 MFMA)"}
 
 SWEEP = [("e4m3", 16, "current"), ("ue5m3", 16, "current"), ("e3m4", 16, "current"), ("e1m6", 16, "current"),
          ("e8m0", 32, "none")]
@@ -173,9 +176,23 @@ def leg_sr(torch, fq, inputs, steps):
     ms = time_graphs(torch, gs, reps, 1)
     total = ntens * quant_bytes(rows, cols, 16)
     gbs = total / (ms * 1e-3) / 1e9
-    del xs
+    del gs
+    # the same sequence with round-to-nearest: the row-wise kernel's rate at
+    # 8192^2 (4 of the 200 calls also read the tensor for the refresh)
+    outs_n = [fq.QTensor.empty(rows, cols, 16, "e4m3", rounding="nearest", amax="delayed") for _ in range(2)]
+    st_n = fq.AmaxState(50)
+
+    def rec_n(_):
+        for t in range(ntens):
+            fq.fp4_quantize(xs[t], 16, "e4m3", rounding="nearest", amax="delayed", state=st_n, out=outs_n[t % 2])
+    gs = GraphSet(torch, 1, rec_n)
+    ms_n = time_graphs(torch, gs, reps, 1)
+    gbs_n = total / (ms_n * 1e-3) / 1e9
+    del xs, gs
     return {"workload": "200 x 8192x8192 bf16 Laplace(1e-4) grads, E4M3 B16, SR Philox, delayed amax N=50",
-            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ms_per_sequence": round(ms, 3)}
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ms_per_sequence": round(ms, 3),
+            "rtn": {"GB/s": round(gbs_n, 1), "frac_hbm": round(gbs_n / HBM_PEAK_GBS, 4),
+                    "ms_per_sequence": round(ms_n, 3), "us_per_call": round(ms_n * 1e3 / ntens, 2)}}
 
 
 def leg_sr_transposed(torch, fq, inputs, steps):
@@ -281,11 +298,14 @@ def leg_dequant(torch, fq, xs):
 
 def leg_gemm(torch, fq, inputs):
     """Llama-2 7B linears at M = 8192: both operands quantized NVFP4 (E4M3
-    block 16, exact dequantize path on bf16/f16 matrix cores) and MXFP4
-    (E8M0 block 32, native scaled FP4 matrix cores)."""
+    block 16, exact in-register FP4->f16 path on f16 matrix cores), MXFP4
+    (E8M0 block 32, native scaled FP4 matrix cores) and UE5M3 block 16
+    (ue5m3-fp4-pretraining "Что сделали": every linear in FP4 with UE5M3
+    scales; exact bf16 path)."""
     shapes = {"up": (11008, 4096), "down": (4096, 11008), "sq": (4096, 4096)}
     res = {}
-    for fmt, block, pol, peak in [("e8m0", 32, "none", "fp4"), ("e4m3", 16, "current", "bf16")]:
+    for fmt, block, pol, peak in [("e8m0", 32, "none", "fp4"), ("e4m3", 16, "current", "bf16"),
+                                  ("ue5m3", 16, "current", "bf16")]:
         for name, (n, k) in shapes.items():
             m = 8192
             a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
@@ -307,7 +327,12 @@ def leg_gemm(torch, fq, inputs):
             res[f"{fmt}_{name}"] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
                                     "frac_fp4_peak": round(tf / MFMA_PEAK_TFLOPS["fp4"], 4),
                                     "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4),
-                                    "frac_path_peak": round(tf / MFMA_PEAK_TFLOPS[peak], 4)}
+                                    "frac_path_peak": round(tf / MFMA_PEAK_TFLOPS[peak], 4),
+                                    "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                                 "peak": MFMA_PEAK_TFLOPS[peak], "unit": "TFLOP/s",
+                                                 "frac": round(tf / MFMA_PEAK_TFLOPS[peak], 4),
+                                                 "kernel": GEMM_KERNEL[fmt], "us_per_launch": round(ms * 1e3, 2),
+                                                 "algo_flops_per_launch": 2 * m * n * k, "traffic": None}}
             del a, w, qa, qw, c, gs
     return res
 
@@ -443,20 +468,37 @@ def leg_wo(torch, fq, inputs):
             algo = n * k // 2 + n * k // 16 + 8 + m * k * 2 + m * n * 2
             gbs = algo / (ms * 1e-3) / 1e9
             res[f"{name}_m{m}"] = {"M": m, "N": n, "K": k, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                                "kernel": "k_wo_gemm", "us_per_launch": round(ms * 1e3, 2),
+                                                "algo_bytes_per_launch": algo, "traffic": None}}
         del qws
     return res
 
 
-def cpu_baseline(min_seconds=10.0):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(min_seconds=10.0, one_thread_seconds=4.0):
     """The CPU oracle (as written, not tuned) on the whole sweep workload:
     full steps (the 4096x4096 tensor through all five formats) repeated
-    until at least min_seconds of CPU time have passed; same bytes
-    accounting as the GPU step."""
+    until at least min_seconds have passed on min(16, usable cores) threads;
+    then one thread on single E4M3 calls for about one_thread_seconds.  Same
+    bytes accounting as the GPU step."""
     import oracle
     import fp4_inputs as inputs
     x = inputs.sweep()
-    threads = min(16, os.cpu_count() or 1)
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = min(16, usable)
     rows, cols = x.shape
     step_bytes = sum(quant_bytes(rows, cols, b) for _, b, _ in SWEEP)
     steps = 0
@@ -468,8 +510,19 @@ def cpu_baseline(min_seconds=10.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    calls = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.quantize_tensor(x, 16, "e4m3", "current", nthreads=1)
+        calls += 1
+        dt1 = time.perf_counter() - t1
+        if dt1 >= one_thread_seconds:
+            break
     return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full sweep steps (4096x4096 bf16, 5 formats) in {dt:.1f} s"}
+            "sample": f"{steps} full sweep steps (4096x4096 bf16, 5 formats) in {dt:.1f} s",
+            "host_cores_usable": usable, "host_cores_total": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": round(calls * quant_bytes(rows, cols, 16) / dt1 / 1e9, 4), "unit": "GB/s",
+                           "sample": f"{calls} E4M3 block-16 calls on the sweep tensor in {dt1:.1f} s"}}
 
 
 def main():
@@ -509,6 +562,16 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     step_bytes = sum(quant_bytes(rows, cols, b) for _, b, _ in SWEEP)
     value = step_bytes / (ms * 1e-3) / 1e9
+
+    # quantization error per format on the sweep tensor (fp64 mean squared
+    # error of the dequantized tensor; gonzo_ML/3986 "Форматы FP4" compares
+    # the scale encodings by the loss they reach)
+    mse = {}
+    ref = xs[0].double()
+    for f, b, p in SWEEP:
+        y = fq.fp4_dequantize(outs[f][0], torch.float32)
+        mse[f"{f}_b{b}"] = float(((y.double() - ref) ** 2).mean())
+    del ref, y
 
     roof = leg_roofline(torch, fq, xs)
     if args.copy_probe:
@@ -553,7 +616,7 @@ def main():
                                    "E4M3/UE5M3/E3M4/E1M6 block 16 (current amax) + E8M0 block 32, RTN",
                        "rows": rows, "cols": cols, "formats": [f for f, _, _ in SWEEP],
                        "rotating_inputs": args.rot, "bytes_per_step": step_bytes},
-            "roofline": roof, "cpu_baseline": cpu, "legs": legs}
+            "quantization_mse": mse, "roofline": roof, "cpu_baseline": cpu, "legs": legs}
     print(json.dumps(line), flush=True)
 
 

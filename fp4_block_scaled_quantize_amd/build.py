@@ -24,7 +24,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-fvisibility=hidden"]
 PER_FILE = {
-    "quant.hip": ["-ffp-contract=off"],
+    # no wave-level aggregation of atomics: it waits for the returned value
+    # at once, where the single-pass refresh needs it only at the end
+    "quant.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
     "api.cpp": ["-ffp-contract=off"],
 }
 SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]

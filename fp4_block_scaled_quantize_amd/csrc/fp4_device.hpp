@@ -125,20 +125,79 @@ __device__ __forceinline__ uint32_t e2m1_rtn_sw(float v)
     return (uint32_t)c | ((f_bits(v) >> 28) & 8u);
 }
 
-// Stochastic E2M1 code of v with 16 random bits r16: the lower grid
-// neighbour lo and the position frac in [0,1) to the upper one are exact;
-// the magnitude rounds up iff r16 < frac * 2^16.
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r16)
+// Stochastic E2M1 codes through the gfx950 scaled SR conversion.  The
+// reading: the magnitude rounds up from its lower grid neighbour lo iff
+// r16 / 2^16 < frac, frac = (|v| - lo) / (hi - lo).  Measured behaviour of
+// v_cvt_scalef32_sr_pk_fp4_f32 on its first element: with the scale's power
+// of two 2^k it takes w = v / 2^k and rounds up iff
+// floor(frac(w) * 2^32) + seed >= 2^32 (the second element derives its
+// random bits from the seed differently, so it is always given 0 here).
+// Two exact steps make that rule the reading's:
+//  - w is |v| rounded up to a multiple of 2^-17 (sign kept), passed as
+//    ceil(|v| 2^17) with scale 2^17.  Every grid spacing is at least 1/2, so
+//    frac(w) * 2^16 rounds frac(v) * 2^16 up to the next multiple of
+//    2^-1, 2^-2 or 2^-3 (never past the next integer: the comparison with
+//    the integer r16 is unchanged), and frac(w) * 2^32 is an integer.
+//  - seed = 2^32 - 1 - r16 * 2^16 = (~r16 << 16) | 0xFFFF, so the rule reads
+//    r16 * 2^16 < frac(w) * 2^32.
+// |v| >= 6 (and infinities) saturate to 6 as in the reading; the sign of v,
+// zero included, is kept.  Checked against the reading on every binary32
+// within 3000 ulps of each grid point and midpoint, 300000 random values
+// below 7 (subnormals included) and values next to multiples of 2^-17, at
+// the boundary variates of each and random ones.
+__device__ __forceinline__ float e2m1_sr_operand(float v)
 {
-    float a = __builtin_fabsf(v);
-    float sp = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
-    float off = a < 2.0f ? 0.0f : (a < 4.0f ? 2.0f : 4.0f);
-    float t = a * sp;                       // exact: power-of-two scaling
-    float fl = __builtin_floorf(t);
-    float frac = t - fl;                    // exact
-    float up = ((float)r16 < frac * 65536.0f) ? 1.0f : 0.0f;
-    float c = a >= 6.0f ? 7.0f : fl + off + up;
-    return (uint32_t)c | ((f_bits(v) >> 28) & 8u);
+    return __builtin_copysignf(__builtin_ceilf(__builtin_fabsf(v) * 0x1p17f), v);
+}
+
+typedef float fp4_f2 __attribute__((ext_vector_type(2)));
+
+// The conversion writes byte J of its destination and keeps the other three
+// (checked on the device).  The compiler's builtin for it does not tie the
+// destination to the value passed as the old one, so the instruction is
+// written here with the destination as an in/out operand.
+template <int J>
+__device__ __forceinline__ uint32_t e2m1_sr_byte(uint32_t old, float v, uint32_t seed)
+{
+    const fp4_f2 pr = {e2m1_sr_operand(v), 0.0f};
+    const float scale = 0x1p17f;
+    if constexpr (J == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(old) : "v"(pr), "v"(seed), "s"(scale));
+    else if constexpr (J == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(old) : "v"(pr), "v"(seed), "s"(scale));
+    else if constexpr (J == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(old) : "v"(pr), "v"(seed), "s"(scale));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(old) : "v"(pr), "v"(seed), "s"(scale));
+    return old;
+}
+
+// Four stochastic E2M1 codes, element k in nibble k, from the 16-bit halves
+// of two random words (element 2j takes the low half of w[j], 2j + 1 the
+// high half).
+__device__ __forceinline__ uint32_t e2m1_sr_pack4(float v0, float v1, float v2, float v3, uint32_t w0, uint32_t w1)
+{
+    const uint32_t n0 = ~w0, n1 = ~w1;
+    uint32_t even = e2m1_sr_byte<0>(0u, v0, (n0 << 16) | 0xFFFFu);
+    uint32_t odd = e2m1_sr_byte<0>(0u, v1, n0 | 0xFFFFu);
+    even = e2m1_sr_byte<1>(even, v2, (n1 << 16) | 0xFFFFu);
+    odd = e2m1_sr_byte<1>(odd, v3, n1 | 0xFFFFu);
+    return even | (odd << 4);
+}
+
+// Eight stochastic E2M1 codes, element k in nibble k (the units' layout).
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float v[8], uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    const uint32_t n0 = ~w0, n1 = ~w1, n2 = ~w2, n3 = ~w3;
+    uint32_t even = e2m1_sr_byte<0>(0u, v[0], (n0 << 16) | 0xFFFFu);
+    uint32_t odd = e2m1_sr_byte<0>(0u, v[1], n0 | 0xFFFFu);
+    even = e2m1_sr_byte<1>(even, v[2], (n1 << 16) | 0xFFFFu);
+    odd = e2m1_sr_byte<1>(odd, v[3], n1 | 0xFFFFu);
+    even = e2m1_sr_byte<2>(even, v[4], (n2 << 16) | 0xFFFFu);
+    odd = e2m1_sr_byte<2>(odd, v[5], n2 | 0xFFFFu);
+    even = e2m1_sr_byte<3>(even, v[6], (n3 << 16) | 0xFFFFu);
+    odd = e2m1_sr_byte<3>(odd, v[7], n3 | 0xFFFFu);
+    return even | (odd << 4);
 }
 
 // E2M1 magnitude code -> value (exact): code 0..7 -> 0,.5,1,1.5,2,3,4,6.

@@ -281,9 +281,17 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t m)
 // the count.  So the epoch cannot change while any workgroup of the launch
 // has yet to read it, every workgroup of a launch uses the same epoch, and
 // each launch (graph replays included) gets a fresh one.
-__device__ __forceinline__ uint32_t launch_epoch(const AmaxDev* st)
+// The state's epoch word, loaded at the start of the kernel (before any slot
+// of this launch is published, so the load overlaps the data loads);
+// launch_epoch turns it into this launch's epoch once the data loads are
+// in flight.
+__device__ __forceinline__ uint32_t epoch_word(const AmaxDev* st)
 {
-    uint32_t e = __hip_atomic_load(&st->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    return __hip_atomic_load(&st->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t launch_epoch(uint32_t word)
+{
+    const uint32_t e = word + 1u;
     return e == 0 ? 1u : e;
 }
 
@@ -432,8 +440,9 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     const uint32_t base = wave * (64u * U);
 
     // issue every load first
-    uint32_t epoch = 0;                          // used by wave 0 only
-    if (FUSED && a.amax_src && threadIdx.x < 64) epoch = launch_epoch(a.amax_src);
+    // (FUSED kernels always have a state; every wave loads the word so no
+    // branch ties the wait for it to the load)
+    const uint32_t eword = FUSED ? epoch_word(a.amax_src) : 0u;
     Unit<InT> un[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -441,6 +450,7 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         if (u < a.nunits) un[j].load(a.x, unit_offset(u, STRIDED, a.upr, a.ld));
         else un[j].zero();
     }
+    const uint32_t epoch = launch_epoch(eword);
 
     // the transformed values (ROT only; units past the end are zeros, and a
     // block's units are all in range or all out of it)
@@ -599,12 +609,16 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         }
         if (SR) {
             U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
-            const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-            packed = 0;
+            if (INT) {
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+                packed = 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                packed |= (INT ? int4_sr_code(v[k], r16) : e2m1_sr(v[k], r16)) << (4 * k);
+                for (int k = 0; k < 8; ++k) {
+                    uint32_t r16 = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                    packed |= int4_sr_code(v[k], r16) << (4 * k);
+                }
+            } else {
+                packed = e2m1_sr_pack8(v, r.x, r.y, r.z, r.w);
             }
         } else if (INT) {
             packed = 0;
@@ -985,11 +999,19 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
             const U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
             const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
             const uint32_t e0 = gc & 7u;                                   // first element of the piece in its unit
+            if (INT) {
 #pragma unroll
-            for (int i = 0; i < EPP; ++i) {
-                const uint32_t e = e0 + i;
-                const uint32_t r16 = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                packed |= (INT ? int4_sr_code(v[i], r16) : e2m1_sr(v[i], r16)) << (4 * i);
+                for (int i = 0; i < EPP; ++i) {
+                    const uint32_t e = e0 + i;
+                    const uint32_t r16 = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    packed |= int4_sr_code(v[i], r16) << (4 * i);
+                }
+            } else if (EPP == 8) {
+                packed = e2m1_sr_pack8(v, r.x, r.y, r.z, r.w);
+            } else {
+                // a 4-element piece: the first or second half of its unit
+                packed = e0 ? e2m1_sr_pack4(v[0], v[1], v[2 % EPP], v[3 % EPP], r.z, r.w)
+                            : e2m1_sr_pack4(v[0], v[1], v[2 % EPP], v[3 % EPP], r.x, r.y);
             }
         } else if (INT) {
 #pragma unroll
@@ -1180,12 +1202,16 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
             if (SR) {
                 const uint32_t u = col * (a.R / 8u) + (rb >> 3) + k;      // unit (i >> 3) of x^T
                 U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
-                const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
                 uint32_t pk = 0;
+                if (INT) {
+                    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t r16 = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                    pk |= (INT ? int4_sr_code(e[i], r16) : e2m1_sr(e[i], r16)) << (4 * i);
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t r16 = (wd[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                        pk |= int4_sr_code(e[i], r16) << (4 * i);
+                    }
+                } else {
+                    pk = e2m1_sr_pack8(e, r.x, r.y, r.z, r.w);
                 }
                 packed[b][k] = pk;
             } else if (INT) {
