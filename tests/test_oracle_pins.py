@@ -1203,3 +1203,13 @@ def test_scale_encode_saturates_far_above_the_top(fmt):
     top = max(c for c in range(256 if fmt == "ue5m3" else 128) if not oracle.scale_is_nan(fmt, c))
     for u in (oracle.scale_max(fmt), oracle.scale_max(fmt) * 1.5, 1e30, 3e38):
         assert oracle.scale_encode(fmt, u) == top, (fmt, u)
+
+
+def test_sr_boundary_tensor_hits_both_outcomes():
+    """The GPU boundary test's tensor (every element next to its own SR
+    decision boundary) does exercise both outcomes in the oracle."""
+    from tests.test_sr_boundary_gpu import SEED, OFFSET, _boundary_tensor
+    x = _boundary_tensor(64, 256, SEED, OFFSET)
+    q, _ = oracle.quantize(x, 32, "e8m0", 1.0, stochastic=True, seed=SEED, offset=OFFSET)
+    qn, _ = oracle.quantize(x, 32, "e8m0", 1.0)
+    assert ((q & 15) != (qn & 15)).any() and ((q & 15) == (qn & 15)).any()

@@ -100,14 +100,3 @@ def test_both_orientations_rowwise_sr_boundaries(dtype):
     q2, s2, _, _ = oracle.quantize_transposed_tensor(xo, 32, "e8m0", "none", stochastic=True, seed=SEED,
                                                      offset=OFFSET + 2, nthreads=8)
     assert_bytes_equal(host(qc.q), q2, f"{dtype} both-call column-wise SR codes")
-
-
-@pytest.mark.skipif(False, reason="")
-def test_boundary_construction_hits_both_sides():
-    """The constructed tensor does exercise both outcomes near the boundary
-    (a check of the oracle's decisions on it)."""
-    x = _boundary_tensor(64, 256, SEED, OFFSET)
-    q, _ = oracle.quantize(x, 32, "e8m0", 1.0, stochastic=True, seed=SEED, offset=OFFSET)
-    qn, _ = oracle.quantize(x, 32, "e8m0", 1.0)
-    lo_nib = (q & 15).astype(int)
-    assert (lo_nib != (qn & 15)).any() and (lo_nib == (qn & 15)).any()
