@@ -62,8 +62,10 @@ def measured_traffic():
     return MEASURED_TRAFFIC["read_bytes"] + MEASURED_TRAFFIC["write_bytes"]
 MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 # the one kernel each GEMM call launches, by the operands' scale encoding
-GEMM_KERNEL = {"e8m0": "k_gemm_mx (scaled FP4 MFMA)", "e4m3": "k_gemm_nv (FP4->f16 in registers, f16 MFMA)",
-               "ue5m3": "k_gemm_dq (bf16 dequantized in LDS, bf16 MFMA)"}
+GEMM_KERNEL = {("e8m0", 32): "k_gemm_mx (scaled FP4 MFMA)",
+               ("e4m3", 16): "k_gemm_nv (FP4->f16 in registers, f16 MFMA)",
+               ("ue5m3", 16): "k_gemm_dq (bf16 dequantized in LDS, bf16 MFMA)",
+               ("e8m0", 16): "k_gemm_mx16 (scaled FP4 MFMA, two instructions per K-half)"}
 
 SWEEP = [("e4m3", 16, "current"), ("ue5m3", 16, "current"), ("e3m4", 16, "current"), ("e1m6", 16, "current"),
          ("e8m0", 32, "none")]
@@ -305,7 +307,7 @@ def leg_gemm(torch, fq, inputs):
     shapes = {"up": (11008, 4096), "down": (4096, 11008), "sq": (4096, 4096)}
     res = {}
     for fmt, block, pol, peak in [("e8m0", 32, "none", "fp4"), ("e4m3", 16, "current", "bf16"),
-                                  ("ue5m3", 16, "current", "bf16")]:
+                                  ("ue5m3", 16, "current", "bf16"), ("e8m0", 16, "none", "fp4")]:
         for name, (n, k) in shapes.items():
             m = 8192
             a = inputs.device_normal((m, k), 0.02, inputs.SEEDS["llama_a"], torch.bfloat16)
@@ -313,10 +315,11 @@ def leg_gemm(torch, fq, inputs):
             qa = fq.fp4_quantize(a, block, fmt, amax=pol)
             qw = fq.fp4_quantize(w, block, fmt, amax=pol)
             c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            key = f"{fmt}_{name}" if block == (32 if fmt == "e8m0" else 16) else f"{fmt}_b{block}_{name}"
             try:
                 fq.fp4_gemm(qa, qw, out=c)
             except fq.Fp4Error as e:
-                res[f"{fmt}_{name}"] = {"error": str(e)}
+                res[key] = {"error": str(e)}
                 continue
 
             def rec(_):
@@ -324,14 +327,14 @@ def leg_gemm(torch, fq, inputs):
             gs = GraphSet(torch, 1, rec)
             ms = time_graphs(torch, gs, 10, 2)
             tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-            res[f"{fmt}_{name}"] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
+            res[key] = {"M": m, "N": n, "K": k, "TFLOP/s": round(tf, 1), "ms": round(ms, 4),
                                     "frac_fp4_peak": round(tf / MFMA_PEAK_TFLOPS["fp4"], 4),
                                     "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4),
                                     "frac_path_peak": round(tf / MFMA_PEAK_TFLOPS[peak], 4),
                                     "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                                  "peak": MFMA_PEAK_TFLOPS[peak], "unit": "TFLOP/s",
                                                  "frac": round(tf / MFMA_PEAK_TFLOPS[peak], 4),
-                                                 "kernel": GEMM_KERNEL[fmt], "us_per_launch": round(ms * 1e3, 2),
+                                                 "kernel": GEMM_KERNEL[(fmt, block)], "us_per_launch": round(ms * 1e3, 2),
                                                  "algo_flops_per_launch": 2 * m * n * k, "traffic": None}}
             del a, w, qa, qw, c, gs
     return res

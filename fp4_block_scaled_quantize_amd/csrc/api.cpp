@@ -456,6 +456,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     p.elem = a->fmt.element;
     hipStream_t s = (hipStream_t)stream;
     if (p.elem == FP4_ELEM_E2M1 && fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
+    if (gemm_mx16_supported(p)) return hip_status(launch_gemm_mx16(p, s));
     if (!gemm_dq_supported(fa, fb, p.elem)) return FP4_ERR_UNSUPPORTED;
     return hip_status(launch_gemm_dq(p, s));
 }

@@ -108,6 +108,10 @@ struct GemmLaunch {
 // every element * scale product of both operands exactly.
 bool gemm_dq_supported(const ScaleFmtHost& fa, const ScaleFmtHost& fb, int elem);
 hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s);
+// E2M1 with E8M0 scales at block 16 on the scaled FP4 matrix instruction,
+// when the stage shape fits.
+bool gemm_mx16_supported(const GemmLaunch& p);
+hipError_t launch_gemm_mx16(const GemmLaunch& p, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
 
 struct WoGemmLaunch {

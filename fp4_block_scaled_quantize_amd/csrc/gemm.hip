@@ -22,6 +22,8 @@
 // Both compute the transposed tile D = W A^T so that each lane owns four
 // consecutive output columns of C (one 8-byte store).  Workgroup tile
 // 256 x 256, four waves of 128 x 128, K double-buffered through LDS.
+#include <type_traits>
+
 #include "fp4_device.hpp"
 #include "fp4_internal.h"
 
@@ -491,6 +493,206 @@ hipError_t launch_gemm_mx(const GemmLaunch& p, hipStream_t s)
 {
     if (p.k % 256 == 0 && p.k >= 512) return launch_mx<256, 2>(p, s);
     return launch_mx<128, 4>(p, s);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 with E8M0 scales per 16 elements (gonzo_ML/3986 "Форматы FP4": groups
+// of 16 with power-of-two scales) on the scaled FP4 matrix instruction.  The
+// instruction takes one scale per 32-element K-half of each operand (lane l
+// supplies row l % 32 and the 32 elements of K-half l / 32 in 4 dwords,
+// scaled by its own scale byte), so every 64-element step runs twice: first
+// with A's second 16-element block of every K-half zeroed, then its first,
+// each time with both operands' scales of the block that remains.  W keeps
+// all its elements: they meet zeros in the other block, so the products are
+// exactly those of the block whose scales are applied.  Twice the matrix
+// instructions of MXFP4, no dequantization.
+//
+// Same tile, waves, DMA and stage shape as k_gemm_mx: stages of 256
+// elements (128 bytes per row), two stages, scale groups of 32 bytes per
+// row (two stages each).
+//
+// (The instruction also takes FP8 E4M3 operands with E8M0 scales: there
+// dwords 0-3 of both lane groups form the first 32-element block, scaled by
+// the byte of lanes 0-31, and dwords 4-7 the second, scaled by the byte of
+// lanes 32-63 -- measured on the device.  A GEMM of MXFP8 operands on it,
+// checked against the exact product, missed the 1e-5 sum|a||b| bound on a
+// few outputs in 10^4 whose operands spread over many binades, so FP8 stays
+// on the exact dequantize path.)
+// ---------------------------------------------------------------------------
+struct Mx16Shape {
+    static constexpr int EPS = 256;                   // elements per stage (128-byte rows)
+    static constexpr int RB = 128;
+    static constexpr int NI = 4;                      // code DMAs per wave per operand (8 rows each)
+    static constexpr int Codes = kTile * RB;          // 32 KiB per operand
+    static constexpr int Bytes = 2 * Codes;
+    static constexpr int SRow = 16;                   // scale bytes per row per stage
+    static constexpr int GS = 2;                      // stages per 32-byte scale group
+    static constexpr int GroupBytes = 2 * kTile * 32; // W then A
+    static constexpr int NKS = 4;                     // 64-element steps per stage
+};
+
+// The scaled matrix instruction taking byte SEL of each operand's scale
+// dword (the instruction's own byte select).
+template <int SEL>
+__device__ __forceinline__ v16f mfma_fp4_sel(const v8i& w, const v8i& a, const v16f& c, uint32_t sw, uint32_t sa)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 4, SEL, (int)sw, SEL, (int)sa);
+}
+
+__global__ __launch_bounds__(kMx4Threads) void k_gemm_mx16(GemmLaunch p)
+{
+    using L = Mx16Shape;
+    constexpr int NS = 2;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;            // 2 x 4 waves: 128 (n) x 64 (m) each
+    const int64_t M = p.m, N = p.n, K = p.k;
+    int tn, tm;
+    tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
+    const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
+    const int64_t rowb = K / 2, rows = K / 16;
+    const int KT = (int)(K / L::EPS);
+    auto row_w = [&](int r) { return n_base + r < N ? n_base + r : N - 1; };
+    auto row_a = [&](int r) { return m_base + r < M ? m_base + r : M - 1; };
+
+    // 32-bit byte offsets of this lane's loads (the launch requires every
+    // operand buffer below 4 GiB), so the loads take a uniform 64-bit base
+    uint32_t offw[L::NI], offa[L::NI];
+#pragma unroll
+    for (int k = 0; k < L::NI; ++k) {
+        const int r = 8 * (L::NI * wave + k) + lane / 8;
+        const int c = (lane % 8) ^ mx_swz<256>(r);
+        offw[k] = (uint32_t)(row_w(r) * rowb + 16 * c);
+        offa[k] = (uint32_t)(row_a(r) * rowb + 16 * c);
+    }
+    // scale groups: two lanes per row, each 16 bytes; LDS unit 2 r + u of
+    // row r holds the row's 16-byte half u ^ b3(r).  A half past the row end
+    // (the last, partial group) is read from the row's last 16 bytes.
+    const int grow = tid >> 1;
+    const int ghalf = (tid & 1) ^ ((grow >> 3) & 1);
+    const uint32_t goff[2] = {(uint32_t)(row_w(grow) * rows), (uint32_t)(row_a(grow) * rows)};
+    uint8_t* const gbuf = smem + NS * L::Bytes;
+
+    auto issue = [&](int kt, int buf, int part) {
+        const int ks = kt < KT ? kt : KT - 1;
+        uint8_t* st = smem + buf * L::Bytes;
+        const uint8_t* bw = p.qb + (int64_t)ks * L::RB;
+        const uint8_t* ba = p.qa + (int64_t)ks * L::RB;
+#pragma unroll
+        for (int k = part * L::NI / 2; k < (part + 1) * L::NI / 2; ++k) {
+            dma16(bw + offw[k], st + 1024 * (L::NI * wave + k));
+            dma16(ba + offa[k], st + L::Codes + 1024 * (L::NI * wave + k));
+        }
+        if (part == 0 && kt % L::GS == 0 && kt < KT) {
+            const int64_t off = (int64_t)(kt / L::GS) * 32 + 16 * ghalf;
+            const uint32_t o = (uint32_t)(off + 16 <= rows ? off : rows - 16);
+            uint8_t* const gb = gbuf + ((kt / L::GS) & 1) * L::GroupBytes;
+            dma16(p.sb + (goff[0] + o), gb + 1024 * wave);
+            dma16(p.sa + (goff[1] + o), gb + L::GroupBytes / 2 + 1024 * wave);
+        }
+    };
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+
+    issue(0, 0, 0);
+    issue(0, 0, 1);
+
+    const int frow = lane & 31, khalf = lane >> 5;
+    // byte 2 (ks & 1) + run of gathered dword ks >> 1 is this lane's block
+    // 2 (2 ks + khalf) + run of the stage: one byte permute per dword
+    const uint32_t psel = khalf ? 0x07060302u : 0x05040100u;
+    for (int kt = 0; kt < KT; ++kt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        const uint8_t* st = smem + (kt % NS) * L::Bytes;
+        // this stage's 16 scale bytes of each fragment row: half h of its
+        // group, which starts at min(32 g + 16 h, rows - 16) of the row
+        const int g = kt / L::GS, h = kt % L::GS;
+        const uint8_t* gb = gbuf + (g & 1) * L::GroupBytes;
+        uint32_t swg[4][2], sag[2][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wn * 128 + 32 * i + frow;
+            const uint4 v = *reinterpret_cast<const uint4*>(gb + 32 * r + 16 * (h ^ ((r >> 3) & 1)));
+            swg[i][0] = __builtin_amdgcn_perm(v.y, v.x, psel);
+            swg[i][1] = __builtin_amdgcn_perm(v.w, v.z, psel);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wm * 64 + 32 * j + frow;
+            const uint4 v = *reinterpret_cast<const uint4*>(gb + L::GroupBytes / 2 + 32 * r + 16 * (h ^ ((r >> 3) & 1)));
+            sag[j][0] = __builtin_amdgcn_perm(v.y, v.x, psel);
+            sag[j][1] = __builtin_amdgcn_perm(v.w, v.z, psel);
+        }
+        auto read_frags = [&](int ks, v4i (&wf)[4], v4i (&af)[2]) {
+            const int c = 2 * ks + khalf;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wn * 128 + 32 * i + frow;
+                wf[i] = *reinterpret_cast<const v4i*>(st + r * L::RB + 16 * (c ^ mx_swz<256>(r)));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = wm * 64 + 32 * j + frow;
+                af[j] = *reinterpret_cast<const v4i*>(st + L::Codes + r * L::RB + 16 * (c ^ mx_swz<256>(r)));
+            }
+        };
+        v4i wf[2][4], af[2][2];
+        read_frags(0, wf[0], af[0]);
+        // one 64-element step; the step index is a template constant so the
+        // matrix instructions' byte selects are immediates
+        auto step = [&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            constexpr int cur = ks & 1, dw = ks >> 1;
+            if (ks + 1 < L::NKS) read_frags(ks + 1, wf[cur ^ 1], af[cur ^ 1]);
+            if (ks < 2) issue(kt + 1, (kt + 1) % NS, ks);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const v4i a = af[cur][j];
+                const v8i a0 = {a[0], a[1], 0, 0, 0, 0, 0, 0}, a1 = {0, 0, a[2], a[3], 0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4i w = wf[cur][i];
+                    const v8i wv = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+                    acc[i][j] = mfma_fp4_sel<2 * (ks & 1)>(wv, a0, acc[i][j], swg[i][dw], sag[j][dw]);
+                    acc[i][j] = mfma_fp4_sel<2 * (ks & 1) + 1>(wv, a1, acc[i][j], swg[i][dw], sag[j][dw]);
+                }
+            }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(NS * L::Bytes + 2 * L::GroupBytes >= kCTileBytes, "the C image fits the LDS");
+    const float gg = p.ga[0] * p.gb[0];
+    store_tile_4x2_lds(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
+}
+
+// E2M1 with E8M0 scales at block 16 on both operands, whole 256-element
+// stages, at least 16 scale bytes per row and operands below 4 GiB.
+bool gemm_mx16_supported(const GemmLaunch& p)
+{
+    if (p.elem != 0 || p.block != 16 || !p.fa.is_e8m0 || !p.fb.is_e8m0) return false;
+    if (p.m * (p.k / 2) >= (int64_t(1) << 32) || p.n * (p.k / 2) >= (int64_t(1) << 32)) return false;
+    return p.k % 256 == 0 && p.k / 16 >= 16;
+}
+
+hipError_t launch_gemm_mx16(const GemmLaunch& p, hipStream_t s)
+{
+    using L = Mx16Shape;
+    constexpr size_t sh = (size_t)2 * L::Bytes + 2 * L::GroupBytes;
+    static_assert(sh <= 160 * 1024, "LDS");
+    hipError_t e = allow_lds(k_gemm_mx16, sh);
+    if (e != hipSuccess) return e;
+    const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
+    hipLaunchKernelGGL(k_gemm_mx16, dim3(tiles), dim3(kMx4Threads), sh, s, p);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
