@@ -24,15 +24,20 @@ bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 //  - epoch/slot/depart: the single-pass refresh exchanges per-workgroup
 //    maxima through `slot` (64-bit {epoch, max bits} words, one per 64-byte
 //    segment so that stores of different workgroups never share a line)
-//    within one launch; every workgroup counts itself out in `depart` once
-//    it no longer needs the slots, and the last one advances `epoch` (so
-//    every workgroup of a launch reads the same epoch) and resets `depart`.
+//    within one launch.  Every workgroup counts itself out once it no
+//    longer needs the slots, in two levels: first in the counter of its
+//    departure group (blockIdx % kDepartGroups; group k's counter is word
+//    kDepartWord of slot segment k), and the last of a group then in
+//    `depart`.  The last group advances `epoch` (so every workgroup of a
+//    launch reads the same epoch); each last one resets what it counted.
 //  - fallbacks: number of workgroups that did not see every other
 //    workgroup's maximum within the wait bound and read the whole tensor
 //    themselves instead (the result is the same either way).
 constexpr int kAmaxParts = 256;
 constexpr int kXchgSlots = 256;
 constexpr int kXchgStride = 8;          // 64-bit words between slots (64 bytes)
+constexpr int kDepartGroups = 8;
+constexpr int kDepartWord = 1;          // word of slot segment k holding group k's departures
 struct AmaxDev {
     float partial[kAmaxParts];
     float stored;
