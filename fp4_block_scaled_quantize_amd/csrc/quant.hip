@@ -342,21 +342,39 @@ __device__ bool grid_exchange(uint32_t m, uint32_t e, AmaxDev* st, uint64_t wait
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         uint32_t tm = 0;
         bool done = false;
-        for (;;) {
+        // two poll rounds in flight: a round's answer takes about a
+        // microsecond, and the next one is issued before it is examined, so
+        // the last publication is seen half a round sooner (about 0.5 us of a
+        // 4096 x 4096 launch).  Lanes past the grid reread the last slot.
+        constexpr int SL = kXchgSlots / 64;
+        auto poll = [&](uint64_t (&w)[SL]) {
+#pragma unroll
+            for (int k = 0; k < SL; ++k) {
+                const uint32_t i = lane + 64 * k < nwg ? lane + 64 * k : nwg - 1;
+                w[k] = __hip_atomic_load(&st->slot[i * kXchgStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        // true once every slot holds this epoch (then tm is the maximum) or
+        // the wait bound has passed
+        auto check = [&](const uint64_t (&w)[SL]) {
             tm = 0;
             bool mine = true;
-            for (uint32_t i = lane; i < nwg; i += 64) {
-                const uint64_t w = __hip_atomic_load(&st->slot[i * kXchgStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool cur = (uint32_t)(w >> 32) == e;
-                mine = mine && cur;
-                if (cur) tm = tm > (uint32_t)w ? tm : (uint32_t)w;
+#pragma unroll
+            for (int k = 0; k < SL; ++k) {
+                const bool c = (uint32_t)(w[k] >> 32) == e;
+                mine = mine && c;
+                if (c) tm = tm > (uint32_t)w[k] ? tm : (uint32_t)w[k];
             }
-            if (__all(mine)) {
-                done = true;
-                break;
-            }
-            if (__builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks) break;
-            __builtin_amdgcn_s_sleep(1);
+            done = __all(mine);
+            return done || __builtin_amdgcn_s_memrealtime() - t0 >= wait_ticks;
+        };
+        uint64_t b0[SL], b1[SL];
+        poll(b0);
+        for (;;) {
+            poll(b1);
+            if (check(b0)) break;
+            poll(b0);
+            if (check(b1)) break;
         }
         tm = wave_umax(tm);
         if (lane == 0) {
