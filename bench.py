@@ -64,7 +64,7 @@ MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 # the one kernel each GEMM call launches, by the operands' scale encoding
 GEMM_KERNEL = {("e8m0", 32): "k_gemm_mx (scaled FP4 MFMA)",
                ("e4m3", 16): "k_gemm_nv (FP4->f16 in registers, f16 MFMA)",
-               ("ue5m3", 16): "k_gemm_dq (bf16 dequantized in LDS, bf16 MFMA)",
+               ("ue5m3", 16): "k_gemm_nv (FP4->fp32 x scale->bf16 in registers, bf16 MFMA)",
                ("e8m0", 16): "k_gemm_mx16 (scaled FP4 MFMA, two instructions per K-half)"}
 
 SWEEP = [("e4m3", 16, "current"), ("ue5m3", 16, "current"), ("e3m4", 16, "current"), ("e1m6", 16, "current"),
@@ -303,7 +303,8 @@ def leg_gemm(torch, fq, inputs):
     block 16, exact in-register FP4->f16 path on f16 matrix cores), MXFP4
     (E8M0 block 32, native scaled FP4 matrix cores) and UE5M3 block 16
     (ue5m3-fp4-pretraining "Что сделали": every linear in FP4 with UE5M3
-    scales; exact bf16 path)."""
+    scales; exact in-register bf16 path, since the products leave f16's
+    range)."""
     shapes = {"up": (11008, 4096), "down": (4096, 11008), "sq": (4096, 4096)}
     res = {}
     for fmt, block, pol, peak in [("e8m0", 32, "none", "fp4"), ("e4m3", 16, "current", "bf16"),

@@ -1036,8 +1036,20 @@ struct NvStage {
     static constexpr int kScaleRow = kMx3BK / BLOCK;           // scale bytes per row per stage
     static constexpr int kScales = kTile * kScaleRow;          // per operand
     static constexpr int kBytes = 2 * kMx3Codes + 2 * kScales;
-    static constexpr int kTable = 2 * 256 * 4;                 // f16x2 decode tables of W and A
+    static constexpr int kTable = 2 * 256 * 4;                 // decode tables of W and A (f16x2 or f32)
 };
+
+// How k_gemm_nv turns codes into matrix operands.
+//  kNvTable: f16, block scales decoded through an LDS table;
+//  kNvE4M3: f16, both scale formats E4M3, decoded by the hardware FP8 -> f16
+//    conversion (exact) instead of the table;
+//  kNvBf16: bf16 for the scale formats whose products leave f16's range
+//    (UE5M3: e2m1 * s up to 6 * 2^15 * 1.875): each code pair is converted
+//    to fp32 (scale 1), multiplied by the fp32 block scale from the table
+//    (exact: at most 6 significant bits) and rounded to a bf16 pair, which
+//    is exact.  gfx950 has no packed bf16 multiply, so this costs two VALU
+//    per element where the f16 forms cost one.
+enum { kNvTable = 0, kNvE4M3 = 1, kNvBf16 = 2 };
 
 // 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times
 // the f16 block scale s2 (replicated in both halves).
@@ -1050,6 +1062,22 @@ __device__ __forceinline__ v8h nv_convert8(uint32_t w, v2h s2)
     return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
+// 8 E2M1 codes times the fp32 block scale s, as bf16 (kNvBf16).
+__device__ __forceinline__ v8bf nv_convert8_bf16(uint32_t w, float s)
+{
+    v8bf r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const v2f e = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                    : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                    : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        r[2 * b] = (__bf16)(e[0] * s);
+        r[2 * b + 1] = (__bf16)(e[1] * s);
+    }
+    return r;
+}
+
 // Fragments of one half stage (chunk pair ks) for one lane: four W and two
 // A 16-byte code fragments and their raw scale bytes (block 16: the two
 // scales of the chunk in one u16; block 32: one byte).
@@ -1058,18 +1086,19 @@ struct NvHalf {
     uint32_t sw[4], sa[2];
 };
 
-// HW_E4M3: both scale formats are E4M3, decoded to f16 by the hardware
-// FP8 -> f16 conversion (exact) instead of the LDS table.
+// CVT: one of kNvTable, kNvE4M3, kNvBf16 (above).
 //
 // Schedule of one 128-element stage (per wave): the fragments of half 1 are
 // read from LDS while half 0's products run; the workgroup barrier sits
 // between the halves, and after it the first half of the next stage is
 // read while half 1's products run.  The conversions of each 32x32x16 step
 // are interleaved with the previous step's products.
-template <int BLOCK, int NS, bool HW_E4M3>
+template <int BLOCK, int NS, int CVT>
 __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 {
     using L = NvStage<BLOCK>;
+    constexpr bool HW_E4M3 = CVT == kNvE4M3, BF16 = CVT == kNvBf16;
+    using V8 = std::conditional_t<BF16, v8bf, v8h>;
     static_assert(NS >= 2, "at least two stages");
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* tab = reinterpret_cast<uint32_t*>(smem + NS * L::kBytes);   // [2][256] f16x2
@@ -1082,13 +1111,20 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     const int64_t rowb = K / 2, rows = K / BLOCK;
     const int KT = (int)(K / kMx3BK);
 
-    // scale code -> f16 (exact for these formats), replicated for packed math
+    // scale code -> f16 (exact for these formats), replicated for packed
+    // math; or -> fp32 for the bf16 form, which (as the dequantize path)
+    // folds the power-of-two part of each tensor scale into the operand's
+    // scales so that products of wide-range scales (E7M0: up to 2^63) stay
+    // inside binary32
+    const float pw = BF16 ? split_pow2(p.gb[0]) : 1.0f, pa = BF16 ? split_pow2(p.ga[0]) : 1.0f;
     if (!HW_E4M3) {
         const int t = tid & 255;
         const ScaleFmtHost& fh = tid < 256 ? p.fb : p.fa;
         const ScaleFmt f{fh.ebits, fh.mbits, fh.bias, fh.maxcode, fh.smax, fh.is_e8m0};
-        const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_decode_any((uint32_t)t, f));
-        tab[tid] = h | (h << 16);
+        const float sv = BF16 ? scale_decode_any((uint32_t)t, f) * (tid < 256 ? pw : pa)
+                              : scale_decode_any((uint32_t)t, f);
+        const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sv);
+        tab[tid] = BF16 ? __float_as_uint(sv) : h | (h << 16);
         __syncthreads();
     }
 
@@ -1168,11 +1204,24 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
         const uint32_t b = BLOCK == 16 ? (t >= 2 ? code >> 8 : code & 0xFFu) : code;
         return __builtin_bit_cast(v2h, tb[b]);
     };
-    auto convert = [&](const NvHalf& h, int t, v8h (&cw)[4], v8h (&ca)[2]) {
+    // fp32 scale of dword t of a chunk (kNvBf16)
+    auto scale_f32 = [&](uint32_t code, int t, const uint32_t* tb) -> float {
+        const uint32_t b = BLOCK == 16 ? (t >= 2 ? code >> 8 : code & 0xFFu) : code;
+        return __uint_as_float(tb[b]);
+    };
+    auto convert = [&](const NvHalf& h, int t, V8 (&cw)[4], V8 (&ca)[2]) {
+        if constexpr (BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][t], scale_of(h.sw[i], t, tab));
+            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8_bf16((uint32_t)h.w[i][t], scale_f32(h.sw[i], t, tab));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
+            for (int j = 0; j < 2; ++j)
+                ca[j] = nv_convert8_bf16((uint32_t)h.a[j][t], scale_f32(h.sa[j], t, tab + 256));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][t], scale_of(h.sw[i], t, tab));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
+        }
     };
 
     v16f acc[4][2];
@@ -1183,10 +1232,10 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 
     // four steps of one half: products of step t with the conversions of
     // step t + 1 (the last step converts step 0 of `next`, if any)
-    auto run_half = [&](const NvHalf& h, const NvHalf& next, bool has_next, v8h (&cw)[4], v8h (&ca)[2]) {
+    auto run_half = [&](const NvHalf& h, const NvHalf& next, bool has_next, V8 (&cw)[4], V8 (&ca)[2]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            v8h nw[4], na[2];
+            V8 nw[4], na[2];
             const bool conv = t < 3 || has_next;
             if (t < 3) convert(h, t + 1, nw, na);
             else if (has_next) convert(next, 0, nw, na);
@@ -1194,12 +1243,16 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cw[i], ca[j], acc[i][j], 0, 0, 0);
+                    if constexpr (BF16)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i], ca[j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cw[i], ca[j], acc[i][j], 0, 0, 0);
             if (conv) {
+                // one matrix instruction, then the VALU of 6 fragments' share
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one matrix instruction
-                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);     // six VALU
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, BF16 ? 12 : 6, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1218,7 +1271,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     __builtin_amdgcn_s_barrier();
     NvHalf f, g;
     load_half(f, 0, 0);
-    v8h cw[4], ca[2];
+    V8 cw[4], ca[2];
     convert(f, 0, cw, ca);
     // The loop body is uniform: after the last stage the prefetch reads a
     // buffer whose contents are never used (a re-loaded copy of the last
@@ -1238,7 +1291,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_assert(NS * L::kBytes >= kCTileBytes, "the C image fits the stage buffers");
-    const float gg = p.ga[0] * p.gb[0];
+    const float gg = BF16 ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
     store_tile_4x2_lds(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
 
@@ -1253,14 +1306,14 @@ static bool exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <
 
 static bool is_e4m3(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits == 4 && f.mbits == 3; }
 
-template <int BLOCK, bool HW>
+template <int BLOCK, int CVT>
 static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 {
     constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<BLOCK>::kBytes + NvStage<BLOCK>::kTable;
-    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, HW>, sh);
+    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, CVT>, sh);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, HW>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, CVT>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
     return hipGetLastError();
 }
 
@@ -1356,12 +1409,16 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     if (f16) {
         const bool hw = is_e4m3(p.fa) && is_e4m3(p.fb);
         if (p.block == 16) {
-            if (hw) return launch_nv<16, true>(p, s);
-            return launch_nv<16, false>(p, s);
+            if (hw) return launch_nv<16, kNvE4M3>(p, s);
+            return launch_nv<16, kNvTable>(p, s);
         }
-        if (hw) return launch_nv<32, true>(p, s);
-        return launch_nv<32, false>(p, s);
+        if (hw) return launch_nv<32, kNvE4M3>(p, s);
+        return launch_nv<32, kNvTable>(p, s);
     }
+    // bf16 in registers for ExMy scales; E8M0 in a pair (whose smallest
+    // products are bf16 subnormals) keeps the LDS dequantize path
+    if (!p.fa.is_e8m0 && !p.fb.is_e8m0)
+        return p.block == 16 ? launch_nv<16, kNvBf16>(p, s) : launch_nv<32, kNvBf16>(p, s);
     dim3 grid((unsigned)((p.n + kTile - 1) / kTile), (unsigned)((p.m + kTile - 1) / kTile));
     const size_t sh = sizeof(DqSmem);
     hipError_t e = hipSuccess;

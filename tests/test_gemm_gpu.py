@@ -115,6 +115,36 @@ def test_e8m0_at_block16_and_mixed_formats():
     _check_gemm(c, a, b, tag="e8m0 x e4m3")
 
 
+@pytest.mark.parametrize("fmt,block", [("ue5m3", 16), ("e5m2", 32), ("e7m0", 16)])
+@pytest.mark.parametrize("m,n,k", [(257, 513, 384), (300, 70, 1280), (64, 256, 128), (1, 33, 640)])
+def test_bf16_register_path_shapes(fmt, block, m, n, k):
+    """Scale formats whose products need bf16 (5 or more exponent bits),
+    converted in registers: ragged tiles, one and many stages."""
+    qa, a = _quant_both(_normal(m, k, 21, dtype="bf16"), block, fmt)
+    qb, b = _quant_both(_normal(n, k, 22, 0.02, dtype="bf16"), block, fmt)
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check_gemm(c, a, b, tag=f"{fmt}/{block} {m}x{n}x{k}")
+
+
+def test_ue5m3_wide_block_range():
+    """Blocks whose magnitudes span 2^-40 .. 1 (current amax): the small
+    blocks take UE5M3's smallest scale codes, the products stay exact."""
+    m, n, k = 128, 256, 512
+    rng = np.random.default_rng(23)
+    def ranged(rows, seed):
+        x = np.random.default_rng(seed).standard_normal((rows, k)).astype(np.float32)
+        e = rng.integers(-40, 1, size=(rows, k // 16)).astype(np.float32)
+        return (x * np.repeat(np.exp2(e), 16, axis=1)).astype(np.float32)
+    xa, xw = ranged(m, 24), ranged(n, 25)
+    for fa, fw in (("ue5m3", "ue5m3"), ("e4m3", "ue5m3"), ("ue5m3", "e4m3")):
+        qa, a = _quant_both(xa, 16, fa)
+        qb, b = _quant_both(xw, 16, fw)
+        c = fq.fp4_gemm(qa, qb)
+        torch.cuda.synchronize()
+        _check_gemm(c, a, b, tag=f"{fa} x {fw} wide range")
+
+
 def test_unsupported_pair_is_rejected():
     x = torch.randn(32, 128, device="cuda")
     qa = fq.fp4_quantize(x, 16, "e1m6")
@@ -148,7 +178,7 @@ def test_empty_k_gives_zero(fmt, block):
     assert bool((y[:, :40] == 0).all()) and bool((y[:, 40:] == 7.0).all())
 
 
-@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e4m3", 16)])
+@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e4m3", 16), ("ue5m3", 16)])
 @pytest.mark.parametrize("wname", ["up", "down", "sq"])
 def test_llama_shapes_sampled_rows(fmt, block, wname):
     """Llama-2 7B linears at M = 8192 (batch 4 x seq 2048): sampled output
