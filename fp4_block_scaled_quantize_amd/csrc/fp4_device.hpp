@@ -548,6 +548,13 @@ __device__ __forceinline__ uint32_t absmax_bits8(const float v[8]) { return absm
 // ---------------------------------------------------------------------------
 struct U4 { uint32_t x, y, z, w; };
 
+// a ^ b ^ c in one gfx950 three-input bit operation (truth table 0x96); the
+// compiler otherwise emits two xors when c is a scalar
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
@@ -555,9 +562,9 @@ __device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1)
         uint64_t p0 = (uint64_t)c.x * 0xD2511F53u;
         uint64_t p1 = (uint64_t)c.z * 0xCD9E8D57u;
         U4 n;
-        n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+        n.x = xor3((uint32_t)(p1 >> 32), c.y, k0);
         n.y = (uint32_t)p1;
-        n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+        n.z = xor3((uint32_t)(p0 >> 32), c.w, k1);
         n.w = (uint32_t)p0;
         c = n;
         k0 += 0x9E3779B9u;
