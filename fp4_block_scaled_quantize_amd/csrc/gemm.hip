@@ -199,14 +199,15 @@ __device__ __forceinline__ void store_tile_4x2(const v16f (&acc)[4][2], float g,
 constexpr int kCTileRow = 2 * kTile + 16;           // bytes per LDS row of the C image
 constexpr int kCTileBytes = kTile * kCTileRow;
 
-__device__ __forceinline__ void store_tile_4x2_lds(const v16f (&acc)[4][2], float g, uint8_t* __restrict__ img,
-                                                   uint16_t* __restrict__ c, int64_t ldc, int wm_off, int wn_off,
-                                                   int64_t m_base, int64_t n_base, int64_t M, int64_t N)
+template <int NJ>
+__device__ __forceinline__ void store_tile_lds(const v16f (&acc)[4][NJ], float g, uint8_t* __restrict__ img,
+                                               uint16_t* __restrict__ c, int64_t ldc, int wm_off, int wn_off,
+                                               int64_t m_base, int64_t n_base, int64_t M, int64_t N)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     __syncthreads();                                 // every wave is done reading the stages
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int ml = wm_off + 32 * j + (lane & 31);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_assert(NS * L::Bytes + (L::Grouped ? 2 * L::GroupBytes : 0) >= kCTileBytes, "the C image fits the LDS");
     const float g = p.ga[0] * p.gb[0];
-    store_tile_4x2_lds(acc, g, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
+    store_tile_lds<2>(acc, g, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
 
 // Kernels with more than 64 KiB of dynamic LDS must opt in once per device.
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx16(GemmLaunch p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_assert(NS * L::Bytes + 2 * L::GroupBytes >= kCTileBytes, "the C image fits the LDS");
     const float gg = p.ga[0] * p.gb[0];
-    store_tile_4x2_lds(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
+    store_tile_lds<2>(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
 }
 
 // E2M1 with E8M0 scales at block 16 on both operands, whole 256-element
@@ -1015,14 +1016,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 }
 
 // ---------------------------------------------------------------------------
-// f16 path (scale formats whose e2m1 * s products are exact in f16: E4M3,
-// E3M4, E2M5, E1M6 -- NVFP4 is E4M3 at block 16).  The stages hold FP4
-// codes and raw scale bytes, loaded straight into LDS as in k_gemm_mx;
-// each wave converts its own fragments to f16 right before the matrix
-// instruction: the hardware FP4 -> f16 conversion (scale 1, exact) and one
-// packed f16 multiply by the block scale per two elements.  Eight waves
-// (2 x 4, 128 x 64 each) so one wave's conversions overlap the other's
-// matrix instructions on the same SIMD.
+// In-register conversion path (scale formats whose e2m1 * s products are
+// exact in f16: E4M3, E3M4, E2M5, E1M6 -- NVFP4 is E4M3 at block 16; and in
+// bf16 the ExMy formats with 5+ exponent bits, UE5M3 among them).  The
+// stages hold FP4 codes and raw scale bytes, loaded straight into LDS as in
+// k_gemm_mx; each wave converts its own fragments right before the matrix
+// instruction: for f16 the hardware FP4 -> f16 conversion (scale 1, exact)
+// and one packed f16 multiply by the block scale per two elements.  The f16
+// forms run eight waves (2 x 4, 128 x 64 each) so one wave's conversions
+// overlap the other's matrix instructions on the same SIMD; the bf16 form
+// four (2 x 2, 128 x 128 each), see launch_nv.
 //
 // K order inside a 128-element stage: lane half h of a 32x32x16 step (ks,
 // t) supplies elements 32 (2 ks + h) + 8 t + 0..7 of its row -- one 16-byte
@@ -1081,9 +1084,10 @@ __device__ __forceinline__ v8bf nv_convert8_bf16(uint32_t w, float s)
 // Fragments of one half stage (chunk pair ks) for one lane: four W and two
 // A 16-byte code fragments and their raw scale bytes (block 16: the two
 // scales of the chunk in one u16; block 32: one byte).
+template <int JA>
 struct NvHalf {
-    v4i w[4], a[2];
-    uint32_t sw[4], sa[2];
+    v4i w[4], a[JA];
+    uint32_t sw[4], sa[JA];
 };
 
 // CVT: one of kNvTable, kNvE4M3, kNvBf16 (above).
@@ -1093,10 +1097,13 @@ struct NvHalf {
 // between the halves, and after it the first half of the next stage is
 // read while half 1's products run.  The conversions of each 32x32x16 step
 // are interleaved with the previous step's products.
-template <int BLOCK, int NS, int CVT>
-__global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
+template <int BLOCK, int NS, int CVT, int WM>
+__global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
 {
     using L = NvStage<BLOCK>;
+    constexpr int NWV = 2 * WM;                 // waves: 2 along n (128 rows of W each) x WM along m
+    constexpr int JA = 8 / WM;                  // 32-row A fragments per wave (its 32 JA rows of A)
+    constexpr int CK = 16 / NWV;                // 16-byte code DMAs per lane per operand and stage
     constexpr bool HW_E4M3 = CVT == kNvE4M3, BF16 = CVT == kNvBf16;
     using V8 = std::conditional_t<BF16, v8bf, v8h>;
     static_assert(NS >= 2, "at least two stages");
@@ -1118,44 +1125,45 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     // inside binary32
     const float pw = BF16 ? split_pow2(p.gb[0]) : 1.0f, pa = BF16 ? split_pow2(p.ga[0]) : 1.0f;
     if (!HW_E4M3) {
-        const int t = tid & 255;
-        const ScaleFmtHost& fh = tid < 256 ? p.fb : p.fa;
-        const ScaleFmt f{fh.ebits, fh.mbits, fh.bias, fh.maxcode, fh.smax, fh.is_e8m0};
-        const float sv = BF16 ? scale_decode_any((uint32_t)t, f) * (tid < 256 ? pw : pa)
-                              : scale_decode_any((uint32_t)t, f);
-        const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sv);
-        tab[tid] = BF16 ? __float_as_uint(sv) : h | (h << 16);
+        for (int e = tid; e < 512; e += 64 * NWV) {
+            const int t = e & 255;
+            const ScaleFmtHost& fh = e < 256 ? p.fb : p.fa;
+            const ScaleFmt f{fh.ebits, fh.mbits, fh.bias, fh.maxcode, fh.smax, fh.is_e8m0};
+            const float sv = BF16 ? scale_decode_any((uint32_t)t, f) * (e < 256 ? pw : pa)
+                                  : scale_decode_any((uint32_t)t, f);
+            const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sv);
+            tab[e] = BF16 ? __float_as_uint(sv) : h | (h << 16);
+        }
         __syncthreads();
     }
 
-    const uint8_t* srcw[2];
-    const uint8_t* srca[2];
+    const uint8_t* srcw[CK];
+    const uint8_t* srca[CK];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int r = 16 * (2 * wave + k) + (lane >> 2);
+    for (int k = 0; k < CK; ++k) {
+        const int r = 16 * (CK * wave + k) + (lane >> 2);
         const int c = (lane & 3) ^ mx_swz<128>(r);
         const int64_t nr = n_base + r < N ? n_base + r : N - 1;
         const int64_t mr = m_base + r < M ? m_base + r : M - 1;
         srcw[k] = p.qb + nr * rowb + 16 * c;
         srca[k] = p.qa + mr * rowb + 16 * c;
     }
-    // scales.  Block 16: 8 bytes per row and stage; DMA j (0: W, 1: A) of
-    // this wave fills dword 64 wave + lane = (row, half) of that operand.
-    // Block 32: 4 bytes per row; waves 0-3 fill W's rows, waves 4-7 A's.
-    constexpr int kSDma = BLOCK == 16 ? 2 : 1;
+    // scales: the stage's dwords of both operands, W's then A's (block 16:
+    // two per row, block 32: one), dword q of them by lane q % (64 NWV) in
+    // DMA q / (64 NWV)
+    constexpr int kSDw = BLOCK == 16 ? 512 : 256;                      // dwords per operand
+    constexpr int kSDma = 2 * kSDw / (64 * NWV);
     const uint8_t* srcs[kSDma];
     int sdst[kSDma];
-    if (BLOCK == 16) {
-        const int q = 64 * wave + lane, r = q >> 1, d = q & 1;
-        srcs[0] = p.sb + (n_base + r < N ? n_base + r : N - 1) * rows + 4 * d;
-        srcs[kSDma - 1] = p.sa + (m_base + r < M ? m_base + r : M - 1) * rows + 4 * d;
-        sdst[0] = 2 * kMx3Codes + 256 * wave;
-        sdst[kSDma - 1] = 2 * kMx3Codes + L::kScales + 256 * wave;
-    } else {
-        const int r = 64 * (wave & 3) + lane;
-        srcs[0] = wave < 4 ? p.sb + (n_base + r < N ? n_base + r : N - 1) * rows
-                           : p.sa + (m_base + r < M ? m_base + r : M - 1) * rows;
-        sdst[0] = 2 * kMx3Codes + (wave < 4 ? 0 : L::kScales) + 256 * (wave & 3);
+#pragma unroll
+    for (int j = 0; j < kSDma; ++j) {
+        const int q = 64 * wave + lane + 64 * NWV * j;
+        const bool is_a = q >= kSDw;
+        const int qq = q - (is_a ? kSDw : 0);
+        const int r = BLOCK == 16 ? qq >> 1 : qq, d = BLOCK == 16 ? qq & 1 : 0;
+        srcs[j] = is_a ? p.sa + (m_base + r < M ? m_base + r : M - 1) * rows + 4 * d
+                       : p.sb + (n_base + r < N ? n_base + r : N - 1) * rows + 4 * d;
+        sdst[j] = 2 * kMx3Codes + (is_a ? L::kScales : 0) + 4 * (qq - lane);
     }
 
     // DMA of stage kt into buffer kt % NS; past the last stage the last one
@@ -1165,17 +1173,17 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
         const int ks = kt < KT ? kt : KT - 1;
         uint8_t* st = smem + (kt % NS) * L::kBytes;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            dma16(srcw[k] + (int64_t)ks * kMx3RB, st + 1024 * (2 * wave + k));
-            dma16(srca[k] + (int64_t)ks * kMx3RB, st + kMx3Codes + 1024 * (2 * wave + k));
+        for (int k = 0; k < CK; ++k) {
+            dma16(srcw[k] + (int64_t)ks * kMx3RB, st + 1024 * (CK * wave + k));
+            dma16(srca[k] + (int64_t)ks * kMx3RB, st + kMx3Codes + 1024 * (CK * wave + k));
         }
 #pragma unroll
         for (int j = 0; j < kSDma; ++j) dma4(srcs[j] + (int64_t)ks * L::kScaleRow, st + sdst[j]);
     };
-    constexpr int kLoads = 4 + kSDma;
+    constexpr int kLoads = 2 * CK + kSDma;
 
     const int frow = lane & 31, khalf = lane >> 5;
-    auto load_half = [&](NvHalf& h, int kt, int ks) {
+    auto load_half = [&](NvHalf<JA>& h, int kt, int ks) {
         const uint8_t* st = smem + (kt % NS) * L::kBytes;
         const uint8_t* ssw = st + 2 * kMx3Codes;
         const uint8_t* ssa = ssw + L::kScales;
@@ -1188,8 +1196,8 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
                                   : (uint32_t)ssw[r * L::kScaleRow + c];
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = wm * 64 + 32 * j + frow;
+        for (int j = 0; j < JA; ++j) {
+            const int r = wm * 32 * JA + 32 * j + frow;
             h.a[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx_swz<128>(r)));
             h.sa[j] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c)
                                   : (uint32_t)ssa[r * L::kScaleRow + c];
@@ -1209,50 +1217,52 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
         const uint32_t b = BLOCK == 16 ? (t >= 2 ? code >> 8 : code & 0xFFu) : code;
         return __uint_as_float(tb[b]);
     };
-    auto convert = [&](const NvHalf& h, int t, V8 (&cw)[4], V8 (&ca)[2]) {
+    auto convert = [&](const NvHalf<JA>& h, int t, V8 (&cw)[4], V8 (&ca)[JA]) {
         if constexpr (BF16) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) cw[i] = nv_convert8_bf16((uint32_t)h.w[i][t], scale_f32(h.sw[i], t, tab));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < JA; ++j)
                 ca[j] = nv_convert8_bf16((uint32_t)h.a[j][t], scale_f32(h.sa[j], t, tab + 256));
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][t], scale_of(h.sw[i], t, tab));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
+            for (int j = 0; j < JA; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
         }
     };
 
-    v16f acc[4][2];
+    v16f acc[4][JA];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < JA; ++j) acc[i][j] = v16f{};
 
     // four steps of one half: products of step t with the conversions of
     // step t + 1 (the last step converts step 0 of `next`, if any)
-    auto run_half = [&](const NvHalf& h, const NvHalf& next, bool has_next, V8 (&cw)[4], V8 (&ca)[2]) {
+    auto run_half = [&](const NvHalf<JA>& h, const NvHalf<JA>& next, bool has_next, V8 (&cw)[4], V8 (&ca)[JA]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            V8 nw[4], na[2];
+            V8 nw[4], na[JA];
             const bool conv = t < 3 || has_next;
             if (t < 3) convert(h, t + 1, nw, na);
             else if (has_next) convert(next, 0, nw, na);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < JA; ++j)
                     if constexpr (BF16)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[i], ca[j], acc[i][j], 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cw[i], ca[j], acc[i][j], 0, 0, 0);
             if (conv) {
-                // one matrix instruction, then the VALU of 6 fragments' share
+                // one matrix instruction, then its share of the next step's
+                // conversions ((4 + JA) fragments, 8 or 16 VALU each)
+                constexpr int kVpm = (4 + JA) * (BF16 ? 16 : 8) / (4 * JA);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < 4 * JA; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, BF16 ? 12 : 6, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kVpm, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1260,7 +1270,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) cw[i] = nw[i];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) ca[j] = na[j];
+                for (int j = 0; j < JA; ++j) ca[j] = na[j];
             }
         }
     };
@@ -1269,9 +1279,9 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     for (int s = 0; s < NS; ++s) issue(s);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * kLoads) : "memory");
     __builtin_amdgcn_s_barrier();
-    NvHalf f, g;
+    NvHalf<JA> f, g;
     load_half(f, 0, 0);
-    V8 cw[4], ca[2];
+    V8 cw[4], ca[JA];
     convert(f, 0, cw, ca);
     // The loop body is uniform: after the last stage the prefetch reads a
     // buffer whose contents are never used (a re-loaded copy of the last
@@ -1292,7 +1302,7 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_nv(GemmLaunch p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     static_assert(NS * L::kBytes >= kCTileBytes, "the C image fits the stage buffers");
     const float gg = BF16 ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
-    store_tile_4x2_lds(acc, gg, smem, p.c, p.ldc, wm * 64, wn * 128, m_base, n_base, M, N);
+    store_tile_lds<JA>(acc, gg, smem, p.c, p.ldc, wm * 32 * JA, wn * 128, m_base, n_base, M, N);
 }
 
 #ifndef FP4_NV_NS
@@ -1306,14 +1316,21 @@ static bool exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <
 
 static bool is_e4m3(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits == 4 && f.mbits == 3; }
 
+// Waves along m: the f16 forms run eight waves (2 x 4, 128 x 64 each), two
+// per SIMD, one converting while the other multiplies; the bf16 form, with
+// twice the conversion work per product, four waves of 128 x 128 (its
+// accumulators in the AGPRs, one wave per SIMD), which convert each A
+// fragment for twice the products (measured: UE5M3 600 -> 743 TFLOP/s at
+// the Llama-2 7B up projection; the f16 forms gain nothing from it).
 template <int BLOCK, int CVT>
 static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 {
+    constexpr int WM = CVT == kNvBf16 ? 2 : 4;
     constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<BLOCK>::kBytes + NvStage<BLOCK>::kTable;
-    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, CVT>, sh);
+    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, CVT, WM>, sh);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, CVT>), dim3(tiles), dim3(kMx4Threads), sh, s, p);
+    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, CVT, WM>), dim3(tiles), dim3(128 * WM), sh, s, p);
     return hipGetLastError();
 }
 
