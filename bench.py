@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "e19763091f706f3e5a5dc035f425500cb860939dcefb11fdf7ebb5edc47cc445",
-    "read_bytes": 33787494,
-    "write_bytes": 9453760,
+    "sha256": "a3d05ab5fdbe1c91f620c4c37d002c4591048713f7bfd310cae086361584aa29",
+    "read_bytes": 33856539,
+    "write_bytes": 9471300,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
