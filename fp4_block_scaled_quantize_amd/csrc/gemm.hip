@@ -6,22 +6,26 @@
 // layers run in FP4; quant_prune_distill/574 "Выводы": weight + activation
 // FP4 for the compute-bound regime.
 //
-// Two kernels:
+// Kernels (each computes the transposed tile D = W A^T, so that each lane
+// owns consecutive output columns of C; workgroup tile 256 x 256; codes and
+// scale bytes reach LDS by direct-to-LDS loads in multi-stage pipelines; the
+// C tile leaves through LDS as whole 16-byte row pieces):
 //  * k_gemm_mx: both operands E8M0 at block 32 (MXFP4).  The gfx950
 //    block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4 takes
 //    FP4 operands and one E8M0 scale per 32 K-elements per row directly: lane
 //    l supplies row (l % 32), K-half (l / 32) as 16 contiguous bytes -- the
 //    packed row-major layout of the quantizer -- and that K-half's scale
-//    byte.  No dequantization.
-//  * k_gemm_dq: any other format pair (E4M3/UE5M3/ExMy at block 16 or 32).
-//    No gfx950 instruction takes a non-power-of-two scale per 16 elements,
-//    so FP4 tiles are dequantized exactly (e2m1 * s has at most 9
-//    significant bits) to f16 or bf16 in LDS and multiplied on the
-//    32x32x16 f16/bf16 matrix cores.
-//
-// Both compute the transposed tile D = W A^T so that each lane owns four
-// consecutive output columns of C (one 8-byte store).  Workgroup tile
-// 256 x 256, four waves of 128 x 128, K double-buffered through LDS.
+//    byte.  No dequantization.  Eight waves of 128 x 64.
+//  * k_gemm_mx16: E8M0 at block 16 on the same instruction, each 64-element
+//    step run twice with the other 16-element block of A zeroed.
+//  * k_gemm_nv: scale formats whose e2m1 * s products are exact in f16
+//    (E4M3 -- NVFP4 --, E3M4, E2M5, E1M6) or, with more exponent bits
+//    (UE5M3, E5M2, E6M1, E7M0), in bf16: each wave converts its fragments in
+//    registers right before the f16 / bf16 32x32x16 matrix instruction.
+//  * k_gemm_dq: the remaining pairs (E8M0 with a non-power-of-two format)
+//    and the INT4, 8- and 6-bit grids: FP4 / integer / FP8 / FP6 tiles are
+//    dequantized exactly to f16 or bf16 in LDS.
+//  * k_wo_gemm: the weight-only GEMM (bf16 X times FP4 W, M <= 16).
 #include <type_traits>
 
 #include "fp4_device.hpp"

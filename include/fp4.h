@@ -206,6 +206,12 @@ FP4_API fp4_status fp4_set_exchange_wait(uint64_t ticks, uint64_t* previous);
 /*
  * fp4_quantize -- quantize x[rows, cols] (row stride ld_x elements, f32 or
  * bf16) into out->q / out->scales / out->tensor_scale with out->fmt.
+ * Pages: gonzo_ML/3986 "Форматы FP4" (E2M1 values, groups of 16, the swept
+ * scale encodings) and "Стохастическая квантизация" (nearest rounding,
+ * stochastic rounding for gradients); quant_prune_distill/486 "Метод" (NVFP4:
+ * group 16 with an E4M3 scale under a tensor scale; MXFP4: group 32 with an
+ * E8M0 scale); ue5m3-fp4-pretraining "Что сделали" (UE5M3 scales, the tensor
+ * maximum refreshed every 50 steps).
  *
  * Per block of B elements (reading of the pages' "shared scale per small
  * group"; every step binary32 round-to-nearest-even):
