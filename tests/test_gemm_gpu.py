@@ -224,6 +224,21 @@ def test_wo_gemm_formats(fmt, block):
     _check_wo(y, x, w, tag=f"wo {fmt}/{block}")
 
 
+@pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e4m3", 32), ("e8m0", 32), ("e8m0", 16), ("ue5m3", 16),
+                                       ("e7m0", 16), ("e1m6", 32), ("e3m4", 16)])
+@pytest.mark.parametrize("n,k", [(37, 256), (300, 2048), (8200, 4096), (129, 8448)])
+def test_wo_gemm_single_row(fmt, block, n, k):
+    """M = 1 (one X row, loaded in 4-byte pieces): scale formats decoded by
+    table, E8M0 as a power of two, E1M6 split into two exact bf16 terms; K
+    from one 128-element chunk per wave to many with a ragged last round
+    (K = 8448), ragged row groups."""
+    qw, w = _quant_both(_normal(n, k, 31, 0.02, dtype="bf16"), block, fmt)
+    x = _normal(1, k, 32, dtype="bf16")
+    y = fq.fp4_wo_gemm(to_device(x), qw)
+    torch.cuda.synchronize()
+    _check_wo(y, x, w, tag=f"wo m=1 {fmt}/{block} {n}x{k}")
+
+
 @pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e8m0", 32), ("e1m6", 32)])
 def test_wo_gemm_many_row_groups(fmt, block):
     """N = 8200: 513 groups of 16 rows (the launch that pairs row groups),
