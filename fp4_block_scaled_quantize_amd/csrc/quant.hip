@@ -1468,6 +1468,13 @@ constexpr int kDQUnroll = 4;                 // units per lane, loads issued tog
 // ROT: the inverse blockwise Hadamard transform follows the binary32
 // dequantization (the G units of a block are adjacent lanes and are all in
 // range or all out of it).
+typedef __bf16 dq_v2bf __attribute__((ext_vector_type(2)));
+typedef float dq_v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, dq_v2bf{(__bf16)a, (__bf16)b});
+}
+
 template <bool OUT_BF16, int BLOCK, bool E8M0, bool ROT, int ELEM>
 __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ scales,
@@ -1507,10 +1514,25 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
         if (u >= nunits) continue;
         const float s = scale_decode_any(sc[j], f);
         float o[8];
+        // E2M1 pairs by the hardware conversion (scale 1: the exact values)
+        float e2[8];
+        if (ELEM == 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const dq_v2f pe = b == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0)
+                                : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1)
+                                : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3);
+                e2[2 * b] = pe[0];
+                e2[2 * b + 1] = pe[1];
+            }
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             float e;
-            if (W6) {
+            if (ELEM == 0) {
+                e = e2[k];
+            } else if (W6) {
                 // bits 6k .. 6k + 5 of the 48-bit unit (w2 holds bits 32..47)
                 const uint64_t bits = (uint64_t)w[j] | ((uint64_t)w2[j] << 32);
                 e = w6_value<ELEM>((uint32_t)(bits >> (6 * k)) & 0x3Fu);
@@ -1518,8 +1540,7 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
                 const uint32_t b = ((k < 4 ? w[j] : w2[j]) >> (8 * (k & 3))) & 0xFFu;
                 e = ELEM == 2 ? scale_decode_any(b, kFp8E4M3) : int8_value(b);
             } else {
-                const uint32_t nib = (w[j] >> (4 * k)) & 0xFu;
-                e = ELEM == 1 ? int4_value(nib) : e2m1_value(nib);
+                e = int4_value((w[j] >> (4 * k)) & 0xFu);
             }
             float t = e * s;
             o[k] = t * g;
@@ -1527,11 +1548,13 @@ __global__ __launch_bounds__(kDQThreads) void k_dequantize(const uint32_t* __res
         if (ROT) rht_inverse<BLOCK / 8>(o, lane & (BLOCK / 8 - 1), signs);
         const uint64_t off = unit_offset(u, strided, upr, ld);
         if (OUT_BF16) {
+            // the hardware pair conversion rounds to nearest even, as the
+            // bit-level rounding does for every finite value
             u32x4 r;
-            r.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-            r.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-            r.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
-            r.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
+            r.x = bf16_pair(o[0], o[1]);
+            r.y = bf16_pair(o[2], o[3]);
+            r.z = bf16_pair(o[4], o[5]);
+            r.w = bf16_pair(o[6], o[7]);
             __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>((uint16_t*)y + off));
         } else {
             f32x4* pp = reinterpret_cast<f32x4*>((float*)y + off);
