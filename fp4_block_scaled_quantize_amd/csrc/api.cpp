@@ -239,9 +239,9 @@ fp4_status fp4_quantize(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor
 // this static device array instead of an fp4_amax_state.  Its size does not
 // depend on the tensor: the single-pass refresh uses at most kXchgSlots
 // exchange words and the two-pass refresh exactly kAmaxParts partials.  It
-// is zero at load; each single-pass launch leaves its departure counts at
-// zero again and the two-pass refresh overwrites every partial, so nothing
-// needs clearing per call.  Host code uses the address hipGetSymbolAddress returns for the
+// is zero at load; each single-pass launch publishes every slot with its
+// epoch and the two-pass refresh overwrites every partial, so nothing needs
+// clearing per call.  Host code uses the address hipGetSymbolAddress returns for the
 // current device, never the array's own (host-side) name.
 // ---------------------------------------------------------------------------
 constexpr size_t kScratchBytes = sizeof(AmaxDev);

@@ -21,29 +21,24 @@ bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 //    path holds in registers) writes one partial maximum per workgroup of
 //    the amax kernel; the quantize kernel of the same call reduces them and
 //    stores the result in `stored`, which calls between refreshes read.
-//  - epoch/slot/depart: the single-pass refresh exchanges per-workgroup
-//    maxima through `slot` (64-bit {epoch, max bits} words, one per 64-byte
-//    segment so that stores of different workgroups never share a line)
-//    within one launch.  Every workgroup counts itself out once it no
-//    longer needs the slots, in two levels: first in the counter of its
-//    departure group (blockIdx % kDepartGroups; group k's counter is word
-//    kDepartWord of slot segment k), and the last of a group then in
-//    `depart`.  The last group advances `epoch` (so every workgroup of a
-//    launch reads the same epoch); each last one resets what it counted.
+//  - slot: the single-pass refresh exchanges per-workgroup maxima through
+//    `slot` (64-bit {epoch, max bits} words, one per 64-byte segment so that
+//    stores of different workgroups never share a line) within one launch.
+//    Every single-pass launch on a device runs the same grid and publishes
+//    every slot, so a workgroup's own slot holds the previous launch's
+//    epoch, and that + 1 is this launch's.
 //  - fallbacks: number of workgroups that did not see every other
 //    workgroup's maximum within the wait bound and read the whole tensor
 //    themselves instead (the result is the same either way).
 constexpr int kAmaxParts = 256;
 constexpr int kXchgSlots = 256;
 constexpr int kXchgStride = 8;          // 64-bit words between slots (64 bytes)
-constexpr int kDepartGroups = 8;
-constexpr int kDepartWord = 1;          // word of slot segment k holding group k's departures
 struct AmaxDev {
     float partial[kAmaxParts];
     float stored;
-    uint32_t epoch;
+    uint32_t reserved;
     uint32_t fallbacks;
-    uint32_t depart;
+    uint32_t reserved2;
     uint32_t pad[60];
     uint64_t slot[kXchgSlots * kXchgStride];
 };

@@ -275,51 +275,28 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t m)
 // bounded in time: a workgroup that gives up takes the maximum of the whole
 // tensor itself (full_tensor_amax), which is the same value, so the result
 // never depends on co-residency.
-// Epochs: every workgroup reads the state's epoch at its start and uses
-// epoch + 1; once it no longer needs the slots it counts itself out
-// (depart_group), and the last workgroup to do so advances the epoch and
-// resets the counts.  So the epoch cannot change while any workgroup of the launch
-// has yet to read it, every workgroup of a launch uses the same epoch, and
-// each launch (graph replays included) gets a fresh one.
-// The state's epoch word, loaded at the start of the kernel (before any slot
-// of this launch is published, so the load overlaps the data loads);
-// launch_epoch turns it into this launch's epoch once the data loads are
-// in flight.
+// Epochs: every single-pass launch on a device runs the same grid (one
+// workgroup per CU, however small the tensor) and every workgroup publishes
+// exactly once per launch, so at the start of a launch every slot carries
+// the previous launch's epoch (0 in a fresh state).  Each workgroup reads
+// its own slot -- written only by itself -- and uses that epoch + 1: the
+// same fresh epoch for every workgroup of the launch (graph replays
+// included), with no counter, no atomic read-modify-write and nothing left
+// to do at the end of the kernel.  (Earlier schemes advanced a stored epoch
+// from the last workgroup to leave; their departure counts cost 0.7-1.4 us
+// per 4096 x 4096 launch in serialized same-address atomics.)
+// The workgroup's own slot is loaded at the start of the kernel (before it
+// publishes, so the load overlaps the data loads); launch_epoch turns it
+// into this launch's epoch.
 __device__ __forceinline__ uint32_t epoch_word(const AmaxDev* st)
 {
-    return __hip_atomic_load(&st->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)(__hip_atomic_load(&st->slot[blockIdx.x * kXchgStride], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) >> 32);
 }
 __device__ __forceinline__ uint32_t launch_epoch(uint32_t word)
 {
     const uint32_t e = word + 1u;
     return e == 0 ? 1u : e;
-}
-
-// Departure of a single-pass launch, in two levels: the 256 workgroups'
-// counts on one word would be serialized by the memory-side atomic unit,
-// and the last workgroup would wait for all of them before it can end
-// (about 0.7 us of a 4096 x 4096 bf16 launch); eight group counters on
-// separate 64-byte segments take them in parallel.  depart_group counts
-// thread 0's workgroup out of its group and returns the group's earlier
-// count; its result is needed only by depart_finish at the kernel's end.
-__device__ __forceinline__ uint32_t depart_group(AmaxDev* st)
-{
-    return (uint32_t)__hip_atomic_fetch_add(&st->slot[(blockIdx.x % kDepartGroups) * kXchgStride + kDepartWord], 1ull,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The last workgroup of a group resets the group counter and counts the
-// group out; the last group resets that count and advances the epoch.
-__device__ __forceinline__ void depart_finish(AmaxDev* st, uint32_t departed, uint32_t epoch)
-{
-    const uint32_t k = blockIdx.x % kDepartGroups;
-    const uint32_t in_group = (gridDim.x - k + kDepartGroups - 1) / kDepartGroups;
-    const uint32_t groups = gridDim.x < (uint32_t)kDepartGroups ? gridDim.x : (uint32_t)kDepartGroups;
-    if (departed != in_group - 1) return;
-    __hip_atomic_store(&st->slot[k * kXchgStride + kDepartWord], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t done = __hip_atomic_fetch_add(&st->depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done != groups - 1) return;
-    __hip_atomic_store(&st->depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&st->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Publishes m and polls; returns true with *gm = the maximum over every
@@ -519,7 +496,6 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
     }
 
     float g = 1.0f, d = QMAX;
-    uint32_t departed = 0;                       // FUSED: the departure count before this workgroup's
     if (!E8M0 && a.amax_src) {
         float am;
         if (FUSED) {
@@ -532,8 +508,6 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
                 if (threadIdx.x == 0)
                     __hip_atomic_fetch_add(&a.amax_src->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            // this workgroup no longer reads the slots or the epoch
-            if (threadIdx.x == 0) departed = depart_group(a.amax_src);
             am = __uint_as_float(gm);
         } else {
             am = tensor_amax(a);
@@ -676,10 +650,6 @@ __global__ __launch_bounds__(FUSED ? kFThreads : kQThreads) void k_quantize(QArg
         }
         if (u < a.nunits) __builtin_nontemporal_store(packed, a.q + u);
     }
-
-    // the last workgroup to leave the slots of a single-pass refresh opens
-    // the next epoch (read only by later launches)
-    if (FUSED && a.amax_src && threadIdx.x == 0) depart_finish(a.amax_src, departed, epoch);
 }
 
 template <typename InT, int BLOCK, bool SR, bool E8M0, bool FUSED, bool ROT, int ELEM>
@@ -778,6 +748,11 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         blocks = (a.nunits + per_wg - 1) / per_wg;
         if (blocks == 0) blocks = 1;
         fused = blocks <= max_wg;
+        // every single-pass launch on the device runs the same grid (each
+        // workgroup derives the launch's epoch from its own slot, so every
+        // slot must be published by every launch); workgroups past the
+        // tensor publish a zero maximum and store nothing
+        if (fused) blocks = max_wg;
         if (!fused) {
             hipError_t e = launch_amax(p.x, p.x_bf16, p.rows, p.cols, p.ld, p.amax_src, s, rot ? p.block : 0,
                                        p.rht_signs);
