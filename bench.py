@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "a3d05ab5fdbe1c91f620c4c37d002c4591048713f7bfd310cae086361584aa29",
-    "read_bytes": 33856539,
-    "write_bytes": 9471300,
+    "sha256": "c4b0a7e2e966193d966bde149ff0655f489e6f2787b9c9c4cb2b7500efeea4b6",
+    "read_bytes": 33864011,
+    "write_bytes": 9453696,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
