@@ -244,6 +244,26 @@ __device__ __forceinline__ void store_tile_lds(const v16f (&acc)[4][NJ], float g
     }
 }
 
+// The scaled matrix instruction taking byte SEL of each operand's scale
+// dword (the instruction's own byte select).
+template <int SEL>
+__device__ __forceinline__ v16f mfma_fp4_sel(const v8i& w, const v8i& a, const v16f& c, uint32_t sw, uint32_t sa)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 4, SEL, (int)sw, SEL, (int)sa);
+}
+// The same with the byte select a run-time step index that unrolling
+// makes constant.
+__device__ __forceinline__ v16f mfma_fp4_step(int ks, const v8i& w, const v8i& a, const v16f& c, uint32_t sw,
+                                              uint32_t sa)
+{
+    switch (ks) {
+    case 0: return mfma_fp4_sel<0>(w, a, c, sw, sa);
+    case 1: return mfma_fp4_sel<1>(w, a, c, sw, sa);
+    case 2: return mfma_fp4_sel<2>(w, a, c, sw, sa);
+    default: return mfma_fp4_sel<3>(w, a, c, sw, sa);
+    }
+}
+
 template <int BK, int NS>
 __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
 {
@@ -415,6 +435,18 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
                                    : (uint64_t)*reinterpret_cast<const uint32_t*>(ssa + 4 * r);
             }
         }
+        // 256-element stages: this stage's 8 scale bytes of a fragment row
+        // gathered once, by one byte permute, into k-step order (byte ks =
+        // block 2 ks + khalf), so each matrix instruction picks its byte
+        // with its own byte select instead of a shift and mask per step
+        uint32_t swb[4], sab[2];
+        if (BK == 256) {
+            const uint32_t psel = khalf ? 0x07050301u : 0x06040200u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) swb[i] = __builtin_amdgcn_perm((uint32_t)(swd[i] >> 32), (uint32_t)swd[i], psel);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sab[j] = __builtin_amdgcn_perm((uint32_t)(sad[j] >> 32), (uint32_t)sad[j], psel);
+        }
         // fragments of chunk pair ks (16-byte chunk c = 2 ks + khalf of each
         // row) are read while the products of pair ks - 1 are issued
         auto read_frags = [&](int ks, v4i (&wf)[4], v4i (&af)[2]) {
@@ -440,13 +472,17 @@ __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx(GemmLaunch p)
             const int sh = 8 * (2 * ks + khalf);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int sw = (int)((swd[i] >> sh) & 0xFFu);
                 const v8i wv = {wf[cur][i][0], wf[cur][i][1], wf[cur][i][2], wf[cur][i][3], 0, 0, 0, 0};
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const int sa = (int)((sad[j] >> sh) & 0xFFu);
                     const v8i av = {af[cur][j][0], af[cur][j][1], af[cur][j][2], af[cur][j][3], 0, 0, 0, 0};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0, sa);
+                    if (BK == 256) {
+                        acc[i][j] = mfma_fp4_step(ks, wv, av, acc[i][j], swb[i], sab[j]);
+                    } else {
+                        const int sw = (int)((swd[i] >> sh) & 0xFFu), sa = (int)((sad[j] >> sh) & 0xFFu);
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 4, 0, sw, 0,
+                                                                                  sa);
+                    }
                 }
             }
             if (ks + 1 < BK / 64) {
@@ -536,13 +572,6 @@ struct Mx16Shape {
     static constexpr int NKS = 4;                     // 64-element steps per stage
 };
 
-// The scaled matrix instruction taking byte SEL of each operand's scale
-// dword (the instruction's own byte select).
-template <int SEL>
-__device__ __forceinline__ v16f mfma_fp4_sel(const v8i& w, const v8i& a, const v16f& c, uint32_t sw, uint32_t sa)
-{
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 4, SEL, (int)sw, SEL, (int)sa);
-}
 
 __global__ __launch_bounds__(kMx4Threads) void k_gemm_mx16(GemmLaunch p)
 {
