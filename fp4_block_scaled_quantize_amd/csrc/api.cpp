@@ -350,7 +350,8 @@ fp4_status fp4_quantize_both(const void* x, int32_t x_dtype, int64_t ld_x, fp4_t
         return FP4_ERR_UNSUPPORTED;
     // a transform would run along different axes, with different maxima
     if (fr.transform != FP4_TRANSFORM_NONE || fl.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;
-    if (elem_is_wide(fr.element)) return FP4_ERR_UNSUPPORTED;
+    // 6-bit codes: whole 16-byte column-wise output chunks need R % 64 == 0
+    if (elem_is_6bit(fr.element) && colwise->cols % 64) return FP4_ERR_SHAPE;
     if (!x && rowwise->rows * rowwise->cols != 0) return FP4_ERR_INVALID_ARG;
     if (x_dtype != FP4_DTYPE_F32 && x_dtype != FP4_DTYPE_BF16) return FP4_ERR_INVALID_ARG;
     const int64_t esz = x_dtype == FP4_DTYPE_BF16 ? 2 : 4;

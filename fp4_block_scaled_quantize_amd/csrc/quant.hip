@@ -908,8 +908,8 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
 // piece p of a tile row holds elements c0 + EPP p .. of row r, and the
 // BLOCK / EPP pieces of a row block sit in adjacent lanes, so the block
 // maximum is a shuffle reduction over those lanes; every rule (scale,
-// nearest or stochastic rounding with the row-wise counter index r C + c)
-// is that of the row-wise kernel.
+// nearest or stochastic rounding with the row-wise counter index r C + c,
+// element grid and packing) is that of the row-wise kernel.
 template <typename InT>
 __device__ __forceinline__ void unpack_piece(const u32x4& w, float v[16 / sizeof(InT)])
 {
@@ -924,13 +924,16 @@ __device__ __forceinline__ void unpack_piece(const u32x4& w, float v[16 / sizeof
     }
 }
 
-template <typename InT, int BLOCK, bool SR, bool E8M0, bool INT>
+template <typename InT, int BLOCK, bool SR, bool E8M0, int ELEM>
 __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoad<InT>& ld, uint32_t r0, uint32_t c0,
                                                   float g, float d)
 {
     constexpr int EPP = TileLoad<InT>::EPP;
     constexpr int NLD = TileLoad<InT>::NLD;
     constexpr int G = BLOCK / EPP;               // lanes per row block
+    constexpr bool INT = ELEM == 1;
+    constexpr bool W8 = ELEM == 2 || ELEM == 3;  // one byte per element
+    constexpr bool W6 = ELEM >= 4;               // six bits per element
     const uint32_t piece = threadIdx.x % TileLoad<InT>::PPR, prow = threadIdx.x / TileLoad<InT>::PPR;
     const uint32_t gc = c0 + piece * EPP;
     const uint32_t sub = threadIdx.x & (G - 1);  // position of this lane's piece in its block
@@ -957,7 +960,10 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
     uint32_t code[NLD];
     auto scale_of = [&](uint32_t m, float* iv) -> uint32_t {
         if (E8M0) {
-            const uint32_t c = scale_code_e8m0(__uint_as_float(m));
+            const uint32_t c = ELEM == 2 ? scale_code_e8m0_emax<8>(__uint_as_float(m))
+                             : ELEM == 3 ? scale_code_e8m0_emax<6>(__uint_as_float(m))
+                             : (ELEM == 5 || ELEM == 6) ? scale_code_e8m0_emax<4>(__uint_as_float(m))
+                             : scale_code_e8m0(__uint_as_float(m));
             *iv = e8m0_inv(c);
             return c;
         }
@@ -1009,12 +1015,74 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
         unpack_piece<InT>(ld.v[k], v);
 #pragma unroll
         for (int i = 0; i < EPP; ++i) v[i] = v[i] * inv[k];
+        const bool in = gr < a.R && gc < a.C;
+        const uint32_t e0 = gc & 7u;                 // first element of the piece in its unit
+        if constexpr (W8 || W6) {
+            // the piece's random 16-bit halves (element e of a unit takes
+            // half e % 2 of word e / 2), then one code per element
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};
+            if (SR) {
+                const uint32_t u = (uint32_t)(((uint64_t)gr * a.C + gc) >> 3);
+                const U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
+                wd[0] = r.x; wd[1] = r.y; wd[2] = r.z; wd[3] = r.w;
+            }
+            auto r16_of = [&](int i) { const uint32_t e = e0 + i; return (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu; };
+            if constexpr (W8) {
+                // bytes of elements 0..3 and 4..7 of the piece
+                uint32_t d0, d1 = 0;
+                if (SR || ELEM == 3) {
+                    uint32_t c[EPP];
+#pragma unroll
+                    for (int i = 0; i < EPP; ++i)
+                        c[i] = SR ? (ELEM == 2 ? fp8_sr_code(v[i], r16_of(i)) : int8_sr_code(v[i], r16_of(i)))
+                                  : int8_rtn_code(v[i]);
+                    d0 = c[0] | (c[1] << 8) | (c[2 % EPP] << 16) | (c[3 % EPP] << 24);
+                    if (EPP == 8) d1 = c[4 % EPP] | (c[5 % EPP] << 8) | (c[6 % EPP] << 16) | (c[7 % EPP] << 24);
+                } else {
+                    d0 = fp8_rtn_pack4(v[0], v[1], v[2 % EPP], v[3 % EPP]);
+                    if (EPP == 8) d1 = fp8_rtn_pack4(v[4 % EPP], v[5 % EPP], v[6 % EPP], v[7 % EPP]);
+                }
+                if (in) {
+                    uint8_t* qd = a.q_row + (uint64_t)gr * a.C + gc;
+                    if (EPP == 8) *(u32x2*)qd = u32x2{d0, d1};
+                    else *(uint32_t*)qd = d0;
+                }
+            } else {
+                // element i of the piece at bit 6 i
+                uint64_t bits = 0;
+                if (SR || ELEM == 6) {
+#pragma unroll
+                    for (int i = 0; i < EPP; ++i)
+                        bits |= (uint64_t)(SR ? w6_sr_code<ELEM>(v[i], r16_of(i)) : w6_rtn_code<ELEM>(v[i])) << (6 * i);
+                } else {
+                    bits = fp6_rtn_pack4_hw<ELEM>(v[0], v[1], v[2 % EPP], v[3 % EPP]);
+                    if (EPP == 8) bits |= (uint64_t)fp6_rtn_pack4_hw<ELEM>(v[4 % EPP], v[5 % EPP], v[6 % EPP], v[7 % EPP]) << 24;
+                }
+                // unit u of the row-major stream at byte 6 u: a whole unit as
+                // three 16-bit stores, a half unit (f32 pieces) as three bytes
+                // at byte 3 of the unit for its second half
+                if (in) {
+                    const uint64_t u = ((uint64_t)gr * a.C + gc) >> 3;
+                    if (EPP == 8) {
+                        uint16_t* dst = reinterpret_cast<uint16_t*>(a.q_row) + 3 * u;
+                        dst[0] = (uint16_t)bits;
+                        dst[1] = (uint16_t)(bits >> 16);
+                        dst[2] = (uint16_t)(bits >> 32);
+                    } else {
+                        uint8_t* dst = a.q_row + 6 * u + 3 * (e0 >> 2);
+                        dst[0] = (uint8_t)bits;
+                        dst[1] = (uint8_t)(bits >> 8);
+                        dst[2] = (uint8_t)(bits >> 16);
+                    }
+                }
+            }
+            continue;
+        }
         uint32_t packed = 0;
         if (SR) {
             const uint32_t u = (uint32_t)(((uint64_t)gr * a.C + gc) >> 3);   // unit (i >> 3), row-wise index
             const U4 r = philox10(U4{u, 0u, a.off0, a.off1}, a.key0, a.key1);
             const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-            const uint32_t e0 = gc & 7u;                                   // first element of the piece in its unit
             if (INT) {
 #pragma unroll
                 for (int i = 0; i < EPP; ++i) {
@@ -1042,7 +1110,7 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
         }
         // plain (not streaming) stores: each is a 32-byte piece of a line
         // that the neighbouring tiles of the super-tile complete in L2
-        if (gr < a.R && gc < a.C) {
+        if (in) {
             uint8_t* qd = a.q_row + (uint64_t)gr * (a.C / 2) + gc / 2;
             if (EPP == 8) *(uint32_t*)qd = packed;
             else *(uint16_t*)qd = (uint16_t)packed;
@@ -1053,16 +1121,15 @@ __device__ __forceinline__ void rowwise_from_tile(const QTArgs& a, const TileLoa
 // ROWS: also the row-wise quantization of the same tile from the loaded
 // registers (x read once for both orientations; no transform).
 // ELEM: the element grid (0 E2M1, 1 INT4, 2 FP8 E4M3, 3 INT8, 4 FP6 E2M3,
-// 5 FP6 E3M2, 6 INT6; the 8- and 6-bit grids transposed-only, the 6-bit
-// ones with R % 64 == 0 so that every output chunk is 16 whole bytes).
+// 5 FP6 E3M2, 6 INT6; the 6-bit ones with R % 64 == 0 so that every
+// column-wise output chunk is 16 whole bytes).
 template <typename InT, int BLOCK, bool SR, bool E8M0, int ELEM, bool ROT, bool ROWS>
-__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && ELEM == 1 ? 4 : 5))))) void k_quantize_t(QTArgs a)
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 ? 2 : (SR ? FP4_T_SR_WAVES : (ROWS && ELEM != 0 ? 4 : 5))))) void k_quantize_t(QTArgs a)
 {
     constexpr bool INT = ELEM == 1;
     constexpr bool W8 = ELEM == 2 || ELEM == 3;
     constexpr bool W6 = ELEM >= 4;
     static_assert(!(ROWS && ROT), "the two orientations would need different transforms and maxima");
-    static_assert(!(ROWS && (W8 || W6)), "the two-orientation variant writes 4-bit codes");
     constexpr float QMAX = ELEM == 1 ? 7.0f : ELEM == 2 ? 448.0f : ELEM == 3 ? 127.0f : ELEM == 4 ? 7.5f
                          : ELEM == 5 ? 28.0f : ELEM == 6 ? 31.0f : 6.0f;   // grid maximum
     constexpr int RPW = kTR / (kTThreads / 64);  // rows of every column per wave
@@ -1118,7 +1185,7 @@ __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(sizeo
     }
 
     ld.store(tile);
-    if (ROWS) rowwise_from_tile<InT, BLOCK, SR, E8M0, INT>(a, ld, r0, c0, g, d);
+    if (ROWS) rowwise_from_tile<InT, BLOCK, SR, E8M0, ELEM>(a, ld, r0, c0, g, d);
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1331,8 +1398,15 @@ static void launch_qt2(const QTArgs& a, bool sr, bool e8, int elem, bool rot, bo
                        hipStream_t s)
 {
     if (rows) {
-        if (elem == 1) launch_qt3<InT, BLOCK, 1, false, true>(a, sr, e8, blocks, s);
-        else launch_qt3<InT, BLOCK, 0, false, true>(a, sr, e8, blocks, s);
+        switch (elem) {
+        case 1: launch_qt3<InT, BLOCK, 1, false, true>(a, sr, e8, blocks, s); break;
+        case 2: launch_qt3<InT, BLOCK, 2, false, true>(a, sr, e8, blocks, s); break;
+        case 3: launch_qt3<InT, BLOCK, 3, false, true>(a, sr, e8, blocks, s); break;
+        case 4: launch_qt3<InT, BLOCK, 4, false, true>(a, sr, e8, blocks, s); break;
+        case 5: launch_qt3<InT, BLOCK, 5, false, true>(a, sr, e8, blocks, s); break;
+        case 6: launch_qt3<InT, BLOCK, 6, false, true>(a, sr, e8, blocks, s); break;
+        default: launch_qt3<InT, BLOCK, 0, false, true>(a, sr, e8, blocks, s); break;
+        }
         return;
     }
     switch (elem) {

@@ -123,8 +123,8 @@ typedef enum fp4_transform {
  * symmetric grid -127..127 (two's complement, zero unsigned).  448 or 127
  * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
  * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
- * Row-wise and column-wise quantize, dequantize and fp4_gemm take them;
- * the two-orientation call and fp4_wo_gemm return UNSUPPORTED for them.
+ * Row-wise, column-wise and two-orientation quantize, dequantize and
+ * fp4_gemm take them; fp4_wo_gemm returns UNSUPPORTED for them.
  * The 6-bit grids (the same page's MXFP6 / MXINT6; reading: the OCP FP6
  * element formats E2M3 and E3M2, and INT6 on -31..31) pack six bits per
  * element as a little-endian bit stream: element c of a row at bits
@@ -132,9 +132,9 @@ typedef enum fp4_transform {
  * E3M2: bias 3, largest 28; sign bit 5, subnormals, no reserved codes;
  * nearest-even, saturating.  INT6: six-bit two's complement, zero unsigned.
  * 7.5, 28 or 31 takes the place of 6; the E8M0 offsets are 2, 4 and 4.
- * Row-wise quantize, dequantize, fp4_gemm and the column-wise call (with
- * R % 64 == 0, SHAPE otherwise) take them; the other calls return
- * UNSUPPORTED. */
+ * Row-wise quantize, dequantize, fp4_gemm and the column-wise and
+ * two-orientation calls (with R % 64 == 0, SHAPE otherwise) take them;
+ * fp4_wo_gemm returns UNSUPPORTED for them. */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,
@@ -304,8 +304,8 @@ FP4_API fp4_status fp4_quantize_transposed(const void* x, int32_t x_dtype, int64
  * (UNSUPPORTED otherwise: a transform along each axis would give the two
  * outputs different maxima).  The amax state counts the pair as one call.
  * Requirements as for the two calls together: R % block == 0, C % block ==
- * 0, x 16-byte aligned with ld_x * sizeof(elem) a multiple of 16, colwise->q
- * 16-byte aligned.  A refresh of the tensor maximum reads x twice (an amax
+ * 0 (R % 64 == 0 for the 6-bit grids), x 16-byte aligned with ld_x *
+ * sizeof(elem) a multiple of 16, colwise->q 16-byte aligned.  A refresh of the tensor maximum reads x twice (an amax
  * pass, then this one); otherwise x is read once.
  */
 FP4_API fp4_status fp4_quantize_both(const void* x, int32_t x_dtype, int64_t ld_x, fp4_tensor* rowwise,

@@ -148,10 +148,12 @@ int main()
         c2.fmt.scale = FP4_SCALE_UE5M3;
         expect("both format mismatch", fp4_quantize_both(x_buf, FP4_DTYPE_F32, 256, &r, &c2, nullptr, 0, 0, nullptr),
                FP4_ERR_UNSUPPORTED);
-        fp4_tensor r8 = tensor(64, 256, 32, FP4_SCALE_E8M0, FP4_AMAX_NONE, FP4_ELEM_FP8_E4M3);
-        fp4_tensor c8 = tensor(256, 64, 32, FP4_SCALE_E8M0, FP4_AMAX_NONE, FP4_ELEM_FP8_E4M3);
-        expect("both 8-bit", fp4_quantize_both(x_buf, FP4_DTYPE_F32, 256, &r8, &c8, nullptr, 0, 0, nullptr),
-               FP4_ERR_UNSUPPORTED);
+        fp4_tensor r6 = tensor(96, 64, 32, FP4_SCALE_E8M0, FP4_AMAX_NONE, FP4_ELEM_FP6_E2M3);
+        fp4_tensor c6b = tensor(64, 96, 32, FP4_SCALE_E8M0, FP4_AMAX_NONE, FP4_ELEM_FP6_E2M3);
+        r6.q = q_buf;
+        c6b.q = q_buf;
+        expect("both 6-bit R % 64", fp4_quantize_both(x_buf, FP4_DTYPE_F32, 64, &r6, &c6b, nullptr, 0, 0, nullptr),
+               FP4_ERR_SHAPE);
     }
     // dequantize, GEMM, weight-only GEMM
     {

@@ -398,8 +398,7 @@ def test_6bit_rejected_elsewhere():
         q6 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element=elem)
         f6 = fq.fp4_quantize(xd, 32, "e8m0", amax="none", element="fp6_e3m2" if elem != "fp6_e3m2" else "int6")
         for call in (lambda: fq.fp4_gemm(q6, f6),
-                     lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q6),
-                     lambda: fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element=elem)):
+                     lambda: fq.fp4_wo_gemm(torch.zeros((1, 256), dtype=torch.bfloat16, device="cuda"), q6)):
             with pytest.raises(fq.Fp4Error) as e:
                 call()
             assert e.value.status == -2

@@ -72,6 +72,63 @@ def test_both_int4(fmt, block, rounding):
     _check_both(x, block, fmt, _policy(fmt), rounding=rounding, seed=9, offset=1, element="int4", tag="both int4")
 
 
+WIDE = ["fp8_e4m3", "int8", "fp6_e2m3", "fp6_e3m2", "int6"]
+
+
+@pytest.mark.parametrize("element", WIDE)
+@pytest.mark.parametrize("fmt,block", [("e8m0", 32), ("e8m0", 16), ("e4m3", 16), ("ue5m3", 32)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+def test_both_wide_grids(element, fmt, block, dtype, rounding):
+    """The 8- and 6-bit grids: row-wise codes one byte (or six bits in the
+    row-major stream) per element, column-wise as the transposed call.  320
+    rows (a whole and a partial 256-row tile, a multiple of 64 for the 6-bit
+    column-wise chunks) by 160 columns (two whole 64-column tiles and a
+    partial one)."""
+    x = _like(320, 160, 800 + block, dtype)
+    _check_both(x, block, fmt, _policy(fmt), rounding=rounding, seed=0x5EED, offset=3, element=element,
+                tag=f"both {element} {fmt}/{block}/{dtype}/{rounding}")
+
+
+@pytest.mark.parametrize("element", WIDE)
+def test_both_wide_grids_larger_and_delayed(element):
+    """2048 x 1536 bf16 with E4M3 scales at block 16, three delayed-amax
+    calls on new tensors (a refresh at the first, the stored maximum after
+    it; nearest rounding first, then stochastic), each against the oracle's
+    sequence."""
+    st = fq.AmaxState(50)
+    ost = oracle.AmaxState(50)
+    for t in range(3):
+        x = _like(2048, 1536, 900 + t)
+        qr, qc = fq.fp4_quantize_both(to_device(x), 16, "e4m3", rounding="stochastic" if t else "nearest",
+                                      amax="delayed", state=st, seed=77, offset=t, element=element)
+        torch.cuda.synchronize()
+        sr = t > 0
+        o_before = ost.calls
+        q, s, g, a = oracle.quantize_tensor(x, 16, "e4m3", "delayed", stochastic=sr, seed=77, offset=t, nthreads=8,
+                                            state=ost, elem=element)
+        tag = f"both {element} call {t}"
+        assert_bytes_equal(host(qr.scales), s, f"{tag} row scales")
+        assert_bytes_equal(host(qr.q), q, f"{tag} row codes")
+        assert_bytes_equal(f32_bits(host(qr.tensor_scale)), f32_bits([g, a]), f"{tag} row tensor_scale")
+        ost.calls = o_before
+        q, s, g, a = oracle.quantize_transposed_tensor(x, 16, "e4m3", "delayed", stochastic=sr, seed=77, offset=t,
+                                                       nthreads=8, state=ost, elem=element)
+        assert_bytes_equal(host(qc.scales), s, f"{tag} col scales")
+        assert_bytes_equal(host(qc.q), q, f"{tag} col codes")
+        assert_bytes_equal(f32_bits(host(qc.tensor_scale)), f32_bits([g, a]), f"{tag} col tensor_scale")
+
+
+@pytest.mark.parametrize("element", ["fp6_e2m3", "fp6_e3m2", "int6"])
+def test_both_6bit_shape_rule(element):
+    """The 6-bit column-wise output needs R % 64 == 0: 96 rows are refused
+    with SHAPE before any launch."""
+    xd = to_device(_like(96, 64, 95))
+    with pytest.raises(fq.Fp4Error) as e:
+        fq.fp4_quantize_both(xd, 32, "e8m0", amax="none", element=element)
+    assert e.value.status == -3
+
+
 def test_both_sweep_full_size():
     _check_both(inputs.sweep(), 16, "e4m3", "current", tag="both sweep")
 
