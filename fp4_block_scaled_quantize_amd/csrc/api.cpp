@@ -61,7 +61,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 105; }
+int32_t fp4_version(void) { return 106; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -471,21 +471,22 @@ fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tens
     if (!y || (!x && w->cols != 0)) return FP4_ERR_INVALID_ARG;
     if (m < 1 || m > 16) return FP4_ERR_UNSUPPORTED;
     if (w->fmt.transform != FP4_TRANSFORM_NONE) return FP4_ERR_UNSUPPORTED;   // x would need the same transform
-    if (elem_is_wide(w->fmt.element)) return FP4_ERR_UNSUPPORTED;
     if (w->cols % 256) return FP4_ERR_SHAPE;
     if (ldx < w->cols || ldy < w->rows) return FP4_ERR_SHAPE;
     if (w->rows == 0) return FP4_OK;
     // an empty K: Y is the empty sum, zero; neither x nor W is read
     if (w->cols == 0) return hip_status(launch_fill_zero_bf16(y, ldy, m, w->rows, (hipStream_t)stream));
     // the kernel addresses W and x with 32-bit byte/element offsets
-    if (w->rows * (w->cols / 2) >= (int64_t(1) << 32) || ldx * m >= (int64_t(1) << 31)) return FP4_ERR_UNSUPPORTED;
+    const int64_t wbits = elem_is_8bit(w->fmt.element) ? 8 : elem_is_6bit(w->fmt.element) ? 6 : 4;
+    if (w->rows * (w->cols * wbits / 8) >= (int64_t(1) << 32) || ldx * m >= (int64_t(1) << 31))
+        return FP4_ERR_UNSUPPORTED;
     if (!aligned16(x) || ldx % 8) return FP4_ERR_ALIGN;
     if (!aligned16(w->q) || ((uintptr_t)w->scales & 3u)) return FP4_ERR_ALIGN;
     WoGemmLaunch p;
     p.x = x; p.ldx = ldx; p.m = m;
     p.qw = w->q; p.sw = w->scales; p.gw = w->tensor_scale;
     p.n = w->rows; p.k = w->cols;
-    p.elem_int4 = w->fmt.element == FP4_ELEM_INT4;
+    p.elem = w->fmt.element;
     p.block = w->fmt.block;
     p.fw = fw;
     p.y = y; p.ldy = ldy;

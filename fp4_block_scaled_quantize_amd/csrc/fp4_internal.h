@@ -121,7 +121,7 @@ struct WoGemmLaunch {
     int32_t block;
     ScaleFmtHost fw;
     uint16_t* y; int64_t ldy;
-    int32_t elem_int4;         // weights on the INT4 grid
+    int32_t elem;              // element grid of the weights (fp4_element)
 };
 
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s);

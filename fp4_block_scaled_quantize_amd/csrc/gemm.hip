@@ -1488,7 +1488,8 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // ---------------------------------------------------------------------------
 // weight-only GEMM: Y[M, N] = bf16(gw * X[M, K] W[N, K]^T), 1 <= M <= 16
 // (quant_prune_distill/574 "Эксперименты": weight-only NVFP4 with a
-// memory-bound kernel for small-batch generation).
+// memory-bound kernel for small-batch generation; quant_prune_distill/486
+// "Метод": the same blocking with 8- and 6-bit elements).
 //
 // A workgroup owns RG groups of 16 rows of W; its NW waves split K in
 // 128-element chunks (wave w takes chunks w, w + NW, ...), and every byte of
@@ -1507,7 +1508,10 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // streams its chunks with direct-to-LDS loads in an order that keeps every
 // four lanes on one 64-byte run of a row (four lanes per cycle) into a
 // private ring of D slots (W, its scales, the chunk's M rows of X), and reads
-// the fragments from there.  A wave reads only what it loaded itself, after
+// the fragments from there.  A chunk row of W is 64 bytes for the 4-bit
+// grids, 128 for the 8-bit ones and 96 for the 6-bit ones; the wide rows sit
+// at a 128-byte pitch (two loads per 16-row group, the 6-bit rows with the
+// lanes of the two pieces past their 96 bytes masked off).  A wave reads only what it loaded itself, after
 // the load counter says it has landed, so the ring needs no barrier.  The
 // 16-byte pieces of a row are XOR-swizzled so that the fragment reads are
 // free of bank conflicts.  The waves' partial tiles are summed in LDS in a
@@ -1532,6 +1536,61 @@ __device__ __forceinline__ v2f elem_pair_f32(uint32_t w, int b)
          : b == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
          : b == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
                   : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+}
+
+// Elements k and k + 1 (k even) of the codes dw of one chunk row piece (the
+// grid's packing: 4-bit nibbles, bytes, or the six-bit stream) as binary32:
+// E2M1 and FP8 E4M3 by the hardware conversions (scale 1, exact), INT4 /
+// INT8 / INT6 sign-extended, FP6 E2M3 / E3M2 through the FP8 E4M3 / E5M2
+// byte of the value times 2^-6 / 2^-12 (exact) and one multiply back.  k is
+// a compile-time constant after unrolling.
+template <int ELEM>
+__device__ __forceinline__ v2f elem_pair_any(const uint32_t* dw, int k)
+{
+    if constexpr (ELEM <= 1) {
+        return elem_pair_f32<ELEM == 1>(dw[k >> 3], (k & 7) >> 1);
+    } else if constexpr (ELEM == 2) {
+        return (k & 3) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[k >> 2], true)
+                       : __builtin_amdgcn_cvt_pk_f32_fp8((int)dw[k >> 2], false);
+    } else if constexpr (ELEM == 3) {
+        const uint32_t w = dw[k >> 2] >> (8 * (k & 3));
+        return v2f{int8_value(w), int8_value(w >> 8)};
+    } else {
+        const int bit = 6 * k, i = bit >> 5, sh = bit & 31;
+        const uint32_t x = sh + 12 <= 32 ? dw[i] >> sh : __builtin_amdgcn_alignbit(dw[i + 1], dw[i], sh);
+        if constexpr (ELEM == 6) {
+            return v2f{(float)((int32_t)(x << 26) >> 26), (float)((int32_t)(x << 20) >> 26)};
+        } else {
+            // the two codes to one byte each, sign bit 5 -> 7: the FP8 byte
+            const uint32_t y = (x & 0x3Fu) | ((x << 2) & 0x3F00u);
+            const uint32_t w = (y & 0x1F1Fu) | ((y & 0x2020u) << 2);
+            const v2f e = ELEM == 4 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false)
+                                    : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+            constexpr float kFold = ELEM == 4 ? 64.0f : 4096.0f;
+            return v2f{e[0] * kFold, e[1] * kFold};
+        }
+    }
+}
+
+// Elements 8t .. 8t + 7 of dw times s as bf16 pairs: hi the truncation of
+// each binary32 product (exact when it fits bf16), with SPLIT lo the exact
+// remainder (products of up to 16 significant bits).
+template <int ELEM, bool SPLIT>
+__device__ __forceinline__ void dq8_any(const uint32_t* dw, int t, float s, v4i& hi, v4i& lo)
+{
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const v2f f = elem_pair_any<ELEM>(dw, 8 * t + 2 * b);
+        const float v0 = f[0] * s, v1 = f[1] * s;
+        if (SPLIT) {
+            const uint32_t h0 = __float_as_uint(v0) & 0xFFFF0000u, h1 = __float_as_uint(v1) & 0xFFFF0000u;
+            const float l0 = v0 - __uint_as_float(h0), l1 = v1 - __uint_as_float(h1);
+            hi[b] = (int)((h0 >> 16) | h1);
+            lo[b] = (int)((__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u));
+        } else {
+            hi[b] = (int)__builtin_amdgcn_perm(__float_as_uint(v1), __float_as_uint(v0), 0x07060302u);
+        }
+    }
 }
 
 // INT: INT4 elements (never POW2: the multiply by s is exact for E8M0 too).
@@ -1573,18 +1632,24 @@ __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i
 
 // One ring slot of the weight-only GEMM (byte offsets).  XQ = 0: M == 1,
 // the single X row arrives by 4-byte loads; else XQ loads of four 256-byte
-// X rows each.
-template <int RG, int XQ>
+// X rows each.  WP: LDS pitch of a W row (64 for the 4-bit grids, 128 for
+// the wider ones).
+template <int RG, int XQ, int WP = 64>
 struct WoSlot {
-    static constexpr int W = 0;                        // row r of group g at 1024 g + 64 r
-    static constexpr int SC = RG * 1024;               // the rows' scales for the chunk (<= 256 bytes)
+    static constexpr int WD = WP / 64;                 // W loads per 16-row group
+    static constexpr int W = 0;                        // row r of group g at 16 WP g + WP r
+    static constexpr int SC = RG * 16 * WP;            // the rows' scales for the chunk (<= 256 bytes)
     static constexpr int X = SC + 256;                 // 256 bytes (128 bf16) per X row
     static constexpr int XRows = XQ == 0 ? 1 : 4 * XQ;
     static constexpr int Bytes = X + 256 * XRows;
-    static constexpr int Loads = RG + 1 + (XQ == 0 ? 1 : XQ);   // direct-to-LDS loads per chunk
+    static constexpr int Loads = RG * WD + 1 + (XQ == 0 ? 1 : XQ);   // direct-to-LDS loads per chunk
 };
 
+// 16-byte piece c of row r sits at c ^ swz(r): 64-byte rows (r >> 1) & 3,
+// 128-byte rows (r >> 1) & 7 (16 consecutive rows, one piece each, on
+// distinct banks)
 __device__ __forceinline__ int wo_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int wo_swz8(int r) { return (r >> 1) & 7; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -1593,10 +1658,13 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, bool INT = false>
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM = 0>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
-    using S = WoSlot<RG, XQ>;
+    constexpr bool WIDE = ELEM >= 2;
+    constexpr int WP = WIDE ? 128 : 64;                        // LDS pitch of a W chunk row
+    constexpr int WB = ELEM <= 1 ? 64 : ELEM <= 3 ? 128 : 96;  // code bytes of a W chunk row
+    using S = WoSlot<RG, XQ, WP>;
     static_assert((D - 1) * S::Loads < 64, "loads in flight exceed the counter");
     extern __shared__ __align__(16) uint8_t wo_ring[];
     __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
@@ -1605,7 +1673,7 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     const int r16 = lane & 15, grp = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * (16 * RG);
     const int64_t N = p.n, K = p.k, M = p.m;
-    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const int64_t rowb = K * (ELEM <= 1 ? 4 : ELEM <= 3 ? 8 : 6) / 8, rows = K / BLOCK;
     const ScaleFmt fw{p.fw.ebits, p.fw.mbits, p.fw.bias, p.fw.maxcode, p.fw.smax, p.fw.is_e8m0};
     const float gw = p.gw[0];
     const float pw = split_pow2(gw);
@@ -1619,19 +1687,27 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     // 32-bit offsets (the ABI bounds W below 4 GiB); rows past N re-read row
     // N - 1, rows of X past M re-read row M - 1 (in bounds, never stored).
     //  W: lane l -> row l / 4 of each group, 16-byte piece (l % 4) ^ swz(row),
-    //     landing at 64 row + 16 (l % 4);
+    //     landing at 64 row + 16 (l % 4); wide grids: load k lane l -> row
+    //     8 k + l / 8, piece (l % 8) ^ swz8(row), landing at 128 row + 16 (l % 8)
+    //     (6-bit: only pieces 0..5 exist; the other lanes stay idle);
     //  scales: 128 / BLOCK bytes per row; block 16: lane l -> 4-byte half
     //     l % 2 of row l / 2, block 32: lane l -> row l;
     //  X: XQ = 0: lane l -> dword l of row 0; else load q, lane l -> row
     //     m = 4 q + l / 16, piece (l % 16) ^ (m % 8), landing at 256 m + 16 (l % 16).
     constexpr int SCB = 128 / BLOCK;
     constexpr int ScLanes = 16 * RG * SCB / 4;
-    uint32_t wsrc[RG];
+    uint32_t wsrc[RG][S::WD];
+    bool wact[S::WD];
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-        const int r = lane >> 2;
-        const int64_t n = n0 + 16 * g + r < N ? n0 + 16 * g + r : N - 1;
-        wsrc[g] = (uint32_t)(n * rowb) + 16u * (uint32_t)((lane & 3) ^ wo_swz(r));
+    for (int k = 0; k < S::WD; ++k) {
+        const int r = WIDE ? 8 * k + (lane >> 3) : lane >> 2;
+        const int pc = WIDE ? (lane & 7) ^ wo_swz8(r) : (lane & 3) ^ wo_swz(r);
+        wact[k] = 16 * pc < WB;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int64_t n = n0 + 16 * g + r < N ? n0 + 16 * g + r : N - 1;
+            wsrc[g][k] = (uint32_t)(n * rowb) + 16u * (uint32_t)pc;
+        }
     }
     uint32_t ssrc;
     {
@@ -1659,7 +1735,10 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
         const uint32_t kc = (uint32_t)(wave + (i < mine ? i : mine - 1) * NW);
         uint8_t* const sl = ring + d * S::Bytes;
 #pragma unroll
-        for (int g = 0; g < RG; ++g) dma16(p.qw + wsrc[g] + kc * 64u, sl + S::W + 1024 * g);
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int k = 0; k < S::WD; ++k)
+                if (ELEM < 4 || wact[k]) dma16(p.qw + wsrc[g][k] + kc * (uint32_t)WB, sl + S::W + 16 * WP * g + 1024 * k);
         if (lane < ScLanes) dma4(p.sw + ssrc + kc * (uint32_t)SCB, sl + S::SC);
         if (XQ == 0) {
             dma4(xsrc[0] + kc * 128u, sl + S::X);
@@ -1675,7 +1754,15 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         xoff[t] = S::X + (XQ == 0 ? 16 * (4 * grp + t) : 256 * mr + 16 * ((4 * grp + t) ^ (mr & 7)));
+    // this lane's 32 elements [32 grp, 32 grp + 32) of its row: one 16-byte
+    // piece (4-bit), two (8-bit), or bytes 24 grp .. 24 grp + 23 (6-bit)
     const int woff = S::W + 64 * r16 + 16 * (grp ^ wo_swz(r16));
+    int woffw[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int byte = ELEM >= 4 ? 24 * grp + 8 * j : 32 * grp + 16 * j;
+        woffw[j] = S::W + WP * r16 + 16 * ((byte >> 4) ^ wo_swz8(r16)) + (byte & 15);
+    }
     const int soff = S::SC + (BLOCK == 16 ? 8 * r16 + 2 * grp : 4 * r16 + grp);
 
     v4f acc[RG];
@@ -1688,23 +1775,48 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
         for (int t = 0; t < 4; ++t) xf[t] = *reinterpret_cast<const v4i*>(sl + xoff[t]);
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-            const v4i wv = *reinterpret_cast<const v4i*>(sl + woff + 1024 * g);
+            v4i wv;
+            uint32_t dw[8];
+            if constexpr (!WIDE) {
+                wv = *reinterpret_cast<const v4i*>(sl + woff + 1024 * g);
+            } else if constexpr (ELEM <= 3) {
+                const v4i w0 = *reinterpret_cast<const v4i*>(sl + woffw[0] + 16 * WP * g);
+                const v4i w1 = *reinterpret_cast<const v4i*>(sl + woffw[1] + 16 * WP * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { dw[i] = (uint32_t)w0[i]; dw[4 + i] = (uint32_t)w1[i]; }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const uint64_t v = *reinterpret_cast<const uint64_t*>(sl + woffw[j] + 16 * WP * g);
+                    dw[2 * j] = (uint32_t)v;
+                    dw[2 * j + 1] = (uint32_t)(v >> 32);
+                }
+                dw[6] = dw[7] = 0u;
+            }
             const uint32_t sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + soff + 128 * g)
                                             : (uint32_t)sl[soff + 64 * g];
             const float s0 = sdec[sc & 0xFFu];
             const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const float st = t < 2 ? s0 : s1;                   // dwords 0,1: the first 16 elements
-                if (SPLIT) {
+                const float st = t < 2 ? s0 : s1;                   // elements 0..15: the first block
+                if constexpr (WIDE) {
                     v4i hi, lo;
-                    dq8_bf16_split<INT>((uint32_t)wv[t], st, hi, lo);
+                    dq8_any<ELEM, SPLIT>(dw, t, st, hi, lo);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                     __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
+                    if (SPLIT)
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                         __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
+                } else if (SPLIT) {
+                    v4i hi, lo;
+                    dq8_bf16_split<ELEM == 1>((uint32_t)wv[t], st, hi, lo);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
                 } else {
-                    const v4i wt = dq8_bf16<POW2, INT>((uint32_t)wv[t], st);
+                    const v4i wt = dq8_bf16<POW2, ELEM == 1>((uint32_t)wv[t], st);
                     acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                      __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
                 }
@@ -1763,33 +1875,55 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     }
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, bool INT = false>
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM = 0>
 static hipError_t launch_wo_k(const WoGemmLaunch& p, hipStream_t s)
 {
-    constexpr size_t sh = (size_t)NW * D * WoSlot<RG, XQ>::Bytes;   // the ring, later the partial tiles
+    constexpr size_t sh = (size_t)NW * D * WoSlot<RG, XQ, ELEM >= 2 ? 128 : 64>::Bytes;   // the ring, later the partial tiles
     static_assert(sh >= sizeof(float) * NW * RG * 256, "partial tiles fit the ring");
     static_assert(sh + sizeof(float) * 256 <= 160 * 1024, "LDS");
     if (sh > 64 * 1024) {
-        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, INT>, sh);
+        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM>, sh);
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
-    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, INT>), grid, block, sh, s, p);
+    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM>), grid, block, sh, s, p);
     return hipGetLastError();
+}
+
+// Significant bits of the largest element of each grid (E2M1 2, INT4 3,
+// FP8 E4M3 4, INT8 7, FP6 E2M3 4, FP6 E3M2 3, INT6 5) plus those of the
+// scale: products with at most 8 are exact in bf16, the others (at most 14)
+// take the hi + lo split.
+static bool wo_exact_in_bf16(int elem, const ScaleFmtHost& f)
+{
+    static const int ebits[7] = {2, 3, 4, 7, 4, 3, 5};
+    const int sbits = f.is_e8m0 ? 1 : f.mbits + 1;
+    return ebits[elem] + sbits <= 8;
+}
+
+template <int NW, int D, int RG, int XQ, int ELEM>
+static hipError_t launch_wo_w(const WoGemmLaunch& p, hipStream_t s)
+{
+    const bool split = !wo_exact_in_bf16(ELEM, p.fw);
+    if (p.block == 16) {
+        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false, ELEM>(p, s);
+        return launch_wo_k<NW, D, RG, XQ, 16, false, false, ELEM>(p, s);
+    }
+    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false, ELEM>(p, s);
+    return launch_wo_k<NW, D, RG, XQ, 32, false, false, ELEM>(p, s);
 }
 
 template <int NW, int D, int RG, int XQ>
 static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
 {
-    if (p.elem_int4) {
-        // INT4 x s is exact in bf16 for at most 4 mantissa bits, else split
-        const bool isplit = !int4_exact_in_bf16(p.fw);
-        if (p.block == 16) {
-            if (isplit) return launch_wo_k<NW, D, RG, XQ, 16, true, false, true>(p, s);
-            return launch_wo_k<NW, D, RG, XQ, 16, false, false, true>(p, s);
-        }
-        if (isplit) return launch_wo_k<NW, D, RG, XQ, 32, true, false, true>(p, s);
-        return launch_wo_k<NW, D, RG, XQ, 32, false, false, true>(p, s);
+    switch (p.elem) {
+    case 1: return launch_wo_w<NW, D, RG, XQ, 1>(p, s);
+    case 2: return launch_wo_w<NW, D, RG, XQ, 2>(p, s);
+    case 3: return launch_wo_w<NW, D, RG, XQ, 3>(p, s);
+    case 4: return launch_wo_w<NW, D, RG, XQ, 4>(p, s);
+    case 5: return launch_wo_w<NW, D, RG, XQ, 5>(p, s);
+    case 6: return launch_wo_w<NW, D, RG, XQ, 6>(p, s);
+    default: break;
     }
     const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
     if (p.block == 16) {
@@ -1806,7 +1940,8 @@ static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
 template <int NW, int D, int RG, int XQ>
 static hipError_t launch_wo_fit(const WoGemmLaunch& p, hipStream_t s)
 {
-    if constexpr ((size_t)NW * D * WoSlot<RG, XQ>::Bytes + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ>(p, s);
+    static_assert((size_t)4 * 2 * WoSlot<RG, XQ, 128>::Bytes + 1024 <= 160 * 1024, "the fallback ring fits");
+    if constexpr ((size_t)NW * D * WoSlot<RG, XQ, 128>::Bytes + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ>(p, s);
     else return launch_wo_x<4, 2, RG, XQ>(p, s);
 }
 

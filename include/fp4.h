@@ -123,8 +123,7 @@ typedef enum fp4_transform {
  * symmetric grid -127..127 (two's complement, zero unsigned).  448 or 127
  * takes the place of 6 in the tensor and block scales; the E8M0 rule uses
  * floor(log2 amax_b) - 8 (FP8) or - 6 (INT8) + 127, the OCP MX offsets.
- * Row-wise, column-wise and two-orientation quantize, dequantize and
- * fp4_gemm take them; fp4_wo_gemm returns UNSUPPORTED for them.
+ * Every call takes them.
  * The 6-bit grids (the same page's MXFP6 / MXINT6; reading: the OCP FP6
  * element formats E2M3 and E3M2, and INT6 on -31..31) pack six bits per
  * element as a little-endian bit stream: element c of a row at bits
@@ -132,9 +131,8 @@ typedef enum fp4_transform {
  * E3M2: bias 3, largest 28; sign bit 5, subnormals, no reserved codes;
  * nearest-even, saturating.  INT6: six-bit two's complement, zero unsigned.
  * 7.5, 28 or 31 takes the place of 6; the E8M0 offsets are 2, 4 and 4.
- * Row-wise quantize, dequantize, fp4_gemm and the column-wise and
- * two-orientation calls (with R % 64 == 0, SHAPE otherwise) take them;
- * fp4_wo_gemm returns UNSUPPORTED for them. */
+ * Every call takes them (the column-wise and two-orientation calls with
+ * R % 64 == 0, SHAPE otherwise). */
 typedef enum fp4_element {
     FP4_ELEM_E2M1 = 0,
     FP4_ELEM_INT4 = 1,
@@ -360,7 +358,10 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
  * 1 <= M <= 16; K % 256 == 0 (K = 0 writes Y = 0 and reads neither x nor w);
  * x 16-byte aligned, ldx % 8 == 0, ldy >= N;
  * w's codes 16-byte and scales 4-byte aligned; w's codes < 4 GiB and no
- * transform on w (UNSUPPORTED otherwise).  E2M1 or INT4 weights.
+ * transform on w (UNSUPPORTED otherwise).  Every element grid: E2M1, INT4
+ * and the 8- and 6-bit ones (quant_prune_distill/486 "Метод": the MX
+ * family's 8- and 6-bit members); each product e(w_nk) s_w enters the bf16
+ * matrix instruction exactly, as one bf16 value or as the sum of two.
  */
 FP4_API fp4_status fp4_wo_gemm(const uint16_t* x, int64_t ldx, int64_t m, const fp4_tensor* w, uint16_t* y,
                        int64_t ldy, void* stream);

@@ -189,9 +189,11 @@ def test_6bit_element_checks():
         b = _tensor(rows=8, cols=256, scale=3)
         a.fmt.element = b.fmt.element = elem
         assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE, 8, None) == -2
-        w = _tensor(rows=8, cols=256)
+        w = _tensor(rows=8, cols=256, q=FAKE)
         w.fmt.element = elem
-        assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -2
+        assert L.fp4_wo_gemm(FAKE, 256, 0, ctypes.byref(w), FAKE, 8, None) == -2   # 6-bit weights accepted: M = 0 decides
+        w.q = FAKE + 4                                 # ... after the 8-byte alignment of their codes
+        assert L.fp4_wo_gemm(FAKE, 256, 1, ctypes.byref(w), FAKE, 8, None) == -4
 
 
 def test_binding_refuses_buffers_too_small_for_the_grid():
