@@ -1630,19 +1630,22 @@ __device__ __forceinline__ void dq8_bf16_split(uint32_t w, float s, v4i& hi, v4i
     }
 }
 
-// One ring slot of the weight-only GEMM (byte offsets).  XQ = 0: M == 1,
-// the single X row arrives by 4-byte loads; else XQ loads of four 256-byte
-// X rows each.  WP: LDS pitch of a W row (64 for the 4-bit grids, 128 for
-// the wider ones).
-template <int RG, int XQ, int WP = 64>
+// One ring slot of the weight-only GEMM (byte offsets).  A chunk is SUB
+// runs of 128 K-elements.  XQ = 0: M == 1, the single X row arrives by
+// 4-byte loads (SUB of them); else XQ * SUB loads of four 256-byte X row
+// pieces each.  WP: LDS pitch of a W chunk row (64 bytes, or 128 for the
+// wider rows); SCB: scale bytes of a row per chunk.
+template <int RG, int XQ, int WP, int SUB, int SCB>
 struct WoSlot {
     static constexpr int WD = WP / 64;                 // W loads per 16-row group
     static constexpr int W = 0;                        // row r of group g at 16 WP g + WP r
-    static constexpr int SC = RG * 16 * WP;            // the rows' scales for the chunk (<= 256 bytes)
-    static constexpr int X = SC + 256;                 // 256 bytes (128 bf16) per X row
+    static constexpr int SC = RG * 16 * WP;            // row r of the slot's 16 RG rows at SC + SCB r
+    static constexpr int SCBytes = (RG * 16 * SCB + 255) / 256 * 256;
+    static constexpr int NSC = (RG * 16 * SCB / 4 + 63) / 64;      // 4-byte scale loads (64 lanes each)
+    static constexpr int X = SC + SCBytes;             // piece h of row m at X + 1024 (SUB (m / 4) + h) + 256 (m % 4)
     static constexpr int XRows = XQ == 0 ? 1 : 4 * XQ;
-    static constexpr int Bytes = X + 256 * XRows;
-    static constexpr int Loads = RG * WD + 1 + (XQ == 0 ? 1 : XQ);   // direct-to-LDS loads per chunk
+    static constexpr int Bytes = X + 256 * SUB * XRows;
+    static constexpr int Loads = RG * WD + NSC + SUB * (XQ == 0 ? 1 : XQ);   // direct-to-LDS loads per chunk
 };
 
 // 16-byte piece c of row r sits at c ^ swz(r): 64-byte rows (r >> 1) & 3,
@@ -1658,13 +1661,24 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM = 0>
+// Code bytes of a W row per 128 K-elements and the LDS pitch of a chunk row.
+template <int ELEM, int SUB>
+struct WoRow {
+    static constexpr int Bytes128 = ELEM <= 1 ? 64 : ELEM <= 3 ? 128 : 96;
+    static constexpr int WB = SUB * Bytes128;
+    static constexpr int WP = WB <= 64 ? 64 : 128;
+};
+
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM = 0, int SUB = 1>
 __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 {
     constexpr bool WIDE = ELEM >= 2;
-    constexpr int WP = WIDE ? 128 : 64;                        // LDS pitch of a W chunk row
-    constexpr int WB = ELEM <= 1 ? 64 : ELEM <= 3 ? 128 : 96;  // code bytes of a W chunk row
-    using S = WoSlot<RG, XQ, WP>;
+    static_assert(SUB == 1 || (SUB == 2 && !WIDE), "two runs per chunk for the 4-bit grids");
+    constexpr int WP = WoRow<ELEM, SUB>::WP;                   // LDS pitch of a W chunk row
+    constexpr int WB = WoRow<ELEM, SUB>::WB;                   // code bytes of a W chunk row
+    constexpr int SCB = 128 * SUB / BLOCK;                     // scale bytes of a row per chunk
+    constexpr int SDW = SCB / 4;                               // ... in dwords
+    using S = WoSlot<RG, XQ, WP, SUB, SCB>;
     static_assert((D - 1) * S::Loads < 64, "loads in flight exceed the counter");
     extern __shared__ __align__(16) uint8_t wo_ring[];
     __shared__ float sdec[256];               // decoded scale times the power-of-two part of g
@@ -1680,28 +1694,28 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     const float gres = gw / pw;
     for (int c = tid; c < 256; c += 64 * NW) sdec[c] = scale_decode_any((uint32_t)c, fw) * pw;
     uint8_t* const ring = wo_ring + wave * (D * S::Bytes);
-    const int nchunks = (int)(K / 128);
+    const int nchunks = (int)(K / (128 * SUB));
     const int mine = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;   // chunks wave, wave + NW, ...
 
     // Global sources of this lane's direct-to-LDS loads for chunk 0, as
     // 32-bit offsets (the ABI bounds W below 4 GiB); rows past N re-read row
     // N - 1, rows of X past M re-read row M - 1 (in bounds, never stored).
-    //  W: lane l -> row l / 4 of each group, 16-byte piece (l % 4) ^ swz(row),
-    //     landing at 64 row + 16 (l % 4); wide grids: load k lane l -> row
-    //     8 k + l / 8, piece (l % 8) ^ swz8(row), landing at 128 row + 16 (l % 8)
-    //     (6-bit: only pieces 0..5 exist; the other lanes stay idle);
-    //  scales: 128 / BLOCK bytes per row; block 16: lane l -> 4-byte half
-    //     l % 2 of row l / 2, block 32: lane l -> row l;
-    //  X: XQ = 0: lane l -> dword l of row 0; else load q, lane l -> row
-    //     m = 4 q + l / 16, piece (l % 16) ^ (m % 8), landing at 256 m + 16 (l % 16).
-    constexpr int SCB = 128 / BLOCK;
-    constexpr int ScLanes = 16 * RG * SCB / 4;
+    //  W: 64-byte rows: lane l -> row l / 4 of each group, 16-byte piece
+    //     (l % 4) ^ swz(row), landing at 64 row + 16 (l % 4); 128-byte pitch:
+    //     load k lane l -> row 8 k + l / 8, piece (l % 8) ^ swz8(row), landing
+    //     at 128 row + 16 (l % 8) (6-bit: only pieces 0..5 exist; the other
+    //     lanes stay idle);
+    //  scales: SCB bytes per row; load j lane l -> dword f % SDW of row
+    //     f / SDW, f = 64 j + l, landing at 4 f;
+    //  X: XQ = 0: load h lane l -> dword l of piece h of row 0; else load
+    //     (q, h), lane l -> row m = 4 q + l / 16, 16 bytes (l % 16) ^ (m % 8)
+    //     of its piece h, landing at 1024 (SUB q + h) + 16 l.
     uint32_t wsrc[RG][S::WD];
     bool wact[S::WD];
 #pragma unroll
     for (int k = 0; k < S::WD; ++k) {
-        const int r = WIDE ? 8 * k + (lane >> 3) : lane >> 2;
-        const int pc = WIDE ? (lane & 7) ^ wo_swz8(r) : (lane & 3) ^ wo_swz(r);
+        const int r = WP == 128 ? 8 * k + (lane >> 3) : lane >> 2;
+        const int pc = WP == 128 ? (lane & 7) ^ wo_swz8(r) : (lane & 3) ^ wo_swz(r);
         wact[k] = 16 * pc < WB;
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
@@ -1709,12 +1723,15 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
             wsrc[g][k] = (uint32_t)(n * rowb) + 16u * (uint32_t)pc;
         }
     }
-    uint32_t ssrc;
-    {
-        const int R = BLOCK == 16 ? lane >> 1 : lane;
+    uint32_t ssrc[S::NSC];
+    bool sact[S::NSC];
+#pragma unroll
+    for (int j = 0; j < S::NSC; ++j) {
+        const int f = 64 * j + lane, R = f / SDW;
+        sact[j] = R < 16 * RG;
         const int64_t rr = R < 16 * RG ? R : 16 * RG - 1;
         const int64_t n = n0 + rr < N ? n0 + rr : N - 1;
-        ssrc = (uint32_t)(n * rows) + (BLOCK == 16 ? 4u * (uint32_t)(lane & 1) : 0u);
+        ssrc[j] = (uint32_t)(n * rows) + 4u * (uint32_t)(f % SDW);
     }
     constexpr int XL = XQ == 0 ? 1 : XQ;
     const uint16_t* xsrc[XL];
@@ -1739,86 +1756,94 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 #pragma unroll
             for (int k = 0; k < S::WD; ++k)
                 if (ELEM < 4 || wact[k]) dma16(p.qw + wsrc[g][k] + kc * (uint32_t)WB, sl + S::W + 16 * WP * g + 1024 * k);
-        if (lane < ScLanes) dma4(p.sw + ssrc + kc * (uint32_t)SCB, sl + S::SC);
-        if (XQ == 0) {
-            dma4(xsrc[0] + kc * 128u, sl + S::X);
-        } else {
 #pragma unroll
-            for (int q = 0; q < XL; ++q) dma16(xsrc[q] + kc * 128u, sl + S::X + 1024 * q);
+        for (int j = 0; j < S::NSC; ++j)
+            if (sact[j]) dma4(p.sw + ssrc[j] + kc * (uint32_t)SCB, sl + S::SC + 256 * j);
+#pragma unroll
+        for (int h = 0; h < SUB; ++h) {
+            if (XQ == 0) {
+                dma4(xsrc[0] + kc * (128u * SUB) + 128 * h, sl + S::X + 256 * h);
+            } else {
+#pragma unroll
+                for (int q = 0; q < XL; ++q)
+                    dma16(xsrc[q] + kc * (128u * SUB) + 128 * h, sl + S::X + 1024 * (SUB * q + h));
+            }
         }
     };
 
-    // this lane's fragment addresses inside a slot
+    // this lane's fragment addresses inside a slot, run h of the chunk
     const int mr = r16 < M ? r16 : (int)M - 1;
-    int xoff[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-        xoff[t] = S::X + (XQ == 0 ? 16 * (4 * grp + t) : 256 * mr + 16 * ((4 * grp + t) ^ (mr & 7)));
-    // this lane's 32 elements [32 grp, 32 grp + 32) of its row: one 16-byte
+    auto xoff = [&](int h, int t) {
+        return S::X + (XQ == 0 ? 256 * h + 16 * (4 * grp + t)
+                               : 1024 * (SUB * (mr >> 2) + h) + 256 * (mr & 3) + 16 * ((4 * grp + t) ^ (mr & 7)));
+    };
+    // this lane's 32 elements [128 h + 32 grp, + 32) of its row: one 16-byte
     // piece (4-bit), two (8-bit), or bytes 24 grp .. 24 grp + 23 (6-bit)
-    const int woff = S::W + 64 * r16 + 16 * (grp ^ wo_swz(r16));
-    int woffw[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int byte = ELEM >= 4 ? 24 * grp + 8 * j : 32 * grp + 16 * j;
-        woffw[j] = S::W + WP * r16 + 16 * ((byte >> 4) ^ wo_swz8(r16)) + (byte & 15);
-    }
-    const int soff = S::SC + (BLOCK == 16 ? 8 * r16 + 2 * grp : 4 * r16 + grp);
+    auto woff = [&](int h, int j) {
+        if (WP == 64) return S::W + 64 * r16 + 16 * (grp ^ wo_swz(r16));
+        const int byte = ELEM >= 4 ? 24 * grp + 8 * j : ELEM >= 2 ? 32 * grp + 16 * j : 64 * h + 16 * grp;
+        return S::W + WP * r16 + 16 * ((byte >> 4) ^ wo_swz8(r16)) + (byte & 15);
+    };
+    // the scale bytes of run h: block 16 two (elements 0..15, 16..31), block 32 one
+    auto soff = [&](int h) { return S::SC + SCB * r16 + (BLOCK == 16 ? 8 * h + 2 * grp : 4 * h + grp); };
 
     v4f acc[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
     auto consume = [&](int d) {
         const uint8_t* const sl = ring + d * S::Bytes;
-        v4i xf[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xf[t] = *reinterpret_cast<const v4i*>(sl + xoff[t]);
+        for (int h = 0; h < SUB; ++h) {
+            v4i xf[4];
 #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            v4i wv;
-            uint32_t dw[8];
-            if constexpr (!WIDE) {
-                wv = *reinterpret_cast<const v4i*>(sl + woff + 1024 * g);
-            } else if constexpr (ELEM <= 3) {
-                const v4i w0 = *reinterpret_cast<const v4i*>(sl + woffw[0] + 16 * WP * g);
-                const v4i w1 = *reinterpret_cast<const v4i*>(sl + woffw[1] + 16 * WP * g);
+            for (int t = 0; t < 4; ++t) xf[t] = *reinterpret_cast<const v4i*>(sl + xoff(h, t));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { dw[i] = (uint32_t)w0[i]; dw[4 + i] = (uint32_t)w1[i]; }
-            } else {
+            for (int g = 0; g < RG; ++g) {
+                v4i wv;
+                uint32_t dw[8];
+                if constexpr (!WIDE) {
+                    wv = *reinterpret_cast<const v4i*>(sl + woff(h, 0) + 16 * WP * g);
+                } else if constexpr (ELEM <= 3) {
+                    const v4i w0 = *reinterpret_cast<const v4i*>(sl + woff(h, 0) + 16 * WP * g);
+                    const v4i w1 = *reinterpret_cast<const v4i*>(sl + woff(h, 1) + 16 * WP * g);
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const uint64_t v = *reinterpret_cast<const uint64_t*>(sl + woffw[j] + 16 * WP * g);
-                    dw[2 * j] = (uint32_t)v;
-                    dw[2 * j + 1] = (uint32_t)(v >> 32);
+                    for (int i = 0; i < 4; ++i) { dw[i] = (uint32_t)w0[i]; dw[4 + i] = (uint32_t)w1[i]; }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        const uint64_t v = *reinterpret_cast<const uint64_t*>(sl + woff(h, j) + 16 * WP * g);
+                        dw[2 * j] = (uint32_t)v;
+                        dw[2 * j + 1] = (uint32_t)(v >> 32);
+                    }
+                    dw[6] = dw[7] = 0u;
                 }
-                dw[6] = dw[7] = 0u;
-            }
-            const uint32_t sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + soff + 128 * g)
-                                            : (uint32_t)sl[soff + 64 * g];
-            const float s0 = sdec[sc & 0xFFu];
-            const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
+                const uint32_t sc = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sl + soff(h) + 16 * SCB * g)
+                                                : (uint32_t)sl[soff(h) + 16 * SCB * g];
+                const float s0 = sdec[sc & 0xFFu];
+                const float s1 = BLOCK == 16 ? sdec[(sc >> 8) & 0xFFu] : s0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float st = t < 2 ? s0 : s1;                   // elements 0..15: the first block
-                if constexpr (WIDE) {
-                    v4i hi, lo;
-                    dq8_any<ELEM, SPLIT>(dw, t, st, hi, lo);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
-                                                                     __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
-                    if (SPLIT)
+                for (int t = 0; t < 4; ++t) {
+                    const float st = t < 2 ? s0 : s1;                   // elements 0..15: the first block
+                    if constexpr (WIDE) {
+                        v4i hi, lo;
+                        dq8_any<ELEM, SPLIT>(dw, t, st, hi, lo);
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                         __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
+                        if (SPLIT)
+                            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                             __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
+                    } else if (SPLIT) {
+                        v4i hi, lo;
+                        dq8_bf16_split<ELEM == 1>((uint32_t)wv[t], st, hi, lo);
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                         __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
                         acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
                                                                          __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
-                } else if (SPLIT) {
-                    v4i hi, lo;
-                    dq8_bf16_split<ELEM == 1>((uint32_t)wv[t], st, hi, lo);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
-                                                                     __builtin_bit_cast(v8bf, hi), acc[g], 0, 0, 0);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
-                                                                     __builtin_bit_cast(v8bf, lo), acc[g], 0, 0, 0);
-                } else {
-                    const v4i wt = dq8_bf16<POW2, ELEM == 1>((uint32_t)wv[t], st);
-                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
-                                                                     __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
+                    } else {
+                        const v4i wt = dq8_bf16<POW2, ELEM == 1>((uint32_t)wv[t], st);
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xf[t]),
+                                                                         __builtin_bit_cast(v8bf, wt), acc[g], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -1875,18 +1900,21 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
     }
 }
 
-template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM = 0>
+template <int RG, int XQ, int ELEM, int SUB, int BLOCK>
+using WoSlotOf = WoSlot<RG, XQ, WoRow<ELEM, SUB>::WP, SUB, 128 * SUB / BLOCK>;
+
+template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM, int SUB>
 static hipError_t launch_wo_k(const WoGemmLaunch& p, hipStream_t s)
 {
-    constexpr size_t sh = (size_t)NW * D * WoSlot<RG, XQ, ELEM >= 2 ? 128 : 64>::Bytes;   // the ring, later the partial tiles
+    constexpr size_t sh = (size_t)NW * D * WoSlotOf<RG, XQ, ELEM, SUB, BLOCK>::Bytes;   // the ring, later the partial tiles
     static_assert(sh >= sizeof(float) * NW * RG * 256, "partial tiles fit the ring");
     static_assert(sh + sizeof(float) * 256 <= 160 * 1024, "LDS");
     if (sh > 64 * 1024) {
-        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM>, sh);
+        const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM, SUB>, sh);
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)((p.n + 16 * RG - 1) / (16 * RG))), block(64 * NW);
-    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM>), grid, block, sh, s, p);
+    hipLaunchKernelGGL((k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM, SUB>), grid, block, sh, s, p);
     return hipGetLastError();
 }
 
@@ -1901,59 +1929,58 @@ static bool wo_exact_in_bf16(int elem, const ScaleFmtHost& f)
     return ebits[elem] + sbits <= 8;
 }
 
-template <int NW, int D, int RG, int XQ, int ELEM>
+// SUB: 128-element runs per chunk of the 4-bit grids (the wider grids
+// take one).
+template <int NW, int D, int RG, int XQ, int ELEM, int SUB>
 static hipError_t launch_wo_w(const WoGemmLaunch& p, hipStream_t s)
 {
+    constexpr int U = ELEM >= 2 ? 1 : SUB;
     const bool split = !wo_exact_in_bf16(ELEM, p.fw);
     if (p.block == 16) {
-        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false, ELEM>(p, s);
-        return launch_wo_k<NW, D, RG, XQ, 16, false, false, ELEM>(p, s);
+        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false, ELEM, U>(p, s);
+        return launch_wo_k<NW, D, RG, XQ, 16, false, false, ELEM, U>(p, s);
     }
-    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false, ELEM>(p, s);
-    return launch_wo_k<NW, D, RG, XQ, 32, false, false, ELEM>(p, s);
+    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false, ELEM, U>(p, s);
+    return launch_wo_k<NW, D, RG, XQ, 32, false, false, ELEM, U>(p, s);
 }
 
-template <int NW, int D, int RG, int XQ>
+template <int NW, int D, int RG, int XQ, int SUB>
 static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
 {
     switch (p.elem) {
-    case 1: return launch_wo_w<NW, D, RG, XQ, 1>(p, s);
-    case 2: return launch_wo_w<NW, D, RG, XQ, 2>(p, s);
-    case 3: return launch_wo_w<NW, D, RG, XQ, 3>(p, s);
-    case 4: return launch_wo_w<NW, D, RG, XQ, 4>(p, s);
-    case 5: return launch_wo_w<NW, D, RG, XQ, 5>(p, s);
-    case 6: return launch_wo_w<NW, D, RG, XQ, 6>(p, s);
+    case 1: return launch_wo_w<NW, D, RG, XQ, 1, SUB>(p, s);
+    case 2: return launch_wo_w<NW, D, RG, XQ, 2, SUB>(p, s);
+    case 3: return launch_wo_w<NW, D, RG, XQ, 3, SUB>(p, s);
+    case 4: return launch_wo_w<NW, D, RG, XQ, 4, SUB>(p, s);
+    case 5: return launch_wo_w<NW, D, RG, XQ, 5, SUB>(p, s);
+    case 6: return launch_wo_w<NW, D, RG, XQ, 6, SUB>(p, s);
     default: break;
     }
     const bool split = !exact_in_bf16(p.fw), pow2 = p.fw.is_e8m0 != 0;
     if (p.block == 16) {
-        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false>(p, s);
-        if (pow2) return launch_wo_k<NW, D, RG, XQ, 16, false, true>(p, s);
-        return launch_wo_k<NW, D, RG, XQ, 16, false, false>(p, s);
+        if (split) return launch_wo_k<NW, D, RG, XQ, 16, true, false, 0, SUB>(p, s);
+        if (pow2) return launch_wo_k<NW, D, RG, XQ, 16, false, true, 0, SUB>(p, s);
+        return launch_wo_k<NW, D, RG, XQ, 16, false, false, 0, SUB>(p, s);
     }
-    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false>(p, s);
-    if (pow2) return launch_wo_k<NW, D, RG, XQ, 32, false, true>(p, s);
-    return launch_wo_k<NW, D, RG, XQ, 32, false, false>(p, s);
+    if (split) return launch_wo_k<NW, D, RG, XQ, 32, true, false, 0, SUB>(p, s);
+    if (pow2) return launch_wo_k<NW, D, RG, XQ, 32, false, true, 0, SUB>(p, s);
+    return launch_wo_k<NW, D, RG, XQ, 32, false, false, 0, SUB>(p, s);
 }
 
-// Ring shape per problem class: NW waves, D slots per wave, RG row groups.
-template <int NW, int D, int RG, int XQ>
+// Ring shape per problem class: NW waves, D slots per wave, RG row groups,
+// SUB runs per chunk; the largest slot of any grid and block must fit.
+template <int NW, int D, int RG, int XQ, int SUB>
 static hipError_t launch_wo_fit(const WoGemmLaunch& p, hipStream_t s)
 {
-    static_assert((size_t)4 * 2 * WoSlot<RG, XQ, 128>::Bytes + 1024 <= 160 * 1024, "the fallback ring fits");
-    if constexpr ((size_t)NW * D * WoSlot<RG, XQ, 128>::Bytes + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ>(p, s);
-    else return launch_wo_x<4, 2, RG, XQ>(p, s);
+    constexpr size_t big = WoSlot<RG, XQ, 128, SUB, 128 * SUB / 16>::Bytes;
+    static_assert((size_t)4 * 2 * big + 1024 <= 160 * 1024, "the fallback ring fits");
+    if constexpr ((size_t)NW * D * big + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ, SUB>(p, s);
+    else return launch_wo_x<4, 2, RG, XQ, SUB>(p, s);
 }
+
 
 constexpr int64_t kWoManyGroups = 512;   // 16-row groups that fill the device on their own
 
-// Per problem class (measured on the Qwen-2.5 7B MLP decode shapes):
-//  M = 1: four waves with four slots each; with fewer than 512 row groups
-//   eight waves, so that the single workgroup per CU still keeps 32 chunks
-//   in flight.
-//  M > 1 with many row groups: two row groups share every X chunk; for
-//   M > 8 the slot is 6.4 KB and two slots per wave keep three workgroups
-//   per CU resident.
 // Zero fill of a bf16 matrix with row stride ld, one 2-byte store per
 // element (a kernel rather than a memset, so graph capture records a kernel
 // node).
@@ -1975,13 +2002,25 @@ hipError_t launch_fill_zero_bf16(uint16_t* c, int64_t ld, int64_t rows, int64_t 
     return hipGetLastError();
 }
 
+// Per problem class (measured on the Qwen-2.5 7B MLP decode shapes):
+//  M = 1: four waves with four slots each; with fewer than 512 row groups
+//   eight waves, so that the single workgroup per CU still keeps 32 chunks
+//   in flight.
+//  M > 1 with many row groups: two row groups share every X chunk; for
+//   M > 8 the slot is 6.4 KB and two slots per wave keep three workgroups
+//   per CU resident.
+//  M > 4 with few row groups (one workgroup per CU): chunks of two
+//   128-element runs, so each wave's X, scale and W loads and waits cover
+//   twice the weight bytes (down projection, M = 16: 19.1 -> 17.3 us; with
+//   many row groups the larger ring costs resident workgroups and is
+//   slower, and at M = 1 the single run per chunk is faster).
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
     const bool many = (p.n + 15) / 16 >= kWoManyGroups;
-    if (p.m == 1) return many ? launch_wo_fit<4, 4, 1, 0>(p, s) : launch_wo_fit<8, 4, 1, 0>(p, s);
-    if (p.m <= 4) return many ? launch_wo_fit<4, 4, 2, 1>(p, s) : launch_wo_fit<4, 4, 1, 1>(p, s);
-    if (p.m <= 8) return many ? launch_wo_fit<4, 4, 2, 2>(p, s) : launch_wo_fit<4, 4, 1, 2>(p, s);
-    return many ? launch_wo_fit<4, 2, 2, 4>(p, s) : launch_wo_fit<4, 4, 1, 4>(p, s);
+    if (p.m == 1) return many ? launch_wo_fit<4, 4, 1, 0, 1>(p, s) : launch_wo_fit<8, 4, 1, 0, 1>(p, s);
+    if (p.m <= 4) return many ? launch_wo_fit<4, 4, 2, 1, 1>(p, s) : launch_wo_fit<4, 4, 1, 1, 1>(p, s);
+    if (p.m <= 8) return many ? launch_wo_fit<4, 4, 2, 2, 1>(p, s) : launch_wo_fit<4, 4, 1, 2, 2>(p, s);
+    return many ? launch_wo_fit<4, 2, 2, 4, 1>(p, s) : launch_wo_fit<4, 4, 1, 4, 2>(p, s);
 }
 
 }  // namespace fp4
