@@ -82,7 +82,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,w8,gemm,wo", help="extra legs (comma list, or 'none')")
+    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,w8,gemm,wo,wowide",
+                   help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 64 MiB device copy three times (calibrates HBM byte counters)")
@@ -419,6 +420,20 @@ def leg_8bit(torch, fq, inputs, xs):
             "us_per_call": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del gs, outs
+    for elem, name in (("fp8_e4m3", "mxfp8"), ("int6", "mxint6")):
+        outs = [(fq.QTensor.empty(rows, cols, 32, "e8m0", amax="none", element=elem),
+                 fq.QTensor.empty(cols, rows, 32, "e8m0", amax="none", element=elem)) for _ in xs]
+
+        def rec_b(_):
+            for j in range(len(xs)):
+                fq.fp4_quantize_both(xs[j], 32, "e8m0", amax="none", out=outs[j], element=elem)
+        gs = GraphSet(torch, 1, rec_b)
+        ms = time_graphs(torch, gs, 20, 3) / len(xs)
+        nb = n * 2 + 2 * (n * fq.ELEMENT_BITS[elem] // 8 + n // 32 + 8)
+        res[f"{name}_quantize_both"] = {
+            "us_per_call": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gs, outs
     m, n, k = 8192, 11008, 4096
     for name, (elem, fmt, block, pol) in {"mxfp8": ("fp8_e4m3", "e8m0", 32, "none"),
                                           "nvint8": ("int8", "e4m3", 16, "current"),
@@ -440,7 +455,8 @@ def leg_8bit(torch, fq, inputs, xs):
                                   "frac_fp8_peak": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4)}
         del a, w, qa, qw, c, gs
     res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each) and "
-                       "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise and column-wise; "
+                       "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise, column-wise and "
+                       "both orientations (MXFP8, MXINT6); "
                        "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8, INT8 with E4M3 block-16 scales, "
                        "MXFP6 (E2M3) and MXINT6")
     return res
@@ -478,6 +494,36 @@ def leg_wo(torch, fq, inputs):
                                                 "kernel": "k_wo_gemm", "us_per_launch": round(ms * 1e3, 2),
                                                 "algo_bytes_per_launch": algo, "traffic": None}}
         del qws
+    return res
+
+
+def leg_wo_wide(torch, fq, inputs):
+    """Weight-only GEMM on the 8- and 6-bit grids with E8M0 block-32 scales
+    (MXFP8, MXINT8, MXFP6 E2M3, MXINT6), W [18944, 3584] and [3584, 18944],
+    M in {1, 16}; 6 weight copies rotate (>= 200 MB)."""
+    res = {}
+    for elem, name in (("fp8_e4m3", "mxfp8"), ("int8", "mxint8"), ("fp6_e2m3", "mxfp6_e2m3"), ("int6", "mxint6")):
+        for proj, (n, k) in {"up": (18944, 3584), "down": (3584, 18944)}.items():
+            w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["decode_" + proj], torch.bfloat16)
+            qws = [fq.fp4_quantize(w, 32, "e8m0", amax="none", element=elem) for _ in range(6)]
+            del w
+            for m in (1, 16):
+                x = inputs.device_normal((m, k), 1.0, 10 + m, torch.bfloat16)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+                def rec(_):
+                    for q in qws:
+                        fq.fp4_wo_gemm(x, q, out=y)
+                gs = GraphSet(torch, 1, rec)
+                ms = time_graphs(torch, gs, 20, 3) / len(qws)
+                algo = n * k * fq.ELEMENT_BITS[elem] // 8 + n * k // 32 + 8 + m * k * 2 + m * n * 2
+                gbs = algo / (ms * 1e-3) / 1e9
+                res[f"{name}_{proj}_m{m}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                del gs
+            del qws
+    res["workload"] = ("Qwen-2.5 7B MLP decode shapes, weights quantized on the 8- and 6-bit grids with E8M0 "
+                       "block-32 scales, bf16 X with M = 1 and 16")
     return res
 
 
@@ -609,6 +655,9 @@ def main():
         torch.cuda.empty_cache()
     if "wo" in want:
         legs["wo_gemm_qwen25"] = leg_wo(torch, fq, inputs)
+        torch.cuda.empty_cache()
+    if "wowide" in want:
+        legs["wo_gemm_qwen25_wide_grids"] = leg_wo_wide(torch, fq, inputs)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {"metric": "FP4 quantize GB/s (% HBM peak); block-scaled FP4 GEMM TFLOP/s (% MFMA peak)",
