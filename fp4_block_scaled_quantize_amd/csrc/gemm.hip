@@ -1903,12 +1903,17 @@ __global__ __launch_bounds__(64 * NW) void k_wo_gemm(WoGemmLaunch p)
 template <int RG, int XQ, int ELEM, int SUB, int BLOCK>
 using WoSlotOf = WoSlot<RG, XQ, WoRow<ELEM, SUB>::WP, SUB, 128 * SUB / BLOCK>;
 
+// A ring of NW waves x D slots when it fits the LDS next to the scale
+// table, else four waves x two slots.
 template <int NW, int D, int RG, int XQ, int BLOCK, bool SPLIT, bool POW2, int ELEM, int SUB>
 static hipError_t launch_wo_k(const WoGemmLaunch& p, hipStream_t s)
 {
     constexpr size_t sh = (size_t)NW * D * WoSlotOf<RG, XQ, ELEM, SUB, BLOCK>::Bytes;   // the ring, later the partial tiles
+    if constexpr (sh + sizeof(float) * 256 > 160 * 1024) {
+        static_assert(NW != 4 || D != 2, "the smallest ring fits");
+        return launch_wo_k<4, 2, RG, XQ, BLOCK, SPLIT, POW2, ELEM, SUB>(p, s);
+    }
     static_assert(sh >= sizeof(float) * NW * RG * 256, "partial tiles fit the ring");
-    static_assert(sh + sizeof(float) * 256 <= 160 * 1024, "LDS");
     if (sh > 64 * 1024) {
         const hipError_t e = allow_lds(k_wo_gemm<NW, D, RG, XQ, BLOCK, SPLIT, POW2, ELEM, SUB>, sh);
         if (e != hipSuccess) return e;
@@ -1967,16 +1972,6 @@ static hipError_t launch_wo_x(const WoGemmLaunch& p, hipStream_t s)
     return launch_wo_k<NW, D, RG, XQ, 32, false, false, 0, SUB>(p, s);
 }
 
-// Ring shape per problem class: NW waves, D slots per wave, RG row groups,
-// SUB runs per chunk; the largest slot of any grid and block must fit.
-template <int NW, int D, int RG, int XQ, int SUB>
-static hipError_t launch_wo_fit(const WoGemmLaunch& p, hipStream_t s)
-{
-    constexpr size_t big = WoSlot<RG, XQ, 128, SUB, 128 * SUB / 16>::Bytes;
-    static_assert((size_t)4 * 2 * big + 1024 <= 160 * 1024, "the fallback ring fits");
-    if constexpr ((size_t)NW * D * big + 1024 <= 160 * 1024) return launch_wo_x<NW, D, RG, XQ, SUB>(p, s);
-    else return launch_wo_x<4, 2, RG, XQ, SUB>(p, s);
-}
 
 
 constexpr int64_t kWoManyGroups = 512;   // 16-row groups that fill the device on their own
@@ -2010,17 +2005,20 @@ hipError_t launch_fill_zero_bf16(uint16_t* c, int64_t ld, int64_t rows, int64_t 
 //   M > 8 the slot is 6.4 KB and two slots per wave keep three workgroups
 //   per CU resident.
 //  M > 4 with few row groups (one workgroup per CU): chunks of two
-//   128-element runs, so each wave's X, scale and W loads and waits cover
-//   twice the weight bytes (down projection, M = 16: 19.1 -> 17.3 us; with
-//   many row groups the larger ring costs resident workgroups and is
+//   128-element runs for the 4-bit grids, so each wave's X, scale and W
+//   loads and waits cover twice the weight bytes (down projection, M = 16:
+//   19.1 -> 17.3 us, where the 10.5 KB slot leaves room for two per wave;
+//   with many row groups the larger ring costs resident workgroups and is
 //   slower, and at M = 1 the single run per chunk is faster).
+//  Each grid takes the ring asked for when its slot fits the LDS, else
+//  four waves x two slots.
 hipError_t launch_wo_gemm(const WoGemmLaunch& p, hipStream_t s)
 {
     const bool many = (p.n + 15) / 16 >= kWoManyGroups;
-    if (p.m == 1) return many ? launch_wo_fit<4, 4, 1, 0, 1>(p, s) : launch_wo_fit<8, 4, 1, 0, 1>(p, s);
-    if (p.m <= 4) return many ? launch_wo_fit<4, 4, 2, 1, 1>(p, s) : launch_wo_fit<4, 4, 1, 1, 1>(p, s);
-    if (p.m <= 8) return many ? launch_wo_fit<4, 4, 2, 2, 1>(p, s) : launch_wo_fit<4, 4, 1, 2, 2>(p, s);
-    return many ? launch_wo_fit<4, 2, 2, 4, 1>(p, s) : launch_wo_fit<4, 4, 1, 4, 2>(p, s);
+    if (p.m == 1) return many ? launch_wo_x<4, 4, 1, 0, 1>(p, s) : launch_wo_x<8, 4, 1, 0, 1>(p, s);
+    if (p.m <= 4) return many ? launch_wo_x<4, 4, 2, 1, 1>(p, s) : launch_wo_x<4, 4, 1, 1, 1>(p, s);
+    if (p.m <= 8) return many ? launch_wo_x<4, 4, 2, 2, 1>(p, s) : launch_wo_x<4, 4, 1, 2, 2>(p, s);
+    return many ? launch_wo_x<4, 2, 2, 4, 1>(p, s) : launch_wo_x<4, 4, 1, 4, 2>(p, s);
 }
 
 }  // namespace fp4
