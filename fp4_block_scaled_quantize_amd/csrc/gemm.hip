@@ -37,6 +37,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 256;        // workgroup tile (rows of W) x (rows of A)
@@ -1067,11 +1068,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_dq(GemmLaunch p)
 // ---------------------------------------------------------------------------
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-template <int BLOCK>
+// A 128-element stage: RB code bytes per row (64 for E2M1, 128 for FP8).
+template <int BLOCK, int RB = kMx3RB>
 struct NvStage {
+    static constexpr int kRB = RB;
+    static constexpr int kCodes = kTile * RB;                  // per operand
     static constexpr int kScaleRow = kMx3BK / BLOCK;           // scale bytes per row per stage
     static constexpr int kScales = kTile * kScaleRow;          // per operand
-    static constexpr int kBytes = 2 * kMx3Codes + 2 * kScales;
+    static constexpr int kBytes = 2 * kCodes + 2 * kScales;
     static constexpr int kTable = 2 * 256 * 4;                 // decode tables of W and A (f16x2 or f32)
 };
 
@@ -1085,7 +1089,11 @@ struct NvStage {
 //    (exact: at most 6 significant bits) and rounded to a bf16 pair, which
 //    is exact.  gfx950 has no packed bf16 multiply, so this costs two VALU
 //    per element where the f16 forms cost one.
-enum { kNvTable = 0, kNvE4M3 = 1, kNvBf16 = 2 };
+//  kNvFp8: FP8 E4M3 elements with E8M0 scales on both operands (MXFP8):
+//    one scaled FP8 -> bf16 conversion per element pair applies the
+//    power-of-two scale exactly (4 significant bits fit bf16), bf16 matrix
+//    instruction.  Rows are 128 code bytes per stage.
+enum { kNvTable = 0, kNvE4M3 = 1, kNvBf16 = 2, kNvFp8 = 3 };
 
 // 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times
 // the f16 block scale s2 (replicated in both halves).
@@ -1114,12 +1122,24 @@ __device__ __forceinline__ v8bf nv_convert8_bf16(uint32_t w, float s)
     return r;
 }
 
-// Fragments of one half stage (chunk pair ks) for one lane: four W and two
-// A 16-byte code fragments and their raw scale bytes (block 16: the two
-// scales of the chunk in one u16; block 32: one byte).
-template <int JA>
+// 8 FP8 E4M3 codes (two dwords, element 4 d + b in byte b of dword d)
+// times the power-of-two scale s, as bf16 (kNvFp8; exact).
+__device__ __forceinline__ v8bf nv_convert8_fp8(uint32_t d0, uint32_t d1, float s)
+{
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, s, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, s, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, s, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, s, true);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Fragments of one half stage (chunk pair ks) for one lane: four W and JA
+// A code fragments of P 16-byte pieces (32 E2M1 or FP8 elements) and their
+// raw scale bytes (block 16: the two scales of the chunk in one u16; block
+// 32: one byte).
+template <int JA, int P = 1>
 struct NvHalf {
-    v4i w[4], a[JA];
+    v4i w[4][P], a[JA][P];
     uint32_t sw[4], sa[JA];
 };
 
@@ -1133,11 +1153,15 @@ struct NvHalf {
 template <int BLOCK, int NS, int CVT, int WM>
 __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
 {
-    using L = NvStage<BLOCK>;
+    constexpr bool FP8 = CVT == kNvFp8;
+    using L = NvStage<BLOCK, FP8 ? 128 : kMx3RB>;
+    constexpr int RB = L::kRB;                  // code bytes per row per stage
+    constexpr int P = RB / 64;                  // 16-byte pieces per lane fragment
+    constexpr int CPR = RB / 16;                // 16-byte chunks per row
     constexpr int NWV = 2 * WM;                 // waves: 2 along n (128 rows of W each) x WM along m
     constexpr int JA = 8 / WM;                  // 32-row A fragments per wave (its 32 JA rows of A)
-    constexpr int CK = 16 / NWV;                // 16-byte code DMAs per lane per operand and stage
-    constexpr bool HW_E4M3 = CVT == kNvE4M3, BF16 = CVT == kNvBf16;
+    constexpr int CK = kTile * CPR / 64 / NWV;  // 16-byte code DMAs per lane per operand and stage
+    constexpr bool HW_E4M3 = CVT == kNvE4M3, BF16 = CVT == kNvBf16 || FP8;
     using V8 = std::conditional_t<BF16, v8bf, v8h>;
     static_assert(NS >= 2, "at least two stages");
     extern __shared__ __align__(16) uint8_t smem[];
@@ -1148,8 +1172,10 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
     int tn, tm;
     tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
     const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
-    const int64_t rowb = K / 2, rows = K / BLOCK;
+    const int64_t rowb = FP8 ? K : K / 2, rows = K / BLOCK;
     const int KT = (int)(K / kMx3BK);
+    // 16-byte chunk c of row r sits at c ^ swz(r) (64- or 128-byte rows)
+    auto swz = [&](int r) { return FP8 ? mx_swz<256>(r) : mx_swz<128>(r); };
 
     // scale code -> f16 (exact for these formats), replicated for packed
     // math; or -> fp32 for the bf16 form, which (as the dequantize path)
@@ -1174,8 +1200,8 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
     const uint8_t* srca[CK];
 #pragma unroll
     for (int k = 0; k < CK; ++k) {
-        const int r = 16 * (CK * wave + k) + (lane >> 2);
-        const int c = (lane & 3) ^ mx_swz<128>(r);
+        const int r = (64 / CPR) * (CK * wave + k) + lane / CPR;
+        const int c = (lane % CPR) ^ swz(r);
         const int64_t nr = n_base + r < N ? n_base + r : N - 1;
         const int64_t mr = m_base + r < M ? m_base + r : M - 1;
         srcw[k] = p.qb + nr * rowb + 16 * c;
@@ -1196,7 +1222,7 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
         const int r = BLOCK == 16 ? qq >> 1 : qq, d = BLOCK == 16 ? qq & 1 : 0;
         srcs[j] = is_a ? p.sa + (m_base + r < M ? m_base + r : M - 1) * rows + 4 * d
                        : p.sb + (n_base + r < N ? n_base + r : N - 1) * rows + 4 * d;
-        sdst[j] = 2 * kMx3Codes + (is_a ? L::kScales : 0) + 4 * (qq - lane);
+        sdst[j] = 2 * L::kCodes + (is_a ? L::kScales : 0) + 4 * (qq - lane);
     }
 
     // DMA of stage kt into buffer kt % NS; past the last stage the last one
@@ -1207,8 +1233,8 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
         uint8_t* st = smem + (kt % NS) * L::kBytes;
 #pragma unroll
         for (int k = 0; k < CK; ++k) {
-            dma16(srcw[k] + (int64_t)ks * kMx3RB, st + 1024 * (CK * wave + k));
-            dma16(srca[k] + (int64_t)ks * kMx3RB, st + kMx3Codes + 1024 * (CK * wave + k));
+            dma16(srcw[k] + (int64_t)ks * RB, st + 1024 * (CK * wave + k));
+            dma16(srca[k] + (int64_t)ks * RB, st + L::kCodes + 1024 * (CK * wave + k));
         }
 #pragma unroll
         for (int j = 0; j < kSDma; ++j) dma4(srcs[j] + (int64_t)ks * L::kScaleRow, st + sdst[j]);
@@ -1216,22 +1242,27 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
     constexpr int kLoads = 2 * CK + kSDma;
 
     const int frow = lane & 31, khalf = lane >> 5;
-    auto load_half = [&](NvHalf<JA>& h, int kt, int ks) {
+    // chunk c = 2 ks + khalf of the row's 32 P-byte chunks: pieces P c ..
+    auto load_half = [&](NvHalf<JA, P>& h, int kt, int ks) {
         const uint8_t* st = smem + (kt % NS) * L::kBytes;
-        const uint8_t* ssw = st + 2 * kMx3Codes;
+        const uint8_t* ssw = st + 2 * L::kCodes;
         const uint8_t* ssa = ssw + L::kScales;
         const int c = 2 * ks + khalf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wn * 128 + 32 * i + frow;
-            h.w[i] = *reinterpret_cast<const v4i*>(st + r * kMx3RB + 16 * (c ^ mx_swz<128>(r)));
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                h.w[i][q] = *reinterpret_cast<const v4i*>(st + r * RB + 16 * ((P * c + q) ^ swz(r)));
             h.sw[i] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssw + r * L::kScaleRow + 2 * c)
                                   : (uint32_t)ssw[r * L::kScaleRow + c];
         }
 #pragma unroll
         for (int j = 0; j < JA; ++j) {
             const int r = wm * 32 * JA + 32 * j + frow;
-            h.a[j] = *reinterpret_cast<const v4i*>(st + kMx3Codes + r * kMx3RB + 16 * (c ^ mx_swz<128>(r)));
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                h.a[j][q] = *reinterpret_cast<const v4i*>(st + L::kCodes + r * RB + 16 * ((P * c + q) ^ swz(r)));
             h.sa[j] = BLOCK == 16 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ssa + r * L::kScaleRow + 2 * c)
                                   : (uint32_t)ssa[r * L::kScaleRow + c];
         }
@@ -1250,18 +1281,28 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
         const uint32_t b = BLOCK == 16 ? (t >= 2 ? code >> 8 : code & 0xFFu) : code;
         return __uint_as_float(tb[b]);
     };
-    auto convert = [&](const NvHalf<JA>& h, int t, V8 (&cw)[4], V8 (&ca)[JA]) {
-        if constexpr (BF16) {
+    auto convert = [&](const NvHalf<JA, P>& h, int t, V8 (&cw)[4], V8 (&ca)[JA]) {
+        if constexpr (FP8) {
+            // elements 8 t .. 8 t + 7: dwords 2 t, 2 t + 1 of the 32 bytes
+            const int q = (2 * t) >> 2, d = (2 * t) & 3;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8_bf16((uint32_t)h.w[i][t], scale_f32(h.sw[i], t, tab));
+            for (int i = 0; i < 4; ++i)
+                cw[i] = nv_convert8_fp8((uint32_t)h.w[i][q % P][d], (uint32_t)h.w[i][q % P][d + 1], scale_f32(h.sw[i], t, tab));
 #pragma unroll
             for (int j = 0; j < JA; ++j)
-                ca[j] = nv_convert8_bf16((uint32_t)h.a[j][t], scale_f32(h.sa[j], t, tab + 256));
+                ca[j] = nv_convert8_fp8((uint32_t)h.a[j][q % P][d], (uint32_t)h.a[j][q % P][d + 1],
+                                        scale_f32(h.sa[j], t, tab + 256));
+        } else if constexpr (BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8_bf16((uint32_t)h.w[i][0][t], scale_f32(h.sw[i], t, tab));
+#pragma unroll
+            for (int j = 0; j < JA; ++j)
+                ca[j] = nv_convert8_bf16((uint32_t)h.a[j][0][t], scale_f32(h.sa[j], t, tab + 256));
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][t], scale_of(h.sw[i], t, tab));
+            for (int i = 0; i < 4; ++i) cw[i] = nv_convert8((uint32_t)h.w[i][0][t], scale_of(h.sw[i], t, tab));
 #pragma unroll
-            for (int j = 0; j < JA; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][t], scale_of(h.sa[j], t, tab + 256));
+            for (int j = 0; j < JA; ++j) ca[j] = nv_convert8((uint32_t)h.a[j][0][t], scale_of(h.sa[j], t, tab + 256));
         }
     };
 
@@ -1273,7 +1314,7 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
 
     // four steps of one half: products of step t with the conversions of
     // step t + 1 (the last step converts step 0 of `next`, if any)
-    auto run_half = [&](const NvHalf<JA>& h, const NvHalf<JA>& next, bool has_next, V8 (&cw)[4], V8 (&ca)[JA]) {
+    auto run_half = [&](const NvHalf<JA, P>& h, const NvHalf<JA, P>& next, bool has_next, V8 (&cw)[4], V8 (&ca)[JA]) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             V8 nw[4], na[JA];
@@ -1291,7 +1332,7 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
             if (conv) {
                 // one matrix instruction, then its share of the next step's
                 // conversions ((4 + JA) fragments, 8 or 16 VALU each)
-                constexpr int kVpm = (4 + JA) * (BF16 ? 16 : 8) / (4 * JA);
+                constexpr int kVpm = (4 + JA) * (FP8 ? 4 : BF16 ? 16 : 8) / (4 * JA);
 #pragma unroll
                 for (int q = 0; q < 4 * JA; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1312,7 +1353,7 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
     for (int s = 0; s < NS; ++s) issue(s);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * kLoads) : "memory");
     __builtin_amdgcn_s_barrier();
-    NvHalf<JA> f, g;
+    NvHalf<JA, P> f, g;
     load_half(f, 0, 0);
     V8 cw[4], ca[JA];
     convert(f, 0, cw, ca);
@@ -1355,15 +1396,20 @@ static bool is_e4m3(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits == 4 &
 // accumulators in the AGPRs, one wave per SIMD), which convert each A
 // fragment for twice the products (measured: UE5M3 600 -> 743 TFLOP/s at
 // the Llama-2 7B up projection; the f16 forms gain nothing from it).
+// bf16 forms: four waves (one per SIMD); FP8 rows (128 bytes per stage)
+// leave room for two stages.
 template <int BLOCK, int CVT>
 static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 {
-    constexpr int WM = CVT == kNvBf16 ? 2 : 4;
-    constexpr size_t sh = (size_t)FP4_NV_NS * NvStage<BLOCK>::kBytes + NvStage<BLOCK>::kTable;
-    hipError_t e = allow_lds(k_gemm_nv<BLOCK, FP4_NV_NS, CVT, WM>, sh);
+    constexpr int WM = CVT == kNvBf16 || CVT == kNvFp8 ? 2 : 4;
+    constexpr int NS = CVT == kNvFp8 ? 2 : FP4_NV_NS;
+    using L = NvStage<BLOCK, CVT == kNvFp8 ? 128 : kMx3RB>;
+    constexpr size_t sh = (size_t)NS * L::kBytes + L::kTable;
+    static_assert(sh <= 160 * 1024, "LDS");
+    hipError_t e = allow_lds(k_gemm_nv<BLOCK, NS, CVT, WM>, sh);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)(((p.n + kTile - 1) / kTile) * ((p.m + kTile - 1) / kTile));
-    hipLaunchKernelGGL((k_gemm_nv<BLOCK, FP4_NV_NS, CVT, WM>), dim3(tiles), dim3(128 * WM), sh, s, p);
+    hipLaunchKernelGGL((k_gemm_nv<BLOCK, NS, CVT, WM>), dim3(tiles), dim3(128 * WM), sh, s, p);
     return hipGetLastError();
 }
 
@@ -1446,6 +1492,9 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     if (p.elem != 0) {
         const int t = dq_type(p.fa, p.fb, p.elem);
         if (t == 0) return hipErrorNotSupported;
+        // MXFP8: FP8 converted in registers with the E8M0 scale applied
+        if (p.elem == 2 && p.fa.is_e8m0 && p.fb.is_e8m0)
+            return p.block == 16 ? launch_nv<16, kNvFp8>(p, s) : launch_nv<32, kNvFp8>(p, s);
         if (p.elem == 1) return launch_dq_grid<1>(p, t == 2, s);
         if (p.elem == 2) return launch_dq_grid<2>(p, false, s);   // bf16 only
         if (p.elem == 3) return launch_dq_grid<3>(p, t == 2, s);
@@ -1518,7 +1567,6 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
 // fixed order (deterministic).
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Exact bf16 dequantization of one dword of 8 E2M1 codes with scale s.  The
 // gfx950 converts apply only the exponent of their scale operand, so:

@@ -325,6 +325,38 @@ def test_8bit_gemm_every_code(elem, fmt):
                            f"{got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}")
 
 
+def test_mxfp8_gemm_subnormal_products():
+    """MXFP8 with E8M0 scales 2^-127 .. 2^-116: every FP8 code times a scale
+    near the bottom of the range, so many products lie below bf16's normal
+    range.  W selects one column per output (as in the every-code test).
+    Products that bf16 holds exactly (its subnormals included) must come out
+    exactly; the others within one bf16 subnormal step (2^-133)."""
+    k = 256
+    codes = np.arange(256, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00
+    q_a = np.stack([codes, codes[::-1], np.roll(codes, 77), np.roll(codes, 150)])
+    rng = np.random.default_rng(31)
+    s_a = rng.integers(0, 12, (4, k // 32), dtype=np.uint8)
+    q_w = np.zeros((k, k), dtype=np.uint8)
+    q_w[np.arange(k), np.arange(k)] = 0x38
+    s_w = np.full((k, k // 32), 127, dtype=np.uint8)
+
+    def qt(q, s):
+        return fq.QTensor(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(),
+                          torch.tensor([1.0, 0.0], dtype=torch.float32).cuda(), q.shape[0], k, 32, "e8m0",
+                          amax="none", element="fp8_e4m3")
+    c = fq.fp4_gemm(qt(q_a, s_a), qt(q_w, s_w))
+    torch.cuda.synchronize()
+    a_hat = oracle.dequantize_f64(q_a, s_a, np.float32(1.0), 32, "e8m0", elem="fp8_e4m3")
+    got = c.float().cpu().numpy().astype(np.float64)
+    exact = oracle.round_to_bf16(a_hat) == a_hat
+    bad = np.argwhere(exact & (got != a_hat))
+    assert bad.size == 0, (f"{len(bad)} bf16-exact products differ; first {tuple(bad[0])}: got "
+                           f"{got[tuple(bad[0])]!r} want {a_hat[tuple(bad[0])]!r}")
+    far = np.argwhere(~exact & (np.abs(got - a_hat) > 2.0 ** -133))
+    assert far.size == 0, f"{len(far)} outputs beyond one bf16 subnormal step; first {tuple(far[0])}"
+
+
 @pytest.mark.parametrize("elem,fmt", [("fp8_e4m3", "e3m4"), ("fp8_e4m3", "e1m6"), ("int8", "ue5m3"),
                                       ("int8", "e3m4"), ("int8", "e5m2")])
 def test_8bit_gemm_inexact_pairing_rejected(elem, fmt):
