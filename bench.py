@@ -386,9 +386,9 @@ def leg_8bit(torch, fq, inputs, xs):
     """The 8- and 6-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
     elements), MXINT8-style (E8M0 block 32), one byte per element, and
     MXFP6 / MXINT6-style (six bits per element), and
-    the GEMM at the Llama-2 7B up-projection shape on the exact dequantize
-    path (MXFP8, MXFP6 and MXINT6 in bf16; INT8 elements with E4M3 block-16
-    scales in f16)."""
+    the GEMM at the Llama-2 7B up-projection shape: MXFP8 on the in-register
+    conversion kernel (bf16), MXFP6 and MXINT6 (bf16) and INT8 elements with
+    E4M3 block-16 scales (f16) on the exact dequantize path."""
     rows, cols = xs[0].shape
     res = {}
     n = rows * cols
@@ -457,8 +457,8 @@ def leg_8bit(torch, fq, inputs, xs):
     res["workload"] = ("4096x4096 bf16 sweep tensor, E8M0 block 32, FP8 E4M3 / INT8 elements (1 byte each) and "
                        "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise, column-wise and "
                        "both orientations (MXFP8, MXINT6); "
-                       "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8, INT8 with E4M3 block-16 scales, "
-                       "MXFP6 (E2M3) and MXINT6")
+                       "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8 (in-register FP8 -> bf16), INT8 with "
+                       "E4M3 block-16 scales, MXFP6 (E2M3) and MXINT6 (exact dequantize path)")
     return res
 
 

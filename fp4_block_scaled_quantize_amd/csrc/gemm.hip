@@ -21,11 +21,13 @@
 //  * k_gemm_nv: scale formats whose e2m1 * s products are exact in f16
 //    (E4M3 -- NVFP4 --, E3M4, E2M5, E1M6) or, with more exponent bits
 //    (UE5M3, E5M2, E6M1, E7M0), in bf16: each wave converts its fragments in
-//    registers right before the f16 / bf16 32x32x16 matrix instruction.
+//    registers right before the f16 / bf16 32x32x16 matrix instruction; the
+//    same kernel takes MXFP8 (FP8 elements, E8M0 scales) to bf16.
 //  * k_gemm_dq: the remaining pairs (E8M0 with a non-power-of-two format)
-//    and the INT4, 8- and 6-bit grids: FP4 / integer / FP8 / FP6 tiles are
-//    dequantized exactly to f16 or bf16 in LDS.
-//  * k_wo_gemm: the weight-only GEMM (bf16 X times FP4 W, M <= 16).
+//    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
+//    tiles are dequantized exactly to f16 or bf16 in LDS.
+//  * k_wo_gemm: the weight-only GEMM (bf16 X times W on any element grid,
+//    M <= 16).
 #include <type_traits>
 
 #include "fp4_device.hpp"
