@@ -386,9 +386,9 @@ def leg_8bit(torch, fq, inputs, xs):
     """The 8- and 6-bit MX grids: the sweep tensor quantized MXFP8-style (E4M3
     elements), MXINT8-style (E8M0 block 32), one byte per element, and
     MXFP6 / MXINT6-style (six bits per element), and
-    the GEMM at the Llama-2 7B up-projection shape: MXFP8 on the in-register
-    conversion kernel (bf16), MXFP6 and MXINT6 (bf16) and INT8 elements with
-    E4M3 block-16 scales (f16) on the exact dequantize path."""
+    the GEMM at the Llama-2 7B up-projection shape: MXFP8 (bf16) and INT8
+    elements with E4M3 block-16 scales (f16) on the in-register conversion
+    kernel, MXFP6 and MXINT6 (bf16) on the exact dequantize path."""
     rows, cols = xs[0].shape
     res = {}
     n = rows * cols
@@ -458,7 +458,8 @@ def leg_8bit(torch, fq, inputs, xs):
                        "FP6 E2M3 / FP6 E3M2 / INT6 elements (6 bits each), RTN, row-wise, column-wise and "
                        "both orientations (MXFP8, MXINT6); "
                        "Llama-2 7B up projection 8192x4096 @ 11008x4096, MXFP8 (in-register FP8 -> bf16), INT8 with "
-                       "E4M3 block-16 scales, MXFP6 (E2M3) and MXINT6 (exact dequantize path)")
+                       "E4M3 block-16 scales (in-register INT8 -> f16), MXFP6 (E2M3) and MXINT6 (exact dequantize "
+                       "path)")
     return res
 
 

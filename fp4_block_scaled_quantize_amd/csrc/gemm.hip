@@ -22,7 +22,8 @@
 //    (E4M3 -- NVFP4 --, E3M4, E2M5, E1M6) or, with more exponent bits
 //    (UE5M3, E5M2, E6M1, E7M0), in bf16: each wave converts its fragments in
 //    registers right before the f16 / bf16 32x32x16 matrix instruction; the
-//    same kernel takes MXFP8 (FP8 elements, E8M0 scales) to bf16.
+//    same kernel takes MXFP8 (FP8 elements, E8M0 scales) to bf16 and INT8
+//    with E4M3 scales to f16.
 //  * k_gemm_dq: the remaining pairs (E8M0 with a non-power-of-two format)
 //    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
 //    tiles are dequantized exactly to f16 or bf16 in LDS.
@@ -1095,7 +1096,12 @@ struct NvStage {
 //    one scaled FP8 -> bf16 conversion per element pair applies the
 //    power-of-two scale exactly (4 significant bits fit bf16), bf16 matrix
 //    instruction.  Rows are 128 code bytes per stage.
-enum { kNvTable = 0, kNvE4M3 = 1, kNvBf16 = 2, kNvFp8 = 3 };
+//  kNvInt8: INT8 elements with E4M3 scales on both operands (NVINT8-style),
+//    f16: each byte in offset binary under the f16 exponent byte 0x64 is
+//    1024 + (e + 128) exactly, one packed subtraction of 1152 leaves e, one
+//    packed multiply by the E4M3 scale (at most 7 + 4 significant bits and
+//    127 * 448 < 65504: exact).  Rows as kNvFp8.
+enum { kNvTable = 0, kNvE4M3 = 1, kNvBf16 = 2, kNvFp8 = 3, kNvInt8 = 4 };
 
 // 8 E2M1 codes (one dword, element 2b in the low nibble of byte b) times
 // the f16 block scale s2 (replicated in both halves).
@@ -1135,6 +1141,20 @@ __device__ __forceinline__ v8bf nv_convert8_fp8(uint32_t d0, uint32_t d1, float 
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// 8 INT8 codes (two dwords, element 4 d + b in byte b of dword d) times the
+// f16 scale s2 (replicated), as f16 (kNvInt8; exact).
+__device__ __forceinline__ v8h nv_convert8_int8(uint32_t d0, uint32_t d1, v2h s2)
+{
+    const uint32_t x0 = d0 ^ 0x80808080u, x1 = d1 ^ 0x80808080u;      // offset binary
+    const v2h k = {(_Float16)1152.0f, (_Float16)1152.0f};
+    // bytes {x.b, 0x64} as f16: 1024 + x.b
+    const v2h h0 = (__builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - k) * s2;
+    const v2h h1 = (__builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - k) * s2;
+    const v2h h2 = (__builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) - k) * s2;
+    const v2h h3 = (__builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) - k) * s2;
+    return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
 // Fragments of one half stage (chunk pair ks) for one lane: four W and JA
 // A code fragments of P 16-byte pieces (32 E2M1 or FP8 elements) and their
 // raw scale bytes (block 16: the two scales of the chunk in one u16; block
@@ -1155,15 +1175,16 @@ struct NvHalf {
 template <int BLOCK, int NS, int CVT, int WM>
 __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
 {
-    constexpr bool FP8 = CVT == kNvFp8;
-    using L = NvStage<BLOCK, FP8 ? 128 : kMx3RB>;
+    constexpr bool FP8 = CVT == kNvFp8, INT8 = CVT == kNvInt8;
+    constexpr bool W8 = FP8 || INT8;            // one byte per element
+    using L = NvStage<BLOCK, W8 ? 128 : kMx3RB>;
     constexpr int RB = L::kRB;                  // code bytes per row per stage
     constexpr int P = RB / 64;                  // 16-byte pieces per lane fragment
     constexpr int CPR = RB / 16;                // 16-byte chunks per row
     constexpr int NWV = 2 * WM;                 // waves: 2 along n (128 rows of W each) x WM along m
     constexpr int JA = 8 / WM;                  // 32-row A fragments per wave (its 32 JA rows of A)
     constexpr int CK = kTile * CPR / 64 / NWV;  // 16-byte code DMAs per lane per operand and stage
-    constexpr bool HW_E4M3 = CVT == kNvE4M3, BF16 = CVT == kNvBf16 || FP8;
+    constexpr bool HW_E4M3 = CVT == kNvE4M3 || INT8, BF16 = CVT == kNvBf16 || FP8;
     using V8 = std::conditional_t<BF16, v8bf, v8h>;
     static_assert(NS >= 2, "at least two stages");
     extern __shared__ __align__(16) uint8_t smem[];
@@ -1174,10 +1195,10 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
     int tn, tm;
     tile_coords((int)((N + kTile - 1) / kTile), (int)((M + kTile - 1) / kTile), &tn, &tm);
     const int64_t n_base = (int64_t)tn * kTile, m_base = (int64_t)tm * kTile;
-    const int64_t rowb = FP8 ? K : K / 2, rows = K / BLOCK;
+    const int64_t rowb = W8 ? K : K / 2, rows = K / BLOCK;
     const int KT = (int)(K / kMx3BK);
     // 16-byte chunk c of row r sits at c ^ swz(r) (64- or 128-byte rows)
-    auto swz = [&](int r) { return FP8 ? mx_swz<256>(r) : mx_swz<128>(r); };
+    auto swz = [&](int r) { return W8 ? mx_swz<256>(r) : mx_swz<128>(r); };
 
     // scale code -> f16 (exact for these formats), replicated for packed
     // math; or -> fp32 for the bf16 form, which (as the dequantize path)
@@ -1284,7 +1305,17 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
         return __uint_as_float(tb[b]);
     };
     auto convert = [&](const NvHalf<JA, P>& h, int t, V8 (&cw)[4], V8 (&ca)[JA]) {
-        if constexpr (FP8) {
+        if constexpr (INT8) {
+            // elements 8 t .. 8 t + 7: dwords 2 t, 2 t + 1 of the 32 bytes
+            const int q = (2 * t) >> 2, d = (2 * t) & 3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cw[i] = nv_convert8_int8((uint32_t)h.w[i][q % P][d], (uint32_t)h.w[i][q % P][d + 1], scale_of(h.sw[i], t, tab));
+#pragma unroll
+            for (int j = 0; j < JA; ++j)
+                ca[j] = nv_convert8_int8((uint32_t)h.a[j][q % P][d], (uint32_t)h.a[j][q % P][d + 1],
+                                         scale_of(h.sa[j], t, tab + 256));
+        } else if constexpr (FP8) {
             // elements 8 t .. 8 t + 7: dwords 2 t, 2 t + 1 of the 32 bytes
             const int q = (2 * t) >> 2, d = (2 * t) & 3;
 #pragma unroll
@@ -1334,7 +1365,7 @@ __global__ __launch_bounds__(128 * WM) void k_gemm_nv(GemmLaunch p)
             if (conv) {
                 // one matrix instruction, then its share of the next step's
                 // conversions ((4 + JA) fragments, 8 or 16 VALU each)
-                constexpr int kVpm = (4 + JA) * (FP8 ? 4 : BF16 ? 16 : 8) / (4 * JA);
+                constexpr int kVpm = (4 + JA) * (FP8 ? 4 : INT8 ? 14 : BF16 ? 16 : 8) / (4 * JA);
 #pragma unroll
                 for (int q = 0; q < 4 * JA; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1398,14 +1429,15 @@ static bool is_e4m3(const ScaleFmtHost& f) { return !f.is_e8m0 && f.ebits == 4 &
 // accumulators in the AGPRs, one wave per SIMD), which convert each A
 // fragment for twice the products (measured: UE5M3 600 -> 743 TFLOP/s at
 // the Llama-2 7B up projection; the f16 forms gain nothing from it).
-// bf16 forms: four waves (one per SIMD); FP8 rows (128 bytes per stage)
-// leave room for two stages.
+// bf16 and 8-bit forms: four waves (one per SIMD); 8-bit rows (128 bytes
+// per stage) leave room for two stages.
 template <int BLOCK, int CVT>
 static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 {
-    constexpr int WM = CVT == kNvBf16 || CVT == kNvFp8 ? 2 : 4;
-    constexpr int NS = CVT == kNvFp8 ? 2 : FP4_NV_NS;
-    using L = NvStage<BLOCK, CVT == kNvFp8 ? 128 : kMx3RB>;
+    constexpr bool W8 = CVT == kNvFp8 || CVT == kNvInt8;
+    constexpr int WM = CVT == kNvBf16 || W8 ? 2 : 4;
+    constexpr int NS = W8 ? 2 : FP4_NV_NS;
+    using L = NvStage<BLOCK, W8 ? 128 : kMx3RB>;
     constexpr size_t sh = (size_t)NS * L::kBytes + L::kTable;
     static_assert(sh <= 160 * 1024, "LDS");
     hipError_t e = allow_lds(k_gemm_nv<BLOCK, NS, CVT, WM>, sh);
@@ -1494,9 +1526,12 @@ hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s)
     if (p.elem != 0) {
         const int t = dq_type(p.fa, p.fb, p.elem);
         if (t == 0) return hipErrorNotSupported;
-        // MXFP8: FP8 converted in registers with the E8M0 scale applied
+        // MXFP8: FP8 converted in registers with the E8M0 scale applied;
+        // INT8 with E4M3 scales: converted in registers to f16
         if (p.elem == 2 && p.fa.is_e8m0 && p.fb.is_e8m0)
             return p.block == 16 ? launch_nv<16, kNvFp8>(p, s) : launch_nv<32, kNvFp8>(p, s);
+        if (p.elem == 3 && is_e4m3(p.fa) && is_e4m3(p.fb))
+            return p.block == 16 ? launch_nv<16, kNvInt8>(p, s) : launch_nv<32, kNvInt8>(p, s);
         if (p.elem == 1) return launch_dq_grid<1>(p, t == 2, s);
         if (p.elem == 2) return launch_dq_grid<2>(p, false, s);   // bf16 only
         if (p.elem == 3) return launch_dq_grid<3>(p, t == 2, s);
