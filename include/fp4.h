@@ -329,19 +329,22 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * quant_prune_distill/574 "Выводы": weight + activation FP4 for the
  * compute-bound regime).  Both operands must use the same block size, the
  * same element grid and the same transform (kind and signs; UNSUPPORTED
- * otherwise).  INT4 operands run on the exact dequantize path (bf16 when
- * int * s fits it exactly for both scale formats, else f16); so do the
- * 8-bit grids: FP8 E4M3 elements in bf16 for scale formats with at most 3
- * mantissa bits (E8M0, E7M0, E6M1, E5M2, E4M3, UE5M3), INT8 elements in
- * bf16 for power-of-two scales (E8M0, E7M0) and in f16 for E4M3 scales;
- * and the 6-bit grids: FP6 E2M3 as FP8, FP6 E3M2 in bf16 for scales with
- * at most 4 mantissa bits, INT6 in bf16 for at most 2 (E8M0, E7M0, E6M1,
- * E5M2) and in f16 for E4M3 / E3M4 / E2M5; other 8- and 6-bit pairings
- * return UNSUPPORTED.
- * Both E8M0 at block 32 run on the gfx950 block-scaled FP4 matrix core
- * instruction; every other format is dequantized exactly to bf16/f16 in
- * LDS and runs on the bf16/f16 matrix cores.  Result within
- * 1e-5 * sum_k |a||b| of the exact product before the bf16 rounding.
+ * otherwise).  Every element times its block scale enters a matrix
+ * instruction exactly, in a 16-bit type chosen per pairing: INT4 in bf16
+ * when int * s fits it exactly for both scale formats, else f16; FP8 E4M3
+ * elements in bf16 for scale formats with at most 3 mantissa bits (E8M0,
+ * E7M0, E6M1, E5M2, E4M3, UE5M3); INT8 in bf16 for power-of-two scales
+ * (E8M0, E7M0) and in f16 for E4M3 scales; FP6 E2M3 as FP8, FP6 E3M2 in
+ * bf16 for scales with at most 4 mantissa bits, INT6 in bf16 for at most 2
+ * (E8M0, E7M0, E6M1, E5M2) and in f16 for E4M3 / E3M4 / E2M5; other 8- and
+ * 6-bit pairings return UNSUPPORTED.
+ * Paths: E2M1 with E8M0 scales on both operands (block 32 or 16) runs on
+ * the gfx950 block-scaled FP4 matrix instruction; E2M1 with the formats
+ * exact in f16 (E4M3, E3M4, E2M5, E1M6) or in bf16 (UE5M3, E5M2, E6M1,
+ * E7M0), MXFP8 (FP8 with E8M0 on both) and INT8 with E4M3 on both are
+ * converted to f16 / bf16 in registers; every other pairing is dequantized
+ * to bf16 / f16 in LDS.  Result within 1e-5 * sum_k |a||b| of the exact
+ * product before the bf16 rounding.
  * K % 128 == 0 (K = 0 writes C = 0 and reads no operand), M and N
  * arbitrary; ldc >= N; c 2-byte aligned (rows that
  * are 8-byte aligned are written with vector stores); operand codes 16-byte
