@@ -338,8 +338,9 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * bf16 for scales with at most 4 mantissa bits, INT6 in bf16 for at most 2
  * (E8M0, E7M0, E6M1, E5M2) and in f16 for E4M3 / E3M4 / E2M5; other 8- and
  * 6-bit pairings return UNSUPPORTED.
- * Paths: E2M1 with E8M0 scales on both operands (block 32 or 16) runs on
- * the gfx950 block-scaled FP4 matrix instruction; E2M1 with the formats
+ * Paths: E2M1 with E8M0 scales on both operands runs on the gfx950
+ * block-scaled FP4 matrix instruction (at block 16 when K % 256 == 0 and
+ * each operand's codes are below 4 GiB; else in LDS); E2M1 with the formats
  * exact in f16 (E4M3, E3M4, E2M5, E1M6) or in bf16 (UE5M3, E5M2, E6M1,
  * E7M0), MXFP8 (FP8 with E8M0 on both) and INT8 with E4M3 on both are
  * converted to f16 / bf16 in registers; every other pairing is dequantized
