@@ -79,10 +79,10 @@ WIDE = ["fp8_e4m3", "int8", "fp6_e2m3", "fp6_e3m2", "int6"]
 
 def test_graph_replay_wide_grids_gemm_and_dequantize():
     """The 8- and 6-bit grids in one captured graph: single-pass current-amax
-    quantize calls (the grid exchange's epoch advances on every replay), a
-    GEMM of two MXFP8 operands quantized in the same graph, and a dequantize
-    of an MXFP6 tensor; each replay with new input values agrees with the
-    oracle."""
+    quantize calls (the grid exchange's epoch advances on every replay),
+    GEMMs of two MXFP8 operands and of two INT8 operands with E4M3 block-16
+    scales quantized in the same graph, and a dequantize of an MXFP6 tensor;
+    each replay with new input values agrees with the oracle."""
     R, C, N = 96, 256, 72
     x = torch.zeros((R, C), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((N, C), dtype=torch.bfloat16, device="cuda")
@@ -91,7 +91,11 @@ def test_graph_replay_wide_grids_gemm_and_dequantize():
     qa = fq.QTensor.empty(R, C, 32, "e8m0", amax="none", element="fp8_e4m3")
     qw = fq.QTensor.empty(N, C, 32, "e8m0", amax="none", element="fp8_e4m3")
     q6 = fq.QTensor.empty(R, C, 32, "e8m0", amax="none", element="fp6_e3m2")
+    st_a8, st_w8 = fq.AmaxState(1), fq.AmaxState(1)
+    qa8 = fq.QTensor.empty(R, C, 16, "e4m3", element="int8")
+    qw8 = fq.QTensor.empty(N, C, 16, "e4m3", element="int8")
     c = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    c8 = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((R, C), dtype=torch.float32, device="cuda")
 
     def record():
@@ -100,6 +104,9 @@ def test_graph_replay_wide_grids_gemm_and_dequantize():
         fq.fp4_quantize(x, 32, "e8m0", amax="none", out=qa, element="fp8_e4m3")
         fq.fp4_quantize(w, 32, "e8m0", amax="none", out=qw, element="fp8_e4m3")
         fq.fp4_gemm(qa, qw, out=c)
+        fq.fp4_quantize(x, 16, "e4m3", state=st_a8, out=qa8, element="int8")
+        fq.fp4_quantize(w, 16, "e4m3", state=st_w8, out=qw8, element="int8")
+        fq.fp4_gemm(qa8, qw8, out=c8)
         fq.fp4_quantize(x, 32, "e8m0", amax="none", out=q6, element="fp6_e3m2")
         fq.fp4_dequantize(q6, torch.float32, out=y)
     side = torch.cuda.Stream()
@@ -132,6 +139,15 @@ def test_graph_replay_wide_grids_gemm_and_dequantize():
         cref, tol = oracle.gemm_ref(a_hat, w_hat)
         ok = oracle.gemm_check(c.float().cpu().numpy().astype(np.float64), cref, tol)
         assert ok.all(), f"replay {rep} gemm: {int((~ok).sum())} outputs out of tolerance"
+        oa = oracle.quantize_tensor(hx, 16, "e4m3", "current", elem="int8")
+        ow = oracle.quantize_tensor(hw, 16, "e4m3", "current", elem="int8")
+        assert_bytes_equal(host(qa8.q), oa[0], f"replay {rep} int8 a codes")
+        assert_bytes_equal(host(qw8.q), ow[0], f"replay {rep} int8 w codes")
+        a_hat = oracle.dequantize_f64(oa[0], oa[1], oa[2], 16, "e4m3", elem="int8")
+        w_hat = oracle.dequantize_f64(ow[0], ow[1], ow[2], 16, "e4m3", elem="int8")
+        cref, tol = oracle.gemm_ref(a_hat, w_hat)
+        ok = oracle.gemm_check(c8.float().cpu().numpy().astype(np.float64), cref, tol)
+        assert ok.all(), f"replay {rep} int8 gemm: {int((~ok).sum())} outputs out of tolerance"
         q, s, g, _ = oracle.quantize_tensor(hx, 32, "e8m0", "none", elem="fp6_e3m2")
         want = oracle.dequantize(q, s, float(g), 32, "e8m0", out="f32", elem="fp6_e3m2")
         assert_bytes_equal(f32_bits(host(y)), f32_bits(want), f"replay {rep} fp6 dequant")
