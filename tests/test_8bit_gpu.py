@@ -252,6 +252,20 @@ def test_8bit_gemm(elem, fmt, block):
     _gemm_check(c, a, w, tag=f"{elem} {fmt}/{block} gemm")
 
 
+@pytest.mark.parametrize("elem,fmt,block", [("fp8_e4m3", "e8m0", 32), ("fp8_e4m3", "e8m0", 16), ("int8", "e4m3", 16),
+                                            ("int8", "e4m3", 32)])
+@pytest.mark.parametrize("m,n,k", [(1, 33, 128), (257, 513, 384), (64, 256, 1152)])
+def test_8bit_gemm_register_path_shapes(elem, fmt, block, m, n, k):
+    """The pairings converted in registers (MXFP8; INT8 with E4M3 scales):
+    one 128-element stage, odd stage counts past the two-stage ring, ragged
+    M and N, a single output row."""
+    qa, a = _quant_pair(_like(m, k, 91 + k, "f32"), block, fmt, elem)
+    qw, w = _quant_pair(_like(n, k, 92 + k, "f32"), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qw)
+    torch.cuda.synchronize()
+    _gemm_check(c, a, w, tag=f"{elem} {fmt}/{block} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("elem", ELEMS)
 def test_8bit_gemm_transform_and_sr(elem):
     """Both operands Hadamard-rotated with the same signs (the product is
