@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="sr,srt,dequant,rht,int4,w8,gemm,wo,wowide",
+    p.add_argument("--legs", default="c1,sr,srt,dequant,rht,int4,w8,gemm,wo,wowide",
                    help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
@@ -280,6 +280,32 @@ def leg_rht(torch, fq, xs):
                 "us_per_call": round(ms * 1e3, 3), "GB/s": round(algo / (ms * 1e-3) / 1e9, 1)}
             del gs, outs
     res["workload"] = "4096x4096 bf16 sweep tensor, RTN, with / without the block-16/32 randomized Hadamard transform"
+    return res
+
+
+def leg_c1(torch, fq, inputs):
+    """The small correctness configuration, timed: B 256x256 fp32 (1% of
+    entries x50) and A 64x256 fp32 quantized NVFP4 (E4M3 block 16, current
+    amax, RTN), then C = A B^T; per-call latency between graph replays
+    (launch-bound at this size)."""
+    b = torch.from_numpy(inputs.small_b()).cuda()
+    a = torch.from_numpy(inputs.small_a()).cuda()
+    st_b, st_a = fq.AmaxState(1), fq.AmaxState(1)
+    qb = fq.QTensor.empty(256, 256, 16, "e4m3")
+    qa = fq.QTensor.empty(64, 256, 16, "e4m3")
+    c = torch.empty((64, 256), dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, fn in {"quantize_b_us": lambda: fq.fp4_quantize(b, 16, "e4m3", state=st_b, out=qb),
+                     "quantize_a_us": lambda: fq.fp4_quantize(a, 16, "e4m3", state=st_a, out=qa),
+                     "gemm_us": lambda: fq.fp4_gemm(qa, qb, out=c)}.items():
+        def rec(_, fn=fn):
+            for _ in range(10):
+                fn()
+        gs = GraphSet(torch, 1, rec)
+        res[name] = round(time_graphs(torch, gs, 20, 3) / 10 * 1e3, 3)
+        del gs
+    res["workload"] = ("256x256 fp32 B and 64x256 fp32 A, NVFP4 (E4M3 B16, current amax, RTN); C = A B^T "
+                       "(8.39 MFLOP); microseconds per call, ten calls per graph replay")
     return res
 
 
@@ -545,6 +571,7 @@ def cpu_baseline(min_seconds=10.0, one_thread_seconds=4.0):
     until at least min_seconds have passed on min(16, usable cores) threads;
     then one thread on single E4M3 calls for about one_thread_seconds.  Same
     bytes accounting as the GPU step."""
+    import numpy as np
     import oracle
     import fp4_inputs as inputs
     x = inputs.sweep()
@@ -569,11 +596,26 @@ def cpu_baseline(min_seconds=10.0, one_thread_seconds=4.0):
         dt1 = time.perf_counter() - t1
         if dt1 >= one_thread_seconds:
             break
+    # the GEMM reference: both operands dequantized exactly in binary64, the
+    # product and the tolerance matrix |A||W|^T (numpy's BLAS threads)
+    ga = inputs.normal((1024, 4096), 0.02, inputs.SEEDS["llama_a"]).astype(np.float32)
+    gw = inputs.normal((1024, 4096), 0.02, inputs.SEEDS["llama_up"]).astype(np.float32)
+    t2 = time.perf_counter()
+    qa_, sa_, g_a, _ = oracle.quantize_tensor(ga, 16, "e4m3", "current", nthreads=threads)
+    qw_, sw_, g_w, _ = oracle.quantize_tensor(gw, 16, "e4m3", "current", nthreads=threads)
+    a_hat = oracle.dequantize_f64(qa_, sa_, g_a, 16, "e4m3")
+    w_hat = oracle.dequantize_f64(qw_, sw_, g_w, 16, "e4m3")
+    oracle.gemm_ref(a_hat, w_hat)
+    dt2 = time.perf_counter() - t2
+    gflop = 2.0 * 1024 * 1024 * 4096 / 1e9
     return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} full sweep steps (4096x4096 bf16, 5 formats) in {dt:.1f} s",
             "host_cores_usable": usable, "host_cores_total": os.cpu_count(), "cpu_model": _cpu_model(),
             "one_thread": {"value": round(calls * quant_bytes(rows, cols, 16) / dt1 / 1e9, 4), "unit": "GB/s",
-                           "sample": f"{calls} E4M3 block-16 calls on the sweep tensor in {dt1:.1f} s"}}
+                           "sample": f"{calls} E4M3 block-16 calls on the sweep tensor in {dt1:.1f} s"},
+            "gemm_oracle": {"value": round(gflop / dt2, 3), "unit": "GFLOP/s",
+                            "sample": f"NVFP4 1024x4096 @ (1024x4096)^T: quantize, binary64 dequantize, product "
+                                      f"and |A||W|^T tolerance in {dt2:.2f} s ({gflop:.1f} GFLOP of the product)"}}
 
 
 def main():
@@ -634,6 +676,8 @@ def main():
         del src, dst
     legs = {}
     want = [] if args.legs == "none" else args.legs.split(",")
+    if "c1" in want:
+        legs["c1_small"] = leg_c1(torch, fq, inputs)
     if "dequant" in want:
         legs["dequant"] = leg_dequant(torch, fq, xs[:8])
     if "rht" in want:
