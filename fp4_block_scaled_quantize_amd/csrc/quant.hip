@@ -300,7 +300,8 @@ __device__ __forceinline__ uint32_t launch_epoch(uint32_t word)
 }
 
 // Publishes m and polls; returns true with *gm = the maximum over every
-// workgroup, or false when the wait bound passed first.
+// workgroup, or false when the wait bound passed first.  A grid of one
+// workgroup has the maximum at hand and publishes nothing.
 template <int T>
 __device__ bool grid_exchange(uint32_t m, uint32_t e, AmaxDev* st, uint64_t wait_ticks, uint32_t* gm)
 {
@@ -310,12 +311,21 @@ __device__ bool grid_exchange(uint32_t m, uint32_t e, AmaxDev* st, uint64_t wait
     m = wave_umax(m);
     if (lane == 0) wmax[wv] = m;
     __syncthreads();
-    if (wv == 0) {
+    const uint32_t nwg = gridDim.x;
+    if (wv == 0 && nwg == 1) {
+        // the whole tensor is in this workgroup: its maximum is the tensor's,
+        // and no slot is written (every slot keeps the epoch of the last
+        // exchange, which is what the next one derives its epoch from)
+        const uint32_t mm = wave_umax(lane < T / 64 ? wmax[lane] : 0u);
+        if (lane == 0) {
+            gmax = mm;
+            gok = 1u;
+        }
+    } else if (wv == 0) {
         const uint32_t mm = wave_umax(lane < T / 64 ? wmax[lane] : 0u);
         if (lane == 0)
             __hip_atomic_store(&st->slot[blockIdx.x * kXchgStride], ((uint64_t)e << 32) | mm, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t nwg = gridDim.x;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         uint32_t tm = 0;
         bool done = false;
@@ -748,11 +758,12 @@ hipError_t launch_quantize(const QuantLaunch& p, hipStream_t s)
         blocks = (a.nunits + per_wg - 1) / per_wg;
         if (blocks == 0) blocks = 1;
         fused = blocks <= max_wg;
-        // every single-pass launch on the device runs the same grid (each
+        // every single-pass launch that exchanges runs the same grid (each
         // workgroup derives the launch's epoch from its own slot, so every
-        // slot must be published by every launch); workgroups past the
-        // tensor publish a zero maximum and store nothing
-        if (fused) blocks = max_wg;
+        // slot must be published by every such launch); workgroups past the
+        // tensor publish a zero maximum and store nothing.  A tensor that
+        // fits one workgroup runs alone and exchanges nothing.
+        if (fused && blocks > 1) blocks = max_wg;
         if (!fused) {
             hipError_t e = launch_amax(p.x, p.x_bf16, p.rows, p.cols, p.ld, p.amax_src, s, rot ? p.block : 0,
                                        p.rht_signs);

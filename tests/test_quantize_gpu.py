@@ -196,10 +196,10 @@ def test_refresh_paths_see_the_whole_tensor():
 
 
 def test_current_repeated_calls_one_state():
-    """Many current-amax calls through one state, with grids of different
-    sizes in turn (1, 3 and 64 workgroups of the single-pass kernel): every
-    call's tensor scale comes from its own tensor, never from a slot left by
-    an earlier call."""
+    """Many current-amax calls through one state, single-workgroup launches
+    (16 x 256, 8 x 64: no exchange, no slot written) in turn with exchanging
+    ones (512 x 384, 2048 x 2048): every call's tensor scale comes from its
+    own tensor, never from a slot left by an earlier call."""
     st = fq.AmaxState(1)
     shapes = [(16, 256), (512, 384), (2048, 2048), (8, 64)]
     for t in range(40):
