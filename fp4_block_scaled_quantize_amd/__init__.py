@@ -71,6 +71,7 @@ def lib():
         "fp4_amax_state_set": (i32, [vp, u64, ctypes.c_float]),
         "fp4_amax_state_fallbacks": (i32, [vp, ctypes.POINTER(u32)]),
         "fp4_set_exchange_wait": (i32, [u64, ctypes.POINTER(u64)]),
+        "fp4_set_gemm_small_outputs": (i32, [i64, ctypes.POINTER(i64)]),
         "fp4_quantize": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
         "fp4_quantize_noalloc": (i32, [vp, i32, i64, T, u64, u64, vp]),
         "fp4_quantize_transposed": (i32, [vp, i32, i64, T, vp, u64, u64, vp]),
@@ -219,6 +220,15 @@ def set_exchange_wait(ticks: int) -> int:
     previous bound."""
     prev = ctypes.c_uint64()
     _check(lib().fp4_set_exchange_wait(ticks, ctypes.byref(prev)), "fp4_set_exchange_wait")
+    return prev.value
+
+
+def set_gemm_small_outputs(outputs: int) -> int:
+    """Set the process-wide bound on M * N up to which fp4_gemm takes the
+    one-wave-per-32x32-tile path for the pairings it covers (E8M0 operands:
+    an eighth of it; 0 turns the path off); returns the previous bound."""
+    prev = ctypes.c_int64()
+    _check(lib().fp4_set_gemm_small_outputs(outputs, ctypes.byref(prev)), "fp4_set_gemm_small_outputs")
     return prev.value
 
 
@@ -414,4 +424,4 @@ def fp4_wo_gemm(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None, st
 
 __all__ = ["fp4_quantize", "fp4_quantize_transposed", "fp4_quantize_both", "fp4_dequantize", "fp4_gemm",
            "fp4_wo_gemm", "AmaxState", "QTensor", "Fp4Error", "SCALE_FORMATS", "lib", "status_string", "LIB_PATH",
-           "set_exchange_wait", "fp4_quantize_noalloc"]
+           "set_exchange_wait", "set_gemm_small_outputs", "fp4_quantize_noalloc"]

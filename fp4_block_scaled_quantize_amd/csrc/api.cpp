@@ -61,7 +61,7 @@ struct fp4_amax_state {
 
 extern "C" {
 
-int32_t fp4_version(void) { return 106; }
+int32_t fp4_version(void) { return 107; }
 
 const char* fp4_status_string(fp4_status st)
 {
@@ -125,6 +125,14 @@ fp4_status fp4_amax_state_fallbacks(const fp4_amax_state* st, uint32_t* n)
 fp4_status fp4_set_exchange_wait(uint64_t ticks, uint64_t* previous)
 {
     const uint64_t old = __atomic_exchange_n(&g_exchange_wait_ticks, ticks, __ATOMIC_RELAXED);
+    if (previous) *previous = old;
+    return FP4_OK;
+}
+
+fp4_status fp4_set_gemm_small_outputs(int64_t outputs, int64_t* previous)
+{
+    if (outputs < 0) return FP4_ERR_INVALID_ARG;
+    const int64_t old = __atomic_exchange_n(&g_gemm_small_outputs, outputs, __ATOMIC_RELAXED);
     if (previous) *previous = old;
     return FP4_OK;
 }
@@ -456,6 +464,7 @@ fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* c, int64
     p.c = c; p.ldc = ldc;
     p.elem = a->fmt.element;
     hipStream_t s = (hipStream_t)stream;
+    if (gemm_small_supported(p)) return hip_status(launch_gemm_small(p, s));
     if (p.elem == FP4_ELEM_E2M1 && fa.is_e8m0 && fb.is_e8m0 && p.block == 32) return hip_status(launch_gemm_mx(p, s));
     if (gemm_mx16_supported(p)) return hip_status(launch_gemm_mx16(p, s));
     if (!gemm_dq_supported(fa, fb, p.elem)) return FP4_ERR_UNSUPPORTED;

@@ -1447,6 +1447,153 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Small products (few 256 x 256 tiles, so the tiled kernels would leave most
+// CUs idle or multiply mostly padding): one wave per 32 x 32 output tile,
+// four waves per workgroup along n, operands straight from global memory
+// into registers, no LDS and no barrier.  Lane l takes row l % 32 of each
+// operand and, of every 64-element chunk, the 16 bytes (32 E2M1 codes) of
+// K-half l / 32: exactly one lane fragment of the scaled FP4 instruction
+// (MXFP4, with the lane's own E8M0 byte), or four 8-element fragments of
+// the f16 instruction after the in-register conversion of the f16-exact
+// forms (the K order inside a chunk permuted identically for both operands,
+// which leaves every dot product unchanged).  Eight chunks are in flight
+// per lane.
+// MODE: 0 E2M1 with E4M3 scales (hardware scale decode), 1 other f16-exact
+// scale formats (decoded in registers), 2 MXFP4.
+// ---------------------------------------------------------------------------
+constexpr int kSmallWaves = 4;
+constexpr int kSmallAhead = 8;
+int64_t g_gemm_small_outputs = (int64_t)1 << 21;
+
+template <int MODE, int BLOCK>
+__global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
+{
+    static_assert(MODE != 2 || BLOCK == 32, "MXFP4 scales cover 32 elements");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n0 = ((int64_t)blockIdx.x * kSmallWaves + wave) * 32, m0 = (int64_t)blockIdx.y * 32;
+    if (n0 >= p.n) return;                    // whole waves only; no barrier follows
+    const int r = lane & 31, h = lane >> 5;
+    const int64_t nr = n0 + r < p.n ? n0 + r : p.n - 1;
+    const int64_t mr = m0 + r < p.m ? m0 + r : p.m - 1;
+    const int64_t rowb = p.k / 2, srow = p.k / BLOCK;
+    const int nc = (int)(p.k / 64);
+    // chunk c of this lane: codes at 32 c + 16 h of the row; scales (block
+    // 16) the dword at 4 c holding both K-halves' two bytes, (block 32) the
+    // u16 at 2 c holding both K-halves' byte
+    const uint8_t* qw = p.qb + nr * rowb + 16 * h;
+    const uint8_t* qa = p.qa + mr * rowb + 16 * h;
+    const uint8_t* sw = p.sb + nr * srow;
+    const uint8_t* sa = p.sa + mr * srow;
+    auto scales_at = [&](const uint8_t* row, int c) -> uint32_t {
+        if (BLOCK == 16) return *reinterpret_cast<const uint32_t*>(row + 4 * c) >> (16 * h);   // 2 bytes
+        return (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * c) >> (8 * h);         // 1 byte
+    };
+    ScaleFmt fw{}, fa{};
+    if (MODE == 1) {
+        fw = ScaleFmt{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
+        fa = ScaleFmt{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
+    }
+    // f16 scale of dword t (elements 8 t .. 8 t + 7 of the lane's 32)
+    auto scale_h = [&](uint32_t code, int t, const ScaleFmt& f) -> v2h {
+        const uint32_t b = BLOCK == 16 && t >= 2 ? (code >> 8) & 0xFFu : code & 0xFFu;
+        if (MODE == 0) {
+            const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+            return v2h{s2[0], s2[0]};
+        }
+        const _Float16 v = (_Float16)scale_decode_any(b, f);
+        return v2h{v, v};
+    };
+
+    v4i cw[kSmallAhead], ca[kSmallAhead];
+    uint32_t cs[kSmallAhead], ct[kSmallAhead];
+    auto load = [&](int i, int c) {
+        const int cc = c < nc ? c : nc - 1;   // past the end: the last chunk again, never used
+        cw[i] = *reinterpret_cast<const v4i*>(qw + 32 * (int64_t)cc);
+        ca[i] = *reinterpret_cast<const v4i*>(qa + 32 * (int64_t)cc);
+        cs[i] = scales_at(sw, cc);
+        ct[i] = scales_at(sa, cc);
+    };
+#pragma unroll
+    for (int i = 0; i < kSmallAhead; ++i) load(i, i);
+    v16f acc = {};
+    for (int c0 = 0; c0 < nc; c0 += kSmallAhead) {
+#pragma unroll
+        for (int i = 0; i < kSmallAhead; ++i) {
+            if (c0 + i < nc) {
+                if constexpr (MODE == 2) {
+                    const v8i w8{cw[i][0], cw[i][1], cw[i][2], cw[i][3], 0, 0, 0, 0};
+                    const v8i a8{ca[i][0], ca[i][1], ca[i][2], ca[i][3], 0, 0, 0, 0};
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a8, acc, 4, 4, 0, (int)(cs[i] & 0xFFu),
+                                                                           0, (int)(ct[i] & 0xFFu));
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const v8h xw = nv_convert8((uint32_t)cw[i][t], scale_h(cs[i], t, fw));
+                        const v8h xa = nv_convert8((uint32_t)ca[i][t], scale_h(ct[i], t, fa));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xw, xa, acc, 0, 0, 0);
+                    }
+                }
+            }
+            load(i, c0 + kSmallAhead + i);
+        }
+    }
+
+    // acc[4 q + e] = D[n0 + 8 q + 4 h + e][m0 + r]: C[m][n .. n + 3] as bf16
+    const int64_t m = m0 + r;
+    if (m >= p.m) return;
+    const float g = p.ga[0] * p.gb[0];
+    uint16_t* crow = p.c + m * p.ldc;
+    const bool vec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + 8 * q + 4 * h;
+        const uint32_t b0 = f32_to_bf16_rne(acc[4 * q + 0] * g), b1 = f32_to_bf16_rne(acc[4 * q + 1] * g);
+        const uint32_t b2 = f32_to_bf16_rne(acc[4 * q + 2] * g), b3 = f32_to_bf16_rne(acc[4 * q + 3] * g);
+        if (vec && n + 3 < p.n) {
+            *reinterpret_cast<uint2*>(crow + n) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
+        } else {
+            if (n + 0 < p.n) crow[n + 0] = (uint16_t)b0;
+            if (n + 1 < p.n) crow[n + 1] = (uint16_t)b1;
+            if (n + 2 < p.n) crow[n + 2] = (uint16_t)b2;
+            if (n + 3 < p.n) crow[n + 3] = (uint16_t)b3;
+        }
+    }
+}
+
+// The small path takes E2M1 operands with E8M0 scales at block 32 or with
+// f16-exact scale formats on both sides, when M * N is at most
+// g_gemm_small_outputs (MXFP4: an eighth of it).  Measured on the MI355X at
+// K = 4096, the small path runs at about 0.27 PFLOP/s whatever the shape,
+// while a 256 x 256 tile of the f16 form takes about 90 us and one of MXFP4
+// about 30 us however few tiles there are: NVFP4 64 x 11008 37 us against
+// 91, 512 x 4096 68 against 89, 256 x 11008 111 against 92 (tiled), and
+// MXFP4 64 x 11008 37 against 31 (tiled).
+bool gemm_small_supported(const GemmLaunch& p)
+{
+    if (p.elem != 0 || (p.m + 31) / 32 > 65535) return false;
+    const int64_t bound = __atomic_load_n(&g_gemm_small_outputs, __ATOMIC_RELAXED);
+    const double mn = (double)p.m * (double)p.n;
+    if (p.fa.is_e8m0 && p.fb.is_e8m0) return p.block == 32 && mn <= (double)bound / 8.0;
+    return exact_in_f16(p.fa) && exact_in_f16(p.fb) && mn <= (double)bound;
+}
+
+hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
+{
+    const dim3 grid((unsigned)((p.n + 32 * kSmallWaves - 1) / (32 * kSmallWaves)), (unsigned)((p.m + 31) / 32));
+    const dim3 t(64 * kSmallWaves);
+    if (p.fa.is_e8m0) {
+        hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
+    } else if (is_e4m3(p.fa) && is_e4m3(p.fb)) {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<0, 16>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<0, 32>), grid, t, 0, s, p);
+    } else {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<1, 16>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<1, 32>), grid, t, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
 // INT4 elements carry 3 significant bits (E2M1: 2), so bf16 holds int * s
 // exactly for scale formats with at most 4 mantissa bits.
 static bool int4_exact_in_bf16(const ScaleFmtHost& f) { return f.is_e8m0 || f.mbits <= 4; }

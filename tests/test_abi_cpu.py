@@ -281,3 +281,18 @@ def test_quantize_noalloc_rejects_before_launch():
     assert L.fp4_quantize_noalloc(FAKE, 1, 64, ctypes.byref(t), 0, 0, None) == -2
     t.fmt.scale = 0
     assert L.fp4_quantize_noalloc(FAKE, 1, 32, ctypes.byref(t), 0, 0, None) == -3   # ld < cols
+
+
+def test_gemm_small_outputs_bound():
+    """fp4_set_gemm_small_outputs swaps the process-wide bound, returns the
+    previous one (2^21 by default) and rejects a negative bound."""
+    L = fq.lib()
+    assert L.fp4_version() >= 107
+    prev = ctypes.c_int64(-1)
+    assert L.fp4_set_gemm_small_outputs(5, ctypes.byref(prev)) == 0
+    first = prev.value
+    assert first == 1 << 21
+    assert L.fp4_set_gemm_small_outputs(first, ctypes.byref(prev)) == 0
+    assert prev.value == 5
+    assert L.fp4_set_gemm_small_outputs(-1, None) == -1
+    assert fq.set_gemm_small_outputs(first) == first

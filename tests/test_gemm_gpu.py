@@ -25,6 +25,17 @@ def _gpu():
         pytest.skip("no GPU")
 
 
+@pytest.fixture(autouse=True)
+def _tiled_kernels():
+    """These tests cover the tiled kernels, small shapes included (the
+    small-product path has its own tests)."""
+    prev = fq.set_gemm_small_outputs(0)
+    try:
+        yield
+    finally:
+        fq.set_gemm_small_outputs(prev)
+
+
 def _policy(fmt):
     return "none" if fmt == "e8m0" else "current"
 
