@@ -27,6 +27,10 @@
 //  * k_gemm_dq: the remaining pairs (E8M0 with a non-power-of-two format)
 //    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
 //    tiles are dequantized exactly to f16 or bf16 in LDS.
+//  * k_gemm_small: small products (E2M1 with f16-exact or E8M0 block-32
+//    scales; M * N up to a process-wide bound): one wave per 32 x 32 output
+//    tile, operands straight from global memory into registers, the same
+//    conversions and matrix instructions, no LDS.
 //  * k_wo_gemm: the weight-only GEMM (bf16 X times W on any element grid,
 //    M <= 16).
 #include <type_traits>
