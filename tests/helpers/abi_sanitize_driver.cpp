@@ -52,6 +52,10 @@ int main()
     uint64_t prev = 0;
     expect("set exchange wait", fp4_set_exchange_wait(123, &prev), FP4_OK);
     expect("restore exchange wait", fp4_set_exchange_wait(prev, nullptr), FP4_OK);
+    int64_t prev_small = 0;
+    expect("set small-product bound", fp4_set_gemm_small_outputs(7, &prev_small), FP4_OK);
+    expect("negative small-product bound", fp4_set_gemm_small_outputs(-1, nullptr), FP4_ERR_INVALID_ARG);
+    expect("restore small-product bound", fp4_set_gemm_small_outputs(prev_small, nullptr), FP4_OK);
 
     fp4_amax_state* st = nullptr;
     expect("state interval 0", fp4_amax_state_create(0, &st), FP4_ERR_INVALID_ARG);

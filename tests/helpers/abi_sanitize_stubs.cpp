@@ -10,6 +10,7 @@
 namespace fp4 {
 
 uint64_t g_exchange_wait_ticks = 20000000;
+int64_t g_gemm_small_outputs = (int64_t)1 << 21;
 
 [[noreturn]] static void reached(const char* what)
 {
@@ -25,6 +26,8 @@ hipError_t launch_gemm_mx(const GemmLaunch&, hipStream_t) { reached("launch_gemm
 bool gemm_mx16_supported(const GemmLaunch&) { reached("gemm_mx16_supported"); }
 hipError_t launch_gemm_mx16(const GemmLaunch&, hipStream_t) { reached("launch_gemm_mx16"); }
 hipError_t launch_gemm_dq(const GemmLaunch&, hipStream_t) { reached("launch_gemm_dq"); }
+bool gemm_small_supported(const GemmLaunch&) { reached("gemm_small_supported"); }
+hipError_t launch_gemm_small(const GemmLaunch&, hipStream_t) { reached("launch_gemm_small"); }
 hipError_t launch_wo_gemm(const WoGemmLaunch&, hipStream_t) { reached("launch_wo_gemm"); }
 hipError_t launch_fill_zero_bf16(uint16_t*, int64_t, int64_t, int64_t, hipStream_t) { reached("fill_zero"); }
 
