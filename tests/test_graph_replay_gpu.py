@@ -1,5 +1,6 @@
 """Column-wise, two-orientation, Hadamard-transformed and 8- / 6-bit grid
-quantize calls, GEMMs and dequantize calls
+quantize calls, the small NVFP4 / MXFP4 configuration, GEMMs and dequantize
+calls
 captured once in a HIP graph and replayed with new input values (eager
 copies and synchronizations between replays): every replay agrees with the
 oracle, the current-amax refreshes included (the captured amax kernel and
@@ -151,3 +152,70 @@ def test_graph_replay_wide_grids_gemm_and_dequantize():
         q, s, g, _ = oracle.quantize_tensor(hx, 32, "e8m0", "none", elem="fp6_e3m2")
         want = oracle.dequantize(q, s, float(g), 32, "e8m0", out="f32", elem="fp6_e3m2")
         assert_bytes_equal(f32_bits(host(y)), f32_bits(want), f"replay {rep} fp6 dequant")
+
+
+def test_graph_replay_small_configuration():
+    """The small NVFP4 configuration captured once: the 256x256 and 64x256
+    fp32 current-amax quantize calls (each fits one workgroup: no grid
+    exchange), a 1024x512 call between them that exchanges on the same state,
+    the small-product GEMM C = A B^T, and the same product of MXFP4 operands;
+    every replay with new values (the maximum moving between the tensors)
+    agrees with the oracle."""
+    b = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    a = torch.zeros((64, 256), dtype=torch.float32, device="cuda")
+    z = torch.zeros((1024, 512), dtype=torch.float32, device="cuda")
+    st = fq.AmaxState(1)
+    qb = fq.QTensor.empty(256, 256, 16, "e4m3")
+    qa = fq.QTensor.empty(64, 256, 16, "e4m3")
+    qz = fq.QTensor.empty(1024, 512, 16, "e4m3")
+    mb = fq.QTensor.empty(256, 256, 32, "e8m0", amax="none")
+    ma = fq.QTensor.empty(64, 256, 32, "e8m0", amax="none")
+    c = torch.empty((64, 256), dtype=torch.bfloat16, device="cuda")
+    cm = torch.empty((64, 256), dtype=torch.bfloat16, device="cuda")
+
+    def record():
+        fq.fp4_quantize(b, 16, "e4m3", state=st, out=qb)
+        fq.fp4_quantize(z, 16, "e4m3", state=st, out=qz)
+        fq.fp4_quantize(a, 16, "e4m3", state=st, out=qa)
+        fq.fp4_gemm(qa, qb, out=c)
+        fq.fp4_quantize(b, 32, "e8m0", amax="none", out=mb)
+        fq.fp4_quantize(a, 32, "e8m0", amax="none", out=ma)
+        fq.fp4_gemm(ma, mb, out=cm)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        record()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        record()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    for rep in range(4):
+        hb = inputs.small_b() * np.float32(2.0 ** (rep - 2))
+        ha = inputs.small_a() * np.float32(3.0 ** (1 - rep))
+        hz = (rng.standard_normal((1024, 512)) * 10.0 ** (rep - 1)).astype(np.float32)
+        b.copy_(torch.from_numpy(hb).cuda())
+        a.copy_(torch.from_numpy(ha).cuda())
+        z.copy_(torch.from_numpy(hz).cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        hats = {}
+        for name, h, qt in (("b", hb, qb), ("z", hz, qz), ("a", ha, qa)):
+            q, s, g, am = oracle.quantize_tensor(h, 16, "e4m3", "current", nthreads=8)
+            assert_bytes_equal(host(qt.q), q, f"replay {rep} {name} codes")
+            assert_bytes_equal(host(qt.scales), s, f"replay {rep} {name} scales")
+            assert_bytes_equal(f32_bits(host(qt.tensor_scale)), f32_bits([g, am]), f"replay {rep} {name} ts")
+            hats[name] = oracle.dequantize_f64(q, s, g, 16, "e4m3")
+        cref, tol = oracle.gemm_ref(hats["a"], hats["b"])
+        ok = oracle.gemm_check(c.float().cpu().numpy().astype(np.float64), cref, tol)
+        assert ok.all(), f"replay {rep} nvfp4 gemm: {int((~ok).sum())} outputs out of tolerance"
+        for h, qt, key in ((hb, mb, "mb"), (ha, ma, "ma")):
+            q, s, g, _ = oracle.quantize_tensor(h, 32, "e8m0", "none", nthreads=8)
+            assert_bytes_equal(host(qt.q), q, f"replay {rep} {key} codes")
+            hats[key] = oracle.dequantize_f64(q, s, g, 32, "e8m0")
+        cref, tol = oracle.gemm_ref(hats["ma"], hats["mb"])
+        ok = oracle.gemm_check(cm.float().cpu().numpy().astype(np.float64), cref, tol)
+        assert ok.all(), f"replay {rep} mxfp4 gemm: {int((~ok).sum())} outputs out of tolerance"
