@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="c1,sr,srt,dequant,rht,int4,w8,gemm,wo,wowide",
+    p.add_argument("--legs", default="c1,sr,srt,dequant,rht,int4,w8,gemm,gemmsmall,wo,wowide",
                    help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
@@ -323,6 +323,46 @@ def leg_dequant(torch, fq, xs):
     algo = n // 2 + n // 16 + 8 + n * 2
     return {"workload": "4096x4096 E4M3 B16 -> bf16", "GB/s": round(algo / (ms * 1e-3) / 1e9, 1),
             "us_per_call": round(ms * 1e3, 3)}
+
+
+def leg_gemm_small(torch, fq, inputs):
+    """Small products on both GEMM paths: the one-wave-per-32x32-tile path
+    (bound raised above every shape) against the tiled kernels (bound 0),
+    NVFP4 (E4M3 block 16) and MXFP4 (E8M0 block 32) at M = 64 / 256 / 512
+    against Llama-2 7B-shaped weights; per-call time between graph replays
+    (ten calls per replay), and the path the default bound picks."""
+    shapes = [(64, 256, 256), (64, 11008, 4096), (256, 11008, 4096), (512, 4096, 4096)]
+    res = {}
+    default = fq.set_gemm_small_outputs(0)
+    fq.set_gemm_small_outputs(default)
+    try:
+        for fmt, block, pol in (("e4m3", 16, "current"), ("e8m0", 32, "none")):
+            for m, n, k in shapes:
+                a = inputs.device_normal((m, k), 1.0, inputs.SEEDS["llama_a"], torch.bfloat16)
+                w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_up"], torch.bfloat16)
+                qa = fq.fp4_quantize(a, block, fmt, amax=pol)
+                qw = fq.fp4_quantize(w, block, fmt, amax=pol)
+                c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+                row = {}
+                for path, bound in (("tiled", 0), ("small", 1 << 40)):
+                    fq.set_gemm_small_outputs(bound)
+
+                    def rec(_):
+                        for _ in range(10):
+                            fq.fp4_gemm(qa, qw, out=c)
+                    gs = GraphSet(torch, 1, rec)
+                    us = time_graphs(torch, gs, 10, 2) / 10 * 1e3
+                    del gs
+                    row[path + "_us"] = round(us, 2)
+                    row[path + "_TFLOP/s"] = round(2.0 * m * n * k / us / 1e6, 1)
+                mn = m * n
+                row["default_path"] = "small" if mn <= (default if fmt != "e8m0" else default // 8) else "tiled"
+                res[f"{fmt}_b{block}_{m}x{n}x{k}"] = row
+    finally:
+        fq.set_gemm_small_outputs(default)
+    res["workload"] = ("small products, A M x K N(0,1) bf16 and W N x K N(0,0.02) bf16 quantized NVFP4 (E4M3 B16, "
+                       "current amax) or MXFP4 (E8M0 B32); the small path against the tiled kernels")
+    return res
 
 
 def leg_gemm(torch, fq, inputs):
@@ -678,6 +718,8 @@ def main():
     want = [] if args.legs == "none" else args.legs.split(",")
     if "c1" in want:
         legs["c1_small"] = leg_c1(torch, fq, inputs)
+    if "gemmsmall" in want:
+        legs["gemm_small_products"] = leg_gemm_small(torch, fq, inputs)
     if "dequant" in want:
         legs["dequant"] = leg_dequant(torch, fq, xs[:8])
     if "rht" in want:
