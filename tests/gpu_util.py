@@ -33,3 +33,21 @@ def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str):
 
 def f32_bits(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def check_gemm_every_output(c_gpu: torch.Tensor, a_hat: np.ndarray, w_hat: np.ndarray, tag: str, block_rows=1024):
+    """Every bf16 output of C = A W^T within the oracle's bound (the bf16
+    rounding of some value within 1e-5 * sum_k |a||w| of the binary64
+    product), the reference taken 1024 rows at a time to bound its memory."""
+    import oracle
+    c = c_gpu.float().cpu().numpy().astype(np.float64)
+    wt, wabs = np.ascontiguousarray(w_hat.T), np.ascontiguousarray(np.abs(w_hat).T)
+    for r0 in range(0, c.shape[0], block_rows):
+        ab = a_hat[r0:r0 + block_rows]
+        cref = ab @ wt
+        tol = 1e-5 * (np.abs(ab) @ wabs)
+        ok = oracle.gemm_check(c[r0:r0 + block_rows], cref, tol)
+        if not ok.all():
+            i, j = np.argwhere(~ok)[0]
+            raise AssertionError(f"{tag}: {int((~ok).sum())} outputs in rows {r0}.. out of tolerance; first "
+                                 f"({r0 + i},{j}) got {c[r0 + i, j]!r} ref {cref[i, j]!r} tol {tol[i, j]!r}")

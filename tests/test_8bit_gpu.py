@@ -13,7 +13,7 @@ import torch
 
 import fp4_inputs as inputs
 import oracle
-from tests.gpu_util import assert_bytes_equal, bf16_bits, f32_bits, host, to_device
+from tests.gpu_util import assert_bytes_equal, bf16_bits, check_gemm_every_output, f32_bits, host, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -285,18 +285,16 @@ def test_8bit_gemm_transform_and_sr(elem):
 
 
 @pytest.mark.parametrize("elem,fmt,block", [("fp8_e4m3", "e8m0", 32), ("int8", "e4m3", 16)])
-def test_8bit_gemm_llama_sampled_rows(elem, fmt, block):
+def test_8bit_gemm_llama_every_output(elem, fmt, block):
     """Llama-2 7B square projection at M = 8192 (batch 4 x seq 2048), the
-    launch the GEMM timing uses: sampled output rows, including both ends of
-    the first tile and the last row, against the binary64 reference."""
+    launch the GEMM timing uses: every output against the binary64
+    reference."""
     shapes = {"a": (8192, 4096), "sq": (4096, 4096)}
     qa, a = _quant_pair(inputs.llama("a", shapes), block, fmt, elem)
     qw, w = _quant_pair(inputs.llama("sq", shapes), block, fmt, elem)
     c = fq.fp4_gemm(qa, qw)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(10)
-    rows = np.unique(np.concatenate([rng.integers(0, 8192, 24), [0, 255, 256, 8191]]))
-    _gemm_check(c, a, w, rows=rows, tag=f"{elem} {fmt} llama sq")
+    check_gemm_every_output(c, a, w, f"{elem} {fmt} llama sq")
 
 
 @pytest.mark.parametrize("elem,fmt", [("fp8_e4m3", "e8m0"), ("int8", "e8m0"), ("int8", "e4m3")])
