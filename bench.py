@@ -285,17 +285,20 @@ def leg_rht(torch, fq, xs):
 
 def leg_c1(torch, fq, inputs):
     """The small correctness configuration, timed: B 256x256 fp32 (1% of
-    entries x50) and A 64x256 fp32 quantized NVFP4 (E4M3 block 16, current
-    amax, RTN), then C = A B^T; per-call latency between graph replays
-    (launch-bound at this size)."""
+    entries x50) quantized NVFP4 (E4M3 block 16, current amax, RTN) and
+    dequantized to fp32, A 64x256 fp32 quantized the same way, then
+    C = A B^T; per-call latency between graph replays (launch-bound at this
+    size)."""
     b = torch.from_numpy(inputs.small_b()).cuda()
     a = torch.from_numpy(inputs.small_a()).cuda()
     st_b, st_a = fq.AmaxState(1), fq.AmaxState(1)
     qb = fq.QTensor.empty(256, 256, 16, "e4m3")
     qa = fq.QTensor.empty(64, 256, 16, "e4m3")
     c = torch.empty((64, 256), dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty((256, 256), dtype=torch.float32, device="cuda")
     res = {}
     for name, fn in {"quantize_b_us": lambda: fq.fp4_quantize(b, 16, "e4m3", state=st_b, out=qb),
+                     "dequantize_b_us": lambda: fq.fp4_dequantize(qb, torch.float32, out=yb),
                      "quantize_a_us": lambda: fq.fp4_quantize(a, 16, "e4m3", state=st_a, out=qa),
                      "gemm_us": lambda: fq.fp4_gemm(qa, qb, out=c)}.items():
         def rec(_, fn=fn):
@@ -304,8 +307,8 @@ def leg_c1(torch, fq, inputs):
         gs = GraphSet(torch, 1, rec)
         res[name] = round(time_graphs(torch, gs, 20, 3) / 10 * 1e3, 3)
         del gs
-    res["workload"] = ("256x256 fp32 B and 64x256 fp32 A, NVFP4 (E4M3 B16, current amax, RTN); C = A B^T "
-                       "(8.39 MFLOP); microseconds per call, ten calls per graph replay")
+    res["workload"] = ("256x256 fp32 B (quantized and dequantized to fp32) and 64x256 fp32 A, NVFP4 (E4M3 B16, "
+                       "current amax, RTN); C = A B^T (8.39 MFLOP); microseconds per call, ten calls per graph replay")
     return res
 
 
