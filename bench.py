@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "0a120c9ce5740db4134aeb3059ef2bbac94f90ee18ce818799a3e5de7390fbce",
-    "read_bytes": 33858971,
+    "sha256": "594d1e97455c43f1bda9e0e52f794a5bbe57daaf8959fc7713194e75181ed209",
+    "read_bytes": 33860392,
     "write_bytes": 9453696,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }

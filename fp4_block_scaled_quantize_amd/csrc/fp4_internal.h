@@ -24,9 +24,10 @@ bool scale_fmt_params(int32_t fmt, ScaleFmtHost* out);
 //  - slot: the single-pass refresh exchanges per-workgroup maxima through
 //    `slot` (64-bit {epoch, max bits} words, one per 64-byte segment so that
 //    stores of different workgroups never share a line) within one launch.
-//    Every single-pass launch on a device runs the same grid and publishes
-//    every slot, so a workgroup's own slot holds the previous launch's
-//    epoch, and that + 1 is this launch's.
+//    Every single-pass launch that exchanges runs the same grid and
+//    publishes every slot (a grid of one writes none), so a workgroup's own
+//    slot holds the previous exchanging launch's epoch, and that + 1 is
+//    this launch's.
 //  - fallbacks: number of workgroups that did not see every other
 //    workgroup's maximum within the wait bound and read the whole tensor
 //    themselves instead (the result is the same either way).

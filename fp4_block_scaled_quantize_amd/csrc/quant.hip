@@ -275,10 +275,11 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t m)
 // bounded in time: a workgroup that gives up takes the maximum of the whole
 // tensor itself (full_tensor_amax), which is the same value, so the result
 // never depends on co-residency.
-// Epochs: every single-pass launch on a device runs the same grid (one
+// Epochs: every single-pass launch that exchanges runs the same grid (one
 // workgroup per CU, however small the tensor) and every workgroup publishes
 // exactly once per launch, so at the start of a launch every slot carries
-// the previous launch's epoch (0 in a fresh state).  Each workgroup reads
+// the previous exchanging launch's epoch (0 in a fresh state); a tensor
+// that fits one workgroup runs as a grid of one, which writes no slot.  Each workgroup reads
 // its own slot -- written only by itself -- and uses that epoch + 1: the
 // same fresh epoch for every workgroup of the launch (graph replays
 // included), with no counter, no atomic read-modify-write and nothing left
