@@ -82,7 +82,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rot", type=int, default=24, help="resident input copies rotated through")
-    p.add_argument("--legs", default="c1,sr,srt,dequant,rht,int4,w8,gemm,gemmsmall,wo,wowide",
+    p.add_argument("--legs", default="small,sr,srt,dequant,rht,int4,w8,gemm,gemmsmall,wo,wowide",
                    help="extra legs (comma list, or 'none')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
@@ -283,7 +283,7 @@ def leg_rht(torch, fq, xs):
     return res
 
 
-def leg_c1(torch, fq, inputs):
+def leg_small_nvfp4(torch, fq, inputs):
     """The small correctness configuration, timed: B 256x256 fp32 (1% of
     entries x50) quantized NVFP4 (E4M3 block 16, current amax, RTN) and
     dequantized to fp32, A 64x256 fp32 quantized the same way, then
@@ -719,8 +719,8 @@ def main():
         del src, dst
     legs = {}
     want = [] if args.legs == "none" else args.legs.split(",")
-    if "c1" in want:
-        legs["c1_small"] = leg_c1(torch, fq, inputs)
+    if "small" in want:
+        legs["small_nvfp4_256x256"] = leg_small_nvfp4(torch, fq, inputs)
     if "gemmsmall" in want:
         legs["gemm_small_products"] = leg_gemm_small(torch, fq, inputs)
     if "dequant" in want:
