@@ -331,7 +331,7 @@ def leg_dequant(torch, fq, xs):
 def leg_gemm_small(torch, fq, inputs):
     """Small products on both GEMM paths: the one-wave-per-32x32-tile path
     (bound raised above every shape) against the tiled kernels (bound 0),
-    NVFP4 (E4M3 block 16) and MXFP4 (E8M0 block 32) at M = 64 / 256 / 512
+    NVFP4 (E4M3 block 16), UE5M3 block 16 and MXFP4 (E8M0 block 32) at M = 64 / 256 / 512
     against Llama-2 7B-shaped weights; per-call time between graph replays
     (ten calls per replay), and the path the default bound picks."""
     shapes = [(64, 256, 256), (64, 11008, 4096), (256, 11008, 4096), (512, 4096, 4096)]
@@ -339,7 +339,7 @@ def leg_gemm_small(torch, fq, inputs):
     default = fq.set_gemm_small_outputs(0)
     fq.set_gemm_small_outputs(default)
     try:
-        for fmt, block, pol in (("e4m3", 16, "current"), ("e8m0", 32, "none")):
+        for fmt, block, pol in (("e4m3", 16, "current"), ("ue5m3", 16, "current"), ("e8m0", 32, "none")):
             for m, n, k in shapes:
                 a = inputs.device_normal((m, k), 1.0, inputs.SEEDS["llama_a"], torch.bfloat16)
                 w = inputs.device_normal((n, k), 0.02, inputs.SEEDS["llama_up"], torch.bfloat16)
@@ -359,12 +359,13 @@ def leg_gemm_small(torch, fq, inputs):
                     row[path + "_us"] = round(us, 2)
                     row[path + "_TFLOP/s"] = round(2.0 * m * n * k / us / 1e6, 1)
                 mn = m * n
-                row["default_path"] = "small" if mn <= (default if fmt != "e8m0" else default // 8) else "tiled"
+                limit = {"e8m0": default / 8, "ue5m3": 1.5 * default}.get(fmt, default)
+                row["default_path"] = "small" if mn <= limit else "tiled"
                 res[f"{fmt}_b{block}_{m}x{n}x{k}"] = row
     finally:
         fq.set_gemm_small_outputs(default)
     res["workload"] = ("small products, A M x K N(0,1) bf16 and W N x K N(0,0.02) bf16 quantized NVFP4 (E4M3 B16, "
-                       "current amax) or MXFP4 (E8M0 B32); the small path against the tiled kernels")
+                       "current amax), UE5M3 B16 or MXFP4 (E8M0 B32); the small path against the tiled kernels")
     return res
 
 

@@ -27,8 +27,8 @@
 //  * k_gemm_dq: the remaining pairs (E8M0 with a non-power-of-two format)
 //    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
 //    tiles are dequantized exactly to f16 or bf16 in LDS.
-//  * k_gemm_small: small products (E2M1 with f16-exact or E8M0 block-32
-//    scales; M * N up to a process-wide bound): one wave per 32 x 32 output
+//  * k_gemm_small: small products (E2M1 with f16- / bf16-exact ExMy or E8M0
+//    block-32 scales; M * N up to a process-wide bound): one wave per 32 x 32 output
 //    tile, operands straight from global memory into registers, the same
 //    conversions and matrix instructions, no LDS.
 //  * k_wo_gemm: the weight-only GEMM (bf16 X times W on any element grid,
@@ -1464,7 +1464,11 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // which leaves every dot product unchanged).  Eight chunks are in flight
 // per lane.
 // MODE: 0 E2M1 with E4M3 scales (hardware scale decode), 1 other f16-exact
-// scale formats (decoded in registers), 2 MXFP4.
+// scale formats (decoded in registers), 2 MXFP4, 3 the bf16-exact ExMy
+// formats (UE5M3, E5M2, E6M1, E7M0, and pairs of them with the f16 ones):
+// codes to fp32, times the fp32 scale with the power-of-two part of the
+// tensor scale folded in (as the tiled bf16 form), to bf16, bf16 matrix
+// instruction.
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 4;
 constexpr int kSmallAhead = 8;
@@ -1494,7 +1498,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
         return (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * c) >> (8 * h);         // 1 byte
     };
     ScaleFmt fw{}, fa{};
-    if (MODE == 1) {
+    const float pw = MODE == 3 ? split_pow2(p.gb[0]) : 1.0f, pa = MODE == 3 ? split_pow2(p.ga[0]) : 1.0f;
+    if (MODE == 1 || MODE == 3) {
         fw = ScaleFmt{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
         fa = ScaleFmt{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
     }
@@ -1507,6 +1512,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
         }
         const _Float16 v = (_Float16)scale_decode_any(b, f);
         return v2h{v, v};
+    };
+    // fp32 scale of dword t times the power-of-two part p of the tensor scale
+    auto scale_f = [&](uint32_t code, int t, const ScaleFmt& f, float pp) -> float {
+        const uint32_t b = BLOCK == 16 && t >= 2 ? (code >> 8) & 0xFFu : code & 0xFFu;
+        return scale_decode_any(b, f) * pp;
     };
 
     v4i cw[kSmallAhead], ca[kSmallAhead];
@@ -1530,6 +1540,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
                     const v8i a8{ca[i][0], ca[i][1], ca[i][2], ca[i][3], 0, 0, 0, 0};
                     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a8, acc, 4, 4, 0, (int)(cs[i] & 0xFFu),
                                                                            0, (int)(ct[i] & 0xFFu));
+                } else if constexpr (MODE == 3) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const v8bf xw = nv_convert8_bf16((uint32_t)cw[i][t], scale_f(cs[i], t, fw, pw));
+                        const v8bf xa = nv_convert8_bf16((uint32_t)ca[i][t], scale_f(ct[i], t, fa, pa));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xw, xa, acc, 0, 0, 0);
+                    }
                 } else {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -1546,7 +1563,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
     // acc[4 q + e] = D[n0 + 8 q + 4 h + e][m0 + r]: C[m][n .. n + 3] as bf16
     const int64_t m = m0 + r;
     if (m >= p.m) return;
-    const float g = p.ga[0] * p.gb[0];
+    const float g = MODE == 3 ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
     uint16_t* crow = p.c + m * p.ldc;
     const bool vec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0);
 #pragma unroll
@@ -1565,21 +1582,26 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
     }
 }
 
-// The small path takes E2M1 operands with E8M0 scales at block 32 or with
-// f16-exact scale formats on both sides, when M * N is at most
-// g_gemm_small_outputs (MXFP4: an eighth of it).  Measured on the MI355X at
+// The small path takes E2M1 operands with E8M0 scales at block 32, or with
+// f16- or bf16-exact ExMy scale formats on both sides (the pairings of the
+// tiled register-conversion kernel), when M * N is at most
+// g_gemm_small_outputs (MXFP4: an eighth of it; the bf16 forms, whose tiled
+// kernel is slower, one and a half times it).  Measured on the MI355X at
 // K = 4096, the small path runs at about 0.27 PFLOP/s whatever the shape,
 // while a 256 x 256 tile of the f16 form takes about 90 us and one of MXFP4
 // about 30 us however few tiles there are: NVFP4 64 x 11008 37 us against
 // 91, 512 x 4096 68 against 89, 256 x 11008 111 against 92 (tiled), and
-// MXFP4 64 x 11008 37 against 31 (tiled).
+// MXFP4 64 x 11008 37 against 31 (tiled); UE5M3 (bf16 form) 64 x 11008 63
+// against 156, 256 x 11008 126 against 160, 512 x 4096 90 against 159.
 bool gemm_small_supported(const GemmLaunch& p)
 {
     if (p.elem != 0 || (p.m + 31) / 32 > 65535) return false;
     const int64_t bound = __atomic_load_n(&g_gemm_small_outputs, __ATOMIC_RELAXED);
     const double mn = (double)p.m * (double)p.n;
     if (p.fa.is_e8m0 && p.fb.is_e8m0) return p.block == 32 && mn <= (double)bound / 8.0;
-    return exact_in_f16(p.fa) && exact_in_f16(p.fb) && mn <= (double)bound;
+    if (p.fa.is_e8m0 || p.fb.is_e8m0) return false;
+    if (exact_in_f16(p.fa) && exact_in_f16(p.fb)) return mn <= (double)bound;
+    return exact_in_bf16(p.fa) && exact_in_bf16(p.fb) && mn <= 1.5 * (double)bound;
 }
 
 hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
@@ -1588,6 +1610,9 @@ hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
     const dim3 t(64 * kSmallWaves);
     if (p.fa.is_e8m0) {
         hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
+    } else if (!(exact_in_f16(p.fa) && exact_in_f16(p.fb))) {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<3, 16>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<3, 32>), grid, t, 0, s, p);
     } else if (is_e4m3(p.fa) && is_e4m3(p.fb)) {
         if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<0, 16>), grid, t, 0, s, p);
         else hipLaunchKernelGGL((k_gemm_small<0, 32>), grid, t, 0, s, p);
