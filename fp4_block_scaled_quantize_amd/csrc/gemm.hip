@@ -28,7 +28,7 @@
 //    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
 //    tiles are dequantized exactly to f16 or bf16 in LDS.
 //  * k_gemm_small: small products (E2M1 with f16- / bf16-exact ExMy or E8M0
-//    block-32 scales; M * N up to a process-wide bound): one wave per 32 x 32 output
+//    scales; M * N up to a process-wide bound): one wave per 32 x 32 output
 //    tile, operands straight from global memory into registers, the same
 //    conversions and matrix instructions, no LDS.
 //  * k_wo_gemm: the weight-only GEMM (bf16 X times W on any element grid,
@@ -1468,7 +1468,9 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // formats (UE5M3, E5M2, E6M1, E7M0, and pairs of them with the f16 ones):
 // codes to fp32, times the fp32 scale with the power-of-two part of the
 // tensor scale folded in (as the tiled bf16 form), to bf16, bf16 matrix
-// instruction.
+// instruction; 4 E8M0 at block 16: the scaled FP4 instruction twice per
+// chunk, A's other 16-element block of each K-half zeroed, with the scale
+// bytes of the block that remains (as k_gemm_mx16).
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 4;
 constexpr int kSmallAhead = 8;
@@ -1478,6 +1480,7 @@ template <int MODE, int BLOCK>
 __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 {
     static_assert(MODE != 2 || BLOCK == 32, "MXFP4 scales cover 32 elements");
+    static_assert(MODE != 4 || BLOCK == 16, "two runs per K-half for blocks of 16");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = ((int64_t)blockIdx.x * kSmallWaves + wave) * 32, m0 = (int64_t)blockIdx.y * 32;
     if (n0 >= p.n) return;                    // whole waves only; no barrier follows
@@ -1540,6 +1543,17 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
                     const v8i a8{ca[i][0], ca[i][1], ca[i][2], ca[i][3], 0, 0, 0, 0};
                     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a8, acc, 4, 4, 0, (int)(cs[i] & 0xFFu),
                                                                            0, (int)(ct[i] & 0xFFu));
+                } else if constexpr (MODE == 4) {
+                    // elements 0..15 of the lane's 32 are dwords 0, 1 (the
+                    // K-half's first block), 16..31 dwords 2, 3
+                    const v8i w8{cw[i][0], cw[i][1], cw[i][2], cw[i][3], 0, 0, 0, 0};
+                    const v8i a0{ca[i][0], ca[i][1], 0, 0, 0, 0, 0, 0};
+                    const v8i a1{0, 0, ca[i][2], ca[i][3], 0, 0, 0, 0};
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a0, acc, 4, 4, 0, (int)(cs[i] & 0xFFu), 0,
+                                                                           (int)(ct[i] & 0xFFu));
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a1, acc, 4, 4, 0,
+                                                                           (int)((cs[i] >> 8) & 0xFFu), 0,
+                                                                           (int)((ct[i] >> 8) & 0xFFu));
                 } else if constexpr (MODE == 3) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -1582,10 +1596,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
     }
 }
 
-// The small path takes E2M1 operands with E8M0 scales at block 32, or with
+// The small path takes E2M1 operands with E8M0 scales (block 32 or 16), or with
 // f16- or bf16-exact ExMy scale formats on both sides (the pairings of the
 // tiled register-conversion kernel), when M * N is at most
-// g_gemm_small_outputs (MXFP4: an eighth of it; the bf16 forms, whose tiled
+// g_gemm_small_outputs (E8M0: an eighth of it; the bf16 forms, whose tiled
 // kernel is slower, one and a half times it).  Measured on the MI355X at
 // K = 4096, the small path runs at about 0.27 PFLOP/s whatever the shape,
 // while a 256 x 256 tile of the f16 form takes about 90 us and one of MXFP4
@@ -1598,7 +1612,7 @@ bool gemm_small_supported(const GemmLaunch& p)
     if (p.elem != 0 || (p.m + 31) / 32 > 65535) return false;
     const int64_t bound = __atomic_load_n(&g_gemm_small_outputs, __ATOMIC_RELAXED);
     const double mn = (double)p.m * (double)p.n;
-    if (p.fa.is_e8m0 && p.fb.is_e8m0) return p.block == 32 && mn <= (double)bound / 8.0;
+    if (p.fa.is_e8m0 && p.fb.is_e8m0) return mn <= (double)bound / 8.0;
     if (p.fa.is_e8m0 || p.fb.is_e8m0) return false;
     if (exact_in_f16(p.fa) && exact_in_f16(p.fb)) return mn <= (double)bound;
     return exact_in_bf16(p.fa) && exact_in_bf16(p.fb) && mn <= 1.5 * (double)bound;
@@ -1609,7 +1623,8 @@ hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
     const dim3 grid((unsigned)((p.n + 32 * kSmallWaves - 1) / (32 * kSmallWaves)), (unsigned)((p.m + 31) / 32));
     const dim3 t(64 * kSmallWaves);
     if (p.fa.is_e8m0) {
-        hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
+        if (p.block == 32) hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<4, 16>), grid, t, 0, s, p);
     } else if (!(exact_in_f16(p.fa) && exact_in_f16(p.fb))) {
         if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<3, 16>), grid, t, 0, s, p);
         else hipLaunchKernelGGL((k_gemm_small<3, 32>), grid, t, 0, s, p);

@@ -347,7 +347,7 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * to bf16 / f16 in LDS.  Small products of E2M1 with f16-exact ExMy scales
  * on both operands (M * N at most the bound of fp4_set_gemm_small_outputs,
  * 2^21 by default), with bf16-exact ExMy scales (1.5 times the bound) or
- * with E8M0 block-32 scales (an eighth of it) run one wave per 32 x 32
+ * with E8M0 scales (an eighth of it) run one wave per 32 x 32
  * output tile with the same conversions and instructions and no LDS.  Result within 1e-5 * sum_k
  * |a||b| of the exact product before the bf16 rounding.
  * K % 128 == 0 (K = 0 writes C = 0 and reads no operand), M and N

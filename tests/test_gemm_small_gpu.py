@@ -1,6 +1,8 @@
 """GPU tolerance tests of the small-product GEMM path (one wave per 32 x 32
-output tile, operands straight into registers): E2M1 with E8M0 block-32
-scales on the scaled FP4 instruction, E2M1 with the f16-exact scale formats
+output tile, operands straight into registers): E2M1 with E8M0 scales on
+the scaled FP4 instruction (block 32, and block 16 as two runs per K-half
+with the other block of A zeroed; gonzo_ML/3986 "Форматы FP4": groups of 16
+with power-of-two scales), E2M1 with the f16-exact scale formats
 (E4M3, E3M4, E2M5, E1M6; gonzo_ML/3986 "Форматы FP4") converted to f16, and
 with UE5M3 and the other wide-exponent formats (ue5m3-fp4-pretraining "Что
 сделали") converted to bf16 in registers.
@@ -82,7 +84,8 @@ SHAPES = [(64, 256, 256), (1, 33, 128), (70, 300, 384), (257, 513, 640), (33, 10
 
 
 @pytest.mark.parametrize("fmt,block", [("e4m3", 16), ("e4m3", 32), ("e3m4", 16), ("e2m5", 32), ("e1m6", 16),
-                                       ("e8m0", 32), ("ue5m3", 16), ("e5m2", 32), ("e6m1", 16), ("e7m0", 16)])
+                                       ("e8m0", 32), ("e8m0", 16), ("ue5m3", 16), ("e5m2", 32), ("e6m1", 16),
+                                       ("e7m0", 16)])
 @pytest.mark.parametrize("m,n,k", SHAPES)
 def test_small_path_formats(small_path, fmt, block, m, n, k):
     qa, a = _quant_both(_normal(m, k, 11 + m), block, fmt)
@@ -108,7 +111,7 @@ def test_small_path_wide_range_and_outliers(small_path):
     """Rows spanning many binades (x 2^-20 .. 2^20 per row) with 1% outliers
     x50: block scales over the whole E4M3 range, and E8M0 scales far apart."""
     rng = np.random.default_rng(5)
-    for fmt, block in (("e4m3", 16), ("e8m0", 32), ("ue5m3", 16), ("e7m0", 32)):
+    for fmt, block in (("e4m3", 16), ("e8m0", 32), ("e8m0", 16), ("ue5m3", 16), ("e7m0", 32)):
         a = _normal(40, 512, 31) * np.exp2(rng.integers(-20, 21, (40, 1))).astype(np.float32)
         w = _normal(72, 512, 32, 0.02)
         w[rng.random(w.shape) < 0.01] *= 50
