@@ -1458,10 +1458,10 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // into registers, no LDS and no barrier.  Lane l takes row l % 32 of each
 // operand and, of every 64-element chunk, the 16 bytes (32 E2M1 codes) of
 // K-half l / 32: exactly one lane fragment of the scaled FP4 instruction
-// (MXFP4, with the lane's own E8M0 byte), or four 8-element fragments of
-// the f16 instruction after the in-register conversion of the f16-exact
-// forms (the K order inside a chunk permuted identically for both operands,
-// which leaves every dot product unchanged).  Eight chunks are in flight
+// (E8M0 scales, with the lane's own scale byte), or four 8-element
+// fragments of the f16 / bf16 instruction after the in-register conversion
+// of the ExMy forms (the K order inside a chunk permuted identically for
+// both operands, which leaves every dot product unchanged).  Eight chunks are in flight
 // per lane.
 // MODE: 0 E2M1 with E4M3 scales (hardware scale decode), 1 other f16-exact
 // scale formats (decoded in registers), 2 MXFP4, 3 the bf16-exact ExMy
