@@ -115,9 +115,9 @@ bool gemm_mx16_supported(const GemmLaunch& p);
 hipError_t launch_gemm_mx16(const GemmLaunch& p, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmLaunch& p, hipStream_t s);
 // Small products on one wave per 32 x 32 output tile (no LDS): E2M1 with
-// E8M0 or f16- / bf16-exact ExMy scales on both operands, M * N at most
-// g_gemm_small_outputs (E8M0: an eighth of it, the bf16 forms 1.5 times
-// it; process-wide).
+// E8M0 or f16- / bf16-exact ExMy scales on both operands, MXFP8, INT8 with
+// E4M3 scales; M * N at most g_gemm_small_outputs (E2M1 with E8M0: an
+// eighth of it, the bf16 forms 1.5 times it; process-wide).
 extern int64_t g_gemm_small_outputs;
 bool gemm_small_supported(const GemmLaunch& p);
 hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s);

@@ -28,7 +28,8 @@
 //    and the INT4, other 8-bit and 6-bit pairings: FP4 / integer / FP8 / FP6
 //    tiles are dequantized exactly to f16 or bf16 in LDS.
 //  * k_gemm_small: small products (E2M1 with f16- / bf16-exact ExMy or E8M0
-//    scales; M * N up to a process-wide bound): one wave per 32 x 32 output
+//    scales, MXFP8, INT8 with E4M3 scales; M * N up to a process-wide
+//    bound): one wave per 32 x 32 output
 //    tile, operands straight from global memory into registers, the same
 //    conversions and matrix instructions, no LDS.
 //  * k_wo_gemm: the weight-only GEMM (bf16 X times W on any element grid,
@@ -1470,7 +1471,11 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // tensor scale folded in (as the tiled bf16 form), to bf16, bf16 matrix
 // instruction; 4 E8M0 at block 16: the scaled FP4 instruction twice per
 // chunk, A's other 16-element block of each K-half zeroed, with the scale
-// bytes of the block that remains (as k_gemm_mx16).
+// bytes of the block that remains (as k_gemm_mx16); 5 FP8 E4M3 elements
+// with E8M0 scales (MXFP8: bytes to bf16 with the scale applied, bf16
+// instruction) and 6 INT8 elements with E4M3 scales (to f16, f16
+// instruction), as k_gemm_nv's 8-bit forms, 32 bytes per lane per chunk
+// and four chunks in flight.
 // ---------------------------------------------------------------------------
 constexpr int kSmallWaves = 4;
 constexpr int kSmallAhead = 8;
@@ -1481,19 +1486,24 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 {
     static_assert(MODE != 2 || BLOCK == 32, "MXFP4 scales cover 32 elements");
     static_assert(MODE != 4 || BLOCK == 16, "two runs per K-half for blocks of 16");
+    constexpr bool W8 = MODE >= 5;                 // one byte per element: 32 bytes per lane per chunk
+    constexpr int AH = W8 ? kSmallAhead / 2 : kSmallAhead;
+    constexpr int NQ = W8 ? 2 : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = ((int64_t)blockIdx.x * kSmallWaves + wave) * 32, m0 = (int64_t)blockIdx.y * 32;
     if (n0 >= p.n) return;                    // whole waves only; no barrier follows
     const int r = lane & 31, h = lane >> 5;
     const int64_t nr = n0 + r < p.n ? n0 + r : p.n - 1;
     const int64_t mr = m0 + r < p.m ? m0 + r : p.m - 1;
-    const int64_t rowb = p.k / 2, srow = p.k / BLOCK;
+    const int64_t rowb = W8 ? p.k : p.k / 2, srow = p.k / BLOCK;
     const int nc = (int)(p.k / 64);
-    // chunk c of this lane: codes at 32 c + 16 h of the row; scales (block
-    // 16) the dword at 4 c holding both K-halves' two bytes, (block 32) the
-    // u16 at 2 c holding both K-halves' byte
-    const uint8_t* qw = p.qb + nr * rowb + 16 * h;
-    const uint8_t* qa = p.qa + mr * rowb + 16 * h;
+    // chunk c of this lane: codes at 32 c + 16 h of the row (one byte per
+    // element: 64 c + 32 h, two 16-byte pieces); scales (block 16) the dword
+    // at 4 c holding both K-halves' two bytes, (block 32) the u16 at 2 c
+    // holding both K-halves' byte
+    constexpr int CB = W8 ? 64 : 32;               // code bytes of a row per chunk
+    const uint8_t* qw = p.qb + nr * rowb + (CB / 2) * h;
+    const uint8_t* qa = p.qa + mr * rowb + (CB / 2) * h;
     const uint8_t* sw = p.sb + nr * srow;
     const uint8_t* sa = p.sa + mr * srow;
     auto scales_at = [&](const uint8_t* row, int c) -> uint32_t {
@@ -1501,15 +1511,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
         return (uint32_t)*reinterpret_cast<const uint16_t*>(row + 2 * c) >> (8 * h);         // 1 byte
     };
     ScaleFmt fw{}, fa{};
-    const float pw = MODE == 3 ? split_pow2(p.gb[0]) : 1.0f, pa = MODE == 3 ? split_pow2(p.ga[0]) : 1.0f;
-    if (MODE == 1 || MODE == 3) {
+    constexpr bool FOLD = MODE == 3 || MODE == 5;   // fp32 scales with the tensor scale's power of two
+    const float pw = FOLD ? split_pow2(p.gb[0]) : 1.0f, pa = FOLD ? split_pow2(p.ga[0]) : 1.0f;
+    if (MODE == 1 || FOLD) {
         fw = ScaleFmt{p.fb.ebits, p.fb.mbits, p.fb.bias, p.fb.maxcode, p.fb.smax, p.fb.is_e8m0};
         fa = ScaleFmt{p.fa.ebits, p.fa.mbits, p.fa.bias, p.fa.maxcode, p.fa.smax, p.fa.is_e8m0};
     }
     // f16 scale of dword t (elements 8 t .. 8 t + 7 of the lane's 32)
     auto scale_h = [&](uint32_t code, int t, const ScaleFmt& f) -> v2h {
         const uint32_t b = BLOCK == 16 && t >= 2 ? (code >> 8) & 0xFFu : code & 0xFFu;
-        if (MODE == 0) {
+        if (MODE == 0 || MODE == 6) {
             const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
             return v2h{s2[0], s2[0]};
         }
@@ -1522,33 +1533,36 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
         return scale_decode_any(b, f) * pp;
     };
 
-    v4i cw[kSmallAhead], ca[kSmallAhead];
-    uint32_t cs[kSmallAhead], ct[kSmallAhead];
+    v4i cw[AH][NQ], ca[AH][NQ];
+    uint32_t cs[AH], ct[AH];
     auto load = [&](int i, int c) {
         const int cc = c < nc ? c : nc - 1;   // past the end: the last chunk again, never used
-        cw[i] = *reinterpret_cast<const v4i*>(qw + 32 * (int64_t)cc);
-        ca[i] = *reinterpret_cast<const v4i*>(qa + 32 * (int64_t)cc);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            cw[i][q] = *reinterpret_cast<const v4i*>(qw + CB * (int64_t)cc + 16 * q);
+            ca[i][q] = *reinterpret_cast<const v4i*>(qa + CB * (int64_t)cc + 16 * q);
+        }
         cs[i] = scales_at(sw, cc);
         ct[i] = scales_at(sa, cc);
     };
 #pragma unroll
-    for (int i = 0; i < kSmallAhead; ++i) load(i, i);
+    for (int i = 0; i < AH; ++i) load(i, i);
     v16f acc = {};
-    for (int c0 = 0; c0 < nc; c0 += kSmallAhead) {
+    for (int c0 = 0; c0 < nc; c0 += AH) {
 #pragma unroll
-        for (int i = 0; i < kSmallAhead; ++i) {
+        for (int i = 0; i < AH; ++i) {
             if (c0 + i < nc) {
                 if constexpr (MODE == 2) {
-                    const v8i w8{cw[i][0], cw[i][1], cw[i][2], cw[i][3], 0, 0, 0, 0};
-                    const v8i a8{ca[i][0], ca[i][1], ca[i][2], ca[i][3], 0, 0, 0, 0};
+                    const v8i w8{cw[i][0][0], cw[i][0][1], cw[i][0][2], cw[i][0][3], 0, 0, 0, 0};
+                    const v8i a8{ca[i][0][0], ca[i][0][1], ca[i][0][2], ca[i][0][3], 0, 0, 0, 0};
                     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a8, acc, 4, 4, 0, (int)(cs[i] & 0xFFu),
                                                                            0, (int)(ct[i] & 0xFFu));
                 } else if constexpr (MODE == 4) {
                     // elements 0..15 of the lane's 32 are dwords 0, 1 (the
                     // K-half's first block), 16..31 dwords 2, 3
-                    const v8i w8{cw[i][0], cw[i][1], cw[i][2], cw[i][3], 0, 0, 0, 0};
-                    const v8i a0{ca[i][0], ca[i][1], 0, 0, 0, 0, 0, 0};
-                    const v8i a1{0, 0, ca[i][2], ca[i][3], 0, 0, 0, 0};
+                    const v8i w8{cw[i][0][0], cw[i][0][1], cw[i][0][2], cw[i][0][3], 0, 0, 0, 0};
+                    const v8i a0{ca[i][0][0], ca[i][0][1], 0, 0, 0, 0, 0, 0};
+                    const v8i a1{0, 0, ca[i][0][2], ca[i][0][3], 0, 0, 0, 0};
                     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a0, acc, 4, 4, 0, (int)(cs[i] & 0xFFu), 0,
                                                                            (int)(ct[i] & 0xFFu));
                     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, a1, acc, 4, 4, 0,
@@ -1557,27 +1571,48 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
                 } else if constexpr (MODE == 3) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const v8bf xw = nv_convert8_bf16((uint32_t)cw[i][t], scale_f(cs[i], t, fw, pw));
-                        const v8bf xa = nv_convert8_bf16((uint32_t)ca[i][t], scale_f(ct[i], t, fa, pa));
+                        const v8bf xw = nv_convert8_bf16((uint32_t)cw[i][0][t], scale_f(cs[i], t, fw, pw));
+                        const v8bf xa = nv_convert8_bf16((uint32_t)ca[i][0][t], scale_f(ct[i], t, fa, pa));
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xw, xa, acc, 0, 0, 0);
+                    }
+                } else if constexpr (MODE == 5) {
+                    // elements 8 t .. 8 t + 7: bytes 8 t .. 8 t + 7 of the 32
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int q = t >> 1, d = (2 * t) & 3;
+                        const v8bf xw = nv_convert8_fp8((uint32_t)cw[i][q][d], (uint32_t)cw[i][q][d + 1],
+                                                        scale_f(cs[i], t, fw, pw));
+                        const v8bf xa = nv_convert8_fp8((uint32_t)ca[i][q][d], (uint32_t)ca[i][q][d + 1],
+                                                        scale_f(ct[i], t, fa, pa));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xw, xa, acc, 0, 0, 0);
+                    }
+                } else if constexpr (MODE == 6) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int q = t >> 1, d = (2 * t) & 3;
+                        const v8h xw = nv_convert8_int8((uint32_t)cw[i][q][d], (uint32_t)cw[i][q][d + 1],
+                                                        scale_h(cs[i], t, fw));
+                        const v8h xa = nv_convert8_int8((uint32_t)ca[i][q][d], (uint32_t)ca[i][q][d + 1],
+                                                        scale_h(ct[i], t, fa));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xw, xa, acc, 0, 0, 0);
                     }
                 } else {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const v8h xw = nv_convert8((uint32_t)cw[i][t], scale_h(cs[i], t, fw));
-                        const v8h xa = nv_convert8((uint32_t)ca[i][t], scale_h(ct[i], t, fa));
+                        const v8h xw = nv_convert8((uint32_t)cw[i][0][t], scale_h(cs[i], t, fw));
+                        const v8h xa = nv_convert8((uint32_t)ca[i][0][t], scale_h(ct[i], t, fa));
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xw, xa, acc, 0, 0, 0);
                     }
                 }
             }
-            load(i, c0 + kSmallAhead + i);
+            load(i, c0 + AH + i);
         }
     }
 
     // acc[4 q + e] = D[n0 + 8 q + 4 h + e][m0 + r]: C[m][n .. n + 3] as bf16
     const int64_t m = m0 + r;
     if (m >= p.m) return;
-    const float g = MODE == 3 ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
+    const float g = FOLD ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
     uint16_t* crow = p.c + m * p.ldc;
     const bool vec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0);
 #pragma unroll
@@ -1597,8 +1632,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 }
 
 // The small path takes E2M1 operands with E8M0 scales (block 32 or 16), or with
-// f16- or bf16-exact ExMy scale formats on both sides (the pairings of the
-// tiled register-conversion kernel), when M * N is at most
+// f16- or bf16-exact ExMy scale formats on both sides, and the 8-bit
+// pairings of the tiled register-conversion kernel (MXFP8, INT8 with E4M3
+// scales), when M * N is at most
 // g_gemm_small_outputs (E8M0: an eighth of it; the bf16 forms, whose tiled
 // kernel is slower, one and a half times it).  Measured on the MI355X at
 // K = 4096, the small path runs at about 0.27 PFLOP/s whatever the shape,
@@ -1609,9 +1645,12 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 // against 156, 256 x 11008 126 against 160, 512 x 4096 90 against 159.
 bool gemm_small_supported(const GemmLaunch& p)
 {
-    if (p.elem != 0 || (p.m + 31) / 32 > 65535) return false;
+    if ((p.m + 31) / 32 > 65535) return false;
     const int64_t bound = __atomic_load_n(&g_gemm_small_outputs, __ATOMIC_RELAXED);
     const double mn = (double)p.m * (double)p.n;
+    if (p.elem == 2) return p.fa.is_e8m0 && p.fb.is_e8m0 && mn <= (double)bound;   // MXFP8
+    if (p.elem == 3) return is_e4m3(p.fa) && is_e4m3(p.fb) && mn <= (double)bound; // INT8 with E4M3 scales
+    if (p.elem != 0) return false;
     if (p.fa.is_e8m0 && p.fb.is_e8m0) return mn <= (double)bound / 8.0;
     if (p.fa.is_e8m0 || p.fb.is_e8m0) return false;
     if (exact_in_f16(p.fa) && exact_in_f16(p.fb)) return mn <= (double)bound;
@@ -1622,7 +1661,13 @@ hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
 {
     const dim3 grid((unsigned)((p.n + 32 * kSmallWaves - 1) / (32 * kSmallWaves)), (unsigned)((p.m + 31) / 32));
     const dim3 t(64 * kSmallWaves);
-    if (p.fa.is_e8m0) {
+    if (p.elem == 2) {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<5, 16>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<5, 32>), grid, t, 0, s, p);
+    } else if (p.elem == 3) {
+        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<6, 16>), grid, t, 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_small<6, 32>), grid, t, 0, s, p);
+    } else if (p.fa.is_e8m0) {
         if (p.block == 32) hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
         else hipLaunchKernelGGL((k_gemm_small<4, 16>), grid, t, 0, s, p);
     } else if (!(exact_in_f16(p.fa) && exact_in_f16(p.fb))) {

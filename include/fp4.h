@@ -345,10 +345,11 @@ FP4_API fp4_status fp4_dequantize(const fp4_tensor* in, void* y, int32_t y_dtype
  * E7M0), MXFP8 (FP8 with E8M0 on both) and INT8 with E4M3 on both are
  * converted to f16 / bf16 in registers; every other pairing is dequantized
  * to bf16 / f16 in LDS.  Small products of E2M1 with f16-exact ExMy scales
- * on both operands (M * N at most the bound of fp4_set_gemm_small_outputs,
- * 2^21 by default), with bf16-exact ExMy scales (1.5 times the bound) or
- * with E8M0 scales (an eighth of it) run one wave per 32 x 32
- * output tile with the same conversions and instructions and no LDS.  Result within 1e-5 * sum_k
+ * on both operands, of MXFP8 and of INT8 with E4M3 scales (M * N at most
+ * the bound of fp4_set_gemm_small_outputs, 2^21 by default), of E2M1 with
+ * bf16-exact ExMy scales (1.5 times the bound) or with E8M0 scales (an
+ * eighth of it) run one wave per 32 x 32 output tile with the same
+ * conversions and instructions and no LDS.  Result within 1e-5 * sum_k
  * |a||b| of the exact product before the bf16 rounding.
  * K % 128 == 0 (K = 0 writes C = 0 and reads no operand), M and N
  * arbitrary; ldc >= N; c 2-byte aligned (rows that
@@ -360,8 +361,8 @@ FP4_API fp4_status fp4_gemm(const fp4_tensor* a, const fp4_tensor* b, uint16_t* 
 /*
  * fp4_set_gemm_small_outputs -- the process-wide bound on M * N (output
  * elements) up to which fp4_gemm takes the small-product path for the
- * pairings it covers (above; E8M0 operands an eighth of it, the bf16-exact
- * ExMy pairings 1.5 times it).  0 turns the
+ * pairings it covers (above; E2M1 with E8M0 an eighth of it, E2M1 with the
+ * bf16-exact ExMy pairings 1.5 times it).  0 turns the
  * path off, so that tests can run the tiled kernels on small shapes.
  * Results on either path meet the same error bound.  The previous value is
  * returned in *previous if not null; a negative bound is

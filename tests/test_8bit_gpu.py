@@ -28,6 +28,18 @@ def _gpu():
         pytest.skip("no GPU")
 
 
+@pytest.fixture(autouse=True)
+def _tiled_kernels():
+    """These GEMM tests cover the tiled kernels, small shapes included (the
+    small-product path runs the every-code and subnormal cases below in its
+    own tests)."""
+    prev = fq.set_gemm_small_outputs(0)
+    try:
+        yield
+    finally:
+        fq.set_gemm_small_outputs(prev)
+
+
 def _policy(fmt, default="current"):
     return "none" if fmt == "e8m0" else default
 

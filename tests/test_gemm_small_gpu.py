@@ -151,3 +151,57 @@ def test_bound_selects_the_path(fmt, block):
     torch.cuda.synchronize()
     _check(c0, a, b, f"tiled {fmt}/{block}")
     _check(c1, a, b, f"small {fmt}/{block}")
+
+
+def _quant_elem(x_np, block, fmt, elem):
+    pol = "none" if fmt == "e8m0" else "current"
+    qt = fq.fp4_quantize(to_device(x_np), block, fmt, amax=pol, element=elem)
+    q, s, g, _ = oracle.quantize_tensor(x_np, block, fmt, pol, nthreads=8, elem=elem)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(qt.q), q, f"{elem} {fmt}/{block} operand codes")
+    assert_bytes_equal(host(qt.scales), s, f"{elem} {fmt}/{block} operand scales")
+    return qt, oracle.dequantize_f64(q, s, g, block, fmt, elem=elem)
+
+
+@pytest.mark.parametrize("elem,fmt,block", [("fp8_e4m3", "e8m0", 32), ("fp8_e4m3", "e8m0", 16),
+                                            ("int8", "e4m3", 16), ("int8", "e4m3", 32)])
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_small_path_8bit(small_path, elem, fmt, block, m, n, k):
+    """The 8-bit pairings of the register-conversion kernel on the small
+    path (quant_prune_distill/486 "Метод": MXFP8; quant_prune_distill/574
+    "Метод": INT8 beside FP8): MXFP8 to bf16 with the E8M0 scale applied,
+    INT8 with E4M3 scales to f16; 32 bytes per lane per chunk."""
+    qa, a = _quant_elem(_normal(m, k, 61 + m), block, fmt, elem)
+    qb, b = _quant_elem(_normal(n, k, 62 + n, 0.02), block, fmt, elem)
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check(c, a, b, f"small {elem} {fmt}/{block} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("elem,fmt,block", [("fp8_e4m3", "e8m0", 32), ("int8", "e4m3", 16)])
+def test_small_path_8bit_wide_range(small_path, elem, fmt, block):
+    """Rows spanning many binades with outliers on the 8-bit grids."""
+    rng = np.random.default_rng(8)
+    a = _normal(40, 512, 33) * np.exp2(rng.integers(-20, 21, (40, 1))).astype(np.float32)
+    w = _normal(72, 512, 34, 0.02)
+    w[rng.random(w.shape) < 0.01] *= 50
+    qa, ah = _quant_elem(a, block, fmt, elem)
+    qb, bh = _quant_elem(w, block, fmt, elem)
+    c = fq.fp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    _check(c, ah, bh, f"wide range {elem} {fmt}/{block}")
+
+
+@pytest.mark.parametrize("elem,fmt", [("fp8_e4m3", "e8m0"), ("int8", "e4m3")])
+def test_small_path_8bit_every_code(small_path, elem, fmt):
+    """Every 8-bit element code through the small path's decode (the tiled
+    kernels' every-code case, run here with the small path forced)."""
+    from tests import test_8bit_gpu
+    test_8bit_gpu.test_8bit_gemm_every_code(elem, fmt)
+
+
+def test_small_path_mxfp8_subnormal_products(small_path):
+    """MXFP8 products below bf16's normal range through the small path (the
+    tiled kernels' subnormal case, run here with the small path forced)."""
+    from tests import test_8bit_gpu
+    test_8bit_gpu.test_mxfp8_gemm_subnormal_products()
