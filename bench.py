@@ -44,9 +44,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "sources": ["fp4_block_scaled_quantize_amd/csrc/quant.hip", "fp4_block_scaled_quantize_amd/csrc/fp4_device.hpp",
                 "fp4_block_scaled_quantize_amd/csrc/fp4_internal.h"],
-    "sha256": "048f12c3f7b5239953c249f1aeb8b2a471d346609454c6daa15b14d619cfefa5",
-    "read_bytes": 33864146,
-    "write_bytes": 9453697,
+    "sha256": "5b9276969ebeac3214d9d7dcb1300c735b2e8947247a76ef0f677e336c4bb3a5",
+    "read_bytes": 33861632,
+    "write_bytes": 9453696,
     "profile": "profiles/quantize_fused_4096_hbm_traffic.md",
 }
 
