@@ -1455,15 +1455,18 @@ static hipError_t launch_nv(const GemmLaunch& p, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Small products (few 256 x 256 tiles, so the tiled kernels would leave most
 // CUs idle or multiply mostly padding): one wave per 32 x 32 output tile,
-// four waves per workgroup along n, operands straight from global memory
-// into registers, no LDS and no barrier.  Lane l takes row l % 32 of each
+// four waves per workgroup along n, or (KSPLIT, for fewer tiles than
+// SIMDs) the four waves of a workgroup splitting K of one tile (chunk c to
+// wave c mod 4) with the partial tiles summed once in LDS at the end in a
+// fixed order; operands straight from global memory into registers.  Lane
+// l takes row l % 32 of each
 // operand and, of every 64-element chunk, the 16 bytes (32 E2M1 codes) of
 // K-half l / 32: exactly one lane fragment of the scaled FP4 instruction
 // (E8M0 scales, with the lane's own scale byte), or four 8-element
 // fragments of the f16 / bf16 instruction after the in-register conversion
 // of the ExMy forms (the K order inside a chunk permuted identically for
-// both operands, which leaves every dot product unchanged).  Eight chunks are in flight
-// per lane.
+// both operands, which leaves every dot product unchanged).  Eight chunks
+// are in flight per lane.
 // MODE: 0 E2M1 with E4M3 scales (hardware scale decode), 1 other f16-exact
 // scale formats (decoded in registers), 2 MXFP4, 3 the bf16-exact ExMy
 // formats (UE5M3, E5M2, E6M1, E7M0, and pairs of them with the f16 ones):
@@ -1481,7 +1484,7 @@ constexpr int kSmallWaves = 4;
 constexpr int kSmallAhead = 8;
 int64_t g_gemm_small_outputs = (int64_t)1 << 21;
 
-template <int MODE, int BLOCK>
+template <int MODE, int BLOCK, bool KSPLIT>
 __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 {
     static_assert(MODE != 2 || BLOCK == 32, "MXFP4 scales cover 32 elements");
@@ -1490,13 +1493,19 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
     constexpr int AH = W8 ? kSmallAhead / 2 : kSmallAhead;
     constexpr int NQ = W8 ? 2 : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = ((int64_t)blockIdx.x * kSmallWaves + wave) * 32, m0 = (int64_t)blockIdx.y * 32;
-    if (n0 >= p.n) return;                    // whole waves only; no barrier follows
+    const int64_t n0 = ((int64_t)blockIdx.x * (KSPLIT ? 1 : kSmallWaves) + (KSPLIT ? 0 : wave)) * 32;
+    const int64_t m0 = (int64_t)blockIdx.y * 32;
+    if (!KSPLIT && n0 >= p.n) return;         // whole waves; this form has no barrier
     const int r = lane & 31, h = lane >> 5;
     const int64_t nr = n0 + r < p.n ? n0 + r : p.n - 1;
     const int64_t mr = m0 + r < p.m ? m0 + r : p.m - 1;
     const int64_t rowb = W8 ? p.k : p.k / 2, srow = p.k / BLOCK;
     const int nc = (int)(p.k / 64);
+    // this wave's chunks: KSPLIT wave, wave + W, wave + 2 W, ... (W waves),
+    // else all of them
+    constexpr int STEP = KSPLIT ? kSmallWaves : 1;
+    const int first = KSPLIT ? wave : 0;
+    const int mine = nc > first ? (nc - first + STEP - 1) / STEP : 0;
     // chunk c of this lane: codes at 32 c + 16 h of the row (one byte per
     // element: 64 c + 32 h, two 16-byte pieces); scales (block 16) the dword
     // at 4 c holding both K-halves' two bytes, (block 32) the u16 at 2 c
@@ -1535,8 +1544,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 
     v4i cw[AH][NQ], ca[AH][NQ];
     uint32_t cs[AH], ct[AH];
-    auto load = [&](int i, int c) {
-        const int cc = c < nc ? c : nc - 1;   // past the end: the last chunk again, never used
+    // the wave's j-th chunk into buffer i (past its last: the last again, or
+    // chunk 0 for a wave with none; never used)
+    auto load = [&](int i, int j) {
+        const int cc = mine == 0 ? 0 : first + STEP * (j < mine ? j : mine - 1);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             cw[i][q] = *reinterpret_cast<const v4i*>(qw + CB * (int64_t)cc + 16 * q);
@@ -1548,10 +1559,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
 #pragma unroll
     for (int i = 0; i < AH; ++i) load(i, i);
     v16f acc = {};
-    for (int c0 = 0; c0 < nc; c0 += AH) {
+    for (int j0 = 0; j0 < mine; j0 += AH) {
 #pragma unroll
         for (int i = 0; i < AH; ++i) {
-            if (c0 + i < nc) {
+            if (j0 + i < mine) {
                 if constexpr (MODE == 2) {
                     const v8i w8{cw[i][0][0], cw[i][0][1], cw[i][0][2], cw[i][0][3], 0, 0, 0, 0};
                     const v8i a8{ca[i][0][0], ca[i][0][1], ca[i][0][2], ca[i][0][3], 0, 0, 0, 0};
@@ -1605,21 +1616,44 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_gemm_small(GemmLaunch p)
                     }
                 }
             }
-            load(i, c0 + AH + i);
+            load(i, j0 + AH + i);
         }
     }
 
-    // acc[4 q + e] = D[n0 + 8 q + 4 h + e][m0 + r]: C[m][n .. n + 3] as bf16
+    // KSPLIT: the waves' partial tiles summed in LDS in wave order
+    // (deterministic); wave w then owns registers 4 w .. 4 w + 3 of the sum
+    constexpr int NQS = KSPLIT ? 1 : 4;           // register quads this wave stores
+    float v[4 * NQS];
+    if constexpr (KSPLIT) {
+        __shared__ float part[kSmallWaves][16][64];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part[wave][e][lane] = acc[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float sum = part[0][4 * wave + e][lane];
+#pragma unroll
+            for (int u = 1; u < kSmallWaves; ++u) sum += part[u][4 * wave + e][lane];
+            v[e] = sum;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = acc[e];
+    }
+
+    // register 4 q + e of the tile is D[n0 + 8 q + 4 h + e][m0 + r]: C[m][n ..
+    // n + 3] as bf16 (KSPLIT: this wave's q = w)
     const int64_t m = m0 + r;
     if (m >= p.m) return;
     const float g = FOLD ? (p.ga[0] / pa) * (p.gb[0] / pw) : p.ga[0] * p.gb[0];
     uint16_t* crow = p.c + m * p.ldc;
     const bool vec = ((p.ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.c) & 7) == 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int qi = 0; qi < NQS; ++qi) {
+        const int q = KSPLIT ? wave : qi;
         const int64_t n = n0 + 8 * q + 4 * h;
-        const uint32_t b0 = f32_to_bf16_rne(acc[4 * q + 0] * g), b1 = f32_to_bf16_rne(acc[4 * q + 1] * g);
-        const uint32_t b2 = f32_to_bf16_rne(acc[4 * q + 2] * g), b3 = f32_to_bf16_rne(acc[4 * q + 3] * g);
+        const uint32_t b0 = f32_to_bf16_rne(v[4 * qi + 0] * g), b1 = f32_to_bf16_rne(v[4 * qi + 1] * g);
+        const uint32_t b2 = f32_to_bf16_rne(v[4 * qi + 2] * g), b3 = f32_to_bf16_rne(v[4 * qi + 3] * g);
         if (vec && n + 3 < p.n) {
             *reinterpret_cast<uint2*>(crow + n) = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
         } else {
@@ -1657,28 +1691,45 @@ bool gemm_small_supported(const GemmLaunch& p)
     return exact_in_bf16(p.fa) && exact_in_bf16(p.fb) && mn <= 1.5 * (double)bound;
 }
 
+// Fewer 32 x 32 output tiles than SIMDs: the four waves of a workgroup split
+// K of one tile (more waves in flight, each a quarter of the chunks);
+// otherwise each wave takes a tile of its own.  Measured on the MI355X
+// (graph replays, us, whole-K waves -> K split): NVFP4 64 x 11008 x 4096
+// 37.1 -> 34.7, UE5M3 62.7 -> 41.6, MXFP8 48 -> 42, 64 x 256 x 256 UE5M3
+// 9.5 -> 7.5 and MXFP4 6.8 -> 5.9; but NVFP4 512 x 4096 x 4096 (2048
+// tiles) 68 -> 85.
+template <int MODE, int BLOCK>
+static void launch_small_mode(const GemmLaunch& p, hipStream_t s)
+{
+    const int64_t tm = (p.m + 31) / 32, tn = (p.n + 31) / 32;
+    const dim3 t(64 * kSmallWaves);
+    if (tm * tn < 1024)
+        hipLaunchKernelGGL((k_gemm_small<MODE, BLOCK, true>), dim3((unsigned)tn, (unsigned)tm), t, 0, s, p);
+    else
+        hipLaunchKernelGGL((k_gemm_small<MODE, BLOCK, false>), dim3((unsigned)((tn + kSmallWaves - 1) / kSmallWaves),
+                           (unsigned)tm), t, 0, s, p);
+}
+
 hipError_t launch_gemm_small(const GemmLaunch& p, hipStream_t s)
 {
-    const dim3 grid((unsigned)((p.n + 32 * kSmallWaves - 1) / (32 * kSmallWaves)), (unsigned)((p.m + 31) / 32));
-    const dim3 t(64 * kSmallWaves);
     if (p.elem == 2) {
-        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<5, 16>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<5, 32>), grid, t, 0, s, p);
+        if (p.block == 16) launch_small_mode<5, 16>(p, s);
+        else launch_small_mode<5, 32>(p, s);
     } else if (p.elem == 3) {
-        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<6, 16>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<6, 32>), grid, t, 0, s, p);
+        if (p.block == 16) launch_small_mode<6, 16>(p, s);
+        else launch_small_mode<6, 32>(p, s);
     } else if (p.fa.is_e8m0) {
-        if (p.block == 32) hipLaunchKernelGGL((k_gemm_small<2, 32>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<4, 16>), grid, t, 0, s, p);
+        if (p.block == 32) launch_small_mode<2, 32>(p, s);
+        else launch_small_mode<4, 16>(p, s);
     } else if (!(exact_in_f16(p.fa) && exact_in_f16(p.fb))) {
-        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<3, 16>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<3, 32>), grid, t, 0, s, p);
+        if (p.block == 16) launch_small_mode<3, 16>(p, s);
+        else launch_small_mode<3, 32>(p, s);
     } else if (is_e4m3(p.fa) && is_e4m3(p.fb)) {
-        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<0, 16>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<0, 32>), grid, t, 0, s, p);
+        if (p.block == 16) launch_small_mode<0, 16>(p, s);
+        else launch_small_mode<0, 32>(p, s);
     } else {
-        if (p.block == 16) hipLaunchKernelGGL((k_gemm_small<1, 16>), grid, t, 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_small<1, 32>), grid, t, 0, s, p);
+        if (p.block == 16) launch_small_mode<1, 16>(p, s);
+        else launch_small_mode<1, 32>(p, s);
     }
     return hipGetLastError();
 }
